@@ -1,0 +1,143 @@
+/* so2conv.h -- C ABI of the MI355X fused edgewise SO(2) convolution.
+ *
+ * The operation (TrimSO(2): Fast and Memory-Efficient Training of Equivariant
+ * Interatomic Potentials; Section 2 Eq.(1)-(2), Section 3.2, Appendix A.1-A.2
+ * and B.1-B.3): for every directed edge e = (j -> i), j = src[e], i = dst[e],
+ *   v_e = pos[j] - pos[i] + shift_e                          (A.1 edge geometry)
+ *   D_e = real Wigner-D blocks of the frame R_e, R_e v_e/|v_e| = +z
+ *   T_e = s_e * (D_e [x_j | x_i]),  s_e = rbf_e W_rad         (B.1, C.1 radial scaling)
+ *   first SO(2) linear per order m (Eq.(1)), gated activation (B.2),
+ *   second SO(2) linear, y_i = sum_{e -> i} (J D_e)^T t_e      (B.3)
+ * with backward (Section 3.3 Eq.(4)) and double backward (Eq.(5), A.3 Eq.(3)).
+ *
+ * Conventions (all arrays row-major, contiguous):
+ *   L = lmax (0..6), M = mmax (0..L), C = channels (multiple of 16, 16..256),
+ *   d = (L+1)^2 node rows in degree-major order (l, m = -l..l), real
+ *   orthonormal harmonics without Condon-Shortley phase (Y_1 ~ (y, z, x)).
+ *   Node features x, y, gx, gy, px: [N, d, C] float32.
+ *   pos, gpos, ppos: [N, 3] float32.  shift, gedge, pedge: [E, 3] float32.
+ *   rbf, grbf, prbf: [E, n_rbf] float32 (n_rbf a multiple of 4).
+ *   w_rad: [n_rbf, (L+1) * 2C], column (l, c_in), c_in < C: source channels.
+ *   w1[0]: [(L+1)*2C, (L+1)*C + L*C]  rows (l, c_in); columns (l, c) then the
+ *          gate columns (l = 1..L, c).
+ *   w1[m]: [(L-m+1)*2C, 2*(L-m+1)*C] = [W_m0 | W_m1], rows (l = m..L, c_in),
+ *          u_+ = T_+ W_m0 - T_- W_m1, u_- = T_+ W_m1 + T_- W_m0 (Eq.(1)), "+"
+ *          is order +m, "-" is order -m.
+ *   w2[0]: [(L+1)*C, (L+1)*C];  w2[m]: [(L-m+1)*C, 2*(L-m+1)*C].
+ *   Gate: l = 0 -> SiLU(u); l >= 1 -> sigmoid(gate_{l,c}) * u for every
+ *   retained order |m| <= min(l, M).
+ *   Graph: dst non-decreasing (edges grouped by receiver).
+ *
+ * Ownership: every array pointer is a caller-owned DEVICE pointer on the
+ * current HIP device, except the pointer arrays w1/w2/gw1/... themselves,
+ * which are HOST arrays of M+1 device pointers. The library never allocates
+ * device memory: scratch comes from the caller's workspace `ws` (size from
+ * so2conv_workspace_bytes), intermediate state kept for differentiation from
+ * `saved` (size from so2conv_saved_bytes). Work is enqueued on `stream`
+ * (a hipStream_t, NULL = default stream); no call synchronises.
+ *
+ * Errors: a negative so2_status is returned and so2conv_last_error() gives a
+ * message (thread-local). Argument checks happen on the host before any
+ * work is enqueued. Outputs are overwritten; a NULL output pointer means "not
+ * requested" and its work is skipped. Results are bitwise reproducible for
+ * identical inputs (fixed-order reductions, no floating-point atomics).
+ */
+#ifndef SO2CONV_H
+#define SO2CONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SO2_OK = 0,
+  SO2_EINVAL = -1,        /* bad argument (null required pointer, bad size, ...) */
+  SO2_EUNSUPPORTED = -2,  /* configuration without compiled kernels */
+  SO2_EWORKSPACE = -3,    /* workspace or saved buffer too small */
+  SO2_EHIP = -4,          /* a HIP runtime call failed */
+  SO2_EDEVICE = -5        /* device-side validation failed */
+} so2_status;
+
+typedef enum { SO2_F32 = 0 } so2_dtype;
+
+typedef struct {
+  int32_t lmax, mmax, channels, n_rbf, dtype, flags;
+} so2conv_cfg;
+
+typedef struct {
+  int32_t n_nodes;
+  int64_t n_edges;
+  const int32_t* src;      /* [E] sender j */
+  const int32_t* dst;      /* [E] receiver i, non-decreasing */
+  const float* shift;      /* [E,3] periodic image shift, or NULL */
+  const int32_t* dst_ptr;  /* [N+1] from so2conv_graph_prepare */
+  const int32_t* src_perm; /* [E]   from so2conv_graph_prepare */
+  const int32_t* src_ptr;  /* [N+1] from so2conv_graph_prepare */
+} so2conv_graph;
+
+/* Incoming-edge CSR over receivers (Appendix B.3) and the stable grouping of
+ * edges by sender used by the source-side sums of the backward (Eq.(4)).
+ * dst_ptr[n] = first edge with dst >= n; src_perm = edge ids sorted stably by
+ * src; src_ptr[n] = first position in src_perm with src >= n. err_word
+ * (device int, caller-zeroed, may be NULL) gets bits OR-ed in: 1 src out of
+ * range, 2 dst out of range, 4 dst decreasing. */
+size_t so2conv_graph_workspace_bytes(int32_t n_nodes, int64_t n_edges);
+int so2conv_graph_prepare(int32_t n_nodes, int64_t n_edges, const int32_t* src, const int32_t* dst,
+                          int32_t* dst_ptr, int32_t* src_perm, int32_t* src_ptr, int32_t* err_word, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* stage: 0 forward, 1 backward, 2 double backward */
+size_t so2conv_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage);
+/* per-edge state written by so2conv_fwd and read by bwd/dbwd */
+size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges);
+
+/* Forward: y [N,d,C]. `saved` (may be NULL) receives the state needed by
+ * so2conv_bwd / so2conv_dbwd for the same inputs. */
+int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
+                const float* w_rad, const float* const* w1, const float* const* w2, float* y, void* saved,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Backward (vector-Jacobian product with cotangent gy, Section 3.3): gx, gpos,
+ * grbf, gw_rad, gw1[m], gw2[m] and gedge = dL/dv_e (for virials). `saved`
+ * must come from so2conv_fwd on the same inputs. gw1/gw2 may be NULL, or hold
+ * NULL entries. */
+int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
+                const float* w_rad, const float* const* w1, const float* const* w2, const void* saved,
+                const float* gy, float* gx, float* gpos, float* grbf, float* gw_rad, float* const* gw1,
+                float* const* gw2, float* gedge, void* ws, size_t ws_bytes, void* stream);
+
+/* Double backward: derivatives of
+ *   L = <px, gx> + <ppos, gpos> + <pedge, gedge> + <prbf, grbf> + <pw, gw>
+ * (the backward's outputs paired with directions; NULL direction = zero) with
+ * respect to gy (ggy = the forward's directional derivative, Eq.(5)), x (gx2),
+ * rbf (grbf2), w_rad, w1, w2. gpos2 (second derivatives in positions) is not
+ * provided by this version and must be NULL. */
+int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
+                 const float* w_rad, const float* const* w1, const float* const* w2, const void* saved,
+                 const float* gy, const float* px, const float* ppos, const float* pedge, const float* prbf,
+                 const float* pw_rad, const float* const* pw1, const float* const* pw2, float* ggy, float* gx2,
+                 float* gpos2, float* grbf2, float* gw_rad2, float* const* gw1_2, float* const* gw2_2, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* Test hook: the first linear's m-major input T (rotation on gather,
+ * Appendix B.1) [E, q*2C], block |m| = 0..M: block 0 columns (l, c_in), block
+ * m columns [+m (l = m..L, c_in) | -m (l = m..L, c_in)], with the pinned edge
+ * frame rows (z >= 0, k = 1/(1+z): (1-x^2k, -xyk, -x), (-xyk, 1-y^2k, -y),
+ * (x, y, z); z < 0, k = 1/(1-z): (1-x^2k, -xyk, x), (xyk, y^2k-1, -y), (x, y, z)). */
+int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos,
+                                const float* rbf, const float* w_rad, float* T_out, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* message of the last failing call on this thread ("" if none) */
+const char* so2conv_last_error(void);
+/* 1 if (lmax, mmax) has compiled kernels */
+int so2conv_supported(int32_t lmax, int32_t mmax);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SO2CONV_H */

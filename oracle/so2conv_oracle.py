@@ -198,6 +198,31 @@ def _so2_linear(Tp, Tm, W):
     return Q00 - Q11, Q10 + Q01
 
 
+def _rotated_inputs(inp: OracleInputs, e_idx, D):
+    """Rotation on gather (B.1): T^(l)[m, c] = s[l, c] * sum_m' D[m, m'] a[m', c], all rows m."""
+    L, C = inp.L, inp.C
+    src, dst = inp.src[e_idx], inp.dst[e_idx]
+    E = e_idx.shape[0]
+    s = (inp.rbf[e_idx] @ inp.w_rad).view(E, L + 1, 2 * C)
+    T = []
+    for l in range(L + 1):
+        blk = slice(l * l, (l + 1) * (l + 1))
+        a = torch.cat([inp.x[src, blk, :], inp.x[dst, blk, :]], -1)         # [E, n, 2C]
+        T.append(s[:, l, None, :] * (D[l] @ a))
+    return T
+
+
+def rotated_inputs(inp: OracleInputs, e_idx=None):
+    """Per degree l, [E', 2l+1, 2C]: the first linear's input before order selection,
+    in the pinned edge frame (used to check the rotation-on-gather stage alone)."""
+    if e_idx is None:
+        e_idx = torch.arange(inp.src.shape[0])
+    v = inp.pos[inp.src[e_idx]] - inp.pos[inp.dst[e_idx]] + inp.shift[e_idx]
+    R = edge_frame(v / torch.linalg.norm(v, dim=-1, keepdim=True))
+    D = [wigner_d(l, R) for l in range(inp.L + 1)]
+    return _rotated_inputs(inp, e_idx, D)
+
+
 def edge_messages(inp: OracleInputs, e_idx: torch.Tensor, roll: torch.Tensor | None = None):
     """Global-frame messages of the edges e_idx: list over l of [E', 2l+1, C].
 
@@ -212,13 +237,7 @@ def edge_messages(inp: OracleInputs, e_idx: torch.Tensor, roll: torch.Tensor | N
     if roll is not None:
         R = _rot_z(roll) @ R
     D = [wigner_d(l, R) for l in range(L + 1)]
-    s = (inp.rbf[e_idx] @ inp.w_rad).view(E, L + 1, 2 * C)
-    # rotation on gather: T^(l)[m, c] = s[l, c] * sum_m' D[m, m'] a[m', c]
-    T = []
-    for l in range(L + 1):
-        blk = slice(l * l, (l + 1) * (l + 1))
-        a = torch.cat([inp.x[src, blk, :], inp.x[dst, blk, :]], -1)         # [E, n, 2C]
-        T.append(s[:, l, None, :] * (D[l] @ a))
+    T = _rotated_inputs(inp, e_idx, D)
     # first SO(2) linear
     u = {}
     T0 = torch.cat([T[l][:, l, :] for l in range(L + 1)], -1)

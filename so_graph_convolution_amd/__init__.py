@@ -1,0 +1,9 @@
+"""MI355X-native fused edgewise SO(2) convolution (forward, backward, double backward).
+
+The computation lives in the HIP library libso2conv.so (C ABI declared in
+include/so2conv.h); this package is its thin PyTorch binding.
+"""
+from ._binding import EXPORTS, LIB_PATH, So2Error, lib  # noqa: F401
+from .ops import (DBWD_KEYS, GRAD_KEYS, Graph, SO2Config, so2conv_bwd, so2conv_dbwd,  # noqa: F401
+                  so2conv_debug_rotate_gather, so2conv_fwd, so2conv_graph_prepare, so2conv_saved_bytes,
+                  so2conv_workspace_bytes, weight_shapes)

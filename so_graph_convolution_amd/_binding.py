@@ -1,0 +1,79 @@
+"""ctypes binding of libso2conv.so (argument marshalling only).
+
+Every step of the convolution runs in the library's HIP kernels; this module
+only passes tensor storage pointers, sizes and the current HIP stream. There
+is no fallback: if the library is missing, importing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libso2conv.so")
+
+SO2_OK, SO2_EINVAL, SO2_EUNSUPPORTED, SO2_EWORKSPACE, SO2_EHIP, SO2_EDEVICE = 0, -1, -2, -3, -4, -5
+
+c_vp = ctypes.c_void_p
+c_sz = ctypes.c_size_t
+c_i32 = ctypes.c_int32
+c_i64 = ctypes.c_int64
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [("lmax", c_i32), ("mmax", c_i32), ("channels", c_i32), ("n_rbf", c_i32), ("dtype", c_i32),
+                ("flags", c_i32)]
+
+
+class GraphC(ctypes.Structure):
+    _fields_ = [("n_nodes", c_i32), ("n_edges", c_i64), ("src", c_vp), ("dst", c_vp), ("shift", c_vp),
+                ("dst_ptr", c_vp), ("src_perm", c_vp), ("src_ptr", c_vp)]
+
+
+EXPORTS = {
+    "so2conv_graph_workspace_bytes": (c_sz, [c_i32, c_i64]),
+    "so2conv_graph_prepare": (ctypes.c_int, [c_i32, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "so2conv_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i32, c_i64, ctypes.c_int]),
+    "so2conv_saved_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i64]),
+    "so2conv_fwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                   c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "so2conv_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                   c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "so2conv_dbwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "so2conv_debug_rotate_gather": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp,
+                                                   c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "so2conv_last_error": (ctypes.c_char_p, []),
+    "so2conv_supported": (ctypes.c_int, [c_i32, c_i32]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with so_graph_convolution_amd/build.py "
+                              "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class So2Error(RuntimeError):
+    def __init__(self, code, where):
+        msg = lib().so2conv_last_error().decode()
+        super().__init__(f"{where} failed with status {code}: {msg}")
+        self.code = code
+
+
+def check(code, where):
+    if code != SO2_OK:
+        raise So2Error(code, where)

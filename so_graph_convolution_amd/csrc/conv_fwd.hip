@@ -1,0 +1,285 @@
+// Forward kernels of the fused SO(2) convolution.
+//
+//   edge_fwd  : rotation on gather (TrimSO(2) page, Section 3.2 and Appendix
+//               B.1): per edge tile, build the frame and compact Wigner rows in
+//               LDS, gather [x_src | x_dst] rows (coalesced over channels),
+//               rotate, apply the radial scale and write the m-major input of
+//               the first SO(2) linear.
+//   gate_fwd  : gated activation on the first linear's output (Appendix B.2):
+//               SiLU on l = 0, sigmoid(gate_l) on every retained order of l >= 1.
+//   node_fwd  : inverse rotation on reduction (Appendix B.3): one block per
+//               target node walks its incoming-edge range (edges sorted by
+//               target), regenerates each edge's rotation rows, accumulates
+//               R^T t in registers and writes the node row once. No atomics.
+#include "ops.hpp"
+#include "dispatch.hpp"
+#include "rotation.hpp"
+
+namespace so2 {
+
+int upload_generators_fwd(const float* host) { return upload_generators_here(host); }
+
+namespace {
+
+constexpr int kTileE = 32;   // edges per LDS tile
+
+// ------------------------------------------------------------------ edge_fwd
+template <int L, int M>
+__global__ __launch_bounds__(256) void edge_fwd_kernel(Dims d, GraphDev g, const float* __restrict__ x,
+                                                       const float* __restrict__ pos, const float* __restrict__ S,
+                                                       float* __restrict__ T) {
+  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
+  __shared__ float sD1[kTileE * 9];
+  __shared__ float sR[kTileE * K];
+  __shared__ float sA[kTileE * ST], sB[kTileE * ST];
+  __shared__ int sNode[2][kTileE];
+
+  const long e0 = (long)blockIdx.x * kTileE;
+  const int ne = (int)min((long)kTileE, g.E - e0);
+  for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+    const long e = e0 + t;
+    const int j = g.src[e], i = g.dst[e];
+    sNode[0][t] = j;
+    sNode[1][t] = i;
+    edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
+  }
+  __syncthreads();
+  wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+
+  const int C = d.C, Ci = 2 * C, wT = d.wT();
+  const int ldS = (L + 1) * Ci;
+  for (int c = threadIdx.x; c < Ci; c += blockDim.x) {
+    const int half = c >= C, cc = c - half * C;
+    for (int t = 0; t < ne; ++t) {
+      const long e = e0 + t;
+      const float* xr = x + (size_t)sNode[half][t] * D * C + cc;
+      float a[D];
+#pragma unroll
+      for (int r = 0; r < D; ++r) a[r] = xr[(size_t)r * C];
+      float o[Q];
+      rot_fwd<L, M>(sR + t * K, a, o);
+      const float* sr = S + (size_t)e * ldS + c;
+      float* tr = T + (size_t)e * wT;
+#pragma unroll
+      for (int l = 0; l <= L; ++l) {
+        const float sc = sr[l * Ci];
+        const int q = qhalf(l, M);
+#pragma unroll
+        for (int m = -q; m <= q; ++m) tr[mm_col(l, m, c, L, Ci)] = sc * o[ridx(l, m, M)];
+      }
+    }
+  }
+}
+
+template <int L, int M>
+struct EdgeFwd {
+  static int run(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, float* T,
+                 hipStream_t s) {
+    const long nb = (g.E + kTileE - 1) / kTileE;
+    if (nb == 0) return hipSuccess;
+    const int threads = min(256, ((2 * d.C + 63) / 64) * 64);
+    hipLaunchKernelGGL((edge_fwd_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, x, pos, S, T);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ node_fwd
+template <int L, int M>
+__global__ __launch_bounds__(256) void node_fwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
+                                                       const float* __restrict__ V, float* __restrict__ y) {
+  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
+  __shared__ float sD1[kTileE * 9];
+  __shared__ float sR[kTileE * K];
+  __shared__ float sA[kTileE * ST], sB[kTileE * ST];
+
+  const int node = blockIdx.x;
+  const int beg = g.dst_ptr[node], end = g.dst_ptr[node + 1];
+  const int C = d.C, wZ = d.wZ();
+  const int c = threadIdx.x;          // one channel per thread (blockDim == C)
+  float acc[D];
+#pragma unroll
+  for (int r = 0; r < D; ++r) acc[r] = 0.f;
+
+  for (int t0 = beg; t0 < end; t0 += kTileE) {
+    const int ne = min(kTileE, end - t0);
+    for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+      const long e = t0 + t;
+      edge_geometry(pos, g.shift, g.src[e], node, e, sD1 + 9 * t);
+    }
+    __syncthreads();
+    wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+    if (c < C) {
+      for (int t = 0; t < ne; ++t) {
+        const float* vr = V + (size_t)(t0 + t) * wZ + c;
+        float tv[Q];
+#pragma unroll
+        for (int l = 0; l <= L; ++l) {
+          const int q = qhalf(l, M);
+#pragma unroll
+          for (int m = -q; m <= q; ++m) tv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
+        }
+        rot_bwd_acc<L, M>(sR + t * K, tv, acc);
+      }
+    }
+    __syncthreads();
+  }
+  if (c < C) {
+    float* yr = y + (size_t)node * D * C + c;
+#pragma unroll
+    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = acc[r];
+  }
+}
+
+template <int L, int M>
+struct NodeFwd {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, hipStream_t s) {
+    if (g.N == 0) return hipSuccess;
+    hipLaunchKernelGGL((node_fwd_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, V, y);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ gate_fwd
+__device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
+
+// one thread per (edge, l, c): reads the gate once, scales every retained order of l
+__global__ void gate_fwd_kernel(Dims d, long E, const float* __restrict__ U, float* __restrict__ Z) {
+  const int L = d.L, M = d.M, C = d.C;
+  const long n = E * (L + 1) * C;
+  const int wU = d.wU(), wZ = d.wZ();
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
+    const long e = idx / ((L + 1) * C);
+    const int rem = (int)(idx - e * (L + 1) * C);
+    const int l = rem / C, c = rem - l * C;
+    const float* ur = U + e * wU;
+    float* zr = Z + e * wZ;
+    if (l == 0) {
+      const float u = ur[c];
+      zr[c] = u * sigm(u);
+    } else {
+      const float gs = sigm(ur[d.gate_col(l, c)]);
+      const int q = qhalf(l, M);
+      for (int m = -q; m <= q; ++m) zr[mm_col(l, m, c, L, C)] = gs * ur[d.u_col(l, m, c)];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ weights
+__global__ void realify_kernel(const float* __restrict__ w, int k, int h, float* __restrict__ wr) {
+  // w: [k][2h] = [W0 | W1]; wr: [2k][2h] = [[W0, W1], [-W1, W0]]
+  const long n = (long)2 * k * 2 * h;
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
+    const int r = (int)(idx / (2 * h)), col = (int)(idx - (long)r * 2 * h);
+    const int rr = r % k, lower = r >= k, right = col >= h, cc = col % h;
+    float v;
+    if (!lower) v = w[(long)rr * 2 * h + col];
+    else v = right ? w[(long)rr * 2 * h + cc] : -w[(long)rr * 2 * h + h + cc];
+    wr[idx] = v;
+  }
+}
+
+__global__ void fold_kernel(const float* __restrict__ gr, int k, int h, float* __restrict__ gw) {
+  // gw[k][2h]: [G00 + G11 | G01 - G10]
+  const long n = (long)k * 2 * h;
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
+    const int r = (int)(idx / (2 * h)), col = (int)(idx - (long)r * 2 * h);
+    const int cc = col % h;
+    const long top = (long)r * 2 * h, bot = (long)(r + k) * 2 * h;
+    gw[idx] = col < h ? gr[top + cc] + gr[bot + h + cc] : gr[top + h + cc] - gr[bot + cc];
+  }
+}
+
+inline int grid_for(long n) {
+  long b = (n + 255) / 256;
+  if (b > 16384) b = 16384;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+}  // namespace
+
+int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, float* T,
+                    hipStream_t s) {
+  return dispatch_lm<EdgeFwd>(d.L, d.M, d, g, x, pos, S, T, s);
+}
+
+int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, hipStream_t s) {
+  return dispatch_lm<NodeFwd>(d.L, d.M, d, g, pos, V, y, s);
+}
+
+int launch_gate_fwd(const Dims& d, long E, const float* U, float* Z, hipStream_t s) {
+  const long n = E * (d.L + 1) * d.C;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_fwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Z);
+  return hipGetLastError();
+}
+
+void realified_shape(const Dims& d, int second, int a, int* rows, int* cols, long* off) {
+  const int win = second ? d.C : 2 * d.C;
+  long o = 0;
+  for (int b = 0; b <= d.M; ++b) {
+    int r, c;
+    if (b == 0) {
+      r = (d.L + 1) * win;
+      c = second ? (d.L + 1) * d.C : (2 * d.L + 1) * d.C;
+    } else {
+      r = 2 * (d.L - b + 1) * win;
+      c = 2 * (d.L - b + 1) * d.C;
+    }
+    if (b == a) {
+      *rows = r;
+      *cols = c;
+      *off = o;
+      return;
+    }
+    o += (long)r * c;
+  }
+}
+
+long realified_size(const Dims& d, int second) {
+  int r, c;
+  long off;
+  realified_shape(d, second, d.M, &r, &c, &off);
+  return off + (long)r * c;
+}
+
+int launch_realify(const Dims& d, int second, const float* const* w, float* wr, hipStream_t s) {
+  for (int a = 0; a <= d.M; ++a) {
+    int r, c;
+    long off;
+    realified_shape(d, second, a, &r, &c, &off);
+    if (a == 0) {
+      hipError_t e = hipMemcpyAsync(wr + off, w[0], sizeof(float) * (size_t)r * c, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+    } else {
+      const int k = r / 2, h = c / 2;
+      hipLaunchKernelGGL(realify_kernel, dim3(grid_for((long)r * c)), dim3(256), 0, s, w[a], k, h, wr + off);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+int launch_fold_grad(const Dims& d, int second, const float* gr, float* const* gw, hipStream_t s) {
+  for (int a = 0; a <= d.M; ++a) {
+    if (!gw[a]) continue;
+    int r, c;
+    long off;
+    realified_shape(d, second, a, &r, &c, &off);
+    if (a == 0) {
+      hipError_t e = hipMemcpyAsync(gw[0], gr + off, sizeof(float) * (size_t)r * c, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+    } else {
+      const int k = r / 2, h = c / 2;
+      hipLaunchKernelGGL(fold_kernel, dim3(grid_for((long)k * c)), dim3(256), 0, s, gr + off, k, h, gw[a]);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+bool lm_supported(int L, int M) { return lm_pair_compiled(L, M); }
+
+}  // namespace so2

@@ -1,0 +1,46 @@
+// Grouped fp32 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
+//
+// The per-order SO(2) linears (TrimSO(2) page, Section 3.1 and Eq.(1)) are
+// the one dense contraction of the convolution: for every retained order a
+// [rows x k] by [k x n] product. One launch covers several such problems.
+//   C = op(A) op(B)   (or C += ... with accumulate)
+//   op(A)[i][k] = TA ? A[k*lda + i] : A[i*lda + k]
+//   op(B)[k][j] = TB ? B[j*ldb + k] : B[k*ldb + j]
+// TA problems (weight gradients, K = edges) are split over K; every split
+// writes its own partial tile and gemm_reduce sums the splits in a fixed
+// order, so results are bitwise reproducible (no atomics).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace so2 {
+
+constexpr int kGemmMaxProbs = 8;
+
+struct GemmProb {
+  const float* A;
+  const float* B;
+  float* C;          // output, or the partial buffer [k_splits][M][N] of a split problem
+  int M, N, K;
+  int lda, ldb, ldc;
+  int tiles_m, tiles_n;
+  int k_splits;      // >= 1
+  int k_chunk;       // K rows per split (multiple of the K tile)
+  int accumulate;    // add into C (non-partial problems only)
+  int partial;       // write split s to C + s*M*N (row pitch N) instead of C
+  int tile_begin;    // first linear tile of this problem
+};
+
+struct GemmBatch {
+  GemmProb p[kGemmMaxProbs];
+  int nprob;
+  int total_tiles;
+};
+
+// Fill tiling fields and launch. Every problem of one batch shares TA/TB.
+// Returns a hipError_t.
+int gemm_run(GemmBatch& b, bool TA, bool TB, hipStream_t s);
+
+// C[i*ldc + j] (+)= sum_{s < splits} P[s][i][j]  (fixed order)
+int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s);
+
+}  // namespace so2

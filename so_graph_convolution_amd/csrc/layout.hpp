@@ -1,0 +1,79 @@
+// Index arithmetic shared by host and device code of the SO(2) convolution library.
+//
+// Notation (TrimSO(2) page, Section 2 and Appendix A.2): L = lmax, M = mmax,
+// C = node channels, Ci = 2C message input channels ([source | target]),
+// degree-major node rows (l, m) at l*l + l + m, retained orders |m| <= min(l, M).
+//
+// "m-major" edge layouts (the GEMM layouts of Appendix B.1/B.3): one row per
+// edge, blocks for |m| = 0..M. With channel width W:
+//   block 0 : columns (l = 0..L, c)                               width (L+1) W
+//   block m : columns [ +m : (l = m..L, c) | -m : (l = m..L, c) ] width 2 (L-m+1) W
+// Total width q_{L,M} W. The first linear's output adds L*C gate columns
+// (l = 1..L, c) to block 0.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace so2 {
+
+constexpr int kMaxL = 6;
+
+__host__ __device__ constexpr inline int imin(int a, int b) { return a < b ? a : b; }
+__host__ __device__ constexpr inline int iabs(int a) { return a < 0 ? -a : a; }
+
+// retained half-width of degree l
+__host__ __device__ constexpr inline int qhalf(int l, int M) { return imin(l, M); }
+
+// q_{L,M} = sum_l (2 min(l,M) + 1)
+__host__ __device__ constexpr inline int q_count(int L, int M) {
+  return (L + 1) * (2 * M + 1) - M * (M + 1);
+}
+
+// offset of the compact rotation rows of degree l; entry (l, m, n) lives at
+// rot_off(l) + (m + qhalf(l)) * (2l+1) + (n + l)
+__host__ __device__ constexpr inline int rot_off(int l, int M) {
+  int o = 0;
+  for (int k = 0; k < l; ++k) o += (2 * qhalf(k, M) + 1) * (2 * k + 1);
+  return o;
+}
+__host__ __device__ constexpr inline int k_count(int L, int M) { return rot_off(L + 1, M); }
+
+// first column of block |m| = a in an m-major layout of channel width W
+__host__ __device__ constexpr inline int mm_block(int a, int L, int W) {
+  // (L+1) + sum_{m'=1}^{a-1} 2 (L - m' + 1)
+  return a == 0 ? 0 : W * ((L + 1) + 2 * ((a - 1) * (L + 1) - (a - 1) * a / 2));
+}
+// width of block |m| = a
+__host__ __device__ constexpr inline int mm_width(int a, int L, int W) {
+  return a == 0 ? (L + 1) * W : 2 * (L - a + 1) * W;
+}
+// column of (l, m, c) in an m-major layout of channel width W
+__host__ __device__ constexpr inline int mm_col(int l, int m, int c, int L, int W) {
+  const int a = iabs(m);
+  return a == 0 ? l * W + c : mm_block(a, L, W) + (m < 0 ? (L - a + 1) * W : 0) + (l - a) * W + c;
+}
+
+// so(3) generator table: degree l block at gen_off(l), (2l+1)^2 entries
+__host__ __device__ constexpr inline int gen_off(int l) { return l == 0 ? 0 : gen_off(l - 1) + (2 * l - 1) * (2 * l - 1); }
+constexpr int kGenSize = gen_off(kMaxL + 1);   // 455 per generator
+
+struct Dims {
+  int L, M, C;
+  __host__ __device__ int Ci() const { return 2 * C; }
+  __host__ __device__ int d() const { return (L + 1) * (L + 1); }
+  __host__ __device__ int q() const { return q_count(L, M); }
+  __host__ __device__ int K() const { return k_count(L, M); }
+  __host__ __device__ int wT() const { return q() * 2 * C; }        // rotated input row
+  __host__ __device__ int wZ() const { return q() * C; }            // hidden / message row
+  __host__ __device__ int wU() const { return q() * C + L * C; }    // first-linear output row
+  // column of block a in the first-linear output (block 0 carries the gate columns)
+  __host__ __device__ int u_block(int a) const { return a == 0 ? 0 : mm_block(a, L, C) + L * C; }
+  __host__ __device__ int u_width(int a) const { return a == 0 ? (2 * L + 1) * C : mm_width(a, L, C); }
+  __host__ __device__ int gate_col(int l, int c) const { return (L + 1) * C + (l - 1) * C + c; }
+  // U column of (l, m, c)
+  __host__ __device__ int u_col(int l, int m, int c) const {
+    return m == 0 ? l * C + c : mm_col(l, m, c, L, C) + L * C;
+  }
+};
+
+}  // namespace so2

@@ -1,0 +1,83 @@
+// Host-side launchers of the convolution's kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include "layout.hpp"
+
+namespace so2 {
+
+struct GraphDev {
+  int N;
+  long E;
+  const int* src;
+  const int* dst;
+  const float* shift;     // [E,3] or null
+  const int* dst_ptr;     // [N+1] incoming-edge ranges (edges sorted by dst)
+  const int* src_perm;    // [E] edge ids ordered by (src, edge id)
+  const int* src_ptr;     // [N+1] ranges into src_perm
+};
+
+// (lmax, mmax) pairs with compiled kernels
+bool lm_supported(int L, int M);
+
+// upload the so(3) generator tables to the current device (idempotent per device)
+int init_generators();
+
+// ---- forward
+// T[e] (m-major, width q*2C) = S[e] * (R_e [x_src | x_dst])
+int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, float* T,
+                     hipStream_t s);
+// Z = gate(U)
+int launch_gate_fwd(const Dims& d, long E, const float* U, float* Z, hipStream_t s);
+// y[i] = sum_{e -> i} R_e^T V[e]
+int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, hipStream_t s);
+
+// ---- backward
+// tbar[e] = R_e gy[dst]; tau[e] = torque of <V, R gy> (for the position gradient)
+int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, float* tbar,
+                    float* tau, hipStream_t s);
+// Ubar from Zbar (gate backward)
+int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, float* Ubar, hipStream_t s);
+// gx[n] (both halves), Sbar[e], tau_dst[e], tau_src[e]
+int launch_node_bwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
+                    const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, hipStream_t s);
+// vbar[e] = rhat x (tau1 + tau2 + tau3) / rho; gpos[n] = sum_out vbar - sum_in vbar
+int launch_pos_grad(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
+                    float* vbar, float* gpos, hipStream_t s);
+
+// ---- double backward (force-training pattern and general directions)
+// Tdot = Sdot*(R a) + S*(Rdot a + R adot), Rdot from the position direction; also writes the
+// per-edge rotation direction omega[e][3]
+int launch_edge_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
+                     const float* ppos, const float* pedge, const float* S, const float* Sdot, float* Tdot,
+                     float* omega, hipStream_t s);
+int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, float* Zdot, hipStream_t s);
+// ydot[i] = sum_e Rdot^T V + R^T Vdot
+int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
+                     const float* Vdot, float* ydot, hipStream_t s);
+// G2 rows [0,E) = R gy[dst], rows [E,2E) = Rdot gy[dst]
+int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
+                         float* G2, hipStream_t s);
+// from ZZ = [Zdot_bar; Zbar] produce UU = [Udot_bar; Ubar]
+int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, float* UU,
+                     hipStream_t s);
+// gx2 and (Sbar, Sdot_bar) from TT = [Tdot_bar; Tbar]
+int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
+                         const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
+                         float* Sbar, float* Sdot_bar, hipStream_t s);
+
+// ---- weights
+// Wr (realified per order): block 0 = W[0]; block m = [[W_m0, W_m1], [-W_m1, W_m0]]
+int launch_realify(const Dims& d, int second, const float* const* w, float* wr, hipStream_t s);
+// fold the realified gradient back: gW_m0 = G00 + G11, gW_m1 = G01 - G10 (m >= 1), gW_0 = G_0
+int launch_fold_grad(const Dims& d, int second, const float* gr, float* const* gw, hipStream_t s);
+
+// realified weight geometry: rows/cols of block a and its offset (floats) in the packed buffer
+void realified_shape(const Dims& d, int second, int a, int* rows, int* cols, long* off);
+long realified_size(const Dims& d, int second);
+
+// ---- graph preparation
+size_t graph_ws_bytes(int N, long E);
+int launch_graph_prepare(int N, long E, const int* src, const int* dst, int* dst_ptr, int* src_perm, int* src_ptr,
+                         void* ws, size_t ws_bytes, int* err_word, hipStream_t s);
+
+}  // namespace so2

@@ -1,0 +1,143 @@
+// Per-tile rotation state (edge frame, compact Wigner rows and their
+// derivatives) built in LDS, and per-channel rotation products kept in
+// registers. Used by every edge- and node-centric kernel.
+#pragma once
+#include "wigner.hpp"
+
+namespace so2 {
+
+// so(3) generators in the real harmonic basis, G_k = d/dt D(exp(t [e_k]_x)) at
+// t = 0, k = x, y, z; degree l block at gen_off(l), (2l+1)^2 row-major.
+// Each translation unit holds its own copy; the host fills every copy once
+// per device (library init) through that unit's upload function.
+static __constant__ float c_gen[3 * kGenSize];
+
+static inline int upload_generators_here(const float* host) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(c_gen), host, sizeof(float) * 3 * kGenSize, 0, hipMemcpyHostToDevice);
+}
+
+// retained-row index of (l, m): rows ordered l = 0..L, m = -q_l..q_l
+__host__ __device__ constexpr inline int ridx(int l, int m, int M) {
+  int o = 0;
+  for (int k = 0; k < l; ++k) o += 2 * qhalf(k, M) + 1;
+  return o + m + qhalf(l, M);
+}
+
+__host__ __device__ constexpr inline int wig_stride_c(int L, int M) {
+  int s = 9;
+  for (int l = 2; l < L; ++l) {
+    const int r = rows_kept(l, L, M);
+    const int w = (2 * r + 1) * (2 * l + 1);
+    s = s > w ? s : w;
+  }
+  return s;
+}
+
+struct EdgeGeo {
+  float rx, ry, rz, rho;
+};
+
+// Edge vector v = pos[src] - pos[dst] + shift (TrimSO(2) page, Appendix A.1),
+// its length and direction, and D^(1) of the edge frame.
+__device__ inline EdgeGeo edge_geometry(const float* __restrict__ pos, const float* __restrict__ shift, int j, int i,
+                                        long e, float* D1) {
+  float vx = pos[3 * j] - pos[3 * i], vy = pos[3 * j + 1] - pos[3 * i + 1], vz = pos[3 * j + 2] - pos[3 * i + 2];
+  if (shift) {
+    vx += shift[3 * e];
+    vy += shift[3 * e + 1];
+    vz += shift[3 * e + 2];
+  }
+  const float rho = sqrtf(vx * vx + vy * vy + vz * vz);
+  const float inv = 1.f / rho;
+  EdgeGeo g{vx * inv, vy * inv, vz * inv, rho};
+  float R[9];
+  edge_frame<float>(g.rx, g.ry, g.rz, R);
+  wigner_l1<float>(R, D1);
+  return g;
+}
+
+// RL[e][k][K] = R_e G_k (retained rows of D_e G_k), k = 0..2; cooperative.
+__device__ inline void rot_generator_products(int L, int M, int ne, const float* R, int ldr, float* RL, int ldrl) {
+  const int K = k_count(L, M);
+  for (int idx = threadIdx.x; idx < ne * 3 * K; idx += blockDim.x) {
+    const int e = idx / (3 * K);
+    int rem = idx - e * 3 * K;
+    const int k = rem / K;
+    rem -= k * K;
+    int l = 0;
+    while (rem >= rot_off(l + 1, M)) ++l;
+    const int n = 2 * l + 1;
+    const int loc = rem - rot_off(l, M);
+    const int mi = loc / n, col = loc - mi * n;
+    const float* Rrow = R + e * ldr + rot_off(l, M) + mi * n;
+    const float* G = c_gen + k * kGenSize + gen_off(l);
+    float s = 0.f;
+    for (int p = 0; p < n; ++p) s += Rrow[p] * G[p * n + col];
+    RL[e * ldrl + k * K + rem] = s;
+  }
+}
+
+// Rd[e][K] = R_e (sum_k w_k G_k) with per-edge weights w[e][3]; cooperative.
+__device__ inline void rot_directional(int L, int M, int ne, const float* R, int ldr, const float* w, int ldw,
+                                       float* Rd, int ldd) {
+  const int K = k_count(L, M);
+  for (int idx = threadIdx.x; idx < ne * K; idx += blockDim.x) {
+    const int e = idx / K;
+    const int rem = idx - e * K;
+    int l = 0;
+    while (rem >= rot_off(l + 1, M)) ++l;
+    const int n = 2 * l + 1;
+    const int loc = rem - rot_off(l, M);
+    const int mi = loc / n, col = loc - mi * n;
+    const float* Rrow = R + e * ldr + rot_off(l, M) + mi * n;
+    const float w0 = w[e * ldw], w1 = w[e * ldw + 1], w2 = w[e * ldw + 2];
+    const float* G0 = c_gen + gen_off(l);
+    const float* G1 = c_gen + kGenSize + gen_off(l);
+    const float* G2 = c_gen + 2 * kGenSize + gen_off(l);
+    float s = 0.f;
+    for (int p = 0; p < n; ++p) s += Rrow[p] * (w0 * G0[p * n + col] + w1 * G1[p * n + col] + w2 * G2[p * n + col]);
+    Rd[e * ldd + rem] = s;
+  }
+}
+
+// o[ridx(l,m)] = sum_n R[l][m][n] a[l*l + l + n]   (rotate degree-major -> retained rows)
+template <int L, int M>
+__device__ __forceinline__ void rot_fwd(const float* __restrict__ R, const float (&a)[(L + 1) * (L + 1)],
+                                        float (&o)[q_count(L, M)]) {
+#pragma unroll
+  for (int l = 0; l <= L; ++l) {
+    const int q = qhalf(l, M), n = 2 * l + 1;
+#pragma unroll
+    for (int m = -q; m <= q; ++m) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < n; ++k) s += R[rot_off(l, M) + (m + q) * n + k] * a[l * l + k];
+      o[ridx(l, m, M)] = s;
+    }
+  }
+}
+
+// o[l*l + l + n] += sum_m R[l][m][n] t[ridx(l,m)]   (inverse rotation of retained rows)
+template <int L, int M>
+__device__ __forceinline__ void rot_bwd_acc(const float* __restrict__ R, const float (&t)[q_count(L, M)],
+                                            float (&o)[(L + 1) * (L + 1)]) {
+#pragma unroll
+  for (int l = 0; l <= L; ++l) {
+    const int q = qhalf(l, M), n = 2 * l + 1;
+#pragma unroll
+    for (int m = -q; m <= q; ++m) {
+      const float tv = t[ridx(l, m, M)];
+#pragma unroll
+      for (int k = 0; k < n; ++k) o[l * l + k] += R[rot_off(l, M) + (m + q) * n + k] * tv;
+    }
+  }
+}
+
+// sum over a wavefront (64 lanes)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace so2

@@ -1,0 +1,232 @@
+"""PyTorch-facing calls of the C ABI (same names as the library's entry points).
+
+Tensors supply device memory, the current HIP stream orders the work; every
+step of the convolution runs in libso2conv.so. Shapes are checked here before
+any pointer is handed to a kernel.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from ._binding import Cfg, GraphC, check, lib
+
+__all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_bwd", "so2conv_dbwd",
+           "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes", "weight_shapes"]
+
+
+@dataclasses.dataclass(frozen=True)
+class SO2Config:
+    lmax: int
+    mmax: int
+    channels: int
+    n_rbf: int
+
+    def c(self) -> Cfg:
+        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, 0, 0)
+
+    @property
+    def d(self) -> int:
+        return (self.lmax + 1) ** 2
+
+
+def weight_shapes(cfg: SO2Config):
+    L, M, C = cfg.lmax, cfg.mmax, cfg.channels
+    w1 = [((L + 1) * 2 * C, (L + 1) * C + L * C)] + [((L - m + 1) * 2 * C, 2 * (L - m + 1) * C) for m in range(1, M + 1)]
+    w2 = [((L + 1) * C, (L + 1) * C)] + [((L - m + 1) * C, 2 * (L - m + 1) * C) for m in range(1, M + 1)]
+    return w1, w2
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype=torch.float32, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _ptr_array(ts, name, shapes):
+    if ts is None:
+        return None, []
+    ts = list(ts)
+    if len(ts) != len(shapes):
+        raise ValueError(f"{name} needs {len(shapes)} blocks")
+    keep = [_dev(t, f"{name}[{i}]", shape=shapes[i]) for i, t in enumerate(ts)]
+    arr = (ctypes.c_void_p * len(ts))(*[None if t is None else t.data_ptr() for t in keep])
+    return ctypes.cast(arr, ctypes.c_void_p), [arr, keep]
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class Graph:
+    """Edges j -> i (src, dst int32, dst non-decreasing) plus the CSR arrays
+    built on the device by so2conv_graph_prepare."""
+
+    def __init__(self, n_nodes, src, dst, shift=None, dst_ptr=None, src_perm=None, src_ptr=None):
+        self.n_nodes = int(n_nodes)
+        self.src = _dev(src, "src", torch.int32)
+        self.dst = _dev(dst, "dst", torch.int32)
+        self.n_edges = int(self.src.shape[0])
+        self.shift = _dev(shift, "shift", shape=(self.n_edges, 3))
+        self.dst_ptr, self.src_perm, self.src_ptr = dst_ptr, src_perm, src_ptr
+
+    def c(self) -> GraphC:
+        return GraphC(self.n_nodes, self.n_edges, self.src.data_ptr(), self.dst.data_ptr(),
+                      None if self.shift is None else self.shift.data_ptr(), self.dst_ptr.data_ptr(),
+                      self.src_perm.data_ptr(), self.src_ptr.data_ptr())
+
+
+def so2conv_graph_prepare(n_nodes, src, dst, shift=None, validate=True) -> Graph:
+    g = Graph(n_nodes, src, dst, shift)
+    dev = g.src.device
+    g.dst_ptr = torch.empty(g.n_nodes + 1, dtype=torch.int32, device=dev)
+    g.src_ptr = torch.empty(g.n_nodes + 1, dtype=torch.int32, device=dev)
+    g.src_perm = torch.empty(max(g.n_edges, 1), dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = _ws(lib().so2conv_graph_workspace_bytes(g.n_nodes, g.n_edges), dev)
+    check(lib().so2conv_graph_prepare(g.n_nodes, g.n_edges, _p(g.src), _p(g.dst), _p(g.dst_ptr), _p(g.src_perm),
+                                      _p(g.src_ptr), _p(err) if validate else None, _p(ws), ws.numel(), _stream()),
+          "so2conv_graph_prepare")
+    if validate:
+        e = int(err.item())
+        if e:
+            raise ValueError(f"invalid graph (error bits {e}: 1 src range, 2 dst range, 4 dst not sorted)")
+    return g
+
+
+def so2conv_workspace_bytes(cfg: SO2Config, n_nodes, n_edges, stage) -> int:
+    c = cfg.c()
+    return int(lib().so2conv_workspace_bytes(ctypes.byref(c), n_nodes, n_edges, stage))
+
+
+def so2conv_saved_bytes(cfg: SO2Config, n_edges) -> int:
+    c = cfg.c()
+    return int(lib().so2conv_saved_bytes(ctypes.byref(c), n_edges))
+
+
+def _common(cfg, g, x, pos, rbf, w_rad):
+    N, E, d, C = g.n_nodes, g.n_edges, cfg.d, cfg.channels
+    _dev(x, "x", shape=(N, d, C))
+    _dev(pos, "pos", shape=(N, 3))
+    _dev(rbf, "rbf", shape=(E, cfg.n_rbf))
+    _dev(w_rad, "w_rad", shape=(cfg.n_rbf, (cfg.lmax + 1) * 2 * C))
+
+
+def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None, ws=None):
+    """Returns (y, saved). `saved=True` allocates the state for bwd/dbwd."""
+    _common(cfg, g, x, pos, rbf, w_rad)
+    s1, s2 = weight_shapes(cfg)
+    p1, k1 = _ptr_array(w1, "w1", s1)
+    p2, k2 = _ptr_array(w2, "w2", s2)
+    y = torch.empty_like(x)
+    if saved is True:
+        saved = _ws(so2conv_saved_bytes(cfg, g.n_edges), x.device)
+    need = so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, 0)
+    if saved is None:
+        need += so2conv_saved_bytes(cfg, g.n_edges)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, x.device)
+    c, gc = cfg.c(), g.c()
+    check(lib().so2conv_fwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2, _p(y),
+                            _p(saved), _p(ws), ws.numel(), _stream()), "so2conv_fwd")
+    return y, saved
+
+
+GRAD_KEYS = ("x", "pos", "rbf", "w_rad", "w1", "w2", "edge")
+
+
+def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, need=GRAD_KEYS, ws=None):
+    """Returns dict gx, gpos, grbf, gw_rad, gw1, gw2, gedge (requested ones)."""
+    _common(cfg, g, x, pos, rbf, w_rad)
+    _dev(gy, "gy", shape=x.shape)
+    s1, s2 = weight_shapes(cfg)
+    p1, k1 = _ptr_array(w1, "w1", s1)
+    p2, k2 = _ptr_array(w2, "w2", s2)
+    dev = x.device
+    out = {}
+    out["gx"] = torch.empty_like(x) if "x" in need else None
+    out["gpos"] = torch.empty_like(pos) if "pos" in need else None
+    out["grbf"] = torch.empty_like(rbf) if "rbf" in need else None
+    out["gw_rad"] = torch.empty_like(w_rad) if "w_rad" in need else None
+    out["gw1"] = [torch.empty(s, device=dev) for s in s1] if "w1" in need else None
+    out["gw2"] = [torch.empty(s, device=dev) for s in s2] if "w2" in need else None
+    out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
+    q1, k3 = _ptr_array(out["gw1"], "gw1", s1)
+    q2, k4 = _ptr_array(out["gw2"], "gw2", s2)
+    nb = so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, 1)
+    if ws is None or ws.numel() < nb:
+        ws = _ws(nb, dev)
+    c, gc = cfg.c(), g.c()
+    check(lib().so2conv_bwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
+                            _p(saved), _p(gy), _p(out["gx"]), _p(out["gpos"]), _p(out["grbf"]), _p(out["gw_rad"]),
+                            q1, q2, _p(out["gedge"]), _p(ws), ws.numel(), _stream()), "so2conv_bwd")
+    return out
+
+
+DBWD_KEYS = ("gy", "x", "rbf", "w_rad", "w1", "w2")
+
+
+def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, px=None, ppos=None, pedge=None,
+                 prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None):
+    """Returns dict ggy, gx2, grbf2, gw_rad2, gw1_2, gw2_2 (requested ones)."""
+    _common(cfg, g, x, pos, rbf, w_rad)
+    _dev(gy, "gy", shape=x.shape)
+    _dev(px, "px", shape=x.shape)
+    _dev(ppos, "ppos", shape=pos.shape)
+    _dev(pedge, "pedge", shape=(g.n_edges, 3))
+    _dev(prbf, "prbf", shape=rbf.shape)
+    _dev(pw_rad, "pw_rad", shape=w_rad.shape)
+    s1, s2 = weight_shapes(cfg)
+    p1, k1 = _ptr_array(w1, "w1", s1)
+    p2, k2 = _ptr_array(w2, "w2", s2)
+    pp1, k5 = _ptr_array(pw1, "pw1", s1)
+    pp2, k6 = _ptr_array(pw2, "pw2", s2)
+    dev = x.device
+    out = {}
+    out["ggy"] = torch.empty_like(x) if "gy" in need else None
+    out["gx2"] = torch.empty_like(x) if "x" in need else None
+    out["grbf2"] = torch.empty_like(rbf) if "rbf" in need else None
+    out["gw_rad2"] = torch.empty_like(w_rad) if "w_rad" in need else None
+    out["gw1_2"] = [torch.empty(s, device=dev) for s in s1] if "w1" in need else None
+    out["gw2_2"] = [torch.empty(s, device=dev) for s in s2] if "w2" in need else None
+    q1, k3 = _ptr_array(out["gw1_2"], "gw1_2", s1)
+    q2, k4 = _ptr_array(out["gw2_2"], "gw2_2", s2)
+    nb = so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, 2)
+    if ws is None or ws.numel() < nb:
+        ws = _ws(nb, dev)
+    c, gc = cfg.c(), g.c()
+    check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
+                             _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf), _p(pw_rad), pp1, pp2,
+                             _p(out["ggy"]), _p(out["gx2"]), None, _p(out["grbf2"]), _p(out["gw_rad2"]), q1, q2,
+                             _p(ws), ws.numel(), _stream()), "so2conv_dbwd")
+    return out
+
+
+def so2conv_debug_rotate_gather(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad):
+    _common(cfg, g, x, pos, rbf, w_rad)
+    L, M = cfg.lmax, cfg.mmax
+    q = (L + 1) * (2 * M + 1) - M * (M + 1)
+    T = torch.empty(g.n_edges, q * 2 * cfg.channels, device=x.device)
+    ws = _ws(g.n_edges * (L + 1) * 2 * cfg.channels * 4 + 4096, x.device)
+    c, gc = cfg.c(), g.c()
+    check(lib().so2conv_debug_rotate_gather(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad),
+                                            _p(T), _p(ws), ws.numel(), _stream()), "so2conv_debug_rotate_gather")
+    return T

@@ -1,0 +1,71 @@
+"""Shared helpers of the GPU parity tests: seeded workloads, device copies,
+oracle evaluation and the comparison metric.
+
+Metric: per output tensor, max |gpu - oracle| / max |oracle| (max-norm
+relative error). The bar for float32 is 1e-4.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import so2_synth
+from oracle import so2conv_oracle as O
+
+TOL_F32 = 1e-4
+
+
+def workload(base="T", **over):
+    cfg = so2_synth.make_config(base, **over)
+    return so2_synth.make_inputs(cfg)
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(d):
+    import so_graph_convolution_amd as K
+    cfg = d["cfg"]
+    dev = torch.device("cuda:0")
+
+    def t(a, dt=torch.float32):
+        return torch.tensor(np.ascontiguousarray(a), dtype=dt, device=dev)
+
+    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf)
+    g = K.so2conv_graph_prepare(cfg.n_atoms, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
+    out = dict(kcfg=kc, g=g, x=t(d["x"]), pos=t(d["pos"]), rbf=t(d["rbf"]), w_rad=t(d["w_rad"]),
+               w1=[t(w) for w in d["w1"]], w2=[t(w) for w in d["w2"]])
+    for k in ("gy", "px", "ppos", "prbf"):
+        if k in d:
+            out[k] = t(d[k])
+    return out
+
+
+def relerr(gpu, ref):
+    if isinstance(gpu, (list, tuple)):
+        return max(relerr(a, b) for a, b in zip(gpu, ref))
+    g = gpu.detach().double().cpu() if isinstance(gpu, torch.Tensor) else torch.as_tensor(gpu, dtype=torch.float64)
+    r = ref.detach().double().cpu() if isinstance(ref, torch.Tensor) else torch.as_tensor(ref, dtype=torch.float64)
+    den = float(r.abs().max())
+    if den == 0.0:
+        return float((g - r).abs().max())
+    return float((g - r).abs().max()) / den
+
+
+def oracle_inputs(d):
+    return O.to_oracle_inputs(d)
+
+
+def m_major(T_by_l, L, M, W):
+    """Assemble oracle per-degree rows [E, 2l+1, W] into the documented m-major layout."""
+    E = T_by_l[0].shape[0]
+    cols = []
+    cols.append(torch.cat([T_by_l[l][:, l, :] for l in range(L + 1)], -1))
+    for m in range(1, M + 1):
+        cols.append(torch.cat([T_by_l[l][:, l + m, :] for l in range(m, L + 1)]
+                              + [T_by_l[l][:, l - m, :] for l in range(m, L + 1)], -1))
+    return torch.cat(cols, -1) if E else torch.zeros(0, sum(c.shape[1] for c in cols))

@@ -1,0 +1,46 @@
+"""The C-ABI library loads on the CPU and exports every entry point that
+include/so2conv.h declares (no compute call is made without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "so2conv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(so2conv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for must in ("so2conv_fwd", "so2conv_bwd", "so2conv_dbwd", "so2conv_graph_prepare", "so2conv_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    from so_graph_convolution_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        pytest.fail("libso2conv.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(_binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_binding.EXPORTS)
+
+
+def test_host_side_argument_checks():
+    """Configuration queries run on the host only."""
+    import so_graph_convolution_amd as K
+    lib = K.lib()
+    assert lib.so2conv_supported(4, 2) == 1
+    assert lib.so2conv_supported(7, 2) == 0
+    good = K.SO2Config(4, 2, 128, 64)
+    assert K.so2conv_saved_bytes(good, 1000) > 0
+    assert K.so2conv_workspace_bytes(good, 100, 1000, 2) > K.so2conv_workspace_bytes(good, 100, 1000, 0)
+    assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 100, 64), 10) == 0       # C not a multiple of 16
+    assert K.so2conv_saved_bytes(K.SO2Config(4, 5, 128, 64), 10) == 0       # mmax > lmax
+    assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 128, 6), 10) == 0        # n_rbf not a multiple of 4
