@@ -1,10 +1,369 @@
-// Backward kernels (placeholder until implemented).
+// Backward kernels of the fused SO(2) convolution (TrimSO(2) page, Section
+// 3.3 Eq.(4) and Appendix B.1-B.3 derivative formulas).
+//
+//   edge_bwd  : the transpose of the reduction: tbar_e = R_e gy[dst] (gather from
+//               the receiver and rotate, coalesced because edges are grouped
+//               by receiver) and the rotation torque of the reduction,
+//               tau_k = <V_e, (R_e G_k) gy[dst]>  (Rbar = t gy^T, B.3).
+//   gate_bwd  : ubar = sigmoid(gate) zbar, gatebar = sigmoid'(gate) sum_m zbar u (B.2);
+//               SiLU' on l = 0.
+//   node_bwd  : the transpose of rotation on gather (Eq.(4)): one block per node
+//               walks its incoming edges (target half of the message input)
+//               and its outgoing edges through the source permutation (source
+//               half), accumulating R^T (s * Tbar) in registers; it also writes
+//               the radial-scale gradient sbar = sum_m Tbar * (R a) and the
+//               rotation torque <s * Tbar, (R G_k) a> (Rbar = xtilde_bar a^T, B.1).
+//   pos_grad  : vbar_e = rhat x tau / rho (the frame depends on the edge
+//               direction only; the operator is invariant to the frame's roll)
+//               and gpos[n] = sum_{src=n} vbar - sum_{dst=n} vbar, per node.
 #include "ops.hpp"
+#include "dispatch.hpp"
 #include "rotation.hpp"
+
 namespace so2 {
+
 int upload_generators_bwd(const float* host) { return upload_generators_here(host); }
-int launch_edge_bwd(const Dims&, const GraphDev&, const float*, const float*, const float*, float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_gate_bwd(const Dims&, long, const float*, const float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_node_bwd(const Dims&, const GraphDev&, const float*, const float*, const float*, const float*, float*, float*, float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_pos_grad(const GraphDev&, const float*, const float*, const float*, const float*, float*, float*, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+// edges per LDS tile so that the tile state stays below 48 KB
+template <int L, int M, int EXTRA>
+constexpr int tile_edges() {
+  constexpr int per = 9 + k_count(L, M) + 2 * wig_stride_c(L, M) + EXTRA + 16;
+  return (32 * per * 4 <= 48 * 1024) ? 32 : (16 * per * 4 <= 48 * 1024) ? 16 : (8 * per * 4 <= 48 * 1024) ? 8 : 4;
 }
+
+__device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
+
+// ------------------------------------------------------------------ edge_bwd
+template <int L, int M>
+__global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
+                                                       const float* __restrict__ gy, const float* __restrict__ V,
+                                                       float* __restrict__ tbar, float* __restrict__ tau) {
+  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRL[TE * 3 * K];
+  __shared__ float sRed[TE * 4 * 3];
+  __shared__ int sDst[TE];
+
+  const long e0 = (long)blockIdx.x * TE;
+  const int ne = (int)min((long)TE, g.E - e0);
+  for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+    const long e = e0 + t;
+    const int i = g.dst[e];
+    sDst[t] = i;
+    edge_geometry(pos, g.shift, g.src[e], i, e, sD1 + 9 * t);
+  }
+  __syncthreads();
+  wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+  rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
+  __syncthreads();
+
+  const int C = d.C, wZ = d.wZ();
+  const int c = threadIdx.x;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const bool act = c < C;
+  for (int t = 0; t < ne; ++t) {
+    const long e = e0 + t;
+    float tk[3] = {0.f, 0.f, 0.f};
+    if (act) {
+      float gv[D];
+      const float* gr = gy + (size_t)sDst[t] * D * C + c;
+#pragma unroll
+      for (int r = 0; r < D; ++r) gv[r] = gr[(size_t)r * C];
+      float o[Q];
+      rot_fwd<L, M>(sR + t * K, gv, o);
+      float* tr = tbar + (size_t)e * wZ + c;
+      const float* vr = V + (size_t)e * wZ + c;
+      float vv[Q];
+#pragma unroll
+      for (int l = 0; l <= L; ++l) {
+        const int q = qhalf(l, M);
+#pragma unroll
+        for (int m = -q; m <= q; ++m) {
+          tr[mm_col(l, m, 0, L, C)] = o[ridx(l, m, M)];
+          vv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        float w[Q];
+        rot_fwd<L, M>(sRL + t * 3 * K + k * K, gv, w);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < Q; ++j) s += vv[j] * w[j];
+        tk[k] = s;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const float s = wave_sum(tk[k]);
+      if (lane == 0) sRed[(t * 4 + wave) * 3 + k] = s;
+    }
+  }
+  __syncthreads();
+  const int nw = blockDim.x / 64;
+  for (int idx = threadIdx.x; idx < ne * 3; idx += blockDim.x) {
+    const int t = idx / 3, k = idx - t * 3;
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += sRed[(t * 4 + w) * 3 + k];
+    tau[(e0 + t) * 3 + k] = s;
+  }
+}
+
+template <int L, int M>
+struct EdgeBwd {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, float* tbar,
+                 float* tau, hipStream_t s) {
+    constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
+    const long nb = (g.E + TE - 1) / TE;
+    if (nb == 0) return hipSuccess;
+    const int threads = ((d.C + 63) / 64) * 64;
+    hipLaunchKernelGGL((edge_bwd_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V, tbar, tau);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ node_bwd
+template <int L, int M>
+__device__ __forceinline__ void node_bwd_edge_half(const Dims& d, const float* __restrict__ sRt,
+                                                   const float* __restrict__ sRLt, const float (&xn)[(L + 1) * (L + 1)],
+                                                   const float* __restrict__ S, const float* __restrict__ Tbar,
+                                                   float* __restrict__ Sbar, long e, int cin,
+                                                   float (&acc)[(L + 1) * (L + 1)], float (&tk)[3]) {
+  constexpr int Q = q_count(L, M), K = k_count(L, M);
+  const int Ci = 2 * d.C, wT = d.wT(), wS = (L + 1) * Ci;
+  float xt[Q];
+  rot_fwd<L, M>(sRt, xn, xt);
+  const float* tb = Tbar + (size_t)e * wT + cin;
+  const float* sr = S + (size_t)e * wS + cin;
+  float* sb = Sbar + (size_t)e * wS + cin;
+  float xb[Q];
+#pragma unroll
+  for (int l = 0; l <= L; ++l) {
+    const int q = qhalf(l, M);
+    const float sc = sr[l * Ci];
+    float sacc = 0.f;
+#pragma unroll
+    for (int m = -q; m <= q; ++m) {
+      const float v = tb[mm_col(l, m, 0, L, Ci)];
+      sacc += v * xt[ridx(l, m, M)];
+      xb[ridx(l, m, M)] = sc * v;
+    }
+    sb[l * Ci] = sacc;
+  }
+  rot_bwd_acc<L, M>(sRt, xb, acc);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    float w[Q];
+    rot_fwd<L, M>(sRLt + k * K, xn, w);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) s += xb[j] * w[j];
+    tk[k] = s;
+  }
+}
+
+template <int L, int M>
+__global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const float* __restrict__ x,
+                                                       const float* __restrict__ pos, const float* __restrict__ S,
+                                                       const float* __restrict__ Tbar, float* __restrict__ gx,
+                                                       float* __restrict__ Sbar, float* __restrict__ tau_dst,
+                                                       float* __restrict__ tau_src) {
+  constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRL[TE * 3 * K];
+  __shared__ float sRed[TE * 4 * 3];
+  __shared__ int sE[TE];
+
+  const int node = blockIdx.x;
+  const int C = d.C;
+  const int c = threadIdx.x;
+  const bool act = c < C;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nw = blockDim.x / 64;
+  float xn[D], acc[D];
+#pragma unroll
+  for (int r = 0; r < D; ++r) {
+    xn[r] = act ? x[((size_t)node * D + r) * C + c] : 0.f;
+    acc[r] = 0.f;
+  }
+
+  for (int pass = 0; pass < 2; ++pass) {
+    // pass 0: incoming edges (this node is the receiver, target half of the input)
+    // pass 1: outgoing edges via the source permutation (source half)
+    const int beg = pass == 0 ? g.dst_ptr[node] : g.src_ptr[node];
+    const int end = pass == 0 ? g.dst_ptr[node + 1] : g.src_ptr[node + 1];
+    float* tau_out = pass == 0 ? tau_dst : tau_src;
+    for (int t0 = beg; t0 < end; t0 += TE) {
+      const int ne = min(TE, end - t0);
+      for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+        const long e = pass == 0 ? (long)(t0 + t) : (long)g.src_perm[t0 + t];
+        sE[t] = (int)e;
+        const int j = pass == 0 ? g.src[e] : node;
+        const int i = pass == 0 ? node : g.dst[e];
+        edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
+      }
+      __syncthreads();
+      wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+      rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
+      __syncthreads();
+      for (int t = 0; t < ne; ++t) {
+        float tk[3] = {0.f, 0.f, 0.f};
+        if (act) {
+          const int cin = pass == 0 ? C + c : c;
+          node_bwd_edge_half<L, M>(d, sR + t * K, sRL + t * 3 * K, xn, S, Tbar, Sbar, sE[t], cin, acc, tk);
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const float s = wave_sum(tk[k]);
+          if (lane == 0) sRed[(t * 4 + wave) * 3 + k] = s;
+        }
+      }
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < ne * 3; idx += blockDim.x) {
+        const int t = idx / 3, k = idx - t * 3;
+        float s = 0.f;
+        for (int w = 0; w < nw; ++w) s += sRed[(t * 4 + w) * 3 + k];
+        tau_out[(size_t)sE[t] * 3 + k] = s;
+      }
+      __syncthreads();
+    }
+  }
+  if (gx && act) {
+#pragma unroll
+    for (int r = 0; r < D; ++r) gx[((size_t)node * D + r) * C + c] = acc[r];
+  }
+}
+
+template <int L, int M>
+struct NodeBwd {
+  static int run(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
+                 const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, hipStream_t s) {
+    if (g.N == 0) return hipSuccess;
+    const int threads = ((d.C + 63) / 64) * 64;
+    hipLaunchKernelGGL((node_bwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, pos, S, Tbar, gx, Sbar,
+                       tau_dst, tau_src);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ gate_bwd
+__global__ void gate_bwd_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Zb,
+                                float* __restrict__ Ub) {
+  const int L = d.L, M = d.M, C = d.C;
+  const long n = E * (L + 1) * C;
+  const int wU = d.wU(), wZ = d.wZ();
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
+    const long e = idx / ((L + 1) * C);
+    const int rem = (int)(idx - e * (L + 1) * C);
+    const int l = rem / C, c = rem - l * C;
+    const float* ur = U + e * wU;
+    const float* zb = Zb + e * wZ;
+    float* ub = Ub + e * wU;
+    if (l == 0) {
+      const float u = ur[c], s = sigm(u);
+      ub[c] = zb[c] * s * (1.f + u * (1.f - s));
+    } else {
+      const float s = sigm(ur[d.gate_col(l, c)]);
+      const int q = qhalf(l, M);
+      float gsum = 0.f;
+      for (int m = -q; m <= q; ++m) {
+        const float z = zb[mm_col(l, m, c, L, C)];
+        const int uc = d.u_col(l, m, c);
+        gsum += z * ur[uc];
+        ub[uc] = s * z;
+      }
+      ub[d.gate_col(l, c)] = s * (1.f - s) * gsum;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ position gradient
+__global__ void vbar_kernel(GraphDev g, const float* __restrict__ pos, const float* __restrict__ t1,
+                            const float* __restrict__ t2, const float* __restrict__ t3, float* __restrict__ vbar) {
+  for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.E; e += (long)gridDim.x * blockDim.x) {
+    const int j = g.src[e], i = g.dst[e];
+    float vx = pos[3 * j] - pos[3 * i], vy = pos[3 * j + 1] - pos[3 * i + 1], vz = pos[3 * j + 2] - pos[3 * i + 2];
+    if (g.shift) {
+      vx += g.shift[3 * e];
+      vy += g.shift[3 * e + 1];
+      vz += g.shift[3 * e + 2];
+    }
+    const float rho = sqrtf(vx * vx + vy * vy + vz * vz), inv = 1.f / rho;
+    const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
+    const float tx = t1[3 * e] + t2[3 * e] + t3[3 * e];
+    const float ty = t1[3 * e + 1] + t2[3 * e + 1] + t3[3 * e + 1];
+    const float tz = t1[3 * e + 2] + t2[3 * e + 2] + t3[3 * e + 2];
+    vbar[3 * e] = (ry * tz - rz * ty) * inv;
+    vbar[3 * e + 1] = (rz * tx - rx * tz) * inv;
+    vbar[3 * e + 2] = (rx * ty - ry * tx) * inv;
+  }
+}
+
+__global__ void node_pos_kernel(GraphDev g, const float* __restrict__ vbar, float* __restrict__ gpos) {
+  for (long n = (long)blockIdx.x * blockDim.x + threadIdx.x; n < g.N; n += (long)gridDim.x * blockDim.x) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+    for (int k = g.src_ptr[n]; k < g.src_ptr[n + 1]; ++k) {
+      const long e = g.src_perm[k];
+      a0 += vbar[3 * e];
+      a1 += vbar[3 * e + 1];
+      a2 += vbar[3 * e + 2];
+    }
+    for (int e = g.dst_ptr[n]; e < g.dst_ptr[n + 1]; ++e) {
+      a0 -= vbar[3 * (long)e];
+      a1 -= vbar[3 * (long)e + 1];
+      a2 -= vbar[3 * (long)e + 2];
+    }
+    gpos[3 * n] = a0;
+    gpos[3 * n + 1] = a1;
+    gpos[3 * n + 2] = a2;
+  }
+}
+
+inline int grid_for(long n) {
+  long b = (n + 255) / 256;
+  if (b > 16384) b = 16384;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+}  // namespace
+
+int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, float* tbar,
+                    float* tau, hipStream_t s) {
+  return dispatch_lm<EdgeBwd>(d.L, d.M, d, g, pos, gy, V, tbar, tau, s);
+}
+
+int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, float* Ubar, hipStream_t s) {
+  const long n = E * (d.L + 1) * d.C;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_bwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Zbar, Ubar);
+  return hipGetLastError();
+}
+
+int launch_node_bwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
+                    const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, hipStream_t s) {
+  return dispatch_lm<NodeBwd>(d.L, d.M, d, g, x, pos, S, Tbar, gx, Sbar, tau_dst, tau_src, s);
+}
+
+int launch_pos_grad(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
+                    float* vbar, float* gpos, hipStream_t s) {
+  if (g.E > 0) {
+    hipLaunchKernelGGL(vbar_kernel, dim3(grid_for(g.E)), dim3(256), 0, s, g, pos, tau1, tau2, tau3, vbar);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (gpos && g.N > 0) {
+    hipLaunchKernelGGL(node_pos_kernel, dim3(grid_for(g.N)), dim3(256), 0, s, g, vbar, gpos);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace so2

@@ -1,12 +1,503 @@
-// Double-backward kernels (placeholder until implemented).
+// Double-backward kernels of the fused SO(2) convolution.
+//
+// The double backward differentiates L = <p, backward(gy)> (TrimSO(2) page,
+// Appendix A.3 Eq.(3): the force term of the training loss) with respect to
+// the inputs and gy. Since the backward is linear in gy, dL/dgy is the
+// forward's directional derivative along p (Eq.(5)), and the remaining
+// derivatives are the reverse of that directional derivative with cotangent
+// gy. Both run here as forward-over-reverse: a tangent ("dual") forward,
+// then its reverse. A position direction moves each edge direction and so
+// rotates its frame: Rdot_e = R_e Omega_e, Omega_e = sum_k w_k G_k with
+// w = drhat x rhat, drhat = (I - rhat rhat^T) dv / rho.
+//
+//   edge_dual     : Tdot = sdot * (R a) + s * (Rdot a + R adot)
+//   gate_dual     : zdot = sigmoid(g) udot + sigmoid'(g) gdot u  (SiLU'(u) udot on l = 0)
+//   node_dual     : ydot_i = sum_e Rdot^T V + R^T Vdot          (= dL/dgy)
+//   edge_bwd_dual : [R gy[dst]; Rdot gy[dst]]   (cotangents of Vdot and V)
+//   gate_dbwd     : cotangents of (udot, u) from those of (zdot, z)
+//   node_bwd_dual : dL/dx = R^T (s Tbar + sdot Tdotbar) + Rdot^T (s Tdotbar) on both
+//                   halves, and the radial-scale cotangents sbar, sdotbar.
 #include "ops.hpp"
+#include "dispatch.hpp"
 #include "rotation.hpp"
+
 namespace so2 {
+
 int upload_generators_dual(const float* host) { return upload_generators_here(host); }
-int launch_edge_dual(const Dims&, const GraphDev&, const float*, const float*, const float*, const float*, const float*, const float*, const float*, float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_gate_dual(const Dims&, long, const float*, const float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_node_dual(const Dims&, const GraphDev&, const float*, const float*, const float*, const float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_edge_bwd_dual(const Dims&, const GraphDev&, const float*, const float*, const float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_gate_dbwd(const Dims&, long, const float*, const float*, const float*, float*, hipStream_t) { return hipErrorNotSupported; }
-int launch_node_bwd_dual(const Dims&, const GraphDev&, const float*, const float*, const float*, const float*, const float*, const float*, const float*, float*, float*, float*, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+template <int L, int M, int EXTRA>
+constexpr int tile_edges() {
+  constexpr int per = 9 + k_count(L, M) + 2 * wig_stride_c(L, M) + EXTRA + 8;
+  return (32 * per * 4 <= 48 * 1024) ? 32 : (16 * per * 4 <= 48 * 1024) ? 16 : (8 * per * 4 <= 48 * 1024) ? 8 : 4;
 }
+
+__device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
+
+// direction of the edge frame's rotation for an edge-vector direction dv
+__device__ inline void frame_rate(const EdgeGeo& gg, float dx, float dy, float dz, float* w) {
+  const float inv = 1.f / gg.rho;
+  const float pr = gg.rx * dx + gg.ry * dy + gg.rz * dz;
+  const float ax = (dx - gg.rx * pr) * inv, ay = (dy - gg.ry * pr) * inv, az = (dz - gg.rz * pr) * inv;
+  // w = drhat x rhat
+  w[0] = ay * gg.rz - az * gg.ry;
+  w[1] = az * gg.rx - ax * gg.rz;
+  w[2] = ax * gg.ry - ay * gg.rx;
+}
+
+// ------------------------------------------------------------------ edge_dual
+template <int L, int M>
+__global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, const float* __restrict__ x,
+                                                        const float* __restrict__ px, const float* __restrict__ pos,
+                                                        const float* __restrict__ ppos,
+                                                        const float* __restrict__ pedge, const float* __restrict__ S,
+                                                        const float* __restrict__ Sdot, float* __restrict__ Tdot,
+                                                        float* __restrict__ omega) {
+  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRd[TE * K];
+  __shared__ float sW[TE * 3];
+  __shared__ int sNode[2][TE];
+
+  const long e0 = (long)blockIdx.x * TE;
+  const int ne = (int)min((long)TE, g.E - e0);
+  for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+    const long e = e0 + t;
+    const int j = g.src[e], i = g.dst[e];
+    sNode[0][t] = j;
+    sNode[1][t] = i;
+    const EdgeGeo gg = edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
+    float dx = 0.f, dy = 0.f, dz = 0.f;
+    if (ppos) {
+      dx = ppos[3 * j] - ppos[3 * i];
+      dy = ppos[3 * j + 1] - ppos[3 * i + 1];
+      dz = ppos[3 * j + 2] - ppos[3 * i + 2];
+    }
+    if (pedge) {
+      dx += pedge[3 * e];
+      dy += pedge[3 * e + 1];
+      dz += pedge[3 * e + 2];
+    }
+    float w[3];
+    frame_rate(gg, dx, dy, dz, w);
+    for (int k = 0; k < 3; ++k) {
+      sW[t * 3 + k] = w[k];
+      omega[e * 3 + k] = w[k];
+    }
+  }
+  __syncthreads();
+  wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+  rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
+  __syncthreads();
+
+  const int C = d.C, Ci = 2 * C, wT = d.wT(), wS = (L + 1) * Ci;
+  for (int c = threadIdx.x; c < Ci; c += blockDim.x) {
+    const int half = c >= C, cc = c - half * C;
+    for (int t = 0; t < ne; ++t) {
+      const long e = e0 + t;
+      const size_t nb = (size_t)sNode[half][t] * D * C + cc;
+      float a[D], ad[D];
+#pragma unroll
+      for (int r = 0; r < D; ++r) {
+        a[r] = x[nb + (size_t)r * C];
+        ad[r] = px ? px[nb + (size_t)r * C] : 0.f;
+      }
+      float xt[Q], y1[Q], y2[Q];
+      rot_fwd<L, M>(sR + t * K, a, xt);
+      rot_fwd<L, M>(sRd + t * K, a, y1);
+      rot_fwd<L, M>(sR + t * K, ad, y2);
+      const float* sr = S + (size_t)e * wS + c;
+      const float* sd = Sdot + (size_t)e * wS + c;
+      float* tr = Tdot + (size_t)e * wT;
+#pragma unroll
+      for (int l = 0; l <= L; ++l) {
+        const float sv = sr[l * Ci], sdv = sd[l * Ci];
+        const int q = qhalf(l, M);
+#pragma unroll
+        for (int m = -q; m <= q; ++m) {
+          const int j = ridx(l, m, M);
+          tr[mm_col(l, m, c, L, Ci)] = sdv * xt[j] + sv * (y1[j] + y2[j]);
+        }
+      }
+    }
+  }
+}
+
+template <int L, int M>
+struct EdgeDual {
+  static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
+                 const float* ppos, const float* pedge, const float* S, const float* Sdot, float* Tdot, float* omega,
+                 hipStream_t s) {
+    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+    const long nb = (g.E + TE - 1) / TE;
+    if (nb == 0) return hipSuccess;
+    const int threads = min(256, ((2 * d.C + 63) / 64) * 64);
+    hipLaunchKernelGGL((edge_dual_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, x, px, pos, ppos, pedge, S,
+                       Sdot, Tdot, omega);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ node_dual
+template <int L, int M>
+__global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
+                                                        const float* __restrict__ omega, const float* __restrict__ V,
+                                                        const float* __restrict__ Vdot, float* __restrict__ ydot) {
+  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRd[TE * K];
+  __shared__ float sW[TE * 3];
+
+  const int node = blockIdx.x;
+  const int beg = g.dst_ptr[node], end = g.dst_ptr[node + 1];
+  const int C = d.C, wZ = d.wZ();
+  const int c = threadIdx.x;
+  float acc[D];
+#pragma unroll
+  for (int r = 0; r < D; ++r) acc[r] = 0.f;
+  for (int t0 = beg; t0 < end; t0 += TE) {
+    const int ne = min(TE, end - t0);
+    for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+      const long e = t0 + t;
+      edge_geometry(pos, g.shift, g.src[e], node, e, sD1 + 9 * t);
+      for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[e * 3 + k];
+    }
+    __syncthreads();
+    wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+    rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
+    __syncthreads();
+    if (c < C) {
+      for (int t = 0; t < ne; ++t) {
+        const float* vr = V + (size_t)(t0 + t) * wZ + c;
+        const float* vd = Vdot + (size_t)(t0 + t) * wZ + c;
+        float tv[Q], tdv[Q];
+#pragma unroll
+        for (int l = 0; l <= L; ++l) {
+          const int q = qhalf(l, M);
+#pragma unroll
+          for (int m = -q; m <= q; ++m) {
+            tv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
+            tdv[ridx(l, m, M)] = vd[mm_col(l, m, 0, L, C)];
+          }
+        }
+        rot_bwd_acc<L, M>(sRd + t * K, tv, acc);
+        rot_bwd_acc<L, M>(sR + t * K, tdv, acc);
+      }
+    }
+    __syncthreads();
+  }
+  if (c < C) {
+    float* yr = ydot + (size_t)node * D * C + c;
+#pragma unroll
+    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = acc[r];
+  }
+}
+
+template <int L, int M>
+struct NodeDual {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
+                 const float* Vdot, float* ydot, hipStream_t s) {
+    if (g.N == 0) return hipSuccess;
+    hipLaunchKernelGGL((node_dual_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, omega, V, Vdot, ydot);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ edge_bwd_dual
+template <int L, int M>
+__global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
+                                                            const float* __restrict__ omega,
+                                                            const float* __restrict__ gy, float* __restrict__ G2) {
+  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRd[TE * K];
+  __shared__ float sW[TE * 3];
+  __shared__ int sDst[TE];
+
+  const long e0 = (long)blockIdx.x * TE;
+  const int ne = (int)min((long)TE, g.E - e0);
+  for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+    const long e = e0 + t;
+    const int i = g.dst[e];
+    sDst[t] = i;
+    edge_geometry(pos, g.shift, g.src[e], i, e, sD1 + 9 * t);
+    for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[e * 3 + k];
+  }
+  __syncthreads();
+  wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+  rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
+  __syncthreads();
+  const int C = d.C, wZ = d.wZ();
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    for (int t = 0; t < ne; ++t) {
+      const long e = e0 + t;
+      float gv[D];
+      const float* gr = gy + (size_t)sDst[t] * D * C + c;
+#pragma unroll
+      for (int r = 0; r < D; ++r) gv[r] = gr[(size_t)r * C];
+      float o1[Q], o2[Q];
+      rot_fwd<L, M>(sR + t * K, gv, o1);
+      rot_fwd<L, M>(sRd + t * K, gv, o2);
+      float* r1 = G2 + (size_t)e * wZ + c;
+      float* r2 = G2 + ((size_t)g.E + e) * wZ + c;
+#pragma unroll
+      for (int l = 0; l <= L; ++l) {
+        const int q = qhalf(l, M);
+#pragma unroll
+        for (int m = -q; m <= q; ++m) {
+          r1[mm_col(l, m, 0, L, C)] = o1[ridx(l, m, M)];
+          r2[mm_col(l, m, 0, L, C)] = o2[ridx(l, m, M)];
+        }
+      }
+    }
+  }
+}
+
+template <int L, int M>
+struct EdgeBwdDual {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, float* G2,
+                 hipStream_t s) {
+    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+    const long nb = (g.E + TE - 1) / TE;
+    if (nb == 0) return hipSuccess;
+    const int threads = ((d.C + 63) / 64) * 64;
+    hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy, G2);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ node_bwd_dual
+template <int L, int M>
+__global__ __launch_bounds__(256) void node_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ x,
+                                                            const float* __restrict__ px,
+                                                            const float* __restrict__ pos,
+                                                            const float* __restrict__ omega,
+                                                            const float* __restrict__ S,
+                                                            const float* __restrict__ Sdot,
+                                                            const float* __restrict__ TT, float* __restrict__ gx2,
+                                                            float* __restrict__ Sbar, float* __restrict__ Sdb) {
+  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRd[TE * K];
+  __shared__ float sW[TE * 3];
+  __shared__ int sE[TE];
+
+  const int node = blockIdx.x;
+  const int C = d.C, Ci = 2 * C, wT = d.wT(), wS = (L + 1) * Ci;
+  const int c = threadIdx.x;
+  const bool act = c < C;
+  float xn[D], xdn[D], acc[D];
+#pragma unroll
+  for (int r = 0; r < D; ++r) {
+    const size_t o = ((size_t)node * D + r) * C + c;
+    xn[r] = act ? x[o] : 0.f;
+    xdn[r] = (act && px) ? px[o] : 0.f;
+    acc[r] = 0.f;
+  }
+  const float* Tdb = TT;
+  const float* Tb = TT + (size_t)g.E * wT;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int beg = pass == 0 ? g.dst_ptr[node] : g.src_ptr[node];
+    const int end = pass == 0 ? g.dst_ptr[node + 1] : g.src_ptr[node + 1];
+    for (int t0 = beg; t0 < end; t0 += TE) {
+      const int ne = min(TE, end - t0);
+      for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+        const long e = pass == 0 ? (long)(t0 + t) : (long)g.src_perm[t0 + t];
+        sE[t] = (int)e;
+        const int j = pass == 0 ? g.src[e] : node;
+        const int i = pass == 0 ? node : g.dst[e];
+        edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
+        for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[e * 3 + k];
+      }
+      __syncthreads();
+      wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+      rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
+      __syncthreads();
+      if (act) {
+        const int cin = pass == 0 ? C + c : c;
+        for (int t = 0; t < ne; ++t) {
+          const long e = sE[t];
+          const float* Rt = sR + t * K;
+          const float* Rdt = sRd + t * K;
+          float xt[Q], y1[Q], y2[Q];
+          rot_fwd<L, M>(Rt, xn, xt);
+          rot_fwd<L, M>(Rdt, xn, y1);
+          rot_fwd<L, M>(Rt, xdn, y2);
+          const float* tdb = Tdb + (size_t)e * wT + cin;
+          const float* tb = Tb + (size_t)e * wT + cin;
+          const float* sr = S + (size_t)e * wS + cin;
+          const float* sd = Sdot + (size_t)e * wS + cin;
+          float u1[Q], u2[Q];   // R^T and Rdot^T operands
+#pragma unroll
+          for (int l = 0; l <= L; ++l) {
+            const int q = qhalf(l, M);
+            const float sv = sr[l * Ci], sdv = sd[l * Ci];
+            float sb = 0.f, sdb = 0.f;
+#pragma unroll
+            for (int m = -q; m <= q; ++m) {
+              const int jj = ridx(l, m, M);
+              const float a1 = tdb[mm_col(l, m, 0, L, Ci)];
+              const float a0 = tb[mm_col(l, m, 0, L, Ci)];
+              u1[jj] = sv * a0 + sdv * a1;
+              u2[jj] = sv * a1;
+              sb += a1 * (y1[jj] + y2[jj]) + a0 * xt[jj];
+              sdb += a1 * xt[jj];
+            }
+            Sbar[(size_t)e * wS + l * Ci + cin] = sb;
+            Sdb[(size_t)e * wS + l * Ci + cin] = sdb;
+          }
+          rot_bwd_acc<L, M>(Rt, u1, acc);
+          rot_bwd_acc<L, M>(Rdt, u2, acc);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (gx2 && act) {
+#pragma unroll
+    for (int r = 0; r < D; ++r) gx2[((size_t)node * D + r) * C + c] = acc[r];
+  }
+}
+
+template <int L, int M>
+struct NodeBwdDual {
+  static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
+                 const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2, float* Sbar,
+                 float* Sdb, hipStream_t s) {
+    if (g.N == 0) return hipSuccess;
+    const int threads = ((d.C + 63) / 64) * 64;
+    hipLaunchKernelGGL((node_bwd_dual_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega, S, Sdot,
+                       TT, gx2, Sbar, Sdb);
+    return hipGetLastError();
+  }
+};
+
+// ------------------------------------------------------------------ gates
+__global__ void gate_dual_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Ud,
+                                 float* __restrict__ Zd) {
+  const int L = d.L, M = d.M, C = d.C;
+  const long n = E * (L + 1) * C;
+  const int wU = d.wU(), wZ = d.wZ();
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
+    const long e = idx / ((L + 1) * C);
+    const int rem = (int)(idx - e * (L + 1) * C);
+    const int l = rem / C, c = rem - l * C;
+    const float* ur = U + e * wU;
+    const float* udr = Ud + e * wU;
+    float* zr = Zd + e * wZ;
+    if (l == 0) {
+      const float u = ur[c], s = sigm(u);
+      zr[c] = s * (1.f + u * (1.f - s)) * udr[c];
+    } else {
+      const int gc = d.gate_col(l, c);
+      const float s = sigm(ur[gc]), sp = s * (1.f - s), gd = udr[gc];
+      const int q = qhalf(l, M);
+      for (int m = -q; m <= q; ++m) {
+        const int uc = d.u_col(l, m, c);
+        zr[mm_col(l, m, c, L, C)] = s * udr[uc] + sp * gd * ur[uc];
+      }
+    }
+  }
+}
+
+// ZZ = [zdot_bar (E rows); zbar (E rows)] -> UU = [udot_bar; ubar]
+__global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Ud,
+                                 const float* __restrict__ ZZ, float* __restrict__ UU) {
+  const int L = d.L, M = d.M, C = d.C;
+  const long n = E * (L + 1) * C;
+  const int wU = d.wU(), wZ = d.wZ();
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
+    const long e = idx / ((L + 1) * C);
+    const int rem = (int)(idx - e * (L + 1) * C);
+    const int l = rem / C, c = rem - l * C;
+    const float* ur = U + e * wU;
+    const float* udr = Ud + e * wU;
+    const float* zdb = ZZ + e * wZ;
+    const float* zb = ZZ + (E + e) * wZ;
+    float* udb = UU + e * wU;
+    float* ub = UU + (E + e) * wU;
+    if (l == 0) {
+      const float u = ur[c], s = sigm(u);
+      const float s1 = s * (1.f + u * (1.f - s));
+      const float s2 = s * (1.f - s) * (2.f + u * (1.f - 2.f * s));
+      udb[c] = s1 * zdb[c];
+      ub[c] = s2 * udr[c] * zdb[c] + s1 * zb[c];
+    } else {
+      const int gc = d.gate_col(l, c);
+      const float s = sigm(ur[gc]), sp = s * (1.f - s), spp = sp * (1.f - 2.f * s), gd = udr[gc];
+      const int q = qhalf(l, M);
+      float gdb = 0.f, gb = 0.f;
+      for (int m = -q; m <= q; ++m) {
+        const int uc = d.u_col(l, m, c), zc = mm_col(l, m, c, L, C);
+        const float a = zdb[zc], b = zb[zc], u = ur[uc], ud = udr[uc];
+        udb[uc] = s * a;
+        ub[uc] = sp * gd * a + s * b;
+        gdb += a * u;
+        gb += spp * gd * u * a + sp * ud * a + sp * u * b;
+      }
+      udb[gc] = sp * gdb;
+      ub[gc] = gb;
+    }
+  }
+}
+
+inline int grid_for(long n) {
+  long b = (n + 255) / 256;
+  if (b > 16384) b = 16384;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+}  // namespace
+
+int launch_edge_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
+                     const float* ppos, const float* pedge, const float* S, const float* Sdot, float* Tdot,
+                     float* omega, hipStream_t s) {
+  return dispatch_lm<EdgeDual>(d.L, d.M, d, g, x, px, pos, ppos, pedge, S, Sdot, Tdot, omega, s);
+}
+
+int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, float* Zdot, hipStream_t s) {
+  const long n = E * (d.L + 1) * d.C;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_dual_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, Zdot);
+  return hipGetLastError();
+}
+
+int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
+                     const float* Vdot, float* ydot, hipStream_t s) {
+  return dispatch_lm<NodeDual>(d.L, d.M, d, g, pos, omega, V, Vdot, ydot, s);
+}
+
+int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
+                         float* G2, hipStream_t s) {
+  return dispatch_lm<EdgeBwdDual>(d.L, d.M, d, g, pos, omega, gy, G2, s);
+}
+
+int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, float* UU,
+                     hipStream_t s) {
+  const long n = E * (d.L + 1) * d.C;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_dbwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, ZZ, UU);
+  return hipGetLastError();
+}
+
+int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
+                         const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
+                         float* Sbar, float* Sdot_bar, hipStream_t s) {
+  return dispatch_lm<NodeBwdDual>(d.L, d.M, d, g, x, px, pos, omega, S, Sdot, TT, gx2, Sbar, Sdot_bar, s);
+}
+
+}  // namespace so2
