@@ -1,0 +1,176 @@
+#!/usr/bin/env python
+"""Benchmark: edges/s of one fused SO(2) convolution step (forward + backward +
+double backward) on one MI355X.
+
+Workload: the UMA/eSEN-like medium system -- 10,000 atoms at 0.08 atoms/A^3 in
+a periodic cube, 6 A cutoff (~725k directed edges), lmax 4, mmax 2, C 128,
+64 Gaussian radial basis functions, float32, weights ~ N(0, 1/C). Synthetic,
+seeded (so2_synth). A step runs so2conv_fwd (keeping the differentiation
+state), so2conv_bwd (all gradients, including weights and positions) and
+so2conv_dbwd (the force-training pattern: directions on x, positions and rbf),
+exactly as training on forces needs them (TrimSO(2) page, Appendix A.3).
+
+The JSON line carries the live roofline of the dominant kernel (the
+matrix-core GEMM of the per-order linears, timed with HIP events on its
+stream) and the CPU oracle timed on the host cores on a bounded edge sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "edges/sec fwd+bwd+dbwd SO(2) conv (lmax=4,C=128); HBM GB/s % of peak"
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def gemm_flops_per_edge(L, M, C):
+    """F = 2 (MAC1 + MAC2): per-edge multiply-adds of the two per-order linears
+    (input width 2C for the first, with its L*C gate columns)."""
+    s = sum((L - m + 1) ** 2 for m in range(1, M + 1))
+    mac1 = 2 * C * C * ((L + 1) * (2 * L + 1) + 4 * s)
+    mac2 = C * C * ((L + 1) ** 2 + 4 * s)
+    return 2.0 * (mac1 + mac2)
+
+
+def cpu_baseline(d, n_edges_sample, seed=0):
+    """Time the float64 oracle (fwd, bwd, dbwd) on a leading block of edges."""
+    import numpy as np
+    import torch
+    from oracle import so2conv_oracle as O
+    cores = min(16, len(os.sched_getaffinity(0)))
+    torch.set_num_threads(cores)
+    inp = O.to_oracle_inputs(d)
+    E = len(d["src"])
+    n = min(n_edges_sample, E)
+    edges = np.arange(n)
+    t = lambda a: torch.tensor(a, dtype=torch.float64)  # noqa: E731
+    gy = t(d["gy"])
+    t0 = time.perf_counter()
+    O.forward(inp, chunk=2048, edges=edges)
+    O.backward(inp, gy, chunk=2048, edges=edges)
+    O.double_backward(inp, gy, px=t(d["px"]), ppos=t(d["ppos"]), prbf=t(d["prbf"]), chunk=2048, edges=edges)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "edges/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {E} edges of the same workload, fwd+bwd+dbwd in float64 "
+                      f"(PyTorch CPU, autograd), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="M")
+    ap.add_argument("--cpu-edges", type=int, default=1024, help="edge sample of the CPU oracle baseline (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the convolution runs on a "
+              "single MI355X, see the design notes on sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import so2_synth
+    import so_graph_convolution_amd as K
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg = so2_synth.CONFIGS[args.config]
+    d = so2_synth.make_inputs(cfg)
+    progress(f"inputs ready: N={cfg.n_atoms} E={len(d['src'])}")
+    E, N = len(d["src"]), cfg.n_atoms
+    dev = torch.device("cuda:0")
+
+    def t(a, dt=torch.float32):
+        return torch.tensor(np.ascontiguousarray(a), dtype=dt, device=dev)
+
+    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf)
+    g = K.so2conv_graph_prepare(N, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
+    x, pos, rbf, w_rad = t(d["x"]), t(d["pos"]), t(d["rbf"]), t(d["w_rad"])
+    w1, w2 = [t(w) for w in d["w1"]], [t(w) for w in d["w2"]]
+    gy, px, ppos, prbf = t(d["gy"]), t(d["px"]), t(d["ppos"]), t(d["prbf"])
+    saved = torch.empty(K.so2conv_saved_bytes(kc, E), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(K.so2conv_workspace_bytes(kc, N, E, s) for s in (0, 1, 2)), dtype=torch.uint8, device=dev)
+    args_c = (kc, g, x, pos, rbf, w_rad, w1, w2)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(times=None):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record()
+        K.so2conv_fwd(*args_c, saved=saved, ws=ws)
+        e1.record()
+        K.so2conv_bwd(*args_c, saved, gy, ws=ws)
+        e2.record()
+        K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws)
+        e3.record()
+        if times is not None:
+            times.append((e0, e1, e2, e3))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    progress("warmup done")
+    K.so2conv_profile_reset()
+    K.so2conv_profile_enable(True)
+    stage = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(stage)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    K.so2conv_profile_enable(False)
+    n_l, gemm_ms, gemm_fl = K.so2conv_profile_read(-1)
+    per_kind = {}
+    for kind, name in ((0, "AB"), (1, "ABt"), (2, "AtB")):
+        n, ms, fl = K.so2conv_profile_read(kind)
+        per_kind[name] = {"launches": n, "avg_ms": ms / max(n, 1), "tflops": fl / max(ms, 1e-9) / 1e9}
+    K.so2conv_profile_reset()
+    st = np.array([[a.elapsed_time(b), b.elapsed_time(c), c.elapsed_time(e)] for a, b, c, e in stage])
+    ms_step = wall * 1e3 / args.steps
+    value = E * args.steps / wall
+    F = gemm_flops_per_edge(cfg.lmax, cfg.mmax, cfg.channels)
+    achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"UMA/eSEN-like medium periodic radius graph ({cfg.name})", "n_atoms": N,
+                   "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
+                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "kernel": "gemm_f32_kernel (fp32 MFMA per-order linears), all launches of the timed steps",
+                     "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
+                     "algorithmic_flops_per_step": gemm_fl / args.steps, "per_kind": per_kind},
+        "stage_ms": {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean()), "dbwd": float(st[:, 2].mean())},
+        "step_gemm_share": gemm_ms / args.steps / ms_step,
+        "step_tflops_8F": 8 * F * E / (ms_step * 1e-3) / 1e12,
+    }
+    progress(f"timed {args.steps} steps: {ms_step:.1f} ms/step")
+    if args.cpu_edges > 0:
+        out["cpu_baseline"] = cpu_baseline(d, args.cpu_edges)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

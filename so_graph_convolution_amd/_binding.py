@@ -45,6 +45,10 @@ EXPORTS = {
     "so2conv_debug_rotate_gather": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp,
                                                    c_vp, c_vp, c_vp, c_sz, c_vp]),
     "so2conv_last_error": (ctypes.c_char_p, []),
+    "so2conv_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "so2conv_profile_reset": (ctypes.c_int, []),
+    "so2conv_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_double)]),
     "so2conv_supported": (ctypes.c_int, [c_i32, c_i32]),
 }
 

@@ -172,13 +172,41 @@ GemmProb prob(const float* A, int lda, const float* B, int ldb, float* C, int ld
   return p;
 }
 
+// ---------------------------------------------------------------- GEMM timing
+// When enabled, every MFMA GEMM launch is bracketed by HIP events on the
+// launching stream and its algorithmic flop count (2 M N K summed over the
+// launch's problems) is recorded; so2conv_profile_read reports the totals.
+struct ProfRec {
+  int kind;          // 0 NN, 1 NT, 2 TN
+  double flops;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
 int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, hipStream_t s) {
   size_t i = 0;
   while (i < ps.size()) {
     GemmBatch b{};
     b.nprob = 0;
-    while (i < ps.size() && b.nprob < kGemmMaxProbs) b.p[b.nprob++] = ps[i++];
-    SO2_HIP(gemm_run(b, TA, TB, s));
+    double flops = 0;
+    while (i < ps.size() && b.nprob < kGemmMaxProbs) {
+      flops += 2.0 * ps[i].M * (double)ps[i].N * ps[i].K;
+      b.p[b.nprob++] = ps[i++];
+    }
+    if (g_prof_on) {
+      ProfRec r{TA ? 2 : (TB ? 1 : 0), flops, nullptr, nullptr};
+      SO2_HIP(hipEventCreate(&r.a));
+      SO2_HIP(hipEventCreate(&r.b));
+      SO2_HIP(hipEventRecord(r.a, s));
+      SO2_HIP(gemm_run(b, TA, TB, s));
+      SO2_HIP(hipEventRecord(r.b, s));
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      g_prof.push_back(r);
+    } else {
+      SO2_HIP(gemm_run(b, TA, TB, s));
+    }
   }
   return SO2_OK;
 }
@@ -341,6 +369,41 @@ size_t ws_dbwd(const Dims& d, int n_rbf, int N, long E) {
 extern "C" {
 
 const char* so2conv_last_error(void) { return g_err.c_str(); }
+
+int so2conv_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return SO2_OK;
+}
+
+int so2conv_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  return SO2_OK;
+}
+
+int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int64_t n = 0;
+  double ms = 0, fl = 0;
+  for (auto& r : g_prof) {
+    if (kind >= 0 && r.kind != kind) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(SO2_EHIP, "hipEventSynchronize failed");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return fail(SO2_EHIP, "hipEventElapsedTime failed");
+    ++n;
+    ms += t;
+    fl += r.flops;
+  }
+  if (launches) *launches = n;
+  if (total_ms) *total_ms = ms;
+  if (total_flops) *total_flops = fl;
+  return SO2_OK;
+}
 
 int so2conv_supported(int32_t lmax, int32_t mmax) { return lm_supported(lmax, mmax) ? 1 : 0; }
 

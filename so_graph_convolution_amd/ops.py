@@ -14,7 +14,8 @@ import torch
 from ._binding import Cfg, GraphC, check, lib
 
 __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_bwd", "so2conv_dbwd",
-           "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes", "weight_shapes"]
+           "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes", "weight_shapes",
+           "so2conv_profile_enable", "so2conv_profile_reset", "so2conv_profile_read"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -218,6 +219,23 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
                              _p(out["ggy"]), _p(out["gx2"]), None, _p(out["grbf2"]), _p(out["gw_rad2"]), q1, q2,
                              _p(ws), ws.numel(), _stream()), "so2conv_dbwd")
     return out
+
+
+def so2conv_profile_enable(on=True):
+    check(lib().so2conv_profile_enable(1 if on else 0), "so2conv_profile_enable")
+
+
+def so2conv_profile_reset():
+    check(lib().so2conv_profile_reset(), "so2conv_profile_reset")
+
+
+def so2conv_profile_read(kind=-1):
+    """(launches, total_ms, total_flops) of the recorded GEMM launches of one kind
+    (0: A B, 1: A B^T, 2: A^T B, -1: all)."""
+    n, ms, fl = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
+    check(lib().so2conv_profile_read(kind, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)),
+          "so2conv_profile_read")
+    return int(n.value), float(ms.value), float(fl.value)
 
 
 def so2conv_debug_rotate_gather(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad):
