@@ -70,7 +70,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="M")
-    ap.add_argument("--cpu-edges", type=int, default=1024, help="edge sample of the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the convolution runs on a "

@@ -1,132 +1,136 @@
-// Grouped fp32 MFMA GEMM: 128x128 block tiles, 4 waves of 64x64, K tile 16,
-// LDS double buffering, XCD-aware linear tile order.
+// Grouped fp32 MFMA GEMM: 128x128 block tiles, 4 waves of 64x64 (2x2
+// v_mfma_f32_32x32x2_f32 tiles each), K tile 16, LDS double buffering,
+// XCD-aware linear tile order.
+//
+// Operand staging: every global load runs along the operand's contiguous
+// dimension (float4 per lane, consecutive lanes on consecutive addresses), and
+// the LDS layout follows the global one:
+//   A row-major [i][k]  -> As[i][k]  pitch BK+4      A transposed [k][i] -> As[k][i] pitch 160
+//   B row-major [k][j]  -> Bs[k][j]  pitch 160       B transposed [j][k] -> Bs[j][k] pitch BK+4
+// An MFMA operand read takes 32 consecutive rows/columns for one k (lanes 0-31)
+// and the next k (lanes 32-63).
 #include "gemm.hpp"
 
 namespace so2 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16;
-constexpr int PAD = 32;          // row pitch 160 floats: the two k rows of one MFMA read hit disjoint banks
-constexpr int LDA_S = BM + PAD;
-constexpr int LDB_S = BN + PAD;
+// Measured on MI355X for the per-order shapes (725k rows, K and N 640..2048):
+// a 2x2 MFMA wave tile with K tile 16 at four waves per SIMD (accumulators in
+// VGPRs) ran at 117-128 TFLOP/s; 4x2 or 2x4 wave tiles (one wave per SIMD)
+// and K tiles of 8 or 32 were slower.
+constexpr int WM = 2, WN = 2;              // 32x32 MFMA tiles per wave
+constexpr int BM = 64 * WM, BN = 64 * WN;  // 2x2 waves per block
+constexpr int BK_TILE = 16;
+constexpr int WAVES_PER_SIMD = 4;
 constexpr int NT = 256;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-struct TileRegs {
-  floatx4 a[2];
-  floatx4 b[2];
+// R = rows of the tile (BM or BN)
+template <int BK, int R>
+struct Cfg {
+  static constexpr int PK = BK + 4;                 // pitch of k-contiguous tiles
+  static constexpr int PW = R + 32;                 // pitch of k-major tiles: two k rows of one read hit disjoint banks
+  static constexpr int KMAJ = BK * PW;              // floats of a k-major tile
+  static constexpr int KCON = R * PK;               // floats of a k-contiguous tile
+  static constexpr int NRC = (R * BK / 4) / NT;     // float4 loads per thread of a k-contiguous tile
+  static constexpr int NRM = (BK * R / 4) / NT;     // float4 loads per thread of a k-major tile
 };
 
-// linear block id -> tile id such that the blocks one XCD receives (round robin
-// dispatch, 8 XCDs) cover a contiguous range of tiles, so tiles sharing an
-// A row panel share that XCD's L2
+template <bool T, int BK, int R>
+constexpr int tile_floats() { return T ? Cfg<BK, R>::KMAJ : Cfg<BK, R>::KCON; }
+
+// linear block id -> tile id such that the blocks one XCD receives (round-robin
+// dispatch over 8 XCDs) cover a contiguous range of tiles
 __device__ inline int xcd_remap(int bid, int total) {
   const int q = total / 8, r = total % 8;
   const int x = bid % 8, i = bid / 8;
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-template <bool TA>
-__device__ inline void load_a(const GemmProb& p, int m0, int k0, int kend, TileRegs& R) {
+// Load one operand tile into registers.
+//   KCONTIG: the global rows run along k (row-major [row][k]); else along the
+//   128-wide dimension (row-major [k][row]).
+template <bool KCONTIG, int BK, int R>
+__device__ inline void load_tile(const float* __restrict__ P, int ld, int r0, int rlim, int k0, int kend,
+                                 floatx4 (&v)[KCONTIG ? Cfg<BK, R>::NRC : Cfg<BK, R>::NRM]) {
   const int t = threadIdx.x;
+  if (KCONTIG) {
+    constexpr int LPR = BK / 4;            // lanes per row
+    constexpr int RPP = NT / LPR;          // rows per pass
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (!TA) {
-      const int i = t % 128, kq = t / 128 + 2 * r;
-      const int gi = m0 + i, gk = k0 + 4 * kq;
-      if (gi < p.M) {
-        const float* src = p.A + (size_t)gi * p.lda + gk;
+    for (int p = 0; p < Cfg<BK, R>::NRC; ++p) {
+      const int row = p * RPP + t / LPR, q = t % LPR;
+      const int gr = r0 + row, gk = k0 + 4 * q;
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+      if (gr < rlim) {
+        const float* src = P + (size_t)gr * ld + gk;
         if (gk + 3 < kend) {
-          v = *reinterpret_cast<const floatx4*>(src);
+          x = *reinterpret_cast<const floatx4*>(src);
         } else {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) v[x] = (gk + x < kend) ? src[x] : 0.f;
+          for (int c = 0; c < 4; ++c) x[c] = (gk + c < kend) ? src[c] : 0.f;
         }
       }
-    } else {
-      const int k = t / 32 + 8 * r, iq = t % 32;
-      const int gk = k0 + k, gi = m0 + 4 * iq;
+      v[p] = x;
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < Cfg<BK, R>::NRM; ++p) {
+      constexpr int LPR = R / 4, KPP = NT / LPR;
+      const int k = p * KPP + t / LPR, q = t % LPR;
+      const int gk = k0 + k, gr = r0 + 4 * q;
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
       if (gk < kend) {
-        const float* src = p.A + (size_t)gk * p.lda + gi;
-        if (gi + 3 < p.M) {
-          v = *reinterpret_cast<const floatx4*>(src);
+        const float* src = P + (size_t)gk * ld + gr;
+        if (gr + 3 < rlim) {
+          x = *reinterpret_cast<const floatx4*>(src);
         } else {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) v[x] = (gi + x < p.M) ? src[x] : 0.f;
+          for (int c = 0; c < 4; ++c) x[c] = (gr + c < rlim) ? src[c] : 0.f;
         }
       }
+      v[p] = x;
     }
-    R.a[r] = v;
   }
 }
 
-template <bool TB>
-__device__ inline void load_b(const GemmProb& p, int n0, int k0, int kend, TileRegs& R) {
+template <bool KCONTIG, int BK, int R>
+__device__ inline void store_tile(float* __restrict__ S, const floatx4 (&v)[KCONTIG ? Cfg<BK, R>::NRC : Cfg<BK, R>::NRM]) {
   const int t = threadIdx.x;
+  if (KCONTIG) {
+    constexpr int LPR = BK / 4, RPP = NT / LPR;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (!TB) {
-      const int k = t / 32 + 8 * r, jq = t % 32;
-      const int gk = k0 + k, gj = n0 + 4 * jq;
-      if (gk < kend) {
-        const float* src = p.B + (size_t)gk * p.ldb + gj;
-        if (gj + 3 < p.N) {
-          v = *reinterpret_cast<const floatx4*>(src);
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) v[x] = (gj + x < p.N) ? src[x] : 0.f;
-        }
-      }
-    } else {
-      const int j = t % 128, kq = t / 128 + 2 * r;
-      const int gj = n0 + j, gk = k0 + 4 * kq;
-      if (gj < p.N) {
-        const float* src = p.B + (size_t)gj * p.ldb + gk;
-        if (gk + 3 < kend) {
-          v = *reinterpret_cast<const floatx4*>(src);
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) v[x] = (gk + x < kend) ? src[x] : 0.f;
-        }
-      }
+    for (int p = 0; p < Cfg<BK, R>::NRC; ++p) {
+      const int row = p * RPP + t / LPR, q = t % LPR;
+      *reinterpret_cast<floatx4*>(S + row * Cfg<BK, R>::PK + 4 * q) = v[p];
     }
-    R.b[r] = v;
-  }
-}
-
-template <bool TA, bool TB>
-__device__ inline void store_tiles(const TileRegs& R, float* As, float* Bs) {
-  const int t = threadIdx.x;
+  } else {
+    constexpr int LPR = R / 4, KPP = NT / LPR;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    if (!TA) {
-      const int i = t % 128, kq = t / 128 + 2 * r;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) As[(4 * kq + x) * LDA_S + i] = R.a[r][x];
-    } else {
-      const int k = t / 32 + 8 * r, iq = t % 32;
-      *reinterpret_cast<floatx4*>(As + k * LDA_S + 4 * iq) = R.a[r];
-    }
-    if (!TB) {
-      const int k = t / 32 + 8 * r, jq = t % 32;
-      *reinterpret_cast<floatx4*>(Bs + k * LDB_S + 4 * jq) = R.b[r];
-    } else {
-      const int j = t % 128, kq = t / 128 + 2 * r;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) Bs[(4 * kq + x) * LDB_S + j] = R.b[r][x];
+    for (int p = 0; p < Cfg<BK, R>::NRM; ++p) {
+      const int k = p * KPP + t / LPR, q = t % LPR;
+      *reinterpret_cast<floatx4*>(S + k * Cfg<BK, R>::PW + 4 * q) = v[p];
     }
   }
 }
 
-template <bool TA, bool TB>
-__global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmBatch batch) {
-  __shared__ float As[2][BK * LDA_S];
-  __shared__ float Bs[2][BK * LDB_S];
+// MFMA operand: element (row, k) of a staged tile
+template <bool KCONTIG, int BK, int R>
+__device__ __forceinline__ float frag(const float* S, int row, int k) {
+  return KCONTIG ? S[row * Cfg<BK, R>::PK + k] : S[k * Cfg<BK, R>::PW + row];
+}
+
+template <bool TA, bool TB, int BK>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, 8))) void gemm_f32_kernel(
+    GemmBatch batch) {
+  // A is k-contiguous when not transposed; B is k-contiguous when transposed
+  constexpr bool AK = !TA, BKC = TB;
+  constexpr int SA = tile_floats<!AK, BK, BM>(), SB = tile_floats<!BKC, BK, BN>();
+  __shared__ float As[2][SA];
+  __shared__ float Bs[2][SB];
 
   const int tile = xcd_remap(blockIdx.x, batch.total_tiles);
   int pi = 0;
@@ -147,43 +151,50 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmBatch batch) {
   const int wm = wave / 2, wn = wave % 2;
   const int li = lane % 32, lk = lane / 32;
 
-  floatx16 acc[2][2];
+  floatx16 acc[WM][WN];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < WM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < WN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int nk = (kend - kbeg + BK - 1) / BK;
-  TileRegs R;
+  floatx4 ra[AK ? Cfg<BK, BM>::NRC : Cfg<BK, BM>::NRM];
+  floatx4 rb[BKC ? Cfg<BK, BN>::NRC : Cfg<BK, BN>::NRM];
   if (nk > 0) {
-    load_a<TA>(p, m0, kbeg, kend, R);
-    load_b<TB>(p, n0, kbeg, kend, R);
-    store_tiles<TA, TB>(R, As[0], Bs[0]);
+    load_tile<AK, BK, BM>(p.A, p.lda, m0, p.M, kbeg, kend, ra);
+    load_tile<BKC, BK, BN>(p.B, p.ldb, n0, p.N, kbeg, kend, rb);
+    store_tile<AK, BK, BM>(As[0], ra);
+    store_tile<BKC, BK, BN>(Bs[0], rb);
   }
   __syncthreads();
 #pragma unroll 1
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      load_a<TA>(p, m0, kbeg + (kt + 1) * BK, kend, R);
-      load_b<TB>(p, n0, kbeg + (kt + 1) * BK, kend, R);
+      load_tile<AK, BK, BM>(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, ra);
+      load_tile<BKC, BK, BN>(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, rb);
     }
-    const float* as = As[cur] + wm * 64 + li;
-    const float* bs = Bs[cur] + wn * 64 + li;
+    const float* as = As[cur];
+    const float* bs = Bs[cur];
+    const int ra0 = wm * 32 * WM + li, rb0 = wn * 32 * WN + li;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 2) {
-      const float a0 = as[(kk + lk) * LDA_S];
-      const float a1 = as[(kk + lk) * LDA_S + 32];
-      const float b0 = bs[(kk + lk) * LDB_S];
-      const float b1 = bs[(kk + lk) * LDB_S + 32];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      float av[WM], bv[WN];
+#pragma unroll
+      for (int a = 0; a < WM; ++a) av[a] = frag<AK, BK, BM>(as, ra0 + 32 * a, kk + lk);
+#pragma unroll
+      for (int b = 0; b < WN; ++b) bv[b] = frag<BKC, BK, BN>(bs, rb0 + 32 * b, kk + lk);
+#pragma unroll
+      for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tiles<TA, TB>(R, As[cur ^ 1], Bs[cur ^ 1]);
+    if (kt + 1 < nk) {
+      store_tile<AK, BK, BM>(As[cur ^ 1], ra);
+      store_tile<BKC, BK, BN>(Bs[cur ^ 1], rb);
+    }
     __syncthreads();
   }
 
@@ -201,14 +212,14 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmBatch batch) {
     acc_in = p.accumulate != 0;
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < WM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int j = n0 + wn * 64 + b * 32 + li;
+    for (int b = 0; b < WN; ++b) {
+      const int j = n0 + wn * 32 * WN + b * 32 + li;
       if (j >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = m0 + wm * 64 + a * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
+        const int i = m0 + wm * 32 * WM + a * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
         if (i < p.M) {
           float* dst = out + (size_t)i * ldo + j;
           *dst = acc_in ? *dst + acc[a][b][r] : acc[a][b][r];
@@ -232,6 +243,7 @@ __global__ void gemm_reduce_kernel(const float* __restrict__ P, int splits, int 
 }  // namespace
 
 int gemm_run(GemmBatch& b, bool TA, bool TB, hipStream_t s) {
+  constexpr int BK = BK_TILE;
   int total = 0;
   for (int q = 0; q < b.nprob; ++q) {
     GemmProb& p = b.p[q];
@@ -245,10 +257,10 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, hipStream_t s) {
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
   dim3 grid(total), block(NT);
-  if (!TA && !TB) hipLaunchKernelGGL((gemm_f32_kernel<false, false>), grid, block, 0, s, b);
-  else if (!TA && TB) hipLaunchKernelGGL((gemm_f32_kernel<false, true>), grid, block, 0, s, b);
-  else if (TA && !TB) hipLaunchKernelGGL((gemm_f32_kernel<true, false>), grid, block, 0, s, b);
-  else hipLaunchKernelGGL((gemm_f32_kernel<true, true>), grid, block, 0, s, b);
+  if (!TA && !TB) hipLaunchKernelGGL((gemm_f32_kernel<false, false, BK>), grid, block, 0, s, b);
+  else if (!TA && TB) hipLaunchKernelGGL((gemm_f32_kernel<false, true, BK>), grid, block, 0, s, b);
+  else if (TA && !TB) hipLaunchKernelGGL((gemm_f32_kernel<true, false, BK>), grid, block, 0, s, b);
+  else hipLaunchKernelGGL((gemm_f32_kernel<true, true, BK>), grid, block, 0, s, b);
   return hipGetLastError();
 }
 
