@@ -89,9 +89,22 @@ int so2conv_graph_prepare(int32_t n_nodes, int64_t n_edges, const int32_t* src, 
                           int32_t* dst_ptr, int32_t* src_perm, int32_t* src_ptr, int32_t* err_word, void* ws,
                           size_t ws_bytes, void* stream);
 
-/* stage: 0 forward, 1 backward, 2 double backward */
+/* Workspace and saved state.
+ * The operator and its derivatives are sums over edges, so every call
+ * processes the edges in contiguous chunks whose size the library picks from
+ * ws_bytes (one chunk when the workspace is large enough); node outputs are
+ * accumulated across chunks in a fixed order, so results do not depend on the
+ * chunk size beyond float rounding of that order.
+ *   so2conv_saved_bytes: the per-edge forward state (about 56 KB per edge at
+ *     lmax 4, C 128) that so2conv_fwd writes into `saved` and bwd/dbwd read.
+ *   so2conv_workspace_bytes(stage): workspace for one chunk covering all edges
+ *     when `saved` is used (stage 0 forward, 1 backward, 2 double backward).
+ *   so2conv_chunked_workspace_bytes(stage, chunk_edges): workspace when `saved`
+ *     is NULL and chunks of chunk_edges edges recompute the forward state
+ *     (bounded memory; backward stages then redo the forward products). */
 size_t so2conv_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage);
-/* per-edge state written by so2conv_fwd and read by bwd/dbwd */
+size_t so2conv_chunked_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage,
+                                       int64_t chunk_edges);
 size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges);
 
 /* Forward: y [N,d,C]. `saved` (may be NULL) receives the state needed by
@@ -102,8 +115,8 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, 
 
 /* Backward (vector-Jacobian product with cotangent gy, Section 3.3): gx, gpos,
  * grbf, gw_rad, gw1[m], gw2[m] and gedge = dL/dv_e (for virials). `saved`
- * must come from so2conv_fwd on the same inputs. gw1/gw2 may be NULL, or hold
- * NULL entries. */
+ * comes from so2conv_fwd on the same inputs, or is NULL (the forward state is
+ * recomputed chunk by chunk). gw1/gw2 may be NULL, or hold NULL entries. */
 int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
                 const float* w_rad, const float* const* w1, const float* const* w2, const void* saved,
                 const float* gy, float* gx, float* gpos, float* grbf, float* gw_rad, float* const* gw1,

@@ -35,6 +35,7 @@ EXPORTS = {
     "so2conv_graph_prepare": (ctypes.c_int, [c_i32, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "so2conv_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i32, c_i64, ctypes.c_int]),
     "so2conv_saved_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i64]),
+    "so2conv_chunked_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i32, c_i64, ctypes.c_int, c_i64]),
     "so2conv_fwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                    c_vp, c_vp, c_vp, c_sz, c_vp]),
     "so2conv_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

@@ -118,6 +118,8 @@ int check_graph(const so2conv_graph* g, GraphDev* gd) {
   gd->dst_ptr = g->dst_ptr;
   gd->src_perm = g->src_perm;
   gd->src_ptr = g->src_ptr;
+  gd->e0 = 0;
+  gd->e1 = g->n_edges;
   return SO2_OK;
 }
 
@@ -316,51 +318,105 @@ int check_weights(const Dims& d, const float* w_rad, const float* const* w1, con
   return SO2_OK;
 }
 
-size_t ws_fwd(const Dims& d) {
+size_t ws_weights(const Dims& d) {
   return al(sizeof(float) * realified_size(d, 0)) + al(sizeof(float) * realified_size(d, 1));
 }
 
-size_t ws_bwd(const Dims& d, int n_rbf, int N, long E) {
-  (void)N;
-  size_t b = ws_fwd(d);
-  const size_t e = (size_t)E;
-  b += al(sizeof(float) * e * d.wZ());            // tbar
-  b += al(sizeof(float) * e * d.wZ());            // Zbar
-  b += al(sizeof(float) * e * d.wU());            // Ubar
-  b += al(sizeof(float) * e * d.wT());            // Tbar
-  b += al(sizeof(float) * e * (d.L + 1) * d.Ci()); // Sbar
-  b += 4 * al(sizeof(float) * e * 3);              // tau x3, vbar
-  b += al(sizeof(float) * realified_size(d, 0)) + al(sizeof(float) * realified_size(d, 1));
-  size_t p = tn_partial_floats(E, 1, 1, 1);  // splits + 1
-  size_t mx = (size_t)realified_size(d, 0);
-  if ((size_t)realified_size(d, 1) > mx) mx = realified_size(d, 1);
-  if ((size_t)n_rbf * (d.L + 1) * d.Ci() > mx) mx = (size_t)n_rbf * (d.L + 1) * d.Ci();
-  b += al(sizeof(float) * p * mx);
+// largest weight-gradient block (floats): realified blocks and the radial matrix
+size_t max_grad_block(const Dims& d, int n_rbf) {
+  size_t mx = (size_t)n_rbf * (d.L + 1) * d.Ci();
+  for (int second = 0; second < 2; ++second)
+    for (int a = 0; a <= d.M; ++a) {
+      int r, c;
+      long off;
+      realified_shape(d, second, a, &r, &c, &off);
+      if ((size_t)r * c > mx) mx = (size_t)r * c;
+    }
+  return mx;
+}
+
+size_t primal_floats(const Dims& d) { return (size_t)(d.L + 1) * d.Ci() + d.wT() + d.wU() + 2 * (size_t)d.wZ(); }
+
+// Workspace of one stage for a chunk of `ec` edges out of E.
+//   stage 0: forward; 1: backward; 2: double backward.
+//   recompute: the per-edge forward state lives in the workspace (saved == NULL).
+size_t ws_need(const Dims& d, int n_rbf, long E, long ec, int stage, bool recompute) {
+  const size_t e = (size_t)ec;
+  const size_t wS = (size_t)(d.L + 1) * d.Ci();
+  size_t b = ws_weights(d);
+  size_t per = recompute ? primal_floats(d) : 0;
+  int nseg = 1;
+  if (stage == 1) {
+    per += 2 * (size_t)d.wZ() + d.wU() + d.wT() + wS + 9;
+    b += ws_weights(d);                               // realified weight gradients
+    b += al(sizeof(float) * 3 * (size_t)E);           // per-edge position gradient (all edges)
+  } else if (stage == 2) {
+    b += 2 * ws_weights(d);                           // direction weights, weight gradients
+    per += wS + d.wT() + 3 + d.wU() + 2 * (size_t)d.wZ() + 4 * (size_t)d.wZ() + 2 * (size_t)d.wU() +
+           2 * (size_t)d.wT() + 2 * wS;
+    nseg = 2;
+  }
+  b += 24 * 256 + sizeof(float) * per * e;           // per-edge buffers (+ alignment)
+  if (stage > 0) {
+    int sp, ch;
+    split_plan(ec, &sp, &ch);
+    b += al(sizeof(float) * (size_t)nseg * (sp + 1) * max_grad_block(d, n_rbf));
+  }
   return b + 4096;
 }
 
-size_t ws_dbwd(const Dims& d, int n_rbf, int N, long E) {
-  (void)N;
-  size_t b = 2 * ws_fwd(d);   // W1r, W2r, pW1r, pW2r
-  const size_t e = (size_t)E;
-  b += al(sizeof(float) * e * (d.L + 1) * d.Ci());  // Sdot
-  b += al(sizeof(float) * e * d.wT());              // Tdot
-  b += al(sizeof(float) * e * 3);                   // omega
-  b += al(sizeof(float) * e * d.wU());              // Udot
-  b += al(sizeof(float) * e * d.wZ());              // Zdot
-  b += al(sizeof(float) * e * d.wZ());              // Vdot
-  b += al(sizeof(float) * 2 * e * d.wZ());          // G2
-  b += al(sizeof(float) * 2 * e * d.wZ());          // ZZ
-  b += al(sizeof(float) * 2 * e * d.wU());          // UU
-  b += al(sizeof(float) * 2 * e * d.wT());          // TT
-  b += 2 * al(sizeof(float) * e * (d.L + 1) * d.Ci());  // Sbar, Sdot_bar
-  b += al(sizeof(float) * realified_size(d, 0)) + al(sizeof(float) * realified_size(d, 1));
-  size_t p = 2 * tn_partial_floats(E, 1, 1, 1);
-  size_t mx = (size_t)realified_size(d, 0);
-  if ((size_t)realified_size(d, 1) > mx) mx = realified_size(d, 1);
-  if ((size_t)n_rbf * (d.L + 1) * d.Ci() > mx) mx = (size_t)n_rbf * (d.L + 1) * d.Ci();
-  b += al(sizeof(float) * p * mx);
-  return b + 4096;
+// edges per chunk that fit in ws_bytes (E if everything fits; 0 if not even 1024 edges do)
+long pick_chunk(const Dims& d, int n_rbf, long E, int stage, bool recompute, size_t ws_bytes) {
+  if (E == 0) return 0;
+  if (ws_need(d, n_rbf, E, E, stage, recompute) <= ws_bytes) return E;
+  long lo = 0, hi = E;
+  while (hi - lo > 1024) {
+    const long mid = (lo + hi) / 2 / 1024 * 1024;
+    if (mid <= lo) break;
+    if (ws_need(d, n_rbf, E, mid, stage, recompute) <= ws_bytes) lo = mid;
+    else hi = mid;
+  }
+  if (lo == 0 && ws_need(d, n_rbf, E, 1024 < E ? 1024 : E, stage, recompute) <= ws_bytes) lo = 1024 < E ? 1024 : E;
+  return lo;
+}
+
+struct Primal {
+  const float *S, *T, *U, *Z, *V;
+};
+
+// forward state of the chunk [g.e0, g.e1) into (S, T, U, Z, V)
+int forward_chunk(const Dims& d, int n_rbf, const GraphDev& g, const float* x, const float* pos, const float* rbf,
+                  const float* w_rad, const float* W1r, const float* W2r, float* S, float* T, float* U, float* Z,
+                  float* V, hipStream_t s) {
+  const int ec = (int)(g.e1 - g.e0);
+  int r;
+  if ((r = radial(d, n_rbf, ec, rbf + (size_t)g.e0 * n_rbf, w_rad, S, s))) return r;
+  SO2_HIP(launch_edge_fwd(d, g, x, pos, S, T, s));
+  std::vector<GemmProb> ps;
+  lin1_probs(d, T, W1r, U, ec, 0, ps);
+  if ((r = run_batch(ps, false, false, s))) return r;
+  SO2_HIP(launch_gate_fwd(d, ec, U, Z, s));
+  ps.clear();
+  lin2_probs(d, Z, W2r, V, ec, 0, ps);
+  return run_batch(ps, false, false, s);
+}
+
+int zero_grads(const Dims& d, int n_rbf, int N, float* gx, float* gpos, float* gw_rad, float* const* gw1,
+               float* const* gw2, hipStream_t s) {
+  int r;
+  const size_t dC = (size_t)d.d() * d.C;
+  if (gx && (r = fill(gx, (size_t)N * dC, s))) return r;
+  if (gpos && (r = fill(gpos, (size_t)N * 3, s))) return r;
+  if (gw_rad && (r = fill(gw_rad, (size_t)n_rbf * (d.L + 1) * d.Ci(), s))) return r;
+  for (int a = 0; a <= d.M; ++a) {
+    int rr, cc;
+    long off;
+    realified_shape(d, 0, a, &rr, &cc, &off);
+    if (gw1 && gw1[a] && (r = fill(gw1[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r;
+    realified_shape(d, 1, a, &rr, &cc, &off);
+    if (gw2 && gw2[a] && (r = fill(gw2[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r;
+  }
+  return SO2_OK;
 }
 
 }  // namespace
@@ -430,14 +486,19 @@ size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges) {
 }
 
 size_t so2conv_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage) {
+  (void)n_nodes;
   Dims d;
-  if (check_cfg(cfg, &d)) return 0;
-  switch (stage) {
-    case 0: return ws_fwd(d) + 4096;
-    case 1: return ws_bwd(d, cfg->n_rbf, n_nodes, n_edges);
-    case 2: return ws_dbwd(d, cfg->n_rbf, n_nodes, n_edges);
-    default: return 0;
-  }
+  if (check_cfg(cfg, &d) || stage < 0 || stage > 2) return 0;
+  return ws_need(d, cfg->n_rbf, n_edges, n_edges, stage, false);
+}
+
+size_t so2conv_chunked_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage,
+                                       int64_t chunk_edges) {
+  (void)n_nodes;
+  Dims d;
+  if (check_cfg(cfg, &d) || stage < 0 || stage > 2 || chunk_edges < 1) return 0;
+  const long ec = chunk_edges < n_edges ? chunk_edges : n_edges;
+  return ws_need(d, cfg->n_rbf, n_edges, ec, stage, true);
 }
 
 int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos,
@@ -470,35 +531,49 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, 
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || (!rbf && gd.E > 0) || !y) return fail(SO2_EINVAL, "NULL input or output");
   if ((r = ensure_init())) return r;
-  const SavedLayout sl = saved_layout(d, cfg->n_rbf, gd.E);
-  size_t need = ws_fwd(d) + 4096 + (saved ? 0 : sl.total);
-  if (!ws || ws_bytes < need) return fail(SO2_EWORKSPACE, "forward workspace too small");
+  const int n_rbf = cfg->n_rbf;
+  const bool recompute = saved == nullptr;
+  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
+  const long ec = pick_chunk(d, n_rbf, gd.E, 0, recompute, ws_bytes);
+  if (gd.E > 0 && ec == 0) return fail(SO2_EWORKSPACE, "forward workspace too small for a 1024-edge chunk");
+  if (ws_bytes < ws_weights(d)) return fail(SO2_EWORKSPACE, "forward workspace too small");
   hipStream_t s = (hipStream_t)stream;
   Arena ar{static_cast<char*>(ws), 0};
   float* W1r = ar.take(realified_size(d, 0));
   float* W2r = ar.take(realified_size(d, 1));
-  char* st = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + ar.used;
-  float* S = reinterpret_cast<float*>(st + sl.S);
-  float* T = reinterpret_cast<float*>(st + sl.T);
-  float* U = reinterpret_cast<float*>(st + sl.U);
-  float* Z = reinterpret_cast<float*>(st + sl.Z);
-  float* V = reinterpret_cast<float*>(st + sl.V);
-  const int E = (int)gd.E;
-
+  const SavedLayout sl = saved_layout(d, n_rbf, gd.E);
+  char* st = static_cast<char*>(saved);
+  float *S = nullptr, *T = nullptr, *U = nullptr, *Z = nullptr, *V = nullptr;
+  if (recompute) {
+    S = ar.take((size_t)ec * (d.L + 1) * d.Ci());
+    T = ar.take((size_t)ec * d.wT());
+    U = ar.take((size_t)ec * d.wU());
+    Z = ar.take((size_t)ec * d.wZ());
+    V = ar.take((size_t)ec * d.wZ());
+  }
   SO2_HIP(launch_realify(d, 0, w1, W1r, s));
   SO2_HIP(launch_realify(d, 1, w2, W2r, s));
-  if (E > 0) {
-    if ((r = radial(d, cfg->n_rbf, E, rbf, w_rad, S, s))) return r;
-    SO2_HIP(launch_edge_fwd(d, gd, x, pos, S, T, s));
-    std::vector<GemmProb> ps;
-    lin1_probs(d, T, W1r, U, E, 0, ps);
-    if ((r = run_batch(ps, false, false, s))) return r;
-    SO2_HIP(launch_gate_fwd(d, E, U, Z, s));
-    ps.clear();
-    lin2_probs(d, Z, W2r, V, E, 0, ps);
-    if ((r = run_batch(ps, false, false, s))) return r;
+  if (gd.E == 0) {
+    GraphDev gc = gd;
+    gc.e0 = gc.e1 = 0;
+    SO2_HIP(launch_node_fwd(d, gc, pos, nullptr, y, 0, s));
+    return SO2_OK;
   }
-  SO2_HIP(launch_node_fwd(d, gd, pos, V, y, s));
+  for (long e0 = 0, c = 0; e0 < gd.E; e0 += ec, ++c) {
+    GraphDev gc = gd;
+    gc.e0 = e0;
+    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
+    float *Sc = S, *Tc = T, *Uc = U, *Zc = Z, *Vc = V;
+    if (!recompute) {
+      Sc = reinterpret_cast<float*>(st + sl.S) + (size_t)e0 * (d.L + 1) * d.Ci();
+      Tc = reinterpret_cast<float*>(st + sl.T) + (size_t)e0 * d.wT();
+      Uc = reinterpret_cast<float*>(st + sl.U) + (size_t)e0 * d.wU();
+      Zc = reinterpret_cast<float*>(st + sl.Z) + (size_t)e0 * d.wZ();
+      Vc = reinterpret_cast<float*>(st + sl.V) + (size_t)e0 * d.wZ();
+    }
+    if ((r = forward_chunk(d, n_rbf, gc, x, pos, rbf, w_rad, W1r, W2r, Sc, Tc, Uc, Zc, Vc, s))) return r;
+    SO2_HIP(launch_node_fwd(d, gc, pos, Vc, y, c > 0, s));
+  }
   return SO2_OK;
 }
 
@@ -513,96 +588,104 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, 
   if ((r = check_cfg(cfg, &d)) || (r = check_graph(g, &gd))) return r;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
-  if (!saved) return fail(SO2_EINVAL, "saved state from so2conv_fwd is required");
   if ((r = ensure_init())) return r;
-  if (!ws || ws_bytes < ws_bwd(d, cfg->n_rbf, gd.N, gd.E)) return fail(SO2_EWORKSPACE, "backward workspace too small");
   hipStream_t s = (hipStream_t)stream;
-  const int E = (int)gd.E, n_rbf = cfg->n_rbf;
+  const int n_rbf = cfg->n_rbf, wS = (d.L + 1) * d.Ci();
+  if (gd.E == 0) return zero_grads(d, n_rbf, gd.N, gx, gpos, gw_rad, gw1, gw2, s);
+  const bool recompute = saved == nullptr;
+  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
+  const long ec = pick_chunk(d, n_rbf, gd.E, 1, recompute, ws_bytes);
+  if (ec == 0) return fail(SO2_EWORKSPACE, "backward workspace too small for a 1024-edge chunk");
   const SavedLayout sl = saved_layout(d, n_rbf, gd.E);
   const char* st = static_cast<const char*>(saved);
-  const float* S = reinterpret_cast<const float*>(st + sl.S);
-  const float* T = reinterpret_cast<const float*>(st + sl.T);
-  const float* U = reinterpret_cast<const float*>(st + sl.U);
-  const float* Z = reinterpret_cast<const float*>(st + sl.Z);
-  const float* V = reinterpret_cast<const float*>(st + sl.V);
   Arena ar{static_cast<char*>(ws), 0};
   float* W1r = ar.take(realified_size(d, 0));
   float* W2r = ar.take(realified_size(d, 1));
-  float* tbar = ar.take((size_t)E * d.wZ());
-  float* Zbar = ar.take((size_t)E * d.wZ());
-  float* Ubar = ar.take((size_t)E * d.wU());
-  float* Tbar = ar.take((size_t)E * d.wT());
-  float* Sbar = ar.take((size_t)E * (d.L + 1) * d.Ci());
-  float* tau1 = ar.take((size_t)E * 3);
-  float* tau2 = ar.take((size_t)E * 3);
-  float* tau3 = ar.take((size_t)E * 3);
-  float* vbar = ar.take((size_t)E * 3);
   float* gW1r = ar.take(realified_size(d, 0));
   float* gW2r = ar.take(realified_size(d, 1));
-  float* P = ar.take(0);
-  const bool want_w1 = !all_null(gw1, d.M + 1), want_w2 = !all_null(gw2, d.M + 1);
-
-  const size_t dC = (size_t)d.d() * d.C;
-  if (E == 0) {
-    if (gx) { if ((r = fill(gx, (size_t)gd.N * dC, s))) return r; }
-    if (gpos) { if ((r = fill(gpos, (size_t)gd.N * 3, s))) return r; }
-    if (gw_rad) { if ((r = fill(gw_rad, (size_t)n_rbf * (d.L + 1) * d.Ci(), s))) return r; }
-    for (int a = 0; a <= d.M; ++a) {
-      int rr, cc;
-      long off;
-      realified_shape(d, 0, a, &rr, &cc, &off);
-      if (gw1 && gw1[a]) { if ((r = fill(gw1[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r; }
-      realified_shape(d, 1, a, &rr, &cc, &off);
-      if (gw2 && gw2[a]) { if ((r = fill(gw2[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r; }
-    }
-    return SO2_OK;
+  float* vbar_all = ar.take((size_t)gd.E * 3);
+  float *S = nullptr, *T = nullptr, *U = nullptr, *Z = nullptr, *V = nullptr;
+  if (recompute) {
+    S = ar.take((size_t)ec * wS);
+    T = ar.take((size_t)ec * d.wT());
+    U = ar.take((size_t)ec * d.wU());
+    Z = ar.take((size_t)ec * d.wZ());
+    V = ar.take((size_t)ec * d.wZ());
   }
+  float* tbar = ar.take((size_t)ec * d.wZ());
+  float* Zbar = ar.take((size_t)ec * d.wZ());
+  float* Ubar = ar.take((size_t)ec * d.wU());
+  float* Tbar = ar.take((size_t)ec * d.wT());
+  float* Sbar = ar.take((size_t)ec * wS);
+  float* tau1 = ar.take((size_t)ec * 3);
+  float* tau2 = ar.take((size_t)ec * 3);
+  float* tau3 = ar.take((size_t)ec * 3);
+  float* P = ar.take(0);
+  float* vbar = gedge ? gedge : vbar_all;
+  const bool want_w1 = !all_null(gw1, d.M + 1), want_w2 = !all_null(gw2, d.M + 1);
 
   SO2_HIP(launch_realify(d, 0, w1, W1r, s));
   SO2_HIP(launch_realify(d, 1, w2, W2r, s));
-  // E -> N transpose: tbar = R gy[dst], tau1 = rotation torque of <V, R gy>
-  SO2_HIP(launch_edge_bwd(d, gd, pos, gy, V, tbar, tau1, s));
-  std::vector<GemmProb> ps;
-  lin2t_probs(d, tbar, W2r, Zbar, E, 0, ps);
-  if ((r = run_batch(ps, false, true, s))) return r;
-  if (want_w2) {
-    for (int a = 0; a <= d.M; ++a) {
-      int rr, cc;
-      long off;
-      realified_shape(d, 1, a, &rr, &cc, &off);
-      TnSeg seg{Z + mm_block(a, d.L, d.C), d.wZ(), tbar + mm_block(a, d.L, d.C), d.wZ(), E};
-      if ((r = run_tn(&seg, 1, rr, cc, gW2r + off, cc, 0, P, s))) return r;
+  for (long e0 = 0, c = 0; e0 < gd.E; e0 += ec, ++c) {
+    GraphDev gc = gd;
+    gc.e0 = e0;
+    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
+    const int n = (int)(gc.e1 - gc.e0);
+    const int acc = c > 0;
+    Primal pr;
+    if (recompute) {
+      if ((r = forward_chunk(d, n_rbf, gc, x, pos, rbf, w_rad, W1r, W2r, S, T, U, Z, V, s))) return r;
+      pr = {S, T, U, Z, V};
+    } else {
+      pr = {reinterpret_cast<const float*>(st + sl.S) + (size_t)e0 * wS,
+            reinterpret_cast<const float*>(st + sl.T) + (size_t)e0 * d.wT(),
+            reinterpret_cast<const float*>(st + sl.U) + (size_t)e0 * d.wU(),
+            reinterpret_cast<const float*>(st + sl.Z) + (size_t)e0 * d.wZ(),
+            reinterpret_cast<const float*>(st + sl.V) + (size_t)e0 * d.wZ()};
     }
-    SO2_HIP(launch_fold_grad(d, 1, gW2r, gw2, s));
-  }
-  SO2_HIP(launch_gate_bwd(d, E, U, Zbar, Ubar, s));
-  ps.clear();
-  lin1t_probs(d, Ubar, W1r, Tbar, E, 0, ps);
-  if ((r = run_batch(ps, false, true, s))) return r;
-  if (want_w1) {
-    for (int a = 0; a <= d.M; ++a) {
-      int rr, cc;
-      long off;
-      realified_shape(d, 0, a, &rr, &cc, &off);
-      TnSeg seg{T + mm_block(a, d.L, d.Ci()), d.wT(), Ubar + d.u_block(a), d.wU(), E};
-      if ((r = run_tn(&seg, 1, rr, cc, gW1r + off, cc, 0, P, s))) return r;
-    }
-    SO2_HIP(launch_fold_grad(d, 0, gW1r, gw1, s));
-  }
-  // N -> E transpose: gx (both halves), Sbar, position torques
-  SO2_HIP(launch_node_bwd(d, gd, x, pos, S, Tbar, gx, Sbar, tau2, tau3, s));
-  if (grbf) {
-    ps.clear();
-    ps.push_back(prob(Sbar, (d.L + 1) * d.Ci(), w_rad, (d.L + 1) * d.Ci(), grbf, n_rbf, E, n_rbf, (d.L + 1) * d.Ci()));
+    // E -> N transpose: tbar = R gy[dst], tau1 = rotation torque of <V, R gy>
+    SO2_HIP(launch_edge_bwd(d, gc, pos, gy, pr.V, tbar, tau1, s));
+    std::vector<GemmProb> ps;
+    lin2t_probs(d, tbar, W2r, Zbar, n, 0, ps);
     if ((r = run_batch(ps, false, true, s))) return r;
+    if (want_w2) {
+      for (int a = 0; a <= d.M; ++a) {
+        int rr, cc;
+        long off;
+        realified_shape(d, 1, a, &rr, &cc, &off);
+        TnSeg seg{pr.Z + mm_block(a, d.L, d.C), d.wZ(), tbar + mm_block(a, d.L, d.C), d.wZ(), n};
+        if ((r = run_tn(&seg, 1, rr, cc, gW2r + off, cc, acc, P, s))) return r;
+      }
+    }
+    SO2_HIP(launch_gate_bwd(d, n, pr.U, Zbar, Ubar, s));
+    ps.clear();
+    lin1t_probs(d, Ubar, W1r, Tbar, n, 0, ps);
+    if ((r = run_batch(ps, false, true, s))) return r;
+    if (want_w1) {
+      for (int a = 0; a <= d.M; ++a) {
+        int rr, cc;
+        long off;
+        realified_shape(d, 0, a, &rr, &cc, &off);
+        TnSeg seg{pr.T + mm_block(a, d.L, d.Ci()), d.wT(), Ubar + d.u_block(a), d.wU(), n};
+        if ((r = run_tn(&seg, 1, rr, cc, gW1r + off, cc, acc, P, s))) return r;
+      }
+    }
+    // N -> E transpose: gx (both halves), Sbar, position torques
+    SO2_HIP(launch_node_bwd(d, gc, x, pos, pr.S, Tbar, gx, Sbar, tau2, tau3, acc, s));
+    if (grbf) {
+      ps.clear();
+      ps.push_back(prob(Sbar, wS, w_rad, wS, grbf + (size_t)e0 * n_rbf, n_rbf, n, n_rbf, wS));
+      if ((r = run_batch(ps, false, true, s))) return r;
+    }
+    if (gw_rad) {
+      TnSeg seg{rbf + (size_t)e0 * n_rbf, n_rbf, Sbar, wS, n};
+      if ((r = run_tn(&seg, 1, n_rbf, wS, gw_rad, wS, acc, P, s))) return r;
+    }
+    if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, tau1, tau2, tau3, vbar, s));
   }
-  if (gw_rad) {
-    TnSeg seg{rbf, n_rbf, Sbar, (d.L + 1) * d.Ci(), E};
-    if ((r = run_tn(&seg, 1, n_rbf, (d.L + 1) * d.Ci(), gw_rad, (d.L + 1) * d.Ci(), 0, P, s))) return r;
-  }
-  if (gpos || gedge) {
-    SO2_HIP(launch_pos_grad(gd, pos, tau1, tau2, tau3, gedge ? gedge : vbar, gpos, s));
-  }
+  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, gW2r, gw2, s));
+  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, gW1r, gw1, s));
+  if (gpos) SO2_HIP(launch_node_pos(gd, vbar, gpos, s));
   return SO2_OK;
 }
 
@@ -619,10 +702,8 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x,
   if ((r = check_cfg(cfg, &d)) || (r = check_graph(g, &gd))) return r;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
-  if (!saved) return fail(SO2_EINVAL, "saved state from so2conv_fwd is required");
   if (gpos2) return fail(SO2_EUNSUPPORTED, "gpos2 (position second derivatives) is not provided; pass NULL");
   if ((r = ensure_init())) return r;
-  if (!ws || ws_bytes < ws_dbwd(d, cfg->n_rbf, gd.N, gd.E)) return fail(SO2_EWORKSPACE, "double-backward workspace too small");
   const bool has_pw1 = !all_null(pw1, d.M + 1), has_pw2 = !all_null(pw2, d.M + 1);
   if (has_pw1)
     for (int a = 0; a <= d.M; ++a)
@@ -630,145 +711,164 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x,
   if (has_pw2)
     for (int a = 0; a <= d.M; ++a)
       if (!pw2[a]) return fail(SO2_EINVAL, "pw2 must be NULL or hold M+1 non-NULL blocks");
-
   hipStream_t s = (hipStream_t)stream;
-  const int E = (int)gd.E, n_rbf = cfg->n_rbf, wS = (d.L + 1) * d.Ci();
+  const int n_rbf = cfg->n_rbf, wS = (d.L + 1) * d.Ci();
+  if (gd.E == 0) {
+    int rr = zero_grads(d, n_rbf, gd.N, gx2, nullptr, gw_rad2, gw1_2, gw2_2, s);
+    if (rr) return rr;
+    if (ggy) return fill(ggy, (size_t)gd.N * d.d() * d.C, s);
+    return SO2_OK;
+  }
+  const bool recompute = saved == nullptr;
+  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
+  const long ec = pick_chunk(d, n_rbf, gd.E, 2, recompute, ws_bytes);
+  if (ec == 0) return fail(SO2_EWORKSPACE, "double-backward workspace too small for a 1024-edge chunk");
   const SavedLayout sl = saved_layout(d, n_rbf, gd.E);
   const char* st = static_cast<const char*>(saved);
-  const float* S = reinterpret_cast<const float*>(st + sl.S);
-  const float* T = reinterpret_cast<const float*>(st + sl.T);
-  const float* U = reinterpret_cast<const float*>(st + sl.U);
-  const float* Z = reinterpret_cast<const float*>(st + sl.Z);
-  const float* V = reinterpret_cast<const float*>(st + sl.V);
   Arena ar{static_cast<char*>(ws), 0};
   float* W1r = ar.take(realified_size(d, 0));
   float* W2r = ar.take(realified_size(d, 1));
   float* pW1r = ar.take(realified_size(d, 0));
   float* pW2r = ar.take(realified_size(d, 1));
-  float* Sdot = ar.take((size_t)E * wS);
-  float* Tdot = ar.take((size_t)E * d.wT());
-  float* omega = ar.take((size_t)E * 3);
-  float* Udot = ar.take((size_t)E * d.wU());
-  float* Zdot = ar.take((size_t)E * d.wZ());
-  float* Vdot = ar.take((size_t)E * d.wZ());
-  float* G2 = ar.take((size_t)2 * E * d.wZ());
-  float* ZZ = ar.take((size_t)2 * E * d.wZ());
-  float* UU = ar.take((size_t)2 * E * d.wU());
-  float* TT = ar.take((size_t)2 * E * d.wT());
-  float* Sbar = ar.take((size_t)E * wS);
-  float* Sdb = ar.take((size_t)E * wS);
   float* gW1r = ar.take(realified_size(d, 0));
   float* gW2r = ar.take(realified_size(d, 1));
+  float *S = nullptr, *T = nullptr, *U = nullptr, *Z = nullptr, *V = nullptr;
+  if (recompute) {
+    S = ar.take((size_t)ec * wS);
+    T = ar.take((size_t)ec * d.wT());
+    U = ar.take((size_t)ec * d.wU());
+    Z = ar.take((size_t)ec * d.wZ());
+    V = ar.take((size_t)ec * d.wZ());
+  }
+  float* Sdot = ar.take((size_t)ec * wS);
+  float* Tdot = ar.take((size_t)ec * d.wT());
+  float* omega = ar.take((size_t)ec * 3);
+  float* Udot = ar.take((size_t)ec * d.wU());
+  float* Zdot = ar.take((size_t)ec * d.wZ());
+  float* Vdot = ar.take((size_t)ec * d.wZ());
+  float* G2 = ar.take((size_t)2 * ec * d.wZ());
+  float* ZZ = ar.take((size_t)2 * ec * d.wZ());
+  float* UU = ar.take((size_t)2 * ec * d.wU());
+  float* TT = ar.take((size_t)2 * ec * d.wT());
+  float* Sbar = ar.take((size_t)ec * wS);
+  float* Sdb = ar.take((size_t)ec * wS);
   float* P = ar.take(0);
   const bool want_w1 = !all_null(gw1_2, d.M + 1), want_w2 = !all_null(gw2_2, d.M + 1);
-  const size_t dC = (size_t)d.d() * d.C;
-
-  if (E == 0) {
-    if (ggy) { if ((r = fill(ggy, (size_t)gd.N * dC, s))) return r; }
-    if (gx2) { if ((r = fill(gx2, (size_t)gd.N * dC, s))) return r; }
-    if (gw_rad2) { if ((r = fill(gw_rad2, (size_t)n_rbf * wS, s))) return r; }
-    for (int a = 0; a <= d.M; ++a) {
-      int rr, cc;
-      long off;
-      realified_shape(d, 0, a, &rr, &cc, &off);
-      if (gw1_2 && gw1_2[a]) { if ((r = fill(gw1_2[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r; }
-      realified_shape(d, 1, a, &rr, &cc, &off);
-      if (gw2_2 && gw2_2[a]) { if ((r = fill(gw2_2[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r; }
-    }
-    return SO2_OK;
-  }
 
   SO2_HIP(launch_realify(d, 0, w1, W1r, s));
   SO2_HIP(launch_realify(d, 1, w2, W2r, s));
   if (has_pw1) SO2_HIP(launch_realify(d, 0, pw1, pW1r, s));
   if (has_pw2) SO2_HIP(launch_realify(d, 1, pw2, pW2r, s));
-
-  // ---- tangent (dual) forward along (px, ppos, pedge, prbf, pW)
-  if (prbf) {
-    if ((r = radial(d, n_rbf, E, prbf, w_rad, Sdot, s))) return r;
-  } else if ((r = fill(Sdot, (size_t)E * wS, s))) {
-    return r;
-  }
-  if (pw_rad) {
-    if ((r = radial(d, n_rbf, E, rbf, pw_rad, Sdot, s, 1))) return r;
-  }
-  SO2_HIP(launch_edge_dual(d, gd, x, px, pos, ppos, pedge, S, Sdot, Tdot, omega, s));
-  std::vector<GemmProb> ps;
-  lin1_probs(d, Tdot, W1r, Udot, E, 0, ps);
-  if ((r = run_batch(ps, false, false, s))) return r;
-  if (has_pw1) {
-    ps.clear();
-    lin1_probs(d, T, pW1r, Udot, E, 1, ps);
-    if ((r = run_batch(ps, false, false, s))) return r;
-  }
-  SO2_HIP(launch_gate_dual(d, E, U, Udot, Zdot, s));
-  ps.clear();
-  lin2_probs(d, Zdot, W2r, Vdot, E, 0, ps);
-  if ((r = run_batch(ps, false, false, s))) return r;
-  if (has_pw2) {
-    ps.clear();
-    lin2_probs(d, Z, pW2r, Vdot, E, 1, ps);
-    if ((r = run_batch(ps, false, false, s))) return r;
-  }
-  // dL/dgy = the forward's directional derivative (Eq.(5))
-  if (ggy) SO2_HIP(launch_node_dual(d, gd, pos, omega, V, Vdot, ggy, s));
-
-  // ---- reverse of the tangent output with cotangent gy
-  SO2_HIP(launch_edge_bwd_dual(d, gd, pos, omega, gy, G2, s));
-  ps.clear();
-  lin2t_probs(d, G2, W2r, ZZ, 2 * E, 0, ps);     // [Zdot_bar; Zbar]
-  if ((r = run_batch(ps, false, true, s))) return r;
-  if (has_pw2) {
-    ps.clear();
-    lin2t_probs(d, G2, pW2r, ZZ + (size_t)E * d.wZ(), E, 1, ps);   // Zbar += tbar pW2^T
-    if ((r = run_batch(ps, false, true, s))) return r;
-  }
-  if (want_w2) {
-    for (int a = 0; a <= d.M; ++a) {
-      int rr, cc;
-      long off;
-      realified_shape(d, 1, a, &rr, &cc, &off);
-      const int bo = mm_block(a, d.L, d.C);
-      TnSeg segs[2] = {{Zdot + bo, d.wZ(), G2 + bo, d.wZ(), E}, {Z + bo, d.wZ(), G2 + (size_t)E * d.wZ() + bo, d.wZ(), E}};
-      if ((r = run_tn(segs, 2, rr, cc, gW2r + off, cc, 0, P, s))) return r;
+  for (long e0 = 0, c = 0; e0 < gd.E; e0 += ec, ++c) {
+    GraphDev gc = gd;
+    gc.e0 = e0;
+    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
+    const int n = (int)(gc.e1 - gc.e0);
+    const int acc = c > 0;
+    const float* rbf_c = rbf + (size_t)e0 * n_rbf;
+    const float* prbf_c = prbf ? prbf + (size_t)e0 * n_rbf : nullptr;
+    Primal pr;
+    if (recompute) {
+      if ((r = forward_chunk(d, n_rbf, gc, x, pos, rbf, w_rad, W1r, W2r, S, T, U, Z, V, s))) return r;
+      pr = {S, T, U, Z, V};
+    } else {
+      pr = {reinterpret_cast<const float*>(st + sl.S) + (size_t)e0 * wS,
+            reinterpret_cast<const float*>(st + sl.T) + (size_t)e0 * d.wT(),
+            reinterpret_cast<const float*>(st + sl.U) + (size_t)e0 * d.wU(),
+            reinterpret_cast<const float*>(st + sl.Z) + (size_t)e0 * d.wZ(),
+            reinterpret_cast<const float*>(st + sl.V) + (size_t)e0 * d.wZ()};
     }
-    SO2_HIP(launch_fold_grad(d, 1, gW2r, gw2_2, s));
-  }
-  SO2_HIP(launch_gate_dbwd(d, E, U, Udot, ZZ, UU, s));   // [Udot_bar; Ubar]
-  ps.clear();
-  lin1t_probs(d, UU, W1r, TT, 2 * E, 0, ps);      // [Tdot_bar; Tbar]
-  if ((r = run_batch(ps, false, true, s))) return r;
-  if (has_pw1) {
-    ps.clear();
-    lin1t_probs(d, UU, pW1r, TT + (size_t)E * d.wT(), E, 1, ps);   // Tbar += Udot_bar pW1^T
-    if ((r = run_batch(ps, false, true, s))) return r;
-  }
-  if (want_w1) {
-    for (int a = 0; a <= d.M; ++a) {
-      int rr, cc;
-      long off;
-      realified_shape(d, 0, a, &rr, &cc, &off);
-      const int ao = mm_block(a, d.L, d.Ci()), uo = d.u_block(a);
-      TnSeg segs[2] = {{Tdot + ao, d.wT(), UU + uo, d.wU(), E}, {T + ao, d.wT(), UU + (size_t)E * d.wU() + uo, d.wU(), E}};
-      if ((r = run_tn(segs, 2, rr, cc, gW1r + off, cc, 0, P, s))) return r;
+
+    // ---- tangent (dual) forward along (px, ppos, pedge, prbf, pW)
+    if (prbf_c) {
+      if ((r = radial(d, n_rbf, n, prbf_c, w_rad, Sdot, s))) return r;
+    } else if ((r = fill(Sdot, (size_t)n * wS, s))) {
+      return r;
     }
-    SO2_HIP(launch_fold_grad(d, 0, gW1r, gw1_2, s));
-  }
-  SO2_HIP(launch_node_bwd_dual(d, gd, x, px, pos, omega, S, Sdot, TT, gx2, Sbar, Sdb, s));
-  if (grbf2) {
-    ps.clear();
-    ps.push_back(prob(Sbar, wS, w_rad, wS, grbf2, n_rbf, E, n_rbf, wS));
-    if ((r = run_batch(ps, false, true, s))) return r;
     if (pw_rad) {
+      if ((r = radial(d, n_rbf, n, rbf_c, pw_rad, Sdot, s, 1))) return r;
+    }
+    SO2_HIP(launch_edge_dual(d, gc, x, px, pos, ppos, pedge, pr.S, Sdot, Tdot, omega, s));
+    std::vector<GemmProb> ps;
+    lin1_probs(d, Tdot, W1r, Udot, n, 0, ps);
+    if ((r = run_batch(ps, false, false, s))) return r;
+    if (has_pw1) {
       ps.clear();
-      ps.push_back(prob(Sdb, wS, pw_rad, wS, grbf2, n_rbf, E, n_rbf, wS, 1));
+      lin1_probs(d, pr.T, pW1r, Udot, n, 1, ps);
+      if ((r = run_batch(ps, false, false, s))) return r;
+    }
+    SO2_HIP(launch_gate_dual(d, n, pr.U, Udot, Zdot, s));
+    ps.clear();
+    lin2_probs(d, Zdot, W2r, Vdot, n, 0, ps);
+    if ((r = run_batch(ps, false, false, s))) return r;
+    if (has_pw2) {
+      ps.clear();
+      lin2_probs(d, pr.Z, pW2r, Vdot, n, 1, ps);
+      if ((r = run_batch(ps, false, false, s))) return r;
+    }
+    // dL/dgy = the forward's directional derivative (Eq.(5))
+    if (ggy) SO2_HIP(launch_node_dual(d, gc, pos, omega, pr.V, Vdot, ggy, acc, s));
+
+    // ---- reverse of the tangent output with cotangent gy
+    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, omega, gy, G2, s));
+    ps.clear();
+    lin2t_probs(d, G2, W2r, ZZ, 2 * n, 0, ps);     // [Zdot_bar; Zbar]
+    if ((r = run_batch(ps, false, true, s))) return r;
+    if (has_pw2) {
+      ps.clear();
+      lin2t_probs(d, G2, pW2r, ZZ + (size_t)n * d.wZ(), n, 1, ps);   // Zbar += tbar pW2^T
       if ((r = run_batch(ps, false, true, s))) return r;
     }
+    if (want_w2) {
+      for (int a = 0; a <= d.M; ++a) {
+        int rr, cc;
+        long off;
+        realified_shape(d, 1, a, &rr, &cc, &off);
+        const int bo = mm_block(a, d.L, d.C);
+        TnSeg segs[2] = {{Zdot + bo, d.wZ(), G2 + bo, d.wZ(), n},
+                         {pr.Z + bo, d.wZ(), G2 + (size_t)n * d.wZ() + bo, d.wZ(), n}};
+        if ((r = run_tn(segs, 2, rr, cc, gW2r + off, cc, acc, P, s))) return r;
+      }
+    }
+    SO2_HIP(launch_gate_dbwd(d, n, pr.U, Udot, ZZ, UU, s));   // [Udot_bar; Ubar]
+    ps.clear();
+    lin1t_probs(d, UU, W1r, TT, 2 * n, 0, ps);      // [Tdot_bar; Tbar]
+    if ((r = run_batch(ps, false, true, s))) return r;
+    if (has_pw1) {
+      ps.clear();
+      lin1t_probs(d, UU, pW1r, TT + (size_t)n * d.wT(), n, 1, ps);   // Tbar += Udot_bar pW1^T
+      if ((r = run_batch(ps, false, true, s))) return r;
+    }
+    if (want_w1) {
+      for (int a = 0; a <= d.M; ++a) {
+        int rr, cc;
+        long off;
+        realified_shape(d, 0, a, &rr, &cc, &off);
+        const int ao = mm_block(a, d.L, d.Ci()), uo = d.u_block(a);
+        TnSeg segs[2] = {{Tdot + ao, d.wT(), UU + uo, d.wU(), n},
+                         {pr.T + ao, d.wT(), UU + (size_t)n * d.wU() + uo, d.wU(), n}};
+        if ((r = run_tn(segs, 2, rr, cc, gW1r + off, cc, acc, P, s))) return r;
+      }
+    }
+    SO2_HIP(launch_node_bwd_dual(d, gc, x, px, pos, omega, pr.S, Sdot, TT, gx2, Sbar, Sdb, acc, s));
+    if (grbf2) {
+      float* out = grbf2 + (size_t)e0 * n_rbf;
+      ps.clear();
+      ps.push_back(prob(Sbar, wS, w_rad, wS, out, n_rbf, n, n_rbf, wS));
+      if ((r = run_batch(ps, false, true, s))) return r;
+      if (pw_rad) {
+        ps.clear();
+        ps.push_back(prob(Sdb, wS, pw_rad, wS, out, n_rbf, n, n_rbf, wS, 1));
+        if ((r = run_batch(ps, false, true, s))) return r;
+      }
+    }
+    if (gw_rad2) {
+      TnSeg segs[2] = {{rbf_c, n_rbf, Sbar, wS, n}, {prbf_c, n_rbf, Sdb, wS, prbf_c ? n : 0}};
+      if ((r = run_tn(segs, 2, n_rbf, wS, gw_rad2, wS, acc, P, s))) return r;
+    }
   }
-  if (gw_rad2) {
-    TnSeg segs[2] = {{rbf, n_rbf, Sbar, wS, E}, {prbf, n_rbf, Sdb, wS, prbf ? E : 0}};
-    if ((r = run_tn(segs, 2, n_rbf, wS, gw_rad2, wS, 0, P, s))) return r;
-  }
+  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, gW2r, gw2_2, s));
+  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, gW1r, gw1_2, s));
   return SO2_OK;
 }
 

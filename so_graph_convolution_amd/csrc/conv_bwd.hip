@@ -49,8 +49,8 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   __shared__ float sRed[TE * 4 * 3];
   __shared__ int sDst[TE];
 
-  const long e0 = (long)blockIdx.x * TE;
-  const int ne = (int)min((long)TE, g.E - e0);
+  const long e0 = g.e0 + (long)blockIdx.x * TE;
+  const int ne = (int)min((long)TE, g.e1 - e0);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int i = g.dst[e];
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const bool act = c < C;
   for (int t = 0; t < ne; ++t) {
-    const long e = e0 + t;
+    const long e = e0 + t - g.e0;   // chunk-relative row
     float tk[3] = {0.f, 0.f, 0.f};
     if (act) {
       float gv[D];
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
     const int t = idx / 3, k = idx - t * 3;
     float s = 0.f;
     for (int w = 0; w < nw; ++w) s += sRed[(t * 4 + w) * 3 + k];
-    tau[(e0 + t) * 3 + k] = s;
+    tau[(e0 + t - g.e0) * 3 + k] = s;
   }
 }
 
@@ -119,8 +119,8 @@ struct EdgeBwd {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, float* tbar,
                  float* tau, hipStream_t s) {
     constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
-    const long nb = (g.E + TE - 1) / TE;
-    if (nb == 0) return hipSuccess;
+    const long nb = (g.e1 - g.e0 + TE - 1) / TE;
+    if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((edge_bwd_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V, tbar, tau);
     return hipGetLastError();
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const
                                                        const float* __restrict__ pos, const float* __restrict__ S,
                                                        const float* __restrict__ Tbar, float* __restrict__ gx,
                                                        float* __restrict__ Sbar, float* __restrict__ tau_dst,
-                                                       float* __restrict__ tau_src) {
+                                                       float* __restrict__ tau_src, int accumulate) {
   constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
   __shared__ float sD1[TE * 9];
@@ -197,14 +197,15 @@ __global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const
   for (int pass = 0; pass < 2; ++pass) {
     // pass 0: incoming edges (this node is the receiver, target half of the input)
     // pass 1: outgoing edges via the source permutation (source half)
-    const int beg = pass == 0 ? g.dst_ptr[node] : g.src_ptr[node];
-    const int end = pass == 0 ? g.dst_ptr[node + 1] : g.src_ptr[node + 1];
+    int beg, end;
+    if (pass == 0) in_range(g, node, &beg, &end);
+    else out_range(g, node, &beg, &end);
     float* tau_out = pass == 0 ? tau_dst : tau_src;
     for (int t0 = beg; t0 < end; t0 += TE) {
       const int ne = min(TE, end - t0);
       for (int t = threadIdx.x; t < ne; t += blockDim.x) {
         const long e = pass == 0 ? (long)(t0 + t) : (long)g.src_perm[t0 + t];
-        sE[t] = (int)e;
+        sE[t] = (int)(e - g.e0);   // chunk-relative row
         const int j = pass == 0 ? g.src[e] : node;
         const int i = pass == 0 ? node : g.dst[e];
         edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
@@ -237,18 +238,22 @@ __global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const
   }
   if (gx && act) {
 #pragma unroll
-    for (int r = 0; r < D; ++r) gx[((size_t)node * D + r) * C + c] = acc[r];
+    for (int r = 0; r < D; ++r) {
+      float* o = gx + ((size_t)node * D + r) * C + c;
+      *o = accumulate ? *o + acc[r] : acc[r];
+    }
   }
 }
 
 template <int L, int M>
 struct NodeBwd {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
-                 const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, hipStream_t s) {
+                 const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, int accumulate,
+                 hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((node_bwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, pos, S, Tbar, gx, Sbar,
-                       tau_dst, tau_src);
+                       tau_dst, tau_src, accumulate);
     return hipGetLastError();
   }
 };
@@ -287,7 +292,8 @@ __global__ void gate_bwd_kernel(Dims d, long E, const float* __restrict__ U, con
 // ------------------------------------------------------------------ position gradient
 __global__ void vbar_kernel(GraphDev g, const float* __restrict__ pos, const float* __restrict__ t1,
                             const float* __restrict__ t2, const float* __restrict__ t3, float* __restrict__ vbar) {
-  for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.E; e += (long)gridDim.x * blockDim.x) {
+  for (long e = g.e0 + (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.e1; e += (long)gridDim.x * blockDim.x) {
+    const long le = e - g.e0;
     const int j = g.src[e], i = g.dst[e];
     float vx = pos[3 * j] - pos[3 * i], vy = pos[3 * j + 1] - pos[3 * i + 1], vz = pos[3 * j + 2] - pos[3 * i + 2];
     if (g.shift) {
@@ -297,9 +303,9 @@ __global__ void vbar_kernel(GraphDev g, const float* __restrict__ pos, const flo
     }
     const float rho = sqrtf(vx * vx + vy * vy + vz * vz), inv = 1.f / rho;
     const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
-    const float tx = t1[3 * e] + t2[3 * e] + t3[3 * e];
-    const float ty = t1[3 * e + 1] + t2[3 * e + 1] + t3[3 * e + 1];
-    const float tz = t1[3 * e + 2] + t2[3 * e + 2] + t3[3 * e + 2];
+    const float tx = t1[3 * le] + t2[3 * le] + t3[3 * le];
+    const float ty = t1[3 * le + 1] + t2[3 * le + 1] + t3[3 * le + 1];
+    const float tz = t1[3 * le + 2] + t2[3 * le + 2] + t3[3 * le + 2];
     vbar[3 * e] = (ry * tz - rz * ty) * inv;
     vbar[3 * e + 1] = (rz * tx - rx * tz) * inv;
     vbar[3 * e + 2] = (rx * ty - ry * tx) * inv;
@@ -348,22 +354,23 @@ int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, fl
 }
 
 int launch_node_bwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
-                    const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, hipStream_t s) {
-  return dispatch_lm<NodeBwd>(d.L, d.M, d, g, x, pos, S, Tbar, gx, Sbar, tau_dst, tau_src, s);
+                    const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, int accumulate,
+                    hipStream_t s) {
+  return dispatch_lm<NodeBwd>(d.L, d.M, d, g, x, pos, S, Tbar, gx, Sbar, tau_dst, tau_src, accumulate, s);
 }
 
-int launch_pos_grad(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
-                    float* vbar, float* gpos, hipStream_t s) {
-  if (g.E > 0) {
-    hipLaunchKernelGGL(vbar_kernel, dim3(grid_for(g.E)), dim3(256), 0, s, g, pos, tau1, tau2, tau3, vbar);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (gpos && g.N > 0) {
-    hipLaunchKernelGGL(node_pos_kernel, dim3(grid_for(g.N)), dim3(256), 0, s, g, vbar, gpos);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+int launch_vbar(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
+                float* vbar, hipStream_t s) {
+  const long n = g.e1 - g.e0;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(vbar_kernel, dim3(grid_for(n)), dim3(256), 0, s, g, pos, tau1, tau2, tau3, vbar);
+  return hipGetLastError();
+}
+
+int launch_node_pos(const GraphDev& g, const float* vbar, float* gpos, hipStream_t s) {
+  if (g.N == 0) return hipSuccess;
+  hipLaunchKernelGGL(node_pos_kernel, dim3(grid_for(g.N)), dim3(256), 0, s, g, vbar, gpos);
+  return hipGetLastError();
 }
 
 }  // namespace so2

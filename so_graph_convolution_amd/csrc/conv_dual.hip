@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
   __shared__ float sW[TE * 3];
   __shared__ int sNode[2][TE];
 
-  const long e0 = (long)blockIdx.x * TE;
-  const int ne = (int)min((long)TE, g.E - e0);
+  const long e0 = g.e0 + (long)blockIdx.x * TE;
+  const int ne = (int)min((long)TE, g.e1 - e0);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int j = g.src[e], i = g.dst[e];
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
     frame_rate(gg, dx, dy, dz, w);
     for (int k = 0; k < 3; ++k) {
       sW[t * 3 + k] = w[k];
-      omega[e * 3 + k] = w[k];
+      omega[(e - g.e0) * 3 + k] = w[k];
     }
   }
   __syncthreads();
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
   for (int c = threadIdx.x; c < Ci; c += blockDim.x) {
     const int half = c >= C, cc = c - half * C;
     for (int t = 0; t < ne; ++t) {
-      const long e = e0 + t;
+      const long e = e0 + t - g.e0;   // chunk-relative row
       const size_t nb = (size_t)sNode[half][t] * D * C + cc;
       float a[D], ad[D];
 #pragma unroll
@@ -133,8 +133,8 @@ struct EdgeDual {
                  const float* ppos, const float* pedge, const float* S, const float* Sdot, float* Tdot, float* omega,
                  hipStream_t s) {
     constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
-    const long nb = (g.E + TE - 1) / TE;
-    if (nb == 0) return hipSuccess;
+    const long nb = (g.e1 - g.e0 + TE - 1) / TE;
+    if (nb <= 0) return hipSuccess;
     const int threads = min(256, ((2 * d.C + 63) / 64) * 64);
     hipLaunchKernelGGL((edge_dual_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, x, px, pos, ppos, pedge, S,
                        Sdot, Tdot, omega);
@@ -146,7 +146,8 @@ struct EdgeDual {
 template <int L, int M>
 __global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                         const float* __restrict__ omega, const float* __restrict__ V,
-                                                        const float* __restrict__ Vdot, float* __restrict__ ydot) {
+                                                        const float* __restrict__ Vdot, float* __restrict__ ydot,
+                                                        int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
   __shared__ float sD1[TE * 9];
@@ -156,7 +157,9 @@ __global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, cons
   __shared__ float sW[TE * 3];
 
   const int node = blockIdx.x;
-  const int beg = g.dst_ptr[node], end = g.dst_ptr[node + 1];
+  int beg, end;
+  in_range(g, node, &beg, &end);
+  if (accumulate && beg == end) return;
   const int C = d.C, wZ = d.wZ();
   const int c = threadIdx.x;
   float acc[D];
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, cons
     for (int t = threadIdx.x; t < ne; t += blockDim.x) {
       const long e = t0 + t;
       edge_geometry(pos, g.shift, g.src[e], node, e, sD1 + 9 * t);
-      for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[e * 3 + k];
+      for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[(e - g.e0) * 3 + k];
     }
     __syncthreads();
     wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
@@ -175,8 +178,8 @@ __global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, cons
     __syncthreads();
     if (c < C) {
       for (int t = 0; t < ne; ++t) {
-        const float* vr = V + (size_t)(t0 + t) * wZ + c;
-        const float* vd = Vdot + (size_t)(t0 + t) * wZ + c;
+        const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
+        const float* vd = Vdot + (size_t)(t0 + t - g.e0) * wZ + c;
         float tv[Q], tdv[Q];
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
@@ -196,16 +199,17 @@ __global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, cons
   if (c < C) {
     float* yr = ydot + (size_t)node * D * C + c;
 #pragma unroll
-    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = acc[r];
+    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = accumulate ? yr[(size_t)r * C] + acc[r] : acc[r];
   }
 }
 
 template <int L, int M>
 struct NodeDual {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
-                 const float* Vdot, float* ydot, hipStream_t s) {
+                 const float* Vdot, float* ydot, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((node_dual_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, omega, V, Vdot, ydot);
+    hipLaunchKernelGGL((node_dual_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, omega, V, Vdot, ydot,
+                       accumulate);
     return hipGetLastError();
   }
 };
@@ -224,14 +228,14 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   __shared__ float sW[TE * 3];
   __shared__ int sDst[TE];
 
-  const long e0 = (long)blockIdx.x * TE;
-  const int ne = (int)min((long)TE, g.E - e0);
+  const long e0 = g.e0 + (long)blockIdx.x * TE;
+  const int ne = (int)min((long)TE, g.e1 - e0);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int i = g.dst[e];
     sDst[t] = i;
     edge_geometry(pos, g.shift, g.src[e], i, e, sD1 + 9 * t);
-    for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[e * 3 + k];
+    for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[(e - g.e0) * 3 + k];
   }
   __syncthreads();
   wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   const int C = d.C, wZ = d.wZ();
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     for (int t = 0; t < ne; ++t) {
-      const long e = e0 + t;
+      const long e = e0 + t - g.e0;   // chunk-relative row
       float gv[D];
       const float* gr = gy + (size_t)sDst[t] * D * C + c;
 #pragma unroll
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
       rot_fwd<L, M>(sR + t * K, gv, o1);
       rot_fwd<L, M>(sRd + t * K, gv, o2);
       float* r1 = G2 + (size_t)e * wZ + c;
-      float* r2 = G2 + ((size_t)g.E + e) * wZ + c;
+      float* r2 = G2 + ((size_t)(g.e1 - g.e0) + e) * wZ + c;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const int q = qhalf(l, M);
@@ -268,8 +272,8 @@ struct EdgeBwdDual {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, float* G2,
                  hipStream_t s) {
     constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
-    const long nb = (g.E + TE - 1) / TE;
-    if (nb == 0) return hipSuccess;
+    const long nb = (g.e1 - g.e0 + TE - 1) / TE;
+    if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy, G2);
     return hipGetLastError();
@@ -285,7 +289,8 @@ __global__ __launch_bounds__(256) void node_bwd_dual_kernel(Dims d, GraphDev g, 
                                                             const float* __restrict__ S,
                                                             const float* __restrict__ Sdot,
                                                             const float* __restrict__ TT, float* __restrict__ gx2,
-                                                            float* __restrict__ Sbar, float* __restrict__ Sdb) {
+                                                            float* __restrict__ Sbar, float* __restrict__ Sdb,
+                                                            int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
   __shared__ float sD1[TE * 9];
@@ -308,19 +313,20 @@ __global__ __launch_bounds__(256) void node_bwd_dual_kernel(Dims d, GraphDev g, 
     acc[r] = 0.f;
   }
   const float* Tdb = TT;
-  const float* Tb = TT + (size_t)g.E * wT;
+  const float* Tb = TT + (size_t)(g.e1 - g.e0) * wT;
   for (int pass = 0; pass < 2; ++pass) {
-    const int beg = pass == 0 ? g.dst_ptr[node] : g.src_ptr[node];
-    const int end = pass == 0 ? g.dst_ptr[node + 1] : g.src_ptr[node + 1];
+    int beg, end;
+    if (pass == 0) in_range(g, node, &beg, &end);
+    else out_range(g, node, &beg, &end);
     for (int t0 = beg; t0 < end; t0 += TE) {
       const int ne = min(TE, end - t0);
       for (int t = threadIdx.x; t < ne; t += blockDim.x) {
         const long e = pass == 0 ? (long)(t0 + t) : (long)g.src_perm[t0 + t];
-        sE[t] = (int)e;
+        sE[t] = (int)(e - g.e0);   // chunk-relative row
         const int j = pass == 0 ? g.src[e] : node;
         const int i = pass == 0 ? node : g.dst[e];
         edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
-        for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[e * 3 + k];
+        for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[(e - g.e0) * 3 + k];
       }
       __syncthreads();
       wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
@@ -368,7 +374,10 @@ __global__ __launch_bounds__(256) void node_bwd_dual_kernel(Dims d, GraphDev g, 
   }
   if (gx2 && act) {
 #pragma unroll
-    for (int r = 0; r < D; ++r) gx2[((size_t)node * D + r) * C + c] = acc[r];
+    for (int r = 0; r < D; ++r) {
+      float* o = gx2 + ((size_t)node * D + r) * C + c;
+      *o = accumulate ? *o + acc[r] : acc[r];
+    }
   }
 }
 
@@ -376,11 +385,11 @@ template <int L, int M>
 struct NodeBwdDual {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
                  const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2, float* Sbar,
-                 float* Sdb, hipStream_t s) {
+                 float* Sdb, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((node_bwd_dual_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega, S, Sdot,
-                       TT, gx2, Sbar, Sdb);
+                       TT, gx2, Sbar, Sdb, accumulate);
     return hipGetLastError();
   }
 };
@@ -477,8 +486,8 @@ int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, f
 }
 
 int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
-                     const float* Vdot, float* ydot, hipStream_t s) {
-  return dispatch_lm<NodeDual>(d.L, d.M, d, g, pos, omega, V, Vdot, ydot, s);
+                     const float* Vdot, float* ydot, int accumulate, hipStream_t s) {
+  return dispatch_lm<NodeDual>(d.L, d.M, d, g, pos, omega, V, Vdot, ydot, accumulate, s);
 }
 
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
@@ -496,8 +505,8 @@ int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, c
 
 int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
                          const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
-                         float* Sbar, float* Sdot_bar, hipStream_t s) {
-  return dispatch_lm<NodeBwdDual>(d.L, d.M, d, g, x, px, pos, omega, S, Sdot, TT, gx2, Sbar, Sdot_bar, s);
+                         float* Sbar, float* Sdot_bar, int accumulate, hipStream_t s) {
+  return dispatch_lm<NodeBwdDual>(d.L, d.M, d, g, x, px, pos, omega, S, Sdot, TT, gx2, Sbar, Sdot_bar, accumulate, s);
 }
 
 }  // namespace so2

@@ -34,8 +34,8 @@ __global__ __launch_bounds__(256) void edge_fwd_kernel(Dims d, GraphDev g, const
   __shared__ float sA[kTileE * ST], sB[kTileE * ST];
   __shared__ int sNode[2][kTileE];
 
-  const long e0 = (long)blockIdx.x * kTileE;
-  const int ne = (int)min((long)kTileE, g.E - e0);
+  const long e0 = g.e0 + (long)blockIdx.x * kTileE;
+  const int ne = (int)min((long)kTileE, g.e1 - e0);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int j = g.src[e], i = g.dst[e];
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void edge_fwd_kernel(Dims d, GraphDev g, const
   for (int c = threadIdx.x; c < Ci; c += blockDim.x) {
     const int half = c >= C, cc = c - half * C;
     for (int t = 0; t < ne; ++t) {
-      const long e = e0 + t;
+      const long e = e0 + t - g.e0;   // chunk-relative row
       const float* xr = x + (size_t)sNode[half][t] * D * C + cc;
       float a[D];
 #pragma unroll
@@ -75,8 +75,8 @@ template <int L, int M>
 struct EdgeFwd {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, float* T,
                  hipStream_t s) {
-    const long nb = (g.E + kTileE - 1) / kTileE;
-    if (nb == 0) return hipSuccess;
+    const long nb = (g.e1 - g.e0 + kTileE - 1) / kTileE;
+    if (nb <= 0) return hipSuccess;
     const int threads = min(256, ((2 * d.C + 63) / 64) * 64);
     hipLaunchKernelGGL((edge_fwd_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, x, pos, S, T);
     return hipGetLastError();
@@ -86,14 +86,17 @@ struct EdgeFwd {
 // ------------------------------------------------------------------ node_fwd
 template <int L, int M>
 __global__ __launch_bounds__(256) void node_fwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
-                                                       const float* __restrict__ V, float* __restrict__ y) {
+                                                       const float* __restrict__ V, float* __restrict__ y,
+                                                       int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   __shared__ float sD1[kTileE * 9];
   __shared__ float sR[kTileE * K];
   __shared__ float sA[kTileE * ST], sB[kTileE * ST];
 
   const int node = blockIdx.x;
-  const int beg = g.dst_ptr[node], end = g.dst_ptr[node + 1];
+  int beg, end;
+  in_range(g, node, &beg, &end);
+  if (accumulate && beg == end) return;
   const int C = d.C, wZ = d.wZ();
   const int c = threadIdx.x;          // one channel per thread (blockDim == C)
   float acc[D];
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(256) void node_fwd_kernel(Dims d, GraphDev g, const
     wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
     if (c < C) {
       for (int t = 0; t < ne; ++t) {
-        const float* vr = V + (size_t)(t0 + t) * wZ + c;
+        const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
         float tv[Q];
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
@@ -126,15 +129,16 @@ __global__ __launch_bounds__(256) void node_fwd_kernel(Dims d, GraphDev g, const
   if (c < C) {
     float* yr = y + (size_t)node * D * C + c;
 #pragma unroll
-    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = acc[r];
+    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = accumulate ? yr[(size_t)r * C] + acc[r] : acc[r];
   }
 }
 
 template <int L, int M>
 struct NodeFwd {
-  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, hipStream_t s) {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
+                 hipStream_t s) {
     if (g.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((node_fwd_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, V, y);
+    hipLaunchKernelGGL((node_fwd_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, V, y, accumulate);
     return hipGetLastError();
   }
 };
@@ -203,8 +207,9 @@ int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const floa
   return dispatch_lm<EdgeFwd>(d.L, d.M, d, g, x, pos, S, T, s);
 }
 
-int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, hipStream_t s) {
-  return dispatch_lm<NodeFwd>(d.L, d.M, d, g, pos, V, y, s);
+int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
+                    hipStream_t s) {
+  return dispatch_lm<NodeFwd>(d.L, d.M, d, g, pos, V, y, accumulate, s);
 }
 
 int launch_gate_fwd(const Dims& d, long E, const float* U, float* Z, hipStream_t s) {

@@ -14,6 +14,7 @@ struct GraphDev {
   const int* dst_ptr;     // [N+1] incoming-edge ranges (edges sorted by dst)
   const int* src_perm;    // [E] edge ids ordered by (src, edge id)
   const int* src_ptr;     // [N+1] ranges into src_perm
+  long e0, e1;            // edge chunk [e0, e1): per-edge buffers are indexed by e - e0
 };
 
 // (lmax, mmax) pairs with compiled kernels
@@ -28,8 +29,9 @@ int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const floa
                      hipStream_t s);
 // Z = gate(U)
 int launch_gate_fwd(const Dims& d, long E, const float* U, float* Z, hipStream_t s);
-// y[i] = sum_{e -> i} R_e^T V[e]
-int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, hipStream_t s);
+// y[i] (+)= sum_{e -> i, e in chunk} R_e^T V[e]
+int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
+                    hipStream_t s);
 
 // ---- backward
 // tbar[e] = R_e gy[dst]; tau[e] = torque of <V, R gy> (for the position gradient)
@@ -39,10 +41,13 @@ int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const fl
 int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, float* Ubar, hipStream_t s);
 // gx[n] (both halves), Sbar[e], tau_dst[e], tau_src[e]
 int launch_node_bwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
-                    const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, hipStream_t s);
-// vbar[e] = rhat x (tau1 + tau2 + tau3) / rho; gpos[n] = sum_out vbar - sum_in vbar
-int launch_pos_grad(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
-                    float* vbar, float* gpos, hipStream_t s);
+                    const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, int accumulate,
+                    hipStream_t s);
+// vbar[e] = rhat x (tau1 + tau2 + tau3) / rho for the chunk's edges (vbar indexed globally)
+int launch_vbar(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
+                float* vbar, hipStream_t s);
+// gpos[n] = sum_out vbar - sum_in vbar over every edge
+int launch_node_pos(const GraphDev& g, const float* vbar, float* gpos, hipStream_t s);
 
 // ---- double backward (force-training pattern and general directions)
 // Tdot = Sdot*(R a) + S*(Rdot a + R adot), Rdot from the position direction; also writes the
@@ -53,7 +58,7 @@ int launch_edge_dual(const Dims& d, const GraphDev& g, const float* x, const flo
 int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, float* Zdot, hipStream_t s);
 // ydot[i] = sum_e Rdot^T V + R^T Vdot
 int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
-                     const float* Vdot, float* ydot, hipStream_t s);
+                     const float* Vdot, float* ydot, int accumulate, hipStream_t s);
 // G2 rows [0,E) = R gy[dst], rows [E,2E) = Rdot gy[dst]
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
                          float* G2, hipStream_t s);
@@ -63,7 +68,7 @@ int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, c
 // gx2 and (Sbar, Sdot_bar) from TT = [Tdot_bar; Tbar]
 int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
                          const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
-                         float* Sbar, float* Sdot_bar, hipStream_t s);
+                         float* Sbar, float* Sdot_bar, int accumulate, hipStream_t s);
 
 // ---- weights
 // Wr (realified per order): block 0 = W[0]; block m = [[W_m0, W_m1], [-W_m1, W_m0]]

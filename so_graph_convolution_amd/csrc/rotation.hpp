@@ -2,6 +2,7 @@
 // derivatives) built in LDS, and per-channel rotation products kept in
 // registers. Used by every edge- and node-centric kernel.
 #pragma once
+#include "ops.hpp"
 #include "wigner.hpp"
 
 namespace so2 {
@@ -131,6 +132,41 @@ __device__ __forceinline__ void rot_bwd_acc(const float* __restrict__ R, const f
       for (int k = 0; k < n; ++k) o[l * l + k] += R[rot_off(l, M) + (m + q) * n + k] * tv;
     }
   }
+}
+
+// Incoming-edge range of `node` clipped to the edge chunk [e0, e1).
+__device__ inline void in_range(const GraphDev& g, int node, int* beg, int* end) {
+  long b = g.dst_ptr[node], e = g.dst_ptr[node + 1];
+  if (b < g.e0) b = g.e0;
+  if (e > g.e1) e = g.e1;
+  *beg = (int)b;
+  *end = (int)(e > b ? e : b);
+}
+
+// Positions [beg, end) in src_perm of the outgoing edges of `node` that lie in
+// the chunk: within a sender's segment the edge ids increase (stable sort), so
+// both ends are found by binary search.
+__device__ inline void out_range(const GraphDev& g, int node, int* beg, int* end) {
+  int b = g.src_ptr[node], e = g.src_ptr[node + 1];
+  if (g.e0 > 0 || g.e1 < g.E) {
+    int lo = b, hi = e;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (g.src_perm[mid] < g.e0) lo = mid + 1;
+      else hi = mid;
+    }
+    const int nb = lo;
+    hi = e;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (g.src_perm[mid] < g.e1) lo = mid + 1;
+      else hi = mid;
+    }
+    b = nb;
+    e = lo;
+  }
+  *beg = b;
+  *end = e;
 }
 
 // sum over a wavefront (64 lanes)

@@ -15,7 +15,8 @@ from ._binding import Cfg, GraphC, check, lib
 
 __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_bwd", "so2conv_dbwd",
            "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes", "weight_shapes",
-           "so2conv_profile_enable", "so2conv_profile_reset", "so2conv_profile_read"]
+           "so2conv_profile_enable", "so2conv_profile_reset", "so2conv_profile_read",
+           "so2conv_chunked_workspace_bytes"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -123,6 +124,29 @@ def so2conv_saved_bytes(cfg: SO2Config, n_edges) -> int:
     return int(lib().so2conv_saved_bytes(ctypes.byref(c), n_edges))
 
 
+def so2conv_chunked_workspace_bytes(cfg: SO2Config, n_nodes, n_edges, stage, chunk_edges) -> int:
+    c = cfg.c()
+    return int(lib().so2conv_chunked_workspace_bytes(ctypes.byref(c), n_nodes, n_edges, stage, chunk_edges))
+
+
+def _ws_for(cfg, g, stage, saved, ws, chunk_edges, device):
+    """Workspace of one stage: one chunk over all edges unless chunk_edges is given;
+    with saved=None the forward state is recomputed inside the workspace."""
+    if ws is not None:
+        return ws
+    if saved is None or chunk_edges is not None:
+        ce = g.n_edges if chunk_edges is None else int(chunk_edges)
+        if saved is None:
+            nb = so2conv_chunked_workspace_bytes(cfg, g.n_nodes, g.n_edges, stage, max(1, ce))
+        else:   # saved state given, chunked workspace for the remaining per-edge buffers
+            nb = so2conv_chunked_workspace_bytes(cfg, g.n_nodes, g.n_edges, stage, max(1, ce)) - \
+                so2conv_chunked_workspace_bytes(cfg, g.n_nodes, g.n_edges, 0, max(1, ce)) + \
+                so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, 0)
+    else:
+        nb = so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, stage)
+    return _ws(nb, device)
+
+
 def _common(cfg, g, x, pos, rbf, w_rad):
     N, E, d, C = g.n_nodes, g.n_edges, cfg.d, cfg.channels
     _dev(x, "x", shape=(N, d, C))
@@ -131,8 +155,9 @@ def _common(cfg, g, x, pos, rbf, w_rad):
     _dev(w_rad, "w_rad", shape=(cfg.n_rbf, (cfg.lmax + 1) * 2 * C))
 
 
-def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None, ws=None):
-    """Returns (y, saved). `saved=True` allocates the state for bwd/dbwd."""
+def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None, ws=None, chunk_edges=None):
+    """Returns (y, saved). `saved=True` allocates the state for bwd/dbwd; with
+    saved=None the state is not kept (chunks of chunk_edges edges)."""
     _common(cfg, g, x, pos, rbf, w_rad)
     s1, s2 = weight_shapes(cfg)
     p1, k1 = _ptr_array(w1, "w1", s1)
@@ -140,11 +165,7 @@ def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None
     y = torch.empty_like(x)
     if saved is True:
         saved = _ws(so2conv_saved_bytes(cfg, g.n_edges), x.device)
-    need = so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, 0)
-    if saved is None:
-        need += so2conv_saved_bytes(cfg, g.n_edges)
-    if ws is None or ws.numel() < need:
-        ws = _ws(need, x.device)
+    ws = _ws_for(cfg, g, 0, saved, ws, chunk_edges, x.device)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_fwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2, _p(y),
                             _p(saved), _p(ws), ws.numel(), _stream()), "so2conv_fwd")
@@ -154,8 +175,10 @@ def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None
 GRAD_KEYS = ("x", "pos", "rbf", "w_rad", "w1", "w2", "edge")
 
 
-def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, need=GRAD_KEYS, ws=None):
-    """Returns dict gx, gpos, grbf, gw_rad, gw1, gw2, gedge (requested ones)."""
+def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, need=GRAD_KEYS, ws=None,
+                chunk_edges=None):
+    """Returns dict gx, gpos, grbf, gw_rad, gw1, gw2, gedge (requested ones).
+    saved=None recomputes the forward state chunk by chunk."""
     _common(cfg, g, x, pos, rbf, w_rad)
     _dev(gy, "gy", shape=x.shape)
     s1, s2 = weight_shapes(cfg)
@@ -172,9 +195,7 @@ def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy,
     out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
     q1, k3 = _ptr_array(out["gw1"], "gw1", s1)
     q2, k4 = _ptr_array(out["gw2"], "gw2", s2)
-    nb = so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, 1)
-    if ws is None or ws.numel() < nb:
-        ws = _ws(nb, dev)
+    ws = _ws_for(cfg, g, 1, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_bwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
                             _p(saved), _p(gy), _p(out["gx"]), _p(out["gpos"]), _p(out["grbf"]), _p(out["gw_rad"]),
@@ -186,7 +207,7 @@ DBWD_KEYS = ("gy", "x", "rbf", "w_rad", "w1", "w2")
 
 
 def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, px=None, ppos=None, pedge=None,
-                 prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None):
+                 prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None, chunk_edges=None):
     """Returns dict ggy, gx2, grbf2, gw_rad2, gw1_2, gw2_2 (requested ones)."""
     _common(cfg, g, x, pos, rbf, w_rad)
     _dev(gy, "gy", shape=x.shape)
@@ -210,9 +231,7 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     out["gw2_2"] = [torch.empty(s, device=dev) for s in s2] if "w2" in need else None
     q1, k3 = _ptr_array(out["gw1_2"], "gw1_2", s1)
     q2, k4 = _ptr_array(out["gw2_2"], "gw2_2", s2)
-    nb = so2conv_workspace_bytes(cfg, g.n_nodes, g.n_edges, 2)
-    if ws is None or ws.numel() < nb:
-        ws = _ws(nb, dev)
+    ws = _ws_for(cfg, g, 2, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
                              _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf), _p(pw_rad), pp1, pp2,
