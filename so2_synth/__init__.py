@@ -234,7 +234,7 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     return r.astype(np.uint32).view(np.float32)
 
 
-def make_inputs(cfg: Config, with_directions: bool = True):
+def make_inputs(cfg: Config, with_directions=True):
     """Draw every input of one workload. Draw order: positions (and cluster
     centres), x, W_rad, W1[0..M], W2[0..M], gy, px, ppos, prbf.
 
@@ -259,12 +259,18 @@ def make_inputs(cfg: Config, with_directions: bool = True):
     out = dict(cfg=cfg, pos=pos, src=src, dst=dst, shift=shift, rbf=rbf, x=x,
                w_rad=w_rad.astype(np.float32),
                w1=[w.astype(np.float32) for w in w1], w2=[w.astype(np.float32) for w in w2])
+    # with_directions: True (all), False (none) or a tuple naming a prefix of
+    # ("gy", "px", "ppos", "prbf"); draws stop after the last one requested, so a
+    # prefix draws exactly the same values as the full set.
     if with_directions:
         E = len(src)
-        out["gy"] = rng.normal(size=(cfg.n_atoms, d, C)).astype(np.float32)
-        out["px"] = rng.normal(size=(cfg.n_atoms, d, C)).astype(np.float32)
-        out["ppos"] = rng.normal(size=(cfg.n_atoms, 3)).astype(np.float32)
-        out["prbf"] = rng.normal(size=(E, cfg.n_rbf)).astype(np.float32)
+        names = ("gy", "px", "ppos", "prbf")
+        want = names if with_directions is True else tuple(with_directions)
+        last = max(names.index(k) for k in want)
+        shapes = {"gy": (cfg.n_atoms, d, C), "px": (cfg.n_atoms, d, C), "ppos": (cfg.n_atoms, 3),
+                  "prbf": (E, cfg.n_rbf)}
+        for k in names[:last + 1]:
+            out[k] = rng.normal(size=shapes[k]).astype(np.float32)
     if cfg.dtype == "bf16":
         for k in ("x", "gy", "px", "w_rad"):
             if k in out:

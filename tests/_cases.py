@@ -69,3 +69,34 @@ def m_major(T_by_l, L, M, W):
         cols.append(torch.cat([T_by_l[l][:, l + m, :] for l in range(m, L + 1)]
                               + [T_by_l[l][:, l - m, :] for l in range(m, L + 1)], -1))
     return torch.cat(cols, -1) if E else torch.zeros(0, sum(c.shape[1] for c in cols))
+
+
+def subgraph(d, edges):
+    """Inputs restricted to the given edges and the nodes they touch (renumbered).
+    Returns (sub_inputs, nodes) with nodes[k] = original id of sub-node k. Node
+    outputs of nodes whose incident edges are all included, and per-edge outputs,
+    equal those of the full problem."""
+    edges = np.asarray(edges)
+    src, dst = d["src"][edges], d["dst"][edges]
+    nodes = np.unique(np.concatenate([src, dst]))
+    remap = {int(n): k for k, n in enumerate(nodes)}
+    sub = dict(d)
+    sub["src"] = np.array([remap[int(v)] for v in src], dtype=np.int32)
+    sub["dst"] = np.array([remap[int(v)] for v in dst], dtype=np.int32)
+    for k in ("shift", "rbf", "prbf"):
+        if k in d:
+            sub[k] = d[k][edges]
+    for k in ("x", "pos", "gy", "px", "ppos"):
+        if k in d:
+            sub[k] = d[k][nodes]
+    import dataclasses
+    sub["cfg"] = dataclasses.replace(d["cfg"], n_atoms=len(nodes))
+    return sub, nodes
+
+
+def incident(d, nodes):
+    return np.nonzero(np.isin(d["dst"], nodes) | np.isin(d["src"], nodes))[0]
+
+
+def incoming(d, nodes):
+    return np.nonzero(np.isin(d["dst"], nodes))[0]
