@@ -41,6 +41,20 @@ def gemm_flops_per_edge(L, M, C):
     return 2.0 * (mac1 + mac2)
 
 
+def measured_gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters (copy-calibrated), or None if the GEMM source changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "gemm_hbm_traffic_medium.json")))
+        src = open(os.path.join(ROOT, "so_graph_convolution_amd", "csrc", "gemm.hip"), "rb").read()
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return rec["gemm_bytes_per_step"] / rec["gemm_launches_per_step"]
+
+
 def cpu_baseline(d, n_edges_sample, seed=0):
     """Time the float64 oracle (fwd, bwd, dbwd) on a leading block of edges."""
     import numpy as np
@@ -71,7 +85,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="M")
     ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(2 ** 28, device="cuda")          # 1 GiB of float32
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4, "copy_bytes_written_per_launch":
+                          dst.numel() * 4, "launches": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the convolution runs on a "
               "single MI355X, see the design notes on sharding)", file=sys.stderr)
@@ -130,11 +157,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     K.so2conv_profile_enable(False)
-    n_l, gemm_ms, gemm_fl = K.so2conv_profile_read(-1)
+    n_l, gemm_ms, gemm_fl, gemm_by = K.so2conv_profile_read(-1)
     per_kind = {}
     for kind, name in ((0, "AB"), (1, "ABt"), (2, "AtB")):
-        n, ms, fl = K.so2conv_profile_read(kind)
-        per_kind[name] = {"launches": n, "avg_ms": ms / max(n, 1), "tflops": fl / max(ms, 1e-9) / 1e9}
+        n, ms, fl, by = K.so2conv_profile_read(kind)
+        per_kind[name] = {"launches": n, "avg_ms": ms / max(n, 1), "tflops": fl / max(ms, 1e-9) / 1e9,
+                          "algorithmic_bytes_per_launch": by / max(n, 1)}
     K.so2conv_profile_reset()
     st = np.array([[a.elapsed_time(b), b.elapsed_time(c), c.elapsed_time(e)] for a, b, c, e in stage])
     ms_step = wall * 1e3 / args.steps
@@ -158,7 +186,8 @@ def main():
                    "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
                    "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": measured_gemm_traffic(),
+                     "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
                      "kernel": "gemm_f32_kernel (fp32 MFMA per-order linears), all launches of the timed steps",
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
                      "algorithmic_flops_per_step": gemm_fl / args.steps, "per_kind": per_kind},

@@ -147,13 +147,14 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
 /* Measurement hook for the per-order GEMMs (the dense products of Section
  * 3.1 and Eq.(1)). While enabled, every matrix-core GEMM launch is bracketed
  * by HIP events on the launching stream and its algorithmic flop count (2 M N K
- * summed over the launch's problems) is recorded. so2conv_profile_read
+ * summed over the launch's problems) and algorithmic bytes (each operand read
+ * once, the output written once) are recorded. so2conv_profile_read
  * synchronises on the recorded events and returns the number of launches, the
- * summed event time (ms) and the summed flops for kind 0 (A B), 1 (A B^T),
+ * summed event time (ms), flops and bytes for kind 0 (A B), 1 (A B^T),
  * 2 (A^T B, weight gradients) or -1 (all). Host-side state, process-wide. */
 int so2conv_profile_enable(int on);
 int so2conv_profile_reset(void);
-int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops);
+int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops, double* total_bytes);
 
 /* message of the last failing call on this thread ("" if none) */
 const char* so2conv_last_error(void);

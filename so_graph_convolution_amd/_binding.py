@@ -49,7 +49,7 @@ EXPORTS = {
     "so2conv_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "so2conv_profile_reset": (ctypes.c_int, []),
     "so2conv_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double),
-                                            ctypes.POINTER(ctypes.c_double)]),
+                                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "so2conv_supported": (ctypes.c_int, [c_i32, c_i32]),
 }
 

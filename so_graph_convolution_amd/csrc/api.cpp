@@ -181,6 +181,7 @@ GemmProb prob(const float* A, int lda, const float* B, int ldb, float* C, int ld
 struct ProfRec {
   int kind;          // 0 NN, 1 NT, 2 TN
   double flops;
+  double bytes;      // algorithmic: A, B read once, C (or the split partials) written once
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
@@ -192,13 +193,16 @@ int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, hipStream_t s) {
   while (i < ps.size()) {
     GemmBatch b{};
     b.nprob = 0;
-    double flops = 0;
+    double flops = 0, bytes = 0;
     while (i < ps.size() && b.nprob < kGemmMaxProbs) {
-      flops += 2.0 * ps[i].M * (double)ps[i].N * ps[i].K;
+      const GemmProb& q = ps[i];
+      flops += 2.0 * q.M * (double)q.N * q.K;
+      bytes += 4.0 * ((double)q.M * q.K + (double)q.K * q.N +
+                      (double)q.M * q.N * (q.partial ? q.k_splits : 1) * (q.accumulate ? 2 : 1));
       b.p[b.nprob++] = ps[i++];
     }
     if (g_prof_on) {
-      ProfRec r{TA ? 2 : (TB ? 1 : 0), flops, nullptr, nullptr};
+      ProfRec r{TA ? 2 : (TB ? 1 : 0), flops, bytes, nullptr, nullptr};
       SO2_HIP(hipEventCreate(&r.a));
       SO2_HIP(hipEventCreate(&r.b));
       SO2_HIP(hipEventRecord(r.a, s));
@@ -442,10 +446,10 @@ int so2conv_profile_reset(void) {
   return SO2_OK;
 }
 
-int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops) {
+int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops, double* total_bytes) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   int64_t n = 0;
-  double ms = 0, fl = 0;
+  double ms = 0, fl = 0, by = 0;
   for (auto& r : g_prof) {
     if (kind >= 0 && r.kind != kind) continue;
     if (hipEventSynchronize(r.b) != hipSuccess) return fail(SO2_EHIP, "hipEventSynchronize failed");
@@ -454,10 +458,12 @@ int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* 
     ++n;
     ms += t;
     fl += r.flops;
+    by += r.bytes;
   }
   if (launches) *launches = n;
   if (total_ms) *total_ms = ms;
   if (total_flops) *total_flops = fl;
+  if (total_bytes) *total_bytes = by;
   return SO2_OK;
 }
 

@@ -249,12 +249,12 @@ def so2conv_profile_reset():
 
 
 def so2conv_profile_read(kind=-1):
-    """(launches, total_ms, total_flops) of the recorded GEMM launches of one kind
-    (0: A B, 1: A B^T, 2: A^T B, -1: all)."""
-    n, ms, fl = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
-    check(lib().so2conv_profile_read(kind, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)),
+    """(launches, total_ms, total_flops, total_bytes) of the recorded GEMM launches of
+    one kind (0: A B, 1: A B^T, 2: A^T B, -1: all)."""
+    n, ms, fl, by = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    check(lib().so2conv_profile_read(kind, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)),
           "so2conv_profile_read")
-    return int(n.value), float(ms.value), float(fl.value)
+    return int(n.value), float(ms.value), float(fl.value), float(by.value)
 
 
 def so2conv_debug_rotate_gather(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad):
