@@ -1,4 +1,4 @@
-// Grouped fp32 MFMA GEMM: 128x128 block tiles, 4 waves of 64x64 (2x2
+// Grouped fp32 MFMA GEMM: 256x128 block tiles, 8 waves of 64x64 (2x2
 // v_mfma_f32_32x32x2_f32 tiles each), K tile 16, LDS double buffering,
 // XCD-aware linear tile order.
 //
@@ -17,13 +17,16 @@ namespace {
 
 // Measured on MI355X for the per-order shapes (725k rows, K and N 640..2048):
 // a 2x2 MFMA wave tile with K tile 16 at four waves per SIMD (accumulators in
-// VGPRs) ran at 117-128 TFLOP/s; 4x2 or 2x4 wave tiles (one wave per SIMD)
-// and K tiles of 8 or 32 were slower.
+// VGPRs) ran at 117-128 TFLOP/s in 128x128 blocks; 4x2 or 2x4 wave tiles
+// (one wave per SIMD) and K tiles of 8 or 32 were slower. 256x128 blocks of
+// 8 waves halve the re-streaming of the (L2-exceeding) weight operand per
+// flop: 123-131 TFLOP/s for A.B and A.B^T.
 constexpr int WM = 2, WN = 2;              // 32x32 MFMA tiles per wave
-constexpr int BM = 64 * WM, BN = 64 * WN;  // 2x2 waves per block
+constexpr int WAVES_M = 4;                 // waves along M (2 along N)
+constexpr int BM = 64 * WAVES_M, BN = 128;
 constexpr int BK_TILE = 16;
 constexpr int WAVES_PER_SIMD = 4;
-constexpr int NT = 256;
+constexpr int NT = 64 * WAVES_M * 2;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -42,12 +45,48 @@ struct Cfg {
 template <bool T, int BK, int R>
 constexpr int tile_floats() { return T ? Cfg<BK, R>::KMAJ : Cfg<BK, R>::KCON; }
 
-// linear block id -> tile id such that the blocks one XCD receives (round-robin
-// dispatch over 8 XCDs) cover a contiguous range of tiles
+// linear block id -> position in a virtual tile order such that the blocks one
+// XCD receives (round-robin dispatch over 8 XCDs) cover a contiguous range
 __device__ inline int xcd_remap(int bid, int total) {
   const int q = total / 8, r = total % 8;
   const int x = bid % 8, i = bid / 8;
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Virtual order: eight slots, slot s holding the s-th eighth of every problem's
+// tiles (problems in order, tiles contiguous inside each share). Combined with
+// xcd_remap, every XCD gets an equal share of each problem -- problems of one
+// launch differ in K, so handing whole problems to XCDs would leave the XCDs
+// with the heavy problem running long -- while tiles that share a row panel
+// stay on one XCD.
+__device__ inline void decode_tile(const GemmBatch& b, int v, int* pi, int* local) {
+  int acc = 0;
+#pragma unroll 1
+  for (int s = 0; s < 8; ++s) {
+    int slot = 0;
+#pragma unroll 1
+    for (int p = 0; p < b.nprob; ++p) {
+      const int T = (p + 1 < b.nprob ? b.p[p + 1].tile_begin : b.total_tiles) - b.p[p].tile_begin;
+      slot += ((s + 1) * T) / 8 - (s * T) / 8;
+    }
+    if (v < acc + slot) {
+      int off = v - acc;
+#pragma unroll 1
+      for (int p = 0; p < b.nprob; ++p) {
+        const int T = (p + 1 < b.nprob ? b.p[p + 1].tile_begin : b.total_tiles) - b.p[p].tile_begin;
+        const int lo = (s * T) / 8, cnt = ((s + 1) * T) / 8 - lo;
+        if (off < cnt) {
+          *pi = p;
+          *local = lo + off;
+          return;
+        }
+        off -= cnt;
+      }
+    }
+    acc += slot;
+  }
+  *pi = 0;
+  *local = 0;
 }
 
 // Load one operand tile into registers.
@@ -132,13 +171,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   __shared__ float As[2][SA];
   __shared__ float Bs[2][SB];
 
-  const int tile = xcd_remap(blockIdx.x, batch.total_tiles);
-  int pi = 0;
-#pragma unroll 1
-  for (int q = 1; q < batch.nprob; ++q)
-    if (tile >= batch.p[q].tile_begin) pi = q;
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
   const GemmProb& p = batch.p[pi];
-  int local = tile - p.tile_begin;
   const int per_split = p.tiles_m * p.tiles_n;
   const int split = local / per_split;
   local -= split * per_split;
@@ -148,7 +183,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   const int kend = min(p.K, kbeg + p.k_chunk);
 
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / 2, wn = wave % 2;   // waves: WAVES_M along M, 2 along N
   const int li = lane % 32, lk = lane / 32;
 
   floatx16 acc[WM][WN];
