@@ -129,46 +129,45 @@ struct EdgeBwd {
 
 // ------------------------------------------------------------------ node_bwd
 template <int L, int M>
-__device__ __forceinline__ void node_bwd_edge_half(const Dims& d, const float* __restrict__ sRt,
-                                                   const float* __restrict__ sRLt, const float (&xn)[(L + 1) * (L + 1)],
+__device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, RotPtr sRLt,
+                                                   const float (&xn)[(L + 1) * (L + 1)],
                                                    const float* __restrict__ S, const float* __restrict__ Tbar,
                                                    float* __restrict__ Sbar, long e, int cin,
                                                    float (&acc)[(L + 1) * (L + 1)], float (&tk)[3]) {
-  constexpr int Q = q_count(L, M), K = k_count(L, M);
+  constexpr int K = k_count(L, M);
   const int Ci = 2 * d.C, wT = d.wT(), wS = (L + 1) * Ci;
-  float xt[Q];
-  rot_fwd<L, M>(sRt, xn, xt);
   const float* tb = Tbar + (size_t)e * wT + cin;
   const float* sr = S + (size_t)e * wS + cin;
   float* sb = Sbar + (size_t)e * wS + cin;
-  float xb[Q];
+  // one pass over the rows of R and R G_k: radial cotangent, transposed
+  // product into acc and the torque
 #pragma unroll
   for (int l = 0; l <= L; ++l) {
-    const int q = qhalf(l, M);
+    const int q = qhalf(l, M), n = 2 * l + 1;
     const float sc = sr[l * Ci];
     float sacc = 0.f;
 #pragma unroll
     for (int m = -q; m <= q; ++m) {
+      const int off = rot_off(l, M) + (m + q) * n;
       const float v = tb[mm_col(l, m, 0, L, Ci)];
-      sacc += v * xt[ridx(l, m, M)];
-      xb[ridx(l, m, M)] = sc * v;
+      const float xb = sc * v;
+      float r[2 * L + 1];
+      load_row<L>(sRt, off, n, r);
+      sacc += v * row_dot<L>(r, xn + l * l, n);
+      row_axpy<L>(r, xb, acc + l * l, n);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        float g[2 * L + 1];
+        load_row<L>(sRLt + k * K, off, n, g);
+        tk[k] += xb * row_dot<L>(g, xn + l * l, n);
+      }
     }
     sb[l * Ci] = sacc;
-  }
-  rot_bwd_acc<L, M>(sRt, xb, acc);
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    float w[Q];
-    rot_fwd<L, M>(sRLt + k * K, xn, w);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < Q; ++j) s += xb[j] * w[j];
-    tk[k] = s;
   }
 }
 
 template <int L, int M>
-__global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const float* __restrict__ x,
+__global__ __launch_bounds__(512) void node_bwd_kernel(Dims d, GraphDev g, const float* __restrict__ x,
                                                        const float* __restrict__ pos, const float* __restrict__ S,
                                                        const float* __restrict__ Tbar, float* __restrict__ gx,
                                                        float* __restrict__ Sbar, float* __restrict__ tau_dst,
@@ -179,14 +178,16 @@ __global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRL[TE * 3 * K];
-  __shared__ float sRed[TE * 4 * 3];
+  __shared__ float sRed[TE * 8 * 3];
   __shared__ int sE[TE];
+  __shared__ float sComb[kCombFallback];
 
   const int node = blockIdx.x;
   const int C = d.C;
-  const int c = threadIdx.x;
+  const int CW = blockDim.x / 2;
+  const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
   const bool act = c < C;
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nw = blockDim.x / 64;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, wpg = CW / 64;
   float xn[D], acc[D];
 #pragma unroll
   for (int r = 0; r < D; ++r) {
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const
       wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
       rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
       __syncthreads();
-      for (int t = 0; t < ne; ++t) {
+      for (int t = grp; t < ne; t += 2) {
         float tk[3] = {0.f, 0.f, 0.f};
         if (act) {
           const int cin = pass == 0 ? C + c : c;
@@ -223,25 +224,24 @@ __global__ __launch_bounds__(256) void node_bwd_kernel(Dims d, GraphDev g, const
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           const float s = wave_sum(tk[k]);
-          if (lane == 0) sRed[(t * 4 + wave) * 3 + k] = s;
+          if (lane == 0) sRed[(t * 8 + wave) * 3 + k] = s;
         }
       }
       __syncthreads();
       for (int idx = threadIdx.x; idx < ne * 3; idx += blockDim.x) {
         const int t = idx / 3, k = idx - t * 3;
+        const int w0 = (t % 2) * wpg;   // waves of the group that handled edge t
         float s = 0.f;
-        for (int w = 0; w < nw; ++w) s += sRed[(t * 4 + w) * 3 + k];
+        for (int w = w0; w < w0 + wpg; ++w) s += sRed[(t * 8 + w) * 3 + k];
         tau_out[(size_t)sE[t] * 3 + k] = s;
       }
       __syncthreads();
     }
   }
-  if (gx && act) {
-#pragma unroll
-    for (int r = 0; r < D; ++r) {
-      float* o = gx + ((size_t)node * D + r) * C + c;
-      *o = accumulate ? *o + acc[r] : acc[r];
-    }
+  if (gx) {
+    int cap;
+    float* cb = comb_buffer(sRL, TE * 3 * K, sComb, CW, &cap);
+    combine_groups<D>(acc, cb, cap, c, grp, CW, act, gx + (size_t)node * D * C, C, accumulate);
   }
 }
 
@@ -251,7 +251,7 @@ struct NodeBwd {
                  const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, int accumulate,
                  hipStream_t s) {
     if (g.N == 0) return hipSuccess;
-    const int threads = ((d.C + 63) / 64) * 64;
+    const int threads = 2 * ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((node_bwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, pos, S, Tbar, gx, Sbar,
                        tau_dst, tau_src, accumulate);
     return hipGetLastError();

@@ -106,21 +106,22 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
         a[r] = x[nb + (size_t)r * C];
         ad[r] = px ? px[nb + (size_t)r * C] : 0.f;
       }
-      float xt[Q], y1[Q], y2[Q];
-      rot_fwd<L, M>(sR + t * K, a, xt);
-      rot_fwd<L, M>(sRd + t * K, a, y1);
-      rot_fwd<L, M>(sR + t * K, ad, y2);
       const float* sr = S + (size_t)e * wS + c;
       const float* sd = Sdot + (size_t)e * wS + c;
       float* tr = Tdot + (size_t)e * wT;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const float sv = sr[l * Ci], sdv = sd[l * Ci];
-        const int q = qhalf(l, M);
+        const int q = qhalf(l, M), n = 2 * l + 1;
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
-          const int j = ridx(l, m, M);
-          tr[mm_col(l, m, c, L, Ci)] = sdv * xt[j] + sv * (y1[j] + y2[j]);
+          const int off = rot_off(l, M) + (m + q) * n;
+          float r[2 * L + 1], rd[2 * L + 1];
+          load_row<L>(sR + t * K, off, n, r);
+          load_row<L>(sRd + t * K, off, n, rd);
+          const float xt = row_dot<L>(r, a + l * l, n), y2 = row_dot<L>(r, ad + l * l, n);
+          const float y1 = row_dot<L>(rd, a + l * l, n);
+          tr[mm_col(l, m, c, L, Ci)] = sdv * xt + sv * (y1 + y2);
         }
       }
     }
@@ -144,7 +145,7 @@ struct EdgeDual {
 
 // ------------------------------------------------------------------ node_dual
 template <int L, int M>
-__global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
+__global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                         const float* __restrict__ omega, const float* __restrict__ V,
                                                         const float* __restrict__ Vdot, float* __restrict__ ydot,
                                                         int accumulate) {
@@ -155,13 +156,15 @@ __global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, cons
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
+  __shared__ float sComb[kCombFallback];
 
   const int node = blockIdx.x;
   int beg, end;
   in_range(g, node, &beg, &end);
   if (accumulate && beg == end) return;
   const int C = d.C, wZ = d.wZ();
-  const int c = threadIdx.x;
+  const int CW = blockDim.x / 2;
+  const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
   float acc[D];
 #pragma unroll
   for (int r = 0; r < D; ++r) acc[r] = 0.f;
@@ -177,30 +180,30 @@ __global__ __launch_bounds__(256) void node_dual_kernel(Dims d, GraphDev g, cons
     rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
     __syncthreads();
     if (c < C) {
-      for (int t = 0; t < ne; ++t) {
+      for (int t = grp; t < ne; t += 2) {
         const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
         const float* vd = Vdot + (size_t)(t0 + t - g.e0) * wZ + c;
-        float tv[Q], tdv[Q];
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
-          const int q = qhalf(l, M);
+          const int q = qhalf(l, M), n = 2 * l + 1;
 #pragma unroll
           for (int m = -q; m <= q; ++m) {
-            tv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
-            tdv[ridx(l, m, M)] = vd[mm_col(l, m, 0, L, C)];
+            const int off = rot_off(l, M) + (m + q) * n;
+            const float v = vr[mm_col(l, m, 0, L, C)], vdv = vd[mm_col(l, m, 0, L, C)];
+            float r[2 * L + 1], rd[2 * L + 1];
+            load_row<L>(sR + t * K, off, n, r);
+            load_row<L>(sRd + t * K, off, n, rd);
+            row_axpy<L>(rd, v, acc + l * l, n);
+            row_axpy<L>(r, vdv, acc + l * l, n);
           }
         }
-        rot_bwd_acc<L, M>(sRd + t * K, tv, acc);
-        rot_bwd_acc<L, M>(sR + t * K, tdv, acc);
       }
     }
     __syncthreads();
   }
-  if (c < C) {
-    float* yr = ydot + (size_t)node * D * C + c;
-#pragma unroll
-    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = accumulate ? yr[(size_t)r * C] + acc[r] : acc[r];
-  }
+  int cap;
+  float* cb = comb_buffer(sR, TE * K, sComb, CW, &cap);
+  combine_groups<D>(acc, cb, cap, c, grp, CW, c < C, ydot + (size_t)node * D * C, C, accumulate);
 }
 
 template <int L, int M>
@@ -208,7 +211,8 @@ struct NodeDual {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
                  const float* Vdot, float* ydot, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((node_dual_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, omega, V, Vdot, ydot,
+    const int threads = 2 * ((d.C + 63) / 64) * 64;
+    hipLaunchKernelGGL((node_dual_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, pos, omega, V, Vdot, ydot,
                        accumulate);
     return hipGetLastError();
   }
@@ -249,18 +253,19 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
       const float* gr = gy + (size_t)sDst[t] * D * C + c;
 #pragma unroll
       for (int r = 0; r < D; ++r) gv[r] = gr[(size_t)r * C];
-      float o1[Q], o2[Q];
-      rot_fwd<L, M>(sR + t * K, gv, o1);
-      rot_fwd<L, M>(sRd + t * K, gv, o2);
       float* r1 = G2 + (size_t)e * wZ + c;
       float* r2 = G2 + ((size_t)(g.e1 - g.e0) + e) * wZ + c;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
-        const int q = qhalf(l, M);
+        const int q = qhalf(l, M), n = 2 * l + 1;
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
-          r1[mm_col(l, m, 0, L, C)] = o1[ridx(l, m, M)];
-          r2[mm_col(l, m, 0, L, C)] = o2[ridx(l, m, M)];
+          const int off = rot_off(l, M) + (m + q) * n;
+          float r[2 * L + 1], rd[2 * L + 1];
+          load_row<L>(sR + t * K, off, n, r);
+          load_row<L>(sRd + t * K, off, n, rd);
+          r1[mm_col(l, m, 0, L, C)] = row_dot<L>(r, gv + l * l, n);
+          r2[mm_col(l, m, 0, L, C)] = row_dot<L>(rd, gv + l * l, n);
         }
       }
     }
@@ -282,7 +287,7 @@ struct EdgeBwdDual {
 
 // ------------------------------------------------------------------ node_bwd_dual
 template <int L, int M>
-__global__ __launch_bounds__(256) void node_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ x,
+__global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ x,
                                                             const float* __restrict__ px,
                                                             const float* __restrict__ pos,
                                                             const float* __restrict__ omega,
@@ -299,10 +304,12 @@ __global__ __launch_bounds__(256) void node_bwd_dual_kernel(Dims d, GraphDev g, 
   __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
   __shared__ int sE[TE];
+  __shared__ float sComb[kCombFallback];
 
   const int node = blockIdx.x;
   const int C = d.C, Ci = 2 * C, wT = d.wT(), wS = (L + 1) * Ci;
-  const int c = threadIdx.x;
+  const int CW = blockDim.x / 2;
+  const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
   const bool act = c < C;
   float xn[D], xdn[D], acc[D];
 #pragma unroll
@@ -334,50 +341,46 @@ __global__ __launch_bounds__(256) void node_bwd_dual_kernel(Dims d, GraphDev g, 
       __syncthreads();
       if (act) {
         const int cin = pass == 0 ? C + c : c;
-        for (int t = 0; t < ne; ++t) {
+        for (int t = grp; t < ne; t += 2) {
           const long e = sE[t];
-          const float* Rt = sR + t * K;
-          const float* Rdt = sRd + t * K;
-          float xt[Q], y1[Q], y2[Q];
-          rot_fwd<L, M>(Rt, xn, xt);
-          rot_fwd<L, M>(Rdt, xn, y1);
-          rot_fwd<L, M>(Rt, xdn, y2);
           const float* tdb = Tdb + (size_t)e * wT + cin;
           const float* tb = Tb + (size_t)e * wT + cin;
           const float* sr = S + (size_t)e * wS + cin;
           const float* sd = Sdot + (size_t)e * wS + cin;
-          float u1[Q], u2[Q];   // R^T and Rdot^T operands
+          // one pass over the rows of R and Rdot: forward products for the
+          // radial cotangents and the transposed products into acc
 #pragma unroll
           for (int l = 0; l <= L; ++l) {
-            const int q = qhalf(l, M);
+            const int q = qhalf(l, M), n = 2 * l + 1;
             const float sv = sr[l * Ci], sdv = sd[l * Ci];
             float sb = 0.f, sdb = 0.f;
 #pragma unroll
             for (int m = -q; m <= q; ++m) {
-              const int jj = ridx(l, m, M);
+              const int off = rot_off(l, M) + (m + q) * n;
               const float a1 = tdb[mm_col(l, m, 0, L, Ci)];
               const float a0 = tb[mm_col(l, m, 0, L, Ci)];
-              u1[jj] = sv * a0 + sdv * a1;
-              u2[jj] = sv * a1;
-              sb += a1 * (y1[jj] + y2[jj]) + a0 * xt[jj];
-              sdb += a1 * xt[jj];
+              float r[2 * L + 1], rd[2 * L + 1];
+              load_row<L>(sR + t * K, off, n, r);
+              load_row<L>(sRd + t * K, off, n, rd);
+              const float xt = row_dot<L>(r, xn + l * l, n), y2 = row_dot<L>(r, xdn + l * l, n);
+              const float y1 = row_dot<L>(rd, xn + l * l, n);
+              sb += a1 * (y1 + y2) + a0 * xt;
+              sdb += a1 * xt;
+              row_axpy<L>(r, sv * a0 + sdv * a1, acc + l * l, n);
+              row_axpy<L>(rd, sv * a1, acc + l * l, n);
             }
             Sbar[(size_t)e * wS + l * Ci + cin] = sb;
             Sdb[(size_t)e * wS + l * Ci + cin] = sdb;
           }
-          rot_bwd_acc<L, M>(Rt, u1, acc);
-          rot_bwd_acc<L, M>(Rdt, u2, acc);
         }
       }
       __syncthreads();
     }
   }
-  if (gx2 && act) {
-#pragma unroll
-    for (int r = 0; r < D; ++r) {
-      float* o = gx2 + ((size_t)node * D + r) * C + c;
-      *o = accumulate ? *o + acc[r] : acc[r];
-    }
+  if (gx2) {
+    int cap;
+    float* cb = comb_buffer(sRd, TE * K, sComb, CW, &cap);
+    combine_groups<D>(acc, cb, cap, c, grp, CW, act, gx2 + (size_t)node * D * C, C, accumulate);
   }
 }
 
@@ -387,7 +390,7 @@ struct NodeBwdDual {
                  const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2, float* Sbar,
                  float* Sdb, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
-    const int threads = ((d.C + 63) / 64) * 64;
+    const int threads = 2 * ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((node_bwd_dual_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega, S, Sdot,
                        TT, gx2, Sbar, Sdb, accumulate);
     return hipGetLastError();

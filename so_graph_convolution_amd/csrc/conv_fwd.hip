@@ -85,20 +85,23 @@ struct EdgeFwd {
 
 // ------------------------------------------------------------------ node_fwd
 template <int L, int M>
-__global__ __launch_bounds__(256) void node_fwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
+__global__ __launch_bounds__(512) void node_fwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                        const float* __restrict__ V, float* __restrict__ y,
                                                        int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   __shared__ float sD1[kTileE * 9];
   __shared__ float sR[kTileE * K];
   __shared__ float sA[kTileE * ST], sB[kTileE * ST];
+  __shared__ float sComb[kCombFallback];
 
   const int node = blockIdx.x;
   int beg, end;
   in_range(g, node, &beg, &end);
   if (accumulate && beg == end) return;
   const int C = d.C, wZ = d.wZ();
-  const int c = threadIdx.x;          // one channel per thread (blockDim == C)
+  const int CW = blockDim.x / 2;
+  const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
+  const bool act = c < C;
   float acc[D];
 #pragma unroll
   for (int r = 0; r < D; ++r) acc[r] = 0.f;
@@ -111,8 +114,8 @@ __global__ __launch_bounds__(256) void node_fwd_kernel(Dims d, GraphDev g, const
     }
     __syncthreads();
     wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
-    if (c < C) {
-      for (int t = 0; t < ne; ++t) {
+    if (act) {
+      for (int t = grp; t < ne; t += 2) {
         const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
         float tv[Q];
 #pragma unroll
@@ -126,11 +129,9 @@ __global__ __launch_bounds__(256) void node_fwd_kernel(Dims d, GraphDev g, const
     }
     __syncthreads();
   }
-  if (c < C) {
-    float* yr = y + (size_t)node * D * C + c;
-#pragma unroll
-    for (int r = 0; r < D; ++r) yr[(size_t)r * C] = accumulate ? yr[(size_t)r * C] + acc[r] : acc[r];
-  }
+  int cap;
+  float* cb = comb_buffer(sR, kTileE * K, sComb, CW, &cap);
+  combine_groups<D>(acc, cb, cap, c, grp, CW, act, y + (size_t)node * D * C, C, accumulate);
 }
 
 template <int L, int M>
@@ -138,7 +139,8 @@ struct NodeFwd {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
                  hipStream_t s) {
     if (g.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((node_fwd_kernel<L, M>), dim3(g.N), dim3(d.C), 0, s, d, g, pos, V, y, accumulate);
+    const int threads = 2 * ((d.C + 63) / 64) * 64;
+    hipLaunchKernelGGL((node_fwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, pos, V, y, accumulate);
     return hipGetLastError();
   }
 };

@@ -101,9 +101,17 @@ __device__ inline void rot_directional(int L, int M, int ne, const float* R, int
   }
 }
 
+// Rotation entries live in LDS and are read with volatile LDS loads: each use
+// is a broadcast LDS read instead of a register kept live across the unrolled
+// loops (which would cost K_{L,M} registers per rotation table and occupancy).
+typedef const float* RotPtr;
+__device__ __forceinline__ float rot_ld(RotPtr p) {
+  return *(const volatile __attribute__((address_space(3))) float*)(p);
+}
+
 // o[ridx(l,m)] = sum_n R[l][m][n] a[l*l + l + n]   (rotate degree-major -> retained rows)
 template <int L, int M>
-__device__ __forceinline__ void rot_fwd(const float* __restrict__ R, const float (&a)[(L + 1) * (L + 1)],
+__device__ __forceinline__ void rot_fwd(RotPtr R, const float (&a)[(L + 1) * (L + 1)],
                                         float (&o)[q_count(L, M)]) {
 #pragma unroll
   for (int l = 0; l <= L; ++l) {
@@ -112,15 +120,39 @@ __device__ __forceinline__ void rot_fwd(const float* __restrict__ R, const float
     for (int m = -q; m <= q; ++m) {
       float s = 0.f;
 #pragma unroll
-      for (int k = 0; k < n; ++k) s += R[rot_off(l, M) + (m + q) * n + k] * a[l * l + k];
+      for (int k = 0; k < n; ++k) s += rot_ld(R + rot_off(l, M) + (m + q) * n + k) * a[l * l + k];
       o[ridx(l, m, M)] = s;
     }
   }
 }
 
+// row (l, m) of a compact rotation table, loaded once into registers
+template <int L>
+__device__ __forceinline__ void load_row(RotPtr R, int off, int n, float (&r)[2 * L + 1]) {
+#pragma unroll
+  for (int k = 0; k < 2 * L + 1; ++k)
+    if (k < n) r[k] = rot_ld(R + off + k);
+}
+
+template <int L>
+__device__ __forceinline__ float row_dot(const float (&r)[2 * L + 1], const float* a, int n) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 2 * L + 1; ++k)
+    if (k < n) s += r[k] * a[k];
+  return s;
+}
+
+template <int L>
+__device__ __forceinline__ void row_axpy(const float (&r)[2 * L + 1], float v, float* o, int n) {
+#pragma unroll
+  for (int k = 0; k < 2 * L + 1; ++k)
+    if (k < n) o[k] += r[k] * v;
+}
+
 // o[l*l + l + n] += sum_m R[l][m][n] t[ridx(l,m)]   (inverse rotation of retained rows)
 template <int L, int M>
-__device__ __forceinline__ void rot_bwd_acc(const float* __restrict__ R, const float (&t)[q_count(L, M)],
+__device__ __forceinline__ void rot_bwd_acc(RotPtr R, const float (&t)[q_count(L, M)],
                                             float (&o)[(L + 1) * (L + 1)]) {
 #pragma unroll
   for (int l = 0; l <= L; ++l) {
@@ -129,7 +161,7 @@ __device__ __forceinline__ void rot_bwd_acc(const float* __restrict__ R, const f
     for (int m = -q; m <= q; ++m) {
       const float tv = t[ridx(l, m, M)];
 #pragma unroll
-      for (int k = 0; k < n; ++k) o[l * l + k] += R[rot_off(l, M) + (m + q) * n + k] * tv;
+      for (int k = 0; k < n; ++k) o[l * l + k] += rot_ld(R + rot_off(l, M) + (m + q) * n + k) * tv;
     }
   }
 }
@@ -167,6 +199,51 @@ __device__ inline void out_range(const GraphDev& g, int node, int* beg, int* end
   }
   *beg = b;
   *end = e;
+}
+
+// Node-centric kernels run two thread groups per node (threads [0, CW) and
+// [CW, 2 CW), CW = C rounded up to 64): group p takes the tile's edges
+// t = p, p + 2, ... with the same channels, doubling the waves in flight per
+// node for the same LDS tile. At the end the groups' register accumulators are
+// combined through LDS (`buf`, capacity `cap` floats, in row chunks) and group
+// 0 writes (or adds) the node row out[r * C + c]. The caller guarantees
+// cap >= CW (one row; see comb_buffer), so every round advances by a row.
+constexpr int kCombFallback = 512;   // floats; CW <= 256
+
+// `tile` (capacity tile_cap) if it holds one channel row of CW floats, else the
+// dedicated fallback buffer
+__device__ __forceinline__ float* comb_buffer(float* tile, int tile_cap, float* fallback, int CW, int* cap) {
+  if (tile_cap >= CW) {
+    *cap = tile_cap;
+    return tile;
+  }
+  *cap = kCombFallback;
+  return fallback;
+}
+
+template <int D>
+__device__ inline void combine_groups(const float (&acc)[D], float* buf, int cap, int c, int grp, int CW, bool act,
+                                      float* out, int C, int accumulate) {
+  const int fit = cap / CW;
+  const int rows = fit < 1 ? 1 : (fit < D ? fit : D);
+  for (int r0 = 0; r0 < D; r0 += rows) {
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int r = 0; r < D; ++r)
+        if (r >= r0 && r < r0 + rows) buf[(r - r0) * CW + c] = acc[r];
+    }
+    __syncthreads();
+    if (grp == 0 && act) {
+#pragma unroll
+      for (int r = 0; r < D; ++r)
+        if (r >= r0 && r < r0 + rows) {
+          const float v = acc[r] + buf[(r - r0) * CW + c];
+          float* o = out + (size_t)r * C + c;
+          *o = accumulate ? *o + v : v;
+        }
+    }
+  }
 }
 
 // sum over a wavefront (64 lanes)
