@@ -14,7 +14,7 @@
  *   L = lmax (0..6), M = mmax (0..L), C = channels (multiple of 16, 16..256),
  *   d = (L+1)^2 node rows in degree-major order (l, m = -l..l), real
  *   orthonormal harmonics without Condon-Shortley phase (Y_1 ~ (y, z, x)).
- *   Node features x, y, gx, gy, px: [N, d, C] float32.
+ *   Node features x, y, gx, gy, px, ggy, gx2: [N, d, C] of the call's dtype.
  *   pos, gpos, ppos: [N, 3] float32.  shift, gedge, pedge: [E, 3] float32.
  *   rbf, grbf, prbf: [E, n_rbf] float32 (n_rbf a multiple of 4).
  *   w_rad: [n_rbf, (L+1) * 2C], column (l, c_in), c_in < C: source channels.
@@ -27,6 +27,16 @@
  *   Gate: l = 0 -> SiLU(u); l >= 1 -> sigmoid(gate_{l,c}) * u for every
  *   retained order |m| <= min(l, M).
  *   Graph: dst non-decreasing (edges grouped by receiver).
+ *
+ * dtype (cfg->dtype): SO2_F32 -- every array float32, float32 arithmetic.
+ *   SO2_BF16 -- node features (x, y, gy, gx, px, ggy, gx2) and weights with
+ *   their gradients (w_rad, w1, w2, gw_*, pw_*) are bfloat16; pos, shift, rbf
+ *   and their gradients and directions stay float32. Node arrays are widened
+ *   to float32 once per call; the per-order products run on bfloat16 matrix
+ *   cores (operands rounded to nearest even) with float32 accumulation, and
+ *   every other step (rotations, gates, reductions, weight-gradient sums)
+ *   computes in float32; outputs are rounded to bfloat16 once at the end.
+ *   Arrays typed `void*` below hold elements of the call's dtype.
  *
  * Ownership: every array pointer is a caller-owned DEVICE pointer on the
  * current HIP device, except the pointer arrays w1/w2/gw1/... themselves,
@@ -61,7 +71,7 @@ typedef enum {
   SO2_EDEVICE = -5        /* device-side validation failed */
 } so2_status;
 
-typedef enum { SO2_F32 = 0 } so2_dtype;
+typedef enum { SO2_F32 = 0, SO2_BF16 = 1 } so2_dtype;
 
 typedef struct {
   int32_t lmax, mmax, channels, n_rbf, dtype, flags;
@@ -96,12 +106,15 @@ int so2conv_graph_prepare(int32_t n_nodes, int64_t n_edges, const int32_t* src, 
  * accumulated across chunks in a fixed order, so results do not depend on the
  * chunk size beyond float rounding of that order.
  *   so2conv_saved_bytes: the per-edge forward state (about 56 KB per edge at
- *     lmax 4, C 128) that so2conv_fwd writes into `saved` and bwd/dbwd read.
+ *     lmax 4, C 128 in float32; 41 KB with bfloat16 operands) that
+ *     so2conv_fwd writes into `saved` and bwd/dbwd read.
  *   so2conv_workspace_bytes(stage): workspace for one chunk covering all edges
  *     when `saved` is used (stage 0 forward, 1 backward, 2 double backward).
  *   so2conv_chunked_workspace_bytes(stage, chunk_edges): workspace when `saved`
  *     is NULL and chunks of chunk_edges edges recompute the forward state
- *     (bounded memory; backward stages then redo the forward products). */
+ *     (bounded memory; backward stages then redo the forward products).
+ * Both include the float32 copies of the node arrays of a bfloat16 call, so
+ * they depend on n_nodes. */
 size_t so2conv_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage);
 size_t so2conv_chunked_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage,
                                        int64_t chunk_edges);
@@ -109,18 +122,18 @@ size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges);
 
 /* Forward: y [N,d,C]. `saved` (may be NULL) receives the state needed by
  * so2conv_bwd / so2conv_dbwd for the same inputs. */
-int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
-                const float* w_rad, const float* const* w1, const float* const* w2, float* y, void* saved,
-                void* ws, size_t ws_bytes, void* stream);
+int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
+                const void* w_rad, const void* const* w1, const void* const* w2, void* y, void* saved, void* ws,
+                size_t ws_bytes, void* stream);
 
 /* Backward (vector-Jacobian product with cotangent gy, Section 3.3): gx, gpos,
  * grbf, gw_rad, gw1[m], gw2[m] and gedge = dL/dv_e (for virials). `saved`
  * comes from so2conv_fwd on the same inputs, or is NULL (the forward state is
  * recomputed chunk by chunk). gw1/gw2 may be NULL, or hold NULL entries. */
-int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
-                const float* w_rad, const float* const* w1, const float* const* w2, const void* saved,
-                const float* gy, float* gx, float* gpos, float* grbf, float* gw_rad, float* const* gw1,
-                float* const* gw2, float* gedge, void* ws, size_t ws_bytes, void* stream);
+int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
+                const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
+                void* gx, float* gpos, float* grbf, void* gw_rad, void* const* gw1, void* const* gw2, float* gedge,
+                void* ws, size_t ws_bytes, void* stream);
 
 /* Double backward: derivatives of
  *   L = <px, gx> + <ppos, gpos> + <pedge, gedge> + <prbf, grbf> + <pw, gw>
@@ -128,20 +141,22 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, 
  * respect to gy (ggy = the forward's directional derivative, Eq.(5)), x (gx2),
  * rbf (grbf2), w_rad, w1, w2. gpos2 (second derivatives in positions) is not
  * provided by this version and must be NULL. */
-int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
-                 const float* w_rad, const float* const* w1, const float* const* w2, const void* saved,
-                 const float* gy, const float* px, const float* ppos, const float* pedge, const float* prbf,
-                 const float* pw_rad, const float* const* pw1, const float* const* pw2, float* ggy, float* gx2,
-                 float* gpos2, float* grbf2, float* gw_rad2, float* const* gw1_2, float* const* gw2_2, void* ws,
-                 size_t ws_bytes, void* stream);
+int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
+                 const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
+                 const void* px, const float* ppos, const float* pedge, const float* prbf, const void* pw_rad,
+                 const void* const* pw1, const void* const* pw2, void* ggy, void* gx2, float* gpos2, float* grbf2,
+                 void* gw_rad2, void* const* gw1_2, void* const* gw2_2, void* ws, size_t ws_bytes, void* stream);
 
 /* Test hook: the first linear's m-major input T (rotation on gather,
  * Appendix B.1) [E, q*2C], block |m| = 0..M: block 0 columns (l, c_in), block
  * m columns [+m (l = m..L, c_in) | -m (l = m..L, c_in)], with the pinned edge
  * frame rows (z >= 0, k = 1/(1+z): (1-x^2k, -xyk, -x), (-xyk, 1-y^2k, -y),
- * (x, y, z); z < 0, k = 1/(1-z): (1-x^2k, -xyk, x), (xyk, y^2k-1, -y), (x, y, z)). */
-int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos,
-                                const float* rbf, const float* w_rad, float* T_out, void* ws, size_t ws_bytes,
+ * (x, y, z); z < 0, k = 1/(1-z): (1-x^2k, -xyk, x), (xyk, y^2k-1, -y), (x, y, z)).
+ * T_out has the call's dtype (the stored GEMM operand). Workspace: E*(L+1)*2C
+ * floats, plus N*d*C + n_rbf*(L+1)*2C floats for a bfloat16 call (each
+ * rounded up to 256 bytes). */
+int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos,
+                                const float* rbf, const void* w_rad, void* T_out, void* ws, size_t ws_bytes,
                                 void* stream);
 
 /* Measurement hook for the per-order GEMMs (the dense products of Section
@@ -151,7 +166,8 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
  * once, the output written once) are recorded. so2conv_profile_read
  * synchronises on the recorded events and returns the number of launches, the
  * summed event time (ms), flops and bytes for kind 0 (A B), 1 (A B^T),
- * 2 (A^T B, weight gradients) or -1 (all). Host-side state, process-wide. */
+ * 2 (A^T B, weight gradients) with float32 operands, 3 (A B^T) and 4 (A^T B)
+ * with bfloat16 operands, or -1 (all). Host-side state, process-wide. */
 int so2conv_profile_enable(int on);
 int so2conv_profile_reset(void);
 int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops, double* total_bytes);

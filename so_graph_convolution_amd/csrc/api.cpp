@@ -88,7 +88,18 @@ int ensure_init() {
 }
 
 // ---------------------------------------------------------------- checks
-int check_cfg(const so2conv_cfg* cfg, Dims* d) {
+// Configuration of one call: sizes and the storage type of the boundary arrays
+// and of the per-edge GEMM operands.
+struct Ctx {
+  Dims d;
+  int n_rbf;
+  int bf;    // 1: bfloat16 boundary arrays and GEMM operands
+  int es;    // bytes per GEMM-operand element
+  size_t node_floats() const { return (size_t)d.d() * d.C; }   // one node row
+  int wS() const { return (d.L + 1) * d.Ci(); }
+};
+
+int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
   if (!cfg) return fail(SO2_EINVAL, "cfg is NULL");
   const int L = cfg->lmax, M = cfg->mmax, C = cfg->channels;
   if (L < 0 || L > kMaxL) return fail(SO2_EUNSUPPORTED, "lmax must be in [0, 6]");
@@ -97,10 +108,13 @@ int check_cfg(const so2conv_cfg* cfg, Dims* d) {
   if (C < 16 || C > 256 || C % 16) return fail(SO2_EUNSUPPORTED, "channels must be a multiple of 16 in [16, 256]");
   if (cfg->n_rbf < 4 || cfg->n_rbf % 4 || cfg->n_rbf > 1024)
     return fail(SO2_EUNSUPPORTED, "n_rbf must be a multiple of 4 in [4, 1024]");
-  if (cfg->dtype != SO2_F32) return fail(SO2_EUNSUPPORTED, "only float32 is supported");
-  d->L = L;
-  d->M = M;
-  d->C = C;
+  if (cfg->dtype != SO2_F32 && cfg->dtype != SO2_BF16) return fail(SO2_EUNSUPPORTED, "dtype must be SO2_F32 or SO2_BF16");
+  c->d.L = L;
+  c->d.M = M;
+  c->d.C = C;
+  c->n_rbf = cfg->n_rbf;
+  c->bf = cfg->dtype == SO2_BF16;
+  c->es = c->bf ? 2 : 4;
   return SO2_OK;
 }
 
@@ -124,29 +138,43 @@ int check_graph(const so2conv_graph* g, GraphDev* gd) {
 }
 
 // ---------------------------------------------------------------- layouts
+// Bump allocator over the caller's workspace. With a null base it only
+// measures: every stage lays out its buffers through one function, used both
+// to size the workspace and to carve it.
+struct Arena {
+  char* base;
+  size_t used;
+  void* bytes(size_t n) {
+    void* p = base ? base + used : nullptr;
+    used += al(n);
+    return p;
+  }
+  float* take(size_t floats) { return static_cast<float*>(bytes(sizeof(float) * floats)); }
+};
+
 struct SavedLayout {
   size_t S, T, U, Z, V, total;
 };
-SavedLayout saved_layout(const Dims& d, int n_rbf, long E) {
-  (void)n_rbf;
+SavedLayout saved_layout(const Ctx& c, long E) {
+  const Dims& d = c.d;
   SavedLayout s;
   size_t o = 0;
   const size_t e = (size_t)E;
-  s.S = o; o += al(sizeof(float) * e * (d.L + 1) * d.Ci());
-  s.T = o; o += al(sizeof(float) * e * d.wT());
+  s.S = o; o += al(sizeof(float) * e * c.wS());
+  s.T = o; o += al((size_t)c.es * e * d.wT());
   s.U = o; o += al(sizeof(float) * e * d.wU());
-  s.Z = o; o += al(sizeof(float) * e * d.wZ());
+  s.Z = o; o += al((size_t)c.es * e * d.wZ());
   s.V = o; o += al(sizeof(float) * e * d.wZ());
   s.total = o;
   return s;
 }
 
-// K chunk of split-K weight-gradient products over edges
+// K chunk of split-K weight-gradient products over edges (a multiple of the GEMM K tile)
 void split_plan(long K, int* splits, int* chunk) {
   long c = 4096;
   long s = (K + c - 1) / c;
   if (s > 256) {
-    c = ((K + 255) / 256 + 15) / 16 * 16;
+    c = ((K + 255) / 256 + kGemmKTile - 1) / kGemmKTile * kGemmKTile;
     s = (K + c - 1) / c;
   }
   if (s < 1) s = 1;
@@ -154,18 +182,203 @@ void split_plan(long K, int* splits, int* chunk) {
   *chunk = (int)c;
 }
 
-struct Arena {
-  char* base;
-  size_t used;
-  float* take(size_t floats) {
-    float* p = reinterpret_cast<float*>(base ? base + used : nullptr);
-    used += al(sizeof(float) * floats);
-    return p;
-  }
+// realified weights of one linear as GEMM B operands: W [rows][cols] and, for
+// bfloat16, its transpose (the forward product A.W runs as A.(W^T)^T)
+struct Lin {
+  const void* W;
+  const void* WT;
 };
+struct LinBuf {
+  void* W;
+  void* WT;
+};
+LinBuf take_lin(Arena& ar, const Ctx& c, int second) {
+  const size_t n = (size_t)realified_size(c.d, second);
+  LinBuf b;
+  b.W = ar.bytes(n * c.es);
+  b.WT = c.bf ? ar.bytes(n * c.es) : nullptr;
+  return b;
+}
+
+// largest weight-gradient block (floats): realified blocks and the radial matrix
+size_t max_grad_block(const Ctx& c) {
+  size_t mx = (size_t)c.n_rbf * c.wS();
+  for (int second = 0; second < 2; ++second)
+    for (int a = 0; a <= c.d.M; ++a) {
+      int r, cc;
+      long off;
+      realified_shape(c.d, second, a, &r, &cc, &off);
+      if ((size_t)r * cc > mx) mx = (size_t)r * cc;
+    }
+  return mx;
+}
+
+float* take_partials(Arena& ar, const Ctx& c, long ec, int nseg) {
+  int sp, ch;
+  split_plan(ec, &sp, &ch);
+  return ar.take((size_t)nseg * (sp + 1) * max_grad_block(c));
+}
+
+struct Primal {
+  const float* S;
+  const void* T;
+  const float* U;
+  const void* Z;
+  const float* V;
+};
+struct PrimalBuf {
+  float* S;
+  void* T;
+  float* U;
+  void* Z;
+  float* V;
+};
+PrimalBuf take_primal(Arena& ar, const Ctx& c, long ec) {
+  const Dims& d = c.d;
+  const size_t e = (size_t)ec;
+  PrimalBuf p;
+  p.S = ar.take(e * c.wS());
+  p.T = ar.bytes(e * d.wT() * c.es);
+  p.U = ar.take(e * d.wU());
+  p.Z = ar.bytes(e * d.wZ() * c.es);
+  p.V = ar.take(e * d.wZ());
+  return p;
+}
+Primal saved_rows(const Ctx& c, const void* saved, long E, long e0) {
+  const SavedLayout sl = saved_layout(c, E);
+  const char* st = static_cast<const char*>(saved);
+  const Dims& d = c.d;
+  return {reinterpret_cast<const float*>(st + sl.S) + (size_t)e0 * c.wS(),
+          st + sl.T + (size_t)e0 * d.wT() * c.es,
+          reinterpret_cast<const float*>(st + sl.U) + (size_t)e0 * d.wU(),
+          st + sl.Z + (size_t)e0 * d.wZ() * c.es,
+          reinterpret_cast<const float*>(st + sl.V) + (size_t)e0 * d.wZ()};
+}
+
+struct FwdWs {
+  LinBuf W1, W2;
+  float *w_rad32, *x32, *y32;
+  PrimalBuf pr;
+};
+void layout_fwd(Arena& ar, const Ctx& c, int N, long ec, bool recompute, FwdWs* w) {
+  w->W1 = take_lin(ar, c, 0);
+  w->W2 = take_lin(ar, c, 1);
+  w->w_rad32 = c.bf ? ar.take((size_t)c.n_rbf * c.wS()) : nullptr;
+  w->x32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
+  w->y32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
+  w->pr = recompute ? take_primal(ar, c, ec) : PrimalBuf{};
+}
+
+struct BwdWs {
+  LinBuf W1, W2;
+  float *gW1r, *gW2r, *vbar_all;
+  float *w_rad32, *x32, *gy32, *gx32, *gw_rad32;
+  PrimalBuf pr;
+  void *tbar, *Ubar;
+  float *Zbar, *Tbar, *Sbar, *tau1, *tau2, *tau3, *P;
+};
+void layout_bwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute, BwdWs* w) {
+  const Dims& d = c.d;
+  const size_t e = (size_t)ec;
+  w->W1 = take_lin(ar, c, 0);
+  w->W2 = take_lin(ar, c, 1);
+  w->gW1r = ar.take(realified_size(d, 0));
+  w->gW2r = ar.take(realified_size(d, 1));
+  w->vbar_all = ar.take((size_t)E * 3);
+  w->w_rad32 = c.bf ? ar.take((size_t)c.n_rbf * c.wS()) : nullptr;
+  w->x32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
+  w->gy32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
+  w->gx32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
+  w->gw_rad32 = c.bf ? ar.take((size_t)c.n_rbf * c.wS()) : nullptr;
+  w->pr = recompute ? take_primal(ar, c, ec) : PrimalBuf{};
+  w->tbar = ar.bytes(e * d.wZ() * c.es);
+  w->Zbar = ar.take(e * d.wZ());
+  w->Ubar = ar.bytes(e * d.wU() * c.es);
+  w->Tbar = ar.take(e * d.wT());
+  w->Sbar = ar.take(e * c.wS());
+  w->tau1 = ar.take(e * 3);
+  w->tau2 = ar.take(e * 3);
+  w->tau3 = ar.take(e * 3);
+  w->P = take_partials(ar, c, ec, 1);
+}
+
+struct DbwdWs {
+  LinBuf W1, W2, pW1, pW2;
+  float *gW1r, *gW2r;
+  float *w_rad32, *pw_rad32, *x32, *px32, *gy32, *ggy32, *gx2_32, *gw_rad2_32;
+  PrimalBuf pr;
+  void *Tdot, *Zdot, *G2, *UU;
+  float *Sdot, *omega, *Udot, *Vdot, *ZZ, *TT, *Sbar, *Sdb, *P;
+};
+void layout_dbwd(Arena& ar, const Ctx& c, int N, long ec, bool recompute, DbwdWs* w) {
+  const Dims& d = c.d;
+  const size_t e = (size_t)ec;
+  w->W1 = take_lin(ar, c, 0);
+  w->W2 = take_lin(ar, c, 1);
+  w->pW1 = take_lin(ar, c, 0);
+  w->pW2 = take_lin(ar, c, 1);
+  w->gW1r = ar.take(realified_size(d, 0));
+  w->gW2r = ar.take(realified_size(d, 1));
+  const size_t nf = (size_t)N * c.node_floats(), rf = (size_t)c.n_rbf * c.wS();
+  w->w_rad32 = c.bf ? ar.take(rf) : nullptr;
+  w->pw_rad32 = c.bf ? ar.take(rf) : nullptr;
+  w->gw_rad2_32 = c.bf ? ar.take(rf) : nullptr;
+  w->x32 = c.bf ? ar.take(nf) : nullptr;
+  w->px32 = c.bf ? ar.take(nf) : nullptr;
+  w->gy32 = c.bf ? ar.take(nf) : nullptr;
+  w->ggy32 = c.bf ? ar.take(nf) : nullptr;
+  w->gx2_32 = c.bf ? ar.take(nf) : nullptr;
+  w->pr = recompute ? take_primal(ar, c, ec) : PrimalBuf{};
+  w->Sdot = ar.take(e * c.wS());
+  w->Tdot = ar.bytes(e * d.wT() * c.es);
+  w->omega = ar.take(e * 3);
+  w->Udot = ar.take(e * d.wU());
+  w->Zdot = ar.bytes(e * d.wZ() * c.es);
+  w->Vdot = ar.take(e * d.wZ());
+  w->G2 = ar.bytes(2 * e * d.wZ() * c.es);
+  w->ZZ = ar.take(2 * e * d.wZ());
+  w->UU = ar.bytes(2 * e * d.wU() * c.es);
+  w->TT = ar.take(2 * e * d.wT());
+  w->Sbar = ar.take(e * c.wS());
+  w->Sdb = ar.take(e * c.wS());
+  w->P = take_partials(ar, c, ec, 2);
+}
+
+// Workspace of one stage for a chunk of `ec` edges out of E.
+//   stage 0: forward; 1: backward; 2: double backward.
+//   recompute: the per-edge forward state lives in the workspace (saved == NULL).
+size_t ws_need(const Ctx& c, int N, long E, long ec, int stage, bool recompute) {
+  Arena ar{nullptr, 0};
+  if (stage == 0) {
+    FwdWs w;
+    layout_fwd(ar, c, N, ec, recompute, &w);
+  } else if (stage == 1) {
+    BwdWs w;
+    layout_bwd(ar, c, N, E, ec, recompute, &w);
+  } else {
+    DbwdWs w;
+    layout_dbwd(ar, c, N, ec, recompute, &w);
+  }
+  return ar.used + 4096;
+}
+
+// edges per chunk that fit in ws_bytes (E if everything fits; 0 if not even 1024 edges do)
+long pick_chunk(const Ctx& c, int N, long E, int stage, bool recompute, size_t ws_bytes) {
+  if (E == 0) return 0;
+  if (ws_need(c, N, E, E, stage, recompute) <= ws_bytes) return E;
+  long lo = 0, hi = E;
+  while (hi - lo > 1024) {
+    const long mid = (lo + hi) / 2 / 1024 * 1024;
+    if (mid <= lo) break;
+    if (ws_need(c, N, E, mid, stage, recompute) <= ws_bytes) lo = mid;
+    else hi = mid;
+  }
+  if (lo == 0 && ws_need(c, N, E, 1024 < E ? 1024 : E, stage, recompute) <= ws_bytes) lo = 1024 < E ? 1024 : E;
+  return lo;
+}
 
 // ---------------------------------------------------------------- gemm helpers
-GemmProb prob(const float* A, int lda, const float* B, int ldb, float* C, int ldc, int M, int N, int K, int acc = 0) {
+GemmProb prob(const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N, int K, int acc = 0) {
   GemmProb p{};
   p.A = A; p.B = B; p.C = C;
   p.M = M; p.N = N; p.K = K;
@@ -174,12 +387,15 @@ GemmProb prob(const float* A, int lda, const float* B, int ldb, float* C, int ld
   return p;
 }
 
+const void* offs(const void* p, size_t elems, int es) { return static_cast<const char*>(p) + elems * es; }
+void* offs(void* p, size_t elems, int es) { return static_cast<char*>(p) + elems * es; }
+
 // ---------------------------------------------------------------- GEMM timing
 // When enabled, every MFMA GEMM launch is bracketed by HIP events on the
 // launching stream and its algorithmic flop count (2 M N K summed over the
 // launch's problems) is recorded; so2conv_profile_read reports the totals.
 struct ProfRec {
-  int kind;          // 0 NN, 1 NT, 2 TN
+  int kind;          // 0 NN, 1 NT, 2 TN (float32); 3 NT, 4 TN (bfloat16)
   double flops;
   double bytes;      // algorithmic: A, B read once, C (or the split partials) written once
   hipEvent_t a, b;
@@ -188,7 +404,8 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 
-int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, hipStream_t s) {
+int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int bf, hipStream_t s) {
+  const double es = bf ? 2.0 : 4.0;
   size_t i = 0;
   while (i < ps.size()) {
     GemmBatch b{};
@@ -197,21 +414,21 @@ int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, hipStream_t s) {
     while (i < ps.size() && b.nprob < kGemmMaxProbs) {
       const GemmProb& q = ps[i];
       flops += 2.0 * q.M * (double)q.N * q.K;
-      bytes += 4.0 * ((double)q.M * q.K + (double)q.K * q.N +
-                      (double)q.M * q.N * (q.partial ? q.k_splits : 1) * (q.accumulate ? 2 : 1));
+      bytes += es * ((double)q.M * q.K + (double)q.K * q.N) +
+               4.0 * (double)q.M * q.N * (q.partial ? q.k_splits : 1) * (q.accumulate ? 2 : 1);
       b.p[b.nprob++] = ps[i++];
     }
     if (g_prof_on) {
-      ProfRec r{TA ? 2 : (TB ? 1 : 0), flops, bytes, nullptr, nullptr};
+      ProfRec r{bf ? (TA ? 4 : 3) : (TA ? 2 : (TB ? 1 : 0)), flops, bytes, nullptr, nullptr};
       SO2_HIP(hipEventCreate(&r.a));
       SO2_HIP(hipEventCreate(&r.b));
       SO2_HIP(hipEventRecord(r.a, s));
-      SO2_HIP(gemm_run(b, TA, TB, s));
+      SO2_HIP(gemm_run(b, TA, TB, bf != 0, s));
       SO2_HIP(hipEventRecord(r.b, s));
       std::lock_guard<std::mutex> lk(g_prof_mu);
       g_prof.push_back(r);
     } else {
-      SO2_HIP(gemm_run(b, TA, TB, s));
+      SO2_HIP(gemm_run(b, TA, TB, bf != 0, s));
     }
   }
   return SO2_OK;
@@ -220,18 +437,14 @@ int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, hipStream_t s) {
 // Weight gradient G[M][N] (+)= sum over segments of A_s^T B_s, A_s [K_s][lda], B_s [K_s][ldb];
 // deterministic split-K through the partial buffer P.
 struct TnSeg {
-  const float* A;
+  const void* A;
   int lda;
-  const float* B;
+  const void* B;
   int ldb;
   long K;
 };
-size_t tn_partial_floats(long K_total_rows, int nseg, int M, int N) {
-  int sp, ch;
-  split_plan(K_total_rows, &sp, &ch);
-  return (size_t)(sp + nseg) * M * N;
-}
-int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int accumulate, float* P, hipStream_t s) {
+int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int accumulate, float* P, int bf,
+           hipStream_t s) {
   std::vector<GemmProb> ps;
   int total_splits = 0;
   for (int q = 0; q < nseg; ++q) {
@@ -247,7 +460,7 @@ int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int acc
     ps.push_back(p);
   }
   if (total_splits == 0) return SO2_OK;
-  int r = run_batch(ps, true, false, s);
+  int r = run_batch(ps, true, false, bf, s);
   if (r) return r;
   SO2_HIP(gemm_reduce(P, total_splits, M, N, G, ldg, accumulate, s));
   return SO2_OK;
@@ -255,6 +468,9 @@ int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int acc
 
 __global__ void fill_kernel(float* p, size_t n, float v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+__global__ void fill16_kernel(unsigned short* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 int fill(float* p, size_t n, hipStream_t s) {
   if (n == 0) return SO2_OK;
@@ -264,57 +480,103 @@ int fill(float* p, size_t n, hipStream_t s) {
   SO2_HIP(hipGetLastError());
   return SO2_OK;
 }
-
-// S = rbf W_rad
-int radial(const Dims& d, int n_rbf, long E, const float* rbf, const float* w_rad, float* S, hipStream_t s, int acc = 0) {
-  std::vector<GemmProb> ps{prob(rbf, n_rbf, w_rad, (d.L + 1) * d.Ci(), S, (d.L + 1) * d.Ci(), (int)E,
-                                (d.L + 1) * d.Ci(), n_rbf, acc)};
-  return run_batch(ps, false, false, s);
+// zero n elements of the boundary type
+int zero(const Ctx& c, void* p, size_t n, hipStream_t s) {
+  if (!c.bf) return fill(static_cast<float*>(p), n, s);
+  if (n == 0) return SO2_OK;
+  size_t b = (n + 255) / 256;
+  if (b > 16384) b = 16384;
+  hipLaunchKernelGGL(fill16_kernel, dim3((unsigned)b), dim3(256), 0, s, static_cast<unsigned short*>(p), n);
+  SO2_HIP(hipGetLastError());
+  return SO2_OK;
 }
 
-// first linear: U[:, block a] = T[:, block a] W1r_a  (rows = E * rowmul stacked)
-void lin1_probs(const Dims& d, const float* T, const float* W1r, float* U, int rows, int acc, std::vector<GemmProb>& ps) {
-  for (int a = 0; a <= d.M; ++a) {
-    int r, c;
-    long off;
-    realified_shape(d, 0, a, &r, &c, &off);
-    ps.push_back(prob(T + mm_block(a, d.L, d.Ci()), d.wT(), W1r + off, c, U + d.u_block(a), d.wU(), rows, c, r, acc));
+// float32 view of a boundary input: itself, or its conversion into `tmp`
+int f32_in(const Ctx& c, const void* in, float* tmp, size_t n, const float** out, hipStream_t s) {
+  if (!in) {
+    *out = nullptr;
+    return SO2_OK;
   }
+  if (!c.bf) {
+    *out = static_cast<const float*>(in);
+    return SO2_OK;
+  }
+  SO2_HIP(launch_to_f32(static_cast<const bf16s*>(in), tmp, n, s));
+  *out = tmp;
+  return SO2_OK;
 }
-void lin2_probs(const Dims& d, const float* Z, const float* W2r, float* V, int rows, int acc, std::vector<GemmProb>& ps) {
-  for (int a = 0; a <= d.M; ++a) {
-    int r, c;
-    long off;
-    realified_shape(d, 1, a, &r, &c, &off);
-    ps.push_back(prob(Z + mm_block(a, d.L, d.C), d.wZ(), W2r + off, c, V + mm_block(a, d.L, d.C), d.wZ(), rows, c, r, acc));
-  }
+// float32 accumulator of a boundary output: itself, or `tmp` (copied back by f32_out)
+float* f32_acc(const Ctx& c, void* out, float* tmp) {
+  if (!out) return nullptr;
+  return c.bf ? tmp : static_cast<float*>(out);
 }
-// transposed products: Tbar[:, a] = Ubar[:, a] W1r_a^T
-void lin1t_probs(const Dims& d, const float* Ub, const float* W1r, float* Tb, int rows, int acc, std::vector<GemmProb>& ps) {
-  for (int a = 0; a <= d.M; ++a) {
-    int r, c;
-    long off;
-    realified_shape(d, 0, a, &r, &c, &off);
-    ps.push_back(prob(Ub + d.u_block(a), d.wU(), W1r + off, c, Tb + mm_block(a, d.L, d.Ci()), d.wT(), rows, r, c, acc));
-  }
-}
-void lin2t_probs(const Dims& d, const float* Vb, const float* W2r, float* Zb, int rows, int acc, std::vector<GemmProb>& ps) {
-  for (int a = 0; a <= d.M; ++a) {
-    int r, c;
-    long off;
-    realified_shape(d, 1, a, &r, &c, &off);
-    ps.push_back(prob(Vb + mm_block(a, d.L, d.C), d.wZ(), W2r + off, c, Zb + mm_block(a, d.L, d.C), d.wZ(), rows, r, c, acc));
-  }
+int f32_out(const Ctx& c, const float* tmp, void* out, size_t n, hipStream_t s) {
+  if (!out || !c.bf) return SO2_OK;
+  SO2_HIP(launch_to_bf16(tmp, static_cast<bf16s*>(out), n, s));
+  return SO2_OK;
 }
 
-bool all_null(const float* const* p, int n) {
+// S = rbf W_rad (float32)
+int radial(const Ctx& c, long E, const float* rbf, const float* w_rad, float* S, hipStream_t s, int acc = 0) {
+  std::vector<GemmProb> ps{prob(rbf, c.n_rbf, w_rad, c.wS(), S, c.wS(), (int)E, c.wS(), c.n_rbf, acc)};
+  return run_batch(ps, false, false, 0, s);
+}
+
+// Per-order products of linear `second` (0: first, 1: second), one problem per order:
+//   forward   : C[:, out block a] (+)= A[:, in block a]  W_a
+//   transposed: C[:, in block a]  (+)= A[:, out block a] W_a^T
+// In-blocks: T (first, width wT) or Z (second, width wZ); out-blocks: U (first,
+// width wU) or V (second, width wZ). A is an operand buffer, C float32.
+int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, const Lin& w, int rows, int acc,
+            hipStream_t s) {
+  const Dims& d = c.d;
+  const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
+  std::vector<GemmProb> ps;
+  for (int a = 0; a <= d.M; ++a) {
+    int r, cc;
+    long off;
+    realified_shape(d, second, a, &r, &cc, &off);
+    const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
+    const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+    if (!transposed) {
+      if (c.bf)
+        ps.push_back(prob(offs(A, ib, c.es), win, offs(w.WT, off, c.es), r, C + ob, wout, rows, cc, r, acc));
+      else
+        ps.push_back(prob(offs(A, ib, c.es), win, offs(w.W, off, c.es), cc, C + ob, wout, rows, cc, r, acc));
+    } else {
+      ps.push_back(prob(offs(A, ob, c.es), wout, offs(w.W, off, c.es), cc, C + ib, win, rows, r, cc, acc));
+    }
+  }
+  return run_batch(ps, false, transposed || c.bf, c.bf, s);
+}
+
+// weight gradient of linear `second` (realified, float32): G_a (+)= sum_s In_s[:, in a]^T Out_s[:, out a]
+int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* const* out, const long* rows, int nseg,
+                 float* G, int acc, float* P, hipStream_t s) {
+  const Dims& d = c.d;
+  const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
+  for (int a = 0; a <= d.M; ++a) {
+    int r, cc;
+    long off;
+    realified_shape(d, second, a, &r, &cc, &off);
+    const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
+    const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+    TnSeg segs[2];
+    for (int q = 0; q < nseg; ++q) segs[q] = {offs(in[q], ib, c.es), win, offs(out[q], ob, c.es), wout, rows[q]};
+    int rr = run_tn(segs, nseg, r, cc, G + off, cc, acc, P, c.bf, s);
+    if (rr) return rr;
+  }
+  return SO2_OK;
+}
+
+bool all_null(const void* const* p, int n) {
   if (!p) return true;
   for (int i = 0; i < n; ++i)
     if (p[i]) return false;
   return true;
 }
 
-int check_weights(const Dims& d, const float* w_rad, const float* const* w1, const float* const* w2) {
+int check_weights(const Dims& d, const void* w_rad, const void* const* w1, const void* const* w2) {
   if (!w_rad) return fail(SO2_EINVAL, "w_rad is NULL");
   if (!w1 || !w2) return fail(SO2_EINVAL, "weight pointer arrays are NULL");
   for (int a = 0; a <= d.M; ++a)
@@ -322,103 +584,38 @@ int check_weights(const Dims& d, const float* w_rad, const float* const* w1, con
   return SO2_OK;
 }
 
-size_t ws_weights(const Dims& d) {
-  return al(sizeof(float) * realified_size(d, 0)) + al(sizeof(float) * realified_size(d, 1));
+int realify(const Ctx& c, int second, const void* const* w, const LinBuf& b, hipStream_t s) {
+  SO2_HIP(launch_realify(c.d, second, w, b.W, b.WT, c.bf, s));
+  return SO2_OK;
 }
-
-// largest weight-gradient block (floats): realified blocks and the radial matrix
-size_t max_grad_block(const Dims& d, int n_rbf) {
-  size_t mx = (size_t)n_rbf * (d.L + 1) * d.Ci();
-  for (int second = 0; second < 2; ++second)
-    for (int a = 0; a <= d.M; ++a) {
-      int r, c;
-      long off;
-      realified_shape(d, second, a, &r, &c, &off);
-      if ((size_t)r * c > mx) mx = (size_t)r * c;
-    }
-  return mx;
-}
-
-size_t primal_floats(const Dims& d) { return (size_t)(d.L + 1) * d.Ci() + d.wT() + d.wU() + 2 * (size_t)d.wZ(); }
-
-// Workspace of one stage for a chunk of `ec` edges out of E.
-//   stage 0: forward; 1: backward; 2: double backward.
-//   recompute: the per-edge forward state lives in the workspace (saved == NULL).
-size_t ws_need(const Dims& d, int n_rbf, long E, long ec, int stage, bool recompute) {
-  const size_t e = (size_t)ec;
-  const size_t wS = (size_t)(d.L + 1) * d.Ci();
-  size_t b = ws_weights(d);
-  size_t per = recompute ? primal_floats(d) : 0;
-  int nseg = 1;
-  if (stage == 1) {
-    per += 2 * (size_t)d.wZ() + d.wU() + d.wT() + wS + 9;
-    b += ws_weights(d);                               // realified weight gradients
-    b += al(sizeof(float) * 3 * (size_t)E);           // per-edge position gradient (all edges)
-  } else if (stage == 2) {
-    b += 2 * ws_weights(d);                           // direction weights, weight gradients
-    per += wS + d.wT() + 3 + d.wU() + 2 * (size_t)d.wZ() + 4 * (size_t)d.wZ() + 2 * (size_t)d.wU() +
-           2 * (size_t)d.wT() + 2 * wS;
-    nseg = 2;
-  }
-  b += 24 * 256 + sizeof(float) * per * e;           // per-edge buffers (+ alignment)
-  if (stage > 0) {
-    int sp, ch;
-    split_plan(ec, &sp, &ch);
-    b += al(sizeof(float) * (size_t)nseg * (sp + 1) * max_grad_block(d, n_rbf));
-  }
-  return b + 4096;
-}
-
-// edges per chunk that fit in ws_bytes (E if everything fits; 0 if not even 1024 edges do)
-long pick_chunk(const Dims& d, int n_rbf, long E, int stage, bool recompute, size_t ws_bytes) {
-  if (E == 0) return 0;
-  if (ws_need(d, n_rbf, E, E, stage, recompute) <= ws_bytes) return E;
-  long lo = 0, hi = E;
-  while (hi - lo > 1024) {
-    const long mid = (lo + hi) / 2 / 1024 * 1024;
-    if (mid <= lo) break;
-    if (ws_need(d, n_rbf, E, mid, stage, recompute) <= ws_bytes) lo = mid;
-    else hi = mid;
-  }
-  if (lo == 0 && ws_need(d, n_rbf, E, 1024 < E ? 1024 : E, stage, recompute) <= ws_bytes) lo = 1024 < E ? 1024 : E;
-  return lo;
-}
-
-struct Primal {
-  const float *S, *T, *U, *Z, *V;
-};
+Lin lin_of(const LinBuf& b) { return Lin{b.W, b.WT}; }
 
 // forward state of the chunk [g.e0, g.e1) into (S, T, U, Z, V)
-int forward_chunk(const Dims& d, int n_rbf, const GraphDev& g, const float* x, const float* pos, const float* rbf,
-                  const float* w_rad, const float* W1r, const float* W2r, float* S, float* T, float* U, float* Z,
-                  float* V, hipStream_t s) {
+int forward_chunk(const Ctx& c, const GraphDev& g, const float* x, const float* pos, const float* rbf,
+                  const float* w_rad, const Lin& W1, const Lin& W2, const PrimalBuf& p, hipStream_t s) {
   const int ec = (int)(g.e1 - g.e0);
   int r;
-  if ((r = radial(d, n_rbf, ec, rbf + (size_t)g.e0 * n_rbf, w_rad, S, s))) return r;
-  SO2_HIP(launch_edge_fwd(d, g, x, pos, S, T, s));
-  std::vector<GemmProb> ps;
-  lin1_probs(d, T, W1r, U, ec, 0, ps);
-  if ((r = run_batch(ps, false, false, s))) return r;
-  SO2_HIP(launch_gate_fwd(d, ec, U, Z, s));
-  ps.clear();
-  lin2_probs(d, Z, W2r, V, ec, 0, ps);
-  return run_batch(ps, false, false, s);
+  if ((r = radial(c, ec, rbf + (size_t)g.e0 * c.n_rbf, w_rad, p.S, s))) return r;
+  SO2_HIP(launch_edge_fwd(c.d, g, x, pos, p.S, p.T, c.bf, s));
+  if ((r = run_lin(c, 0, false, p.T, p.U, W1, ec, 0, s))) return r;
+  SO2_HIP(launch_gate_fwd(c.d, ec, p.U, p.Z, c.bf, s));
+  return run_lin(c, 1, false, p.Z, p.V, W2, ec, 0, s);
 }
 
-int zero_grads(const Dims& d, int n_rbf, int N, float* gx, float* gpos, float* gw_rad, float* const* gw1,
-               float* const* gw2, hipStream_t s) {
+int zero_grads(const Ctx& c, int N, void* gx, float* gpos, void* gw_rad, void* const* gw1, void* const* gw2,
+               hipStream_t s) {
   int r;
-  const size_t dC = (size_t)d.d() * d.C;
-  if (gx && (r = fill(gx, (size_t)N * dC, s))) return r;
+  const Dims& d = c.d;
+  if (gx && (r = zero(c, gx, (size_t)N * c.node_floats(), s))) return r;
   if (gpos && (r = fill(gpos, (size_t)N * 3, s))) return r;
-  if (gw_rad && (r = fill(gw_rad, (size_t)n_rbf * (d.L + 1) * d.Ci(), s))) return r;
+  if (gw_rad && (r = zero(c, gw_rad, (size_t)c.n_rbf * c.wS(), s))) return r;
   for (int a = 0; a <= d.M; ++a) {
     int rr, cc;
     long off;
     realified_shape(d, 0, a, &rr, &cc, &off);
-    if (gw1 && gw1[a] && (r = fill(gw1[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r;
+    if (gw1 && gw1[a] && (r = zero(c, gw1[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r;
     realified_shape(d, 1, a, &rr, &cc, &off);
-    if (gw2 && gw2[a] && (r = fill(gw2[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r;
+    if (gw2 && gw2[a] && (r = zero(c, gw2[a], (size_t)(a ? rr / 2 : rr) * cc, s))) return r;
   }
   return SO2_OK;
 }
@@ -486,226 +683,203 @@ int so2conv_graph_prepare(int32_t n_nodes, int64_t n_edges, const int32_t* src, 
 }
 
 size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges) {
-  Dims d;
-  if (check_cfg(cfg, &d)) return 0;
-  return saved_layout(d, cfg->n_rbf, n_edges).total;
+  Ctx c;
+  if (check_cfg(cfg, &c) || n_edges < 0) return 0;
+  return saved_layout(c, n_edges).total;
 }
 
 size_t so2conv_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage) {
-  (void)n_nodes;
-  Dims d;
-  if (check_cfg(cfg, &d) || stage < 0 || stage > 2) return 0;
-  return ws_need(d, cfg->n_rbf, n_edges, n_edges, stage, false);
+  Ctx c;
+  if (check_cfg(cfg, &c) || stage < 0 || stage > 2 || n_nodes < 0 || n_edges < 0) return 0;
+  return ws_need(c, n_nodes, n_edges, n_edges, stage, false);
 }
 
 size_t so2conv_chunked_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage,
                                        int64_t chunk_edges) {
-  (void)n_nodes;
-  Dims d;
-  if (check_cfg(cfg, &d) || stage < 0 || stage > 2 || chunk_edges < 1) return 0;
+  Ctx c;
+  if (check_cfg(cfg, &c) || stage < 0 || stage > 2 || chunk_edges < 1 || n_nodes < 0 || n_edges < 0) return 0;
   const long ec = chunk_edges < n_edges ? chunk_edges : n_edges;
-  return ws_need(d, cfg->n_rbf, n_edges, ec, stage, true);
+  return ws_need(c, n_nodes, n_edges, ec, stage, true);
 }
 
-int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos,
-                                const float* rbf, const float* w_rad, float* T_out, void* ws, size_t ws_bytes,
+int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos,
+                                const float* rbf, const void* w_rad, void* T_out, void* ws, size_t ws_bytes,
                                 void* stream) {
   g_err.clear();
-  Dims d;
+  Ctx c;
   GraphDev gd;
   int r;
-  if ((r = check_cfg(cfg, &d)) || (r = check_graph(g, &gd))) return r;
+  if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
   if ((r = ensure_init())) return r;
   if (!x || !pos || !rbf || !w_rad || !T_out) return fail(SO2_EINVAL, "NULL input");
-  const size_t need = al(sizeof(float) * (size_t)gd.E * (d.L + 1) * d.Ci());
-  if (!ws || ws_bytes < need) return fail(SO2_EWORKSPACE, "workspace too small (needs E*(L+1)*2C floats)");
+  Arena ar{nullptr, 0};
+  ar.take((size_t)gd.E * c.wS());
+  if (c.bf) {
+    ar.take((size_t)gd.N * c.node_floats());
+    ar.take((size_t)c.n_rbf * c.wS());
+  }
+  if (!ws || ws_bytes < ar.used) return fail(SO2_EWORKSPACE, "workspace too small for the rotate-gather hook");
   hipStream_t s = (hipStream_t)stream;
-  float* S = static_cast<float*>(ws);
-  if ((r = radial(d, cfg->n_rbf, gd.E, rbf, w_rad, S, s))) return r;
-  SO2_HIP(launch_edge_fwd(d, gd, x, pos, S, T_out, s));
+  ar = Arena{static_cast<char*>(ws), 0};
+  float* S = ar.take((size_t)gd.E * c.wS());
+  float* xt = c.bf ? ar.take((size_t)gd.N * c.node_floats()) : nullptr;
+  float* wt = c.bf ? ar.take((size_t)c.n_rbf * c.wS()) : nullptr;
+  const float *x32, *w32;
+  if ((r = f32_in(c, x, xt, (size_t)gd.N * c.node_floats(), &x32, s))) return r;
+  if ((r = f32_in(c, w_rad, wt, (size_t)c.n_rbf * c.wS(), &w32, s))) return r;
+  if ((r = radial(c, gd.E, rbf, w32, S, s))) return r;
+  SO2_HIP(launch_edge_fwd(c.d, gd, x32, pos, S, T_out, c.bf, s));
   return SO2_OK;
 }
 
-int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
-                const float* w_rad, const float* const* w1, const float* const* w2, float* y, void* saved, void* ws,
+int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
+                const void* w_rad, const void* const* w1, const void* const* w2, void* y, void* saved, void* ws,
                 size_t ws_bytes, void* stream) {
   g_err.clear();
-  Dims d;
+  Ctx c;
   GraphDev gd;
   int r;
-  if ((r = check_cfg(cfg, &d)) || (r = check_graph(g, &gd))) return r;
+  if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
+  const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || (!rbf && gd.E > 0) || !y) return fail(SO2_EINVAL, "NULL input or output");
   if ((r = ensure_init())) return r;
-  const int n_rbf = cfg->n_rbf;
   const bool recompute = saved == nullptr;
   if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
-  const long ec = pick_chunk(d, n_rbf, gd.E, 0, recompute, ws_bytes);
+  const long ec = pick_chunk(c, gd.N, gd.E, 0, recompute, ws_bytes);
   if (gd.E > 0 && ec == 0) return fail(SO2_EWORKSPACE, "forward workspace too small for a 1024-edge chunk");
-  if (ws_bytes < ws_weights(d)) return fail(SO2_EWORKSPACE, "forward workspace too small");
+  if (ws_bytes < ws_need(c, gd.N, gd.E, 0, 0, recompute)) return fail(SO2_EWORKSPACE, "forward workspace too small");
   hipStream_t s = (hipStream_t)stream;
   Arena ar{static_cast<char*>(ws), 0};
-  float* W1r = ar.take(realified_size(d, 0));
-  float* W2r = ar.take(realified_size(d, 1));
-  const SavedLayout sl = saved_layout(d, n_rbf, gd.E);
-  char* st = static_cast<char*>(saved);
-  float *S = nullptr, *T = nullptr, *U = nullptr, *Z = nullptr, *V = nullptr;
-  if (recompute) {
-    S = ar.take((size_t)ec * (d.L + 1) * d.Ci());
-    T = ar.take((size_t)ec * d.wT());
-    U = ar.take((size_t)ec * d.wU());
-    Z = ar.take((size_t)ec * d.wZ());
-    V = ar.take((size_t)ec * d.wZ());
-  }
-  SO2_HIP(launch_realify(d, 0, w1, W1r, s));
-  SO2_HIP(launch_realify(d, 1, w2, W2r, s));
+  FwdWs w;
+  layout_fwd(ar, c, gd.N, ec, recompute, &w);
+  const size_t nf = (size_t)gd.N * c.node_floats();
+  const float *x32, *wr32;
+  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
+  if ((r = f32_in(c, w_rad, w.w_rad32, (size_t)c.n_rbf * c.wS(), &wr32, s))) return r;
+  float* y32 = f32_acc(c, y, w.y32);
+  if ((r = realify(c, 0, w1, w.W1, s)) || (r = realify(c, 1, w2, w.W2, s))) return r;
   if (gd.E == 0) {
     GraphDev gc = gd;
     gc.e0 = gc.e1 = 0;
-    SO2_HIP(launch_node_fwd(d, gc, pos, nullptr, y, 0, s));
-    return SO2_OK;
+    SO2_HIP(launch_node_fwd(d, gc, pos, nullptr, y32, 0, s));
+    return f32_out(c, y32, y, nf, s);
   }
-  for (long e0 = 0, c = 0; e0 < gd.E; e0 += ec, ++c) {
+  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
     GraphDev gc = gd;
     gc.e0 = e0;
     gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
-    float *Sc = S, *Tc = T, *Uc = U, *Zc = Z, *Vc = V;
+    PrimalBuf p = w.pr;
     if (!recompute) {
-      Sc = reinterpret_cast<float*>(st + sl.S) + (size_t)e0 * (d.L + 1) * d.Ci();
-      Tc = reinterpret_cast<float*>(st + sl.T) + (size_t)e0 * d.wT();
-      Uc = reinterpret_cast<float*>(st + sl.U) + (size_t)e0 * d.wU();
-      Zc = reinterpret_cast<float*>(st + sl.Z) + (size_t)e0 * d.wZ();
-      Vc = reinterpret_cast<float*>(st + sl.V) + (size_t)e0 * d.wZ();
+      const SavedLayout sl = saved_layout(c, gd.E);
+      char* st = static_cast<char*>(saved);
+      p.S = reinterpret_cast<float*>(st + sl.S) + (size_t)e0 * c.wS();
+      p.T = st + sl.T + (size_t)e0 * d.wT() * c.es;
+      p.U = reinterpret_cast<float*>(st + sl.U) + (size_t)e0 * d.wU();
+      p.Z = st + sl.Z + (size_t)e0 * d.wZ() * c.es;
+      p.V = reinterpret_cast<float*>(st + sl.V) + (size_t)e0 * d.wZ();
     }
-    if ((r = forward_chunk(d, n_rbf, gc, x, pos, rbf, w_rad, W1r, W2r, Sc, Tc, Uc, Zc, Vc, s))) return r;
-    SO2_HIP(launch_node_fwd(d, gc, pos, Vc, y, c > 0, s));
+    if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, lin_of(w.W1), lin_of(w.W2), p, s))) return r;
+    SO2_HIP(launch_node_fwd(d, gc, pos, p.V, y32, k > 0, s));
   }
-  return SO2_OK;
+  return f32_out(c, y32, y, nf, s);
 }
 
-int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
-                const float* w_rad, const float* const* w1, const float* const* w2, const void* saved,
-                const float* gy, float* gx, float* gpos, float* grbf, float* gw_rad, float* const* gw1,
-                float* const* gw2, float* gedge, void* ws, size_t ws_bytes, void* stream) {
+int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
+                const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
+                void* gx, float* gpos, float* grbf, void* gw_rad, void* const* gw1, void* const* gw2, float* gedge,
+                void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
-  Dims d;
+  Ctx c;
   GraphDev gd;
   int r;
-  if ((r = check_cfg(cfg, &d)) || (r = check_graph(g, &gd))) return r;
+  if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
+  const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
   if ((r = ensure_init())) return r;
   hipStream_t s = (hipStream_t)stream;
-  const int n_rbf = cfg->n_rbf, wS = (d.L + 1) * d.Ci();
-  if (gd.E == 0) return zero_grads(d, n_rbf, gd.N, gx, gpos, gw_rad, gw1, gw2, s);
+  const int n_rbf = c.n_rbf, wS = c.wS();
+  if (gd.E == 0) return zero_grads(c, gd.N, gx, gpos, gw_rad, gw1, gw2, s);
   const bool recompute = saved == nullptr;
   if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
-  const long ec = pick_chunk(d, n_rbf, gd.E, 1, recompute, ws_bytes);
+  const long ec = pick_chunk(c, gd.N, gd.E, 1, recompute, ws_bytes);
   if (ec == 0) return fail(SO2_EWORKSPACE, "backward workspace too small for a 1024-edge chunk");
-  const SavedLayout sl = saved_layout(d, n_rbf, gd.E);
-  const char* st = static_cast<const char*>(saved);
   Arena ar{static_cast<char*>(ws), 0};
-  float* W1r = ar.take(realified_size(d, 0));
-  float* W2r = ar.take(realified_size(d, 1));
-  float* gW1r = ar.take(realified_size(d, 0));
-  float* gW2r = ar.take(realified_size(d, 1));
-  float* vbar_all = ar.take((size_t)gd.E * 3);
-  float *S = nullptr, *T = nullptr, *U = nullptr, *Z = nullptr, *V = nullptr;
-  if (recompute) {
-    S = ar.take((size_t)ec * wS);
-    T = ar.take((size_t)ec * d.wT());
-    U = ar.take((size_t)ec * d.wU());
-    Z = ar.take((size_t)ec * d.wZ());
-    V = ar.take((size_t)ec * d.wZ());
-  }
-  float* tbar = ar.take((size_t)ec * d.wZ());
-  float* Zbar = ar.take((size_t)ec * d.wZ());
-  float* Ubar = ar.take((size_t)ec * d.wU());
-  float* Tbar = ar.take((size_t)ec * d.wT());
-  float* Sbar = ar.take((size_t)ec * wS);
-  float* tau1 = ar.take((size_t)ec * 3);
-  float* tau2 = ar.take((size_t)ec * 3);
-  float* tau3 = ar.take((size_t)ec * 3);
-  float* P = ar.take(0);
-  float* vbar = gedge ? gedge : vbar_all;
+  BwdWs w;
+  layout_bwd(ar, c, gd.N, gd.E, ec, recompute, &w);
+  const size_t nf = (size_t)gd.N * c.node_floats();
+  const float *x32, *gy32, *wr32;
+  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
+  if ((r = f32_in(c, gy, w.gy32, nf, &gy32, s))) return r;
+  if ((r = f32_in(c, w_rad, w.w_rad32, (size_t)n_rbf * wS, &wr32, s))) return r;
+  float* gx_acc = f32_acc(c, gx, w.gx32);
+  float* gwr_acc = f32_acc(c, gw_rad, w.gw_rad32);
+  float* vbar = gedge ? gedge : w.vbar_all;
   const bool want_w1 = !all_null(gw1, d.M + 1), want_w2 = !all_null(gw2, d.M + 1);
+  const Lin W1 = lin_of(w.W1), W2 = lin_of(w.W2);
 
-  SO2_HIP(launch_realify(d, 0, w1, W1r, s));
-  SO2_HIP(launch_realify(d, 1, w2, W2r, s));
-  for (long e0 = 0, c = 0; e0 < gd.E; e0 += ec, ++c) {
+  if ((r = realify(c, 0, w1, w.W1, s)) || (r = realify(c, 1, w2, w.W2, s))) return r;
+  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
     GraphDev gc = gd;
     gc.e0 = e0;
     gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
     const int n = (int)(gc.e1 - gc.e0);
-    const int acc = c > 0;
+    const int acc = k > 0;
     Primal pr;
     if (recompute) {
-      if ((r = forward_chunk(d, n_rbf, gc, x, pos, rbf, w_rad, W1r, W2r, S, T, U, Z, V, s))) return r;
-      pr = {S, T, U, Z, V};
+      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
+      pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
     } else {
-      pr = {reinterpret_cast<const float*>(st + sl.S) + (size_t)e0 * wS,
-            reinterpret_cast<const float*>(st + sl.T) + (size_t)e0 * d.wT(),
-            reinterpret_cast<const float*>(st + sl.U) + (size_t)e0 * d.wU(),
-            reinterpret_cast<const float*>(st + sl.Z) + (size_t)e0 * d.wZ(),
-            reinterpret_cast<const float*>(st + sl.V) + (size_t)e0 * d.wZ()};
+      pr = saved_rows(c, saved, gd.E, e0);
     }
     // E -> N transpose: tbar = R gy[dst], tau1 = rotation torque of <V, R gy>
-    SO2_HIP(launch_edge_bwd(d, gc, pos, gy, pr.V, tbar, tau1, s));
-    std::vector<GemmProb> ps;
-    lin2t_probs(d, tbar, W2r, Zbar, n, 0, ps);
-    if ((r = run_batch(ps, false, true, s))) return r;
+    SO2_HIP(launch_edge_bwd(d, gc, pos, gy32, pr.V, w.tbar, w.tau1, c.bf, s));
+    if ((r = run_lin(c, 1, true, w.tbar, w.Zbar, W2, n, 0, s))) return r;
     if (want_w2) {
-      for (int a = 0; a <= d.M; ++a) {
-        int rr, cc;
-        long off;
-        realified_shape(d, 1, a, &rr, &cc, &off);
-        TnSeg seg{pr.Z + mm_block(a, d.L, d.C), d.wZ(), tbar + mm_block(a, d.L, d.C), d.wZ(), n};
-        if ((r = run_tn(&seg, 1, rr, cc, gW2r + off, cc, acc, P, s))) return r;
-      }
+      const void* in[1] = {pr.Z};
+      const void* out[1] = {w.tbar};
+      const long rows[1] = {n};
+      if ((r = run_lin_grad(c, 1, in, out, rows, 1, w.gW2r, acc, w.P, s))) return r;
     }
-    SO2_HIP(launch_gate_bwd(d, n, pr.U, Zbar, Ubar, s));
-    ps.clear();
-    lin1t_probs(d, Ubar, W1r, Tbar, n, 0, ps);
-    if ((r = run_batch(ps, false, true, s))) return r;
+    SO2_HIP(launch_gate_bwd(d, n, pr.U, w.Zbar, w.Ubar, c.bf, s));
+    if ((r = run_lin(c, 0, true, w.Ubar, w.Tbar, W1, n, 0, s))) return r;
     if (want_w1) {
-      for (int a = 0; a <= d.M; ++a) {
-        int rr, cc;
-        long off;
-        realified_shape(d, 0, a, &rr, &cc, &off);
-        TnSeg seg{pr.T + mm_block(a, d.L, d.Ci()), d.wT(), Ubar + d.u_block(a), d.wU(), n};
-        if ((r = run_tn(&seg, 1, rr, cc, gW1r + off, cc, acc, P, s))) return r;
-      }
+      const void* in[1] = {pr.T};
+      const void* out[1] = {w.Ubar};
+      const long rows[1] = {n};
+      if ((r = run_lin_grad(c, 0, in, out, rows, 1, w.gW1r, acc, w.P, s))) return r;
     }
     // N -> E transpose: gx (both halves), Sbar, position torques
-    SO2_HIP(launch_node_bwd(d, gc, x, pos, pr.S, Tbar, gx, Sbar, tau2, tau3, acc, s));
+    SO2_HIP(launch_node_bwd(d, gc, x32, pos, pr.S, w.Tbar, gx_acc, w.Sbar, w.tau2, w.tau3, acc, s));
     if (grbf) {
-      ps.clear();
-      ps.push_back(prob(Sbar, wS, w_rad, wS, grbf + (size_t)e0 * n_rbf, n_rbf, n, n_rbf, wS));
-      if ((r = run_batch(ps, false, true, s))) return r;
+      std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, grbf + (size_t)e0 * n_rbf, n_rbf, n, n_rbf, wS)};
+      if ((r = run_batch(ps, false, true, 0, s))) return r;
     }
-    if (gw_rad) {
-      TnSeg seg{rbf + (size_t)e0 * n_rbf, n_rbf, Sbar, wS, n};
-      if ((r = run_tn(&seg, 1, n_rbf, wS, gw_rad, wS, acc, P, s))) return r;
+    if (gwr_acc) {
+      TnSeg seg{rbf + (size_t)e0 * n_rbf, n_rbf, w.Sbar, wS, n};
+      if ((r = run_tn(&seg, 1, n_rbf, wS, gwr_acc, wS, acc, w.P, 0, s))) return r;
     }
-    if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, tau1, tau2, tau3, vbar, s));
+    if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, w.tau1, w.tau2, w.tau3, vbar, s));
   }
-  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, gW2r, gw2, s));
-  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, gW1r, gw1, s));
+  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r, gw2, c.bf, s));
+  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r, gw1, c.bf, s));
   if (gpos) SO2_HIP(launch_node_pos(gd, vbar, gpos, s));
-  return SO2_OK;
+  if ((r = f32_out(c, gx_acc, gx, nf, s))) return r;
+  return f32_out(c, gwr_acc, gw_rad, (size_t)n_rbf * wS, s);
 }
 
-int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x, const float* pos, const float* rbf,
-                 const float* w_rad, const float* const* w1, const float* const* w2, const void* saved,
-                 const float* gy, const float* px, const float* ppos, const float* pedge, const float* prbf,
-                 const float* pw_rad, const float* const* pw1, const float* const* pw2, float* ggy, float* gx2,
-                 float* gpos2, float* grbf2, float* gw_rad2, float* const* gw1_2, float* const* gw2_2, void* ws,
-                 size_t ws_bytes, void* stream) {
+int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
+                 const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
+                 const void* px, const float* ppos, const float* pedge, const float* prbf, const void* pw_rad,
+                 const void* const* pw1, const void* const* pw2, void* ggy, void* gx2, float* gpos2, float* grbf2,
+                 void* gw_rad2, void* const* gw1_2, void* const* gw2_2, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
-  Dims d;
+  Ctx c;
   GraphDev gd;
   int r;
-  if ((r = check_cfg(cfg, &d)) || (r = check_graph(g, &gd))) return r;
+  if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
+  const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
   if (gpos2) return fail(SO2_EUNSUPPORTED, "gpos2 (position second derivatives) is not provided; pass NULL");
@@ -718,164 +892,113 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const float* x,
     for (int a = 0; a <= d.M; ++a)
       if (!pw2[a]) return fail(SO2_EINVAL, "pw2 must be NULL or hold M+1 non-NULL blocks");
   hipStream_t s = (hipStream_t)stream;
-  const int n_rbf = cfg->n_rbf, wS = (d.L + 1) * d.Ci();
+  const int n_rbf = c.n_rbf, wS = c.wS();
   if (gd.E == 0) {
-    int rr = zero_grads(d, n_rbf, gd.N, gx2, nullptr, gw_rad2, gw1_2, gw2_2, s);
+    int rr = zero_grads(c, gd.N, gx2, nullptr, gw_rad2, gw1_2, gw2_2, s);
     if (rr) return rr;
-    if (ggy) return fill(ggy, (size_t)gd.N * d.d() * d.C, s);
+    if (ggy) return zero(c, ggy, (size_t)gd.N * c.node_floats(), s);
     return SO2_OK;
   }
   const bool recompute = saved == nullptr;
   if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
-  const long ec = pick_chunk(d, n_rbf, gd.E, 2, recompute, ws_bytes);
+  const long ec = pick_chunk(c, gd.N, gd.E, 2, recompute, ws_bytes);
   if (ec == 0) return fail(SO2_EWORKSPACE, "double-backward workspace too small for a 1024-edge chunk");
-  const SavedLayout sl = saved_layout(d, n_rbf, gd.E);
-  const char* st = static_cast<const char*>(saved);
   Arena ar{static_cast<char*>(ws), 0};
-  float* W1r = ar.take(realified_size(d, 0));
-  float* W2r = ar.take(realified_size(d, 1));
-  float* pW1r = ar.take(realified_size(d, 0));
-  float* pW2r = ar.take(realified_size(d, 1));
-  float* gW1r = ar.take(realified_size(d, 0));
-  float* gW2r = ar.take(realified_size(d, 1));
-  float *S = nullptr, *T = nullptr, *U = nullptr, *Z = nullptr, *V = nullptr;
-  if (recompute) {
-    S = ar.take((size_t)ec * wS);
-    T = ar.take((size_t)ec * d.wT());
-    U = ar.take((size_t)ec * d.wU());
-    Z = ar.take((size_t)ec * d.wZ());
-    V = ar.take((size_t)ec * d.wZ());
-  }
-  float* Sdot = ar.take((size_t)ec * wS);
-  float* Tdot = ar.take((size_t)ec * d.wT());
-  float* omega = ar.take((size_t)ec * 3);
-  float* Udot = ar.take((size_t)ec * d.wU());
-  float* Zdot = ar.take((size_t)ec * d.wZ());
-  float* Vdot = ar.take((size_t)ec * d.wZ());
-  float* G2 = ar.take((size_t)2 * ec * d.wZ());
-  float* ZZ = ar.take((size_t)2 * ec * d.wZ());
-  float* UU = ar.take((size_t)2 * ec * d.wU());
-  float* TT = ar.take((size_t)2 * ec * d.wT());
-  float* Sbar = ar.take((size_t)ec * wS);
-  float* Sdb = ar.take((size_t)ec * wS);
-  float* P = ar.take(0);
+  DbwdWs w;
+  layout_dbwd(ar, c, gd.N, ec, recompute, &w);
+  const size_t nf = (size_t)gd.N * c.node_floats(), rf = (size_t)n_rbf * wS;
+  const float *x32, *px32, *gy32, *wr32, *pwr32;
+  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
+  if ((r = f32_in(c, px, w.px32, nf, &px32, s))) return r;
+  if ((r = f32_in(c, gy, w.gy32, nf, &gy32, s))) return r;
+  if ((r = f32_in(c, w_rad, w.w_rad32, rf, &wr32, s))) return r;
+  if ((r = f32_in(c, pw_rad, w.pw_rad32, rf, &pwr32, s))) return r;
+  float* ggy_acc = f32_acc(c, ggy, w.ggy32);
+  float* gx2_acc = f32_acc(c, gx2, w.gx2_32);
+  float* gwr2_acc = f32_acc(c, gw_rad2, w.gw_rad2_32);
   const bool want_w1 = !all_null(gw1_2, d.M + 1), want_w2 = !all_null(gw2_2, d.M + 1);
+  const Lin W1 = lin_of(w.W1), W2 = lin_of(w.W2), pW1 = lin_of(w.pW1), pW2 = lin_of(w.pW2);
 
-  SO2_HIP(launch_realify(d, 0, w1, W1r, s));
-  SO2_HIP(launch_realify(d, 1, w2, W2r, s));
-  if (has_pw1) SO2_HIP(launch_realify(d, 0, pw1, pW1r, s));
-  if (has_pw2) SO2_HIP(launch_realify(d, 1, pw2, pW2r, s));
-  for (long e0 = 0, c = 0; e0 < gd.E; e0 += ec, ++c) {
+  if ((r = realify(c, 0, w1, w.W1, s)) || (r = realify(c, 1, w2, w.W2, s))) return r;
+  if (has_pw1 && (r = realify(c, 0, pw1, w.pW1, s))) return r;
+  if (has_pw2 && (r = realify(c, 1, pw2, w.pW2, s))) return r;
+  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
     GraphDev gc = gd;
     gc.e0 = e0;
     gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
     const int n = (int)(gc.e1 - gc.e0);
-    const int acc = c > 0;
+    const int acc = k > 0;
     const float* rbf_c = rbf + (size_t)e0 * n_rbf;
     const float* prbf_c = prbf ? prbf + (size_t)e0 * n_rbf : nullptr;
     Primal pr;
     if (recompute) {
-      if ((r = forward_chunk(d, n_rbf, gc, x, pos, rbf, w_rad, W1r, W2r, S, T, U, Z, V, s))) return r;
-      pr = {S, T, U, Z, V};
+      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
+      pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
     } else {
-      pr = {reinterpret_cast<const float*>(st + sl.S) + (size_t)e0 * wS,
-            reinterpret_cast<const float*>(st + sl.T) + (size_t)e0 * d.wT(),
-            reinterpret_cast<const float*>(st + sl.U) + (size_t)e0 * d.wU(),
-            reinterpret_cast<const float*>(st + sl.Z) + (size_t)e0 * d.wZ(),
-            reinterpret_cast<const float*>(st + sl.V) + (size_t)e0 * d.wZ()};
+      pr = saved_rows(c, saved, gd.E, e0);
     }
 
     // ---- tangent (dual) forward along (px, ppos, pedge, prbf, pW)
     if (prbf_c) {
-      if ((r = radial(d, n_rbf, n, prbf_c, w_rad, Sdot, s))) return r;
-    } else if ((r = fill(Sdot, (size_t)n * wS, s))) {
+      if ((r = radial(c, n, prbf_c, wr32, w.Sdot, s))) return r;
+    } else if ((r = fill(w.Sdot, (size_t)n * wS, s))) {
       return r;
     }
-    if (pw_rad) {
-      if ((r = radial(d, n_rbf, n, rbf_c, pw_rad, Sdot, s, 1))) return r;
+    if (pwr32) {
+      if ((r = radial(c, n, rbf_c, pwr32, w.Sdot, s, 1))) return r;
     }
-    SO2_HIP(launch_edge_dual(d, gc, x, px, pos, ppos, pedge, pr.S, Sdot, Tdot, omega, s));
-    std::vector<GemmProb> ps;
-    lin1_probs(d, Tdot, W1r, Udot, n, 0, ps);
-    if ((r = run_batch(ps, false, false, s))) return r;
-    if (has_pw1) {
-      ps.clear();
-      lin1_probs(d, pr.T, pW1r, Udot, n, 1, ps);
-      if ((r = run_batch(ps, false, false, s))) return r;
-    }
-    SO2_HIP(launch_gate_dual(d, n, pr.U, Udot, Zdot, s));
-    ps.clear();
-    lin2_probs(d, Zdot, W2r, Vdot, n, 0, ps);
-    if ((r = run_batch(ps, false, false, s))) return r;
-    if (has_pw2) {
-      ps.clear();
-      lin2_probs(d, pr.Z, pW2r, Vdot, n, 1, ps);
-      if ((r = run_batch(ps, false, false, s))) return r;
-    }
+    SO2_HIP(launch_edge_dual(d, gc, x32, px32, pos, ppos, pedge, pr.S, w.Sdot, w.Tdot, w.omega, c.bf, s));
+    if ((r = run_lin(c, 0, false, w.Tdot, w.Udot, W1, n, 0, s))) return r;
+    if (has_pw1 && (r = run_lin(c, 0, false, pr.T, w.Udot, pW1, n, 1, s))) return r;
+    SO2_HIP(launch_gate_dual(d, n, pr.U, w.Udot, w.Zdot, c.bf, s));
+    if ((r = run_lin(c, 1, false, w.Zdot, w.Vdot, W2, n, 0, s))) return r;
+    if (has_pw2 && (r = run_lin(c, 1, false, pr.Z, w.Vdot, pW2, n, 1, s))) return r;
     // dL/dgy = the forward's directional derivative (Eq.(5))
-    if (ggy) SO2_HIP(launch_node_dual(d, gc, pos, omega, pr.V, Vdot, ggy, acc, s));
+    if (ggy_acc) SO2_HIP(launch_node_dual(d, gc, pos, w.omega, pr.V, w.Vdot, ggy_acc, acc, s));
 
     // ---- reverse of the tangent output with cotangent gy
-    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, omega, gy, G2, s));
-    ps.clear();
-    lin2t_probs(d, G2, W2r, ZZ, 2 * n, 0, ps);     // [Zdot_bar; Zbar]
-    if ((r = run_batch(ps, false, true, s))) return r;
-    if (has_pw2) {
-      ps.clear();
-      lin2t_probs(d, G2, pW2r, ZZ + (size_t)n * d.wZ(), n, 1, ps);   // Zbar += tbar pW2^T
-      if ((r = run_batch(ps, false, true, s))) return r;
-    }
+    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, s));
+    // [Zdot_bar; Zbar] = G2 W2^T (2n stacked rows)
+    if ((r = run_lin(c, 1, true, w.G2, w.ZZ, W2, 2 * n, 0, s))) return r;
+    // Zbar += tbar pW2^T
+    if (has_pw2 && (r = run_lin(c, 1, true, w.G2, w.ZZ + (size_t)n * d.wZ(), pW2, n, 1, s))) return r;
     if (want_w2) {
-      for (int a = 0; a <= d.M; ++a) {
-        int rr, cc;
-        long off;
-        realified_shape(d, 1, a, &rr, &cc, &off);
-        const int bo = mm_block(a, d.L, d.C);
-        TnSeg segs[2] = {{Zdot + bo, d.wZ(), G2 + bo, d.wZ(), n},
-                         {pr.Z + bo, d.wZ(), G2 + (size_t)n * d.wZ() + bo, d.wZ(), n}};
-        if ((r = run_tn(segs, 2, rr, cc, gW2r + off, cc, acc, P, s))) return r;
-      }
+      const void* in[2] = {w.Zdot, pr.Z};
+      const void* out[2] = {w.G2, offs(static_cast<const void*>(w.G2), (size_t)n * d.wZ(), c.es)};
+      const long rows[2] = {n, n};
+      if ((r = run_lin_grad(c, 1, in, out, rows, 2, w.gW2r, acc, w.P, s))) return r;
     }
-    SO2_HIP(launch_gate_dbwd(d, n, pr.U, Udot, ZZ, UU, s));   // [Udot_bar; Ubar]
-    ps.clear();
-    lin1t_probs(d, UU, W1r, TT, 2 * n, 0, ps);      // [Tdot_bar; Tbar]
-    if ((r = run_batch(ps, false, true, s))) return r;
-    if (has_pw1) {
-      ps.clear();
-      lin1t_probs(d, UU, pW1r, TT + (size_t)n * d.wT(), n, 1, ps);   // Tbar += Udot_bar pW1^T
-      if ((r = run_batch(ps, false, true, s))) return r;
-    }
+    SO2_HIP(launch_gate_dbwd(d, n, pr.U, w.Udot, w.ZZ, w.UU, c.bf, s));   // [Udot_bar; Ubar]
+    // [Tdot_bar; Tbar] = UU W1^T
+    if ((r = run_lin(c, 0, true, w.UU, w.TT, W1, 2 * n, 0, s))) return r;
+    // Tbar += Udot_bar pW1^T
+    if (has_pw1 && (r = run_lin(c, 0, true, w.UU, w.TT + (size_t)n * d.wT(), pW1, n, 1, s))) return r;
     if (want_w1) {
-      for (int a = 0; a <= d.M; ++a) {
-        int rr, cc;
-        long off;
-        realified_shape(d, 0, a, &rr, &cc, &off);
-        const int ao = mm_block(a, d.L, d.Ci()), uo = d.u_block(a);
-        TnSeg segs[2] = {{Tdot + ao, d.wT(), UU + uo, d.wU(), n},
-                         {pr.T + ao, d.wT(), UU + (size_t)n * d.wU() + uo, d.wU(), n}};
-        if ((r = run_tn(segs, 2, rr, cc, gW1r + off, cc, acc, P, s))) return r;
-      }
+      const void* in[2] = {w.Tdot, pr.T};
+      const void* out[2] = {w.UU, offs(static_cast<const void*>(w.UU), (size_t)n * d.wU(), c.es)};
+      const long rows[2] = {n, n};
+      if ((r = run_lin_grad(c, 0, in, out, rows, 2, w.gW1r, acc, w.P, s))) return r;
     }
-    SO2_HIP(launch_node_bwd_dual(d, gc, x, px, pos, omega, pr.S, Sdot, TT, gx2, Sbar, Sdb, acc, s));
+    SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, w.TT, gx2_acc, w.Sbar, w.Sdb, acc, s));
     if (grbf2) {
       float* out = grbf2 + (size_t)e0 * n_rbf;
-      ps.clear();
-      ps.push_back(prob(Sbar, wS, w_rad, wS, out, n_rbf, n, n_rbf, wS));
-      if ((r = run_batch(ps, false, true, s))) return r;
-      if (pw_rad) {
-        ps.clear();
-        ps.push_back(prob(Sdb, wS, pw_rad, wS, out, n_rbf, n, n_rbf, wS, 1));
-        if ((r = run_batch(ps, false, true, s))) return r;
+      std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, out, n_rbf, n, n_rbf, wS)};
+      if ((r = run_batch(ps, false, true, 0, s))) return r;
+      if (pwr32) {
+        std::vector<GemmProb> ps2{prob(w.Sdb, wS, pwr32, wS, out, n_rbf, n, n_rbf, wS, 1)};
+        if ((r = run_batch(ps2, false, true, 0, s))) return r;
       }
     }
-    if (gw_rad2) {
-      TnSeg segs[2] = {{rbf_c, n_rbf, Sbar, wS, n}, {prbf_c, n_rbf, Sdb, wS, prbf_c ? n : 0}};
-      if ((r = run_tn(segs, 2, n_rbf, wS, gw_rad2, wS, acc, P, s))) return r;
+    if (gwr2_acc) {
+      TnSeg segs[2] = {{rbf_c, n_rbf, w.Sbar, wS, n}, {prbf_c, n_rbf, w.Sdb, wS, prbf_c ? n : 0}};
+      if ((r = run_tn(segs, 2, n_rbf, wS, gwr2_acc, wS, acc, w.P, 0, s))) return r;
     }
   }
-  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, gW2r, gw2_2, s));
-  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, gW1r, gw1_2, s));
-  return SO2_OK;
+  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r, gw2_2, c.bf, s));
+  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r, gw1_2, c.bf, s));
+  if ((r = f32_out(c, ggy_acc, ggy, nf, s))) return r;
+  if ((r = f32_out(c, gx2_acc, gx2, nf, s))) return r;
+  return f32_out(c, gwr2_acc, gw_rad2, rf, s);
 }
 
 }  // extern "C"

@@ -36,10 +36,10 @@ constexpr int tile_edges() {
 __device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
 // ------------------------------------------------------------------ edge_bwd
-template <int L, int M>
+template <int L, int M, typename OT>
 __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                        const float* __restrict__ gy, const float* __restrict__ V,
-                                                       float* __restrict__ tbar, float* __restrict__ tau) {
+                                                       OT* __restrict__ tbar, float* __restrict__ tau) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
   __shared__ float sD1[TE * 9];
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
       for (int r = 0; r < D; ++r) gv[r] = gr[(size_t)r * C];
       float o[Q];
       rot_fwd<L, M>(sR + t * K, gv, o);
-      float* tr = tbar + (size_t)e * wZ + c;
+      OT* tr = tbar + (size_t)e * wZ + c;
       const float* vr = V + (size_t)e * wZ + c;
       float vv[Q];
 #pragma unroll
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
         const int q = qhalf(l, M);
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
-          tr[mm_col(l, m, 0, L, C)] = o[ridx(l, m, M)];
+          st(tr + mm_col(l, m, 0, L, C), o[ridx(l, m, M)]);
           vv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
         }
       }
@@ -116,13 +116,18 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
 
 template <int L, int M>
 struct EdgeBwd {
-  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, float* tbar,
-                 float* tau, hipStream_t s) {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, void* tbar,
+                 float* tau, int bf16, hipStream_t s) {
     constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
-    hipLaunchKernelGGL((edge_bwd_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V, tbar, tau);
+    if (bf16)
+      hipLaunchKernelGGL((edge_bwd_kernel<L, M, bf16s>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V,
+                         static_cast<bf16s*>(tbar), tau);
+    else
+      hipLaunchKernelGGL((edge_bwd_kernel<L, M, float>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V,
+                         static_cast<float*>(tbar), tau);
     return hipGetLastError();
   }
 };
@@ -259,8 +264,9 @@ struct NodeBwd {
 };
 
 // ------------------------------------------------------------------ gate_bwd
+template <typename OT>
 __global__ void gate_bwd_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Zb,
-                                float* __restrict__ Ub) {
+                                OT* __restrict__ Ub) {
   const int L = d.L, M = d.M, C = d.C;
   const long n = E * (L + 1) * C;
   const int wU = d.wU(), wZ = d.wZ();
@@ -270,10 +276,10 @@ __global__ void gate_bwd_kernel(Dims d, long E, const float* __restrict__ U, con
     const int l = rem / C, c = rem - l * C;
     const float* ur = U + e * wU;
     const float* zb = Zb + e * wZ;
-    float* ub = Ub + e * wU;
+    OT* ub = Ub + e * wU;
     if (l == 0) {
       const float u = ur[c], s = sigm(u);
-      ub[c] = zb[c] * s * (1.f + u * (1.f - s));
+      st(ub + c, zb[c] * s * (1.f + u * (1.f - s)));
     } else {
       const float s = sigm(ur[d.gate_col(l, c)]);
       const int q = qhalf(l, M);
@@ -282,9 +288,9 @@ __global__ void gate_bwd_kernel(Dims d, long E, const float* __restrict__ U, con
         const float z = zb[mm_col(l, m, c, L, C)];
         const int uc = d.u_col(l, m, c);
         gsum += z * ur[uc];
-        ub[uc] = s * z;
+        st(ub + uc, s * z);
       }
-      ub[d.gate_col(l, c)] = s * (1.f - s) * gsum;
+      st(ub + d.gate_col(l, c), s * (1.f - s) * gsum);
     }
   }
 }
@@ -341,15 +347,20 @@ inline int grid_for(long n) {
 
 }  // namespace
 
-int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, float* tbar,
-                    float* tau, hipStream_t s) {
-  return dispatch_lm<EdgeBwd>(d.L, d.M, d, g, pos, gy, V, tbar, tau, s);
+int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, void* tbar,
+                    float* tau, int bf16, hipStream_t s) {
+  return dispatch_lm<EdgeBwd>(d.L, d.M, d, g, pos, gy, V, tbar, tau, bf16, s);
 }
 
-int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, float* Ubar, hipStream_t s) {
+int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, void* Ubar, int bf16, hipStream_t s) {
   const long n = E * (d.L + 1) * d.C;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_bwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Zbar, Ubar);
+  if (bf16)
+    hipLaunchKernelGGL(gate_bwd_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Zbar,
+                       static_cast<bf16s*>(Ubar));
+  else
+    hipLaunchKernelGGL(gate_bwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Zbar,
+                       static_cast<float*>(Ubar));
   return hipGetLastError();
 }
 

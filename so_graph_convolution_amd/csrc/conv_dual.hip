@@ -47,12 +47,12 @@ __device__ inline void frame_rate(const EdgeGeo& gg, float dx, float dy, float d
 }
 
 // ------------------------------------------------------------------ edge_dual
-template <int L, int M>
+template <int L, int M, typename OT>
 __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, const float* __restrict__ x,
                                                         const float* __restrict__ px, const float* __restrict__ pos,
                                                         const float* __restrict__ ppos,
                                                         const float* __restrict__ pedge, const float* __restrict__ S,
-                                                        const float* __restrict__ Sdot, float* __restrict__ Tdot,
+                                                        const float* __restrict__ Sdot, OT* __restrict__ Tdot,
                                                         float* __restrict__ omega) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
       }
       const float* sr = S + (size_t)e * wS + c;
       const float* sd = Sdot + (size_t)e * wS + c;
-      float* tr = Tdot + (size_t)e * wT;
+      OT* tr = Tdot + (size_t)e * wT;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const float sv = sr[l * Ci], sdv = sd[l * Ci];
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
           load_row<L>(sRd + t * K, off, n, rd);
           const float xt = row_dot<L>(r, a + l * l, n), y2 = row_dot<L>(r, ad + l * l, n);
           const float y1 = row_dot<L>(rd, a + l * l, n);
-          tr[mm_col(l, m, c, L, Ci)] = sdv * xt + sv * (y1 + y2);
+          st(tr + mm_col(l, m, c, L, Ci), sdv * xt + sv * (y1 + y2));
         }
       }
     }
@@ -131,14 +131,18 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
 template <int L, int M>
 struct EdgeDual {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
-                 const float* ppos, const float* pedge, const float* S, const float* Sdot, float* Tdot, float* omega,
-                 hipStream_t s) {
+                 const float* ppos, const float* pedge, const float* S, const float* Sdot, void* Tdot, float* omega,
+                 int bf16, hipStream_t s) {
     constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     if (nb <= 0) return hipSuccess;
     const int threads = min(256, ((2 * d.C + 63) / 64) * 64);
-    hipLaunchKernelGGL((edge_dual_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, x, px, pos, ppos, pedge, S,
-                       Sdot, Tdot, omega);
+    if (bf16)
+      hipLaunchKernelGGL((edge_dual_kernel<L, M, bf16s>), dim3(nb), dim3(threads), 0, s, d, g, x, px, pos, ppos,
+                         pedge, S, Sdot, static_cast<bf16s*>(Tdot), omega);
+    else
+      hipLaunchKernelGGL((edge_dual_kernel<L, M, float>), dim3(nb), dim3(threads), 0, s, d, g, x, px, pos, ppos,
+                         pedge, S, Sdot, static_cast<float*>(Tdot), omega);
     return hipGetLastError();
   }
 };
@@ -219,10 +223,10 @@ struct NodeDual {
 };
 
 // ------------------------------------------------------------------ edge_bwd_dual
-template <int L, int M>
+template <int L, int M, typename OT>
 __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                             const float* __restrict__ omega,
-                                                            const float* __restrict__ gy, float* __restrict__ G2) {
+                                                            const float* __restrict__ gy, OT* __restrict__ G2) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
   __shared__ float sD1[TE * 9];
@@ -253,8 +257,8 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
       const float* gr = gy + (size_t)sDst[t] * D * C + c;
 #pragma unroll
       for (int r = 0; r < D; ++r) gv[r] = gr[(size_t)r * C];
-      float* r1 = G2 + (size_t)e * wZ + c;
-      float* r2 = G2 + ((size_t)(g.e1 - g.e0) + e) * wZ + c;
+      OT* r1 = G2 + (size_t)e * wZ + c;
+      OT* r2 = G2 + ((size_t)(g.e1 - g.e0) + e) * wZ + c;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const int q = qhalf(l, M), n = 2 * l + 1;
@@ -264,8 +268,8 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
           float r[2 * L + 1], rd[2 * L + 1];
           load_row<L>(sR + t * K, off, n, r);
           load_row<L>(sRd + t * K, off, n, rd);
-          r1[mm_col(l, m, 0, L, C)] = row_dot<L>(r, gv + l * l, n);
-          r2[mm_col(l, m, 0, L, C)] = row_dot<L>(rd, gv + l * l, n);
+          st(r1 + mm_col(l, m, 0, L, C), row_dot<L>(r, gv + l * l, n));
+          st(r2 + mm_col(l, m, 0, L, C), row_dot<L>(rd, gv + l * l, n));
         }
       }
     }
@@ -274,13 +278,18 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
 
 template <int L, int M>
 struct EdgeBwdDual {
-  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, float* G2,
-                 hipStream_t s) {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, void* G2,
+                 int bf16, hipStream_t s) {
     constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
-    hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy, G2);
+    if (bf16)
+      hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M, bf16s>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy,
+                         static_cast<bf16s*>(G2));
+    else
+      hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M, float>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy,
+                         static_cast<float*>(G2));
     return hipGetLastError();
   }
 };
@@ -398,8 +407,9 @@ struct NodeBwdDual {
 };
 
 // ------------------------------------------------------------------ gates
+template <typename OT>
 __global__ void gate_dual_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Ud,
-                                 float* __restrict__ Zd) {
+                                 OT* __restrict__ Zd) {
   const int L = d.L, M = d.M, C = d.C;
   const long n = E * (L + 1) * C;
   const int wU = d.wU(), wZ = d.wZ();
@@ -409,25 +419,26 @@ __global__ void gate_dual_kernel(Dims d, long E, const float* __restrict__ U, co
     const int l = rem / C, c = rem - l * C;
     const float* ur = U + e * wU;
     const float* udr = Ud + e * wU;
-    float* zr = Zd + e * wZ;
+    OT* zr = Zd + e * wZ;
     if (l == 0) {
       const float u = ur[c], s = sigm(u);
-      zr[c] = s * (1.f + u * (1.f - s)) * udr[c];
+      st(zr + c, s * (1.f + u * (1.f - s)) * udr[c]);
     } else {
       const int gc = d.gate_col(l, c);
       const float s = sigm(ur[gc]), sp = s * (1.f - s), gd = udr[gc];
       const int q = qhalf(l, M);
       for (int m = -q; m <= q; ++m) {
         const int uc = d.u_col(l, m, c);
-        zr[mm_col(l, m, c, L, C)] = s * udr[uc] + sp * gd * ur[uc];
+        st(zr + mm_col(l, m, c, L, C), s * udr[uc] + sp * gd * ur[uc]);
       }
     }
   }
 }
 
 // ZZ = [zdot_bar (E rows); zbar (E rows)] -> UU = [udot_bar; ubar]
+template <typename OT>
 __global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Ud,
-                                 const float* __restrict__ ZZ, float* __restrict__ UU) {
+                                 const float* __restrict__ ZZ, OT* __restrict__ UU) {
   const int L = d.L, M = d.M, C = d.C;
   const long n = E * (L + 1) * C;
   const int wU = d.wU(), wZ = d.wZ();
@@ -439,14 +450,14 @@ __global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, co
     const float* udr = Ud + e * wU;
     const float* zdb = ZZ + e * wZ;
     const float* zb = ZZ + (E + e) * wZ;
-    float* udb = UU + e * wU;
-    float* ub = UU + (E + e) * wU;
+    OT* udb = UU + e * wU;
+    OT* ub = UU + (E + e) * wU;
     if (l == 0) {
       const float u = ur[c], s = sigm(u);
       const float s1 = s * (1.f + u * (1.f - s));
       const float s2 = s * (1.f - s) * (2.f + u * (1.f - 2.f * s));
-      udb[c] = s1 * zdb[c];
-      ub[c] = s2 * udr[c] * zdb[c] + s1 * zb[c];
+      st(udb + c, s1 * zdb[c]);
+      st(ub + c, s2 * udr[c] * zdb[c] + s1 * zb[c]);
     } else {
       const int gc = d.gate_col(l, c);
       const float s = sigm(ur[gc]), sp = s * (1.f - s), spp = sp * (1.f - 2.f * s), gd = udr[gc];
@@ -455,13 +466,13 @@ __global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, co
       for (int m = -q; m <= q; ++m) {
         const int uc = d.u_col(l, m, c), zc = mm_col(l, m, c, L, C);
         const float a = zdb[zc], b = zb[zc], u = ur[uc], ud = udr[uc];
-        udb[uc] = s * a;
-        ub[uc] = sp * gd * a + s * b;
+        st(udb + uc, s * a);
+        st(ub + uc, sp * gd * a + s * b);
         gdb += a * u;
         gb += spp * gd * u * a + sp * ud * a + sp * u * b;
       }
-      udb[gc] = sp * gdb;
-      ub[gc] = gb;
+      st(udb + gc, sp * gdb);
+      st(ub + gc, gb);
     }
   }
 }
@@ -476,15 +487,20 @@ inline int grid_for(long n) {
 }  // namespace
 
 int launch_edge_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
-                     const float* ppos, const float* pedge, const float* S, const float* Sdot, float* Tdot,
-                     float* omega, hipStream_t s) {
-  return dispatch_lm<EdgeDual>(d.L, d.M, d, g, x, px, pos, ppos, pedge, S, Sdot, Tdot, omega, s);
+                     const float* ppos, const float* pedge, const float* S, const float* Sdot, void* Tdot,
+                     float* omega, int bf16, hipStream_t s) {
+  return dispatch_lm<EdgeDual>(d.L, d.M, d, g, x, px, pos, ppos, pedge, S, Sdot, Tdot, omega, bf16, s);
 }
 
-int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, float* Zdot, hipStream_t s) {
+int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, void* Zdot, int bf16, hipStream_t s) {
   const long n = E * (d.L + 1) * d.C;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_dual_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, Zdot);
+  if (bf16)
+    hipLaunchKernelGGL(gate_dual_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot,
+                       static_cast<bf16s*>(Zdot));
+  else
+    hipLaunchKernelGGL(gate_dual_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot,
+                       static_cast<float*>(Zdot));
   return hipGetLastError();
 }
 
@@ -494,15 +510,20 @@ int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const f
 }
 
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
-                         float* G2, hipStream_t s) {
-  return dispatch_lm<EdgeBwdDual>(d.L, d.M, d, g, pos, omega, gy, G2, s);
+                         void* G2, int bf16, hipStream_t s) {
+  return dispatch_lm<EdgeBwdDual>(d.L, d.M, d, g, pos, omega, gy, G2, bf16, s);
 }
 
-int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, float* UU,
+int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, void* UU, int bf16,
                      hipStream_t s) {
   const long n = E * (d.L + 1) * d.C;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_dbwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, ZZ, UU);
+  if (bf16)
+    hipLaunchKernelGGL(gate_dbwd_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, ZZ,
+                       static_cast<bf16s*>(UU));
+  else
+    hipLaunchKernelGGL(gate_dbwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, ZZ,
+                       static_cast<float*>(UU));
   return hipGetLastError();
 }
 

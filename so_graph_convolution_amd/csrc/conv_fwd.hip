@@ -24,10 +24,10 @@ namespace {
 constexpr int kTileE = 32;   // edges per LDS tile
 
 // ------------------------------------------------------------------ edge_fwd
-template <int L, int M>
+template <int L, int M, typename OT>
 __global__ __launch_bounds__(256) void edge_fwd_kernel(Dims d, GraphDev g, const float* __restrict__ x,
                                                        const float* __restrict__ pos, const float* __restrict__ S,
-                                                       float* __restrict__ T) {
+                                                       OT* __restrict__ T) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   __shared__ float sD1[kTileE * 9];
   __shared__ float sR[kTileE * K];
@@ -59,13 +59,13 @@ __global__ __launch_bounds__(256) void edge_fwd_kernel(Dims d, GraphDev g, const
       float o[Q];
       rot_fwd<L, M>(sR + t * K, a, o);
       const float* sr = S + (size_t)e * ldS + c;
-      float* tr = T + (size_t)e * wT;
+      OT* tr = T + (size_t)e * wT;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const float sc = sr[l * Ci];
         const int q = qhalf(l, M);
 #pragma unroll
-        for (int m = -q; m <= q; ++m) tr[mm_col(l, m, c, L, Ci)] = sc * o[ridx(l, m, M)];
+        for (int m = -q; m <= q; ++m) st(tr + mm_col(l, m, c, L, Ci), sc * o[ridx(l, m, M)]);
       }
     }
   }
@@ -73,12 +73,17 @@ __global__ __launch_bounds__(256) void edge_fwd_kernel(Dims d, GraphDev g, const
 
 template <int L, int M>
 struct EdgeFwd {
-  static int run(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, float* T,
-                 hipStream_t s) {
+  static int run(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, void* T,
+                 int bf16, hipStream_t s) {
     const long nb = (g.e1 - g.e0 + kTileE - 1) / kTileE;
     if (nb <= 0) return hipSuccess;
     const int threads = min(256, ((2 * d.C + 63) / 64) * 64);
-    hipLaunchKernelGGL((edge_fwd_kernel<L, M>), dim3(nb), dim3(threads), 0, s, d, g, x, pos, S, T);
+    if (bf16)
+      hipLaunchKernelGGL((edge_fwd_kernel<L, M, bf16s>), dim3(nb), dim3(threads), 0, s, d, g, x, pos, S,
+                         static_cast<bf16s*>(T));
+    else
+      hipLaunchKernelGGL((edge_fwd_kernel<L, M, float>), dim3(nb), dim3(threads), 0, s, d, g, x, pos, S,
+                         static_cast<float*>(T));
     return hipGetLastError();
   }
 };
@@ -149,7 +154,8 @@ struct NodeFwd {
 __device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
 // one thread per (edge, l, c): reads the gate once, scales every retained order of l
-__global__ void gate_fwd_kernel(Dims d, long E, const float* __restrict__ U, float* __restrict__ Z) {
+template <typename OT>
+__global__ void gate_fwd_kernel(Dims d, long E, const float* __restrict__ U, OT* __restrict__ Z) {
   const int L = d.L, M = d.M, C = d.C;
   const long n = E * (L + 1) * C;
   const int wU = d.wU(), wZ = d.wZ();
@@ -158,41 +164,62 @@ __global__ void gate_fwd_kernel(Dims d, long E, const float* __restrict__ U, flo
     const int rem = (int)(idx - e * (L + 1) * C);
     const int l = rem / C, c = rem - l * C;
     const float* ur = U + e * wU;
-    float* zr = Z + e * wZ;
+    OT* zr = Z + e * wZ;
     if (l == 0) {
       const float u = ur[c];
-      zr[c] = u * sigm(u);
+      st(zr + c, u * sigm(u));
     } else {
       const float gs = sigm(ur[d.gate_col(l, c)]);
       const int q = qhalf(l, M);
-      for (int m = -q; m <= q; ++m) zr[mm_col(l, m, c, L, C)] = gs * ur[d.u_col(l, m, c)];
+      for (int m = -q; m <= q; ++m) st(zr + mm_col(l, m, c, L, C), gs * ur[d.u_col(l, m, c)]);
     }
   }
 }
 
 // ------------------------------------------------------------------ weights
-__global__ void realify_kernel(const float* __restrict__ w, int k, int h, float* __restrict__ wr) {
-  // w: [k][2h] = [W0 | W1]; wr: [2k][2h] = [[W0, W1], [-W1, W0]]
-  const long n = (long)2 * k * 2 * h;
+// block of w: [k][2h] = [W0 | W1] (plain: [k][h2] copied as is);
+// realified: [2k][2h] = [[W0, W1], [-W1, W0]]; transposed output: [2h][2k]
+template <typename IT, typename OT, bool TRANS>
+__global__ void realify_kernel(const IT* __restrict__ w, int k, int h, int plain, OT* __restrict__ wr) {
+  const int rows = plain ? k : 2 * k, cols = plain ? h : 2 * h;
+  const long n = (long)rows * cols;
   for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
-    const int r = (int)(idx / (2 * h)), col = (int)(idx - (long)r * 2 * h);
-    const int rr = r % k, lower = r >= k, right = col >= h, cc = col % h;
+    int r, col;
+    if (TRANS) {
+      col = (int)(idx / rows);
+      r = (int)(idx - (long)col * rows);
+    } else {
+      r = (int)(idx / cols);
+      col = (int)(idx - (long)r * cols);
+    }
     float v;
-    if (!lower) v = w[(long)rr * 2 * h + col];
-    else v = right ? w[(long)rr * 2 * h + cc] : -w[(long)rr * 2 * h + h + cc];
-    wr[idx] = v;
+    if (plain) {
+      v = ld(w + (long)r * cols + col);
+    } else {
+      const int rr = r % k, lower = r >= k, right = col >= h, cc = col % h;
+      if (!lower) v = ld(w + (long)rr * 2 * h + col);
+      else v = right ? ld(w + (long)rr * 2 * h + cc) : -ld(w + (long)rr * 2 * h + h + cc);
+    }
+    st(wr + idx, v);
   }
 }
 
-__global__ void fold_kernel(const float* __restrict__ gr, int k, int h, float* __restrict__ gw) {
+template <typename OT>
+__global__ void fold_kernel(const float* __restrict__ gr, int k, int h, OT* __restrict__ gw) {
   // gw[k][2h]: [G00 + G11 | G01 - G10]
   const long n = (long)k * 2 * h;
   for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
     const int r = (int)(idx / (2 * h)), col = (int)(idx - (long)r * 2 * h);
     const int cc = col % h;
     const long top = (long)r * 2 * h, bot = (long)(r + k) * 2 * h;
-    gw[idx] = col < h ? gr[top + cc] + gr[bot + h + cc] : gr[top + h + cc] - gr[bot + cc];
+    st(gw + idx, col < h ? gr[top + cc] + gr[bot + h + cc] : gr[top + h + cc] - gr[bot + cc]);
   }
+}
+
+template <typename IT, typename OT>
+__global__ void convert_kernel(const IT* __restrict__ in, OT* __restrict__ out, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    st(out + i, ld(in + i));
 }
 
 inline int grid_for(long n) {
@@ -204,9 +231,9 @@ inline int grid_for(long n) {
 
 }  // namespace
 
-int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, float* T,
-                    hipStream_t s) {
-  return dispatch_lm<EdgeFwd>(d.L, d.M, d, g, x, pos, S, T, s);
+int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, void* T,
+                    int bf16, hipStream_t s) {
+  return dispatch_lm<EdgeFwd>(d.L, d.M, d, g, x, pos, S, T, bf16, s);
 }
 
 int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
@@ -214,10 +241,13 @@ int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const fl
   return dispatch_lm<NodeFwd>(d.L, d.M, d, g, pos, V, y, accumulate, s);
 }
 
-int launch_gate_fwd(const Dims& d, long E, const float* U, float* Z, hipStream_t s) {
+int launch_gate_fwd(const Dims& d, long E, const float* U, void* Z, int bf16, hipStream_t s) {
   const long n = E * (d.L + 1) * d.C;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_fwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Z);
+  if (bf16)
+    hipLaunchKernelGGL(gate_fwd_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, static_cast<bf16s*>(Z));
+  else
+    hipLaunchKernelGGL(gate_fwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, static_cast<float*>(Z));
   return hipGetLastError();
 }
 
@@ -250,41 +280,74 @@ long realified_size(const Dims& d, int second) {
   return off + (long)r * c;
 }
 
-int launch_realify(const Dims& d, int second, const float* const* w, float* wr, hipStream_t s) {
+template <typename IT, typename OT, bool TRANS>
+int realify_block(const void* w, int k, int h, int plain, void* out, hipStream_t s) {
+  const long n = (long)(plain ? k : 2 * k) * (plain ? h : 2 * h);
+  hipLaunchKernelGGL((realify_kernel<IT, OT, TRANS>), dim3(grid_for(n)), dim3(256), 0, s, static_cast<const IT*>(w), k,
+                     h, plain, static_cast<OT*>(out));
+  return hipGetLastError();
+}
+
+int launch_realify(const Dims& d, int second, const void* const* w, void* wr, void* wrt, int bf16, hipStream_t s) {
   for (int a = 0; a <= d.M; ++a) {
     int r, c;
     long off;
     realified_shape(d, second, a, &r, &c, &off);
-    if (a == 0) {
-      hipError_t e = hipMemcpyAsync(wr + off, w[0], sizeof(float) * (size_t)r * c, hipMemcpyDeviceToDevice, s);
-      if (e != hipSuccess) return e;
+    const int plain = a == 0;
+    const int k = plain ? r : r / 2, h = plain ? c : c / 2;
+    int e;
+    if (!bf16) {
+      if (plain) {
+        e = hipMemcpyAsync(static_cast<float*>(wr) + off, w[0], sizeof(float) * (size_t)r * c,
+                           hipMemcpyDeviceToDevice, s);
+      } else {
+        e = realify_block<float, float, false>(w[a], k, h, 0, static_cast<float*>(wr) + off, s);
+      }
     } else {
-      const int k = r / 2, h = c / 2;
-      hipLaunchKernelGGL(realify_kernel, dim3(grid_for((long)r * c)), dim3(256), 0, s, w[a], k, h, wr + off);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      e = realify_block<bf16s, bf16s, false>(w[a], k, h, plain, static_cast<bf16s*>(wr) + off, s);
+      if (e == hipSuccess && wrt)
+        e = realify_block<bf16s, bf16s, true>(w[a], k, h, plain, static_cast<bf16s*>(wrt) + off, s);
     }
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-int launch_fold_grad(const Dims& d, int second, const float* gr, float* const* gw, hipStream_t s) {
+int launch_fold_grad(const Dims& d, int second, const float* gr, void* const* gw, int bf16, hipStream_t s) {
   for (int a = 0; a <= d.M; ++a) {
     if (!gw[a]) continue;
     int r, c;
     long off;
     realified_shape(d, second, a, &r, &c, &off);
+    hipError_t e;
     if (a == 0) {
-      hipError_t e = hipMemcpyAsync(gw[0], gr + off, sizeof(float) * (size_t)r * c, hipMemcpyDeviceToDevice, s);
-      if (e != hipSuccess) return e;
+      if (bf16) e = (hipError_t)launch_to_bf16(gr + off, static_cast<bf16s*>(gw[0]), (size_t)r * c, s);
+      else e = hipMemcpyAsync(gw[0], gr + off, sizeof(float) * (size_t)r * c, hipMemcpyDeviceToDevice, s);
     } else {
       const int k = r / 2, h = c / 2;
-      hipLaunchKernelGGL(fold_kernel, dim3(grid_for((long)k * c)), dim3(256), 0, s, gr + off, k, h, gw[a]);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      if (bf16)
+        hipLaunchKernelGGL(fold_kernel<bf16s>, dim3(grid_for((long)k * c)), dim3(256), 0, s, gr + off, k, h,
+                           static_cast<bf16s*>(gw[a]));
+      else
+        hipLaunchKernelGGL(fold_kernel<float>, dim3(grid_for((long)k * c)), dim3(256), 0, s, gr + off, k, h,
+                           static_cast<float*>(gw[a]));
+      e = hipGetLastError();
     }
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+int launch_to_f32(const bf16s* in, float* out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((convert_kernel<bf16s, float>), dim3(grid_for((long)n)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+int launch_to_bf16(const float* in, bf16s* out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((convert_kernel<float, bf16s>), dim3(grid_for((long)n)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
 }
 
 bool lm_supported(int L, int M) { return lm_pair_compiled(L, M); }

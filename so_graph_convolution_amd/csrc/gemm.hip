@@ -1,6 +1,7 @@
-// Grouped fp32 MFMA GEMM: 256x128 block tiles, 8 waves of 64x64 (2x2
-// v_mfma_f32_32x32x2_f32 tiles each), K tile 16, LDS double buffering,
-// XCD-aware linear tile order.
+// Grouped MFMA GEMMs: 256x128 block tiles, 8 waves of 64x64 (2x2 32x32 MFMA
+// tiles each), LDS double buffering, XCD-aware linear tile order.
+//   float32 operands : v_mfma_f32_32x32x2_f32, K tile 16
+//   bfloat16 operands: v_mfma_f32_32x32x16_bf16, K tile 32
 //
 // Operand staging: every global load runs along the operand's contiguous
 // dimension (float4 per lane, consecutive lanes on consecutive addresses), and
@@ -162,6 +163,38 @@ __device__ __forceinline__ float frag(const float* S, int row, int k) {
   return KCONTIG ? S[row * Cfg<BK, R>::PK + k] : S[k * Cfg<BK, R>::PW + row];
 }
 
+// epilogue: lane holds rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of each 32x32 tile
+__device__ inline void store_acc(const GemmProb& p, int split, int m0, int n0, int wm, int wn, int li, int lk,
+                                 const floatx16 (&acc)[WM][WN]) {
+  float* out;
+  int ldo;
+  bool acc_in;
+  if (p.partial) {
+    out = p.C + (size_t)split * p.M * p.N;
+    ldo = p.N;
+    acc_in = false;
+  } else {
+    out = p.C;
+    ldo = p.ldc;
+    acc_in = p.accumulate != 0;
+  }
+#pragma unroll
+  for (int a = 0; a < WM; ++a)
+#pragma unroll
+    for (int b = 0; b < WN; ++b) {
+      const int j = n0 + wn * 32 * WN + b * 32 + li;
+      if (j >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = m0 + wm * 32 * WM + a * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
+        if (i < p.M) {
+          float* dst = out + (size_t)i * ldo + j;
+          *dst = acc_in ? *dst + acc[a][b][r] : acc[a][b][r];
+        }
+      }
+    }
+}
+
 template <bool TA, bool TB, int BK>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, 8))) void gemm_f32_kernel(
     GemmBatch batch) {
@@ -198,8 +231,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   floatx4 ra[AK ? Cfg<BK, BM>::NRC : Cfg<BK, BM>::NRM];
   floatx4 rb[BKC ? Cfg<BK, BN>::NRC : Cfg<BK, BN>::NRM];
   if (nk > 0) {
-    load_tile<AK, BK, BM>(p.A, p.lda, m0, p.M, kbeg, kend, ra);
-    load_tile<BKC, BK, BN>(p.B, p.ldb, n0, p.N, kbeg, kend, rb);
+    load_tile<AK, BK, BM>(static_cast<const float*>(p.A), p.lda, m0, p.M, kbeg, kend, ra);
+    load_tile<BKC, BK, BN>(static_cast<const float*>(p.B), p.ldb, n0, p.N, kbeg, kend, rb);
     store_tile<AK, BK, BM>(As[0], ra);
     store_tile<BKC, BK, BN>(Bs[0], rb);
   }
@@ -208,8 +241,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      load_tile<AK, BK, BM>(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, ra);
-      load_tile<BKC, BK, BN>(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, rb);
+      load_tile<AK, BK, BM>(static_cast<const float*>(p.A), p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, ra);
+      load_tile<BKC, BK, BN>(static_cast<const float*>(p.B), p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, rb);
     }
     const float* as = As[cur];
     const float* bs = Bs[cur];
@@ -233,34 +266,190 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
     __syncthreads();
   }
 
-  // epilogue: lane holds rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of each 32x32 tile
-  float* out;
-  int ldo;
-  bool acc_in;
-  if (p.partial) {
-    out = p.C + (size_t)split * p.M * p.N;
-    ldo = p.N;
-    acc_in = false;
-  } else {
-    out = p.C;
-    ldo = p.ldc;
-    acc_in = p.accumulate != 0;
+  store_acc(p, split, m0, n0, wm, wn, li, lk, acc);
+}
+
+
+// ---------------------------------------------------------------- bfloat16 operands
+// LDS tiles hold every operand k-contiguous: row r of a tile is 32 bf16 (four
+// 16-byte chunks of 8 k values) at a pitch of 20 dwords, and the chunks of
+// rows 8..15 of every 16 rows are swapped pairwise. An MFMA operand read is
+// one 16-byte chunk per lane (row lane%32, chunk 2*ks + lane/32); with the
+// pitch, any 8 consecutive rows of one chunk fall on disjoint banks, and the
+// swap keeps the transposing stores of k-major operands (below) off each
+// other's banks.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int BKH = 32;
+constexpr int PD = 20;
+
+__device__ __forceinline__ int lds_chunk(int row, int q) { return row * PD + 4 * (q ^ ((row >> 3) & 1)); }
+
+template <int R>
+struct CfgH {
+  static constexpr int TILE = R * PD;        // dwords of one staged tile
+  static constexpr int NKC = R * 4 / NT;     // 16-byte chunks per thread of a k-contiguous tile
+};
+
+// k-contiguous operand (global [row][k]): one 16-byte chunk per load
+template <int R>
+__device__ inline void ldh_kc(const unsigned short* __restrict__ P, int ld, int r0, int rlim, int k0, int kend,
+                              u32x4 (&v)[CfgH<R>::NKC]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < CfgH<R>::NKC; ++p) {
+    const int idx = p * NT + t, row = idx >> 2, q = idx & 3;
+    const int gr = r0 + row, gk = k0 + 8 * q;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (gr < rlim && gk < kend) {
+      const unsigned short* src = P + (size_t)gr * ld + gk;
+      if (gk + 8 <= kend) {
+        x = *reinterpret_cast<const u32x4*>(src);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (gk + c < kend) x[c / 2] |= (unsigned)src[c] << (16 * (c % 2));
+      }
+    }
+    v[p] = x;
   }
+}
+
+template <int R>
+__device__ inline void sth_kc(unsigned* S, const u32x4 (&v)[CfgH<R>::NKC]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < CfgH<R>::NKC; ++p) {
+    const int idx = p * NT + t;
+    *reinterpret_cast<u32x4*>(S + lds_chunk(idx >> 2, idx & 3)) = v[p];
+  }
+}
+
+// k-major operand (global [k][row]): thread t < 2R takes the unit of rows
+// (2c, 2c+1) x k (8g .. 8g+7), c = t % (R/2), g = t / (R/2): eight 4-byte
+// loads (consecutive lanes on consecutive row pairs), transposed in registers
+// into one 16-byte chunk per row.
+template <int R>
+__device__ inline void ldh_km(const unsigned short* __restrict__ P, int ld, int r0, int rlim, int k0, int kend,
+                              unsigned (&w)[8]) {
+  const int t = threadIdx.x;
+  const int c = t % (R / 2), g = t / (R / 2);
+  const int gr = r0 + 2 * c;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = 0u;
+  if (t >= 2 * R) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int gk = k0 + 8 * g + j;
+    if (gk < kend) {
+      const unsigned short* src = P + (size_t)gk * ld + gr;
+      if (gr + 1 < rlim) w[j] = *reinterpret_cast<const unsigned*>(src);
+      else if (gr < rlim) w[j] = src[0];
+    }
+  }
+}
+
+template <int R>
+__device__ inline void sth_km(unsigned* S, const unsigned (&w)[8]) {
+  const int t = threadIdx.x;
+  if (t >= 2 * R) return;
+  const int c = t % (R / 2), g = t / (R / 2);
+  u32x4 lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = (w[2 * i] & 0xffffu) | (w[2 * i + 1] << 16);
+    hi[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xffff0000u);
+  }
+  *reinterpret_cast<u32x4*>(S + lds_chunk(2 * c, g)) = lo;
+  *reinterpret_cast<u32x4*>(S + lds_chunk(2 * c + 1, g)) = hi;
+}
+
+// TA = false: C = A.B^T (both operands k-contiguous); TA = true: C = A^T.B
+// (both k-major)
+template <bool TA>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, 8))) void gemm_bf16_kernel(
+    GemmBatch batch) {
+  __shared__ unsigned As[2][CfgH<BM>::TILE];
+  __shared__ unsigned Bs[2][CfgH<BN>::TILE];
+
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * p.k_chunk;
+  const int kend = min(p.K, kbeg + p.k_chunk);
+  const unsigned short* A = static_cast<const unsigned short*>(p.A);
+  const unsigned short* B = static_cast<const unsigned short*>(p.B);
+
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave / 2, wn = wave % 2;
+  const int li = lane % 32, lk = lane / 32;
+
+  floatx16 acc[WM][WN];
 #pragma unroll
   for (int a = 0; a < WM; ++a)
 #pragma unroll
-    for (int b = 0; b < WN; ++b) {
-      const int j = n0 + wn * 32 * WN + b * 32 + li;
-      if (j >= p.N) continue;
+    for (int b = 0; b < WN; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = m0 + wm * 32 * WM + a * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
-        if (i < p.M) {
-          float* dst = out + (size_t)i * ldo + j;
-          *dst = acc_in ? *dst + acc[a][b][r] : acc[a][b][r];
-        }
-      }
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const int nk = (kend - kbeg + BKH - 1) / BKH;
+  u32x4 ra[TA ? 1 : CfgH<BM>::NKC], rb[TA ? 1 : CfgH<BN>::NKC];
+  unsigned wa[8], wb[8];
+  auto load = [&](int k0) {
+    if constexpr (TA) {
+      ldh_km<BM>(A, p.lda, m0, p.M, k0, kend, wa);
+      ldh_km<BN>(B, p.ldb, n0, p.N, k0, kend, wb);
+    } else {
+      ldh_kc<BM>(A, p.lda, m0, p.M, k0, kend, ra);
+      ldh_kc<BN>(B, p.ldb, n0, p.N, k0, kend, rb);
     }
+  };
+  auto store = [&](int buf) {
+    if constexpr (TA) {
+      sth_km<BM>(As[buf], wa);
+      sth_km<BN>(Bs[buf], wb);
+    } else {
+      sth_kc<BM>(As[buf], ra);
+      sth_kc<BN>(Bs[buf], rb);
+    }
+  };
+  if (nk > 0) {
+    load(kbeg);
+    store(0);
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kbeg + (kt + 1) * BKH);
+    const unsigned* as = As[cur];
+    const unsigned* bs = Bs[cur];
+    const int ra0 = wm * 32 * WM + li, rb0 = wn * 32 * WN + li;
+#pragma unroll
+    for (int ks = 0; ks < BKH / 16; ++ks) {
+      const int q = 2 * ks + lk;
+      bf16x8 av[WM], bv[WN];
+#pragma unroll
+      for (int a = 0; a < WM; ++a)
+        av[a] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + lds_chunk(ra0 + 32 * a, q)));
+#pragma unroll
+      for (int b = 0; b < WN; ++b)
+        bv[b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + lds_chunk(rb0 + 32 * b, q)));
+#pragma unroll
+      for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+  store_acc(p, split, m0, n0, wm, wn, li, lk, acc);
 }
 
 __global__ void gemm_reduce_kernel(const float* __restrict__ P, int splits, int M, int N, float* __restrict__ C,
@@ -277,8 +466,9 @@ __global__ void gemm_reduce_kernel(const float* __restrict__ P, int splits, int 
 
 }  // namespace
 
-int gemm_run(GemmBatch& b, bool TA, bool TB, hipStream_t s) {
+int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   constexpr int BK = BK_TILE;
+  if (bf16 && TA == TB) return hipErrorInvalidValue;
   int total = 0;
   for (int q = 0; q < b.nprob; ++q) {
     GemmProb& p = b.p[q];
@@ -292,6 +482,11 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, hipStream_t s) {
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
   dim3 grid(total), block(NT);
+  if (bf16) {
+    if (TA) hipLaunchKernelGGL((gemm_bf16_kernel<true>), grid, block, 0, s, b);
+    else hipLaunchKernelGGL((gemm_bf16_kernel<false>), grid, block, 0, s, b);
+    return hipGetLastError();
+  }
   if (!TA && !TB) hipLaunchKernelGGL((gemm_f32_kernel<false, false, BK>), grid, block, 0, s, b);
   else if (!TA && TB) hipLaunchKernelGGL((gemm_f32_kernel<false, true, BK>), grid, block, 0, s, b);
   else if (TA && !TB) hipLaunchKernelGGL((gemm_f32_kernel<true, false, BK>), grid, block, 0, s, b);

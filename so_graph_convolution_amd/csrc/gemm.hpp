@@ -1,4 +1,6 @@
-// Grouped fp32 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
+// Grouped GEMMs on CDNA4 matrix cores: float32 operands
+// (v_mfma_f32_32x32x2_f32) or bfloat16 operands (v_mfma_f32_32x32x16_bf16),
+// float32 accumulation and output in both cases.
 //
 // The per-order SO(2) linears (TrimSO(2) page, Section 3.1 and Eq.(1)) are
 // the one dense contraction of the convolution: for every retained order a
@@ -6,6 +8,8 @@
 //   C = op(A) op(B)   (or C += ... with accumulate)
 //   op(A)[i][k] = TA ? A[k*lda + i] : A[i*lda + k]
 //   op(B)[k][j] = TB ? B[j*ldb + k] : B[k*ldb + j]
+// The bfloat16 kernels take A.B^T and A^T.B only (a forward product uses the
+// transposed copy of the weight).
 // TA problems (weight gradients, K = edges) are split over K; every split
 // writes its own partial tile and gemm_reduce sums the splits in a fixed
 // order, so results are bitwise reproducible (no atomics).
@@ -17,8 +21,8 @@ namespace so2 {
 constexpr int kGemmMaxProbs = 8;
 
 struct GemmProb {
-  const float* A;
-  const float* B;
+  const void* A;     // float or bfloat16 elements (one type per launch)
+  const void* B;
   float* C;          // output, or the partial buffer [k_splits][M][N] of a split problem
   int M, N, K;
   int lda, ldb, ldc;
@@ -36,9 +40,13 @@ struct GemmBatch {
   int total_tiles;
 };
 
-// Fill tiling fields and launch. Every problem of one batch shares TA/TB.
-// Returns a hipError_t.
-int gemm_run(GemmBatch& b, bool TA, bool TB, hipStream_t s);
+// Fill tiling fields and launch. Every problem of one batch shares TA/TB and
+// the operand type. Returns a hipError_t (hipErrorInvalidValue for a bfloat16
+// A.B or A^T.B^T).
+int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s);
+
+// K tile of the kernels: split chunks of TA problems are multiples of it
+constexpr int kGemmKTile = 32;
 
 // C[i*ldc + j] (+)= sum_{s < splits} P[s][i][j]  (fixed order)
 int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s);

@@ -1,0 +1,31 @@
+// Storage types of the GEMM operands. The bfloat16 path keeps node arrays,
+// GEMM outputs and every reduction in float32 and stores only the per-edge
+// operands of the per-order linears (and the realified weights) as bfloat16,
+// rounded to nearest even.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace so2 {
+
+struct bf16s {
+  unsigned short u;
+};
+
+__host__ __device__ inline float bf16_to_f32(unsigned short h) {
+  return __builtin_bit_cast(float, (unsigned)h << 16);
+}
+
+// round to nearest even; NaN stays NaN
+__host__ __device__ inline unsigned short f32_to_bf16(float f) {
+  unsigned u = __builtin_bit_cast(unsigned, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(bf16s* p, float v) { p->u = f32_to_bf16(v); }
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const bf16s* p) { return bf16_to_f32(p->u); }
+
+}  // namespace so2

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include "layout.hpp"
+#include "numeric.hpp"
 
 namespace so2 {
 
@@ -23,22 +24,25 @@ bool lm_supported(int L, int M);
 // upload the so(3) generator tables to the current device (idempotent per device)
 int init_generators();
 
+// Buffers marked "operand" below hold the per-edge inputs of the per-order
+// linears: float32, or bfloat16 when the launcher's bf16 flag is set.
+
 // ---- forward
-// T[e] (m-major, width q*2C) = S[e] * (R_e [x_src | x_dst])
-int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, float* T,
-                     hipStream_t s);
-// Z = gate(U)
-int launch_gate_fwd(const Dims& d, long E, const float* U, float* Z, hipStream_t s);
+// T[e] (operand; m-major, width q*2C) = S[e] * (R_e [x_src | x_dst])
+int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S, void* T,
+                    int bf16, hipStream_t s);
+// Z (operand) = gate(U)
+int launch_gate_fwd(const Dims& d, long E, const float* U, void* Z, int bf16, hipStream_t s);
 // y[i] (+)= sum_{e -> i, e in chunk} R_e^T V[e]
 int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
                     hipStream_t s);
 
 // ---- backward
-// tbar[e] = R_e gy[dst]; tau[e] = torque of <V, R gy> (for the position gradient)
-int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, float* tbar,
-                    float* tau, hipStream_t s);
-// Ubar from Zbar (gate backward)
-int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, float* Ubar, hipStream_t s);
+// tbar[e] (operand) = R_e gy[dst]; tau[e] = torque of <V, R gy> (for the position gradient)
+int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, void* tbar,
+                    float* tau, int bf16, hipStream_t s);
+// Ubar (operand) from Zbar (gate backward)
+int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, void* Ubar, int bf16, hipStream_t s);
 // gx[n] (both halves), Sbar[e], tau_dst[e], tau_src[e]
 int launch_node_bwd(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
                     const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, int accumulate,
@@ -50,20 +54,21 @@ int launch_vbar(const GraphDev& g, const float* pos, const float* tau1, const fl
 int launch_node_pos(const GraphDev& g, const float* vbar, float* gpos, hipStream_t s);
 
 // ---- double backward (force-training pattern and general directions)
-// Tdot = Sdot*(R a) + S*(Rdot a + R adot), Rdot from the position direction; also writes the
-// per-edge rotation direction omega[e][3]
+// Tdot (operand) = Sdot*(R a) + S*(Rdot a + R adot), Rdot from the position direction; also
+// writes the per-edge rotation direction omega[e][3]
 int launch_edge_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
-                     const float* ppos, const float* pedge, const float* S, const float* Sdot, float* Tdot,
-                     float* omega, hipStream_t s);
-int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, float* Zdot, hipStream_t s);
+                     const float* ppos, const float* pedge, const float* S, const float* Sdot, void* Tdot,
+                     float* omega, int bf16, hipStream_t s);
+// Zdot (operand)
+int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, void* Zdot, int bf16, hipStream_t s);
 // ydot[i] = sum_e Rdot^T V + R^T Vdot
 int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
                      const float* Vdot, float* ydot, int accumulate, hipStream_t s);
-// G2 rows [0,E) = R gy[dst], rows [E,2E) = Rdot gy[dst]
+// G2 (operand) rows [0,E) = R gy[dst], rows [E,2E) = Rdot gy[dst]
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
-                         float* G2, hipStream_t s);
-// from ZZ = [Zdot_bar; Zbar] produce UU = [Udot_bar; Ubar]
-int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, float* UU,
+                         void* G2, int bf16, hipStream_t s);
+// from ZZ = [Zdot_bar; Zbar] produce UU (operand) = [Udot_bar; Ubar]
+int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, void* UU, int bf16,
                      hipStream_t s);
 // gx2 and (Sbar, Sdot_bar) from TT = [Tdot_bar; Tbar]
 int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
@@ -71,10 +76,16 @@ int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const
                          float* Sbar, float* Sdot_bar, int accumulate, hipStream_t s);
 
 // ---- weights
-// Wr (realified per order): block 0 = W[0]; block m = [[W_m0, W_m1], [-W_m1, W_m0]]
-int launch_realify(const Dims& d, int second, const float* const* w, float* wr, hipStream_t s);
-// fold the realified gradient back: gW_m0 = G00 + G11, gW_m1 = G01 - G10 (m >= 1), gW_0 = G_0
-int launch_fold_grad(const Dims& d, int second, const float* gr, float* const* gw, hipStream_t s);
+// Wr (realified per order): block 0 = W[0]; block m = [[W_m0, W_m1], [-W_m1, W_m0]].
+// float32: w and wr float. bfloat16: w bfloat16; wr holds every block
+// bfloat16 and wrt (if not null) every block transposed ([cols][rows]).
+int launch_realify(const Dims& d, int second, const void* const* w, void* wr, void* wrt, int bf16, hipStream_t s);
+// fold the realified float32 gradient back: gW_m0 = G00 + G11, gW_m1 = G01 - G10 (m >= 1),
+// gW_0 = G_0; gw blocks float32 or bfloat16
+int launch_fold_grad(const Dims& d, int second, const float* gr, void* const* gw, int bf16, hipStream_t s);
+// dtype conversions of n elements
+int launch_to_f32(const bf16s* in, float* out, size_t n, hipStream_t s);
+int launch_to_bf16(const float* in, bf16s* out, size_t n, hipStream_t s);
 
 // realified weight geometry: rows/cols of block a and its offset (floats) in the packed buffer
 void realified_shape(const Dims& d, int second, int a, int* rows, int* cols, long* off);

@@ -19,15 +19,31 @@ __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2con
            "so2conv_chunked_workspace_bytes"]
 
 
+_DTYPES = {"f32": (0, torch.float32), "bf16": (1, torch.bfloat16)}
+
+
 @dataclasses.dataclass(frozen=True)
 class SO2Config:
+    """dtype "f32": every array float32. dtype "bf16": node features, weights and
+    their gradients bfloat16 (positions, shifts, rbf and their gradients stay
+    float32); the per-order products run on bfloat16 matrix cores with float32
+    accumulation."""
     lmax: int
     mmax: int
     channels: int
     n_rbf: int
+    dtype: str = "f32"
+
+    def __post_init__(self):
+        if self.dtype not in _DTYPES:
+            raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
 
     def c(self) -> Cfg:
-        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, 0, 0)
+        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0], 0)
+
+    @property
+    def torch_dtype(self):
+        return _DTYPES[self.dtype][1]
 
     @property
     def d(self) -> int:
@@ -63,13 +79,13 @@ def _dev(t, name, dtype=torch.float32, shape=None):
     return t
 
 
-def _ptr_array(ts, name, shapes):
+def _ptr_array(ts, name, shapes, dtype):
     if ts is None:
         return None, []
     ts = list(ts)
     if len(ts) != len(shapes):
         raise ValueError(f"{name} needs {len(shapes)} blocks")
-    keep = [_dev(t, f"{name}[{i}]", shape=shapes[i]) for i, t in enumerate(ts)]
+    keep = [_dev(t, f"{name}[{i}]", dtype=dtype, shape=shapes[i]) for i, t in enumerate(ts)]
     arr = (ctypes.c_void_p * len(ts))(*[None if t is None else t.data_ptr() for t in keep])
     return ctypes.cast(arr, ctypes.c_void_p), [arr, keep]
 
@@ -149,10 +165,10 @@ def _ws_for(cfg, g, stage, saved, ws, chunk_edges, device):
 
 def _common(cfg, g, x, pos, rbf, w_rad):
     N, E, d, C = g.n_nodes, g.n_edges, cfg.d, cfg.channels
-    _dev(x, "x", shape=(N, d, C))
+    _dev(x, "x", dtype=cfg.torch_dtype, shape=(N, d, C))
     _dev(pos, "pos", shape=(N, 3))
     _dev(rbf, "rbf", shape=(E, cfg.n_rbf))
-    _dev(w_rad, "w_rad", shape=(cfg.n_rbf, (cfg.lmax + 1) * 2 * C))
+    _dev(w_rad, "w_rad", dtype=cfg.torch_dtype, shape=(cfg.n_rbf, (cfg.lmax + 1) * 2 * C))
 
 
 def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None, ws=None, chunk_edges=None):
@@ -160,8 +176,9 @@ def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None
     saved=None the state is not kept (chunks of chunk_edges edges)."""
     _common(cfg, g, x, pos, rbf, w_rad)
     s1, s2 = weight_shapes(cfg)
-    p1, k1 = _ptr_array(w1, "w1", s1)
-    p2, k2 = _ptr_array(w2, "w2", s2)
+    dt = cfg.torch_dtype
+    p1, k1 = _ptr_array(w1, "w1", s1, dt)
+    p2, k2 = _ptr_array(w2, "w2", s2, dt)
     y = torch.empty_like(x)
     if saved is True:
         saved = _ws(so2conv_saved_bytes(cfg, g.n_edges), x.device)
@@ -180,21 +197,22 @@ def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy,
     """Returns dict gx, gpos, grbf, gw_rad, gw1, gw2, gedge (requested ones).
     saved=None recomputes the forward state chunk by chunk."""
     _common(cfg, g, x, pos, rbf, w_rad)
-    _dev(gy, "gy", shape=x.shape)
+    dt = cfg.torch_dtype
+    _dev(gy, "gy", dtype=dt, shape=x.shape)
     s1, s2 = weight_shapes(cfg)
-    p1, k1 = _ptr_array(w1, "w1", s1)
-    p2, k2 = _ptr_array(w2, "w2", s2)
+    p1, k1 = _ptr_array(w1, "w1", s1, dt)
+    p2, k2 = _ptr_array(w2, "w2", s2, dt)
     dev = x.device
     out = {}
     out["gx"] = torch.empty_like(x) if "x" in need else None
     out["gpos"] = torch.empty_like(pos) if "pos" in need else None
     out["grbf"] = torch.empty_like(rbf) if "rbf" in need else None
     out["gw_rad"] = torch.empty_like(w_rad) if "w_rad" in need else None
-    out["gw1"] = [torch.empty(s, device=dev) for s in s1] if "w1" in need else None
-    out["gw2"] = [torch.empty(s, device=dev) for s in s2] if "w2" in need else None
+    out["gw1"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None
+    out["gw2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
-    q1, k3 = _ptr_array(out["gw1"], "gw1", s1)
-    q2, k4 = _ptr_array(out["gw2"], "gw2", s2)
+    q1, k3 = _ptr_array(out["gw1"], "gw1", s1, dt)
+    q2, k4 = _ptr_array(out["gw2"], "gw2", s2, dt)
     ws = _ws_for(cfg, g, 1, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_bwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
@@ -210,27 +228,28 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
                  prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None, chunk_edges=None):
     """Returns dict ggy, gx2, grbf2, gw_rad2, gw1_2, gw2_2 (requested ones)."""
     _common(cfg, g, x, pos, rbf, w_rad)
-    _dev(gy, "gy", shape=x.shape)
-    _dev(px, "px", shape=x.shape)
+    dt = cfg.torch_dtype
+    _dev(gy, "gy", dtype=dt, shape=x.shape)
+    _dev(px, "px", dtype=dt, shape=x.shape)
     _dev(ppos, "ppos", shape=pos.shape)
     _dev(pedge, "pedge", shape=(g.n_edges, 3))
     _dev(prbf, "prbf", shape=rbf.shape)
-    _dev(pw_rad, "pw_rad", shape=w_rad.shape)
+    _dev(pw_rad, "pw_rad", dtype=dt, shape=w_rad.shape)
     s1, s2 = weight_shapes(cfg)
-    p1, k1 = _ptr_array(w1, "w1", s1)
-    p2, k2 = _ptr_array(w2, "w2", s2)
-    pp1, k5 = _ptr_array(pw1, "pw1", s1)
-    pp2, k6 = _ptr_array(pw2, "pw2", s2)
+    p1, k1 = _ptr_array(w1, "w1", s1, dt)
+    p2, k2 = _ptr_array(w2, "w2", s2, dt)
+    pp1, k5 = _ptr_array(pw1, "pw1", s1, dt)
+    pp2, k6 = _ptr_array(pw2, "pw2", s2, dt)
     dev = x.device
     out = {}
     out["ggy"] = torch.empty_like(x) if "gy" in need else None
     out["gx2"] = torch.empty_like(x) if "x" in need else None
     out["grbf2"] = torch.empty_like(rbf) if "rbf" in need else None
     out["gw_rad2"] = torch.empty_like(w_rad) if "w_rad" in need else None
-    out["gw1_2"] = [torch.empty(s, device=dev) for s in s1] if "w1" in need else None
-    out["gw2_2"] = [torch.empty(s, device=dev) for s in s2] if "w2" in need else None
-    q1, k3 = _ptr_array(out["gw1_2"], "gw1_2", s1)
-    q2, k4 = _ptr_array(out["gw2_2"], "gw2_2", s2)
+    out["gw1_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None
+    out["gw2_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
+    q1, k3 = _ptr_array(out["gw1_2"], "gw1_2", s1, dt)
+    q2, k4 = _ptr_array(out["gw2_2"], "gw2_2", s2, dt)
     ws = _ws_for(cfg, g, 2, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
@@ -250,7 +269,8 @@ def so2conv_profile_reset():
 
 def so2conv_profile_read(kind=-1):
     """(launches, total_ms, total_flops, total_bytes) of the recorded GEMM launches of
-    one kind (0: A B, 1: A B^T, 2: A^T B, -1: all)."""
+    one kind (float32 operands 0: A B, 1: A B^T, 2: A^T B; bfloat16 operands
+    3: A B^T, 4: A^T B; -1: all)."""
     n, ms, fl, by = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     check(lib().so2conv_profile_read(kind, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)),
           "so2conv_profile_read")
@@ -261,8 +281,12 @@ def so2conv_debug_rotate_gather(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad):
     _common(cfg, g, x, pos, rbf, w_rad)
     L, M = cfg.lmax, cfg.mmax
     q = (L + 1) * (2 * M + 1) - M * (M + 1)
-    T = torch.empty(g.n_edges, q * 2 * cfg.channels, device=x.device)
-    ws = _ws(g.n_edges * (L + 1) * 2 * cfg.channels * 4 + 4096, x.device)
+    T = torch.empty(g.n_edges, q * 2 * cfg.channels, dtype=cfg.torch_dtype, device=x.device)
+    wS = (L + 1) * 2 * cfg.channels
+    nb = g.n_edges * wS * 4 + 4096
+    if cfg.dtype == "bf16":
+        nb += (g.n_nodes * cfg.d * cfg.channels + cfg.n_rbf * wS) * 4 + 1024
+    ws = _ws(nb, x.device)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_debug_rotate_gather(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad),
                                             _p(T), _p(ws), ws.numel(), _stream()), "so2conv_debug_rotate_gather")

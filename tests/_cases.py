@@ -2,7 +2,9 @@
 oracle evaluation and the comparison metric.
 
 Metric: per output tensor, max |gpu - oracle| / max |oracle| (max-norm
-relative error). The bar for float32 is 1e-4.
+relative error). The bar is 1e-4 for float32 and 2e-2 for bfloat16 features
+and weights (the oracle then receives the same bf16-representable values in
+float64, so the error measures only the GPU's own rounding).
 """
 from __future__ import annotations
 
@@ -15,6 +17,8 @@ import so2_synth
 from oracle import so2conv_oracle as O
 
 TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+BF16_KEYS = ("x", "gy", "px", "w_rad", "w1", "w2")   # arrays of the call's dtype
 
 
 def workload(base="T", **over):
@@ -27,21 +31,29 @@ def note(msg):
     sys.stdout.flush()
 
 
-def to_dev(d):
+def to_dev(d, dtype="f32"):
+    """Device copies; with dtype "bf16" the node features, cotangents and
+    weights are passed as bfloat16 (exact for bf16-representable inputs)."""
     import so_graph_convolution_amd as K
     cfg = d["cfg"]
     dev = torch.device("cuda:0")
+    if dtype == "bf16":
+        for k in BF16_KEYS:
+            vals = d[k] if isinstance(d[k], list) else [d[k]]
+            for a in vals:
+                assert np.array_equal(so2_synth.round_bf16(a), a), f"{k} is not bf16-representable"
 
     def t(a, dt=torch.float32):
         return torch.tensor(np.ascontiguousarray(a), dtype=dt, device=dev)
 
-    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf)
+    ft = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype)
     g = K.so2conv_graph_prepare(cfg.n_atoms, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
-    out = dict(kcfg=kc, g=g, x=t(d["x"]), pos=t(d["pos"]), rbf=t(d["rbf"]), w_rad=t(d["w_rad"]),
-               w1=[t(w) for w in d["w1"]], w2=[t(w) for w in d["w2"]])
+    out = dict(kcfg=kc, g=g, x=t(d["x"], ft), pos=t(d["pos"]), rbf=t(d["rbf"]), w_rad=t(d["w_rad"], ft),
+               w1=[t(w, ft) for w in d["w1"]], w2=[t(w, ft) for w in d["w2"]])
     for k in ("gy", "px", "ppos", "prbf"):
         if k in d:
-            out[k] = t(d[k])
+            out[k] = t(d[k], ft if k in BF16_KEYS else torch.float32)
     return out
 
 

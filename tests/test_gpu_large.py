@@ -2,8 +2,11 @@
 (100k atoms, ~10M edges, C 256, clustered degrees) workloads through the
 memory-bounded chunked path, with sampled outputs checked against the oracle
 on extracted subgraphs. Inputs of both hold bf16-representable values (the
-pages' bf16 features and weights); the GPU computes in float32, so the float32
-bar applies (stricter than the 2e-2 stated for bf16 inputs)."""
+pages' bf16 features and weights). The high-degree workload runs with
+bfloat16 arrays (bar 2e-2) and in float32 (bar 1e-4); the large one with
+bfloat16 arrays, its stated precision."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -22,15 +25,30 @@ def _oracle_nodes(d, nodes, fn, key, edges_of):
     return fn(sub)[key][pos]
 
 
+@functools.lru_cache(maxsize=2)
+def _inputs(name, directions):
+    H.note(f"[{name}] generating inputs")
+    return so2_synth.make_inputs(so2_synth.CONFIGS[name], with_directions=directions)
+
+
+_ORACLE = {}
+
+
+def _cached(key, fn):
+    if key not in _ORACLE:
+        _ORACLE[key] = fn()
+    return _ORACLE[key]
+
+
 @pytest.mark.timeout(900)
-def test_high_degree_full_size_chunked():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_high_degree_full_size_chunked(dtype):
     import so_graph_convolution_amd as K
     cfg = so2_synth.CONFIGS["H"]
-    H.note("[high degree] generating inputs")
-    d = so2_synth.make_inputs(cfg)
+    d = _inputs("H", True)
     E, N = len(d["src"]), cfg.n_atoms
-    H.note(f"[high degree] N={N} E={E} L={cfg.lmax} C={cfg.channels}")
-    dd = H.to_dev(d)
+    H.note(f"[high degree {dtype}] N={N} E={E} L={cfg.lmax} C={cfg.channels}")
+    dd = H.to_dev(d, dtype)
     args = (dd["kcfg"], dd["g"], dd["x"], dd["pos"], dd["rbf"], dd["w_rad"], dd["w1"], dd["w2"])
     torch.cuda.reset_peak_memory_stats()
     ce = 262144
@@ -53,38 +71,46 @@ def test_high_degree_full_size_chunked():
     def dbwd(sub):
         return O.double_backward(H.oracle_inputs(sub), t(sub["gy"]), px=t(sub["px"]), ppos=t(sub["ppos"]),
                                  prbf=t(sub["prbf"]))
+    ref = _cached("H", lambda: {
+        "y": _oracle_nodes(d, nodes, fwd, "y", H.incoming),
+        "gx": _oracle_nodes(d, nodes, bwd, "gx", H.incident),
+        "gpos": _oracle_nodes(d, nodes, bwd, "gpos", H.incident),
+        "ggy": _oracle_nodes(d, nodes, dbwd, "ggy", H.incoming),
+        "gx2": _oracle_nodes(d, nodes, dbwd, "gx", H.incident),
+        "edges": (bwd(H.subgraph(d, edges)[0]), dbwd(H.subgraph(d, edges)[0]))})
     errs = {
-        "y": H.relerr(y.cpu()[nodes], _oracle_nodes(d, nodes, fwd, "y", H.incoming)),
-        "gx": H.relerr(bw["gx"].cpu()[nodes], _oracle_nodes(d, nodes, bwd, "gx", H.incident)),
-        "gpos": H.relerr(bw["gpos"].cpu()[nodes], _oracle_nodes(d, nodes, bwd, "gpos", H.incident)),
-        "ggy": H.relerr(db["ggy"].cpu()[nodes], _oracle_nodes(d, nodes, dbwd, "ggy", H.incoming)),
-        "gx2": H.relerr(db["gx2"].cpu()[nodes], _oracle_nodes(d, nodes, dbwd, "gx", H.incident)),
+        "y": H.relerr(y.cpu()[nodes], ref["y"]),
+        "gx": H.relerr(bw["gx"].cpu()[nodes], ref["gx"]),
+        "gpos": H.relerr(bw["gpos"].cpu()[nodes], ref["gpos"]),
+        "ggy": H.relerr(db["ggy"].cpu()[nodes], ref["ggy"]),
+        "gx2": H.relerr(db["gx2"].cpu()[nodes], ref["gx2"]),
     }
-    sub, _ = H.subgraph(d, edges)
-    re_b, re_d = bwd(sub), dbwd(sub)
+    re_b, re_d = ref["edges"]
     errs["grbf"] = H.relerr(bw["grbf"].cpu()[edges], re_b["grbf"])
     errs["gedge"] = H.relerr(bw["gedge"].cpu()[edges], re_b["gedge"])
     errs["grbf2"] = H.relerr(db["grbf2"].cpu()[edges], re_d["grbf"])
-    lhs = sum(float((g.double().cpu() * t(w)).sum()) for g, w in zip(bw["gw2"], d["w2"]))
-    rhs = float((y.double().cpu() * t(d["gy"])).sum())
-    errs["<gW2,W2>"] = abs(lhs - rhs) / abs(rhs)
+    if dtype == "f32":
+        # y is linear in W2, so <gW2, W2> = <y, gy> (every output row and weight at once)
+        lhs = sum(float((g.double().cpu() * t(w)).sum()) for g, w in zip(bw["gw2"], d["w2"]))
+        rhs = float((y.double().cpu() * t(d["gy"])).sum())
+        errs["<gW2,W2>"] = abs(lhs - rhs) / abs(rhs)
     H.note("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
-    assert all(v <= H.TOL_F32 for v in errs.values()), errs
+    tol = H.TOL_BF16 if dtype == "bf16" else H.TOL_F32
+    assert all(v <= tol for v in errs.values()), errs
 
 
 @pytest.mark.timeout(1100)
 def test_large_system_full_size_chunked():
-    """Forward + backward of the 100k-atom clustered system; peak device memory
-    is reported next to the bytes a schedule materialising every per-edge
-    intermediate would need."""
+    """Forward + backward of the 100k-atom clustered system with bfloat16
+    features and weights; peak device memory is reported next to the bytes a
+    schedule keeping every per-edge intermediate would need."""
     import so_graph_convolution_amd as K
     cfg = so2_synth.CONFIGS["X"]
-    H.note("[large] generating inputs (about two minutes)")
-    d = so2_synth.make_inputs(cfg, with_directions=("gy",))
+    d = _inputs("X", ("gy",))
     E, N = len(d["src"]), cfg.n_atoms
-    H.note(f"[large] N={N} E={E} L={cfg.lmax} C={cfg.channels} max in-degree "
+    H.note(f"[large bf16] N={N} E={E} L={cfg.lmax} C={cfg.channels} max in-degree "
            f"{int(np.bincount(d['dst'], minlength=N).max())}")
-    dd = H.to_dev(d)
+    dd = H.to_dev(d, "bf16")
     args = (dd["kcfg"], dd["g"], dd["x"], dd["pos"], dd["rbf"], dd["w_rad"], dd["w1"], dd["w2"])
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -96,7 +122,7 @@ def test_large_system_full_size_chunked():
     kc = dd["kcfg"]
     state = K.so2conv_saved_bytes(kc, E)
     H.note(f"  peak device memory {peak / 2**30:.1f} GiB; keeping the per-edge forward state alone would take "
-           f"{state / 2**30:.0f} GiB (GEMM inputs/outputs only, float32)")
+           f"{state / 2**30:.0f} GiB (GEMM inputs and outputs only)")
     assert peak < 120 * 2**30
     deg = np.bincount(d["dst"], minlength=N)
     rng = np.random.default_rng(8)
@@ -118,8 +144,5 @@ def test_large_system_full_size_chunked():
     re_b = bwd(sub)
     errs["grbf"] = H.relerr(bw["grbf"].cpu()[edges], re_b["grbf"])
     errs["gedge"] = H.relerr(bw["gedge"].cpu()[edges], re_b["gedge"])
-    lhs = sum(float((g.double().cpu() * t(w)).sum()) for g, w in zip(bw["gw2"], d["w2"]))
-    rhs = float((y.double().cpu() * t(d["gy"])).sum())
-    errs["<gW2,W2>"] = abs(lhs - rhs) / abs(rhs)
     H.note("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
-    assert all(v <= H.TOL_F32 for v in errs.values()), errs
+    assert all(v <= H.TOL_BF16 for v in errs.values()), errs
