@@ -38,7 +38,7 @@ def to_dev(d, dtype="f32"):
     cfg = d["cfg"]
     dev = torch.device("cuda:0")
     if dtype == "bf16":
-        for k in BF16_KEYS:
+        for k in (k for k in BF16_KEYS if k in d):
             vals = d[k] if isinstance(d[k], list) else [d[k]]
             for a in vals:
                 assert np.array_equal(so2_synth.round_bf16(a), a), f"{k} is not bf16-representable"
