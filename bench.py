@@ -13,6 +13,10 @@ exactly as training on forces needs them (TrimSO(2) page, Appendix A.3).
 The JSON line carries the live roofline of the dominant kernel (the
 matrix-core GEMM of the per-order linears, timed with HIP events on its
 stream) and the CPU oracle timed on the host cores on a bounded edge sample.
+
+--config / --dtype select another workload of so2_synth (e.g. the
+EquiformerV3-like high-degree system H with its bfloat16 features and
+weights) for the same step; the default is the medium system in float32.
 """
 from __future__ import annotations
 
@@ -29,7 +33,12 @@ if ROOT not in sys.path:
 
 METRIC = "edges/sec fwd+bwd+dbwd SO(2) conv (lmax=4,C=128); HBM GB/s % of peak"
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0     # dense
 PEAK_HBM_GBS = 8000.0
+WORKLOADS = {"T": "tiny periodic radius graph", "S": "eSEN-like small periodic radius graph",
+             "M": "UMA/eSEN-like medium periodic radius graph", "H": "EquiformerV3-like high-degree periodic radius graph",
+             "X": "large clustered periodic radius graph", "P1": "EquiformerV3 captured-batch-sized radius graph",
+             "P2": "uniform random K-target graph"}
 
 
 def gemm_flops_per_edge(L, M, C):
@@ -41,10 +50,13 @@ def gemm_flops_per_edge(L, M, C):
     return 2.0 * (mac1 + mac2)
 
 
-def measured_gemm_traffic():
+def measured_gemm_traffic(config, dtype):
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    counters (copy-calibrated), or None if the GEMM source changed since."""
+    counters (copy-calibrated) of the medium float32 step, or None for another
+    workload or if the GEMM source changed since."""
     import hashlib
+    if config != "M" or dtype != "f32":
+        return None
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "gemm_hbm_traffic_medium.json")))
         src = open(os.path.join(ROOT, "so_graph_convolution_amd", "csrc", "gemm.hip"), "rb").read()
@@ -84,6 +96,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="M")
+    ap.add_argument("--dtype", choices=("f32", "bf16"), default=None,
+                    help="array dtype (default: the workload's own: f32 for M, bf16 for H and X)")
     ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
@@ -113,6 +127,9 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = so2_synth.CONFIGS[args.config]
+    dtype = args.dtype or cfg.dtype
+    if dtype == "bf16" and cfg.dtype != "bf16":
+        cfg = so2_synth.make_config(args.config, dtype="bf16")   # bf16-representable inputs
     d = so2_synth.make_inputs(cfg)
     progress(f"inputs ready: N={cfg.n_atoms} E={len(d['src'])}")
     E, N = len(d["src"]), cfg.n_atoms
@@ -121,13 +138,21 @@ def main():
     def t(a, dt=torch.float32):
         return torch.tensor(np.ascontiguousarray(a), dtype=dt, device=dev)
 
-    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf)
+    ft = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype)
     g = K.so2conv_graph_prepare(N, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
-    x, pos, rbf, w_rad = t(d["x"]), t(d["pos"]), t(d["rbf"]), t(d["w_rad"])
-    w1, w2 = [t(w) for w in d["w1"]], [t(w) for w in d["w2"]]
-    gy, px, ppos, prbf = t(d["gy"]), t(d["px"]), t(d["ppos"]), t(d["prbf"])
-    saved = torch.empty(K.so2conv_saved_bytes(kc, E), dtype=torch.uint8, device=dev)
-    ws = torch.empty(max(K.so2conv_workspace_bytes(kc, N, E, s) for s in (0, 1, 2)), dtype=torch.uint8, device=dev)
+    x, pos, rbf, w_rad = t(d["x"], ft), t(d["pos"]), t(d["rbf"]), t(d["w_rad"], ft)
+    w1, w2 = [t(w, ft) for w in d["w1"]], [t(w, ft) for w in d["w2"]]
+    gy, px, ppos, prbf = t(d["gy"], ft), t(d["px"], ft), t(d["ppos"]), t(d["prbf"])
+    saved_b = K.so2conv_saved_bytes(kc, E)
+    ws_b = max(K.so2conv_workspace_bytes(kc, N, E, s) for s in (0, 1, 2))
+    chunked = saved_b + ws_b > 200 * 2**30
+    if chunked:   # workspace for chunks of about 256k edges (the library picks the chunk from its size)
+        ws_b = max(K.so2conv_chunked_workspace_bytes(kc, N, E, s, 262144) for s in (0, 1, 2))
+    progress(f"saved state {saved_b / 2**30:.1f} GiB, workspace {ws_b / 2**30:.1f} GiB"
+             + (" (edge chunks)" if chunked else ""))
+    saved = torch.empty(saved_b, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
     args_c = (kc, g, x, pos, rbf, w_rad, w1, w2)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -159,7 +184,8 @@ def main():
     K.so2conv_profile_enable(False)
     n_l, gemm_ms, gemm_fl, gemm_by = K.so2conv_profile_read(-1)
     per_kind = {}
-    for kind, name in ((0, "AB"), (1, "ABt"), (2, "AtB")):
+    kinds = ((3, "ABt"), (4, "AtB")) if dtype == "bf16" else ((0, "AB"), (1, "ABt"), (2, "AtB"))
+    for kind, name in kinds:
         n, ms, fl, by = K.so2conv_profile_read(kind)
         per_kind[name] = {"launches": n, "avg_ms": ms / max(n, 1), "tflops": fl / max(ms, 1e-9) / 1e9,
                           "algorithmic_bytes_per_launch": by / max(n, 1)}
@@ -169,6 +195,9 @@ def main():
     value = E * args.steps / wall
     F = gemm_flops_per_edge(cfg.lmax, cfg.mmax, cfg.channels)
     achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_MFMA_TFLOPS if dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    kname = ("gemm_bf16_kernel (bf16 MFMA" if dtype == "bf16" else "gemm_f32_kernel (fp32 MFMA") + \
+        " per-order linears), all launches of the timed steps"
     out = {
         "metric": METRIC,
         "value": value,
@@ -180,15 +209,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": f"UMA/eSEN-like medium periodic radius graph ({cfg.name})", "n_atoms": N,
+        "config": {"workload": f"{WORKLOADS.get(cfg.name, cfg.name)} ({cfg.name})", "n_atoms": N,
                    "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
-                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": measured_gemm_traffic(),
+                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)",
+                   "edge_chunks": chunked},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": measured_gemm_traffic(args.config, dtype),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
-                     "kernel": "gemm_f32_kernel (fp32 MFMA per-order linears), all launches of the timed steps",
+                     "kernel": kname,
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
                      "algorithmic_flops_per_step": gemm_fl / args.steps, "per_kind": per_kind},
         "stage_ms": {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean()), "dbwd": float(st[:, 2].mean())},
