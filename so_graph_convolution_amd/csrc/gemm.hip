@@ -271,24 +271,37 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
 
 
 // ---------------------------------------------------------------- bfloat16 operands
-// LDS tiles hold every operand k-contiguous: row r of a tile is 32 bf16 (four
-// 16-byte chunks of 8 k values) at a pitch of 20 dwords, and the chunks of
-// rows 8..15 of every 16 rows are swapped pairwise. An MFMA operand read is
-// one 16-byte chunk per lane (row lane%32, chunk 2*ks + lane/32); with the
-// pitch, any 8 consecutive rows of one chunk fall on disjoint banks, and the
-// swap keeps the transposing stores of k-major operands (below) off each
-// other's banks.
+// Block tile 256x256 of 16 waves (64x64 each, 2x2 v_mfma_f32_32x32x16_bf16),
+// K tile 64, one block per CU (147 KB of LDS for two stages). Measured on
+// MI355X for the per-order shapes (725k rows): 256x128 blocks with K tile 32
+// reached 425-700 TFLOP/s for A.B^T and 375-515 for A^T.B; this tiling
+// 495-805 and 453-652 (the longer K tile gives the next tile's loads more MFMA
+// time to land behind).
+//
+// LDS tiles hold every operand k-contiguous: row r of a tile is BKH bf16 (16-byte
+// chunks of 8 k values) at a pitch of BKH/2 + 4 dwords, and the chunks of rows
+// 8..15 of every 16 rows are swapped pairwise. An MFMA operand read is one
+// 16-byte chunk per lane (row lane%32, chunk 2*ks + lane/32); with the pitch,
+// any 8 consecutive rows of one chunk fall on disjoint banks, and the swap
+// keeps the transposing stores of k-major operands (below) off each other's
+// banks.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int BKH = 32;
-constexpr int PD = 20;
+constexpr int BMH = 256, BNH = 256;          // block tile
+constexpr int NWH = (BMH / 64) * (BNH / 64);  // waves (64x64 wave tiles)
+constexpr int NTH = 64 * NWH;                 // threads
+constexpr int BKH = 64;                       // K tile
+constexpr int PD = BKH / 2 + 4;               // LDS row pitch (dwords)
+constexpr int CPR = BKH / 8;                  // 16-byte chunks per row
+static_assert(kGemmKTile % BKH == 0 && kGemmKTile % BK_TILE == 0, "split chunks must be whole K tiles");
 
 __device__ __forceinline__ int lds_chunk(int row, int q) { return row * PD + 4 * (q ^ ((row >> 3) & 1)); }
 
 template <int R>
 struct CfgH {
-  static constexpr int TILE = R * PD;        // dwords of one staged tile
-  static constexpr int NKC = R * 4 / NT;     // 16-byte chunks per thread of a k-contiguous tile
+  static constexpr int NKC = (R * CPR + NTH - 1) / NTH;        // 16-byte chunks per thread, k-contiguous operand
+  static constexpr int UNITS = R * BKH / 16;                   // 8k x 2row units of a k-major operand
+  static constexpr int NKM = (UNITS + NTH - 1) / NTH;
 };
 
 // k-contiguous operand (global [row][k]): one 16-byte chunk per load
@@ -298,10 +311,10 @@ __device__ inline void ldh_kc(const unsigned short* __restrict__ P, int ld, int 
   const int t = threadIdx.x;
 #pragma unroll
   for (int p = 0; p < CfgH<R>::NKC; ++p) {
-    const int idx = p * NT + t, row = idx >> 2, q = idx & 3;
+    const int idx = p * NTH + t, row = idx / CPR, q = idx % CPR;
     const int gr = r0 + row, gk = k0 + 8 * q;
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (gr < rlim && gk < kend) {
+    if (idx < R * CPR && gr < rlim && gk < kend) {
       const unsigned short* src = P + (size_t)gr * ld + gk;
       if (gk + 8 <= kend) {
         x = *reinterpret_cast<const u32x4*>(src);
@@ -320,57 +333,63 @@ __device__ inline void sth_kc(unsigned* S, const u32x4 (&v)[CfgH<R>::NKC]) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int p = 0; p < CfgH<R>::NKC; ++p) {
-    const int idx = p * NT + t;
-    *reinterpret_cast<u32x4*>(S + lds_chunk(idx >> 2, idx & 3)) = v[p];
+    const int idx = p * NTH + t;
+    if (idx < R * CPR) *reinterpret_cast<u32x4*>(S + lds_chunk(idx / CPR, idx % CPR)) = v[p];
   }
 }
 
-// k-major operand (global [k][row]): thread t < 2R takes the unit of rows
-// (2c, 2c+1) x k (8g .. 8g+7), c = t % (R/2), g = t / (R/2): eight 4-byte
-// loads (consecutive lanes on consecutive row pairs), transposed in registers
-// into one 16-byte chunk per row.
+// k-major operand (global [k][row]): unit u = (rows 2c, 2c+1) x (k 8g .. 8g+7),
+// c = u % (R/2), g = u / (R/2): eight 4-byte loads (consecutive lanes on
+// consecutive row pairs), transposed in registers into one 16-byte chunk per row.
 template <int R>
 __device__ inline void ldh_km(const unsigned short* __restrict__ P, int ld, int r0, int rlim, int k0, int kend,
-                              unsigned (&w)[8]) {
+                              unsigned (&w)[CfgH<R>::NKM][8]) {
   const int t = threadIdx.x;
-  const int c = t % (R / 2), g = t / (R / 2);
-  const int gr = r0 + 2 * c;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = 0u;
-  if (t >= 2 * R) return;
+  for (int p = 0; p < CfgH<R>::NKM; ++p) {
+    const int u = p * NTH + t;
+    const int c = u % (R / 2), g = u / (R / 2);
+    const int gr = r0 + 2 * c;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int gk = k0 + 8 * g + j;
-    if (gk < kend) {
-      const unsigned short* src = P + (size_t)gk * ld + gr;
-      if (gr + 1 < rlim) w[j] = *reinterpret_cast<const unsigned*>(src);
-      else if (gr < rlim) w[j] = src[0];
+    for (int j = 0; j < 8; ++j) {
+      unsigned x = 0u;
+      const int gk = k0 + 8 * g + j;
+      if (u < CfgH<R>::UNITS && gk < kend) {
+        const unsigned short* src = P + (size_t)gk * ld + gr;
+        if (gr + 1 < rlim) x = *reinterpret_cast<const unsigned*>(src);
+        else if (gr < rlim) x = src[0];
+      }
+      w[p][j] = x;
     }
   }
 }
 
 template <int R>
-__device__ inline void sth_km(unsigned* S, const unsigned (&w)[8]) {
+__device__ inline void sth_km(unsigned* S, const unsigned (&w)[CfgH<R>::NKM][8]) {
   const int t = threadIdx.x;
-  if (t >= 2 * R) return;
-  const int c = t % (R / 2), g = t / (R / 2);
-  u32x4 lo, hi;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[i] = (w[2 * i] & 0xffffu) | (w[2 * i + 1] << 16);
-    hi[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xffff0000u);
+  for (int p = 0; p < CfgH<R>::NKM; ++p) {
+    const int u = p * NTH + t;
+    if (u >= CfgH<R>::UNITS) continue;
+    const int c = u % (R / 2), g = u / (R / 2);
+    u32x4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = (w[p][2 * i] & 0xffffu) | (w[p][2 * i + 1] << 16);
+      hi[i] = (w[p][2 * i] >> 16) | (w[p][2 * i + 1] & 0xffff0000u);
+    }
+    *reinterpret_cast<u32x4*>(S + lds_chunk(2 * c, g)) = lo;
+    *reinterpret_cast<u32x4*>(S + lds_chunk(2 * c + 1, g)) = hi;
   }
-  *reinterpret_cast<u32x4*>(S + lds_chunk(2 * c, g)) = lo;
-  *reinterpret_cast<u32x4*>(S + lds_chunk(2 * c + 1, g)) = hi;
 }
 
 // TA = false: C = A.B^T (both operands k-contiguous); TA = true: C = A^T.B
 // (both k-major)
 template <bool TA>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, 8))) void gemm_bf16_kernel(
-    GemmBatch batch) {
-  __shared__ unsigned As[2][CfgH<BM>::TILE];
-  __shared__ unsigned Bs[2][CfgH<BN>::TILE];
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_bf16_kernel(GemmBatch batch) {
+  constexpr int NWN = BNH / 64;
+  __shared__ unsigned As[2][BMH * PD];
+  __shared__ unsigned Bs[2][BNH * PD];
 
   int pi, local;
   decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
@@ -379,14 +398,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   const int split = local / per_split;
   local -= split * per_split;
   const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BMH, n0 = tn * BNH;
   const int kbeg = split * p.k_chunk;
   const int kend = min(p.K, kbeg + p.k_chunk);
   const unsigned short* A = static_cast<const unsigned short*>(p.A);
   const unsigned short* B = static_cast<const unsigned short*>(p.B);
 
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int li = lane % 32, lk = lane / 32;
 
   floatx16 acc[WM][WN];
@@ -398,24 +417,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int nk = (kend - kbeg + BKH - 1) / BKH;
-  u32x4 ra[TA ? 1 : CfgH<BM>::NKC], rb[TA ? 1 : CfgH<BN>::NKC];
-  unsigned wa[8], wb[8];
+  u32x4 ra[TA ? 1 : CfgH<BMH>::NKC], rb[TA ? 1 : CfgH<BNH>::NKC];
+  unsigned wa[TA ? CfgH<BMH>::NKM : 1][8], wb[TA ? CfgH<BNH>::NKM : 1][8];
   auto load = [&](int k0) {
     if constexpr (TA) {
-      ldh_km<BM>(A, p.lda, m0, p.M, k0, kend, wa);
-      ldh_km<BN>(B, p.ldb, n0, p.N, k0, kend, wb);
+      ldh_km<BMH>(A, p.lda, m0, p.M, k0, kend, wa);
+      ldh_km<BNH>(B, p.ldb, n0, p.N, k0, kend, wb);
     } else {
-      ldh_kc<BM>(A, p.lda, m0, p.M, k0, kend, ra);
-      ldh_kc<BN>(B, p.ldb, n0, p.N, k0, kend, rb);
+      ldh_kc<BMH>(A, p.lda, m0, p.M, k0, kend, ra);
+      ldh_kc<BNH>(B, p.ldb, n0, p.N, k0, kend, rb);
     }
   };
   auto store = [&](int buf) {
     if constexpr (TA) {
-      sth_km<BM>(As[buf], wa);
-      sth_km<BN>(Bs[buf], wb);
+      sth_km<BMH>(As[buf], wa);
+      sth_km<BNH>(Bs[buf], wb);
     } else {
-      sth_kc<BM>(As[buf], ra);
-      sth_kc<BN>(Bs[buf], rb);
+      sth_kc<BMH>(As[buf], ra);
+      sth_kc<BNH>(Bs[buf], rb);
     }
   };
   if (nk > 0) {
@@ -469,11 +488,12 @@ __global__ void gemm_reduce_kernel(const float* __restrict__ P, int splits, int 
 int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   constexpr int BK = BK_TILE;
   if (bf16 && TA == TB) return hipErrorInvalidValue;
+  const int bm = bf16 ? BMH : BM, bn = bf16 ? BNH : BN;
   int total = 0;
   for (int q = 0; q < b.nprob; ++q) {
     GemmProb& p = b.p[q];
-    p.tiles_m = (p.M + BM - 1) / BM;
-    p.tiles_n = (p.N + BN - 1) / BN;
+    p.tiles_m = (p.M + bm - 1) / bm;
+    p.tiles_n = (p.N + bn - 1) / bn;
     if (p.k_splits < 1) p.k_splits = 1;
     if (p.k_splits == 1 && p.k_chunk <= 0) p.k_chunk = p.K;
     p.tile_begin = total;
@@ -483,8 +503,8 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   if (total == 0) return hipSuccess;
   dim3 grid(total), block(NT);
   if (bf16) {
-    if (TA) hipLaunchKernelGGL((gemm_bf16_kernel<true>), grid, block, 0, s, b);
-    else hipLaunchKernelGGL((gemm_bf16_kernel<false>), grid, block, 0, s, b);
+    if (TA) hipLaunchKernelGGL((gemm_bf16_kernel<true>), grid, dim3(NTH), 0, s, b);
+    else hipLaunchKernelGGL((gemm_bf16_kernel<false>), grid, dim3(NTH), 0, s, b);
     return hipGetLastError();
   }
   if (!TA && !TB) hipLaunchKernelGGL((gemm_f32_kernel<false, false, BK>), grid, block, 0, s, b);

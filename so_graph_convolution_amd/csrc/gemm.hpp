@@ -46,7 +46,7 @@ struct GemmBatch {
 int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s);
 
 // K tile of the kernels: split chunks of TA problems are multiples of it
-constexpr int kGemmKTile = 32;
+constexpr int kGemmKTile = 64;
 
 // C[i*ldc + j] (+)= sum_{s < splits} P[s][i][j]  (fixed order)
 int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s);
