@@ -139,8 +139,10 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
  *   L = <px, gx> + <ppos, gpos> + <pedge, gedge> + <prbf, grbf> + <pw, gw>
  * (the backward's outputs paired with directions; NULL direction = zero) with
  * respect to gy (ggy = the forward's directional derivative, Eq.(5)), x (gx2),
- * rbf (grbf2), w_rad, w1, w2. gpos2 (second derivatives in positions) is not
- * provided by this version and must be NULL. */
+ * pos (gpos2 [N,3] float32, through the frames and their rotation rates;
+ * rbf is an input, so its dependence on positions is the caller's chain
+ * rule through grbf2), rbf (grbf2), w_rad, w1, w2. Any output may be NULL;
+ * gpos2 costs a further pass over the rotation's generator rows. */
 int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
                  const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
                  const void* px, const float* ppos, const float* pedge, const float* prbf, const void* pw_rad,

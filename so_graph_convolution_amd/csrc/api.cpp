@@ -304,13 +304,13 @@ void layout_bwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute,
 
 struct DbwdWs {
   LinBuf W1, W2, pW1, pW2;
-  float *gW1r, *gW2r;
+  float *gW1r, *gW2r, *vbar2_all, *p2e, *p2d, *p2s;
   float *w_rad32, *pw_rad32, *x32, *px32, *gy32, *ggy32, *gx2_32, *gw_rad2_32;
   PrimalBuf pr;
   void *Tdot, *Zdot, *G2, *UU;
   float *Sdot, *omega, *Udot, *Vdot, *ZZ, *TT, *Sbar, *Sdb, *P;
 };
-void layout_dbwd(Arena& ar, const Ctx& c, int N, long ec, bool recompute, DbwdWs* w) {
+void layout_dbwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute, DbwdWs* w) {
   const Dims& d = c.d;
   const size_t e = (size_t)ec;
   w->W1 = take_lin(ar, c, 0);
@@ -319,6 +319,10 @@ void layout_dbwd(Arena& ar, const Ctx& c, int N, long ec, bool recompute, DbwdWs
   w->pW2 = take_lin(ar, c, 1);
   w->gW1r = ar.take(realified_size(d, 0));
   w->gW2r = ar.take(realified_size(d, 1));
+  w->vbar2_all = ar.take((size_t)E * 3);      // position derivative per edge vector (all edges)
+  w->p2e = ar.take(e * 6);
+  w->p2d = ar.take(e * 6);
+  w->p2s = ar.take(e * 6);
   const size_t nf = (size_t)N * c.node_floats(), rf = (size_t)c.n_rbf * c.wS();
   w->w_rad32 = c.bf ? ar.take(rf) : nullptr;
   w->pw_rad32 = c.bf ? ar.take(rf) : nullptr;
@@ -357,7 +361,7 @@ size_t ws_need(const Ctx& c, int N, long E, long ec, int stage, bool recompute) 
     layout_bwd(ar, c, N, E, ec, recompute, &w);
   } else {
     DbwdWs w;
-    layout_dbwd(ar, c, N, ec, recompute, &w);
+    layout_dbwd(ar, c, N, E, ec, recompute, &w);
   }
   return ar.used + 4096;
 }
@@ -882,7 +886,6 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
-  if (gpos2) return fail(SO2_EUNSUPPORTED, "gpos2 (position second derivatives) is not provided; pass NULL");
   if ((r = ensure_init())) return r;
   const bool has_pw1 = !all_null(pw1, d.M + 1), has_pw2 = !all_null(pw2, d.M + 1);
   if (has_pw1)
@@ -894,7 +897,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   hipStream_t s = (hipStream_t)stream;
   const int n_rbf = c.n_rbf, wS = c.wS();
   if (gd.E == 0) {
-    int rr = zero_grads(c, gd.N, gx2, nullptr, gw_rad2, gw1_2, gw2_2, s);
+    int rr = zero_grads(c, gd.N, gx2, gpos2, gw_rad2, gw1_2, gw2_2, s);
     if (rr) return rr;
     if (ggy) return zero(c, ggy, (size_t)gd.N * c.node_floats(), s);
     return SO2_OK;
@@ -905,7 +908,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   if (ec == 0) return fail(SO2_EWORKSPACE, "double-backward workspace too small for a 1024-edge chunk");
   Arena ar{static_cast<char*>(ws), 0};
   DbwdWs w;
-  layout_dbwd(ar, c, gd.N, ec, recompute, &w);
+  layout_dbwd(ar, c, gd.N, gd.E, ec, recompute, &w);
   const size_t nf = (size_t)gd.N * c.node_floats(), rf = (size_t)n_rbf * wS;
   const float *x32, *px32, *gy32, *wr32, *pwr32;
   if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
@@ -957,7 +960,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
     if (ggy_acc) SO2_HIP(launch_node_dual(d, gc, pos, w.omega, pr.V, w.Vdot, ggy_acc, acc, s));
 
     // ---- reverse of the tangent output with cotangent gy
-    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, s));
+    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, pr.V, w.Vdot, gpos2 ? w.p2e : nullptr, s));
     // [Zdot_bar; Zbar] = G2 W2^T (2n stacked rows)
     if ((r = run_lin(c, 1, true, w.G2, w.ZZ, W2, 2 * n, 0, s))) return r;
     // Zbar += tbar pW2^T
@@ -979,7 +982,9 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
       const long rows[2] = {n, n};
       if ((r = run_lin_grad(c, 0, in, out, rows, 2, w.gW1r, acc, w.P, s))) return r;
     }
-    SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, w.TT, gx2_acc, w.Sbar, w.Sdb, acc, s));
+    SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, w.TT, gx2_acc, w.Sbar, w.Sdb,
+                                 gpos2 ? w.p2d : nullptr, gpos2 ? w.p2s : nullptr, acc, s));
+    if (gpos2) SO2_HIP(launch_pos2(gc, pos, ppos, pedge, w.omega, w.p2e, w.p2d, w.p2s, w.vbar2_all, s));
     if (grbf2) {
       float* out = grbf2 + (size_t)e0 * n_rbf;
       std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, out, n_rbf, n, n_rbf, wS)};
@@ -996,6 +1001,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   }
   if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r, gw2_2, c.bf, s));
   if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r, gw1_2, c.bf, s));
+  if (gpos2) SO2_HIP(launch_node_pos(gd, w.vbar2_all, gpos2, s));
   if ((r = f32_out(c, ggy_acc, ggy, nf, s))) return r;
   if ((r = f32_out(c, gx2_acc, gx2, nf, s))) return r;
   return f32_out(c, gwr2_acc, gw_rad2, rf, s);

@@ -223,17 +223,26 @@ struct NodeDual {
 };
 
 // ------------------------------------------------------------------ edge_bwd_dual
-template <int L, int M, typename OT>
+// G2 = [R gy; Rdot gy] per edge. With P2 (position derivatives of the double
+// backward) it also writes, per edge, the rotation torque and rotation-rate
+// cotangent of ydot = sum_e (Rdot^T V + R^T Vdot):
+//   p2[e][k]     = Vdot^T (R G_k) gy + V^T (Rdot G_k) gy   (<Rbar, R G_k> + <Rdotbar, Rdot G_k>)
+//   p2[e][3 + k] = V^T (R G_k) gy                           (<Rdotbar, R G_k>)
+template <int L, int M, typename OT, bool P2>
 __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                             const float* __restrict__ omega,
-                                                            const float* __restrict__ gy, OT* __restrict__ G2) {
-  constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+                                                            const float* __restrict__ gy, OT* __restrict__ G2,
+                                                            const float* __restrict__ V,
+                                                            const float* __restrict__ Vdot, float* __restrict__ p2) {
+  constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 6 * k_count(L, M) + 24 : 0)>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
+  __shared__ float sRL[P2 ? TE * 3 * K : 1], sRdL[P2 ? TE * 3 * K : 1];
+  __shared__ float sRed[P2 ? TE * 4 * 6 : 1];
   __shared__ int sDst[TE];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
@@ -248,11 +257,19 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   __syncthreads();
   wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
   rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
+  if (P2) {
+    __syncthreads();
+    rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
+    rot_generator_products(L, M, ne, sRd, K, sRdL, 3 * K);
+  }
   __syncthreads();
   const int C = d.C, wZ = d.wZ();
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    for (int t = 0; t < ne; ++t) {
-      const long e = e0 + t - g.e0;   // chunk-relative row
+  const int c = threadIdx.x, lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const bool act = c < C;
+  for (int t = 0; t < ne; ++t) {
+    const long e = e0 + t - g.e0;   // chunk-relative row
+    float tk[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (act) {
       float gv[D];
       const float* gr = gy + (size_t)sDst[t] * D * C + c;
 #pragma unroll
@@ -272,30 +289,81 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
           st(r2 + mm_col(l, m, 0, L, C), row_dot<L>(rd, gv + l * l, n));
         }
       }
+      if (P2) {   // a pass of its own: no stores between the generator-row loads
+        const float* vr = V + (size_t)e * wZ + c;
+        const float* vdr = Vdot + (size_t)e * wZ + c;
+#pragma unroll
+        for (int l = 0; l <= L; ++l) {
+          const int q = qhalf(l, M), n = 2 * l + 1;
+#pragma unroll
+          for (int m = -q; m <= q; ++m) {
+            const int off = rot_off(l, M) + (m + q) * n;
+            const float v = vr[mm_col(l, m, 0, L, C)], vd = vdr[mm_col(l, m, 0, L, C)];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+              float gk[2 * L + 1], gdk[2 * L + 1];
+              load_row<L>(sRL + t * 3 * K + k * K, off, n, gk);
+              load_row<L>(sRdL + t * 3 * K + k * K, off, n, gdk);
+              const float a = row_dot<L>(gk, gv + l * l, n), b = row_dot<L>(gdk, gv + l * l, n);
+              tk[k] += vd * a + v * b;
+              tk[3 + k] += v * a;
+            }
+          }
+        }
+      }
+    }
+    if (P2) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        const float sum = wave_sum(tk[k]);
+        if (lane == 0) sRed[(t * 4 + wave) * 6 + k] = sum;
+      }
+    }
+  }
+  if (P2) {
+    __syncthreads();
+    const int nw = blockDim.x / 64;
+    for (int idx = threadIdx.x; idx < ne * 6; idx += blockDim.x) {
+      const int t = idx / 6, k = idx - t * 6;
+      float sum = 0.f;
+      for (int w = 0; w < nw; ++w) sum += sRed[(t * 4 + w) * 6 + k];
+      p2[(e0 + t - g.e0) * 6 + k] = sum;
     }
   }
 }
 
 template <int L, int M>
 struct EdgeBwdDual {
-  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, void* G2,
-                 int bf16, hipStream_t s) {
-    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+  template <typename OT, bool P2>
+  static void go(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, void* G2,
+                 const float* V, const float* Vdot, float* p2, hipStream_t s) {
+    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 6 * k_count(L, M) + 24 : 0)>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
-    if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
-    if (bf16)
-      hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M, bf16s>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy,
-                         static_cast<bf16s*>(G2));
-    else
-      hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M, float>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy,
-                         static_cast<float*>(G2));
+    hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M, OT, P2>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy,
+                       static_cast<OT*>(G2), V, Vdot, p2);
+  }
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, void* G2,
+                 int bf16, const float* V, const float* Vdot, float* p2, hipStream_t s) {
+    if (g.e1 <= g.e0) return hipSuccess;
+    if (bf16) {
+      if (p2) go<bf16s, true>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
+      else go<bf16s, false>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
+    } else {
+      if (p2) go<float, true>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
+      else go<float, false>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
+    }
     return hipGetLastError();
   }
 };
 
 // ------------------------------------------------------------------ node_bwd_dual
-template <int L, int M>
+// With P2 it also writes, per edge of each half, the torque and rotation-rate
+// cotangent of the rotation on gather in the tangent forward (T = S (R a),
+// Tdot = Sdot (R a) + S (Rdot a + R adot)), with Tbar, Tdotbar their cotangents:
+//   p2[e][k]     = (S Tbar + Sdot Tdotbar)^T (R G_k) a + (S Tdotbar)^T ((R G_k) adot + (Rdot G_k) a)
+//   p2[e][3 + k] = (S Tdotbar)^T (R G_k) a
+template <int L, int M, bool P2>
 __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ x,
                                                             const float* __restrict__ px,
                                                             const float* __restrict__ pos,
@@ -304,14 +372,17 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
                                                             const float* __restrict__ Sdot,
                                                             const float* __restrict__ TT, float* __restrict__ gx2,
                                                             float* __restrict__ Sbar, float* __restrict__ Sdb,
+                                                            float* __restrict__ p2_dst, float* __restrict__ p2_src,
                                                             int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 6 * k_count(L, M) + 48 : 0)>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
+  __shared__ float sRL[P2 ? TE * 3 * K : 1], sRdL[P2 ? TE * 3 * K : 1];
+  __shared__ float sRed[P2 ? TE * 8 * 6 : 1];
   __shared__ int sE[TE];
   __shared__ float sComb[kCombFallback];
 
@@ -320,6 +391,7 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
   const int CW = blockDim.x / 2;
   const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
   const bool act = c < C;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, wpg = CW / 64;
   float xn[D], xdn[D], acc[D];
 #pragma unroll
   for (int r = 0; r < D; ++r) {
@@ -334,6 +406,7 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
     int beg, end;
     if (pass == 0) in_range(g, node, &beg, &end);
     else out_range(g, node, &beg, &end);
+    float* p2_out = pass == 0 ? p2_dst : p2_src;
     for (int t0 = beg; t0 < end; t0 += TE) {
       const int ne = min(TE, end - t0);
       for (int t = threadIdx.x; t < ne; t += blockDim.x) {
@@ -347,10 +420,16 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
       __syncthreads();
       wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
       rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
+      if (P2) {
+        __syncthreads();
+        rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
+        rot_generator_products(L, M, ne, sRd, K, sRdL, 3 * K);
+      }
       __syncthreads();
-      if (act) {
-        const int cin = pass == 0 ? C + c : c;
-        for (int t = grp; t < ne; t += 2) {
+      const int cin = pass == 0 ? C + c : c;
+      for (int t = grp; t < ne; t += 2) {
+        float tk[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (act) {
           const long e = sE[t];
           const float* tdb = Tdb + (size_t)e * wT + cin;
           const float* tb = Tb + (size_t)e * wT + cin;
@@ -375,12 +454,41 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
               const float y1 = row_dot<L>(rd, xn + l * l, n);
               sb += a1 * (y1 + y2) + a0 * xt;
               sdb += a1 * xt;
-              row_axpy<L>(r, sv * a0 + sdv * a1, acc + l * l, n);
-              row_axpy<L>(rd, sv * a1, acc + l * l, n);
+              const float u1 = sv * a0 + sdv * a1, u2 = sv * a1;
+              row_axpy<L>(r, u1, acc + l * l, n);
+              row_axpy<L>(rd, u2, acc + l * l, n);
+              if (P2) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                  float gk[2 * L + 1], gdk[2 * L + 1];
+                  load_row<L>(sRL + t * 3 * K + k * K, off, n, gk);
+                  load_row<L>(sRdL + t * 3 * K + k * K, off, n, gdk);
+                  const float ga = row_dot<L>(gk, xn + l * l, n);
+                  tk[k] += u1 * ga + u2 * (row_dot<L>(gk, xdn + l * l, n) + row_dot<L>(gdk, xn + l * l, n));
+                  tk[3 + k] += u2 * ga;
+                }
+              }
             }
             Sbar[(size_t)e * wS + l * Ci + cin] = sb;
             Sdb[(size_t)e * wS + l * Ci + cin] = sdb;
           }
+        }
+        if (P2) {
+#pragma unroll
+          for (int k = 0; k < 6; ++k) {
+            const float sum = wave_sum(tk[k]);
+            if (lane == 0) sRed[(t * 8 + wave) * 6 + k] = sum;
+          }
+        }
+      }
+      if (P2) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < ne * 6; idx += blockDim.x) {
+          const int t = idx / 6, k = idx - t * 6;
+          const int w0 = (t % 2) * wpg;   // waves of the group that handled edge t
+          float sum = 0.f;
+          for (int w = w0; w < w0 + wpg; ++w) sum += sRed[(t * 8 + w) * 6 + k];
+          p2_out[(size_t)sE[t] * 6 + k] = sum;
         }
       }
       __syncthreads();
@@ -397,14 +505,53 @@ template <int L, int M>
 struct NodeBwdDual {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
                  const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2, float* Sbar,
-                 float* Sdb, int accumulate, hipStream_t s) {
+                 float* Sdb, float* p2_dst, float* p2_src, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = 2 * ((d.C + 63) / 64) * 64;
-    hipLaunchKernelGGL((node_bwd_dual_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega, S, Sdot,
-                       TT, gx2, Sbar, Sdb, accumulate);
+    if (p2_dst)
+      hipLaunchKernelGGL((node_bwd_dual_kernel<L, M, true>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega,
+                         S, Sdot, TT, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
+    else
+      hipLaunchKernelGGL((node_bwd_dual_kernel<L, M, false>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega,
+                         S, Sdot, TT, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
     return hipGetLastError();
   }
 };
+
+// ------------------------------------------------------------------ position derivatives (double backward)
+// Per edge: the frame depends on r = v/|v| (v = pos[src] - pos[dst] + shift)
+// and the tangent rotation rate is w = (dv x v)/|v|^2 (dv = ppos[src] -
+// ppos[dst] + pedge). With the torque tau of R (including Rdot = R W, whose
+// R-dependence adds <Rdotbar, Rdot G_k> + (w x wbar)_k through the so(3)
+// commutators) and the rate cotangent wbar:
+//   vbar2 = r x tau / |v| + (wbar x dv)/|v|^2 - 2 (wbar . w) v/|v|^2
+__global__ void pos2_kernel(GraphDev g, const float* __restrict__ pos, const float* __restrict__ ppos,
+                            const float* __restrict__ pedge, const float* __restrict__ omega,
+                            const float* __restrict__ pe, const float* __restrict__ pd, const float* __restrict__ ps,
+                            float* __restrict__ vbar2) {
+  for (long e = g.e0 + (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.e1; e += (long)gridDim.x * blockDim.x) {
+    const long le = e - g.e0;
+    const int j = g.src[e], i = g.dst[e];
+    float v[3], dv[3] = {0.f, 0.f, 0.f}, w[3], tau[3], wb[3];
+    for (int k = 0; k < 3; ++k) {
+      v[k] = pos[3 * j + k] - pos[3 * i + k] + (g.shift ? g.shift[3 * e + k] : 0.f);
+      if (ppos) dv[k] = ppos[3 * j + k] - ppos[3 * i + k];
+      if (pedge) dv[k] += pedge[3 * e + k];
+      w[k] = omega[3 * le + k];
+      tau[k] = pe[6 * le + k] + pd[6 * le + k] + ps[6 * le + k];
+      wb[k] = pe[6 * le + 3 + k] + pd[6 * le + 3 + k] + ps[6 * le + 3 + k];
+    }
+    tau[0] += w[1] * wb[2] - w[2] * wb[1];
+    tau[1] += w[2] * wb[0] - w[0] * wb[2];
+    tau[2] += w[0] * wb[1] - w[1] * wb[0];
+    const float rho2 = v[0] * v[0] + v[1] * v[1] + v[2] * v[2], inv2 = 1.f / rho2, inv = sqrtf(inv2);
+    const float r[3] = {v[0] * inv, v[1] * inv, v[2] * inv};
+    const float wbw = 2.f * (wb[0] * w[0] + wb[1] * w[1] + wb[2] * w[2]);
+    vbar2[3 * e] = (r[1] * tau[2] - r[2] * tau[1]) * inv + (wb[1] * dv[2] - wb[2] * dv[1] - wbw * v[0]) * inv2;
+    vbar2[3 * e + 1] = (r[2] * tau[0] - r[0] * tau[2]) * inv + (wb[2] * dv[0] - wb[0] * dv[2] - wbw * v[1]) * inv2;
+    vbar2[3 * e + 2] = (r[0] * tau[1] - r[1] * tau[0]) * inv + (wb[0] * dv[1] - wb[1] * dv[0] - wbw * v[2]) * inv2;
+  }
+}
 
 // ------------------------------------------------------------------ gates
 template <typename OT>
@@ -510,8 +657,16 @@ int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const f
 }
 
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
-                         void* G2, int bf16, hipStream_t s) {
-  return dispatch_lm<EdgeBwdDual>(d.L, d.M, d, g, pos, omega, gy, G2, bf16, s);
+                         void* G2, int bf16, const float* V, const float* Vdot, float* p2, hipStream_t s) {
+  return dispatch_lm<EdgeBwdDual>(d.L, d.M, d, g, pos, omega, gy, G2, bf16, V, Vdot, p2, s);
+}
+
+int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const float* pedge, const float* omega,
+                const float* pe, const float* pd, const float* ps, float* vbar2, hipStream_t s) {
+  const long n = g.e1 - g.e0;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pos2_kernel, dim3(grid_for(n)), dim3(256), 0, s, g, pos, ppos, pedge, omega, pe, pd, ps, vbar2);
+  return hipGetLastError();
 }
 
 int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, void* UU, int bf16,
@@ -529,8 +684,9 @@ int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, c
 
 int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
                          const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
-                         float* Sbar, float* Sdot_bar, int accumulate, hipStream_t s) {
-  return dispatch_lm<NodeBwdDual>(d.L, d.M, d, g, x, px, pos, omega, S, Sdot, TT, gx2, Sbar, Sdot_bar, accumulate, s);
+                         float* Sbar, float* Sdot_bar, float* p2_dst, float* p2_src, int accumulate, hipStream_t s) {
+  return dispatch_lm<NodeBwdDual>(d.L, d.M, d, g, x, px, pos, omega, S, Sdot, TT, gx2, Sbar, Sdot_bar, p2_dst, p2_src,
+                                  accumulate, s);
 }
 
 }  // namespace so2

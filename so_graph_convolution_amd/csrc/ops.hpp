@@ -64,16 +64,22 @@ int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, v
 // ydot[i] = sum_e Rdot^T V + R^T Vdot
 int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
                      const float* Vdot, float* ydot, int accumulate, hipStream_t s);
-// G2 (operand) rows [0,E) = R gy[dst], rows [E,2E) = Rdot gy[dst]
+// G2 (operand) rows [0,E) = R gy[dst], rows [E,2E) = Rdot gy[dst]; with p2 (not null)
+// also the per-edge torque and rate cotangent [E][6] of ydot's rotations
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
-                         void* G2, int bf16, hipStream_t s);
+                         void* G2, int bf16, const float* V, const float* Vdot, float* p2, hipStream_t s);
+// vbar2[e] (global edge index) = position derivative of the double backward per edge vector,
+// from the three [E][6] torque/rate parts (chunk-relative rows)
+int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const float* pedge, const float* omega,
+                const float* pe, const float* pd, const float* ps, float* vbar2, hipStream_t s);
 // from ZZ = [Zdot_bar; Zbar] produce UU (operand) = [Udot_bar; Ubar]
 int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, void* UU, int bf16,
                      hipStream_t s);
-// gx2 and (Sbar, Sdot_bar) from TT = [Tdot_bar; Tbar]
+// gx2 and (Sbar, Sdot_bar) from TT = [Tdot_bar; Tbar]; with p2_dst/p2_src (not null) also the
+// per-edge torque and rate cotangent [E][6] of the rotation on gather, per half
 int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
                          const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
-                         float* Sbar, float* Sdot_bar, int accumulate, hipStream_t s);
+                         float* Sbar, float* Sdot_bar, float* p2_dst, float* p2_src, int accumulate, hipStream_t s);
 
 // ---- weights
 // Wr (realified per order): block 0 = W[0]; block m = [[W_m0, W_m1], [-W_m1, W_m0]].

@@ -221,12 +221,13 @@ def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy,
     return out
 
 
-DBWD_KEYS = ("gy", "x", "rbf", "w_rad", "w1", "w2")
+DBWD_KEYS = ("gy", "x", "rbf", "w_rad", "w1", "w2")   # the force-training pattern; add "pos" for gpos2
 
 
 def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, px=None, ppos=None, pedge=None,
                  prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None, chunk_edges=None):
-    """Returns dict ggy, gx2, grbf2, gw_rad2, gw1_2, gw2_2 (requested ones)."""
+    """Returns dict ggy, gx2, gpos2, grbf2, gw_rad2, gw1_2, gw2_2 (requested ones; gpos2
+    only when "pos" is in need)."""
     _common(cfg, g, x, pos, rbf, w_rad)
     dt = cfg.torch_dtype
     _dev(gy, "gy", dtype=dt, shape=x.shape)
@@ -244,6 +245,7 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     out = {}
     out["ggy"] = torch.empty_like(x) if "gy" in need else None
     out["gx2"] = torch.empty_like(x) if "x" in need else None
+    out["gpos2"] = torch.empty_like(pos) if "pos" in need else None
     out["grbf2"] = torch.empty_like(rbf) if "rbf" in need else None
     out["gw_rad2"] = torch.empty_like(w_rad) if "w_rad" in need else None
     out["gw1_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None
@@ -254,7 +256,8 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
                              _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf), _p(pw_rad), pp1, pp2,
-                             _p(out["ggy"]), _p(out["gx2"]), None, _p(out["grbf2"]), _p(out["gw_rad2"]), q1, q2,
+                             _p(out["ggy"]), _p(out["gx2"]), _p(out["gpos2"]), _p(out["grbf2"]), _p(out["gw_rad2"]),
+                             q1, q2,
                              _p(ws), ws.numel(), _stream()), "so2conv_dbwd")
     return out
 
