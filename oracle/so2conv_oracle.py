@@ -163,16 +163,21 @@ def _rot_z(psi: torch.Tensor) -> torch.Tensor:
 
 # ----------------------------------------------------------------------------- inputs
 class OracleInputs:
-    """float64 torch views of one workload (indices stay int64)."""
+    """float64 torch views of one workload (indices stay int64). `env` ([E] or
+    None) is the optional per-edge cutoff envelope that scales each message
+    before the receiver sum (TrimSO(2) page, Appendix C.1 Implementation: eSEN
+    and UMA sum messages with their cutoff envelopes)."""
 
-    def __init__(self, lmax, mmax, channels, pos, x, src, dst, shift, rbf, w_rad, w1, w2):
+    def __init__(self, lmax, mmax, channels, pos, x, src, dst, shift, rbf, w_rad, w1, w2, env=None):
         self.L, self.M, self.C = lmax, mmax, channels
         self.pos, self.x, self.rbf, self.w_rad = pos, x, rbf, w_rad
         self.w1, self.w2 = list(w1), list(w2)
         self.src, self.dst, self.shift = src, dst, shift
+        self.env = env
 
     def leaves(self):
-        return [self.x, self.pos, self.rbf, self.w_rad] + self.w1 + self.w2
+        return [self.x, self.pos, self.rbf, self.w_rad] + self.w1 + self.w2 + \
+            ([self.env] if self.env is not None else [])
 
 
 def to_oracle_inputs(d: dict, requires_grad=False) -> OracleInputs:
@@ -184,7 +189,8 @@ def to_oracle_inputs(d: dict, requires_grad=False) -> OracleInputs:
     return OracleInputs(cfg.lmax, cfg.mmax, cfg.channels, t(d["pos"]), t(d["x"]),
                         torch.tensor(d["src"], dtype=torch.int64), torch.tensor(d["dst"], dtype=torch.int64),
                         torch.tensor(np.asarray(d["shift"], np.float64), dtype=DT), t(d["rbf"]),
-                        t(d["w_rad"]), [t(w) for w in d["w1"]], [t(w) for w in d["w2"]])
+                        t(d["w_rad"]), [t(w) for w in d["w1"]], [t(w) for w in d["w2"]],
+                        t(d["env"]) if d.get("env") is not None else None)
 
 
 # ----------------------------------------------------------------------------- forward
@@ -290,6 +296,8 @@ def _scatter(inp: OracleInputs, e_idx, msgs, n_nodes):
     y = torch.zeros(n_nodes, d, inp.C, dtype=DT)
     dst = inp.dst[e_idx]
     for l, msg in enumerate(msgs):
+        if inp.env is not None:
+            msg = msg * inp.env[e_idx][:, None, None]
         y[:, l * l:(l + 1) * (l + 1), :] = y[:, l * l:(l + 1) * (l + 1), :].index_add(0, dst, msg)
     return y
 
@@ -315,13 +323,15 @@ def _grads(out, wrt, grad_out, create_graph=False):
 def backward(inp: OracleInputs, gy: torch.Tensor, chunk=4096, edges=None, with_edge_grad=False):
     """Vector-Jacobian product of `forward` with cotangent gy.
 
-    Returns dict with gx, gpos, grbf, gw_rad, gw1 (list), gw2 (list) and, if
-    requested, gedge [E,3] = dL/dv_e (derivative with respect to each edge vector)."""
+    Returns dict with gx, gpos, grbf, gw_rad, gw1 (list), gw2 (list), genv (if
+    the inputs carry an envelope) and, if requested, gedge [E,3] = dL/dv_e
+    (derivative with respect to each edge vector)."""
     leaves = [t.detach().requires_grad_(True) for t in inp.leaves()]
     nw = len(inp.w1)
+    has_env = inp.env is not None
     inp2 = OracleInputs(inp.L, inp.M, inp.C, leaves[1], leaves[0], inp.src, inp.dst,
                         inp.shift.detach().clone().requires_grad_(with_edge_grad), leaves[2], leaves[3],
-                        leaves[4:4 + nw], leaves[4 + nw:])
+                        leaves[4:4 + nw], leaves[4 + nw:4 + 2 * nw], leaves[4 + 2 * nw] if has_env else None)
     N = inp.x.shape[0]
     acc = [torch.zeros_like(t) for t in leaves]
     gedge = torch.zeros_like(inp.shift) if with_edge_grad else None
@@ -334,24 +344,30 @@ def backward(inp: OracleInputs, gy: torch.Tensor, chunk=4096, edges=None, with_e
         if with_edge_grad:
             gedge += g[-1]
     out = dict(gx=acc[0], gpos=acc[1], grbf=acc[2], gw_rad=acc[3],
-               gw1=acc[4:4 + nw], gw2=acc[4 + nw:])
+               gw1=acc[4:4 + nw], gw2=acc[4 + nw:4 + 2 * nw])
+    if has_env:
+        out["genv"] = acc[4 + 2 * nw]
     if with_edge_grad:
         out["gedge"] = gedge
     return out
 
 
 def double_backward(inp: OracleInputs, gy: torch.Tensor, px=None, ppos=None, prbf=None,
-                    pw_rad=None, pw1=None, pw2=None, pedge=None, chunk=2048, edges=None):
-    """Derivatives of L = <px, gx> + <ppos, gpos> + <prbf, grbf> + <pW, gW> (+ <pedge, gedge>),
-    where (gx, gpos, grbf, gW, gedge) = backward(inp, gy), with respect to
-    gy (-> ggy), x, pos, rbf, W_rad, W1, W2. None directions are zero."""
+                    pw_rad=None, pw1=None, pw2=None, pedge=None, penv=None, chunk=2048, edges=None):
+    """Derivatives of L = <px, gx> + <ppos, gpos> + <prbf, grbf> + <pW, gW> (+ <pedge, gedge>)
+    (+ <penv, genv>), where (gx, gpos, grbf, gW, gedge, genv) = backward(inp, gy), with
+    respect to gy (-> ggy), x, pos, rbf, W_rad, W1, W2 and the envelope (-> genv, if
+    the inputs carry one). None directions are zero."""
     leaves = [t.detach().requires_grad_(True) for t in inp.leaves()]
     gyl = gy.detach().clone().requires_grad_(True)
     nw = len(inp.w1)
+    has_env = inp.env is not None
     shift = inp.shift.detach().clone().requires_grad_(pedge is not None)
     inp2 = OracleInputs(inp.L, inp.M, inp.C, leaves[1], leaves[0], inp.src, inp.dst, shift,
-                        leaves[2], leaves[3], leaves[4:4 + nw], leaves[4 + nw:])
-    dirs = [px, ppos, prbf, pw_rad] + list(pw1 or [None] * nw) + list(pw2 or [None] * nw)
+                        leaves[2], leaves[3], leaves[4:4 + nw], leaves[4 + nw:4 + 2 * nw],
+                        leaves[4 + 2 * nw] if has_env else None)
+    dirs = [px, ppos, prbf, pw_rad] + list(pw1 or [None] * nw) + list(pw2 or [None] * nw) + \
+        ([penv] if has_env else [])
     N = inp.x.shape[0]
     acc = [torch.zeros_like(t) for t in leaves]
     accgy = torch.zeros_like(gy)
@@ -369,5 +385,8 @@ def double_backward(inp: OracleInputs, gy: torch.Tensor, px=None, ppos=None, prb
         for k in range(len(leaves)):
             acc[k] += h[k]
         accgy += h[-1]
-    return dict(ggy=accgy, gx=acc[0], gpos=acc[1], grbf=acc[2], gw_rad=acc[3],
-                gw1=acc[4:4 + nw], gw2=acc[4 + nw:])
+    out = dict(ggy=accgy, gx=acc[0], gpos=acc[1], grbf=acc[2], gw_rad=acc[3],
+               gw1=acc[4:4 + nw], gw2=acc[4 + nw:4 + 2 * nw])
+    if has_env:
+        out["genv"] = acc[4 + 2 * nw]
+    return out

@@ -153,7 +153,7 @@ def test_mmax0_needs_only_harmonics():
 # ----------------------------------------------------------------------------- derivatives
 def _perturbed(inp, which, p, eps):
     new = O.OracleInputs(inp.L, inp.M, inp.C, inp.pos, inp.x, inp.src, inp.dst, inp.shift,
-                         inp.rbf, inp.w_rad, list(inp.w1), list(inp.w2))
+                         inp.rbf, inp.w_rad, list(inp.w1), list(inp.w2), inp.env)
     if which == "w1":
         new.w1 = [w + eps * q for w, q in zip(inp.w1, p)]
     elif which == "w2":
