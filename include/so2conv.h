@@ -17,6 +17,11 @@
  *   Node features x, y, gx, gy, px, ggy, gx2: [N, d, C] of the call's dtype.
  *   pos, gpos, ppos: [N, 3] float32.  shift, gedge, pedge: [E, 3] float32.
  *   rbf, grbf, prbf: [E, n_rbf] float32 (n_rbf a multiple of 4).
+ *   env, genv, penv, genv2: [E] float32, the optional per-edge cutoff envelope
+ *   (Appendix C.1: eSEN and UMA sum messages with their cutoff envelopes):
+ *   y_i = sum_{e -> i} env_e (J D_e)^T t_e. NULL env = no envelope (then genv,
+ *   penv and genv2 must be NULL). Like rbf it is an input: its dependence on
+ *   positions is the caller's chain rule through genv / genv2.
  *   w_rad: [n_rbf, (L+1) * 2C], column (l, c_in), c_in < C: source channels.
  *   w1[0]: [(L+1)*2C, (L+1)*C + L*C]  rows (l, c_in); columns (l, c) then the
  *          gate columns (l = 1..L, c).
@@ -123,31 +128,32 @@ size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges);
 /* Forward: y [N,d,C]. `saved` (may be NULL) receives the state needed by
  * so2conv_bwd / so2conv_dbwd for the same inputs. */
 int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
-                const void* w_rad, const void* const* w1, const void* const* w2, void* y, void* saved, void* ws,
-                size_t ws_bytes, void* stream);
+                const float* env, const void* w_rad, const void* const* w1, const void* const* w2, void* y,
+                void* saved, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward (vector-Jacobian product with cotangent gy, Section 3.3): gx, gpos,
- * grbf, gw_rad, gw1[m], gw2[m] and gedge = dL/dv_e (for virials). `saved`
+ * grbf, genv, gw_rad, gw1[m], gw2[m] and gedge = dL/dv_e (for virials). `saved`
  * comes from so2conv_fwd on the same inputs, or is NULL (the forward state is
  * recomputed chunk by chunk). gw1/gw2 may be NULL, or hold NULL entries. */
 int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
-                const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
-                void* gx, float* gpos, float* grbf, void* gw_rad, void* const* gw1, void* const* gw2, float* gedge,
-                void* ws, size_t ws_bytes, void* stream);
+                const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
+                const void* gy, void* gx, float* gpos, float* grbf, float* genv, void* gw_rad, void* const* gw1,
+                void* const* gw2, float* gedge, void* ws, size_t ws_bytes, void* stream);
 
 /* Double backward: derivatives of
- *   L = <px, gx> + <ppos, gpos> + <pedge, gedge> + <prbf, grbf> + <pw, gw>
+ *   L = <px, gx> + <ppos, gpos> + <pedge, gedge> + <prbf, grbf> + <penv, genv> + <pw, gw>
  * (the backward's outputs paired with directions; NULL direction = zero) with
  * respect to gy (ggy = the forward's directional derivative, Eq.(5)), x (gx2),
  * pos (gpos2 [N,3] float32, through the frames and their rotation rates;
  * rbf is an input, so its dependence on positions is the caller's chain
- * rule through grbf2), rbf (grbf2), w_rad, w1, w2. Any output may be NULL;
+ * rule through grbf2), rbf (grbf2), env (genv2), w_rad, w1, w2. Any output may be NULL;
  * gpos2 costs a further pass over the rotation's generator rows. */
 int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
-                 const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
-                 const void* px, const float* ppos, const float* pedge, const float* prbf, const void* pw_rad,
-                 const void* const* pw1, const void* const* pw2, void* ggy, void* gx2, float* gpos2, float* grbf2,
-                 void* gw_rad2, void* const* gw1_2, void* const* gw2_2, void* ws, size_t ws_bytes, void* stream);
+                 const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
+                 const void* gy, const void* px, const float* ppos, const float* pedge, const float* prbf,
+                 const float* penv, const void* pw_rad, const void* const* pw1, const void* const* pw2, void* ggy,
+                 void* gx2, float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1_2,
+                 void* const* gw2_2, void* ws, size_t ws_bytes, void* stream);
 
 /* Test hook: the first linear's m-major input T (rotation on gather,
  * Appendix B.1) [E, q*2C], block |m| = 0..M: block 0 columns (l, c_in), block

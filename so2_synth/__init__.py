@@ -226,6 +226,14 @@ def _weights(rng, cfg: Config):
     return w_rad, w1, w2
 
 
+def cosine_envelope(d: dict) -> np.ndarray:
+    """Caller-side cutoff envelope per edge, 0.5 (cos(pi rho / rc) + 1) of the edge
+    length (a smooth cutoff used as synthetic envelope input; float32)."""
+    v = d["pos"][d["src"]].astype(np.float64) - d["pos"][d["dst"]] + d["shift"]
+    rho = np.sqrt((v * v).sum(1))
+    return (0.5 * (np.cos(np.pi * rho / d["cfg"].rc) + 1.0)).astype(np.float32)
+
+
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), returned as float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)

@@ -737,8 +737,8 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
 }
 
 int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
-                const void* w_rad, const void* const* w1, const void* const* w2, void* y, void* saved, void* ws,
-                size_t ws_bytes, void* stream) {
+                const float* env, const void* w_rad, const void* const* w1, const void* const* w2, void* y,
+                void* saved, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   Ctx c;
   GraphDev gd;
@@ -766,7 +766,7 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
   if (gd.E == 0) {
     GraphDev gc = gd;
     gc.e0 = gc.e1 = 0;
-    SO2_HIP(launch_node_fwd(d, gc, pos, nullptr, y32, 0, s));
+    SO2_HIP(launch_node_fwd(d, gc, pos, nullptr, nullptr, y32, 0, s));
     return f32_out(c, y32, y, nf, s);
   }
   for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
@@ -784,15 +784,15 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
       p.V = reinterpret_cast<float*>(st + sl.V) + (size_t)e0 * d.wZ();
     }
     if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, lin_of(w.W1), lin_of(w.W2), p, s))) return r;
-    SO2_HIP(launch_node_fwd(d, gc, pos, p.V, y32, k > 0, s));
+    SO2_HIP(launch_node_fwd(d, gc, pos, p.V, env, y32, k > 0, s));
   }
   return f32_out(c, y32, y, nf, s);
 }
 
 int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
-                const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
-                void* gx, float* gpos, float* grbf, void* gw_rad, void* const* gw1, void* const* gw2, float* gedge,
-                void* ws, size_t ws_bytes, void* stream) {
+                const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
+                const void* gy, void* gx, float* gpos, float* grbf, float* genv, void* gw_rad, void* const* gw1,
+                void* const* gw2, float* gedge, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   Ctx c;
   GraphDev gd;
@@ -801,6 +801,7 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
   const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
+  if (genv && !env) return fail(SO2_EINVAL, "genv requested without an envelope");
   if ((r = ensure_init())) return r;
   hipStream_t s = (hipStream_t)stream;
   const int n_rbf = c.n_rbf, wS = c.wS();
@@ -838,7 +839,7 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
       pr = saved_rows(c, saved, gd.E, e0);
     }
     // E -> N transpose: tbar = R gy[dst], tau1 = rotation torque of <V, R gy>
-    SO2_HIP(launch_edge_bwd(d, gc, pos, gy32, pr.V, w.tbar, w.tau1, c.bf, s));
+    SO2_HIP(launch_edge_bwd(d, gc, pos, gy32, pr.V, env, w.tbar, w.tau1, genv, c.bf, s));
     if ((r = run_lin(c, 1, true, w.tbar, w.Zbar, W2, n, 0, s))) return r;
     if (want_w2) {
       const void* in[1] = {pr.Z};
@@ -874,10 +875,11 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
 }
 
 int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
-                 const void* w_rad, const void* const* w1, const void* const* w2, const void* saved, const void* gy,
-                 const void* px, const float* ppos, const float* pedge, const float* prbf, const void* pw_rad,
-                 const void* const* pw1, const void* const* pw2, void* ggy, void* gx2, float* gpos2, float* grbf2,
-                 void* gw_rad2, void* const* gw1_2, void* const* gw2_2, void* ws, size_t ws_bytes, void* stream) {
+                 const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
+                 const void* gy, const void* px, const float* ppos, const float* pedge, const float* prbf,
+                 const float* penv, const void* pw_rad, const void* const* pw1, const void* const* pw2, void* ggy,
+                 void* gx2, float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1_2,
+                 void* const* gw2_2, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   Ctx c;
   GraphDev gd;
@@ -886,6 +888,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
+  if ((penv || genv2) && !env) return fail(SO2_EINVAL, "penv or genv2 given without an envelope");
   if ((r = ensure_init())) return r;
   const bool has_pw1 = !all_null(pw1, d.M + 1), has_pw2 = !all_null(pw2, d.M + 1);
   if (has_pw1)
@@ -957,10 +960,11 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
     if ((r = run_lin(c, 1, false, w.Zdot, w.Vdot, W2, n, 0, s))) return r;
     if (has_pw2 && (r = run_lin(c, 1, false, pr.Z, w.Vdot, pW2, n, 1, s))) return r;
     // dL/dgy = the forward's directional derivative (Eq.(5))
-    if (ggy_acc) SO2_HIP(launch_node_dual(d, gc, pos, w.omega, pr.V, w.Vdot, ggy_acc, acc, s));
+    if (ggy_acc) SO2_HIP(launch_node_dual(d, gc, pos, w.omega, pr.V, w.Vdot, env, penv, ggy_acc, acc, s));
 
     // ---- reverse of the tangent output with cotangent gy
-    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, pr.V, w.Vdot, gpos2 ? w.p2e : nullptr, s));
+    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, pr.V, w.Vdot, env, penv,
+                                 gpos2 ? w.p2e : nullptr, genv2, s));
     // [Zdot_bar; Zbar] = G2 W2^T (2n stacked rows)
     if ((r = run_lin(c, 1, true, w.G2, w.ZZ, W2, 2 * n, 0, s))) return r;
     // Zbar += tbar pW2^T

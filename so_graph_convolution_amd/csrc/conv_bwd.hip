@@ -36,17 +36,20 @@ constexpr int tile_edges() {
 __device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
 // ------------------------------------------------------------------ edge_bwd
+// With an envelope (env, per edge) the message is env_e V_e: tbar and the
+// torque scale by env_e, and genv_e = <V_e, R_e gy[dst]>.
 template <int L, int M, typename OT>
 __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                        const float* __restrict__ gy, const float* __restrict__ V,
-                                                       OT* __restrict__ tbar, float* __restrict__ tau) {
+                                                       const float* __restrict__ env, OT* __restrict__ tbar,
+                                                       float* __restrict__ tau, float* __restrict__ genv) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRL[TE * 3 * K];
-  __shared__ float sRed[TE * 4 * 3];
+  __shared__ float sRed[TE * 4 * 4];
   __shared__ int sDst[TE];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
@@ -68,7 +71,8 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   const bool act = c < C;
   for (int t = 0; t < ne; ++t) {
     const long e = e0 + t - g.e0;   // chunk-relative row
-    float tk[3] = {0.f, 0.f, 0.f};
+    const float ev = env ? env[e0 + t] : 1.f;
+    float tk[4] = {0.f, 0.f, 0.f, 0.f};
     if (act) {
       float gv[D];
       const float* gr = gy + (size_t)sDst[t] * D * C + c;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
         const int q = qhalf(l, M);
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
-          st(tr + mm_col(l, m, 0, L, C), o[ridx(l, m, M)]);
+          st(tr + mm_col(l, m, 0, L, C), ev * o[ridx(l, m, M)]);
           vv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
         }
       }
@@ -95,39 +99,43 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < Q; ++j) s += vv[j] * w[j];
-        tk[k] = s;
+        tk[k] = ev * s;
       }
-    }
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
+      for (int j = 0; j < Q; ++j) tk[3] += vv[j] * o[j];
+    }
+    const int nr = genv ? 4 : 3;
+    for (int k = 0; k < nr; ++k) {
       const float s = wave_sum(tk[k]);
-      if (lane == 0) sRed[(t * 4 + wave) * 3 + k] = s;
+      if (lane == 0) sRed[(t * 4 + wave) * 4 + k] = s;
     }
   }
   __syncthreads();
   const int nw = blockDim.x / 64;
-  for (int idx = threadIdx.x; idx < ne * 3; idx += blockDim.x) {
-    const int t = idx / 3, k = idx - t * 3;
+  for (int idx = threadIdx.x; idx < ne * 4; idx += blockDim.x) {
+    const int t = idx / 4, k = idx - t * 4;
+    if (k == 3 && !genv) continue;
     float s = 0.f;
-    for (int w = 0; w < nw; ++w) s += sRed[(t * 4 + w) * 3 + k];
-    tau[(e0 + t - g.e0) * 3 + k] = s;
+    for (int w = 0; w < nw; ++w) s += sRed[(t * 4 + w) * 4 + k];
+    if (k < 3) tau[(e0 + t - g.e0) * 3 + k] = s;
+    else genv[e0 + t] = s;
   }
 }
 
 template <int L, int M>
 struct EdgeBwd {
-  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, void* tbar,
-                 float* tau, int bf16, hipStream_t s) {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V,
+                 const float* env, void* tbar, float* tau, float* genv, int bf16, hipStream_t s) {
     constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
     if (bf16)
-      hipLaunchKernelGGL((edge_bwd_kernel<L, M, bf16s>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V,
-                         static_cast<bf16s*>(tbar), tau);
+      hipLaunchKernelGGL((edge_bwd_kernel<L, M, bf16s>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V, env,
+                         static_cast<bf16s*>(tbar), tau, genv);
     else
-      hipLaunchKernelGGL((edge_bwd_kernel<L, M, float>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V,
-                         static_cast<float*>(tbar), tau);
+      hipLaunchKernelGGL((edge_bwd_kernel<L, M, float>), dim3(nb), dim3(threads), 0, s, d, g, pos, gy, V, env,
+                         static_cast<float*>(tbar), tau, genv);
     return hipGetLastError();
   }
 };
@@ -347,9 +355,9 @@ inline int grid_for(long n) {
 
 }  // namespace
 
-int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, void* tbar,
-                    float* tau, int bf16, hipStream_t s) {
-  return dispatch_lm<EdgeBwd>(d.L, d.M, d, g, pos, gy, V, tbar, tau, bf16, s);
+int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V,
+                    const float* env, void* tbar, float* tau, float* genv, int bf16, hipStream_t s) {
+  return dispatch_lm<EdgeBwd>(d.L, d.M, d, g, pos, gy, V, env, tbar, tau, genv, bf16, s);
 }
 
 int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, void* Ubar, int bf16, hipStream_t s) {

@@ -151,7 +151,8 @@ struct EdgeDual {
 template <int L, int M>
 __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                         const float* __restrict__ omega, const float* __restrict__ V,
-                                                        const float* __restrict__ Vdot, float* __restrict__ ydot,
+                                                        const float* __restrict__ Vdot, const float* __restrict__ env,
+                                                        const float* __restrict__ penv, float* __restrict__ ydot,
                                                         int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
@@ -187,6 +188,8 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
       for (int t = grp; t < ne; t += 2) {
         const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
         const float* vd = Vdot + (size_t)(t0 + t - g.e0) * wZ + c;
+        // message env V: tangent env (Rdot^T V + R^T Vdot) + penv R^T V
+        const float ev = env ? env[t0 + t] : 1.f, pv = penv ? penv[t0 + t] : 0.f;
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
           const int q = qhalf(l, M), n = 2 * l + 1;
@@ -197,8 +200,8 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
             float r[2 * L + 1], rd[2 * L + 1];
             load_row<L>(sR + t * K, off, n, r);
             load_row<L>(sRd + t * K, off, n, rd);
-            row_axpy<L>(rd, v, acc + l * l, n);
-            row_axpy<L>(r, vdv, acc + l * l, n);
+            row_axpy<L>(rd, ev * v, acc + l * l, n);
+            row_axpy<L>(r, ev * vdv + pv * v, acc + l * l, n);
           }
         }
       }
@@ -213,11 +216,11 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
 template <int L, int M>
 struct NodeDual {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
-                 const float* Vdot, float* ydot, int accumulate, hipStream_t s) {
+                 const float* Vdot, const float* env, const float* penv, float* ydot, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = 2 * ((d.C + 63) / 64) * 64;
-    hipLaunchKernelGGL((node_dual_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, pos, omega, V, Vdot, ydot,
-                       accumulate);
+    hipLaunchKernelGGL((node_dual_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, pos, omega, V, Vdot, env,
+                       penv, ydot, accumulate);
     return hipGetLastError();
   }
 };
@@ -228,21 +231,27 @@ struct NodeDual {
 // cotangent of ydot = sum_e (Rdot^T V + R^T Vdot):
 //   p2[e][k]     = Vdot^T (R G_k) gy + V^T (Rdot G_k) gy   (<Rbar, R G_k> + <Rdotbar, Rdot G_k>)
 //   p2[e][3 + k] = V^T (R G_k) gy                           (<Rdotbar, R G_k>)
+// With an envelope the tangent message is env (Rdot^T V + R^T Vdot) + penv R^T V:
+// G2 = [env R gy; env Rdot gy + penv R gy], the torque terms scale alike, and
+// genv2_e = <Rdot gy, V> + <R gy, Vdot>.
 template <int L, int M, typename OT, bool P2>
 __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                             const float* __restrict__ omega,
                                                             const float* __restrict__ gy, OT* __restrict__ G2,
                                                             const float* __restrict__ V,
-                                                            const float* __restrict__ Vdot, float* __restrict__ p2) {
+                                                            const float* __restrict__ Vdot,
+                                                            const float* __restrict__ env,
+                                                            const float* __restrict__ penv, float* __restrict__ p2,
+                                                            float* __restrict__ genv2) {
   constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 6 * k_count(L, M) + 24 : 0)>();
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + 28 + (P2 ? 6 * k_count(L, M) : 0)>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
   __shared__ float sRL[P2 ? TE * 3 * K : 1], sRdL[P2 ? TE * 3 * K : 1];
-  __shared__ float sRed[P2 ? TE * 4 * 6 : 1];
+  __shared__ float sRed[TE * 4 * 7];
   __shared__ int sDst[TE];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
@@ -268,7 +277,8 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   const bool act = c < C;
   for (int t = 0; t < ne; ++t) {
     const long e = e0 + t - g.e0;   // chunk-relative row
-    float tk[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float ev = env ? env[e0 + t] : 1.f, pv = penv ? penv[e0 + t] : 0.f;
+    float tk[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (act) {
       float gv[D];
       const float* gr = gy + (size_t)sDst[t] * D * C + c;
@@ -276,6 +286,8 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
       for (int r = 0; r < D; ++r) gv[r] = gr[(size_t)r * C];
       OT* r1 = G2 + (size_t)e * wZ + c;
       OT* r2 = G2 + ((size_t)(g.e1 - g.e0) + e) * wZ + c;
+      const float* vr0 = V + (size_t)e * wZ + c;
+      const float* vdr0 = Vdot + (size_t)e * wZ + c;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const int q = qhalf(l, M), n = 2 * l + 1;
@@ -285,8 +297,10 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
           float r[2 * L + 1], rd[2 * L + 1];
           load_row<L>(sR + t * K, off, n, r);
           load_row<L>(sRd + t * K, off, n, rd);
-          st(r1 + mm_col(l, m, 0, L, C), row_dot<L>(r, gv + l * l, n));
-          st(r2 + mm_col(l, m, 0, L, C), row_dot<L>(rd, gv + l * l, n));
+          const float s1 = row_dot<L>(r, gv + l * l, n), s2 = row_dot<L>(rd, gv + l * l, n);
+          st(r1 + mm_col(l, m, 0, L, C), ev * s1);
+          st(r2 + mm_col(l, m, 0, L, C), ev * s2 + pv * s1);
+          if (genv2) tk[6] += vr0[mm_col(l, m, 0, L, C)] * s2 + vdr0[mm_col(l, m, 0, L, C)] * s1;
         }
       }
       if (P2) {   // a pass of its own: no stores between the generator-row loads
@@ -305,8 +319,8 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
               load_row<L>(sRL + t * 3 * K + k * K, off, n, gk);
               load_row<L>(sRdL + t * 3 * K + k * K, off, n, gdk);
               const float a = row_dot<L>(gk, gv + l * l, n), b = row_dot<L>(gdk, gv + l * l, n);
-              tk[k] += vd * a + v * b;
-              tk[3 + k] += v * a;
+              tk[k] += ev * (vd * a + v * b) + pv * v * a;
+              tk[3 + k] += ev * v * a;
             }
           }
         }
@@ -316,18 +330,24 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
         const float sum = wave_sum(tk[k]);
-        if (lane == 0) sRed[(t * 4 + wave) * 6 + k] = sum;
+        if (lane == 0) sRed[(t * 4 + wave) * 7 + k] = sum;
       }
     }
+    if (genv2) {
+      const float sum = wave_sum(tk[6]);
+      if (lane == 0) sRed[(t * 4 + wave) * 7 + 6] = sum;
+    }
   }
-  if (P2) {
+  if (P2 || genv2) {
     __syncthreads();
     const int nw = blockDim.x / 64;
-    for (int idx = threadIdx.x; idx < ne * 6; idx += blockDim.x) {
-      const int t = idx / 6, k = idx - t * 6;
+    for (int idx = threadIdx.x; idx < ne * 7; idx += blockDim.x) {
+      const int t = idx / 7, k = idx - t * 7;
+      if ((k < 6 && !P2) || (k == 6 && !genv2)) continue;
       float sum = 0.f;
-      for (int w = 0; w < nw; ++w) sum += sRed[(t * 4 + w) * 6 + k];
-      p2[(e0 + t - g.e0) * 6 + k] = sum;
+      for (int w = 0; w < nw; ++w) sum += sRed[(t * 4 + w) * 7 + k];
+      if (k < 6) p2[(e0 + t - g.e0) * 6 + k] = sum;
+      else genv2[e0 + t] = sum;
     }
   }
 }
@@ -336,22 +356,24 @@ template <int L, int M>
 struct EdgeBwdDual {
   template <typename OT, bool P2>
   static void go(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, void* G2,
-                 const float* V, const float* Vdot, float* p2, hipStream_t s) {
-    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 6 * k_count(L, M) + 24 : 0)>();
+                 const float* V, const float* Vdot, const float* env, const float* penv, float* p2, float* genv2,
+                 hipStream_t s) {
+    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + 28 + (P2 ? 6 * k_count(L, M) : 0)>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     const int threads = ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M, OT, P2>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy,
-                       static_cast<OT*>(G2), V, Vdot, p2);
+                       static_cast<OT*>(G2), V, Vdot, env, penv, p2, genv2);
   }
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, void* G2,
-                 int bf16, const float* V, const float* Vdot, float* p2, hipStream_t s) {
+                 int bf16, const float* V, const float* Vdot, const float* env, const float* penv, float* p2,
+                 float* genv2, hipStream_t s) {
     if (g.e1 <= g.e0) return hipSuccess;
     if (bf16) {
-      if (p2) go<bf16s, true>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
-      else go<bf16s, false>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
+      if (p2) go<bf16s, true>(d, g, pos, omega, gy, G2, V, Vdot, env, penv, p2, genv2, s);
+      else go<bf16s, false>(d, g, pos, omega, gy, G2, V, Vdot, env, penv, p2, genv2, s);
     } else {
-      if (p2) go<float, true>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
-      else go<float, false>(d, g, pos, omega, gy, G2, V, Vdot, p2, s);
+      if (p2) go<float, true>(d, g, pos, omega, gy, G2, V, Vdot, env, penv, p2, genv2, s);
+      else go<float, false>(d, g, pos, omega, gy, G2, V, Vdot, env, penv, p2, genv2, s);
     }
     return hipGetLastError();
   }
@@ -652,13 +674,15 @@ int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, v
 }
 
 int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
-                     const float* Vdot, float* ydot, int accumulate, hipStream_t s) {
-  return dispatch_lm<NodeDual>(d.L, d.M, d, g, pos, omega, V, Vdot, ydot, accumulate, s);
+                     const float* Vdot, const float* env, const float* penv, float* ydot, int accumulate,
+                     hipStream_t s) {
+  return dispatch_lm<NodeDual>(d.L, d.M, d, g, pos, omega, V, Vdot, env, penv, ydot, accumulate, s);
 }
 
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
-                         void* G2, int bf16, const float* V, const float* Vdot, float* p2, hipStream_t s) {
-  return dispatch_lm<EdgeBwdDual>(d.L, d.M, d, g, pos, omega, gy, G2, bf16, V, Vdot, p2, s);
+                         void* G2, int bf16, const float* V, const float* Vdot, const float* env, const float* penv,
+                         float* p2, float* genv2, hipStream_t s) {
+  return dispatch_lm<EdgeBwdDual>(d.L, d.M, d, g, pos, omega, gy, G2, bf16, V, Vdot, env, penv, p2, genv2, s);
 }
 
 int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const float* pedge, const float* omega,

@@ -91,8 +91,8 @@ struct EdgeFwd {
 // ------------------------------------------------------------------ node_fwd
 template <int L, int M>
 __global__ __launch_bounds__(512) void node_fwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
-                                                       const float* __restrict__ V, float* __restrict__ y,
-                                                       int accumulate) {
+                                                       const float* __restrict__ V, const float* __restrict__ env,
+                                                       float* __restrict__ y, int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
   __shared__ float sD1[kTileE * 9];
   __shared__ float sR[kTileE * K];
@@ -122,12 +122,13 @@ __global__ __launch_bounds__(512) void node_fwd_kernel(Dims d, GraphDev g, const
     if (act) {
       for (int t = grp; t < ne; t += 2) {
         const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
+        const float ev = env ? env[t0 + t] : 1.f;   // cutoff envelope of the message
         float tv[Q];
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
           const int q = qhalf(l, M);
 #pragma unroll
-          for (int m = -q; m <= q; ++m) tv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
+          for (int m = -q; m <= q; ++m) tv[ridx(l, m, M)] = ev * vr[mm_col(l, m, 0, L, C)];
         }
         rot_bwd_acc<L, M>(sR + t * K, tv, acc);
       }
@@ -141,11 +142,11 @@ __global__ __launch_bounds__(512) void node_fwd_kernel(Dims d, GraphDev g, const
 
 template <int L, int M>
 struct NodeFwd {
-  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
-                 hipStream_t s) {
+  static int run(const Dims& d, const GraphDev& g, const float* pos, const float* V, const float* env, float* y,
+                 int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = 2 * ((d.C + 63) / 64) * 64;
-    hipLaunchKernelGGL((node_fwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, pos, V, y, accumulate);
+    hipLaunchKernelGGL((node_fwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, pos, V, env, y, accumulate);
     return hipGetLastError();
   }
 };
@@ -236,9 +237,9 @@ int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const floa
   return dispatch_lm<EdgeFwd>(d.L, d.M, d, g, x, pos, S, T, bf16, s);
 }
 
-int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
-                    hipStream_t s) {
-  return dispatch_lm<NodeFwd>(d.L, d.M, d, g, pos, V, y, accumulate, s);
+int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, const float* env, float* y,
+                    int accumulate, hipStream_t s) {
+  return dispatch_lm<NodeFwd>(d.L, d.M, d, g, pos, V, env, y, accumulate, s);
 }
 
 int launch_gate_fwd(const Dims& d, long E, const float* U, void* Z, int bf16, hipStream_t s) {

@@ -33,14 +33,15 @@ int launch_edge_fwd(const Dims& d, const GraphDev& g, const float* x, const floa
                     int bf16, hipStream_t s);
 // Z (operand) = gate(U)
 int launch_gate_fwd(const Dims& d, long E, const float* U, void* Z, int bf16, hipStream_t s);
-// y[i] (+)= sum_{e -> i, e in chunk} R_e^T V[e]
-int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, float* y, int accumulate,
-                    hipStream_t s);
+// y[i] (+)= sum_{e -> i, e in chunk} env[e] R_e^T V[e]  (env: per-edge envelope, null = 1)
+int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const float* V, const float* env, float* y,
+                    int accumulate, hipStream_t s);
 
 // ---- backward
-// tbar[e] (operand) = R_e gy[dst]; tau[e] = torque of <V, R gy> (for the position gradient)
-int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V, void* tbar,
-                    float* tau, int bf16, hipStream_t s);
+// tbar[e] (operand) = env_e R_e gy[dst]; tau[e] = torque of env_e <V, R gy> (for the
+// position gradient); genv[e] (global index, if not null) = <V, R gy>
+int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V,
+                    const float* env, void* tbar, float* tau, float* genv, int bf16, hipStream_t s);
 // Ubar (operand) from Zbar (gate backward)
 int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, void* Ubar, int bf16, hipStream_t s);
 // gx[n] (both halves), Sbar[e], tau_dst[e], tau_src[e]
@@ -61,13 +62,16 @@ int launch_edge_dual(const Dims& d, const GraphDev& g, const float* x, const flo
                      float* omega, int bf16, hipStream_t s);
 // Zdot (operand)
 int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, void* Zdot, int bf16, hipStream_t s);
-// ydot[i] = sum_e Rdot^T V + R^T Vdot
+// ydot[i] = sum_e env (Rdot^T V + R^T Vdot) + penv R^T V
 int launch_node_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* V,
-                     const float* Vdot, float* ydot, int accumulate, hipStream_t s);
-// G2 (operand) rows [0,E) = R gy[dst], rows [E,2E) = Rdot gy[dst]; with p2 (not null)
-// also the per-edge torque and rate cotangent [E][6] of ydot's rotations
+                     const float* Vdot, const float* env, const float* penv, float* ydot, int accumulate,
+                     hipStream_t s);
+// G2 (operand) rows [0,E) = env R gy[dst], rows [E,2E) = env Rdot gy[dst] + penv R gy[dst];
+// with p2 (not null) also the per-edge torque and rate cotangent [E][6] of ydot's
+// rotations; with genv2 (not null, global index) the envelope derivative
 int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy,
-                         void* G2, int bf16, const float* V, const float* Vdot, float* p2, hipStream_t s);
+                         void* G2, int bf16, const float* V, const float* Vdot, const float* env, const float* penv,
+                         float* p2, float* genv2, hipStream_t s);
 // vbar2[e] (global edge index) = position derivative of the double backward per edge vector,
 // from the three [E][6] torque/rate parts (chunk-relative rows)
 int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const float* pedge, const float* omega,

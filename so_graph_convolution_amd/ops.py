@@ -163,18 +163,21 @@ def _ws_for(cfg, g, stage, saved, ws, chunk_edges, device):
     return _ws(nb, device)
 
 
-def _common(cfg, g, x, pos, rbf, w_rad):
+def _common(cfg, g, x, pos, rbf, w_rad, env=None):
     N, E, d, C = g.n_nodes, g.n_edges, cfg.d, cfg.channels
     _dev(x, "x", dtype=cfg.torch_dtype, shape=(N, d, C))
     _dev(pos, "pos", shape=(N, 3))
     _dev(rbf, "rbf", shape=(E, cfg.n_rbf))
     _dev(w_rad, "w_rad", dtype=cfg.torch_dtype, shape=(cfg.n_rbf, (cfg.lmax + 1) * 2 * C))
+    _dev(env, "env", shape=(E,))
 
 
-def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None, ws=None, chunk_edges=None):
+def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None, ws=None, chunk_edges=None,
+                env=None):
     """Returns (y, saved). `saved=True` allocates the state for bwd/dbwd; with
-    saved=None the state is not kept (chunks of chunk_edges edges)."""
-    _common(cfg, g, x, pos, rbf, w_rad)
+    saved=None the state is not kept (chunks of chunk_edges edges). `env` [E]
+    float32: optional per-edge cutoff envelope multiplying each message."""
+    _common(cfg, g, x, pos, rbf, w_rad, env)
     s1, s2 = weight_shapes(cfg)
     dt = cfg.torch_dtype
     p1, k1 = _ptr_array(w1, "w1", s1, dt)
@@ -184,19 +187,19 @@ def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None
         saved = _ws(so2conv_saved_bytes(cfg, g.n_edges), x.device)
     ws = _ws_for(cfg, g, 0, saved, ws, chunk_edges, x.device)
     c, gc = cfg.c(), g.c()
-    check(lib().so2conv_fwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2, _p(y),
-                            _p(saved), _p(ws), ws.numel(), _stream()), "so2conv_fwd")
+    check(lib().so2conv_fwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1, p2,
+                            _p(y), _p(saved), _p(ws), ws.numel(), _stream()), "so2conv_fwd")
     return y, saved
 
 
-GRAD_KEYS = ("x", "pos", "rbf", "w_rad", "w1", "w2", "edge")
+GRAD_KEYS = ("x", "pos", "rbf", "w_rad", "w1", "w2", "edge", "env")
 
 
 def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, need=GRAD_KEYS, ws=None,
-                chunk_edges=None):
-    """Returns dict gx, gpos, grbf, gw_rad, gw1, gw2, gedge (requested ones).
-    saved=None recomputes the forward state chunk by chunk."""
-    _common(cfg, g, x, pos, rbf, w_rad)
+                chunk_edges=None, env=None):
+    """Returns dict gx, gpos, grbf, gw_rad, gw1, gw2, gedge and, with an envelope,
+    genv (requested ones). saved=None recomputes the forward state chunk by chunk."""
+    _common(cfg, g, x, pos, rbf, w_rad, env)
     dt = cfg.torch_dtype
     _dev(gy, "gy", dtype=dt, shape=x.shape)
     s1, s2 = weight_shapes(cfg)
@@ -211,13 +214,15 @@ def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy,
     out["gw1"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None
     out["gw2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
+    out["genv"] = torch.empty(g.n_edges, device=dev) if ("env" in need and env is not None) else None
     q1, k3 = _ptr_array(out["gw1"], "gw1", s1, dt)
     q2, k4 = _ptr_array(out["gw2"], "gw2", s2, dt)
     ws = _ws_for(cfg, g, 1, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
-    check(lib().so2conv_bwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
-                            _p(saved), _p(gy), _p(out["gx"]), _p(out["gpos"]), _p(out["grbf"]), _p(out["gw_rad"]),
-                            q1, q2, _p(out["gedge"]), _p(ws), ws.numel(), _stream()), "so2conv_bwd")
+    check(lib().so2conv_bwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1, p2,
+                            _p(saved), _p(gy), _p(out["gx"]), _p(out["gpos"]), _p(out["grbf"]), _p(out["genv"]),
+                            _p(out["gw_rad"]), q1, q2, _p(out["gedge"]), _p(ws), ws.numel(), _stream()),
+          "so2conv_bwd")
     return out
 
 
@@ -225,10 +230,12 @@ DBWD_KEYS = ("gy", "x", "rbf", "w_rad", "w1", "w2")   # the force-training patte
 
 
 def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, px=None, ppos=None, pedge=None,
-                 prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None, chunk_edges=None):
-    """Returns dict ggy, gx2, gpos2, grbf2, gw_rad2, gw1_2, gw2_2 (requested ones; gpos2
-    only when "pos" is in need)."""
-    _common(cfg, g, x, pos, rbf, w_rad)
+                 prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None, chunk_edges=None, env=None,
+                 penv=None):
+    """Returns dict ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1_2, gw2_2 (requested ones;
+    gpos2 only when "pos" is in need, genv2 when "env" is and an envelope is given)."""
+    _common(cfg, g, x, pos, rbf, w_rad, env)
+    _dev(penv, "penv", shape=(g.n_edges,))
     dt = cfg.torch_dtype
     _dev(gy, "gy", dtype=dt, shape=x.shape)
     _dev(px, "px", dtype=dt, shape=x.shape)
@@ -246,6 +253,7 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     out["ggy"] = torch.empty_like(x) if "gy" in need else None
     out["gx2"] = torch.empty_like(x) if "x" in need else None
     out["gpos2"] = torch.empty_like(pos) if "pos" in need else None
+    out["genv2"] = torch.empty(g.n_edges, device=dev) if ("env" in need and env is not None) else None
     out["grbf2"] = torch.empty_like(rbf) if "rbf" in need else None
     out["gw_rad2"] = torch.empty_like(w_rad) if "w_rad" in need else None
     out["gw1_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None
@@ -254,10 +262,10 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     q2, k4 = _ptr_array(out["gw2_2"], "gw2_2", s2, dt)
     ws = _ws_for(cfg, g, 2, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
-    check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad), p1, p2,
-                             _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf), _p(pw_rad), pp1, pp2,
-                             _p(out["ggy"]), _p(out["gx2"]), _p(out["gpos2"]), _p(out["grbf2"]), _p(out["gw_rad2"]),
-                             q1, q2,
+    check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1,
+                             p2, _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf), _p(penv), _p(pw_rad), pp1,
+                             pp2, _p(out["ggy"]), _p(out["gx2"]), _p(out["gpos2"]), _p(out["grbf2"]),
+                             _p(out["genv2"]), _p(out["gw_rad2"]), q1, q2,
                              _p(ws), ws.numel(), _stream()), "so2conv_dbwd")
     return out
 
