@@ -98,6 +98,10 @@ def main():
     ap.add_argument("--config", default="M")
     ap.add_argument("--dtype", choices=("f32", "bf16"), default=None,
                     help="array dtype (default: the workload's own: f32 for M, bf16 for H and X)")
+    ap.add_argument("--pos2", action="store_true",
+                    help="the double backward also returns position derivatives (gpos2)")
+    ap.add_argument("--envelope", action="store_true",
+                    help="per-edge cutoff envelope on the messages (with genv, and genv2 in the double backward)")
     ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
@@ -144,6 +148,9 @@ def main():
     x, pos, rbf, w_rad = t(d["x"], ft), t(d["pos"]), t(d["rbf"]), t(d["w_rad"], ft)
     w1, w2 = [t(w, ft) for w in d["w1"]], [t(w, ft) for w in d["w2"]]
     gy, px, ppos, prbf = t(d["gy"], ft), t(d["px"], ft), t(d["ppos"]), t(d["prbf"])
+    env = t(so2_synth.cosine_envelope(d)) if args.envelope else None
+    db_need = ("gy", "x", "rbf", "w_rad", "w1", "w2") + (("pos",) if args.pos2 else ()) + \
+        (("env",) if args.envelope else ())
     saved_b = K.so2conv_saved_bytes(kc, E)
     ws_b = max(K.so2conv_workspace_bytes(kc, N, E, s) for s in (0, 1, 2))
     chunked = saved_b + ws_b > 200 * 2**30
@@ -159,11 +166,11 @@ def main():
     def step(times=None):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record()
-        K.so2conv_fwd(*args_c, saved=saved, ws=ws)
+        K.so2conv_fwd(*args_c, saved=saved, ws=ws, env=env)
         e1.record()
-        K.so2conv_bwd(*args_c, saved, gy, ws=ws)
+        K.so2conv_bwd(*args_c, saved, gy, ws=ws, env=env)
         e2.record()
-        K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws)
+        K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env, need=db_need)
         e3.record()
         if times is not None:
             times.append((e0, e1, e2, e3))
@@ -213,7 +220,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{WORKLOADS.get(cfg.name, cfg.name)} ({cfg.name})", "n_atoms": N,
                    "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
-                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)",
+                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)"
+                   + (", dbwd with gpos2" if args.pos2 else "") + (", cutoff envelope" if args.envelope else ""),
                    "edge_chunks": chunked},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_gemm_traffic(args.config, dtype),

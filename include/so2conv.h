@@ -78,6 +78,16 @@ typedef enum {
 
 typedef enum { SO2_F32 = 0, SO2_BF16 = 1 } so2_dtype;
 
+/* cfg->flags */
+enum {
+  /* Validate the inputs on the device before any compute kernel: edge indices
+   * in range, receivers non-decreasing, no zero-length edge, finite positions,
+   * shifts, rbf and envelope. The call then synchronises its stream and returns
+   * SO2_EDEVICE (message: the failed checks) instead of computing; the word of
+   * the last checked call stays readable through so2conv_debug_status. */
+  SO2_DEBUG_CHECKS = 2
+};
+
 typedef struct {
   int32_t lmax, mmax, channels, n_rbf, dtype, flags;
 } so2conv_cfg;
@@ -179,6 +189,14 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
 int so2conv_profile_enable(int on);
 int so2conv_profile_reset(void);
 int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops, double* total_bytes);
+
+/* Synchronises `stream` and reports the device-side validation word of the
+ * current device left by the last call with SO2_DEBUG_CHECKS (each such call
+ * clears it first): SO2_OK if clear, else SO2_EDEVICE with the failed checks in
+ * so2conv_last_error() (bits: 1 src out of range, 2 dst out of range,
+ * 4 dst decreasing, 8 zero-length edge, 16 non-finite input); the word is
+ * cleared. */
+int so2conv_debug_status(void* stream);
 
 /* message of the last failing call on this thread ("" if none) */
 const char* so2conv_last_error(void);

@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libso2conv.so")
 
 SO2_OK, SO2_EINVAL, SO2_EUNSUPPORTED, SO2_EWORKSPACE, SO2_EHIP, SO2_EDEVICE = 0, -1, -2, -3, -4, -5
+SO2_DEBUG_CHECKS = 2
 
 c_vp = ctypes.c_void_p
 c_sz = ctypes.c_size_t
@@ -52,6 +53,7 @@ EXPORTS = {
     "so2conv_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "so2conv_supported": (ctypes.c_int, [c_i32, c_i32]),
+    "so2conv_debug_status": (ctypes.c_int, [c_vp]),
 }
 
 _lib = None

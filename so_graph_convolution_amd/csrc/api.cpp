@@ -95,6 +95,7 @@ struct Ctx {
   int n_rbf;
   int bf;    // 1: bfloat16 boundary arrays and GEMM operands
   int es;    // bytes per GEMM-operand element
+  int debug; // SO2_DEBUG_CHECKS
   size_t node_floats() const { return (size_t)d.d() * d.C; }   // one node row
   int wS() const { return (d.L + 1) * d.Ci(); }
 };
@@ -109,6 +110,8 @@ int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
   if (cfg->n_rbf < 4 || cfg->n_rbf % 4 || cfg->n_rbf > 1024)
     return fail(SO2_EUNSUPPORTED, "n_rbf must be a multiple of 4 in [4, 1024]");
   if (cfg->dtype != SO2_F32 && cfg->dtype != SO2_BF16) return fail(SO2_EUNSUPPORTED, "dtype must be SO2_F32 or SO2_BF16");
+  if (cfg->flags & ~SO2_DEBUG_CHECKS) return fail(SO2_EINVAL, "unknown cfg flags");
+  c->debug = (cfg->flags & SO2_DEBUG_CHECKS) != 0;
   c->d.L = L;
   c->d.M = M;
   c->d.C = C;
@@ -134,6 +137,66 @@ int check_graph(const so2conv_graph* g, GraphDev* gd) {
   gd->src_ptr = g->src_ptr;
   gd->e0 = 0;
   gd->e1 = g->n_edges;
+  return SO2_OK;
+}
+
+// ---------------------------------------------------------------- debug checks
+// Word of failed checks of this device (bits as in so2conv_debug_status).
+__device__ unsigned g_debug_word;
+
+__global__ void validate_kernel(GraphDev g, const float* __restrict__ pos, const float* __restrict__ rbf, int n_rbf,
+                                const float* __restrict__ env) {
+  unsigned bits = 0;
+  for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.E; e += (long)gridDim.x * blockDim.x) {
+    const int j = g.src[e], i = g.dst[e];
+    const bool jr = j >= 0 && j < g.N, ir = i >= 0 && i < g.N;
+    if (!jr) bits |= 1u;
+    if (!ir) bits |= 2u;
+    if (e > 0 && g.dst[e - 1] > i) bits |= 4u;
+    if (jr && ir) {
+      float r2 = 0.f;
+      bool fin = true;
+      for (int k = 0; k < 3; ++k) {
+        const float v = pos[3 * j + k] - pos[3 * i + k] + (g.shift ? g.shift[3 * e + k] : 0.f);
+        fin = fin && isfinite(v);
+        r2 += v * v;
+      }
+      if (!fin) bits |= 16u;
+      else if (!(r2 > 0.f)) bits |= 8u;
+    }
+    for (int k = 0; k < n_rbf; ++k)
+      if (!isfinite(rbf[(size_t)e * n_rbf + k])) bits |= 16u;
+    if (env && !isfinite(env[e])) bits |= 16u;
+  }
+  if (bits) atomicOr(&g_debug_word, bits);
+}
+
+std::string debug_bits_text(unsigned b) {
+  std::string m;
+  const char* names[] = {"src out of range", "dst out of range", "dst decreasing", "zero-length edge",
+                         "non-finite input"};
+  for (int k = 0; k < 5; ++k)
+    if (b & (1u << k)) m += (m.empty() ? "" : ", ") + std::string(names[k]);
+  return m;
+}
+
+// SO2_DEBUG_CHECKS: validate, wait for the verdict, and refuse to compute on bad inputs
+int debug_validate(const Ctx& c, const GraphDev& g, const float* pos, const float* rbf, const float* env,
+                   hipStream_t s) {
+  if (!c.debug) return SO2_OK;
+  const unsigned zero = 0;
+  SO2_HIP(hipStreamSynchronize(s));
+  SO2_HIP(hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &zero, sizeof(zero)));
+  if (g.E > 0) {
+    long b = (g.E + 255) / 256;
+    if (b > 4096) b = 4096;
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)b), dim3(256), 0, s, g, pos, rbf, c.n_rbf, env);
+    SO2_HIP(hipGetLastError());
+  }
+  SO2_HIP(hipStreamSynchronize(s));
+  unsigned w = 0;
+  SO2_HIP(hipMemcpyFromSymbol(&w, HIP_SYMBOL(g_debug_word), sizeof(w)));
+  if (w) return fail(SO2_EDEVICE, "device-side validation failed: " + debug_bits_text(w));
   return SO2_OK;
 }
 
@@ -670,6 +733,16 @@ int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* 
 
 int so2conv_supported(int32_t lmax, int32_t mmax) { return lm_supported(lmax, mmax) ? 1 : 0; }
 
+int so2conv_debug_status(void* stream) {
+  g_err.clear();
+  SO2_HIP(hipStreamSynchronize((hipStream_t)stream));
+  unsigned w = 0, zero = 0;
+  SO2_HIP(hipMemcpyFromSymbol(&w, HIP_SYMBOL(g_debug_word), sizeof(w)));
+  if (!w) return SO2_OK;
+  SO2_HIP(hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &zero, sizeof(zero)));
+  return fail(SO2_EDEVICE, "device-side validation failed: " + debug_bits_text(w));
+}
+
 size_t so2conv_graph_workspace_bytes(int32_t n_nodes, int64_t n_edges) { return graph_ws_bytes(n_nodes, n_edges); }
 
 int so2conv_graph_prepare(int32_t n_nodes, int64_t n_edges, const int32_t* src, const int32_t* dst, int32_t* dst_ptr,
@@ -748,6 +821,7 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
   if (!x || !pos || (!rbf && gd.E > 0) || !y) return fail(SO2_EINVAL, "NULL input or output");
   if ((r = ensure_init())) return r;
+  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
   const bool recompute = saved == nullptr;
   if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
   const long ec = pick_chunk(c, gd.N, gd.E, 0, recompute, ws_bytes);
@@ -803,6 +877,7 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
   if (genv && !env) return fail(SO2_EINVAL, "genv requested without an envelope");
   if ((r = ensure_init())) return r;
+  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
   hipStream_t s = (hipStream_t)stream;
   const int n_rbf = c.n_rbf, wS = c.wS();
   if (gd.E == 0) return zero_grads(c, gd.N, gx, gpos, gw_rad, gw1, gw2, s);
@@ -890,6 +965,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
   if ((penv || genv2) && !env) return fail(SO2_EINVAL, "penv or genv2 given without an envelope");
   if ((r = ensure_init())) return r;
+  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
   const bool has_pw1 = !all_null(pw1, d.M + 1), has_pw2 = !all_null(pw2, d.M + 1);
   if (has_pw1)
     for (int a = 0; a <= d.M; ++a)

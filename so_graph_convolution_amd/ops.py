@@ -11,12 +11,12 @@ import dataclasses
 
 import torch
 
-from ._binding import Cfg, GraphC, check, lib
+from ._binding import SO2_DEBUG_CHECKS, Cfg, GraphC, check, lib
 
 __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_bwd", "so2conv_dbwd",
            "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes", "weight_shapes",
            "so2conv_profile_enable", "so2conv_profile_reset", "so2conv_profile_read",
-           "so2conv_chunked_workspace_bytes"]
+           "so2conv_chunked_workspace_bytes", "so2conv_debug_status"]
 
 
 _DTYPES = {"f32": (0, torch.float32), "bf16": (1, torch.bfloat16)}
@@ -27,19 +27,22 @@ class SO2Config:
     """dtype "f32": every array float32. dtype "bf16": node features, weights and
     their gradients bfloat16 (positions, shifts, rbf and their gradients stay
     float32); the per-order products run on bfloat16 matrix cores with float32
-    accumulation."""
+    accumulation. debug_checks: validate the inputs on the device before
+    computing (the call synchronises and raises on bad inputs)."""
     lmax: int
     mmax: int
     channels: int
     n_rbf: int
     dtype: str = "f32"
+    debug_checks: bool = False
 
     def __post_init__(self):
         if self.dtype not in _DTYPES:
             raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
 
     def c(self) -> Cfg:
-        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0], 0)
+        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0],
+                   SO2_DEBUG_CHECKS if self.debug_checks else 0)
 
     @property
     def torch_dtype(self):
@@ -302,3 +305,9 @@ def so2conv_debug_rotate_gather(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad):
     check(lib().so2conv_debug_rotate_gather(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(w_rad),
                                             _p(T), _p(ws), ws.numel(), _stream()), "so2conv_debug_rotate_gather")
     return T
+
+
+def so2conv_debug_status():
+    """Synchronise the current stream and raise So2Error (status -5) if the last
+    call with debug_checks found bad inputs on this device."""
+    check(lib().so2conv_debug_status(_stream()), "so2conv_debug_status")

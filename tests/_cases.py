@@ -31,7 +31,7 @@ def note(msg):
     sys.stdout.flush()
 
 
-def to_dev(d, dtype="f32"):
+def to_dev(d, dtype="f32", validate_graph=True):
     """Device copies; with dtype "bf16" the node features, cotangents and
     weights are passed as bfloat16 (exact for bf16-representable inputs)."""
     import so_graph_convolution_amd as K
@@ -48,7 +48,8 @@ def to_dev(d, dtype="f32"):
 
     ft = torch.bfloat16 if dtype == "bf16" else torch.float32
     kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype)
-    g = K.so2conv_graph_prepare(cfg.n_atoms, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
+    g = K.so2conv_graph_prepare(cfg.n_atoms, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]),
+                                validate=validate_graph)
     out = dict(kcfg=kc, g=g, x=t(d["x"], ft), pos=t(d["pos"]), rbf=t(d["rbf"]), w_rad=t(d["w_rad"], ft),
                w1=[t(w, ft) for w in d["w1"]], w2=[t(w, ft) for w in d["w2"]])
     for k in ("gy", "px", "ppos", "prbf"):

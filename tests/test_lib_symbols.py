@@ -44,3 +44,20 @@ def test_host_side_argument_checks():
     assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 100, 64), 10) == 0       # C not a multiple of 16
     assert K.so2conv_saved_bytes(K.SO2Config(4, 5, 128, 64), 10) == 0       # mmax > lmax
     assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 128, 6), 10) == 0        # n_rbf not a multiple of 4
+
+
+def test_host_side_dtype_and_flag_checks():
+    """bf16 halves the stored GEMM operands; unknown cfg flags are rejected."""
+    import ctypes
+
+    import so_graph_convolution_amd as K
+    from so_graph_convolution_amd._binding import Cfg
+    f32, bf16 = K.SO2Config(4, 2, 128, 64), K.SO2Config(4, 2, 128, 64, "bf16")
+    # per edge at lmax 4, C 128: S, U, V float32 and T, Z bfloat16 -> 41,216 bytes (55,808 in float32)
+    assert K.so2conv_saved_bytes(f32, 1024) == 1024 * 55808
+    assert K.so2conv_saved_bytes(bf16, 1024) == 1024 * 41216
+    assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 128, 64, debug_checks=True), 8) > 0
+    bad = Cfg(4, 2, 128, 64, 0, 4)       # unknown flag bit
+    assert K.lib().so2conv_saved_bytes(ctypes.byref(bad), 8) == 0
+    odd = Cfg(4, 2, 128, 64, 7, 0)       # unknown dtype
+    assert K.lib().so2conv_saved_bytes(ctypes.byref(odd), 8) == 0
