@@ -1,0 +1,95 @@
+"""Pins for the spherical-projection oracle (TrimSO(2) page, Appendix B.4):
+a brute-force loop over every index of the definition on a tiny case, the
+page's reassociation B_l = W_l A, linearity in x and in each channel map,
+and central finite differences for the backward and the double backward."""
+import itertools
+
+import pytest
+import torch
+
+from oracle import grid_oracle as GO
+
+DT = torch.float64
+
+
+def _case(L=2, C_in=3, C_h=4, C_out=2, n_g=5, N=3, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=g, dtype=DT)  # noqa: E731
+    d = (L + 1) ** 2
+    return r(N, d, C_in), r(n_g, d), r(L + 1, C_in, C_h), r(C_h, C_out)
+
+
+def test_brute_force_definition():
+    x, G, W, A = _case()
+    N, d, C_in = x.shape
+    n_g, C_h, C_out, L = G.shape[0], W.shape[2], A.shape[1], W.shape[0] - 1
+    U = GO.forward(x, G, W, A)
+    for i, gp, c in itertools.product(range(N), range(n_g), range(C_out)):
+        s = 0.0
+        for l in range(L + 1):
+            for m in range(2 * l + 1):
+                j = l * l + m
+                for k in range(C_in):
+                    for h in range(C_h):
+                        s += float(G[gp, j]) * float(x[i, j, k]) * float(W[l, k, h]) * float(A[h, c])
+        assert abs(float(U[i, gp, c]) - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_reassociation_with_B():
+    """sum_l G_l (X^(l) B_l) with B_l = W_l A equals the definition."""
+    x, G, W, A = _case(L=3, C_in=4, C_h=6, C_out=3, n_g=7, N=4, seed=1)
+    B = W @ A
+    U2 = sum(torch.einsum("gm,nmc->ngc", G[:, l * l:(l + 1) ** 2], x[:, l * l:(l + 1) ** 2, :] @ B[l])
+             for l in range(W.shape[0]))
+    assert torch.allclose(GO.forward(x, G, W, A), U2, atol=1e-12)
+
+
+def test_linear_in_each_argument():
+    x, G, W, A = _case(seed=2)
+    x2, _, W2, A2 = _case(seed=3)
+    f = GO.forward
+    assert torch.allclose(f(x + 2 * x2, G, W, A), f(x, G, W, A) + 2 * f(x2, G, W, A), atol=1e-12)
+    assert torch.allclose(f(x, G, W + W2, A), f(x, G, W, A) + f(x, G, W2, A), atol=1e-12)
+    assert torch.allclose(f(x, G, W, A - A2), f(x, G, W, A) - f(x, G, W, A2), atol=1e-12)
+
+
+def _dot(a, b):
+    return float((a * b).sum())
+
+
+@pytest.mark.parametrize("which", ["x", "W", "A"])
+def test_backward_matches_fd(which):
+    x, G, W, A = _case(L=3, C_in=3, C_h=5, C_out=4, n_g=9, N=3, seed=4)
+    gU = torch.randn(x.shape[0], G.shape[0], A.shape[1], generator=torch.Generator().manual_seed(5), dtype=DT)
+    g = GO.backward(x, G, W, A, gU)
+    q = torch.randn_like({"x": x, "W": W, "A": A}[which])
+    eps = 1e-6
+
+    def f(e):
+        args = dict(x=x, W=W, A=A)
+        args[which] = args[which] + e * q
+        return _dot(GO.forward(args["x"], G, args["W"], args["A"]), gU)
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    assert abs(_dot(g["g" + which], q) - fd) <= 1e-7 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("which", ["gU", "x", "W", "A"])
+def test_double_backward_matches_fd(which):
+    x, G, W, A = _case(L=2, C_in=3, C_h=4, C_out=3, n_g=8, N=3, seed=6)
+    gen = torch.Generator().manual_seed(7)
+    r = lambda t: torch.randn(t.shape, generator=gen, dtype=DT)  # noqa: E731
+    gU = torch.randn(x.shape[0], G.shape[0], A.shape[1], generator=gen, dtype=DT)
+    px, pW, pA = r(x), r(W), r(A)
+    dd = GO.double_backward(x, G, W, A, gU, px=px, pW=pW, pA=pA)
+    base = dict(x=x, W=W, A=A, gU=gU)
+    q = r(base[which])
+    eps = 1e-6
+
+    def L(e):
+        a = dict(base)
+        a[which] = a[which] + e * q
+        g = GO.backward(a["x"], G, a["W"], a["A"], a["gU"])
+        return _dot(g["gx"], px) + _dot(g["gW"], pW) + _dot(g["gA"], pA)
+    fd = (L(eps) - L(-eps)) / (2 * eps)
+    key = {"gU": "ggU", "x": "gx", "W": "gW", "A": "gA"}[which]
+    assert abs(_dot(dd[key], q) - fd) <= 1e-7 * max(1.0, abs(fd))
