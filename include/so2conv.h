@@ -177,6 +177,32 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
                                 const float* rbf, const void* w_rad, void* T_out, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* ---- Node-to-node spherical projection with fused channel maps (Appendix B.4,
+ * spherical activations). Per node i with coefficient rows X_i^(l) = x[i][l^2..(l+1)^2)
+ * (n_l x c_in):
+ *   U_i = sum_l G_l (X_i^(l) B_l),  B_l = W_l A        (= [sum_l G_l X_i^(l) W_l] A)
+ * G: [n_grid, (L+1)^2] float32, column block l = the degree-l basis at the
+ * grid points (caller-supplied; any matrix). W: [L+1, c_in, c_h], A: [c_h, c_out],
+ * x: [N, (L+1)^2, c_in], U: [N, n_grid, c_out]; float32 only. The library forms
+ * B_l once (never the c_h-wide coefficient or grid arrays), runs X B on the
+ * matrix cores and applies G per node. Backward: gx = (G^T gU) B^T per degree,
+ * gB = X^T (G^T gU), gW = gB A^T, gA = sum_l W_l^T gB_l. Double backward of
+ * L = <px, gx> + <pW, gW> + <pA, gA> (NULL direction = zero): ggU, gx2, gW2, gA2.
+ * Channel counts: multiples of 4 up to 1024; lmax <= 6; n_grid <= 65536.
+ * Workspace from so2grid_workspace_bytes (stage 0 fwd, 1 bwd, 2 dbwd). */
+typedef struct {
+  int32_t lmax, c_in, c_h, c_out, n_grid, dtype, flags;
+} so2grid_cfg;
+size_t so2grid_workspace_bytes(const so2grid_cfg* cfg, int32_t n_nodes, int stage);
+int so2grid_fwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
+                const float* A, float* U, void* ws, size_t ws_bytes, void* stream);
+int so2grid_bwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
+                const float* A, const float* gU, float* gx, float* gW, float* gA, void* ws, size_t ws_bytes,
+                void* stream);
+int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
+                 const float* A, const float* gU, const float* px, const float* pW, const float* pA, float* ggU,
+                 float* gx2, float* gW2, float* gA2, void* ws, size_t ws_bytes, void* stream);
+
 /* Measurement hook for the per-order GEMMs (the dense products of Section
  * 3.1 and Eq.(1)). While enabled, every matrix-core GEMM launch is bracketed
  * by HIP events on the launching stream and its algorithmic flop count (2 M N K

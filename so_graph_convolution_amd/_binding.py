@@ -26,6 +26,11 @@ class Cfg(ctypes.Structure):
                 ("flags", c_i32)]
 
 
+class GridCfg(ctypes.Structure):
+    _fields_ = [("lmax", c_i32), ("c_in", c_i32), ("c_h", c_i32), ("c_out", c_i32), ("n_grid", c_i32),
+                ("dtype", c_i32), ("flags", c_i32)]
+
+
 class GraphC(ctypes.Structure):
     _fields_ = [("n_nodes", c_i32), ("n_edges", c_i64), ("src", c_vp), ("dst", c_vp), ("shift", c_vp),
                 ("dst_ptr", c_vp), ("src_perm", c_vp), ("src_ptr", c_vp)]
@@ -54,6 +59,13 @@ EXPORTS = {
                                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "so2conv_supported": (ctypes.c_int, [c_i32, c_i32]),
     "so2conv_debug_status": (ctypes.c_int, [c_vp]),
+    "so2grid_workspace_bytes": (c_sz, [ctypes.POINTER(GridCfg), c_i32, ctypes.c_int]),
+    # (cfg, N, x, G, W, A, U, ws, ws_bytes, stream)
+    "so2grid_fwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 6 + [c_sz, c_vp]),
+    # (cfg, N, x, G, W, A, gU, gx, gW, gA, ws, ws_bytes, stream)
+    "so2grid_bwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 9 + [c_sz, c_vp]),
+    # (cfg, N, x, G, W, A, gU, px, pW, pA, ggU, gx2, gW2, gA2, ws, ws_bytes, stream)
+    "so2grid_dbwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 13 + [c_sz, c_vp]),
 }
 
 _lib = None

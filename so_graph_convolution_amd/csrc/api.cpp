@@ -1,5 +1,6 @@
 // C ABI of the fused SO(2) convolution: argument checks, workspace layout and
 // the kernel schedules of the forward, backward and double backward.
+#include <algorithm>
 #include <complex>
 #include <cstdio>
 #include <cstring>
@@ -687,6 +688,121 @@ int zero_grads(const Ctx& c, int N, void* gx, float* gpos, void* gw_rad, void* c
   return SO2_OK;
 }
 
+// ---------------------------------------------------------------- spherical projection
+struct GridCtx {
+  int L, Cin, Ch, Cout, ng, N;
+  int d() const { return (L + 1) * (L + 1); }
+};
+
+int check_grid(const so2grid_cfg* cfg, int32_t N, GridCtx* g) {
+  if (!cfg) return fail(SO2_EINVAL, "cfg is NULL");
+  if (cfg->lmax < 0 || cfg->lmax > kMaxL) return fail(SO2_EUNSUPPORTED, "lmax must be in [0, 6]");
+  for (int c : {cfg->c_in, cfg->c_h, cfg->c_out})
+    if (c < 4 || c > 1024 || c % 4) return fail(SO2_EUNSUPPORTED, "channel counts must be multiples of 4 in [4, 1024]");
+  if (cfg->n_grid < 1 || cfg->n_grid > 65536) return fail(SO2_EUNSUPPORTED, "n_grid must be in [1, 65536]");
+  if (cfg->dtype != SO2_F32) return fail(SO2_EUNSUPPORTED, "the spherical projection is float32 only");
+  if (cfg->flags) return fail(SO2_EINVAL, "unknown cfg flags");
+  if (N < 0) return fail(SO2_EINVAL, "negative node count");
+  *g = GridCtx{cfg->lmax, cfg->c_in, cfg->c_h, cfg->c_out, cfg->n_grid, N};
+  return SO2_OK;
+}
+
+// per-(l, m) row problems over all nodes: C[:, j] (+)= op(A[:, j]) with the
+// channel map of degree l; rows are node rows j = l^2 + m of [N][d][.]
+int grid_rows(const GridCtx& g, const float* A, int wa, const float* Bm, int ldb, bool tb, float* C, int wc,
+              int K, int Nn, int acc, hipStream_t s) {
+  std::vector<GemmProb> ps;
+  for (int l = 0; l <= g.L; ++l)
+    for (int m = 0; m < 2 * l + 1; ++m) {
+      const int j = l * l + m;
+      ps.push_back(prob(A + (size_t)j * wa, g.d() * wa, Bm + (size_t)l * (tb ? Nn : K) * ldb, ldb,
+                        C + (size_t)j * wc, g.d() * wc, g.N, Nn, K, acc));
+    }
+  return run_batch(ps, false, tb, 0, s);
+}
+
+// Gm_l (+)= sum_m X[:, l^2+m]^T Z[:, l^2+m]  (Gm: [L+1][Cx][Cz], split-K over nodes)
+int grid_wgrad(const GridCtx& g, const float* X, int wx, const float* Z, int wz, float* Gm, int acc, float* P,
+               hipStream_t s) {
+  for (int l = 0; l <= g.L; ++l) {
+    std::vector<TnSeg> segs;
+    for (int m = 0; m < 2 * l + 1; ++m) {
+      const int j = l * l + m;
+      segs.push_back(TnSeg{X + (size_t)j * wx, g.d() * wx, Z + (size_t)j * wz, g.d() * wz, g.N});
+    }
+    int r = run_tn(segs.data(), (int)segs.size(), wx, wz, Gm + (size_t)l * wx * wz, wz, acc, P, 0, s);
+    if (r) return r;
+  }
+  return SO2_OK;
+}
+
+// split-K partials of the largest weight-gradient product: degree L sums 2L+1
+// segments of N rows each (the channel-map products have K <= 1024, one split each)
+size_t grid_partials(const GridCtx& g) {
+  int sp, ch;
+  split_plan(g.N, &sp, &ch);
+  const int mx = std::max(std::max(g.Cin, g.Ch), g.Cout);
+  const int segs = std::max(2 * g.L + 1, g.L + 1);
+  return (size_t)segs * std::max(sp, 1) * mx * mx;
+}
+
+struct GridWs {
+  float *B, *pB, *Y, *Z, *gB, *gB2, *P;
+};
+void layout_grid(Arena& ar, const GridCtx& g, int stage, GridWs* w) {
+  const size_t bsz = (size_t)(g.L + 1) * g.Cin * g.Cout, nf = (size_t)g.N * g.d() * g.Cout;
+  *w = GridWs{};
+  w->B = ar.take(bsz);
+  if (stage == 0) {
+    w->Y = ar.take(nf);
+    return;
+  }
+  w->Z = ar.take(nf);
+  w->gB = ar.take(bsz);
+  if (stage == 2) {
+    w->pB = ar.take(bsz);
+    w->Y = ar.take(nf);
+    w->gB2 = ar.take(bsz);
+  }
+  w->P = ar.take(grid_partials(g));
+}
+
+size_t grid_ws_need(const GridCtx& g, int stage) {
+  Arena ar{nullptr, 0};
+  GridWs w;
+  layout_grid(ar, g, stage, &w);
+  return ar.used + 4096;
+}
+
+// B_l = W_l A (or += )
+int grid_channel_map(const GridCtx& g, const float* W, const float* A, float* B, int acc, hipStream_t s) {
+  std::vector<GemmProb> ps;
+  for (int l = 0; l <= g.L; ++l)
+    ps.push_back(prob(W + (size_t)l * g.Cin * g.Ch, g.Ch, A, g.Cout, B + (size_t)l * g.Cin * g.Cout, g.Cout, g.Cin,
+                      g.Cout, g.Ch, acc));
+  return run_batch(ps, false, false, 0, s);
+}
+
+// gW_l (+)= Gm_l A^T   and   gA (+)= sum_l W_l^T Gm_l
+int grid_map_grads(const GridCtx& g, const float* Gm, const float* W, const float* A, float* gW, float* gA, int acc,
+                   float* P, hipStream_t s) {
+  int r;
+  if (gW) {
+    std::vector<GemmProb> ps;
+    for (int l = 0; l <= g.L; ++l)
+      ps.push_back(prob(Gm + (size_t)l * g.Cin * g.Cout, g.Cout, A, g.Cout, gW + (size_t)l * g.Cin * g.Ch, g.Ch, g.Cin,
+                        g.Ch, g.Cout, acc));
+    if ((r = run_batch(ps, false, true, 0, s))) return r;
+  }
+  if (gA) {
+    std::vector<TnSeg> segs;
+    for (int l = 0; l <= g.L; ++l)
+      segs.push_back(TnSeg{W + (size_t)l * g.Cin * g.Ch, g.Ch, Gm + (size_t)l * g.Cin * g.Cout, g.Cout, g.Cin});
+    if ((r = run_tn(segs.data(), (int)segs.size(), g.Ch, g.Cout, gA, g.Cout, acc, P, 0, s))) return r;
+  }
+  return SO2_OK;
+}
+
 }  // namespace
 
 // =====================================================================================
@@ -1085,6 +1201,131 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   if ((r = f32_out(c, ggy_acc, ggy, nf, s))) return r;
   if ((r = f32_out(c, gx2_acc, gx2, nf, s))) return r;
   return f32_out(c, gwr2_acc, gw_rad2, rf, s);
+}
+
+// ---------------------------------------------------------------- spherical projection entry points
+size_t so2grid_workspace_bytes(const so2grid_cfg* cfg, int32_t n_nodes, int stage) {
+  GridCtx g;
+  if (check_grid(cfg, n_nodes, &g) || stage < 0 || stage > 2) return 0;
+  return grid_ws_need(g, stage);
+}
+
+int so2grid_fwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
+                const float* A, float* U, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  GridCtx g;
+  int r;
+  if ((r = check_grid(cfg, n_nodes, &g))) return r;
+  if (!G || !W || !A || (g.N > 0 && (!x || !U))) return fail(SO2_EINVAL, "NULL input or output");
+  if (g.N == 0) return SO2_OK;
+  if (!ws || ws_bytes < grid_ws_need(g, 0)) return fail(SO2_EWORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  Arena ar{static_cast<char*>(ws), 0};
+  GridWs w;
+  layout_grid(ar, g, 0, &w);
+  if ((r = grid_channel_map(g, W, A, w.B, 0, s))) return r;                          // B_l = W_l A
+  if ((r = grid_rows(g, x, g.Cin, w.B, g.Cout, false, w.Y, g.Cout, g.Cin, g.Cout, 0, s))) return r;   // Y = X B
+  SO2_HIP(launch_grid_apply(g.L, g.N, g.ng, g.Cout, G, w.Y, U, s));                 // U = G Y
+  return SO2_OK;
+}
+
+int so2grid_bwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
+                const float* A, const float* gU, float* gx, float* gW, float* gA, void* ws, size_t ws_bytes,
+                void* stream) {
+  g_err.clear();
+  GridCtx g;
+  int r;
+  if ((r = check_grid(cfg, n_nodes, &g))) return r;
+  if (!G || !W || !A || (g.N > 0 && (!x || !gU))) return fail(SO2_EINVAL, "NULL input");
+  hipStream_t s = (hipStream_t)stream;
+  if (g.N == 0) {   // no nodes: zero weight gradients
+    if (gW && (r = fill(gW, (size_t)(g.L + 1) * g.Cin * g.Ch, s))) return r;
+    if (gA && (r = fill(gA, (size_t)g.Ch * g.Cout, s))) return r;
+    return SO2_OK;
+  }
+  if (!ws || ws_bytes < grid_ws_need(g, 1)) return fail(SO2_EWORKSPACE, "workspace too small");
+  Arena ar{static_cast<char*>(ws), 0};
+  GridWs w;
+  layout_grid(ar, g, 1, &w);
+  if ((r = grid_channel_map(g, W, A, w.B, 0, s))) return r;
+  SO2_HIP(launch_grid_apply_t(g.L, g.N, g.ng, g.Cout, G, gU, w.Z, s));              // Z = G^T gU
+  if (gx && (r = grid_rows(g, w.Z, g.Cout, w.B, g.Cout, true, gx, g.Cin, g.Cout, g.Cin, 0, s))) return r;  // Z B^T
+  if (gW || gA) {
+    if ((r = grid_wgrad(g, x, g.Cin, w.Z, g.Cout, w.gB, 0, w.P, s))) return r;      // Bbar_l = X^T Z
+    if ((r = grid_map_grads(g, w.gB, W, A, gW, gA, 0, w.P, s))) return r;
+  }
+  return SO2_OK;
+}
+
+int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
+                 const float* A, const float* gU, const float* px, const float* pW, const float* pA, float* ggU,
+                 float* gx2, float* gW2, float* gA2, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  GridCtx g;
+  int r;
+  if ((r = check_grid(cfg, n_nodes, &g))) return r;
+  if (!G || !W || !A || (g.N > 0 && (!x || !gU))) return fail(SO2_EINVAL, "NULL input");
+  hipStream_t s = (hipStream_t)stream;
+  if (g.N == 0) {
+    if (gW2 && (r = fill(gW2, (size_t)(g.L + 1) * g.Cin * g.Ch, s))) return r;
+    if (gA2 && (r = fill(gA2, (size_t)g.Ch * g.Cout, s))) return r;
+    return SO2_OK;
+  }
+  if (!ws || ws_bytes < grid_ws_need(g, 2)) return fail(SO2_EWORKSPACE, "workspace too small");
+  Arena ar{static_cast<char*>(ws), 0};
+  GridWs w;
+  layout_grid(ar, g, 2, &w);
+  const size_t nf = (size_t)g.N * g.d();
+  const bool has_pB = pW || pA;
+  if ((r = grid_channel_map(g, W, A, w.B, 0, s))) return r;
+  if (pW && (r = grid_channel_map(g, pW, A, w.pB, 0, s))) return r;                 // pB = pW A + W pA
+  if (pA && (r = grid_channel_map(g, W, pA, w.pB, pW ? 1 : 0, s))) return r;
+  SO2_HIP(launch_grid_apply_t(g.L, g.N, g.ng, g.Cout, G, gU, w.Z, s));              // Z = G^T gU
+  // dL/dgU = G (px B + x pB)
+  if (ggU) {
+    if (!px && !has_pB) {
+      if ((r = fill(ggU, (size_t)g.N * g.ng * g.Cout, s))) return r;
+    } else {
+      if (px && (r = grid_rows(g, px, g.Cin, w.B, g.Cout, false, w.Y, g.Cout, g.Cin, g.Cout, 0, s))) return r;
+      if (has_pB && (r = grid_rows(g, x, g.Cin, w.pB, g.Cout, false, w.Y, g.Cout, g.Cin, g.Cout, px ? 1 : 0, s)))
+        return r;
+      SO2_HIP(launch_grid_apply(g.L, g.N, g.ng, g.Cout, G, w.Y, ggU, s));
+    }
+  }
+  // dL/dx = Z pB^T
+  if (gx2) {
+    if (has_pB) {
+      if ((r = grid_rows(g, w.Z, g.Cout, w.pB, g.Cout, true, gx2, g.Cin, g.Cout, g.Cin, 0, s))) return r;
+    } else if ((r = fill(gx2, nf * g.Cin, s))) {
+      return r;
+    }
+  }
+  // dL/dW = (px^T Z) A^T + Bbar pA^T ; dL/dA = sum W^T (px^T Z) + sum pW^T Bbar
+  if (gW2 || gA2) {
+    if (gW2 && (r = fill(gW2, (size_t)(g.L + 1) * g.Cin * g.Ch, s))) return r;
+    if (gA2 && (r = fill(gA2, (size_t)g.Ch * g.Cout, s))) return r;
+    if (px) {
+      if ((r = grid_wgrad(g, px, g.Cin, w.Z, g.Cout, w.gB2, 0, w.P, s))) return r;
+      if ((r = grid_map_grads(g, w.gB2, W, A, gW2, gA2, 1, w.P, s))) return r;
+    }
+    if (has_pB) {
+      if ((r = grid_wgrad(g, x, g.Cin, w.Z, g.Cout, w.gB, 0, w.P, s))) return r;   // Bbar
+      if (pA && gW2) {   // gW2_l += Bbar_l pA^T
+        std::vector<GemmProb> ps;
+        for (int l = 0; l <= g.L; ++l)
+          ps.push_back(prob(w.gB + (size_t)l * g.Cin * g.Cout, g.Cout, pA, g.Cout, gW2 + (size_t)l * g.Cin * g.Ch,
+                            g.Ch, g.Cin, g.Ch, g.Cout, 1));
+        if ((r = run_batch(ps, false, true, 0, s))) return r;
+      }
+      if (pW && gA2) {   // gA2 += sum_l pW_l^T Bbar_l
+        std::vector<TnSeg> segs;
+        for (int l = 0; l <= g.L; ++l)
+          segs.push_back(TnSeg{pW + (size_t)l * g.Cin * g.Ch, g.Ch, w.gB + (size_t)l * g.Cin * g.Cout, g.Cout, g.Cin});
+        if ((r = run_tn(segs.data(), (int)segs.size(), g.Ch, g.Cout, gA2, g.Cout, 1, w.P, 0, s))) return r;
+      }
+    }
+  }
+  return SO2_OK;
 }
 
 }  // extern "C"

@@ -101,6 +101,11 @@ int launch_to_bf16(const float* in, bf16s* out, size_t n, hipStream_t s);
 void realified_shape(const Dims& d, int second, int a, int* rows, int* cols, long* off);
 long realified_size(const Dims& d, int second);
 
+// ---- node-to-node spherical projection: per node U = G Y (G: [ng][(L+1)^2]; Y, Z: [N][(L+1)^2][C];
+// U: [N][ng][C]) and Z = G^T U
+int launch_grid_apply(int L, int N, int ng, int C, const float* G, const float* Y, float* U, hipStream_t s);
+int launch_grid_apply_t(int L, int N, int ng, int C, const float* G, const float* U, float* Z, hipStream_t s);
+
 // ---- graph preparation
 size_t graph_ws_bytes(int N, long E);
 int launch_graph_prepare(int N, long E, const int* src, const int* dst, int* dst_ptr, int* src_perm, int* src_ptr,

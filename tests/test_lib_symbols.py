@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "so2conv.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(so2conv_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(so2(?:conv|grid)_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_entry_points():
