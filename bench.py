@@ -90,6 +90,76 @@ def cpu_baseline(d, n_edges_sample, seed=0):
                       f"(PyTorch CPU, autograd), {dt:.1f} s"}
 
 
+def bench_grid(args):
+    """Node-to-node spherical projection (U = sum_l G_l X^(l) W_l A; Appendix B.4) at
+    EquiformerV3's widths (lmax 4, C 128, FFN hidden 512) on the medium system's
+    10,000 nodes, a 100-point grid: fwd + bwd + dbwd (all directions)."""
+    import numpy as np
+    import torch
+    import so_graph_convolution_amd as K
+
+    def progress(msg):
+        print(f"[bench grid] {msg}", file=sys.stderr, flush=True)
+    L, ci, ch, co, ng, N = 4, 128, 512, 512, 100, 10000
+    d = (L + 1) ** 2
+    rng = np.random.default_rng(7)
+    host = dict(x=rng.normal(size=(N, d, ci)), G=rng.normal(size=(ng, d)) / np.sqrt(d),
+                W=rng.normal(size=(L + 1, ci, ch)) / np.sqrt(ci), A=rng.normal(size=(ch, co)) / np.sqrt(ch),
+                gU=rng.normal(size=(N, ng, co)), px=rng.normal(size=(N, d, ci)),
+                pW=rng.normal(size=(L + 1, ci, ch)) / np.sqrt(ci), pA=rng.normal(size=(ch, co)) / np.sqrt(ch))
+    g = {k: torch.tensor(v.astype(np.float32), device="cuda") for k, v in host.items()}
+    cfg = K.GridConfig(L, ci, ch, co, ng)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(times=None):
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        K.so2grid_fwd(cfg, g["x"], g["G"], g["W"], g["A"])
+        e[1].record()
+        K.so2grid_bwd(cfg, g["x"], g["G"], g["W"], g["A"], g["gU"])
+        e[2].record()
+        K.so2grid_dbwd(cfg, g["x"], g["G"], g["W"], g["A"], g["gU"], px=g["px"], pW=g["pW"], pA=g["pA"])
+        e[3].record()
+        if times is not None:
+            times.append(e)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in st]).mean(0)
+    # algorithmic HBM bytes of the forward: read x, G, W, A; write U
+    fwd_bytes = 4.0 * (N * d * ci + ng * d + (L + 1) * ci * ch + ch * co + N * ng * co)
+    out = {"metric": "nodes/sec fwd+bwd+dbwd spherical projection (lmax=4, c 128/512/512, 100-point grid)",
+           "value": N * args.steps / wall, "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "EquiformerV3-width node-to-node spherical projection on 10,000 nodes",
+                      "lmax": L, "c_in": ci, "c_h": ch, "c_out": co, "n_grid": ng, "n_nodes": N},
+           "stage_ms": {"fwd": float(ms[0]), "bwd": float(ms[1]), "dbwd": float(ms[2])},
+           "fwd_hbm": {"algorithmic_bytes": fwd_bytes, "GBs": fwd_bytes / (ms[0] * 1e-3) / 1e9,
+                       "frac_of_8TBs": fwd_bytes / (ms[0] * 1e-3) / 8e12},
+           "materialising_bytes_avoided": 4.0 * (N * d * ch + N * ng * ch) * 2}
+    progress(f"{out['ms_per_step']:.2f} ms/step")
+    if args.cpu_edges > 0:
+        import oracle.grid_oracle as GO
+        torch.set_num_threads(min(16, len(os.sched_getaffinity(0))))
+        n = 200
+        r = {k: torch.tensor(v[:n] if k in ("x", "gU", "px") else v, dtype=torch.float64) for k, v in host.items()}
+        t1 = time.perf_counter()
+        GO.forward(r["x"], r["G"], r["W"], r["A"])
+        GO.backward(r["x"], r["G"], r["W"], r["A"], r["gU"])
+        GO.double_backward(r["x"], r["G"], r["W"], r["A"], r["gU"], px=r["px"], pW=r["pW"], pA=r["pA"])
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": n / dt, "unit": "nodes/s", "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": f"first {n} of {N} nodes, fwd+bwd+dbwd in float64, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +170,8 @@ def main():
                     help="array dtype (default: the workload's own: f32 for M, bf16 for H and X)")
     ap.add_argument("--pos2", action="store_true",
                     help="the double backward also returns position derivatives (gpos2)")
+    ap.add_argument("--op", choices=("conv", "grid"), default="conv",
+                    help="conv: the SO(2) convolution step (default); grid: the node-to-node spherical projection")
     ap.add_argument("--envelope", action="store_true",
                     help="per-edge cutoff envelope on the messages (with genv, and genv2 in the double backward)")
     ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
@@ -116,6 +188,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4, "copy_bytes_written_per_launch":
                           dst.numel() * 4, "launches": 3}), flush=True)
+        return
+    if args.op == "grid" and args.gpus == 1:
+        bench_grid(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the convolution runs on a "

@@ -721,29 +721,52 @@ int grid_rows(const GridCtx& g, const float* A, int wa, const float* Bm, int ldb
   return run_batch(ps, false, tb, 0, s);
 }
 
-// Gm_l (+)= sum_m X[:, l^2+m]^T Z[:, l^2+m]  (Gm: [L+1][Cx][Cz], split-K over nodes)
+// split of the node dimension of the weight-gradient products: about 16
+// splits (so that all (l, m) products together fill the GPU), 256..4096 rows
+void grid_split(long N, int* splits, int* chunk) {
+  long c = ((N + 15) / 16 + kGemmKTile - 1) / kGemmKTile * kGemmKTile;
+  c = c < 256 ? 256 : (c > 4096 ? 4096 : c);
+  long s = (N + c - 1) / c;
+  *splits = (int)(s < 1 ? 1 : s);
+  *chunk = (int)c;
+}
+
+// Gm_l (+)= sum_m X[:, l^2+m]^T Z[:, l^2+m]  (Gm: [L+1][wx][wz]): every (l, m)
+// product in one grouped launch, split over nodes into partials, then one
+// fixed-order reduction per degree
 int grid_wgrad(const GridCtx& g, const float* X, int wx, const float* Z, int wz, float* Gm, int acc, float* P,
                hipStream_t s) {
+  if (g.N == 0) return SO2_OK;
+  int sp, ch;
+  grid_split(g.N, &sp, &ch);
+  std::vector<GemmProb> ps;
+  size_t off = 0;
+  for (int j = 0; j < g.d(); ++j) {
+    GemmProb p = prob(X + (size_t)j * wx, g.d() * wx, Z + (size_t)j * wz, g.d() * wz, P + off, wz, wx, wz, g.N);
+    p.k_splits = sp;
+    p.k_chunk = ch;
+    p.partial = 1;
+    ps.push_back(p);
+    off += (size_t)sp * wx * wz;
+  }
+  int r = run_batch(ps, true, false, 0, s);
+  if (r) return r;
+  off = 0;
   for (int l = 0; l <= g.L; ++l) {
-    std::vector<TnSeg> segs;
-    for (int m = 0; m < 2 * l + 1; ++m) {
-      const int j = l * l + m;
-      segs.push_back(TnSeg{X + (size_t)j * wx, g.d() * wx, Z + (size_t)j * wz, g.d() * wz, g.N});
-    }
-    int r = run_tn(segs.data(), (int)segs.size(), wx, wz, Gm + (size_t)l * wx * wz, wz, acc, P, 0, s);
-    if (r) return r;
+    const int n = (2 * l + 1) * sp;
+    SO2_HIP(gemm_reduce(P + off, n, wx, wz, Gm + (size_t)l * wx * wz, wz, acc, s));
+    off += (size_t)n * wx * wz;
   }
   return SO2_OK;
 }
 
-// split-K partials of the largest weight-gradient product: degree L sums 2L+1
-// segments of N rows each (the channel-map products have K <= 1024, one split each)
+// partials: every (l, m) product's splits at once, or the channel-map products
+// (L+1 segments of one split each)
 size_t grid_partials(const GridCtx& g) {
   int sp, ch;
-  split_plan(g.N, &sp, &ch);
+  grid_split(g.N, &sp, &ch);
   const int mx = std::max(std::max(g.Cin, g.Ch), g.Cout);
-  const int segs = std::max(2 * g.L + 1, g.L + 1);
-  return (size_t)segs * std::max(sp, 1) * mx * mx;
+  return (size_t)std::max(g.d() * sp, g.L + 1) * mx * mx;
 }
 
 struct GridWs {

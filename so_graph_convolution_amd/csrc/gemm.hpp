@@ -18,7 +18,7 @@
 
 namespace so2 {
 
-constexpr int kGemmMaxProbs = 8;
+constexpr int kGemmMaxProbs = 32;   // problems per launch (kernel argument < 4 KB)
 
 struct GemmProb {
   const void* A;     // float or bfloat16 elements (one type per launch)
