@@ -93,3 +93,49 @@ def test_double_backward_matches_fd(which):
     fd = (L(eps) - L(-eps)) / (2 * eps)
     key = {"gU": "ggU", "x": "gx", "W": "gW", "A": "gA"}[which]
     assert abs(_dot(dd[key], q) - fd) <= 1e-7 * max(1.0, abs(fd))
+
+
+def _basis(L, u):
+    """[n_g, (L+1)^2] real orthonormal harmonics at the unit vectors u."""
+    from oracle.so2conv_oracle import real_sh
+    return torch.cat([real_sh(l, u) for l in range(L + 1)], dim=-1)
+
+
+def _unit(n, g):
+    v = torch.randn(n, 3, generator=g, dtype=DT)
+    return v / v.norm(dim=-1, keepdim=True)
+
+
+def test_addition_theorem_closed_form():
+    """With G the harmonics at grid points u_g, identity channel maps and the
+    coefficients of Y(u0) as the node's features, the projection is the
+    zonal kernel sum_l (2l+1)/(4 pi) P_l(u_g . u0) (addition theorem)."""
+    from scipy.special import eval_legendre
+    L, n_g = 4, 23
+    g = torch.Generator().manual_seed(5)
+    u, u0 = _unit(n_g, g), _unit(1, g)
+    G = _basis(L, u)
+    x = _basis(L, u0).reshape(1, -1, 1)                       # one node, one channel
+    W = torch.ones(L + 1, 1, 1, dtype=DT)
+    U = GO.forward(x, G, W, torch.ones(1, 1, dtype=DT))[0, :, 0]
+    t = (u @ u0[0]).numpy()
+    ref = sum((2 * l + 1) / (4 * torch.pi) * eval_legendre(l, t) for l in range(L + 1))
+    assert torch.allclose(U, torch.as_tensor(ref), atol=1e-12, rtol=0)
+
+
+def test_rotating_features_rotates_the_grid():
+    """Features rotated by D(Q) read on the grid u equal the unrotated features
+    read on the grid Q^T u (Y(Q^T u) = D(Q)^T Y(u))."""
+    from oracle.so2conv_oracle import wigner_d
+    L, n_g = 3, 11
+    g = torch.Generator().manual_seed(6)
+    x, _, W, A = _case(L=L, C_in=3, C_h=4, C_out=2, n_g=n_g, N=2, seed=7)
+    Q, _ = torch.linalg.qr(torch.randn(3, 3, generator=g, dtype=DT))
+    if torch.det(Q) < 0:
+        Q = -Q
+    u = _unit(n_g, g)
+    xr = torch.cat([torch.einsum("mk,nkc->nmc", wigner_d(l, Q), x[:, l * l:(l + 1) ** 2])
+                    for l in range(L + 1)], dim=1)
+    lhs = GO.forward(xr, _basis(L, u), W, A)
+    rhs = GO.forward(x, _basis(L, u @ Q), W, A)
+    assert torch.allclose(lhs, rhs, atol=1e-11, rtol=0)
