@@ -177,6 +177,53 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
                                 const float* rbf, const void* w_rad, void* T_out, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* ---- Mixture of linear experts (Appendix C.1, Implementation: UMA's edge
+ * projections use system-dependent mixtures of linear experts; Table 2: 64
+ * experts for UMA). A batch of S systems: system s owns the receiver-sorted
+ * edges [sys_edge_ptr[s], sys_edge_ptr[s+1]) (a structure's nodes form one
+ * range, so its incoming edges are contiguous) and float32 coefficients
+ * coef[s][0..K). Every edge of system s uses
+ *   W1_m(s) = sum_k coef[s][k] W1_m^(k),   W2_m(s) = sum_k coef[s][k] W2_m^(k)
+ * for every order m in place of the plain operator's w1[m], w2[m]; w_rad is
+ * shared. Expert stacks: w1e[m] is [K][rows][cols] of the plain w1[m] layout
+ * (same for w2e, their gradients and directions), in cfg->dtype. The per-order
+ * products run as one grouped GEMM over (system, order) problems; weight
+ * gradients are per system (split-K over its edges, fixed order), then
+ *   gw1e[m][k] = sum_s coef[s][k] gW1_m(s),  gcoef[s][k] = sum_m <W1_m^(k), gW1_m(s)> + (same for W2).
+ * The double backward takes directions pw1e, pw2e, pcoef (NULL = zero) as
+ * the plain one takes pw1, pw2, and returns gw1e_2, gw2e_2, gcoef2 (the
+ * first-order per-system gradients it then needs cost one more weight-gradient
+ * product per linear). Every other argument, output and error is as in
+ * so2conv_fwd/bwd/dbwd; a graph without edges gives zero gradients.
+ * sys_edge_ptr is a HOST array [S+1] with p[0] = 0, p[S] = n_edges,
+ * non-decreasing (empty systems allowed); n_systems in [1, 65536]; n_experts a
+ * multiple of 4 in [4, 1024]; errors SO2_EINVAL / SO2_EUNSUPPORTED otherwise.
+ * Workspace: so2mole_workspace_bytes(stage, chunk_edges) for chunks of
+ * chunk_edges edges (0: all edges in one chunk), valid with or without `saved`. */
+typedef struct {
+  int32_t n_systems;
+  int32_t n_experts;
+  const int64_t* sys_edge_ptr;
+} so2mole_cfg;
+size_t so2mole_workspace_bytes(const so2conv_cfg* cfg, const so2mole_cfg* mole, int32_t n_nodes, int64_t n_edges,
+                               int stage, int64_t chunk_edges);
+int so2mole_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
+                const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
+                const void* const* w2e, const float* coef, void* y, void* saved, void* ws, size_t ws_bytes,
+                void* stream);
+int so2mole_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
+                const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
+                const void* const* w2e, const float* coef, const void* saved, const void* gy, void* gx, float* gpos,
+                float* grbf, float* genv, void* gw_rad, void* const* gw1e, void* const* gw2e, float* gcoef,
+                float* gedge, void* ws, size_t ws_bytes, void* stream);
+int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
+                 const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
+                 const void* const* w2e, const float* coef, const void* saved, const void* gy, const void* px,
+                 const float* ppos, const float* pedge, const float* prbf, const float* penv, const void* pw_rad,
+                 const void* const* pw1e, const void* const* pw2e, const float* pcoef, void* ggy, void* gx2,
+                 float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1e_2, void* const* gw2e_2,
+                 float* gcoef2, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Node-to-node spherical projection with fused channel maps (Appendix B.4,
  * spherical activations). Per node i with coefficient rows X_i^(l) = x[i][l^2..(l+1)^2)
  * (n_l x c_in):

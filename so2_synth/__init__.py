@@ -286,3 +286,40 @@ def make_inputs(cfg: Config, with_directions=True):
         out["w1"] = [round_bf16(w) for w in out["w1"]]
         out["w2"] = [round_bf16(w) for w in out["w2"]]
     return out
+
+
+def mixture_inputs(d: dict, n_systems: int, n_experts: int, seed: int = 0, empty_system: bool = False,
+                   bf16: bool = False) -> dict:
+    """Inputs of the mixture of linear experts (TrimSO(2) page, Appendix C.1,
+    UMA's system-dependent mixtures; Table 2: 64 experts): the batch's nodes
+    split into n_systems contiguous ranges (one more, empty, system when
+    empty_system), their receiver-sorted edge offsets sys_edge_ptr [S+1],
+    expert stacks w1e[m] / w2e[m] [K, rows, cols] drawn like the plain weights,
+    coefficients coef [S, K] (a softmax of standard normal logits per system;
+    the page does not say how UMA forms them, they are an input here) and
+    directions pcoef, pw1e, pw2e (standard normal). bf16: experts and their
+    directions rounded to bfloat16 values."""
+    cfg = d["cfg"]
+    rng = np.random.default_rng(10_000 + seed)
+    N = cfg.n_atoms
+    bounds = [round(N * s / n_systems) for s in range(n_systems + 1)]
+    if empty_system:
+        bounds = bounds[:1] + bounds[1:2] + bounds[1:]          # system 1 has no nodes
+    sys_edge_ptr = np.searchsorted(np.asarray(d["dst"]), bounds).astype(np.int64)
+    sys_edge_ptr[0], sys_edge_ptr[-1] = 0, len(d["dst"])
+    S = len(bounds) - 1
+    w1s, w2s = weight_shapes(cfg.lmax, cfg.mmax, cfg.channels)
+
+    def stack(shapes, scale):
+        return [rng.normal(0.0, scale, size=(n_experts,) + s).astype(np.float32) for s in shapes]
+    sc = 1.0 / math.sqrt(cfg.channels)
+    w1e, w2e = stack(w1s, sc), stack(w2s, sc)
+    logits = rng.normal(size=(S, n_experts))
+    coef = np.exp(logits - logits.max(1, keepdims=True))
+    coef = (coef / coef.sum(1, keepdims=True)).astype(np.float32)
+    pcoef = rng.normal(size=(S, n_experts)).astype(np.float32)
+    pw1e, pw2e = stack(w1s, 1.0), stack(w2s, 1.0)
+    if bf16:
+        w1e, w2e = [round_bf16(w) for w in w1e], [round_bf16(w) for w in w2e]
+        pw1e, pw2e = [round_bf16(w) for w in pw1e], [round_bf16(w) for w in pw2e]
+    return dict(sys_edge_ptr=sys_edge_ptr, w1e=w1e, w2e=w2e, coef=coef, pcoef=pcoef, pw1e=pw1e, pw2e=pw2e)

@@ -9,3 +9,5 @@ from .ops import (DBWD_KEYS, GRAD_KEYS, Graph, SO2Config, so2conv_bwd, so2conv_d
                   so2conv_workspace_bytes, weight_shapes, so2conv_profile_enable, so2conv_profile_read,
                   so2conv_profile_reset, so2conv_chunked_workspace_bytes, so2conv_debug_status)
 from .grid_ops import GridConfig, so2grid_bwd, so2grid_dbwd, so2grid_fwd, so2grid_workspace_bytes  # noqa: F401
+from .mole_ops import (Mixture, expert_shapes, so2mole_bwd, so2mole_dbwd, so2mole_fwd,  # noqa: F401
+                       so2mole_workspace_bytes)

@@ -31,6 +31,10 @@ class GridCfg(ctypes.Structure):
                 ("dtype", c_i32), ("flags", c_i32)]
 
 
+class MoleCfg(ctypes.Structure):
+    _fields_ = [("n_systems", c_i32), ("n_experts", c_i32), ("sys_edge_ptr", c_vp)]
+
+
 class GraphC(ctypes.Structure):
     _fields_ = [("n_nodes", c_i32), ("n_edges", c_i64), ("src", c_vp), ("dst", c_vp), ("shift", c_vp),
                 ("dst_ptr", c_vp), ("src_perm", c_vp), ("src_ptr", c_vp)]
@@ -59,6 +63,14 @@ EXPORTS = {
                                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "so2conv_supported": (ctypes.c_int, [c_i32, c_i32]),
     "so2conv_debug_status": (ctypes.c_int, [c_vp]),
+    "so2mole_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), ctypes.POINTER(MoleCfg), c_i32, c_i64, ctypes.c_int,
+                                       c_i64]),
+    "so2mole_fwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), ctypes.POINTER(MoleCfg)] + [c_vp] * 11
+                    + [c_sz, c_vp]),
+    "so2mole_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), ctypes.POINTER(MoleCfg)] + [c_vp] * 20
+                    + [c_sz, c_vp]),
+    "so2mole_dbwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), ctypes.POINTER(MoleCfg)]
+                     + [c_vp] * 29 + [c_sz, c_vp]),
     "so2grid_workspace_bytes": (c_sz, [ctypes.POINTER(GridCfg), c_i32, ctypes.c_int]),
     # (cfg, N, x, G, W, A, U, ws, ws_bytes, stream)
     "so2grid_fwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 6 + [c_sz, c_vp]),

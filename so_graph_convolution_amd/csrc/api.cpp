@@ -97,6 +97,8 @@ struct Ctx {
   int bf;    // 1: bfloat16 boundary arrays and GEMM operands
   int es;    // bytes per GEMM-operand element
   int debug; // SO2_DEBUG_CHECKS
+  int ns = 1; // weight sets: one per system (the plain operator has one)
+  int nk = 0; // experts of a mixture (0: plain operator)
   size_t node_floats() const { return (size_t)d.d() * d.C; }   // one node row
   int wS() const { return (d.L + 1) * d.Ci(); }
 };
@@ -264,6 +266,59 @@ LinBuf take_lin(Arena& ar, const Ctx& c, int second) {
   return b;
 }
 
+std::vector<LinBuf> take_lins(Arena& ar, const Ctx& c, int second) {
+  std::vector<LinBuf> v(c.ns);
+  for (auto& b : v) b = take_lin(ar, c, second);
+  return v;
+}
+std::vector<float*> take_grads(Arena& ar, const Ctx& c, int second) {
+  std::vector<float*> v(c.ns);
+  for (auto& g : v) g = ar.take(realified_size(c.d, second));
+  return v;
+}
+
+// user-layout block a of linear `second`: [k][cols] (a = 0) or [k][2h] (a >= 1)
+long user_block(const Dims& d, int second, int a) {
+  int r, cc;
+  long off;
+  realified_shape(d, second, a, &r, &cc, &off);
+  return (long)(a ? r / 2 : r) * cc;
+}
+long user_size(const Dims& d, int second) {
+  long n = 0;
+  for (int a = 0; a <= d.M; ++a) n += user_block(d, second, a);
+  return n;
+}
+long max_user_block(const Dims& d) {
+  long n = 0;
+  for (int second = 0; second < 2; ++second)
+    for (int a = 0; a <= d.M; ++a) n = std::max(n, user_block(d, second, a));
+  return n;
+}
+
+// K chunk of the coefficient-gradient products (K = a user block's size)
+constexpr long kCoefChunk = 4096;
+static_assert(kCoefChunk % kGemmKTile == 0, "coefficient split chunks must be whole K tiles");
+
+// Mixture of linear experts: merged weights of every system (block-major:
+// block a of linear `second` holds [S][user_block] at S * (offset of a)),
+// a second such buffer for the double backward, float32 staging of one
+// expert block (bfloat16 experts or expert gradients), and the split-K
+// partials of the coefficient gradients.
+struct MixWs {
+  float *merged, *merged2, *we32, *gwe32, *P;
+};
+void take_mix(Arena& ar, const Ctx& c, int stage, MixWs* m) {
+  *m = MixWs{};
+  if (!c.nk) return;
+  const size_t pm = (size_t)std::max(user_size(c.d, 0), user_size(c.d, 1)), mb = (size_t)max_user_block(c.d);
+  m->merged = ar.take((size_t)c.ns * pm);
+  m->merged2 = stage == 2 ? ar.take((size_t)c.ns * pm) : nullptr;
+  m->we32 = c.bf ? ar.take((size_t)c.nk * mb) : nullptr;
+  m->gwe32 = c.bf && stage > 0 ? ar.take((size_t)c.nk * mb) : nullptr;
+  m->P = stage > 0 ? ar.take((size_t)((mb + kCoefChunk - 1) / kCoefChunk) * c.ns * c.nk) : nullptr;
+}
+
 // largest weight-gradient block (floats): realified blocks and the radial matrix
 size_t max_grad_block(const Ctx& c) {
   size_t mx = (size_t)c.n_rbf * c.wS();
@@ -320,13 +375,15 @@ Primal saved_rows(const Ctx& c, const void* saved, long E, long e0) {
 }
 
 struct FwdWs {
-  LinBuf W1, W2;
+  std::vector<LinBuf> W1, W2;
+  MixWs mix;
   float *w_rad32, *x32, *y32;
   PrimalBuf pr;
 };
 void layout_fwd(Arena& ar, const Ctx& c, int N, long ec, bool recompute, FwdWs* w) {
-  w->W1 = take_lin(ar, c, 0);
-  w->W2 = take_lin(ar, c, 1);
+  w->W1 = take_lins(ar, c, 0);
+  w->W2 = take_lins(ar, c, 1);
+  take_mix(ar, c, 0, &w->mix);
   w->w_rad32 = c.bf ? ar.take((size_t)c.n_rbf * c.wS()) : nullptr;
   w->x32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
   w->y32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
@@ -334,8 +391,10 @@ void layout_fwd(Arena& ar, const Ctx& c, int N, long ec, bool recompute, FwdWs* 
 }
 
 struct BwdWs {
-  LinBuf W1, W2;
-  float *gW1r, *gW2r, *vbar_all;
+  std::vector<LinBuf> W1, W2;
+  std::vector<float*> gW1r, gW2r;
+  MixWs mix;
+  float* vbar_all;
   float *w_rad32, *x32, *gy32, *gx32, *gw_rad32;
   PrimalBuf pr;
   void *tbar, *Ubar;
@@ -344,10 +403,11 @@ struct BwdWs {
 void layout_bwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute, BwdWs* w) {
   const Dims& d = c.d;
   const size_t e = (size_t)ec;
-  w->W1 = take_lin(ar, c, 0);
-  w->W2 = take_lin(ar, c, 1);
-  w->gW1r = ar.take(realified_size(d, 0));
-  w->gW2r = ar.take(realified_size(d, 1));
+  w->W1 = take_lins(ar, c, 0);
+  w->W2 = take_lins(ar, c, 1);
+  w->gW1r = take_grads(ar, c, 0);
+  w->gW2r = take_grads(ar, c, 1);
+  take_mix(ar, c, 1, &w->mix);
   w->vbar_all = ar.take((size_t)E * 3);
   w->w_rad32 = c.bf ? ar.take((size_t)c.n_rbf * c.wS()) : nullptr;
   w->x32 = c.bf ? ar.take((size_t)N * c.node_floats()) : nullptr;
@@ -367,8 +427,10 @@ void layout_bwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute,
 }
 
 struct DbwdWs {
-  LinBuf W1, W2, pW1, pW2;
-  float *gW1r, *gW2r, *vbar2_all, *p2e, *p2d, *p2s;
+  std::vector<LinBuf> W1, W2, pW1, pW2;
+  std::vector<float*> gW1r, gW2r, gW1f, gW2f;   // gW*f: first-order weight gradients (mixture directions)
+  MixWs mix;
+  float *vbar2_all, *p2e, *p2d, *p2s;
   float *w_rad32, *pw_rad32, *x32, *px32, *gy32, *ggy32, *gx2_32, *gw_rad2_32;
   PrimalBuf pr;
   void *Tdot, *Zdot, *G2, *UU;
@@ -377,12 +439,17 @@ struct DbwdWs {
 void layout_dbwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute, DbwdWs* w) {
   const Dims& d = c.d;
   const size_t e = (size_t)ec;
-  w->W1 = take_lin(ar, c, 0);
-  w->W2 = take_lin(ar, c, 1);
-  w->pW1 = take_lin(ar, c, 0);
-  w->pW2 = take_lin(ar, c, 1);
-  w->gW1r = ar.take(realified_size(d, 0));
-  w->gW2r = ar.take(realified_size(d, 1));
+  w->W1 = take_lins(ar, c, 0);
+  w->W2 = take_lins(ar, c, 1);
+  w->pW1 = take_lins(ar, c, 0);
+  w->pW2 = take_lins(ar, c, 1);
+  w->gW1r = take_grads(ar, c, 0);
+  w->gW2r = take_grads(ar, c, 1);
+  if (c.nk) {
+    w->gW1f = take_grads(ar, c, 0);
+    w->gW2f = take_grads(ar, c, 1);
+  }
+  take_mix(ar, c, 2, &w->mix);
   w->vbar2_all = ar.take((size_t)E * 3);      // position derivative per edge vector (all edges)
   w->p2e = ar.take(e * 6);
   w->p2d = ar.take(e * 6);
@@ -590,49 +657,85 @@ int radial(const Ctx& c, long E, const float* rbf, const float* w_rad, float* S,
   return run_batch(ps, false, false, 0, s);
 }
 
-// Per-order products of linear `second` (0: first, 1: second), one problem per order:
+// Weights of one linear per system: edges [e[s], e[s+1]) use W[s] (the plain
+// operator is one system holding every edge).
+struct WSet {
+  std::vector<long> e;
+  std::vector<Lin> W;
+};
+WSet wset(const std::vector<long>& e, const std::vector<LinBuf>& b) {
+  WSet w{e, {}};
+  for (const LinBuf& x : b) w.W.push_back(Lin{x.W, x.WT});
+  return w;
+}
+
+// Per-order products of linear `second` (0: first, 1: second) over the chunk
+// of n edges starting at edge e0, one problem per (system, order):
 //   forward   : C[:, out block a] (+)= A[:, in block a]  W_a
 //   transposed: C[:, in block a]  (+)= A[:, out block a] W_a^T
 // In-blocks: T (first, width wT) or Z (second, width wZ); out-blocks: U (first,
-// width wU) or V (second, width wZ). A is an operand buffer, C float32.
-int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, const Lin& w, int rows, int acc,
-            hipStream_t s) {
+// width wU) or V (second, width wZ). A is an operand buffer, C float32;
+// `stacks` copies of the chunk's rows follow each other in A and C (the
+// double backward's stacked 2n-row products).
+int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, const WSet& w, long e0, int n,
+            int stacks, int acc, hipStream_t s) {
   const Dims& d = c.d;
   const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
+  const int lda = transposed ? wout : win, ldc = transposed ? win : wout;
   std::vector<GemmProb> ps;
-  for (int a = 0; a <= d.M; ++a) {
-    int r, cc;
-    long off;
-    realified_shape(d, second, a, &r, &cc, &off);
-    const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
-    const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
-    if (!transposed) {
-      if (c.bf)
-        ps.push_back(prob(offs(A, ib, c.es), win, offs(w.WT, off, c.es), r, C + ob, wout, rows, cc, r, acc));
-      else
-        ps.push_back(prob(offs(A, ib, c.es), win, offs(w.W, off, c.es), cc, C + ob, wout, rows, cc, r, acc));
-    } else {
-      ps.push_back(prob(offs(A, ob, c.es), wout, offs(w.W, off, c.es), cc, C + ib, win, rows, r, cc, acc));
+  for (int q = 0; q < stacks; ++q)
+    for (size_t sy = 0; sy < w.W.size(); ++sy) {
+      const long lo = std::max(w.e[sy], e0), hi = std::min(w.e[sy + 1], e0 + n);
+      if (hi <= lo) continue;
+      const long r0 = (long)q * n + (lo - e0);
+      const int rows = (int)(hi - lo);
+      const Lin& W = w.W[sy];
+      const void* Ar = offs(A, (size_t)r0 * lda, c.es);
+      float* Cr = C + (size_t)r0 * ldc;
+      for (int a = 0; a <= d.M; ++a) {
+        int r, cc;
+        long off;
+        realified_shape(d, second, a, &r, &cc, &off);
+        const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
+        const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+        if (!transposed) {
+          if (c.bf)
+            ps.push_back(prob(offs(Ar, ib, c.es), win, offs(W.WT, off, c.es), r, Cr + ob, wout, rows, cc, r, acc));
+          else
+            ps.push_back(prob(offs(Ar, ib, c.es), win, offs(W.W, off, c.es), cc, Cr + ob, wout, rows, cc, r, acc));
+        } else {
+          ps.push_back(prob(offs(Ar, ob, c.es), wout, offs(W.W, off, c.es), cc, Cr + ib, win, rows, r, cc, acc));
+        }
+      }
     }
-  }
   return run_batch(ps, false, transposed || c.bf, c.bf, s);
 }
 
-// weight gradient of linear `second` (realified, float32): G_a (+)= sum_s In_s[:, in a]^T Out_s[:, out a]
-int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* const* out, const long* rows, int nseg,
-                 float* G, int acc, float* P, hipStream_t s) {
+// weight gradient of linear `second` per system (realified, float32) over the
+// chunk of n edges at e0: G[s]_a (+)= sum_q In_q[:, in a]^T Out_q[:, out a] on
+// the system's rows. A system's first chunk overwrites its gradient unless
+// `zeroed` (then every chunk accumulates into gradients cleared beforehand).
+int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* const* out, int nseg, int n,
+                 const WSet& w, long e0, const std::vector<float*>& G, bool zeroed, float* P, hipStream_t s) {
   const Dims& d = c.d;
   const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
-  for (int a = 0; a <= d.M; ++a) {
-    int r, cc;
-    long off;
-    realified_shape(d, second, a, &r, &cc, &off);
-    const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
-    const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
-    TnSeg segs[2];
-    for (int q = 0; q < nseg; ++q) segs[q] = {offs(in[q], ib, c.es), win, offs(out[q], ob, c.es), wout, rows[q]};
-    int rr = run_tn(segs, nseg, r, cc, G + off, cc, acc, P, c.bf, s);
-    if (rr) return rr;
+  for (size_t sy = 0; sy < w.W.size(); ++sy) {
+    const long lo = std::max(w.e[sy], e0), hi = std::min(w.e[sy + 1], e0 + n);
+    if (hi <= lo) continue;
+    const int acc = zeroed || lo != w.e[sy];
+    for (int a = 0; a <= d.M; ++a) {
+      int r, cc;
+      long off;
+      realified_shape(d, second, a, &r, &cc, &off);
+      const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
+      const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+      TnSeg segs[2];
+      for (int q = 0; q < nseg; ++q)
+        segs[q] = {offs(in[q], (size_t)(lo - e0) * win + ib, c.es), win,
+                   offs(out[q], (size_t)(lo - e0) * wout + ob, c.es), wout, hi - lo};
+      int rr = run_tn(segs, nseg, r, cc, G[sy] + off, cc, acc, P, c.bf, s);
+      if (rr) return rr;
+    }
   }
   return SO2_OK;
 }
@@ -656,18 +759,156 @@ int realify(const Ctx& c, int second, const void* const* w, const LinBuf& b, hip
   SO2_HIP(launch_realify(c.d, second, w, b.W, b.WT, c.bf, s));
   return SO2_OK;
 }
-Lin lin_of(const LinBuf& b) { return Lin{b.W, b.WT}; }
+
+// ---------------------------------------------------------------- mixture of linear experts
+// System-dependent mixture (TrimSO(2) page, Appendix C.1: UMA's edge
+// projections use system-dependent mixtures of linear experts; Table 2: 64
+// experts): system s uses W(s) = sum_k coef[s][k] W^(k) for both linears and
+// every order. Experts are stacked per order block as [K][user block].
+struct MixIn {
+  std::vector<long> e;   // S+1 edge offsets of the systems
+  const float* coef;     // [S][K], device, float32
+};
+
+// merged (+)= coef . We for every order block of linear `second`: [S][K] x [K][block]
+int mix_linear(const Ctx& c, int second, const void* const* we, const float* coef, float* merged, float* we32,
+               int acc, hipStream_t s) {
+  long off = 0;
+  for (int a = 0; a <= c.d.M; ++a) {
+    const long pm = user_block(c.d, second, a);
+    const float* w32;
+    int r;
+    if ((r = f32_in(c, we[a], we32, (size_t)c.nk * pm, &w32, s))) return r;
+    std::vector<GemmProb> ps{
+        prob(coef, c.nk, w32, (int)pm, merged + (size_t)c.ns * off, (int)pm, c.ns, (int)pm, c.nk, acc)};
+    if ((r = run_batch(ps, false, false, 0, s))) return r;
+    off += pm;
+  }
+  return SO2_OK;
+}
+
+// block pointers of system sy inside a block-major merged buffer
+void sys_blocks(const Ctx& c, int second, float* merged, int sy, void** bp) {
+  long off = 0;
+  for (int a = 0; a <= c.d.M; ++a) {
+    const long pm = user_block(c.d, second, a);
+    bp[a] = merged + (size_t)c.ns * off + (size_t)sy * pm;
+    off += pm;
+  }
+}
+
+int realify_systems(const Ctx& c, int second, float* merged, const std::vector<LinBuf>& b, hipStream_t s) {
+  for (int sy = 0; sy < c.ns; ++sy) {
+    void* bp[kMaxL + 1];
+    sys_blocks(c, second, merged, sy, bp);
+    SO2_HIP(launch_realify(c.d, second, bp, b[sy].W, b[sy].WT, c.bf, s, 1));
+  }
+  return SO2_OK;
+}
+
+// every system's realified gradient of linear `second` folded into a
+// block-major merged buffer (float32, user layout)
+int fold_systems(const Ctx& c, int second, const std::vector<float*>& G, float* merged, hipStream_t s) {
+  for (int sy = 0; sy < c.ns; ++sy) {
+    void* bp[kMaxL + 1];
+    sys_blocks(c, second, merged, sy, bp);
+    SO2_HIP(launch_fold_grad(c.d, second, G[sy], bp, 0, s));
+  }
+  return SO2_OK;
+}
+
+// C (+)= A B^T, A [M][K], B [N][K] (float32), split over K with a fixed-order reduction
+int nt_split(const float* A, int lda, const float* B, int ldb, float* C, int ldc, int M, int N, long K, int acc,
+             float* P, hipStream_t s) {
+  const int sp = (int)((K + kCoefChunk - 1) / kCoefChunk);
+  GemmProb p = prob(A, lda, B, ldb, P, N, M, N, (int)K);
+  p.k_splits = sp;
+  p.k_chunk = (int)kCoefChunk;
+  p.partial = 1;
+  std::vector<GemmProb> ps{p};
+  int r = run_batch(ps, false, true, 0, s);
+  if (r) return r;
+  SO2_HIP(gemm_reduce(P, sp, M, N, C, ldc, acc, s));
+  return SO2_OK;
+}
+
+// Expert and coefficient gradients of linear `second` from the per-system
+// gradients Gm (block-major, float32), for every order block a:
+//   gwe[a]  = coefA^T Gm[a] (+ coefB^T Gm2[a])             [K][S] x [S][block]
+//   gcoef  (+)= Gm[a] WeA[a]^T (+ Gm2[a] WeB[a]^T)         [S][block] x [block][K]
+// The second terms (the double backward's directions on coef and experts)
+// are skipped where their operands are null. gcoef accumulates from the
+// first product on when gcoef_acc.
+int mix_grads(const Ctx& c, int second, const float* Gm, const float* coefA, const void* const* WeA, const float* Gm2,
+              const float* coefB, const void* const* WeB, void* const* gwe, float* gcoef, bool gcoef_acc,
+              const MixWs& mw, hipStream_t s) {
+  long off = 0;
+  int r;
+  bool cacc = gcoef_acc;
+  for (int a = 0; a <= c.d.M; ++a) {
+    const long pm = user_block(c.d, second, a);
+    const float* GA = Gm + (size_t)c.ns * off;
+    const float* GB = Gm2 ? Gm2 + (size_t)c.ns * off : nullptr;
+    if (gcoef) {
+      const float* w32;
+      if ((r = f32_in(c, WeA[a], mw.we32, (size_t)c.nk * pm, &w32, s))) return r;
+      if ((r = nt_split(GA, (int)pm, w32, (int)pm, gcoef, c.nk, c.ns, c.nk, pm, cacc, mw.P, s))) return r;
+      cacc = true;
+      if (GB && WeB && WeB[a]) {
+        if ((r = f32_in(c, WeB[a], mw.we32, (size_t)c.nk * pm, &w32, s))) return r;
+        if ((r = nt_split(GB, (int)pm, w32, (int)pm, gcoef, c.nk, c.ns, c.nk, pm, 1, mw.P, s))) return r;
+      }
+    }
+    if (gwe && gwe[a]) {
+      float* out = c.bf ? mw.gwe32 : static_cast<float*>(gwe[a]);
+      std::vector<GemmProb> p1{prob(coefA, c.nk, GA, (int)pm, out, (int)pm, c.nk, (int)pm, c.ns)};
+      if ((r = run_batch(p1, true, false, 0, s))) return r;
+      if (GB && coefB) {   // accumulates onto the first product: its own launch, after it
+        std::vector<GemmProb> p2{prob(coefB, c.nk, GB, (int)pm, out, (int)pm, c.nk, (int)pm, c.ns, 1)};
+        if ((r = run_batch(p2, true, false, 0, s))) return r;
+      }
+      if (c.bf) SO2_HIP(launch_to_bf16(out, static_cast<bf16s*>(gwe[a]), (size_t)c.nk * pm, s));
+    }
+    off += pm;
+  }
+  return SO2_OK;
+}
+
+// realified weights of both linears per system: the user's (plain operator)
+// or the merged mixture
+int prepare_weights(const Ctx& c, const MixIn* mx, const void* const* w1, const void* const* w2,
+                    const std::vector<LinBuf>& B1, const std::vector<LinBuf>& B2, const MixWs& mw, hipStream_t s) {
+  int r;
+  if (!mx) {
+    if ((r = realify(c, 0, w1, B1[0], s)) || (r = realify(c, 1, w2, B2[0], s))) return r;
+    return SO2_OK;
+  }
+  if ((r = mix_linear(c, 0, w1, mx->coef, mw.merged, mw.we32, 0, s))) return r;
+  if ((r = realify_systems(c, 0, mw.merged, B1, s))) return r;
+  if ((r = mix_linear(c, 1, w2, mx->coef, mw.merged, mw.we32, 0, s))) return r;
+  return realify_systems(c, 1, mw.merged, B2, s);
+}
+
+std::vector<long> sys_edges(const MixIn* mx, long E) { return mx ? mx->e : std::vector<long>{0, E}; }
+
+int zero_sets(const std::vector<float*>& G, size_t n, hipStream_t s) {
+  for (float* g : G) {
+    int r = fill(g, n, s);
+    if (r) return r;
+  }
+  return SO2_OK;
+}
 
 // forward state of the chunk [g.e0, g.e1) into (S, T, U, Z, V)
 int forward_chunk(const Ctx& c, const GraphDev& g, const float* x, const float* pos, const float* rbf,
-                  const float* w_rad, const Lin& W1, const Lin& W2, const PrimalBuf& p, hipStream_t s) {
+                  const float* w_rad, const WSet& W1, const WSet& W2, const PrimalBuf& p, hipStream_t s) {
   const int ec = (int)(g.e1 - g.e0);
   int r;
   if ((r = radial(c, ec, rbf + (size_t)g.e0 * c.n_rbf, w_rad, p.S, s))) return r;
   SO2_HIP(launch_edge_fwd(c.d, g, x, pos, p.S, p.T, c.bf, s));
-  if ((r = run_lin(c, 0, false, p.T, p.U, W1, ec, 0, s))) return r;
+  if ((r = run_lin(c, 0, false, p.T, p.U, W1, g.e0, ec, 1, 0, s))) return r;
   SO2_HIP(launch_gate_fwd(c.d, ec, p.U, p.Z, c.bf, s));
-  return run_lin(c, 1, false, p.Z, p.V, W2, ec, 0, s);
+  return run_lin(c, 1, false, p.Z, p.V, W2, g.e0, ec, 1, 0, s);
 }
 
 int zero_grads(const Ctx& c, int N, void* gx, float* gpos, void* gw_rad, void* const* gw1, void* const* gw2,
@@ -826,6 +1067,325 @@ int grid_map_grads(const GridCtx& g, const float* Gm, const float* W, const floa
   return SO2_OK;
 }
 
+// forward of the plain operator (mx == NULL) or of the mixture of experts
+// (w1, w2: expert stacks)
+int conv_fwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, const float* pos, const float* rbf,
+             const float* env, const void* w_rad, const void* const* w1, const void* const* w2, void* y, void* saved,
+             void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  const Dims& d = c.d;
+  if ((r = check_weights(d, w_rad, w1, w2))) return r;
+  if (!x || !pos || (!rbf && gd.E > 0) || !y) return fail(SO2_EINVAL, "NULL input or output");
+  if ((r = ensure_init())) return r;
+  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
+  const bool recompute = saved == nullptr;
+  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
+  const long ec = pick_chunk(c, gd.N, gd.E, 0, recompute, ws_bytes);
+  if (gd.E > 0 && ec == 0) return fail(SO2_EWORKSPACE, "forward workspace too small for a 1024-edge chunk");
+  if (ws_bytes < ws_need(c, gd.N, gd.E, 0, 0, recompute)) return fail(SO2_EWORKSPACE, "forward workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  Arena ar{static_cast<char*>(ws), 0};
+  FwdWs w;
+  layout_fwd(ar, c, gd.N, ec, recompute, &w);
+  const size_t nf = (size_t)gd.N * c.node_floats();
+  const float *x32, *wr32;
+  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
+  if ((r = f32_in(c, w_rad, w.w_rad32, (size_t)c.n_rbf * c.wS(), &wr32, s))) return r;
+  float* y32 = f32_acc(c, y, w.y32);
+  if ((r = prepare_weights(c, mx, w1, w2, w.W1, w.W2, w.mix, s))) return r;
+  const std::vector<long> se = sys_edges(mx, gd.E);
+  const WSet W1 = wset(se, w.W1), W2 = wset(se, w.W2);
+  if (gd.E == 0) {
+    GraphDev gc = gd;
+    gc.e0 = gc.e1 = 0;
+    SO2_HIP(launch_node_fwd(d, gc, pos, nullptr, nullptr, y32, 0, s));
+    return f32_out(c, y32, y, nf, s);
+  }
+  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
+    GraphDev gc = gd;
+    gc.e0 = e0;
+    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
+    PrimalBuf p = w.pr;
+    if (!recompute) {
+      const SavedLayout sl = saved_layout(c, gd.E);
+      char* st = static_cast<char*>(saved);
+      p.S = reinterpret_cast<float*>(st + sl.S) + (size_t)e0 * c.wS();
+      p.T = st + sl.T + (size_t)e0 * d.wT() * c.es;
+      p.U = reinterpret_cast<float*>(st + sl.U) + (size_t)e0 * d.wU();
+      p.Z = st + sl.Z + (size_t)e0 * d.wZ() * c.es;
+      p.V = reinterpret_cast<float*>(st + sl.V) + (size_t)e0 * d.wZ();
+    }
+    if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, p, s))) return r;
+    SO2_HIP(launch_node_fwd(d, gc, pos, p.V, env, y32, k > 0, s));
+  }
+  return f32_out(c, y32, y, nf, s);
+}
+
+// backward of the plain operator (mx == NULL) or of the mixture (w1, w2,
+// gw1, gw2: expert stacks; gcoef: coefficient gradient)
+int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, const float* pos, const float* rbf,
+             const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
+             const void* gy, void* gx, float* gpos, float* grbf, float* genv, void* gw_rad, void* const* gw1,
+             void* const* gw2, float* gcoef, float* gedge, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  const Dims& d = c.d;
+  if ((r = check_weights(d, w_rad, w1, w2))) return r;
+  if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
+  if (genv && !env) return fail(SO2_EINVAL, "genv requested without an envelope");
+  if ((r = ensure_init())) return r;
+  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
+  hipStream_t s = (hipStream_t)stream;
+  const int n_rbf = c.n_rbf, wS = c.wS();
+  if (gd.E == 0 && !mx) return zero_grads(c, gd.N, gx, gpos, gw_rad, gw1, gw2, s);
+  const bool recompute = saved == nullptr;
+  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
+  const long ec = pick_chunk(c, gd.N, gd.E, 1, recompute, ws_bytes);
+  if (ec == 0) return fail(SO2_EWORKSPACE, "backward workspace too small for a 1024-edge chunk");
+  Arena ar{static_cast<char*>(ws), 0};
+  BwdWs w;
+  layout_bwd(ar, c, gd.N, gd.E, ec, recompute, &w);
+  const size_t nf = (size_t)gd.N * c.node_floats();
+  const float *x32, *gy32, *wr32;
+  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
+  if ((r = f32_in(c, gy, w.gy32, nf, &gy32, s))) return r;
+  if ((r = f32_in(c, w_rad, w.w_rad32, (size_t)n_rbf * wS, &wr32, s))) return r;
+  float* gx_acc = f32_acc(c, gx, w.gx32);
+  float* gwr_acc = f32_acc(c, gw_rad, w.gw_rad32);
+  float* vbar = gedge ? gedge : w.vbar_all;
+  const bool want_w1 = !all_null(gw1, d.M + 1) || gcoef, want_w2 = !all_null(gw2, d.M + 1) || gcoef;
+  if ((r = prepare_weights(c, mx, w1, w2, w.W1, w.W2, w.mix, s))) return r;
+  const std::vector<long> se = sys_edges(mx, gd.E);
+  const WSet W1 = wset(se, w.W1), W2 = wset(se, w.W2);
+  if (mx && want_w1 && (r = zero_sets(w.gW1r, realified_size(d, 0), s))) return r;
+  if (mx && want_w2 && (r = zero_sets(w.gW2r, realified_size(d, 1), s))) return r;
+  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
+    GraphDev gc = gd;
+    gc.e0 = e0;
+    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
+    const int n = (int)(gc.e1 - gc.e0);
+    const int acc = k > 0;
+    Primal pr;
+    if (recompute) {
+      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
+      pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
+    } else {
+      pr = saved_rows(c, saved, gd.E, e0);
+    }
+    // E -> N transpose: tbar = R gy[dst], tau1 = rotation torque of <V, R gy>
+    SO2_HIP(launch_edge_bwd(d, gc, pos, gy32, pr.V, env, w.tbar, w.tau1, genv, c.bf, s));
+    if ((r = run_lin(c, 1, true, w.tbar, w.Zbar, W2, e0, n, 1, 0, s))) return r;
+    if (want_w2) {
+      const void* in[1] = {pr.Z};
+      const void* out[1] = {w.tbar};
+      if ((r = run_lin_grad(c, 1, in, out, 1, n, W2, e0, w.gW2r, mx != nullptr, w.P, s))) return r;
+    }
+    SO2_HIP(launch_gate_bwd(d, n, pr.U, w.Zbar, w.Ubar, c.bf, s));
+    if ((r = run_lin(c, 0, true, w.Ubar, w.Tbar, W1, e0, n, 1, 0, s))) return r;
+    if (want_w1) {
+      const void* in[1] = {pr.T};
+      const void* out[1] = {w.Ubar};
+      if ((r = run_lin_grad(c, 0, in, out, 1, n, W1, e0, w.gW1r, mx != nullptr, w.P, s))) return r;
+    }
+    // N -> E transpose: gx (both halves), Sbar, position torques
+    SO2_HIP(launch_node_bwd(d, gc, x32, pos, pr.S, w.Tbar, gx_acc, w.Sbar, w.tau2, w.tau3, acc, s));
+    if (grbf) {
+      std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, grbf + (size_t)e0 * n_rbf, n_rbf, n, n_rbf, wS)};
+      if ((r = run_batch(ps, false, true, 0, s))) return r;
+    }
+    if (gwr_acc) {
+      TnSeg seg{rbf + (size_t)e0 * n_rbf, n_rbf, w.Sbar, wS, n};
+      if ((r = run_tn(&seg, 1, n_rbf, wS, gwr_acc, wS, acc, w.P, 0, s))) return r;
+    }
+    if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, w.tau1, w.tau2, w.tau3, vbar, s));
+  }
+  if (!mx) {
+    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2, c.bf, s));
+    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1, c.bf, s));
+  } else {
+    for (int second = 0; second < 2; ++second) {
+      if (!(second ? want_w2 : want_w1)) continue;
+      if ((r = fold_systems(c, second, second ? w.gW2r : w.gW1r, w.mix.merged, s))) return r;
+      if ((r = mix_grads(c, second, w.mix.merged, mx->coef, second ? w2 : w1, nullptr, nullptr, nullptr,
+                         second ? gw2 : gw1, gcoef, second == 1 && want_w1, w.mix, s)))
+        return r;
+    }
+  }
+  if (gpos) SO2_HIP(launch_node_pos(gd, vbar, gpos, s));
+  if ((r = f32_out(c, gx_acc, gx, nf, s))) return r;
+  return f32_out(c, gwr_acc, gw_rad, (size_t)n_rbf * wS, s);
+}
+
+// double backward of the plain operator (mx == NULL) or of the mixture
+// (w1, w2, pw1, pw2, gw1_2, gw2_2: expert stacks; pcoef: direction on the
+// coefficients; gcoef2: their derivative)
+int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, const float* pos, const float* rbf,
+              const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
+              const void* gy, const void* px, const float* ppos, const float* pedge, const float* prbf,
+              const float* penv, const void* pw_rad, const void* const* pw1, const void* const* pw2,
+              const float* pcoef, void* ggy, void* gx2, float* gpos2, float* grbf2, float* genv2, void* gw_rad2,
+              void* const* gw1_2, void* const* gw2_2, float* gcoef2, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  const Dims& d = c.d;
+  if ((r = check_weights(d, w_rad, w1, w2))) return r;
+  if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
+  if ((penv || genv2) && !env) return fail(SO2_EINVAL, "penv or genv2 given without an envelope");
+  if ((r = ensure_init())) return r;
+  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
+  const bool has_pwe1 = !all_null(pw1, d.M + 1), has_pwe2 = !all_null(pw2, d.M + 1);
+  // directions on the weights of each system: the user's (plain), or
+  // coef pWe + pcoef We (mixture)
+  const bool has_pw1 = has_pwe1 || (mx && pcoef), has_pw2 = has_pwe2 || (mx && pcoef);
+  // first-order weight gradients per system, needed for the mixture's directions
+  const bool first = mx && (pcoef || has_pwe1 || has_pwe2);
+  if (has_pwe1)
+    for (int a = 0; a <= d.M; ++a)
+      if (!pw1[a]) return fail(SO2_EINVAL, "pw1 must be NULL or hold M+1 non-NULL blocks");
+  if (has_pwe2)
+    for (int a = 0; a <= d.M; ++a)
+      if (!pw2[a]) return fail(SO2_EINVAL, "pw2 must be NULL or hold M+1 non-NULL blocks");
+  hipStream_t s = (hipStream_t)stream;
+  const int n_rbf = c.n_rbf, wS = c.wS();
+  if (gd.E == 0 && !mx) {
+    int rr = zero_grads(c, gd.N, gx2, gpos2, gw_rad2, gw1_2, gw2_2, s);
+    if (rr) return rr;
+    if (ggy) return zero(c, ggy, (size_t)gd.N * c.node_floats(), s);
+    return SO2_OK;
+  }
+  const bool recompute = saved == nullptr;
+  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
+  const long ec = pick_chunk(c, gd.N, gd.E, 2, recompute, ws_bytes);
+  if (ec == 0) return fail(SO2_EWORKSPACE, "double-backward workspace too small for a 1024-edge chunk");
+  Arena ar{static_cast<char*>(ws), 0};
+  DbwdWs w;
+  layout_dbwd(ar, c, gd.N, gd.E, ec, recompute, &w);
+  const size_t nf = (size_t)gd.N * c.node_floats(), rf = (size_t)n_rbf * wS;
+  const float *x32, *px32, *gy32, *wr32, *pwr32;
+  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
+  if ((r = f32_in(c, px, w.px32, nf, &px32, s))) return r;
+  if ((r = f32_in(c, gy, w.gy32, nf, &gy32, s))) return r;
+  if ((r = f32_in(c, w_rad, w.w_rad32, rf, &wr32, s))) return r;
+  if ((r = f32_in(c, pw_rad, w.pw_rad32, rf, &pwr32, s))) return r;
+  float* ggy_acc = f32_acc(c, ggy, w.ggy32);
+  float* gx2_acc = f32_acc(c, gx2, w.gx2_32);
+  float* gwr2_acc = f32_acc(c, gw_rad2, w.gw_rad2_32);
+  const bool want_w1 = !all_null(gw1_2, d.M + 1) || gcoef2, want_w2 = !all_null(gw2_2, d.M + 1) || gcoef2;
+  if ((r = prepare_weights(c, mx, w1, w2, w.W1, w.W2, w.mix, s))) return r;
+  if (!mx) {
+    if (has_pw1 && (r = realify(c, 0, pw1, w.pW1[0], s))) return r;
+    if (has_pw2 && (r = realify(c, 1, pw2, w.pW2[0], s))) return r;
+  } else {
+    for (int second = 0; second < 2; ++second) {
+      const bool hp = second ? has_pw2 : has_pw1, hwe = second ? has_pwe2 : has_pwe1;
+      if (!hp) continue;
+      if (hwe && (r = mix_linear(c, second, second ? pw2 : pw1, mx->coef, w.mix.merged, w.mix.we32, 0, s)))
+        return r;
+      if (pcoef && (r = mix_linear(c, second, second ? w2 : w1, pcoef, w.mix.merged, w.mix.we32, hwe, s))) return r;
+      if ((r = realify_systems(c, second, w.mix.merged, second ? w.pW2 : w.pW1, s))) return r;
+    }
+    if (want_w1 && (r = zero_sets(w.gW1r, realified_size(d, 0), s))) return r;
+    if (want_w2 && (r = zero_sets(w.gW2r, realified_size(d, 1), s))) return r;
+    if (first && want_w1 && (r = zero_sets(w.gW1f, realified_size(d, 0), s))) return r;
+    if (first && want_w2 && (r = zero_sets(w.gW2f, realified_size(d, 1), s))) return r;
+  }
+  const std::vector<long> se = sys_edges(mx, gd.E);
+  const WSet W1 = wset(se, w.W1), W2 = wset(se, w.W2), pW1 = wset(se, w.pW1), pW2 = wset(se, w.pW2);
+  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
+    GraphDev gc = gd;
+    gc.e0 = e0;
+    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
+    const int n = (int)(gc.e1 - gc.e0);
+    const int acc = k > 0;
+    const float* rbf_c = rbf + (size_t)e0 * n_rbf;
+    const float* prbf_c = prbf ? prbf + (size_t)e0 * n_rbf : nullptr;
+    Primal pr;
+    if (recompute) {
+      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
+      pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
+    } else {
+      pr = saved_rows(c, saved, gd.E, e0);
+    }
+
+    // ---- tangent (dual) forward along (px, ppos, pedge, prbf, pW)
+    if (prbf_c) {
+      if ((r = radial(c, n, prbf_c, wr32, w.Sdot, s))) return r;
+    } else if ((r = fill(w.Sdot, (size_t)n * wS, s))) {
+      return r;
+    }
+    if (pwr32) {
+      if ((r = radial(c, n, rbf_c, pwr32, w.Sdot, s, 1))) return r;
+    }
+    SO2_HIP(launch_edge_dual(d, gc, x32, px32, pos, ppos, pedge, pr.S, w.Sdot, w.Tdot, w.omega, c.bf, s));
+    if ((r = run_lin(c, 0, false, w.Tdot, w.Udot, W1, e0, n, 1, 0, s))) return r;
+    if (has_pw1 && (r = run_lin(c, 0, false, pr.T, w.Udot, pW1, e0, n, 1, 1, s))) return r;
+    SO2_HIP(launch_gate_dual(d, n, pr.U, w.Udot, w.Zdot, c.bf, s));
+    if ((r = run_lin(c, 1, false, w.Zdot, w.Vdot, W2, e0, n, 1, 0, s))) return r;
+    if (has_pw2 && (r = run_lin(c, 1, false, pr.Z, w.Vdot, pW2, e0, n, 1, 1, s))) return r;
+    // dL/dgy = the forward's directional derivative (Eq.(5))
+    if (ggy_acc) SO2_HIP(launch_node_dual(d, gc, pos, w.omega, pr.V, w.Vdot, env, penv, ggy_acc, acc, s));
+
+    // ---- reverse of the tangent output with cotangent gy
+    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, pr.V, w.Vdot, env, penv,
+                                 gpos2 ? w.p2e : nullptr, genv2, s));
+    // [Zdot_bar; Zbar] = G2 W2^T (2n stacked rows)
+    if ((r = run_lin(c, 1, true, w.G2, w.ZZ, W2, e0, n, 2, 0, s))) return r;
+    // Zbar += tbar pW2^T
+    if (has_pw2 && (r = run_lin(c, 1, true, w.G2, w.ZZ + (size_t)n * d.wZ(), pW2, e0, n, 1, 1, s))) return r;
+    if (want_w2) {
+      const void* in[2] = {w.Zdot, pr.Z};
+      const void* out[2] = {w.G2, offs(static_cast<const void*>(w.G2), (size_t)n * d.wZ(), c.es)};
+      if ((r = run_lin_grad(c, 1, in, out, 2, n, W2, e0, w.gW2r, mx != nullptr, w.P, s))) return r;
+      // first-order gradient Z^T tbar (tbar: the first n rows of G2)
+      if (first && (r = run_lin_grad(c, 1, &in[1], out, 1, n, W2, e0, w.gW2f, true, w.P, s))) return r;
+    }
+    SO2_HIP(launch_gate_dbwd(d, n, pr.U, w.Udot, w.ZZ, w.UU, c.bf, s));   // [Udot_bar; Ubar]
+    // [Tdot_bar; Tbar] = UU W1^T
+    if ((r = run_lin(c, 0, true, w.UU, w.TT, W1, e0, n, 2, 0, s))) return r;
+    // Tbar += Udot_bar pW1^T
+    if (has_pw1 && (r = run_lin(c, 0, true, w.UU, w.TT + (size_t)n * d.wT(), pW1, e0, n, 1, 1, s))) return r;
+    if (want_w1) {
+      const void* in[2] = {w.Tdot, pr.T};
+      const void* out[2] = {w.UU, offs(static_cast<const void*>(w.UU), (size_t)n * d.wU(), c.es)};
+      if ((r = run_lin_grad(c, 0, in, out, 2, n, W1, e0, w.gW1r, mx != nullptr, w.P, s))) return r;
+      // first-order gradient T^T Ubar (Ubar: the first n rows of UU)
+      if (first && (r = run_lin_grad(c, 0, &in[1], out, 1, n, W1, e0, w.gW1f, true, w.P, s))) return r;
+    }
+    SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, w.TT, gx2_acc, w.Sbar, w.Sdb,
+                                 gpos2 ? w.p2d : nullptr, gpos2 ? w.p2s : nullptr, acc, s));
+    if (gpos2) SO2_HIP(launch_pos2(gc, pos, ppos, pedge, w.omega, w.p2e, w.p2d, w.p2s, w.vbar2_all, s));
+    if (grbf2) {
+      float* out = grbf2 + (size_t)e0 * n_rbf;
+      std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, out, n_rbf, n, n_rbf, wS)};
+      if ((r = run_batch(ps, false, true, 0, s))) return r;
+      if (pwr32) {
+        std::vector<GemmProb> ps2{prob(w.Sdb, wS, pwr32, wS, out, n_rbf, n, n_rbf, wS, 1)};
+        if ((r = run_batch(ps2, false, true, 0, s))) return r;
+      }
+    }
+    if (gwr2_acc) {
+      TnSeg segs[2] = {{rbf_c, n_rbf, w.Sbar, wS, n}, {prbf_c, n_rbf, w.Sdb, wS, prbf_c ? n : 0}};
+      if ((r = run_tn(segs, 2, n_rbf, wS, gwr2_acc, wS, acc, w.P, 0, s))) return r;
+    }
+  }
+  if (!mx) {
+    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2_2, c.bf, s));
+    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1_2, c.bf, s));
+  } else {
+    for (int second = 0; second < 2; ++second) {
+      if (!(second ? want_w2 : want_w1)) continue;
+      if ((r = fold_systems(c, second, second ? w.gW2r : w.gW1r, w.mix.merged, s))) return r;
+      if (first && (r = fold_systems(c, second, second ? w.gW2f : w.gW1f, w.mix.merged2, s))) return r;
+      if ((r = mix_grads(c, second, w.mix.merged, mx->coef, second ? w2 : w1, first ? w.mix.merged2 : nullptr,
+                         pcoef, second ? pw2 : pw1, second ? gw2_2 : gw1_2, gcoef2, second == 1 && want_w1,
+                         w.mix, s)))
+        return r;
+    }
+  }
+  if (gpos2) SO2_HIP(launch_node_pos(gd, w.vbar2_all, gpos2, s));
+  if ((r = f32_out(c, ggy_acc, ggy, nf, s))) return r;
+  if ((r = f32_out(c, gx2_acc, gx2, nf, s))) return r;
+  return f32_out(c, gwr2_acc, gw_rad2, rf, s);
+}
+
 }  // namespace
 
 // =====================================================================================
@@ -956,50 +1516,7 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
   GraphDev gd;
   int r;
   if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
-  const Dims& d = c.d;
-  if ((r = check_weights(d, w_rad, w1, w2))) return r;
-  if (!x || !pos || (!rbf && gd.E > 0) || !y) return fail(SO2_EINVAL, "NULL input or output");
-  if ((r = ensure_init())) return r;
-  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
-  const bool recompute = saved == nullptr;
-  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
-  const long ec = pick_chunk(c, gd.N, gd.E, 0, recompute, ws_bytes);
-  if (gd.E > 0 && ec == 0) return fail(SO2_EWORKSPACE, "forward workspace too small for a 1024-edge chunk");
-  if (ws_bytes < ws_need(c, gd.N, gd.E, 0, 0, recompute)) return fail(SO2_EWORKSPACE, "forward workspace too small");
-  hipStream_t s = (hipStream_t)stream;
-  Arena ar{static_cast<char*>(ws), 0};
-  FwdWs w;
-  layout_fwd(ar, c, gd.N, ec, recompute, &w);
-  const size_t nf = (size_t)gd.N * c.node_floats();
-  const float *x32, *wr32;
-  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
-  if ((r = f32_in(c, w_rad, w.w_rad32, (size_t)c.n_rbf * c.wS(), &wr32, s))) return r;
-  float* y32 = f32_acc(c, y, w.y32);
-  if ((r = realify(c, 0, w1, w.W1, s)) || (r = realify(c, 1, w2, w.W2, s))) return r;
-  if (gd.E == 0) {
-    GraphDev gc = gd;
-    gc.e0 = gc.e1 = 0;
-    SO2_HIP(launch_node_fwd(d, gc, pos, nullptr, nullptr, y32, 0, s));
-    return f32_out(c, y32, y, nf, s);
-  }
-  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
-    GraphDev gc = gd;
-    gc.e0 = e0;
-    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
-    PrimalBuf p = w.pr;
-    if (!recompute) {
-      const SavedLayout sl = saved_layout(c, gd.E);
-      char* st = static_cast<char*>(saved);
-      p.S = reinterpret_cast<float*>(st + sl.S) + (size_t)e0 * c.wS();
-      p.T = st + sl.T + (size_t)e0 * d.wT() * c.es;
-      p.U = reinterpret_cast<float*>(st + sl.U) + (size_t)e0 * d.wU();
-      p.Z = st + sl.Z + (size_t)e0 * d.wZ() * c.es;
-      p.V = reinterpret_cast<float*>(st + sl.V) + (size_t)e0 * d.wZ();
-    }
-    if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, lin_of(w.W1), lin_of(w.W2), p, s))) return r;
-    SO2_HIP(launch_node_fwd(d, gc, pos, p.V, env, y32, k > 0, s));
-  }
-  return f32_out(c, y32, y, nf, s);
+  return conv_fwd(c, gd, nullptr, x, pos, rbf, env, w_rad, w1, w2, y, saved, ws, ws_bytes, stream);
 }
 
 int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
@@ -1011,81 +1528,8 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
   GraphDev gd;
   int r;
   if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
-  const Dims& d = c.d;
-  if ((r = check_weights(d, w_rad, w1, w2))) return r;
-  if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
-  if (genv && !env) return fail(SO2_EINVAL, "genv requested without an envelope");
-  if ((r = ensure_init())) return r;
-  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
-  hipStream_t s = (hipStream_t)stream;
-  const int n_rbf = c.n_rbf, wS = c.wS();
-  if (gd.E == 0) return zero_grads(c, gd.N, gx, gpos, gw_rad, gw1, gw2, s);
-  const bool recompute = saved == nullptr;
-  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
-  const long ec = pick_chunk(c, gd.N, gd.E, 1, recompute, ws_bytes);
-  if (ec == 0) return fail(SO2_EWORKSPACE, "backward workspace too small for a 1024-edge chunk");
-  Arena ar{static_cast<char*>(ws), 0};
-  BwdWs w;
-  layout_bwd(ar, c, gd.N, gd.E, ec, recompute, &w);
-  const size_t nf = (size_t)gd.N * c.node_floats();
-  const float *x32, *gy32, *wr32;
-  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
-  if ((r = f32_in(c, gy, w.gy32, nf, &gy32, s))) return r;
-  if ((r = f32_in(c, w_rad, w.w_rad32, (size_t)n_rbf * wS, &wr32, s))) return r;
-  float* gx_acc = f32_acc(c, gx, w.gx32);
-  float* gwr_acc = f32_acc(c, gw_rad, w.gw_rad32);
-  float* vbar = gedge ? gedge : w.vbar_all;
-  const bool want_w1 = !all_null(gw1, d.M + 1), want_w2 = !all_null(gw2, d.M + 1);
-  const Lin W1 = lin_of(w.W1), W2 = lin_of(w.W2);
-
-  if ((r = realify(c, 0, w1, w.W1, s)) || (r = realify(c, 1, w2, w.W2, s))) return r;
-  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
-    GraphDev gc = gd;
-    gc.e0 = e0;
-    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
-    const int n = (int)(gc.e1 - gc.e0);
-    const int acc = k > 0;
-    Primal pr;
-    if (recompute) {
-      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
-      pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
-    } else {
-      pr = saved_rows(c, saved, gd.E, e0);
-    }
-    // E -> N transpose: tbar = R gy[dst], tau1 = rotation torque of <V, R gy>
-    SO2_HIP(launch_edge_bwd(d, gc, pos, gy32, pr.V, env, w.tbar, w.tau1, genv, c.bf, s));
-    if ((r = run_lin(c, 1, true, w.tbar, w.Zbar, W2, n, 0, s))) return r;
-    if (want_w2) {
-      const void* in[1] = {pr.Z};
-      const void* out[1] = {w.tbar};
-      const long rows[1] = {n};
-      if ((r = run_lin_grad(c, 1, in, out, rows, 1, w.gW2r, acc, w.P, s))) return r;
-    }
-    SO2_HIP(launch_gate_bwd(d, n, pr.U, w.Zbar, w.Ubar, c.bf, s));
-    if ((r = run_lin(c, 0, true, w.Ubar, w.Tbar, W1, n, 0, s))) return r;
-    if (want_w1) {
-      const void* in[1] = {pr.T};
-      const void* out[1] = {w.Ubar};
-      const long rows[1] = {n};
-      if ((r = run_lin_grad(c, 0, in, out, rows, 1, w.gW1r, acc, w.P, s))) return r;
-    }
-    // N -> E transpose: gx (both halves), Sbar, position torques
-    SO2_HIP(launch_node_bwd(d, gc, x32, pos, pr.S, w.Tbar, gx_acc, w.Sbar, w.tau2, w.tau3, acc, s));
-    if (grbf) {
-      std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, grbf + (size_t)e0 * n_rbf, n_rbf, n, n_rbf, wS)};
-      if ((r = run_batch(ps, false, true, 0, s))) return r;
-    }
-    if (gwr_acc) {
-      TnSeg seg{rbf + (size_t)e0 * n_rbf, n_rbf, w.Sbar, wS, n};
-      if ((r = run_tn(&seg, 1, n_rbf, wS, gwr_acc, wS, acc, w.P, 0, s))) return r;
-    }
-    if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, w.tau1, w.tau2, w.tau3, vbar, s));
-  }
-  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r, gw2, c.bf, s));
-  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r, gw1, c.bf, s));
-  if (gpos) SO2_HIP(launch_node_pos(gd, vbar, gpos, s));
-  if ((r = f32_out(c, gx_acc, gx, nf, s))) return r;
-  return f32_out(c, gwr_acc, gw_rad, (size_t)n_rbf * wS, s);
+  return conv_bwd(c, gd, nullptr, x, pos, rbf, env, w_rad, w1, w2, saved, gy, gx, gpos, grbf, genv, gw_rad, gw1, gw2,
+                  nullptr, gedge, ws, ws_bytes, stream);
 }
 
 int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
@@ -1099,131 +1543,128 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
   GraphDev gd;
   int r;
   if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
-  const Dims& d = c.d;
-  if ((r = check_weights(d, w_rad, w1, w2))) return r;
-  if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
-  if ((penv || genv2) && !env) return fail(SO2_EINVAL, "penv or genv2 given without an envelope");
-  if ((r = ensure_init())) return r;
-  if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
-  const bool has_pw1 = !all_null(pw1, d.M + 1), has_pw2 = !all_null(pw2, d.M + 1);
-  if (has_pw1)
-    for (int a = 0; a <= d.M; ++a)
-      if (!pw1[a]) return fail(SO2_EINVAL, "pw1 must be NULL or hold M+1 non-NULL blocks");
-  if (has_pw2)
-    for (int a = 0; a <= d.M; ++a)
-      if (!pw2[a]) return fail(SO2_EINVAL, "pw2 must be NULL or hold M+1 non-NULL blocks");
-  hipStream_t s = (hipStream_t)stream;
-  const int n_rbf = c.n_rbf, wS = c.wS();
+  return conv_dbwd(c, gd, nullptr, x, pos, rbf, env, w_rad, w1, w2, saved, gy, px, ppos, pedge, prbf, penv, pw_rad,
+                   pw1, pw2, nullptr, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1_2, gw2_2, nullptr, ws, ws_bytes,
+                   stream);
+}
+
+// ---------------------------------------------------------------- mixture of linear experts entry points
+}  // extern "C"
+
+namespace {
+
+int check_mole(const Ctx& c0, const so2mole_cfg* m, long E, Ctx* c, MixIn* mx) {
+  *c = c0;
+  if (!m) return fail(SO2_EINVAL, "mixture cfg is NULL");
+  if (m->n_systems < 1 || m->n_systems > 65536) return fail(SO2_EUNSUPPORTED, "n_systems must be in [1, 65536]");
+  if (m->n_experts < 4 || m->n_experts > 1024 || m->n_experts % 4)
+    return fail(SO2_EUNSUPPORTED, "n_experts must be a multiple of 4 in [4, 1024]");
+  if (!m->sys_edge_ptr) return fail(SO2_EINVAL, "sys_edge_ptr is NULL");
+  const int64_t* p = m->sys_edge_ptr;
+  if (p[0] != 0 || p[m->n_systems] != E) return fail(SO2_EINVAL, "sys_edge_ptr must run from 0 to n_edges");
+  for (int s = 0; s < m->n_systems; ++s)
+    if (p[s + 1] < p[s]) return fail(SO2_EINVAL, "sys_edge_ptr must be non-decreasing");
+  c->ns = m->n_systems;
+  c->nk = m->n_experts;
+  mx->e.assign(p, p + m->n_systems + 1);
+  mx->coef = nullptr;
+  return SO2_OK;
+}
+
+int check_mole_call(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* m, const float* coef, Ctx* c,
+                    GraphDev* gd, MixIn* mx) {
+  Ctx c0;
+  int r;
+  if ((r = check_cfg(cfg, &c0)) || (r = check_graph(g, gd)) || (r = check_mole(c0, m, gd->E, c, mx))) return r;
+  if (!coef) return fail(SO2_EINVAL, "coef is NULL");
+  mx->coef = coef;
+  return SO2_OK;
+}
+
+// outputs of a mixture call on a graph without edges: every gradient is zero
+int zero_mole_grads(const Ctx& c, void* const* gw1, void* const* gw2, float* gcoef, hipStream_t s) {
+  int r;
+  for (int second = 0; second < 2; ++second) {
+    void* const* gw = second ? gw2 : gw1;
+    if (!gw) continue;
+    for (int a = 0; a <= c.d.M; ++a)
+      if (gw[a] && (r = zero(c, gw[a], (size_t)c.nk * user_block(c.d, second, a), s))) return r;
+  }
+  if (gcoef && (r = fill(gcoef, (size_t)c.ns * c.nk, s))) return r;
+  return SO2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t so2mole_workspace_bytes(const so2conv_cfg* cfg, const so2mole_cfg* mole, int32_t n_nodes, int64_t n_edges,
+                               int stage, int64_t chunk_edges) {
+  Ctx c0, c;
+  MixIn mx;
+  if (check_cfg(cfg, &c0) || stage < 0 || stage > 2 || n_nodes < 0 || n_edges < 0 || chunk_edges < 0) return 0;
+  if (check_mole(c0, mole, n_edges, &c, &mx)) return 0;
+  const long ec = chunk_edges == 0 || chunk_edges > n_edges ? n_edges : chunk_edges;
+  return ws_need(c, n_nodes, n_edges, ec, stage, true);
+}
+
+int so2mole_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
+                const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
+                const void* const* w2e, const float* coef, void* y, void* saved, void* ws, size_t ws_bytes,
+                void* stream) {
+  g_err.clear();
+  Ctx c;
+  GraphDev gd;
+  MixIn mx;
+  int r;
+  if ((r = check_mole_call(cfg, g, mole, coef, &c, &gd, &mx))) return r;
+  return conv_fwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, y, saved, ws, ws_bytes, stream);
+}
+
+int so2mole_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
+                const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
+                const void* const* w2e, const float* coef, const void* saved, const void* gy, void* gx, float* gpos,
+                float* grbf, float* genv, void* gw_rad, void* const* gw1e, void* const* gw2e, float* gcoef,
+                float* gedge, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Ctx c;
+  GraphDev gd;
+  MixIn mx;
+  int r;
+  if ((r = check_mole_call(cfg, g, mole, coef, &c, &gd, &mx))) return r;
   if (gd.E == 0) {
-    int rr = zero_grads(c, gd.N, gx2, gpos2, gw_rad2, gw1_2, gw2_2, s);
-    if (rr) return rr;
-    if (ggy) return zero(c, ggy, (size_t)gd.N * c.node_floats(), s);
-    return SO2_OK;
+    if ((r = check_weights(c.d, w_rad, w1e, w2e))) return r;
+    hipStream_t s = (hipStream_t)stream;
+    if ((r = zero_grads(c, gd.N, gx, gpos, gw_rad, nullptr, nullptr, s))) return r;
+    return zero_mole_grads(c, gw1e, gw2e, gcoef, s);
   }
-  const bool recompute = saved == nullptr;
-  if (!ws) return fail(SO2_EWORKSPACE, "workspace is NULL");
-  const long ec = pick_chunk(c, gd.N, gd.E, 2, recompute, ws_bytes);
-  if (ec == 0) return fail(SO2_EWORKSPACE, "double-backward workspace too small for a 1024-edge chunk");
-  Arena ar{static_cast<char*>(ws), 0};
-  DbwdWs w;
-  layout_dbwd(ar, c, gd.N, gd.E, ec, recompute, &w);
-  const size_t nf = (size_t)gd.N * c.node_floats(), rf = (size_t)n_rbf * wS;
-  const float *x32, *px32, *gy32, *wr32, *pwr32;
-  if ((r = f32_in(c, x, w.x32, nf, &x32, s))) return r;
-  if ((r = f32_in(c, px, w.px32, nf, &px32, s))) return r;
-  if ((r = f32_in(c, gy, w.gy32, nf, &gy32, s))) return r;
-  if ((r = f32_in(c, w_rad, w.w_rad32, rf, &wr32, s))) return r;
-  if ((r = f32_in(c, pw_rad, w.pw_rad32, rf, &pwr32, s))) return r;
-  float* ggy_acc = f32_acc(c, ggy, w.ggy32);
-  float* gx2_acc = f32_acc(c, gx2, w.gx2_32);
-  float* gwr2_acc = f32_acc(c, gw_rad2, w.gw_rad2_32);
-  const bool want_w1 = !all_null(gw1_2, d.M + 1), want_w2 = !all_null(gw2_2, d.M + 1);
-  const Lin W1 = lin_of(w.W1), W2 = lin_of(w.W2), pW1 = lin_of(w.pW1), pW2 = lin_of(w.pW2);
+  return conv_bwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, saved, gy, gx, gpos, grbf, genv, gw_rad, gw1e, gw2e,
+                  gcoef, gedge, ws, ws_bytes, stream);
+}
 
-  if ((r = realify(c, 0, w1, w.W1, s)) || (r = realify(c, 1, w2, w.W2, s))) return r;
-  if (has_pw1 && (r = realify(c, 0, pw1, w.pW1, s))) return r;
-  if (has_pw2 && (r = realify(c, 1, pw2, w.pW2, s))) return r;
-  for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
-    GraphDev gc = gd;
-    gc.e0 = e0;
-    gc.e1 = e0 + ec < gd.E ? e0 + ec : gd.E;
-    const int n = (int)(gc.e1 - gc.e0);
-    const int acc = k > 0;
-    const float* rbf_c = rbf + (size_t)e0 * n_rbf;
-    const float* prbf_c = prbf ? prbf + (size_t)e0 * n_rbf : nullptr;
-    Primal pr;
-    if (recompute) {
-      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
-      pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
-    } else {
-      pr = saved_rows(c, saved, gd.E, e0);
-    }
-
-    // ---- tangent (dual) forward along (px, ppos, pedge, prbf, pW)
-    if (prbf_c) {
-      if ((r = radial(c, n, prbf_c, wr32, w.Sdot, s))) return r;
-    } else if ((r = fill(w.Sdot, (size_t)n * wS, s))) {
-      return r;
-    }
-    if (pwr32) {
-      if ((r = radial(c, n, rbf_c, pwr32, w.Sdot, s, 1))) return r;
-    }
-    SO2_HIP(launch_edge_dual(d, gc, x32, px32, pos, ppos, pedge, pr.S, w.Sdot, w.Tdot, w.omega, c.bf, s));
-    if ((r = run_lin(c, 0, false, w.Tdot, w.Udot, W1, n, 0, s))) return r;
-    if (has_pw1 && (r = run_lin(c, 0, false, pr.T, w.Udot, pW1, n, 1, s))) return r;
-    SO2_HIP(launch_gate_dual(d, n, pr.U, w.Udot, w.Zdot, c.bf, s));
-    if ((r = run_lin(c, 1, false, w.Zdot, w.Vdot, W2, n, 0, s))) return r;
-    if (has_pw2 && (r = run_lin(c, 1, false, pr.Z, w.Vdot, pW2, n, 1, s))) return r;
-    // dL/dgy = the forward's directional derivative (Eq.(5))
-    if (ggy_acc) SO2_HIP(launch_node_dual(d, gc, pos, w.omega, pr.V, w.Vdot, env, penv, ggy_acc, acc, s));
-
-    // ---- reverse of the tangent output with cotangent gy
-    SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, pr.V, w.Vdot, env, penv,
-                                 gpos2 ? w.p2e : nullptr, genv2, s));
-    // [Zdot_bar; Zbar] = G2 W2^T (2n stacked rows)
-    if ((r = run_lin(c, 1, true, w.G2, w.ZZ, W2, 2 * n, 0, s))) return r;
-    // Zbar += tbar pW2^T
-    if (has_pw2 && (r = run_lin(c, 1, true, w.G2, w.ZZ + (size_t)n * d.wZ(), pW2, n, 1, s))) return r;
-    if (want_w2) {
-      const void* in[2] = {w.Zdot, pr.Z};
-      const void* out[2] = {w.G2, offs(static_cast<const void*>(w.G2), (size_t)n * d.wZ(), c.es)};
-      const long rows[2] = {n, n};
-      if ((r = run_lin_grad(c, 1, in, out, rows, 2, w.gW2r, acc, w.P, s))) return r;
-    }
-    SO2_HIP(launch_gate_dbwd(d, n, pr.U, w.Udot, w.ZZ, w.UU, c.bf, s));   // [Udot_bar; Ubar]
-    // [Tdot_bar; Tbar] = UU W1^T
-    if ((r = run_lin(c, 0, true, w.UU, w.TT, W1, 2 * n, 0, s))) return r;
-    // Tbar += Udot_bar pW1^T
-    if (has_pw1 && (r = run_lin(c, 0, true, w.UU, w.TT + (size_t)n * d.wT(), pW1, n, 1, s))) return r;
-    if (want_w1) {
-      const void* in[2] = {w.Tdot, pr.T};
-      const void* out[2] = {w.UU, offs(static_cast<const void*>(w.UU), (size_t)n * d.wU(), c.es)};
-      const long rows[2] = {n, n};
-      if ((r = run_lin_grad(c, 0, in, out, rows, 2, w.gW1r, acc, w.P, s))) return r;
-    }
-    SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, w.TT, gx2_acc, w.Sbar, w.Sdb,
-                                 gpos2 ? w.p2d : nullptr, gpos2 ? w.p2s : nullptr, acc, s));
-    if (gpos2) SO2_HIP(launch_pos2(gc, pos, ppos, pedge, w.omega, w.p2e, w.p2d, w.p2s, w.vbar2_all, s));
-    if (grbf2) {
-      float* out = grbf2 + (size_t)e0 * n_rbf;
-      std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, out, n_rbf, n, n_rbf, wS)};
-      if ((r = run_batch(ps, false, true, 0, s))) return r;
-      if (pwr32) {
-        std::vector<GemmProb> ps2{prob(w.Sdb, wS, pwr32, wS, out, n_rbf, n, n_rbf, wS, 1)};
-        if ((r = run_batch(ps2, false, true, 0, s))) return r;
-      }
-    }
-    if (gwr2_acc) {
-      TnSeg segs[2] = {{rbf_c, n_rbf, w.Sbar, wS, n}, {prbf_c, n_rbf, w.Sdb, wS, prbf_c ? n : 0}};
-      if ((r = run_tn(segs, 2, n_rbf, wS, gwr2_acc, wS, acc, w.P, 0, s))) return r;
-    }
+int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
+                 const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
+                 const void* const* w2e, const float* coef, const void* saved, const void* gy, const void* px,
+                 const float* ppos, const float* pedge, const float* prbf, const float* penv, const void* pw_rad,
+                 const void* const* pw1e, const void* const* pw2e, const float* pcoef, void* ggy, void* gx2,
+                 float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1e_2, void* const* gw2e_2,
+                 float* gcoef2, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Ctx c;
+  GraphDev gd;
+  MixIn mx;
+  int r;
+  if ((r = check_mole_call(cfg, g, mole, coef, &c, &gd, &mx))) return r;
+  if (gd.E == 0) {
+    if ((r = check_weights(c.d, w_rad, w1e, w2e))) return r;
+    hipStream_t s = (hipStream_t)stream;
+    if ((r = zero_grads(c, gd.N, gx2, gpos2, gw_rad2, nullptr, nullptr, s))) return r;
+    if (ggy && (r = zero(c, ggy, (size_t)gd.N * c.node_floats(), s))) return r;
+    return zero_mole_grads(c, gw1e_2, gw2e_2, gcoef2, s);
   }
-  if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r, gw2_2, c.bf, s));
-  if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r, gw1_2, c.bf, s));
-  if (gpos2) SO2_HIP(launch_node_pos(gd, w.vbar2_all, gpos2, s));
-  if ((r = f32_out(c, ggy_acc, ggy, nf, s))) return r;
-  if ((r = f32_out(c, gx2_acc, gx2, nf, s))) return r;
-  return f32_out(c, gwr2_acc, gw_rad2, rf, s);
+  return conv_dbwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, saved, gy, px, ppos, pedge, prbf, penv, pw_rad,
+                   pw1e, pw2e, pcoef, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2, ws, ws_bytes,
+                   stream);
 }
 
 // ---------------------------------------------------------------- spherical projection entry points

@@ -289,7 +289,8 @@ int realify_block(const void* w, int k, int h, int plain, void* out, hipStream_t
   return hipGetLastError();
 }
 
-int launch_realify(const Dims& d, int second, const void* const* w, void* wr, void* wrt, int bf16, hipStream_t s) {
+int launch_realify(const Dims& d, int second, const void* const* w, void* wr, void* wrt, int bf16, hipStream_t s,
+                   int in_f32) {
   for (int a = 0; a <= d.M; ++a) {
     int r, c;
     long off;
@@ -297,7 +298,11 @@ int launch_realify(const Dims& d, int second, const void* const* w, void* wr, vo
     const int plain = a == 0;
     const int k = plain ? r : r / 2, h = plain ? c : c / 2;
     int e;
-    if (!bf16) {
+    if (bf16 && in_f32) {
+      e = realify_block<float, bf16s, false>(w[a], k, h, plain, static_cast<bf16s*>(wr) + off, s);
+      if (e == hipSuccess && wrt)
+        e = realify_block<float, bf16s, true>(w[a], k, h, plain, static_cast<bf16s*>(wrt) + off, s);
+    } else if (!bf16) {
       if (plain) {
         e = hipMemcpyAsync(static_cast<float*>(wr) + off, w[0], sizeof(float) * (size_t)r * c,
                            hipMemcpyDeviceToDevice, s);

@@ -87,9 +87,11 @@ int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const
 
 // ---- weights
 // Wr (realified per order): block 0 = W[0]; block m = [[W_m0, W_m1], [-W_m1, W_m0]].
-// float32: w and wr float. bfloat16: w bfloat16; wr holds every block
-// bfloat16 and wrt (if not null) every block transposed ([cols][rows]).
-int launch_realify(const Dims& d, int second, const void* const* w, void* wr, void* wrt, int bf16, hipStream_t s);
+// float32: w and wr float. bfloat16: w bfloat16 (float32 with in_f32); wr
+// holds every block bfloat16 and wrt (if not null) every block transposed
+// ([cols][rows]).
+int launch_realify(const Dims& d, int second, const void* const* w, void* wr, void* wrt, int bf16, hipStream_t s,
+                   int in_f32 = 0);
 // fold the realified float32 gradient back: gW_m0 = G00 + G11, gW_m1 = G01 - G10 (m >= 1),
 // gW_0 = G_0; gw blocks float32 or bfloat16
 int launch_fold_grad(const Dims& d, int second, const float* gr, void* const* gw, int bf16, hipStream_t s);

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "so2conv.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(so2(?:conv|grid)_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(so2(?:conv|grid|mole)_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_entry_points():
@@ -61,3 +61,33 @@ def test_host_side_dtype_and_flag_checks():
     assert K.lib().so2conv_saved_bytes(ctypes.byref(bad), 8) == 0
     odd = Cfg(4, 2, 128, 64, 7, 0)       # unknown dtype
     assert K.lib().so2conv_saved_bytes(ctypes.byref(odd), 8) == 0
+
+
+def test_mixture_host_checks():
+    """Mixture arguments are checked on the host before any device work: the
+    workspace query returns 0 and the entry points return SO2_EINVAL /
+    SO2_EUNSUPPORTED with a message (graph pointers are never dereferenced)."""
+    import ctypes
+
+    import numpy as np
+
+    import so_graph_convolution_amd as K
+    from so_graph_convolution_amd._binding import GraphC, MoleCfg
+    cfg = K.SO2Config(4, 2, 128, 64)
+    good = K.Mixture(64, [0, 400, 400, 1000])
+    plain = K.so2conv_workspace_bytes(cfg, 100, 1000, 1)
+    assert K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1) > plain
+    assert K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1, 256) < K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1)
+    assert K.so2mole_workspace_bytes(cfg, K.Mixture(64, [0, 500, 400, 1000]), 100, 1000, 1) == 0   # decreasing
+    assert K.so2mole_workspace_bytes(cfg, K.Mixture(64, [0, 400, 999]), 100, 1000, 1) == 0        # wrong end
+    assert K.so2mole_workspace_bytes(cfg, K.Mixture(6, [0, 1000]), 100, 1000, 1) == 0             # K % 4
+    c = cfg.c()
+    fake = 0x1000
+    g = GraphC(100, 1000, fake, fake, None, fake, fake, fake)
+    bad_ptr = np.array([0, 700, 600, 1000], dtype=np.int64)
+    m = MoleCfg(3, 64, bad_ptr.ctypes.data)
+    r = K.lib().so2mole_fwd(ctypes.byref(c), ctypes.byref(g), ctypes.byref(m), *([None] * 11), 0, None)
+    assert r == -1 and b"non-decreasing" in K.lib().so2conv_last_error()
+    m = MoleCfg(3, 10, np.array([0, 100, 200, 1000], dtype=np.int64).ctypes.data)
+    r = K.lib().so2mole_bwd(ctypes.byref(c), ctypes.byref(g), ctypes.byref(m), *([None] * 20), 0, None)
+    assert r == -2 and b"n_experts" in K.lib().so2conv_last_error()
