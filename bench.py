@@ -90,6 +90,32 @@ def cpu_baseline(d, n_edges_sample, seed=0):
                       f"(PyTorch CPU, autograd), {dt:.1f} s"}
 
 
+def cpu_baseline_mole(d, m, n_edges_sample):
+    """Time the float64 mixture oracle (fwd, bwd, dbwd) on a leading block of
+    edges (the systems' edge ranges clipped to it)."""
+    import numpy as np
+    import torch
+    from oracle import mole_oracle as MO
+    from oracle import so2conv_oracle as O
+    cores = min(16, len(os.sched_getaffinity(0)))
+    torch.set_num_threads(cores)
+    base = O.to_oracle_inputs(d)
+    E = len(d["src"])
+    n = min(n_edges_sample, E)
+    sp = np.minimum(m["sys_edge_ptr"], n).tolist()
+    t = lambda a: torch.tensor(np.asarray(a), dtype=torch.float64)  # noqa: E731
+    w1e, w2e, coef, gy = [t(w) for w in m["w1e"]], [t(w) for w in m["w2e"]], t(m["coef"]), t(d["gy"])
+    t0 = time.perf_counter()
+    MO.forward(base, w1e, w2e, coef, sp, chunk=2048)
+    MO.backward(base, w1e, w2e, coef, sp, gy, chunk=2048)
+    MO.double_backward(base, w1e, w2e, coef, sp, gy, px=t(d["px"]), ppos=t(d["ppos"]), prbf=t(d["prbf"]),
+                       chunk=2048)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "edges/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {E} edges of the same workload, fwd+bwd+dbwd in float64 "
+                      f"(PyTorch CPU, autograd, mixture oracle), {dt:.1f} s"}
+
+
 def bench_grid(args):
     """Node-to-node spherical projection (U = sum_l G_l X^(l) W_l A; Appendix B.4) at
     EquiformerV3's widths (lmax 4, C 128, FFN hidden 512) on the medium system's
@@ -170,8 +196,11 @@ def main():
                     help="array dtype (default: the workload's own: f32 for M, bf16 for H and X)")
     ap.add_argument("--pos2", action="store_true",
                     help="the double backward also returns position derivatives (gpos2)")
-    ap.add_argument("--op", choices=("conv", "grid"), default="conv",
-                    help="conv: the SO(2) convolution step (default); grid: the node-to-node spherical projection")
+    ap.add_argument("--op", choices=("conv", "grid", "mole"), default="conv",
+                    help="conv: the SO(2) convolution step (default); grid: the node-to-node spherical projection; "
+                         "mole: the convolution with a system-dependent mixture of linear experts")
+    ap.add_argument("--systems", type=int, default=16, help="systems of the batch (--op mole)")
+    ap.add_argument("--experts", type=int, default=64, help="linear experts (--op mole; 64 for UMA)")
     ap.add_argument("--envelope", action="store_true",
                     help="per-edge cutoff envelope on the messages (with genv, and genv2 in the double backward)")
     ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
@@ -224,13 +253,26 @@ def main():
     w1, w2 = [t(w, ft) for w in d["w1"]], [t(w, ft) for w in d["w2"]]
     gy, px, ppos, prbf = t(d["gy"], ft), t(d["px"], ft), t(d["ppos"]), t(d["prbf"])
     env = t(so2_synth.cosine_envelope(d)) if args.envelope else None
+    mole = args.op == "mole"
+    if mole:   # the node range split into `systems` structures, each with its own coefficients
+        mix_in = so2_synth.mixture_inputs(d, args.systems, args.experts, seed=0, bf16=dtype == "bf16")
+        mix = K.Mixture(args.experts, mix_in["sys_edge_ptr"])
+        w1e, w2e = [t(w, ft) for w in mix_in["w1e"]], [t(w, ft) for w in mix_in["w2e"]]
+        coef = t(mix_in["coef"])
+        progress(f"mixture: {args.systems} systems, {args.experts} experts")
     db_need = ("gy", "x", "rbf", "w_rad", "w1", "w2") + (("pos",) if args.pos2 else ()) + \
         (("env",) if args.envelope else ())
     saved_b = K.so2conv_saved_bytes(kc, E)
-    ws_b = max(K.so2conv_workspace_bytes(kc, N, E, s) for s in (0, 1, 2))
+    if mole:
+        ws_b = max(K.so2mole_workspace_bytes(kc, mix, N, E, s, 0) for s in (0, 1, 2))
+    else:
+        ws_b = max(K.so2conv_workspace_bytes(kc, N, E, s) for s in (0, 1, 2))
     chunked = saved_b + ws_b > 200 * 2**30
     if chunked:   # workspace for chunks of about 256k edges (the library picks the chunk from its size)
-        ws_b = max(K.so2conv_chunked_workspace_bytes(kc, N, E, s, 262144) for s in (0, 1, 2))
+        if mole:
+            ws_b = max(K.so2mole_workspace_bytes(kc, mix, N, E, s, 262144) for s in (0, 1, 2))
+        else:
+            ws_b = max(K.so2conv_chunked_workspace_bytes(kc, N, E, s, 262144) for s in (0, 1, 2))
     progress(f"saved state {saved_b / 2**30:.1f} GiB, workspace {ws_b / 2**30:.1f} GiB"
              + (" (edge chunks)" if chunked else ""))
     saved = torch.empty(saved_b, dtype=torch.uint8, device=dev)
@@ -238,14 +280,24 @@ def main():
     args_c = (kc, g, x, pos, rbf, w_rad, w1, w2)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    args_m = (kc, g, mix, x, pos, rbf, w_rad, w1e, w2e, coef) if mole else None
+
     def step(times=None):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record()
-        K.so2conv_fwd(*args_c, saved=saved, ws=ws, env=env)
-        e1.record()
-        K.so2conv_bwd(*args_c, saved, gy, ws=ws, env=env)
-        e2.record()
-        K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env, need=db_need)
+        if mole:
+            K.so2mole_fwd(*args_m, saved=saved, ws=ws, env=env)
+            e1.record()
+            K.so2mole_bwd(*args_m, saved, gy, ws=ws, env=env)
+            e2.record()
+            K.so2mole_dbwd(*args_m, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env,
+                           need=db_need + ("coef",))
+        else:
+            K.so2conv_fwd(*args_c, saved=saved, ws=ws, env=env)
+            e1.record()
+            K.so2conv_bwd(*args_c, saved, gy, ws=ws, env=env)
+            e2.record()
+            K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env, need=db_need)
         e3.record()
         if times is not None:
             times.append((e0, e1, e2, e3))
@@ -296,10 +348,11 @@ def main():
         "config": {"workload": f"{WORKLOADS.get(cfg.name, cfg.name)} ({cfg.name})", "n_atoms": N,
                    "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
                    "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)"
-                   + (", dbwd with gpos2" if args.pos2 else "") + (", cutoff envelope" if args.envelope else ""),
+                   + (", dbwd with gpos2" if args.pos2 else "") + (", cutoff envelope" if args.envelope else "")
+                   + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else ""),
                    "edge_chunks": chunked},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": measured_gemm_traffic(args.config, dtype),
+                     "frac": achieved / peak, "traffic": None if mole else measured_gemm_traffic(args.config, dtype),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
                      "kernel": kname,
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
@@ -310,7 +363,8 @@ def main():
     }
     progress(f"timed {args.steps} steps: {ms_step:.1f} ms/step")
     if args.cpu_edges > 0:
-        out["cpu_baseline"] = cpu_baseline(d, args.cpu_edges)
+        out["cpu_baseline"] = cpu_baseline_mole(d, mix_in, args.cpu_edges) if mole else \
+            cpu_baseline(d, args.cpu_edges)
     print(json.dumps(out), flush=True)
 
 

@@ -198,8 +198,10 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
  * sys_edge_ptr is a HOST array [S+1] with p[0] = 0, p[S] = n_edges,
  * non-decreasing (empty systems allowed); n_systems in [1, 65536]; n_experts a
  * multiple of 4 in [4, 1024]; errors SO2_EINVAL / SO2_EUNSUPPORTED otherwise.
- * Workspace: so2mole_workspace_bytes(stage, chunk_edges) for chunks of
- * chunk_edges edges (0: all edges in one chunk), valid with or without `saved`. */
+ * Workspace: so2mole_workspace_bytes(stage, chunk_edges): chunk_edges = 0
+ * sizes one chunk over all edges that uses `saved` (as so2conv_workspace_bytes);
+ * chunk_edges > 0 sizes chunks of that many edges that recompute the forward
+ * state when `saved` is NULL (as so2conv_chunked_workspace_bytes). */
 typedef struct {
   int32_t n_systems;
   int32_t n_experts;

@@ -332,10 +332,14 @@ size_t max_grad_block(const Ctx& c) {
   return mx;
 }
 
+// split-K partials of one order's weight-gradient launch: nseg segments of up
+// to ec rows, cut at system borders (each system's rows split on their own,
+// at most ceil(rows / 4096) + 1 splits each)
 float* take_partials(Arena& ar, const Ctx& c, long ec, int nseg) {
   int sp, ch;
   split_plan(ec, &sp, &ch);
-  return ar.take((size_t)nseg * (sp + 1) * max_grad_block(c));
+  const long bound = std::max<long>(sp, (ec + 4095) / 4096) + 1 + (c.ns > 1 ? c.ns : 0);
+  return ar.take((size_t)nseg * bound * max_grad_block(c));
 }
 
 struct Primal {
@@ -713,29 +717,51 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
 
 // weight gradient of linear `second` per system (realified, float32) over the
 // chunk of n edges at e0: G[s]_a (+)= sum_q In_q[:, in a]^T Out_q[:, out a] on
-// the system's rows. A system's first chunk overwrites its gradient unless
-// `zeroed` (then every chunk accumulates into gradients cleared beforehand).
+// the system's rows. One launch per order covers every system (each split
+// over its own rows into its own partials), then one fixed-order reduction
+// per system. A system's first chunk overwrites its gradient unless `zeroed`
+// (then every chunk accumulates into gradients cleared beforehand).
 int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* const* out, int nseg, int n,
                  const WSet& w, long e0, const std::vector<float*>& G, bool zeroed, float* P, hipStream_t s) {
   const Dims& d = c.d;
   const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
-  for (size_t sy = 0; sy < w.W.size(); ++sy) {
-    const long lo = std::max(w.e[sy], e0), hi = std::min(w.e[sy + 1], e0 + n);
-    if (hi <= lo) continue;
-    const int acc = zeroed || lo != w.e[sy];
-    for (int a = 0; a <= d.M; ++a) {
-      int r, cc;
-      long off;
-      realified_shape(d, second, a, &r, &cc, &off);
-      const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
-      const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
-      TnSeg segs[2];
-      for (int q = 0; q < nseg; ++q)
-        segs[q] = {offs(in[q], (size_t)(lo - e0) * win + ib, c.es), win,
-                   offs(out[q], (size_t)(lo - e0) * wout + ob, c.es), wout, hi - lo};
-      int rr = run_tn(segs, nseg, r, cc, G[sy] + off, cc, acc, P, c.bf, s);
-      if (rr) return rr;
+  struct Red {
+    size_t sy, poff;
+    int splits, acc;
+  };
+  for (int a = 0; a <= d.M; ++a) {
+    int r, cc;
+    long off;
+    realified_shape(d, second, a, &r, &cc, &off);
+    const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
+    const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+    std::vector<GemmProb> ps;
+    std::vector<Red> red;
+    size_t poff = 0;
+    for (size_t sy = 0; sy < w.W.size(); ++sy) {
+      const long lo = std::max(w.e[sy], e0), hi = std::min(w.e[sy + 1], e0 + n);
+      if (hi <= lo) continue;
+      Red rd{sy, poff, 0, zeroed || lo != w.e[sy]};
+      for (int q = 0; q < nseg; ++q) {
+        int sp, ch;
+        split_plan(hi - lo, &sp, &ch);
+        GemmProb p = prob(offs(in[q], (size_t)(lo - e0) * win + ib, c.es), win,
+                          offs(out[q], (size_t)(lo - e0) * wout + ob, c.es), wout, P + poff, cc, r, cc,
+                          (int)(hi - lo));
+        p.k_splits = sp;
+        p.k_chunk = ch;
+        p.partial = 1;
+        ps.push_back(p);
+        poff += (size_t)sp * r * cc;
+        rd.splits += sp;
+      }
+      red.push_back(rd);
     }
+    if (ps.empty()) continue;
+    int rr = run_batch(ps, true, false, c.bf, s);
+    if (rr) return rr;
+    for (const Red& rd : red)
+      SO2_HIP(gemm_reduce(P + rd.poff, rd.splits, r, cc, G[rd.sy] + off, cc, rd.acc, s));
   }
   return SO2_OK;
 }
@@ -1604,7 +1630,8 @@ size_t so2mole_workspace_bytes(const so2conv_cfg* cfg, const so2mole_cfg* mole, 
   MixIn mx;
   if (check_cfg(cfg, &c0) || stage < 0 || stage > 2 || n_nodes < 0 || n_edges < 0 || chunk_edges < 0) return 0;
   if (check_mole(c0, mole, n_edges, &c, &mx)) return 0;
-  const long ec = chunk_edges == 0 || chunk_edges > n_edges ? n_edges : chunk_edges;
+  if (chunk_edges == 0) return ws_need(c, n_nodes, n_edges, n_edges, stage, false);
+  const long ec = chunk_edges > n_edges ? n_edges : chunk_edges;
   return ws_need(c, n_nodes, n_edges, ec, stage, true);
 }
 

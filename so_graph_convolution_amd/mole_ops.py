@@ -39,10 +39,15 @@ def so2mole_workspace_bytes(cfg: SO2Config, mix: Mixture, n_nodes, n_edges, stag
                                              int(chunk_edges or 0)))
 
 
-def _ws_for(cfg, mix, g, stage, ws, chunk_edges, device):
+def _ws_for(cfg, mix, g, stage, saved, ws, chunk_edges, device):
+    """One chunk over all edges using `saved`, else chunks of chunk_edges (all
+    edges by default) that recompute the forward state."""
     if ws is not None:
         return ws
-    return _ws(so2mole_workspace_bytes(cfg, mix, g.n_nodes, g.n_edges, stage, chunk_edges or 0), device)
+    if saved is not None and chunk_edges is None:
+        return _ws(so2mole_workspace_bytes(cfg, mix, g.n_nodes, g.n_edges, stage, 0), device)
+    ce = max(1, g.n_edges if chunk_edges is None else int(chunk_edges))
+    return _ws(so2mole_workspace_bytes(cfg, mix, g.n_nodes, g.n_edges, stage, ce), device)
 
 
 def _experts(cfg, mix, w1e, w2e, name1="w1e", name2="w2e"):
@@ -63,7 +68,7 @@ def so2mole_fwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e,
     y = torch.empty_like(x)
     if saved is True:
         saved = _ws(so2conv_saved_bytes(cfg, g.n_edges), x.device)
-    ws = _ws_for(cfg, mix, g, 0, ws, chunk_edges, x.device)
+    ws = _ws_for(cfg, mix, g, 0, saved, ws, chunk_edges, x.device)
     c, gc, m = cfg.c(), g.c(), mix.c()
     check(lib().so2mole_fwd(ctypes.byref(c), ctypes.byref(gc), ctypes.byref(m), _p(x), _p(pos), _p(rbf), _p(env),
                             _p(w_rad), p1, p2, _p(coef), _p(y), _p(saved), _p(ws), ws.numel(), _stream()),
@@ -92,7 +97,7 @@ def so2mole_bwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e,
     out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
     out["genv"] = torch.empty(g.n_edges, device=dev) if ("env" in need and env is not None) else None
     q1, q2, keep2 = _experts(cfg, mix, out["gw1e"], out["gw2e"], "gw1e", "gw2e")
-    ws = _ws_for(cfg, mix, g, 1, ws, chunk_edges, dev)
+    ws = _ws_for(cfg, mix, g, 1, saved, ws, chunk_edges, dev)
     c, gc, m = cfg.c(), g.c(), mix.c()
     check(lib().so2mole_bwd(ctypes.byref(c), ctypes.byref(gc), ctypes.byref(m), _p(x), _p(pos), _p(rbf), _p(env),
                             _p(w_rad), p1, p2, _p(coef), _p(saved), _p(gy), _p(out["gx"]), _p(out["gpos"]),
@@ -128,7 +133,7 @@ def so2mole_dbwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e
     out["gw2e_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     out["gcoef2"] = torch.empty_like(coef) if "coef" in need else None
     q1, q2, keep3 = _experts(cfg, mix, out["gw1e_2"], out["gw2e_2"], "gw1e_2", "gw2e_2")
-    ws = _ws_for(cfg, mix, g, 2, ws, chunk_edges, dev)
+    ws = _ws_for(cfg, mix, g, 2, saved, ws, chunk_edges, dev)
     c, gc, m = cfg.c(), g.c(), mix.c()
     check(lib().so2mole_dbwd(ctypes.byref(c), ctypes.byref(gc), ctypes.byref(m), _p(x), _p(pos), _p(rbf), _p(env),
                              _p(w_rad), p1, p2, _p(coef), _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf),

@@ -77,7 +77,8 @@ def test_mixture_host_checks():
     good = K.Mixture(64, [0, 400, 400, 1000])
     plain = K.so2conv_workspace_bytes(cfg, 100, 1000, 1)
     assert K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1) > plain
-    assert K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1, 256) < K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1)
+    assert K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1, 256) < K.so2mole_workspace_bytes(cfg, good, 100, 1000, 1,
+                                                                                              1000)
     assert K.so2mole_workspace_bytes(cfg, K.Mixture(64, [0, 500, 400, 1000]), 100, 1000, 1) == 0   # decreasing
     assert K.so2mole_workspace_bytes(cfg, K.Mixture(64, [0, 400, 999]), 100, 1000, 1) == 0        # wrong end
     assert K.so2mole_workspace_bytes(cfg, K.Mixture(6, [0, 1000]), 100, 1000, 1) == 0             # K % 4
