@@ -53,13 +53,14 @@ def gemm_flops_per_edge(L, M, C):
 def measured_gemm_traffic(config, dtype):
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters (copy-calibrated) of the medium float32 step, or None for another
-    workload or if the GEMM source changed since."""
+    workload or if the GEMM source (gemm.hip, gemm.hpp) changed since."""
     import hashlib
     if config != "M" or dtype != "f32":
         return None
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "gemm_hbm_traffic_medium.json")))
-        src = open(os.path.join(ROOT, "so_graph_convolution_amd", "csrc", "gemm.hip"), "rb").read()
+        csrc = os.path.join(ROOT, "so_graph_convolution_amd", "csrc")
+        src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("gemm.hip", "gemm.hpp"))
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
