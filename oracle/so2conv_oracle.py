@@ -163,10 +163,12 @@ def _rot_z(psi: torch.Tensor) -> torch.Tensor:
 
 # ----------------------------------------------------------------------------- inputs
 class OracleInputs:
-    """float64 torch views of one workload (indices stay int64). `env` ([E] or
-    None) is the optional per-edge cutoff envelope that scales each message
-    before the receiver sum (TrimSO(2) page, Appendix C.1 Implementation: eSEN
-    and UMA sum messages with their cutoff envelopes)."""
+    """float64 torch views of one workload (indices stay int64). `env` (None,
+    [E] or [E, H]) weights each message before the receiver sum (TrimSO(2)
+    page, Appendix C.1 Implementation: eSEN and UMA sum messages with their
+    cutoff envelopes, one weight per edge; EquiformerV3 applies attention
+    weights before aggregation, one weight per edge and head, head h covering
+    channels [h C/H, (h+1) C/H))."""
 
     def __init__(self, lmax, mmax, channels, pos, x, src, dst, shift, rbf, w_rad, w1, w2, env=None):
         self.L, self.M, self.C = lmax, mmax, channels
@@ -295,9 +297,13 @@ def _scatter(inp: OracleInputs, e_idx, msgs, n_nodes):
     d = (inp.L + 1) ** 2
     y = torch.zeros(n_nodes, d, inp.C, dtype=DT)
     dst = inp.dst[e_idx]
+    w = None
+    if inp.env is not None:
+        w = inp.env[e_idx]
+        w = w[:, None] if w.dim() == 1 else w.repeat_interleave(inp.C // w.shape[1], dim=1)   # [E', C]
     for l, msg in enumerate(msgs):
-        if inp.env is not None:
-            msg = msg * inp.env[e_idx][:, None, None]
+        if w is not None:
+            msg = msg * w[:, None, :]
         y[:, l * l:(l + 1) * (l + 1), :] = y[:, l * l:(l + 1) * (l + 1), :].index_add(0, dst, msg)
     return y
 
