@@ -17,11 +17,15 @@
  *   Node features x, y, gx, gy, px, ggy, gx2: [N, d, C] of the call's dtype.
  *   pos, gpos, ppos: [N, 3] float32.  shift, gedge, pedge: [E, 3] float32.
  *   rbf, grbf, prbf: [E, n_rbf] float32 (n_rbf a multiple of 4).
- *   env, genv, penv, genv2: [E] float32, the optional per-edge cutoff envelope
- *   (Appendix C.1: eSEN and UMA sum messages with their cutoff envelopes):
- *   y_i = sum_{e -> i} env_e (J D_e)^T t_e. NULL env = no envelope (then genv,
- *   penv and genv2 must be NULL). Like rbf it is an input: its dependence on
- *   positions is the caller's chain rule through genv / genv2.
+ *   env, genv, penv, genv2: [E, H] float32 (H = cfg->heads), optional weights
+ *   of each message before the receiver sum (Appendix C.1: eSEN and UMA sum
+ *   messages with their cutoff envelopes, H = 1; EquiformerV3 applies
+ *   attention weights before aggregation, one per head): channel c of the
+ *   message belongs to head c / (C / H), and
+ *   y_i[:, c] = sum_{e -> i} env[e, head(c)] ((J D_e)^T t_e)[:, c].
+ *   NULL env = no weights (then genv, penv and genv2 must be NULL). Like rbf
+ *   it is an input: its dependence on positions or on other features (an
+ *   attention softmax) is the caller's chain rule through genv / genv2.
  *   w_rad: [n_rbf, (L+1) * 2C], column (l, c_in), c_in < C: source channels.
  *   w1[0]: [(L+1)*2C, (L+1)*C + L*C]  rows (l, c_in); columns (l, c) then the
  *          gate columns (l = 1..L, c).
@@ -82,14 +86,16 @@ typedef enum { SO2_F32 = 0, SO2_BF16 = 1 } so2_dtype;
 enum {
   /* Validate the inputs on the device before any compute kernel: edge indices
    * in range, receivers non-decreasing, no zero-length edge, finite positions,
-   * shifts, rbf and envelope. The call then synchronises its stream and returns
+   * shifts, rbf and message weights. The call then synchronises its stream and returns
    * SO2_EDEVICE (message: the failed checks) instead of computing; the word of
    * the last checked call stays readable through so2conv_debug_status. */
   SO2_DEBUG_CHECKS = 2
 };
 
+/* heads: 0 or 1 = one weight per edge; H > 1 divides channels, C / H is 16,
+ * 32 or a multiple of 64, H <= 16 (else SO2_EUNSUPPORTED). */
 typedef struct {
-  int32_t lmax, mmax, channels, n_rbf, dtype, flags;
+  int32_t lmax, mmax, channels, n_rbf, dtype, flags, heads;
 } so2conv_cfg;
 
 typedef struct {

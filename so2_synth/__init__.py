@@ -323,3 +323,23 @@ def mixture_inputs(d: dict, n_systems: int, n_experts: int, seed: int = 0, empty
         w1e, w2e = [round_bf16(w) for w in w1e], [round_bf16(w) for w in w2e]
         pw1e, pw2e = [round_bf16(w) for w in pw1e], [round_bf16(w) for w in pw2e]
     return dict(sys_edge_ptr=sys_edge_ptr, w1e=w1e, w2e=w2e, coef=coef, pcoef=pcoef, pw1e=pw1e, pw2e=pw2e)
+
+
+def attention_weights(d: dict, heads: int, seed: int = 0) -> np.ndarray:
+    """Synthetic per-head attention weights [E, heads] (float32): standard
+    normal logits per (edge, head), normalised by a softmax over each
+    receiver's incoming edges (the weights EquiformerV3 applies before
+    aggregation, TrimSO(2) page Appendix C.1; how the model forms the logits
+    is outside the operator, they are an input here)."""
+    rng = np.random.default_rng(20_000 + seed)
+    dst = np.asarray(d["dst"])
+    E = len(dst)
+    logits = rng.normal(size=(E, heads))
+    out = np.zeros((E, heads))
+    if E:
+        starts = np.flatnonzero(np.r_[True, dst[1:] != dst[:-1]])
+        ends = np.r_[starts[1:], E]
+        for a, b in zip(starts, ends):
+            z = np.exp(logits[a:b] - logits[a:b].max(0))
+            out[a:b] = z / z.sum(0)
+    return out.astype(np.float32)

@@ -23,7 +23,7 @@ c_i64 = ctypes.c_int64
 
 class Cfg(ctypes.Structure):
     _fields_ = [("lmax", c_i32), ("mmax", c_i32), ("channels", c_i32), ("n_rbf", c_i32), ("dtype", c_i32),
-                ("flags", c_i32)]
+                ("flags", c_i32), ("heads", c_i32)]
 
 
 class GridCfg(ctypes.Structure):

@@ -114,10 +114,15 @@ int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
     return fail(SO2_EUNSUPPORTED, "n_rbf must be a multiple of 4 in [4, 1024]");
   if (cfg->dtype != SO2_F32 && cfg->dtype != SO2_BF16) return fail(SO2_EUNSUPPORTED, "dtype must be SO2_F32 or SO2_BF16");
   if (cfg->flags & ~SO2_DEBUG_CHECKS) return fail(SO2_EINVAL, "unknown cfg flags");
+  const int H = cfg->heads == 0 ? 1 : cfg->heads;
+  if (H < 1 || H > kMaxHeads || C % H) return fail(SO2_EUNSUPPORTED, "heads must divide channels, at most 16");
+  if (H > 1 && (C / H) % 64 && C / H != 16 && C / H != 32)
+    return fail(SO2_EUNSUPPORTED, "channels per head must be 16, 32 or a multiple of 64");
   c->debug = (cfg->flags & SO2_DEBUG_CHECKS) != 0;
   c->d.L = L;
   c->d.M = M;
   c->d.C = C;
+  c->d.H = H;
   c->n_rbf = cfg->n_rbf;
   c->bf = cfg->dtype == SO2_BF16;
   c->es = c->bf ? 2 : 4;
@@ -148,7 +153,7 @@ int check_graph(const so2conv_graph* g, GraphDev* gd) {
 __device__ unsigned g_debug_word;
 
 __global__ void validate_kernel(GraphDev g, const float* __restrict__ pos, const float* __restrict__ rbf, int n_rbf,
-                                const float* __restrict__ env) {
+                                const float* __restrict__ env, int heads) {
   unsigned bits = 0;
   for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.E; e += (long)gridDim.x * blockDim.x) {
     const int j = g.src[e], i = g.dst[e];
@@ -169,7 +174,9 @@ __global__ void validate_kernel(GraphDev g, const float* __restrict__ pos, const
     }
     for (int k = 0; k < n_rbf; ++k)
       if (!isfinite(rbf[(size_t)e * n_rbf + k])) bits |= 16u;
-    if (env && !isfinite(env[e])) bits |= 16u;
+    if (env)
+      for (int h = 0; h < heads; ++h)
+        if (!isfinite(env[e * heads + h])) bits |= 16u;
   }
   if (bits) atomicOr(&g_debug_word, bits);
 }
@@ -193,7 +200,7 @@ int debug_validate(const Ctx& c, const GraphDev& g, const float* pos, const floa
   if (g.E > 0) {
     long b = (g.E + 255) / 256;
     if (b > 4096) b = 4096;
-    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)b), dim3(256), 0, s, g, pos, rbf, c.n_rbf, env);
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)b), dim3(256), 0, s, g, pos, rbf, c.n_rbf, env, c.d.H);
     SO2_HIP(hipGetLastError());
   }
   SO2_HIP(hipStreamSynchronize(s));

@@ -36,8 +36,10 @@ constexpr int tile_edges() {
 __device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
 // ------------------------------------------------------------------ edge_bwd
-// With an envelope (env, per edge) the message is env_e V_e: tbar and the
-// torque scale by env_e, and genv_e = <V_e, R_e gy[dst]>.
+// With per-edge message weights (env [E, H]: a cutoff envelope, H = 1, or
+// attention weights per head, channel c in head c / (C / H)) the message is
+// env_{e,h(c)} V_e[:, c]: tbar and the torque scale per channel, and
+// genv_{e,h} = <V_e, R_e gy[dst]> over the channels of head h.
 template <int L, int M, typename OT>
 __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                        const float* __restrict__ gy, const float* __restrict__ V,
@@ -50,6 +52,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRL[TE * 3 * K];
   __shared__ float sRed[TE * 4 * 4];
+  __shared__ float sHead[TE * kMaxHeads];
   __shared__ int sDst[TE];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
@@ -64,6 +67,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
   rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
   __syncthreads();
+  const int H = d.H, head = c_head(d, threadIdx.x);
 
   const int C = d.C, wZ = d.wZ();
   const int c = threadIdx.x;
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   const bool act = c < C;
   for (int t = 0; t < ne; ++t) {
     const long e = e0 + t - g.e0;   // chunk-relative row
-    const float ev = env ? env[e0 + t] : 1.f;
+    const float ev = env ? env[(e0 + t) * H + head] : 1.f;
     float tk[4] = {0.f, 0.f, 0.f, 0.f};
     if (act) {
       float gv[D];
@@ -104,22 +108,25 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
 #pragma unroll
       for (int j = 0; j < Q; ++j) tk[3] += vv[j] * o[j];
     }
-    const int nr = genv ? 4 : 3;
-    for (int k = 0; k < nr; ++k) {
+    for (int k = 0; k < 3; ++k) {
       const float s = wave_sum(tk[k]);
       if (lane == 0) sRed[(t * 4 + wave) * 4 + k] = s;
     }
+    if (genv) head_partial(tk[3], d, c, t, sRed, 4, 3, sHead);
   }
   __syncthreads();
   const int nw = blockDim.x / 64;
-  for (int idx = threadIdx.x; idx < ne * 4; idx += blockDim.x) {
-    const int t = idx / 4, k = idx - t * 4;
-    if (k == 3 && !genv) continue;
+  for (int idx = threadIdx.x; idx < ne * 3; idx += blockDim.x) {
+    const int t = idx / 3, k = idx - t * 3;
     float s = 0.f;
     for (int w = 0; w < nw; ++w) s += sRed[(t * 4 + w) * 4 + k];
-    if (k < 3) tau[(e0 + t - g.e0) * 3 + k] = s;
-    else genv[e0 + t] = s;
+    tau[(e0 + t - g.e0) * 3 + k] = s;
   }
+  if (genv)
+    for (int idx = threadIdx.x; idx < ne * H; idx += blockDim.x) {
+      const int t = idx / H, h = idx - t * H;
+      genv[(e0 + t) * H + h] = head_total(d, t, h, sRed, 4, 3, sHead);
+    }
 }
 
 template <int L, int M>

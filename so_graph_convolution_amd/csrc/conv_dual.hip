@@ -188,8 +188,9 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
       for (int t = grp; t < ne; t += 2) {
         const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
         const float* vd = Vdot + (size_t)(t0 + t - g.e0) * wZ + c;
-        // message env V: tangent env (Rdot^T V + R^T Vdot) + penv R^T V
-        const float ev = env ? env[t0 + t] : 1.f, pv = penv ? penv[t0 + t] : 0.f;
+        // message env V (weights of c's head): tangent env (Rdot^T V + R^T Vdot) + penv R^T V
+        const size_t wi = (size_t)(t0 + t) * d.H + c / d.hs();
+        const float ev = env ? env[wi] : 1.f, pv = penv ? penv[wi] : 0.f;
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
           const int q = qhalf(l, M), n = 2 * l + 1;
@@ -233,7 +234,7 @@ struct NodeDual {
 //   p2[e][3 + k] = V^T (R G_k) gy                           (<Rdotbar, R G_k>)
 // With an envelope the tangent message is env (Rdot^T V + R^T Vdot) + penv R^T V:
 // G2 = [env R gy; env Rdot gy + penv R gy], the torque terms scale alike, and
-// genv2_e = <Rdot gy, V> + <R gy, Vdot>.
+// genv2_e = <Rdot gy, V> + <R gy, Vdot> (per head of channels with weights [E, H]).
 template <int L, int M, typename OT, bool P2>
 __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, const float* __restrict__ pos,
                                                             const float* __restrict__ omega,
@@ -252,6 +253,7 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   __shared__ float sW[TE * 3];
   __shared__ float sRL[P2 ? TE * 3 * K : 1], sRdL[P2 ? TE * 3 * K : 1];
   __shared__ float sRed[TE * 4 * 7];
+  __shared__ float sHead[TE * kMaxHeads];
   __shared__ int sDst[TE];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
@@ -275,9 +277,10 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   const int C = d.C, wZ = d.wZ();
   const int c = threadIdx.x, lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const bool act = c < C;
+  const int H = d.H, head = c_head(d, c);
   for (int t = 0; t < ne; ++t) {
     const long e = e0 + t - g.e0;   // chunk-relative row
-    const float ev = env ? env[e0 + t] : 1.f, pv = penv ? penv[e0 + t] : 0.f;
+    const float ev = env ? env[(e0 + t) * H + head] : 1.f, pv = penv ? penv[(e0 + t) * H + head] : 0.f;
     float tk[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (act) {
       float gv[D];
@@ -333,22 +336,23 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
         if (lane == 0) sRed[(t * 4 + wave) * 7 + k] = sum;
       }
     }
-    if (genv2) {
-      const float sum = wave_sum(tk[6]);
-      if (lane == 0) sRed[(t * 4 + wave) * 7 + 6] = sum;
-    }
+    if (genv2) head_partial(tk[6], d, c, t, sRed, 7, 6, sHead);
   }
   if (P2 || genv2) {
     __syncthreads();
     const int nw = blockDim.x / 64;
-    for (int idx = threadIdx.x; idx < ne * 7; idx += blockDim.x) {
-      const int t = idx / 7, k = idx - t * 7;
-      if ((k < 6 && !P2) || (k == 6 && !genv2)) continue;
-      float sum = 0.f;
-      for (int w = 0; w < nw; ++w) sum += sRed[(t * 4 + w) * 7 + k];
-      if (k < 6) p2[(e0 + t - g.e0) * 6 + k] = sum;
-      else genv2[e0 + t] = sum;
-    }
+    if (P2)
+      for (int idx = threadIdx.x; idx < ne * 6; idx += blockDim.x) {
+        const int t = idx / 6, k = idx - t * 6;
+        float sum = 0.f;
+        for (int w = 0; w < nw; ++w) sum += sRed[(t * 4 + w) * 7 + k];
+        p2[(e0 + t - g.e0) * 6 + k] = sum;
+      }
+    if (genv2)
+      for (int idx = threadIdx.x; idx < ne * H; idx += blockDim.x) {
+        const int t = idx / H, h = idx - t * H;
+        genv2[(e0 + t) * H + h] = head_total(d, t, h, sRed, 7, 6, sHead);
+      }
   }
 }
 

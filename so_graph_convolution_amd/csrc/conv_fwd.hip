@@ -122,7 +122,7 @@ __global__ __launch_bounds__(512) void node_fwd_kernel(Dims d, GraphDev g, const
     if (act) {
       for (int t = grp; t < ne; t += 2) {
         const float* vr = V + (size_t)(t0 + t - g.e0) * wZ + c;
-        const float ev = env ? env[t0 + t] : 1.f;   // cutoff envelope of the message
+        const float ev = env ? env[(size_t)(t0 + t) * d.H + c / d.hs()] : 1.f;   // message weight of c's head
         float tv[Q];
 #pragma unroll
         for (int l = 0; l <= L; ++l) {

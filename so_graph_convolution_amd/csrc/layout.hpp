@@ -57,9 +57,13 @@ __host__ __device__ constexpr inline int mm_col(int l, int m, int c, int L, int 
 __host__ __device__ constexpr inline int gen_off(int l) { return l == 0 ? 0 : gen_off(l - 1) + (2 * l - 1) * (2 * l - 1); }
 constexpr int kGenSize = gen_off(kMaxL + 1);   // 455 per generator
 
+constexpr int kMaxHeads = 16;   // heads of the per-edge message weights (C / heads >= 16)
+
 struct Dims {
   int L, M, C;
+  int H = 1;   // heads of the per-edge message weights: channel c belongs to head c / (C / H)
   __host__ __device__ int Ci() const { return 2 * C; }
+  __host__ __device__ int hs() const { return C / H; }                // channels per head
   __host__ __device__ int d() const { return (L + 1) * (L + 1); }
   __host__ __device__ int q() const { return q_count(L, M); }
   __host__ __device__ int K() const { return k_count(L, M); }

@@ -253,4 +253,40 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// sum over aligned groups of `width` lanes (a power of two <= 64), same
+// butterfly order in every group; every lane receives its group's sum
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// head of channel c (channels past C map to head 0; their values are unused)
+__device__ __forceinline__ int c_head(const Dims& d, int c) { return c < d.C ? c / d.hs() : 0; }
+
+// Per-head sums of the per-channel values of edge slot t (one thread per
+// channel c, lane/wave of a block of at most 4 waves): heads of hs = C / H
+// channels. Heads that are whole waves (or H = 1) take the wave sums through
+// red[(t * 4 + wave) * stride + k]; heads of 16 or 32 channels are summed
+// inside the wave into hsum[t * kMaxHeads + head].
+__device__ __forceinline__ void head_partial(float v, const Dims& d, int c, int t, float* red, int stride, int k,
+                                             float* hsum) {
+  const int hs = d.hs(), lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  if (d.H > 1 && hs < 64) {
+    const float s = group_sum(v, hs);
+    if (c < d.C && lane % hs == 0) hsum[t * kMaxHeads + c / hs] = s;
+  } else {
+    const float s = wave_sum(v);
+    if (lane == 0) red[(t * 4 + wave) * stride + k] = s;
+  }
+}
+// the head total written by head_partial (after a barrier)
+__device__ __forceinline__ float head_total(const Dims& d, int t, int h, const float* red, int stride, int k,
+                                            const float* hsum) {
+  const int hs = d.hs();
+  if (d.H > 1 && hs < 64) return hsum[t * kMaxHeads + h];
+  float s = 0.f;
+  for (int w = (h * hs) / 64; w < ((h + 1) * hs + 63) / 64; ++w) s += red[(t * 4 + w) * stride + k];
+  return s;
+}
+
 }  // namespace so2

@@ -95,7 +95,7 @@ def so2mole_bwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e,
     out["gw2e"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     out["gcoef"] = torch.empty_like(coef) if "coef" in need else None
     out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
-    out["genv"] = torch.empty(g.n_edges, device=dev) if ("env" in need and env is not None) else None
+    out["genv"] = torch.empty_like(env) if ("env" in need and env is not None) else None
     q1, q2, keep2 = _experts(cfg, mix, out["gw1e"], out["gw2e"], "gw1e", "gw2e")
     ws = _ws_for(cfg, mix, g, 1, saved, ws, chunk_edges, dev)
     c, gc, m = cfg.c(), g.c(), mix.c()
@@ -114,7 +114,7 @@ def so2mole_dbwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e
     dt = cfg.torch_dtype
     for t, n, shp, tdt in ((gy, "gy", x.shape, dt), (px, "px", x.shape, dt), (ppos, "ppos", pos.shape, torch.float32),
                            (pedge, "pedge", (g.n_edges, 3), torch.float32), (prbf, "prbf", rbf.shape, torch.float32),
-                           (pw_rad, "pw_rad", w_rad.shape, dt), (penv, "penv", (g.n_edges,), torch.float32),
+                           (pw_rad, "pw_rad", w_rad.shape, dt), (penv, "penv", cfg.env_shape(g.n_edges), torch.float32),
                            (coef, "coef", (mix.n_systems, mix.n_experts), torch.float32),
                            (pcoef, "pcoef", (mix.n_systems, mix.n_experts), torch.float32)):
         _dev(t, n, dtype=tdt, shape=shp)
@@ -126,7 +126,7 @@ def so2mole_dbwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e
     out["ggy"] = torch.empty_like(x) if "gy" in need else None
     out["gx2"] = torch.empty_like(x) if "x" in need else None
     out["gpos2"] = torch.empty_like(pos) if "pos" in need else None
-    out["genv2"] = torch.empty(g.n_edges, device=dev) if ("env" in need and env is not None) else None
+    out["genv2"] = torch.empty_like(env) if ("env" in need and env is not None) else None
     out["grbf2"] = torch.empty_like(rbf) if "rbf" in need else None
     out["gw_rad2"] = torch.empty_like(w_rad) if "w_rad" in need else None
     out["gw1e_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None

@@ -28,13 +28,16 @@ class SO2Config:
     their gradients bfloat16 (positions, shifts, rbf and their gradients stay
     float32); the per-order products run on bfloat16 matrix cores with float32
     accumulation. debug_checks: validate the inputs on the device before
-    computing (the call synchronises and raises on bad inputs)."""
+    computing (the call synchronises and raises on bad inputs). heads: the
+    per-edge message weights `env` are [E] (heads = 1: a cutoff envelope) or
+    [E, heads] (attention weights per head of channels/heads channels)."""
     lmax: int
     mmax: int
     channels: int
     n_rbf: int
     dtype: str = "f32"
     debug_checks: bool = False
+    heads: int = 1
 
     def __post_init__(self):
         if self.dtype not in _DTYPES:
@@ -42,7 +45,10 @@ class SO2Config:
 
     def c(self) -> Cfg:
         return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0],
-                   SO2_DEBUG_CHECKS if self.debug_checks else 0)
+                   SO2_DEBUG_CHECKS if self.debug_checks else 0, self.heads)
+
+    def env_shape(self, n_edges):
+        return (n_edges,) if self.heads == 1 else (n_edges, self.heads)
 
     @property
     def torch_dtype(self):
@@ -172,7 +178,7 @@ def _common(cfg, g, x, pos, rbf, w_rad, env=None):
     _dev(pos, "pos", shape=(N, 3))
     _dev(rbf, "rbf", shape=(E, cfg.n_rbf))
     _dev(w_rad, "w_rad", dtype=cfg.torch_dtype, shape=(cfg.n_rbf, (cfg.lmax + 1) * 2 * C))
-    _dev(env, "env", shape=(E,))
+    _dev(env, "env", shape=cfg.env_shape(E))
 
 
 def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None, ws=None, chunk_edges=None,
@@ -217,7 +223,7 @@ def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy,
     out["gw1"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None
     out["gw2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
-    out["genv"] = torch.empty(g.n_edges, device=dev) if ("env" in need and env is not None) else None
+    out["genv"] = torch.empty_like(env) if ("env" in need and env is not None) else None
     q1, k3 = _ptr_array(out["gw1"], "gw1", s1, dt)
     q2, k4 = _ptr_array(out["gw2"], "gw2", s2, dt)
     ws = _ws_for(cfg, g, 1, saved, ws, chunk_edges, dev)
@@ -238,7 +244,7 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     """Returns dict ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1_2, gw2_2 (requested ones;
     gpos2 only when "pos" is in need, genv2 when "env" is and an envelope is given)."""
     _common(cfg, g, x, pos, rbf, w_rad, env)
-    _dev(penv, "penv", shape=(g.n_edges,))
+    _dev(penv, "penv", shape=cfg.env_shape(g.n_edges))
     dt = cfg.torch_dtype
     _dev(gy, "gy", dtype=dt, shape=x.shape)
     _dev(px, "px", dtype=dt, shape=x.shape)
@@ -256,7 +262,7 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     out["ggy"] = torch.empty_like(x) if "gy" in need else None
     out["gx2"] = torch.empty_like(x) if "x" in need else None
     out["gpos2"] = torch.empty_like(pos) if "pos" in need else None
-    out["genv2"] = torch.empty(g.n_edges, device=dev) if ("env" in need and env is not None) else None
+    out["genv2"] = torch.empty_like(env) if ("env" in need and env is not None) else None
     out["grbf2"] = torch.empty_like(rbf) if "rbf" in need else None
     out["gw_rad2"] = torch.empty_like(w_rad) if "w_rad" in need else None
     out["gw1_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s1] if "w1" in need else None

@@ -1,7 +1,11 @@
-"""Per-edge cutoff envelope on the messages (y_i = sum env_e R_e^T t_e):
-forward, backward (incl. genv, gpos, gedge) and double backward (incl. a
-direction penv on the envelope, genv2 and gpos2) through the C ABI against
-the oracle; float32 and bf16, one chunk and 1024-edge chunks."""
+"""Per-edge cutoff envelope on the messages (y_i = sum env_e R_e^T t_e) and
+per-head attention weights (env [E, H], channel c weighted by its head's
+weight): forward, backward (incl. genv, gpos, gedge) and double backward
+(incl. a direction penv on the weights, genv2 and gpos2) through the C ABI
+against the oracle; float32 and bf16, one chunk and 1024-edge chunks; heads
+of 16 and 32 channels (summed inside a wave) and of one and two waves."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -21,21 +25,39 @@ CASES = [
                               min_dist=0.0), "f32", 1024),
     ("l3m2_c32_bf16", dict(n_atoms=40, box=8.0, rc=4.0, lmax=3, mmax=2, channels=32, n_rbf=8, seed=14), "bf16", None),
 ]
+HEAD_CASES = [
+    # name, workload overrides, dtype, chunk_edges, heads
+    ("l4m2_c128_h8", dict(n_atoms=100, box=11.0, rc=4.0, lmax=4, mmax=2, channels=128, n_rbf=16, seed=6,
+                          min_dist=0.0), "f32", None, 8),
+    ("l4m2_c128_h2_chunked", dict(n_atoms=100, box=11.0, rc=4.0, lmax=4, mmax=2, channels=128, n_rbf=16, seed=7,
+                                  min_dist=0.0), "f32", 1024, 2),
+    ("l2m2_c256_h2", dict(n_atoms=40, box=8.0, rc=4.0, lmax=2, mmax=2, channels=256, n_rbf=8, seed=15), "f32",
+     None, 2),
+    ("l3m2_c64_h2_bf16", dict(n_atoms=40, box=8.0, rc=4.0, lmax=3, mmax=2, channels=64, n_rbf=8, seed=14), "bf16",
+     None, 2),
+    ("l6m2_c96_h3", dict(n_atoms=48, box=9.0, rc=4.5, lmax=6, mmax=2, channels=96, n_rbf=8, seed=11), "f32", None, 3),
+]
 BW = {"gx": "gx", "gpos": "gpos", "grbf": "grbf", "genv": "genv", "gw_rad": "gw_rad", "gw1": "gw1", "gw2": "gw2",
       "gedge": "gedge"}
 DB = {"ggy": "ggy", "gx2": "gx", "gpos2": "gpos", "grbf2": "grbf", "genv2": "genv", "gw_rad2": "gw_rad",
       "gw1_2": "gw1", "gw2_2": "gw2"}
 
 
-@pytest.mark.parametrize("name,over,dtype,chunk", CASES, ids=[c[0] for c in CASES])
-def test_envelope_matches_oracle(name, over, dtype, chunk):
+@pytest.mark.parametrize("name,over,dtype,chunk,heads", [c + (1,) for c in CASES] + HEAD_CASES,
+                         ids=[c[0] for c in CASES] + [c[0] for c in HEAD_CASES])
+def test_envelope_matches_oracle(name, over, dtype, chunk, heads):
     import so_graph_convolution_amd as K
     d = dict(H.workload("T", dtype=dtype, **over))
     E = len(d["src"])
-    d["env"] = so2_synth.cosine_envelope(d)
-    penv = np.random.default_rng(41).normal(size=E).astype(np.float32)
-    H.note(f"[envelope] {name} E={E} dtype={dtype} chunks={chunk}")
+    if heads == 1:
+        d["env"] = so2_synth.cosine_envelope(d)
+        penv = np.random.default_rng(41).normal(size=E).astype(np.float32)
+    else:
+        d["env"] = (so2_synth.attention_weights(d, heads, seed=3) * so2_synth.cosine_envelope(d)[:, None])
+        penv = np.random.default_rng(41).normal(size=(E, heads)).astype(np.float32)
+    H.note(f"[envelope] {name} E={E} dtype={dtype} chunks={chunk} heads={heads}")
     dd = H.to_dev(d, dtype)
+    dd["kcfg"] = dataclasses.replace(dd["kcfg"], heads=heads)
     env = torch.tensor(d["env"], device="cuda")
     args = (dd["kcfg"], dd["g"], dd["x"], dd["pos"], dd["rbf"], dd["w_rad"], dd["w1"], dd["w2"])
     keep = chunk is None
