@@ -204,6 +204,8 @@ def main():
     ap.add_argument("--experts", type=int, default=64, help="linear experts (--op mole; 64 for UMA)")
     ap.add_argument("--envelope", action="store_true",
                     help="per-edge cutoff envelope on the messages (with genv, and genv2 in the double backward)")
+    ap.add_argument("--heads", type=int, default=1,
+                    help="per-head attention weights on the messages (EquiformerV3: 8 heads), times the envelope")
     ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
@@ -248,12 +250,17 @@ def main():
         return torch.tensor(np.ascontiguousarray(a), dtype=dt, device=dev)
 
     ft = torch.bfloat16 if dtype == "bf16" else torch.float32
-    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype)
+    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype, heads=args.heads)
     g = K.so2conv_graph_prepare(N, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
     x, pos, rbf, w_rad = t(d["x"], ft), t(d["pos"]), t(d["rbf"]), t(d["w_rad"], ft)
     w1, w2 = [t(w, ft) for w in d["w1"]], [t(w, ft) for w in d["w2"]]
     gy, px, ppos, prbf = t(d["gy"], ft), t(d["px"], ft), t(d["ppos"]), t(d["prbf"])
-    env = t(so2_synth.cosine_envelope(d)) if args.envelope else None
+    if args.heads > 1:
+        args.envelope = True
+        d["env"] = so2_synth.attention_weights(d, args.heads, seed=0) * so2_synth.cosine_envelope(d)[:, None]
+    elif args.envelope:
+        d["env"] = so2_synth.cosine_envelope(d)
+    env = t(d["env"]) if args.envelope else None
     mole = args.op == "mole"
     if mole:   # the node range split into `systems` structures, each with its own coefficients
         mix_in = so2_synth.mixture_inputs(d, args.systems, args.experts, seed=0, bf16=dtype == "bf16")
@@ -303,6 +310,7 @@ def main():
         if times is not None:
             times.append((e0, e1, e2, e3))
 
+    torch.cuda.reset_peak_memory_stats()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -349,7 +357,9 @@ def main():
         "config": {"workload": f"{WORKLOADS.get(cfg.name, cfg.name)} ({cfg.name})", "n_atoms": N,
                    "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
                    "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)"
-                   + (", dbwd with gpos2" if args.pos2 else "") + (", cutoff envelope" if args.envelope else "")
+                   + (", dbwd with gpos2" if args.pos2 else "")
+                   + (f", {args.heads}-head attention weights times the cutoff envelope" if args.heads > 1
+                      else (", cutoff envelope" if args.envelope else ""))
                    + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else ""),
                    "edge_chunks": chunked},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
@@ -360,6 +370,7 @@ def main():
                      "algorithmic_flops_per_step": gemm_fl / args.steps, "per_kind": per_kind},
         "stage_ms": {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean()), "dbwd": float(st[:, 2].mean())},
         "step_gemm_share": gemm_ms / args.steps / ms_step,
+        "peak_device_memory_GiB": torch.cuda.max_memory_allocated() / 2**30,
         "step_tflops_8F": 8 * F * E / (ms_step * 1e-3) / 1e12,
     }
     progress(f"timed {args.steps} steps: {ms_step:.1f} ms/step")
