@@ -327,7 +327,8 @@ def main():
     K.so2conv_profile_enable(False)
     n_l, gemm_ms, gemm_fl, gemm_by = K.so2conv_profile_read(-1)
     per_kind = {}
-    kinds = ((3, "ABt"), (4, "AtB")) if dtype == "bf16" else ((0, "AB"), (1, "ABt"), (2, "AtB"))
+    kinds = ((3, "ABt"), (4, "AtB")) if dtype == "bf16" else \
+        ((0, "AB"), (1, "ABt"), (2, "AtB"), (5, "AB complex"), (6, "ABt complex"), (7, "AtB complex"))
     for kind, name in kinds:
         n, ms, fl, by = K.so2conv_profile_read(kind)
         per_kind[name] = {"launches": n, "avg_ms": ms / max(n, 1), "tflops": fl / max(ms, 1e-9) / 1e9,
@@ -339,8 +340,9 @@ def main():
     F = gemm_flops_per_edge(cfg.lmax, cfg.mmax, cfg.channels)
     achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_BF16_MFMA_TFLOPS if dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    kname = ("gemm_bf16_kernel (bf16 MFMA" if dtype == "bf16" else "gemm_f32_kernel (fp32 MFMA") + \
-        " per-order linears), all launches of the timed steps"
+    kname = ("gemm_bf16_kernel (bf16 MFMA per-order linears)" if dtype == "bf16" else
+             "gemm_f32_kernel (order 0) and gemm_cplx_kernel (orders >= 1, three real products per complex "
+             "one; fp32 MFMA)") + ", all launches of the timed steps"
     out = {
         "metric": METRIC,
         "value": value,

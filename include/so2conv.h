@@ -266,7 +266,9 @@ int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const 
  * synchronises on the recorded events and returns the number of launches, the
  * summed event time (ms), flops and bytes for kind 0 (A B), 1 (A B^T),
  * 2 (A^T B, weight gradients) with float32 operands, 3 (A B^T) and 4 (A^T B)
- * with bfloat16 operands, or -1 (all). Host-side state, process-wide. */
+ * with bfloat16 operands, 5 (A B), 6 (A B^T), 7 (A^T B) as complex float32
+ * products of orders m >= 1 (flops: the three real products executed), or
+ * -1 (all). Host-side state, process-wide. */
 int so2conv_profile_enable(int on);
 int so2conv_profile_reset(void);
 int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* total_flops, double* total_bytes);

@@ -260,6 +260,7 @@ void split_plan(long K, int* splits, int* chunk) {
 struct Lin {
   const void* W;
   const void* WT;
+  const float* U[kMaxL + 1];   // float32: user-layout blocks [k][2h] of orders >= 1 (complex products)
 };
 struct LinBuf {
   void* W;
@@ -307,20 +308,24 @@ long max_user_block(const Dims& d) {
 constexpr long kCoefChunk = 4096;
 static_assert(kCoefChunk % kGemmKTile == 0, "coefficient split chunks must be whole K tiles");
 
-// Mixture of linear experts: merged weights of every system (block-major:
-// block a of linear `second` holds [S][user_block] at S * (offset of a)),
-// a second such buffer for the double backward, float32 staging of one
+// Mixture of linear experts: merged weights of every system per linear
+// (block-major: block a holds [S][user_block] at S * (offset of a)), the
+// merged weight directions of the double backward, float32 staging of one
 // expert block (bfloat16 experts or expert gradients), and the split-K
 // partials of the coefficient gradients.
 struct MixWs {
-  float *merged, *merged2, *we32, *gwe32, *P;
+  float* merged[2];    // merged weights of each linear; at the end, the per-system gradients
+  float* pmerged[2];   // double backward: merged directions; at the end, the first-order gradients
+  float *we32, *gwe32, *P;
 };
 void take_mix(Arena& ar, const Ctx& c, int stage, MixWs* m) {
   *m = MixWs{};
   if (!c.nk) return;
-  const size_t pm = (size_t)std::max(user_size(c.d, 0), user_size(c.d, 1)), mb = (size_t)max_user_block(c.d);
-  m->merged = ar.take((size_t)c.ns * pm);
-  m->merged2 = stage == 2 ? ar.take((size_t)c.ns * pm) : nullptr;
+  const size_t mb = (size_t)max_user_block(c.d);
+  for (int second = 0; second < 2; ++second) {
+    m->merged[second] = ar.take((size_t)c.ns * user_size(c.d, second));
+    m->pmerged[second] = stage == 2 ? ar.take((size_t)c.ns * user_size(c.d, second)) : nullptr;
+  }
   m->we32 = c.bf ? ar.take((size_t)c.nk * mb) : nullptr;
   m->gwe32 = c.bf && stage > 0 ? ar.take((size_t)c.nk * mb) : nullptr;
   m->P = stage > 0 ? ar.take((size_t)((mb + kCoefChunk - 1) / kCoefChunk) * c.ns * c.nk) : nullptr;
@@ -541,7 +546,7 @@ void* offs(void* p, size_t elems, int es) { return static_cast<char*>(p) + elems
 // launching stream and its algorithmic flop count (2 M N K summed over the
 // launch's problems) is recorded; so2conv_profile_read reports the totals.
 struct ProfRec {
-  int kind;          // 0 NN, 1 NT, 2 TN (float32); 3 NT, 4 TN (bfloat16)
+  int kind;          // 0 NN, 1 NT, 2 TN (float32); 3 NT, 4 TN (bfloat16); 5 NN, 6 NT, 7 TN (complex float32)
   double flops;
   double bytes;      // algorithmic: A, B read once, C (or the split partials) written once
   hipEvent_t a, b;
@@ -551,6 +556,7 @@ bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 
 int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int bf, hipStream_t s) {
+  if (ps.empty()) return SO2_OK;
   const double es = bf ? 2.0 : 4.0;
   size_t i = 0;
   while (i < ps.size()) {
@@ -559,13 +565,15 @@ int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int bf, hipStream_t s
     double flops = 0, bytes = 0;
     while (i < ps.size() && b.nprob < kGemmMaxProbs) {
       const GemmProb& q = ps[i];
-      flops += 2.0 * q.M * (double)q.N * q.K;
-      bytes += es * ((double)q.M * q.K + (double)q.K * q.N) +
-               4.0 * (double)q.M * q.N * (q.partial ? q.k_splits : 1) * (q.accumulate ? 2 : 1);
+      const double f = q.cplx ? 2.0 : 1.0;   // complex: both halves of A and B, real and imaginary C
+      flops += (q.cplx ? 3.0 : 1.0) * 2.0 * q.M * (double)q.N * q.K;
+      bytes += es * f * ((double)q.M * q.K + (double)q.K * q.N) +
+               4.0 * f * (double)q.M * q.N * (q.partial ? q.k_splits : 1) * (q.accumulate ? 2 : 1);
       b.p[b.nprob++] = ps[i++];
     }
     if (g_prof_on) {
-      ProfRec r{bf ? (TA ? 4 : 3) : (TA ? 2 : (TB ? 1 : 0)), flops, bytes, nullptr, nullptr};
+      const int kind = ps[0].cplx ? (TA ? 7 : (TB ? 6 : 5)) : (bf ? (TA ? 4 : 3) : (TA ? 2 : (TB ? 1 : 0)));
+      ProfRec r{kind, flops, bytes, nullptr, nullptr};
       SO2_HIP(hipEventCreate(&r.a));
       SO2_HIP(hipEventCreate(&r.b));
       SO2_HIP(hipEventRecord(r.a, s));
@@ -674,10 +682,33 @@ struct WSet {
   std::vector<long> e;
   std::vector<Lin> W;
 };
-WSet wset(const std::vector<long>& e, const std::vector<LinBuf>& b) {
+// user-layout blocks: the caller's arrays (one system) or each system's
+// merged blocks (`merged`, block-major, see sys_blocks)
+void sys_blocks(const Ctx& c, int second, float* merged, int sy, void** bp);
+WSet wset(const Ctx& c, int second, const std::vector<long>& e, const std::vector<LinBuf>& b,
+          const void* const* user, float* merged) {
   WSet w{e, {}};
-  for (const LinBuf& x : b) w.W.push_back(Lin{x.W, x.WT});
+  for (size_t sy = 0; sy < b.size(); ++sy) {
+    Lin l{b[sy].W, b[sy].WT, {}};
+    void* bp[kMaxL + 1] = {};
+    if (merged) sys_blocks(c, second, merged, (int)sy, bp);
+    for (int a = 0; a <= c.d.M; ++a)
+      l.U[a] = static_cast<const float*>(merged ? bp[a] : (user ? user[a] : nullptr));
+    w.W.push_back(l);
+  }
   return w;
+}
+
+// complex product of order a >= 1 (float32): see GemmProb
+GemmProb prob_cx(const void* A, int lda, int dA, const void* B, int ldb, int dB, float* C, int ldc, int M, int N,
+                 int K, float sA, float sB, int acc = 0) {
+  GemmProb p = prob(A, lda, B, ldb, C, ldc, M, N, K, acc);
+  p.cplx = 1;
+  p.dA = dA;
+  p.dB = dB;
+  p.sA = sA;
+  p.sB = sB;
+  return p;
 }
 
 // Per-order products of linear `second` (0: first, 1: second) over the chunk
@@ -693,7 +724,7 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
   const Dims& d = c.d;
   const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
   const int lda = transposed ? wout : win, ldc = transposed ? win : wout;
-  std::vector<GemmProb> ps;
+  std::vector<GemmProb> ps, pc;   // real products; complex products (float32, orders >= 1)
   for (int q = 0; q < stacks; ++q)
     for (size_t sy = 0; sy < w.W.size(); ++sy) {
       const long lo = std::max(w.e[sy], e0), hi = std::min(w.e[sy + 1], e0 + n);
@@ -709,6 +740,15 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
         realified_shape(d, second, a, &r, &cc, &off);
         const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
         const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+        if (a > 0 && !c.bf) {
+          // (T+ + i T-)(W0 + i W1) forward; (U+ + i U-)(W0 - i W1)^T transposed
+          const int k = r / 2, h = cc / 2;
+          if (!transposed)
+            pc.push_back(prob_cx(offs(Ar, ib, c.es), win, k, W.U[a], cc, h, Cr + ob, wout, rows, h, k, 1.f, 1.f, acc));
+          else
+            pc.push_back(prob_cx(offs(Ar, ob, c.es), wout, h, W.U[a], cc, h, Cr + ib, win, rows, k, h, 1.f, -1.f, acc));
+          continue;
+        }
         if (!transposed) {
           if (c.bf)
             ps.push_back(prob(offs(Ar, ib, c.es), win, offs(W.WT, off, c.es), r, Cr + ob, wout, rows, cc, r, acc));
@@ -719,7 +759,9 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
         }
       }
     }
-  return run_batch(ps, false, transposed || c.bf, c.bf, s);
+  int rr = run_batch(ps, false, transposed || c.bf, c.bf, s);
+  if (rr) return rr;
+  return run_batch(pc, false, transposed, 0, s);
 }
 
 // weight gradient of linear `second` per system (realified, float32) over the
@@ -742,6 +784,7 @@ int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* co
     realified_shape(d, second, a, &r, &cc, &off);
     const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
     const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+    const bool cx = a > 0 && !c.bf;
     std::vector<GemmProb> ps;
     std::vector<Red> red;
     size_t poff = 0;
@@ -752,14 +795,17 @@ int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* co
       for (int q = 0; q < nseg; ++q) {
         int sp, ch;
         split_plan(hi - lo, &sp, &ch);
-        GemmProb p = prob(offs(in[q], (size_t)(lo - e0) * win + ib, c.es), win,
-                          offs(out[q], (size_t)(lo - e0) * wout + ob, c.es), wout, P + poff, cc, r, cc,
-                          (int)(hi - lo));
+        const void* Aq = offs(in[q], (size_t)(lo - e0) * win + ib, c.es);
+        const void* Bq = offs(out[q], (size_t)(lo - e0) * wout + ob, c.es);
+        // float32, orders >= 1: (T+ - i T-)^T (Ubar+ + i Ubar-) straight into the user layout [k][2h]
+        GemmProb p = cx ? prob_cx(Aq, win, r / 2, Bq, wout, cc / 2, P + poff, cc, r / 2, cc / 2, (int)(hi - lo),
+                                  -1.f, 1.f)
+                        : prob(Aq, win, Bq, wout, P + poff, cc, r, cc, (int)(hi - lo));
         p.k_splits = sp;
         p.k_chunk = ch;
         p.partial = 1;
         ps.push_back(p);
-        poff += (size_t)sp * r * cc;
+        poff += (size_t)sp * (cx ? r / 2 : r) * cc;
         rd.splits += sp;
       }
       red.push_back(rd);
@@ -768,7 +814,7 @@ int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* co
     int rr = run_batch(ps, true, false, c.bf, s);
     if (rr) return rr;
     for (const Red& rd : red)
-      SO2_HIP(gemm_reduce(P + rd.poff, rd.splits, r, cc, G[rd.sy] + off, cc, rd.acc, s));
+      SO2_HIP(gemm_reduce(P + rd.poff, rd.splits, cx ? r / 2 : r, cc, G[rd.sy] + off, cc, rd.acc, s));
   }
   return SO2_OK;
 }
@@ -845,7 +891,7 @@ int fold_systems(const Ctx& c, int second, const std::vector<float*>& G, float* 
   for (int sy = 0; sy < c.ns; ++sy) {
     void* bp[kMaxL + 1];
     sys_blocks(c, second, merged, sy, bp);
-    SO2_HIP(launch_fold_grad(c.d, second, G[sy], bp, 0, s));
+    SO2_HIP(launch_fold_grad(c.d, second, G[sy], bp, 0, s, !c.bf));
   }
   return SO2_OK;
 }
@@ -916,10 +962,10 @@ int prepare_weights(const Ctx& c, const MixIn* mx, const void* const* w1, const 
     if ((r = realify(c, 0, w1, B1[0], s)) || (r = realify(c, 1, w2, B2[0], s))) return r;
     return SO2_OK;
   }
-  if ((r = mix_linear(c, 0, w1, mx->coef, mw.merged, mw.we32, 0, s))) return r;
-  if ((r = realify_systems(c, 0, mw.merged, B1, s))) return r;
-  if ((r = mix_linear(c, 1, w2, mx->coef, mw.merged, mw.we32, 0, s))) return r;
-  return realify_systems(c, 1, mw.merged, B2, s);
+  if ((r = mix_linear(c, 0, w1, mx->coef, mw.merged[0], mw.we32, 0, s))) return r;
+  if ((r = realify_systems(c, 0, mw.merged[0], B1, s))) return r;
+  if ((r = mix_linear(c, 1, w2, mx->coef, mw.merged[1], mw.we32, 0, s))) return r;
+  return realify_systems(c, 1, mw.merged[1], B2, s);
 }
 
 std::vector<long> sys_edges(const MixIn* mx, long E) { return mx ? mx->e : std::vector<long>{0, E}; }
@@ -1127,7 +1173,7 @@ int conv_fwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
   float* y32 = f32_acc(c, y, w.y32);
   if ((r = prepare_weights(c, mx, w1, w2, w.W1, w.W2, w.mix, s))) return r;
   const std::vector<long> se = sys_edges(mx, gd.E);
-  const WSet W1 = wset(se, w.W1), W2 = wset(se, w.W2);
+  const WSet W1 = wset(c, 0, se, w.W1, w1, w.mix.merged[0]), W2 = wset(c, 1, se, w.W2, w2, w.mix.merged[1]);
   if (gd.E == 0) {
     GraphDev gc = gd;
     gc.e0 = gc.e1 = 0;
@@ -1188,7 +1234,7 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
   const bool want_w1 = !all_null(gw1, d.M + 1) || gcoef, want_w2 = !all_null(gw2, d.M + 1) || gcoef;
   if ((r = prepare_weights(c, mx, w1, w2, w.W1, w.W2, w.mix, s))) return r;
   const std::vector<long> se = sys_edges(mx, gd.E);
-  const WSet W1 = wset(se, w.W1), W2 = wset(se, w.W2);
+  const WSet W1 = wset(c, 0, se, w.W1, w1, w.mix.merged[0]), W2 = wset(c, 1, se, w.W2, w2, w.mix.merged[1]);
   if (mx && want_w1 && (r = zero_sets(w.gW1r, realified_size(d, 0), s))) return r;
   if (mx && want_w2 && (r = zero_sets(w.gW2r, realified_size(d, 1), s))) return r;
   for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
@@ -1232,14 +1278,15 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
     if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, w.tau1, w.tau2, w.tau3, vbar, s));
   }
   if (!mx) {
-    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2, c.bf, s));
-    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1, c.bf, s));
+    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2, c.bf, s, !c.bf));
+    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1, c.bf, s, !c.bf));
   } else {
     for (int second = 0; second < 2; ++second) {
       if (!(second ? want_w2 : want_w1)) continue;
-      if ((r = fold_systems(c, second, second ? w.gW2r : w.gW1r, w.mix.merged, s))) return r;
-      if ((r = mix_grads(c, second, w.mix.merged, mx->coef, second ? w2 : w1, nullptr, nullptr, nullptr,
-                         second ? gw2 : gw1, gcoef, second == 1 && want_w1, w.mix, s)))
+      float* gm = w.mix.merged[second];   // the merged weights are no longer needed
+      if ((r = fold_systems(c, second, second ? w.gW2r : w.gW1r, gm, s))) return r;
+      if ((r = mix_grads(c, second, gm, mx->coef, second ? w2 : w1, nullptr, nullptr, nullptr, second ? gw2 : gw1,
+                         gcoef, second == 1 && want_w1, w.mix, s)))
         return r;
     }
   }
@@ -1310,10 +1357,10 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     for (int second = 0; second < 2; ++second) {
       const bool hp = second ? has_pw2 : has_pw1, hwe = second ? has_pwe2 : has_pwe1;
       if (!hp) continue;
-      if (hwe && (r = mix_linear(c, second, second ? pw2 : pw1, mx->coef, w.mix.merged, w.mix.we32, 0, s)))
-        return r;
-      if (pcoef && (r = mix_linear(c, second, second ? w2 : w1, pcoef, w.mix.merged, w.mix.we32, hwe, s))) return r;
-      if ((r = realify_systems(c, second, w.mix.merged, second ? w.pW2 : w.pW1, s))) return r;
+      float* pm = w.mix.pmerged[second];
+      if (hwe && (r = mix_linear(c, second, second ? pw2 : pw1, mx->coef, pm, w.mix.we32, 0, s))) return r;
+      if (pcoef && (r = mix_linear(c, second, second ? w2 : w1, pcoef, pm, w.mix.we32, hwe, s))) return r;
+      if ((r = realify_systems(c, second, pm, second ? w.pW2 : w.pW1, s))) return r;
     }
     if (want_w1 && (r = zero_sets(w.gW1r, realified_size(d, 0), s))) return r;
     if (want_w2 && (r = zero_sets(w.gW2r, realified_size(d, 1), s))) return r;
@@ -1321,7 +1368,8 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     if (first && want_w2 && (r = zero_sets(w.gW2f, realified_size(d, 1), s))) return r;
   }
   const std::vector<long> se = sys_edges(mx, gd.E);
-  const WSet W1 = wset(se, w.W1), W2 = wset(se, w.W2), pW1 = wset(se, w.pW1), pW2 = wset(se, w.pW2);
+  const WSet W1 = wset(c, 0, se, w.W1, w1, w.mix.merged[0]), W2 = wset(c, 1, se, w.W2, w2, w.mix.merged[1]);
+  const WSet pW1 = wset(c, 0, se, w.pW1, pw1, w.mix.pmerged[0]), pW2 = wset(c, 1, se, w.pW2, pw2, w.mix.pmerged[1]);
   for (long e0 = 0, k = 0; e0 < gd.E; e0 += ec, ++k) {
     GraphDev gc = gd;
     gc.e0 = e0;
@@ -1400,16 +1448,17 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     }
   }
   if (!mx) {
-    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2_2, c.bf, s));
-    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1_2, c.bf, s));
+    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2_2, c.bf, s, !c.bf));
+    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1_2, c.bf, s, !c.bf));
   } else {
     for (int second = 0; second < 2; ++second) {
       if (!(second ? want_w2 : want_w1)) continue;
-      if ((r = fold_systems(c, second, second ? w.gW2r : w.gW1r, w.mix.merged, s))) return r;
-      if (first && (r = fold_systems(c, second, second ? w.gW2f : w.gW1f, w.mix.merged2, s))) return r;
-      if ((r = mix_grads(c, second, w.mix.merged, mx->coef, second ? w2 : w1, first ? w.mix.merged2 : nullptr,
-                         pcoef, second ? pw2 : pw1, second ? gw2_2 : gw1_2, gcoef2, second == 1 && want_w1,
-                         w.mix, s)))
+      // the merged weights and directions are no longer needed: they take the gradients
+      float *gm = w.mix.merged[second], *gf = w.mix.pmerged[second];
+      if ((r = fold_systems(c, second, second ? w.gW2r : w.gW1r, gm, s))) return r;
+      if (first && (r = fold_systems(c, second, second ? w.gW2f : w.gW1f, gf, s))) return r;
+      if ((r = mix_grads(c, second, gm, mx->coef, second ? w2 : w1, first ? gf : nullptr, pcoef,
+                         second ? pw2 : pw1, second ? gw2_2 : gw1_2, gcoef2, second == 1 && want_w1, w.mix, s)))
         return r;
     }
   }

@@ -319,14 +319,17 @@ int launch_realify(const Dims& d, int second, const void* const* w, void* wr, vo
   return hipSuccess;
 }
 
-int launch_fold_grad(const Dims& d, int second, const float* gr, void* const* gw, int bf16, hipStream_t s) {
+int launch_fold_grad(const Dims& d, int second, const float* gr, void* const* gw, int bf16, hipStream_t s,
+                     int user_layout) {
   for (int a = 0; a <= d.M; ++a) {
     if (!gw[a]) continue;
     int r, c;
     long off;
     realified_shape(d, second, a, &r, &c, &off);
     hipError_t e;
-    if (a == 0) {
+    if (a > 0 && user_layout && !bf16) {   // already [k][2h] at the block's offset
+      e = hipMemcpyAsync(gw[a], gr + off, sizeof(float) * (size_t)(r / 2) * c, hipMemcpyDeviceToDevice, s);
+    } else if (a == 0) {
       if (bf16) e = (hipError_t)launch_to_bf16(gr + off, static_cast<bf16s*>(gw[0]), (size_t)r * c, s);
       else e = hipMemcpyAsync(gw[0], gr + off, sizeof(float) * (size_t)r * c, hipMemcpyDeviceToDevice, s);
     } else {

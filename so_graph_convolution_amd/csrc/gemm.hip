@@ -1,7 +1,7 @@
-// Grouped MFMA GEMMs: 256x128 block tiles, 8 waves of 64x64 (2x2 32x32 MFMA
-// tiles each), LDS double buffering, XCD-aware linear tile order.
-//   float32 operands : v_mfma_f32_32x32x2_f32, K tile 16
-//   bfloat16 operands: v_mfma_f32_32x32x16_bf16, K tile 32
+// Grouped MFMA GEMMs with LDS double buffering and an XCD-aware linear tile order.
+//   float32 operands : 256x128 blocks, 8 waves of 64x64 (2x2 v_mfma_f32_32x32x2_f32), K tile 16
+//   complex float32  : 128 x 64-complex blocks, three real products per complex one (below)
+//   bfloat16 operands: 256x256 blocks, 16 waves of 64x64 (v_mfma_f32_32x32x16_bf16), K tile 64
 //
 // Operand staging: every global load runs along the operand's contiguous
 // dimension (float4 per lane, consecutive lanes on consecutive addresses), and
@@ -270,6 +270,169 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
 }
 
 
+// ---------------------------------------------------------------- complex products (float32)
+// Block tile 128 rows x 64 complex columns of 8 waves (4 along M x 2 along N),
+// each wave 32x32 complex outputs with three accumulators (P1, P2, P3 of the
+// three-product form); K tile 16; a, b, c, d staged as four LDS tiles in the
+// layout of the real kernel, the sums a + sA b and c + sB d formed from the
+// fragments in registers. 64 KB of LDS for two stages: two blocks per CU.
+// Measured on MI355X at the per-order shapes (725k rows): 1.17-1.26x faster
+// than the realified product with four real products.
+constexpr int CBM = 128, CBN = 64, CBK = 16, CNT = 512;
+template <bool KCONTIG, int R>
+struct CT {
+  static constexpr int PK = CBK + 4;
+  static constexpr int PW = R + 32;
+  static constexpr int FL = KCONTIG ? R * PK : CBK * PW;
+  static constexpr int V4 = R * CBK / 4;
+  static constexpr int NL = (V4 + CNT - 1) / CNT;
+};
+template <bool KCONTIG, int R>
+__device__ inline void cload(const float* __restrict__ P, int ld, int r0, int rlim, int k0, int kend,
+                             floatx4 (&v)[CT<KCONTIG, R>::NL]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < CT<KCONTIG, R>::NL; ++p) {
+    const int idx = p * CNT + t;
+    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+    if (idx < CT<KCONTIG, R>::V4) {
+      if (KCONTIG) {
+        const int row = idx / (CBK / 4), q = idx % (CBK / 4);
+        const int gr = r0 + row, gk = k0 + 4 * q;
+        if (gr < rlim) {
+          const float* src = P + (size_t)gr * ld + gk;
+          if (gk + 3 < kend) x = *reinterpret_cast<const floatx4*>(src);
+          else
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[c] = (gk + c < kend) ? src[c] : 0.f;
+        }
+      } else {
+        const int k = idx / (R / 4), q = idx % (R / 4);
+        const int gk = k0 + k, gr = r0 + 4 * q;
+        if (gk < kend) {
+          const float* src = P + (size_t)gk * ld + gr;
+          if (gr + 3 < rlim) x = *reinterpret_cast<const floatx4*>(src);
+          else
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[c] = (gr + c < rlim) ? src[c] : 0.f;
+        }
+      }
+    }
+    v[p] = x;
+  }
+}
+template <bool KCONTIG, int R>
+__device__ inline void cstore(float* __restrict__ S, const floatx4 (&v)[CT<KCONTIG, R>::NL]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < CT<KCONTIG, R>::NL; ++p) {
+    const int idx = p * CNT + t;
+    if (idx < CT<KCONTIG, R>::V4) {
+      if (KCONTIG) {
+        const int row = idx / (CBK / 4), q = idx % (CBK / 4);
+        *reinterpret_cast<floatx4*>(S + row * CT<KCONTIG, R>::PK + 4 * q) = v[p];
+      } else {
+        const int k = idx / (R / 4), q = idx % (R / 4);
+        *reinterpret_cast<floatx4*>(S + k * CT<KCONTIG, R>::PW + 4 * q) = v[p];
+      }
+    }
+  }
+}
+template <bool KCONTIG, int R>
+__device__ __forceinline__ float cfrag(const float* S, int row, int k) {
+  return KCONTIG ? S[row * CT<KCONTIG, R>::PK + k] : S[k * CT<KCONTIG, R>::PW + row];
+}
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_cplx_kernel(GemmBatch batch) {
+  constexpr bool AK = !TA, BKC = TB;
+  __shared__ float Aa[2][CT<AK, CBM>::FL], Ab[2][CT<AK, CBM>::FL];
+  __shared__ float Bc[2][CT<BKC, CBN>::FL], Bd[2][CT<BKC, CBN>::FL];
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * CBM, n0 = tn * CBN;
+  const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave / 2, wn = wave % 2, li = lane % 32, lk = lane / 32;
+  floatx16 acc1, acc2, acc3;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc1[r] = acc2[r] = acc3[r] = 0.f;
+  const float* A0 = static_cast<const float*>(p.A);
+  const float* A1 = A0 + p.dA;
+  const float* B0 = static_cast<const float*>(p.B);
+  const float* B1 = B0 + p.dB;
+  const float sA = p.sA, sB = p.sB;
+  const int nk = (kend - kbeg + CBK - 1) / CBK;
+  floatx4 ra0[CT<AK, CBM>::NL], ra1[CT<AK, CBM>::NL], rb0[CT<BKC, CBN>::NL], rb1[CT<BKC, CBN>::NL];
+  auto load = [&](int k0) {
+    cload<AK, CBM>(A0, p.lda, m0, p.M, k0, kend, ra0);
+    cload<AK, CBM>(A1, p.lda, m0, p.M, k0, kend, ra1);
+    cload<BKC, CBN>(B0, p.ldb, n0, p.N, k0, kend, rb0);
+    cload<BKC, CBN>(B1, p.ldb, n0, p.N, k0, kend, rb1);
+  };
+  auto store = [&](int b) {
+    cstore<AK, CBM>(Aa[b], ra0);
+    cstore<AK, CBM>(Ab[b], ra1);
+    cstore<BKC, CBN>(Bc[b], rb0);
+    cstore<BKC, CBN>(Bd[b], rb1);
+  };
+  if (nk > 0) {
+    load(kbeg);
+    store(0);
+  }
+  __syncthreads();
+  const int ar = wm * 32 + li, br = wn * 32 + li;
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kbeg + (kt + 1) * CBK);
+#pragma unroll
+    for (int kk = 0; kk < CBK; kk += 2) {
+      const float fa = cfrag<AK, CBM>(Aa[cur], ar, kk + lk), fb = cfrag<AK, CBM>(Ab[cur], ar, kk + lk);
+      const float fc = cfrag<BKC, CBN>(Bc[cur], br, kk + lk), fd = cfrag<BKC, CBN>(Bd[cur], br, kk + lk);
+      const float fs = fa + sA * fb, fw = fc + sB * fd;
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, fc, acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(fb, fd, acc2, 0, 0, 0);
+      acc3 = __builtin_amdgcn_mfma_f32_32x32x2f32(fs, fw, acc3, 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+  const float sig = sA * sB;
+  float* out;
+  int ldo;
+  bool acc_in;
+  if (p.partial) {
+    out = p.C + (size_t)split * p.M * 2 * p.N;
+    ldo = 2 * p.N;
+    acc_in = false;
+  } else {
+    out = p.C;
+    ldo = p.ldc;
+    acc_in = p.accumulate != 0;
+  }
+  const int j = n0 + wn * 32 + li;
+  if (j < p.N) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = m0 + wm * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
+      if (i < p.M) {
+        const float t2 = sig * acc2[r];
+        const float re = acc1[r] - t2, im = acc3[r] - acc1[r] - t2;
+        float* d0 = out + (size_t)i * ldo + j;
+        float* d1 = d0 + p.N;
+        *d0 = acc_in ? *d0 + re : re;
+        *d1 = acc_in ? *d1 + im : im;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- bfloat16 operands
 // Block tile 256x256 of 16 waves (64x64 each, 2x2 v_mfma_f32_32x32x16_bf16),
 // K tile 64, one block per CU (147 KB of LDS for two stages). Measured on
@@ -293,7 +456,8 @@ constexpr int NTH = 64 * NWH;                 // threads
 constexpr int BKH = 64;                       // K tile
 constexpr int PD = BKH / 2 + 4;               // LDS row pitch (dwords)
 constexpr int CPR = BKH / 8;                  // 16-byte chunks per row
-static_assert(kGemmKTile % BKH == 0 && kGemmKTile % BK_TILE == 0, "split chunks must be whole K tiles");
+static_assert(kGemmKTile % BKH == 0 && kGemmKTile % BK_TILE == 0 && kGemmKTile % CBK == 0,
+              "split chunks must be whole K tiles");
 
 __device__ __forceinline__ int lds_chunk(int row, int q) { return row * PD + 4 * (q ^ ((row >> 3) & 1)); }
 
@@ -487,8 +651,12 @@ __global__ void gemm_reduce_kernel(const float* __restrict__ P, int splits, int 
 
 int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   constexpr int BK = BK_TILE;
+  const bool cx = b.nprob > 0 && b.p[0].cplx;
   if (bf16 && TA == TB) return hipErrorInvalidValue;
-  const int bm = bf16 ? BMH : BM, bn = bf16 ? BNH : BN;
+  if (cx && (bf16 || (TA && TB))) return hipErrorInvalidValue;
+  for (int q = 0; q < b.nprob; ++q)
+    if ((b.p[q].cplx != 0) != cx) return hipErrorInvalidValue;
+  const int bm = cx ? CBM : (bf16 ? BMH : BM), bn = cx ? CBN : (bf16 ? BNH : BN);
   int total = 0;
   for (int q = 0; q < b.nprob; ++q) {
     GemmProb& p = b.p[q];
@@ -502,6 +670,12 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
   dim3 grid(total), block(NT);
+  if (cx) {
+    if (!TA && !TB) hipLaunchKernelGGL((gemm_cplx_kernel<false, false>), grid, dim3(CNT), 0, s, b);
+    else if (!TA && TB) hipLaunchKernelGGL((gemm_cplx_kernel<false, true>), grid, dim3(CNT), 0, s, b);
+    else hipLaunchKernelGGL((gemm_cplx_kernel<true, false>), grid, dim3(CNT), 0, s, b);
+    return hipGetLastError();
+  }
   if (bf16) {
     if (TA) hipLaunchKernelGGL((gemm_bf16_kernel<true>), grid, dim3(NTH), 0, s, b);
     else hipLaunchKernelGGL((gemm_bf16_kernel<false>), grid, dim3(NTH), 0, s, b);

@@ -13,6 +13,15 @@
 // TA problems (weight gradients, K = edges) are split over K; every split
 // writes its own partial tile and gemm_reduce sums the splits in a fixed
 // order, so results are bitwise reproducible (no atomics).
+//
+// Complex problems (float32 only): the per-order products of orders m >= 1
+// are complex products (TrimSO(2) page, Eq.(1): u+ + i u- = (T+ + i T-)(W0 + i W1)),
+// taken with three real products instead of four:
+//   op(A) = a + i sA b,  op(B) = c + i sB d   (b, d at element offsets dA, dB from a, c)
+//   P1 = a c, P2 = b d, P3 = (a + sA b)(c + sB d)
+//   Re = P1 - sA sB P2,  Im = P3 - P1 - sA sB P2
+// M, N, K are the complex sizes; the real part goes to C, the imaginary part
+// N columns to its right (a split writes [M][2N] partials).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -32,6 +41,9 @@ struct GemmProb {
   int accumulate;    // add into C (non-partial problems only)
   int partial;       // write split s to C + s*M*N (row pitch N) instead of C
   int tile_begin;    // first linear tile of this problem
+  int cplx;          // complex problem (all problems of a launch agree)
+  int dA, dB;        // complex: element offsets of b from a and of d from c
+  float sA, sB;      // complex: signs of b and d (+1 or -1)
 };
 
 struct GemmBatch {

@@ -93,8 +93,11 @@ int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const
 int launch_realify(const Dims& d, int second, const void* const* w, void* wr, void* wrt, int bf16, hipStream_t s,
                    int in_f32 = 0);
 // fold the realified float32 gradient back: gW_m0 = G00 + G11, gW_m1 = G01 - G10 (m >= 1),
-// gW_0 = G_0; gw blocks float32 or bfloat16
-int launch_fold_grad(const Dims& d, int second, const float* gr, void* const* gw, int bf16, hipStream_t s);
+// gW_0 = G_0; gw blocks float32 or bfloat16. user_layout (float32): blocks
+// m >= 1 already hold [gW_m0 | gW_m1] ([k][2h], from the complex products) at
+// their realified offsets and are copied.
+int launch_fold_grad(const Dims& d, int second, const float* gr, void* const* gw, int bf16, hipStream_t s,
+                     int user_layout = 0);
 // dtype conversions of n elements
 int launch_to_f32(const bf16s* in, float* out, size_t n, hipStream_t s);
 int launch_to_bf16(const float* in, bf16s* out, size_t n, hipStream_t s);
