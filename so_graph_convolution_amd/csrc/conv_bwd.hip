@@ -82,19 +82,22 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
       const float* gr = gy + (size_t)sDst[t] * D * C + c;
 #pragma unroll
       for (int r = 0; r < D; ++r) gv[r] = gr[(size_t)r * C];
-      float o[Q];
-      rot_fwd<L, M>(sR + t * K, gv, o);
-      OT* tr = tbar + (size_t)e * wZ + c;
       const float* vr = V + (size_t)e * wZ + c;
-      float vv[Q];
+      float vv[Q];   // the message row's loads in flight during the rotation
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const int q = qhalf(l, M);
 #pragma unroll
-        for (int m = -q; m <= q; ++m) {
-          st(tr + mm_col(l, m, 0, L, C), ev * o[ridx(l, m, M)]);
-          vv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
-        }
+        for (int m = -q; m <= q; ++m) vv[ridx(l, m, M)] = vr[mm_col(l, m, 0, L, C)];
+      }
+      float o[Q];
+      rot_fwd<L, M>(sR + t * K, gv, o);
+      OT* tr = tbar + (size_t)e * wZ + c;
+#pragma unroll
+      for (int l = 0; l <= L; ++l) {
+        const int q = qhalf(l, M);
+#pragma unroll
+        for (int m = -q; m <= q; ++m) st(tr + mm_col(l, m, 0, L, C), ev * o[ridx(l, m, M)]);
       }
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
@@ -160,16 +163,21 @@ __device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, Ro
   const float* sr = S + (size_t)e * wS + cin;
   float* sb = Sbar + (size_t)e * wS + cin;
   // one pass over the rows of R and R G_k: radial cotangent, transposed
-  // product into acc and the torque
+  // product into acc and the torque. The global loads of a degree are issued
+  // together before its rows (one memory latency per degree, not per row);
+  // its radial cotangent store closes it.
 #pragma unroll
   for (int l = 0; l <= L; ++l) {
     const int q = qhalf(l, M), n = 2 * l + 1;
+    float tv[2 * M + 1];
+#pragma unroll
+    for (int m = -q; m <= q; ++m) tv[m + q] = tb[mm_col(l, m, 0, L, Ci)];
     const float sc = sr[l * Ci];
     float sacc = 0.f;
 #pragma unroll
     for (int m = -q; m <= q; ++m) {
       const int off = rot_off(l, M) + (m + q) * n;
-      const float v = tb[mm_col(l, m, 0, L, Ci)];
+      const float v = tv[m + q];
       const float xb = sc * v;
       float r[2 * L + 1];
       load_row<L>(sRt, off, n, r);

@@ -109,9 +109,15 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
       const float* sr = S + (size_t)e * wS + c;
       const float* sd = Sdot + (size_t)e * wS + c;
       OT* tr = Tdot + (size_t)e * wT;
+      float svv[L + 1], sdvv[L + 1];   // every load of the edge before its stores
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
-        const float sv = sr[l * Ci], sdv = sd[l * Ci];
+        svv[l] = sr[l * Ci];
+        sdvv[l] = sd[l * Ci];
+      }
+#pragma unroll
+      for (int l = 0; l <= L; ++l) {
+        const float sv = svv[l], sdv = sdvv[l];
         const int q = qhalf(l, M), n = 2 * l + 1;
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
@@ -194,10 +200,16 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
           const int q = qhalf(l, M), n = 2 * l + 1;
+          float vv[2 * M + 1], vvd[2 * M + 1];   // the degree's loads together: one latency per degree
+#pragma unroll
+          for (int m = -q; m <= q; ++m) {
+            vv[m + q] = vr[mm_col(l, m, 0, L, C)];
+            vvd[m + q] = vd[mm_col(l, m, 0, L, C)];
+          }
 #pragma unroll
           for (int m = -q; m <= q; ++m) {
             const int off = rot_off(l, M) + (m + q) * n;
-            const float v = vr[mm_col(l, m, 0, L, C)], vdv = vd[mm_col(l, m, 0, L, C)];
+            const float v = vv[m + q], vdv = vvd[m + q];
             float r[2 * L + 1], rd[2 * L + 1];
             load_row<L>(sR + t * K, off, n, r);
             load_row<L>(sRd + t * K, off, n, rd);
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
           load_row<L>(sRd + t * K, off, n, rd);
           const float s1 = row_dot<L>(r, gv + l * l, n), s2 = row_dot<L>(rd, gv + l * l, n);
           st(r1 + mm_col(l, m, 0, L, C), ev * s1);
-          st(r2 + mm_col(l, m, 0, L, C), ev * s2 + pv * s1);
+          st(r2 + mm_col(l, m, 0, L, C), __builtin_fmaf(ev, s2, pv * s1));   // fused alike in every instantiation
           if (genv2) tk[6] += vr0[mm_col(l, m, 0, L, C)] * s2 + vdr0[mm_col(l, m, 0, L, C)] * s1;
         }
       }
@@ -462,25 +474,35 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
           const float* sr = S + (size_t)e * wS + cin;
           const float* sd = Sdot + (size_t)e * wS + cin;
           // one pass over the rows of R and Rdot: forward products for the
-          // radial cotangents and the transposed products into acc
+          // radial cotangents and the transposed products into acc. A
+          // degree's global loads are issued together before its rows (one
+          // memory latency per degree); its radial cotangent stores close it.
 #pragma unroll
           for (int l = 0; l <= L; ++l) {
             const int q = qhalf(l, M), n = 2 * l + 1;
+            float v1[2 * M + 1], v0[2 * M + 1];
+#pragma unroll
+            for (int m = -q; m <= q; ++m) {
+              v1[m + q] = tdb[mm_col(l, m, 0, L, Ci)];
+              v0[m + q] = tb[mm_col(l, m, 0, L, Ci)];
+            }
             const float sv = sr[l * Ci], sdv = sd[l * Ci];
             float sb = 0.f, sdb = 0.f;
 #pragma unroll
             for (int m = -q; m <= q; ++m) {
               const int off = rot_off(l, M) + (m + q) * n;
-              const float a1 = tdb[mm_col(l, m, 0, L, Ci)];
-              const float a0 = tb[mm_col(l, m, 0, L, Ci)];
+              const float a1 = v1[m + q];
+              const float a0 = v0[m + q];
               float r[2 * L + 1], rd[2 * L + 1];
               load_row<L>(sR + t * K, off, n, r);
               load_row<L>(sRd + t * K, off, n, rd);
               const float xt = row_dot<L>(r, xn + l * l, n), y2 = row_dot<L>(r, xdn + l * l, n);
               const float y1 = row_dot<L>(rd, xn + l * l, n);
-              sb += a1 * (y1 + y2) + a0 * xt;
-              sdb += a1 * xt;
-              const float u1 = sv * a0 + sdv * a1, u2 = sv * a1;
+              // explicit fused forms: every instantiation (with or without the
+              // position derivatives) rounds alike
+              sb = __builtin_fmaf(a0, xt, __builtin_fmaf(a1, y1 + y2, sb));
+              sdb = __builtin_fmaf(a1, xt, sdb);
+              const float u1 = __builtin_fmaf(sv, a0, sdv * a1), u2 = sv * a1;
               row_axpy<L>(r, u1, acc + l * l, n);
               row_axpy<L>(rd, u2, acc + l * l, n);
               if (P2) {

@@ -56,13 +56,16 @@ __global__ __launch_bounds__(256) void edge_fwd_kernel(Dims d, GraphDev g, const
       float a[D];
 #pragma unroll
       for (int r = 0; r < D; ++r) a[r] = xr[(size_t)r * C];
+      const float* sr = S + (size_t)e * ldS + c;
+      float scv[L + 1];   // every load of the edge before the rotation and its stores
+#pragma unroll
+      for (int l = 0; l <= L; ++l) scv[l] = sr[l * Ci];
       float o[Q];
       rot_fwd<L, M>(sR + t * K, a, o);
-      const float* sr = S + (size_t)e * ldS + c;
       OT* tr = T + (size_t)e * wT;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
-        const float sc = sr[l * Ci];
+        const float sc = scv[l];
         const int q = qhalf(l, M);
 #pragma unroll
         for (int m = -q; m <= q; ++m) st(tr + mm_col(l, m, c, L, Ci), sc * o[ridx(l, m, M)]);
