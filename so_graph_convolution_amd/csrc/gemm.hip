@@ -6,10 +6,15 @@
 // Operand staging: every global load runs along the operand's contiguous
 // dimension (float4 per lane, consecutive lanes on consecutive addresses), and
 // the LDS layout follows the global one:
-//   A row-major [i][k]  -> As[i][k]  pitch BK+4      A transposed [k][i] -> As[k][i] pitch 160
-//   B row-major [k][j]  -> Bs[k][j]  pitch 160       B transposed [j][k] -> Bs[j][k] pitch BK+4
-// An MFMA operand read takes 32 consecutive rows/columns for one k (lanes 0-31)
-// and the next k (lanes 32-63).
+//   A row-major [i][k]  -> As[i][k]  pitch BK+4      A transposed [k][i] -> As[k][i] pitch BM+4
+//   B row-major [k][j]  -> Bs[k][j]  pitch BN+4      B transposed [j][k] -> Bs[j][k] pitch BK+4
+// The sum over k does not depend on which k an MFMA step takes, so step s of a
+// K tile (BK/2 steps of v_mfma_f32_32x32x2_f32) gives lane half lk (lanes
+// 0-31, 32-63) k = (BK/2) lk + s in both operands. A lane's values of a
+// k-contiguous tile are then adjacent (128-bit LDS reads; pitch BK+4 starts
+// any 16 rows on distinct 4-bank groups); a k-major tile is read one value
+// per step, 32 consecutive rows per lane half, and its pitch R+4 puts the two
+// halves (BK/2 rows apart) on disjoint banks.
 #include "gemm.hpp"
 
 namespace so2 {
@@ -36,7 +41,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 template <int BK, int R>
 struct Cfg {
   static constexpr int PK = BK + 4;                 // pitch of k-contiguous tiles
-  static constexpr int PW = R + 32;                 // pitch of k-major tiles: two k rows of one read hit disjoint banks
+  static constexpr int PW = R + 4;                  // pitch of k-major tiles: (BK/2) PW = 32 mod 64 banks
   static constexpr int KMAJ = BK * PW;              // floats of a k-major tile
   static constexpr int KCON = R * PK;               // floats of a k-contiguous tile
   static constexpr int NRC = (R * BK / 4) / NT;     // float4 loads per thread of a k-contiguous tile
@@ -157,10 +162,22 @@ __device__ inline void store_tile(float* __restrict__ S, const floatx4 (&v)[KCON
   }
 }
 
-// MFMA operand: element (row, k) of a staged tile
+// MFMA operands of one K tile for lane half lk: row `row`, k = (BK/2) lk + s
 template <bool KCONTIG, int BK, int R>
-__device__ __forceinline__ float frag(const float* S, int row, int k) {
-  return KCONTIG ? S[row * Cfg<BK, R>::PK + k] : S[k * Cfg<BK, R>::PW + row];
+__device__ __forceinline__ void frag(const float* S, int row, int lk, float (&f)[BK / 2]) {
+  static_assert(BK % 8 == 0, "two 128-bit reads per lane half");
+  if (KCONTIG) {
+    const floatx4* q = reinterpret_cast<const floatx4*>(S + row * Cfg<BK, R>::PK + (BK / 2) * lk);
+#pragma unroll
+    for (int v = 0; v < BK / 8; ++v) {
+      const floatx4 u = q[v];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) f[4 * v + c] = u[c];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < BK / 2; ++s) f[s] = S[((BK / 2) * lk + s) * Cfg<BK, R>::PW + row];
+  }
 }
 
 // epilogue: lane holds rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of each 32x32 tile
@@ -201,8 +218,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   // A is k-contiguous when not transposed; B is k-contiguous when transposed
   constexpr bool AK = !TA, BKC = TB;
   constexpr int SA = tile_floats<!AK, BK, BM>(), SB = tile_floats<!BKC, BK, BN>();
-  __shared__ float As[2][SA];
-  __shared__ float Bs[2][SB];
+  __shared__ __attribute__((aligned(16))) float As[2][SA];
+  __shared__ __attribute__((aligned(16))) float Bs[2][SB];
 
   int pi, local;
   decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
@@ -247,18 +264,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
     const float* as = As[cur];
     const float* bs = Bs[cur];
     const int ra0 = wm * 32 * WM + li, rb0 = wn * 32 * WN + li;
+    float av[WM][BK / 2], bv[WN][BK / 2];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      float av[WM], bv[WN];
+    for (int a = 0; a < WM; ++a) frag<AK, BK, BM>(as, ra0 + 32 * a, lk, av[a]);
 #pragma unroll
-      for (int a = 0; a < WM; ++a) av[a] = frag<AK, BK, BM>(as, ra0 + 32 * a, kk + lk);
+    for (int b = 0; b < WN; ++b) frag<BKC, BK, BN>(bs, rb0 + 32 * b, lk, bv[b]);
 #pragma unroll
-      for (int b = 0; b < WN; ++b) bv[b] = frag<BKC, BK, BN>(bs, rb0 + 32 * b, kk + lk);
+    for (int s = 0; s < BK / 2; ++s)
 #pragma unroll
       for (int a = 0; a < WM; ++a)
 #pragma unroll
-        for (int b = 0; b < WN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
-    }
+        for (int b = 0; b < WN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][s], bv[b][s], acc[a][b], 0, 0, 0);
     if (kt + 1 < nk) {
       store_tile<AK, BK, BM>(As[cur ^ 1], ra);
       store_tile<BKC, BK, BN>(Bs[cur ^ 1], rb);
@@ -273,16 +290,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
 // ---------------------------------------------------------------- complex products (float32)
 // Block tile 128 rows x 64 complex columns of 8 waves (4 along M x 2 along N),
 // each wave 32x32 complex outputs with three accumulators (P1, P2, P3 of the
-// three-product form); K tile 16; a, b, c, d staged as four LDS tiles in the
-// layout of the real kernel, the sums a + sA b and c + sB d formed from the
-// fragments in registers. 64 KB of LDS for two stages: two blocks per CU.
-// Measured on MI355X at the per-order shapes (725k rows): 1.17-1.26x faster
-// than the realified product with four real products.
+// three-product form); K tile 16; a, b, c, d staged as four LDS tiles, the
+// sums a + sA b and c + sB d formed from the fragments in registers. 64 KB of
+// LDS for two stages: two blocks per CU. Measured on MI355X at the per-order
+// shapes (725k rows): 1.17-1.26x faster than the realified product with four
+// real products.
+//
+// The sum over k does not depend on which k each MFMA step takes, so step s
+// (0..7) of lane half lk takes k = 8 lk + s in both operands: a lane's eight
+// values of a k-contiguous tile are adjacent and arrive in two 128-bit LDS
+// reads (pitch 20 dwords: any 16 rows start on distinct 4-bank groups). A
+// k-major tile is read one value per step at pitch R + 4, which puts the two
+// lane halves (8 rows apart) on disjoint banks.
 constexpr int CBM = 128, CBN = 64, CBK = 16, CNT = 512;
 template <bool KCONTIG, int R>
 struct CT {
   static constexpr int PK = CBK + 4;
-  static constexpr int PW = R + 32;
+  static constexpr int PW = R + 4;
   static constexpr int FL = KCONTIG ? R * PK : CBK * PW;
   static constexpr int V4 = R * CBK / 4;
   static constexpr int NL = (V4 + CNT - 1) / CNT;
@@ -338,16 +362,61 @@ __device__ inline void cstore(float* __restrict__ S, const floatx4 (&v)[CT<KCONT
     }
   }
 }
+// The eight values of one K tile that lane half lk feeds its MFMA steps with:
+// row `row`, k = 8 lk + s.
 template <bool KCONTIG, int R>
-__device__ __forceinline__ float cfrag(const float* S, int row, int k) {
-  return KCONTIG ? S[row * CT<KCONTIG, R>::PK + k] : S[k * CT<KCONTIG, R>::PW + row];
+__device__ __forceinline__ void cfrag(const float* S, int row, int lk, float (&f)[CBK / 2]) {
+  if (KCONTIG) {
+    const floatx4* q = reinterpret_cast<const floatx4*>(S + row * CT<KCONTIG, R>::PK + 8 * lk);
+    const floatx4 u = q[0], w = q[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f[c] = u[c];
+      f[4 + c] = w[c];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < CBK / 2; ++s) f[s] = S[(8 * lk + s) * CT<KCONTIG, R>::PW + row];
+  }
+}
+
+// epilogue: Re = P1 - sig P2 to C, Im = P3 - P1 - sig P2 N columns right (sig = sA sB)
+__device__ inline void cplx_store(const GemmProb& p, int split, int m0, int n0, int wm, int wn, int li, int lk,
+                                  float sig, const floatx16& acc1, const floatx16& acc2, const floatx16& acc3) {
+  float* out;
+  int ldo;
+  bool acc_in;
+  if (p.partial) {
+    out = p.C + (size_t)split * p.M * 2 * p.N;
+    ldo = 2 * p.N;
+    acc_in = false;
+  } else {
+    out = p.C;
+    ldo = p.ldc;
+    acc_in = p.accumulate != 0;
+  }
+  const int j = n0 + wn * 32 + li;
+  if (j < p.N) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = m0 + wm * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
+      if (i < p.M) {
+        const float t2 = sig * acc2[r];
+        const float re = acc1[r] - t2, im = acc3[r] - acc1[r] - t2;
+        float* d0 = out + (size_t)i * ldo + j;
+        float* d1 = d0 + p.N;
+        *d0 = acc_in ? *d0 + re : re;
+        *d1 = acc_in ? *d1 + im : im;
+      }
+    }
+  }
 }
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_cplx_kernel(GemmBatch batch) {
   constexpr bool AK = !TA, BKC = TB;
-  __shared__ float Aa[2][CT<AK, CBM>::FL], Ab[2][CT<AK, CBM>::FL];
-  __shared__ float Bc[2][CT<BKC, CBN>::FL], Bd[2][CT<BKC, CBN>::FL];
+  __shared__ __attribute__((aligned(16))) float Aa[2][CT<AK, CBM>::FL], Ab[2][CT<AK, CBM>::FL];
+  __shared__ __attribute__((aligned(16))) float Bc[2][CT<BKC, CBN>::FL], Bd[2][CT<BKC, CBN>::FL];
   int pi, local;
   decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
   const GemmProb& p = batch.p[pi];
@@ -391,46 +460,263 @@ __global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load(kbeg + (kt + 1) * CBK);
+    float fa[CBK / 2], fb[CBK / 2], fc[CBK / 2], fd[CBK / 2];
+    cfrag<AK, CBM>(Aa[cur], ar, lk, fa);
+    cfrag<AK, CBM>(Ab[cur], ar, lk, fb);
+    cfrag<BKC, CBN>(Bc[cur], br, lk, fc);
+    cfrag<BKC, CBN>(Bd[cur], br, lk, fd);
 #pragma unroll
-    for (int kk = 0; kk < CBK; kk += 2) {
-      const float fa = cfrag<AK, CBM>(Aa[cur], ar, kk + lk), fb = cfrag<AK, CBM>(Ab[cur], ar, kk + lk);
-      const float fc = cfrag<BKC, CBN>(Bc[cur], br, kk + lk), fd = cfrag<BKC, CBN>(Bd[cur], br, kk + lk);
-      const float fs = fa + sA * fb, fw = fc + sB * fd;
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, fc, acc1, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(fb, fd, acc2, 0, 0, 0);
+    for (int s = 0; s < CBK / 2; ++s) {
+      const float fs = fa[s] + sA * fb[s], fw = fc[s] + sB * fd[s];
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s], fc[s], acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[s], fd[s], acc2, 0, 0, 0);
       acc3 = __builtin_amdgcn_mfma_f32_32x32x2f32(fs, fw, acc3, 0, 0, 0);
     }
     if (kt + 1 < nk) store(cur ^ 1);
     __syncthreads();
   }
-  const float sig = sA * sB;
-  float* out;
-  int ldo;
-  bool acc_in;
-  if (p.partial) {
-    out = p.C + (size_t)split * p.M * 2 * p.N;
-    ldo = 2 * p.N;
-    acc_in = false;
+  cplx_store(p, split, m0, n0, wm, wn, li, lk, sA * sB, acc1, acc2, acc3);
+}
+
+// ---------------------------------------------------------------- direct-to-LDS staging (float32)
+// gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from global memory
+// straight into LDS: lane l writes bytes [16 l, 16 l + 16) of a 1 KB block
+// with a wave-uniform base, from any per-lane address. The kernels below build
+// their 16-k operand tiles from such blocks in a ring of three stages: the
+// loads of k tile t + 2 are in flight while tile t is multiplied, with no
+// register staging and no LDS store instructions (measured on MI355X at the
+// per-order shapes, 725k rows: 5-6% faster than the register-staged kernels
+// above, which remain for operands without 16-byte alignment).
+//
+// The lane -> element map of a block is free, which gives the tile layouts:
+//   k-contiguous tile (R rows x 16 k): block b holds rows 16b .. 16b+15; lane
+//     l carries k chunk q = l/16 (four k) of row 16b + l%16, so chunk q of a
+//     row sits at 16q + row%16 (16-byte units). A fragment read (16 rows, one
+//     chunk) covers 256 contiguous bytes.
+//   k-major tile (16 k x R columns): block b holds k rows b KPB .. b KPB +
+//     KPB-1 (KPB = 256/R) at R floats apart, and blocks sit BLK = 256 + 1024/R
+//     floats apart, so k and k + 8 (the two lane halves of a read) are 32
+//     banks apart ((8/KPB) BLK = 32 mod 64).
+// Every wave issues three loads per stage, so a wave's vmcnt tells when its
+// part of a stage has landed, and a barrier after that wait publishes the
+// stage. A tile that runs past the end of K (the last of a split) is staged
+// through registers, zero-filled, into the same positions. Rows (columns)
+// past the operand's edge load the last valid row (column chunk) instead:
+// they only reach outputs that are not stored.
+constexpr int DNS = 3;   // stages
+template <bool KCONTIG, int R>
+struct DT {
+  static constexpr int NB = R / 16;                     // 1 KB blocks per tile
+  static constexpr int KPB = 256 / R;                   // k-major: k rows per block
+  static constexpr int BLK = KCONTIG ? 256 : 256 + 1024 / R;
+  static constexpr int FL = NB * BLK;                   // floats per tile
+};
+struct DSlot {
+  const float* src;   // this lane's 16 bytes in the split's first k tile
+  long step;          // elements between consecutive k tiles
+  int dst;            // block offset within a stage (floats)
+  int kofs;           // k of this lane's data within a tile (first of four if k-contiguous)
+  int kc;             // k-contiguous data
+};
+template <bool KCONTIG, int R>
+__device__ inline DSlot dslot(int b, const float* P, int ld, int r0, int rlim, int kbeg, int lane, int base) {
+  DSlot d;
+  if (KCONTIG) {
+    const int row = min(r0 + 16 * b + lane % 16, rlim - 1), q = lane / 16;
+    d.src = P + (size_t)row * ld + kbeg + 4 * q;
+    d.step = 16;
+    d.kofs = 4 * q;
+    d.kc = 1;
+    d.dst = base + b * 256;
   } else {
-    out = p.C;
-    ldo = p.ldc;
-    acc_in = p.accumulate != 0;
+    constexpr int LPR = R / 4;
+    const int k = b * DT<false, R>::KPB + lane / LPR, col = min(r0 + 4 * (lane % LPR), rlim - 4);
+    d.src = P + (size_t)(kbeg + k) * ld + col;
+    d.step = 16L * ld;
+    d.kofs = k;
+    d.kc = 0;
+    d.dst = base + b * DT<false, R>::BLK;
   }
-  const int j = n0 + wn * 32 + li;
-  if (j < p.N) {
+  return d;
+}
+__device__ __forceinline__ void dma16(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+// stage k tile t (of a split holding nkk k values) into st
+__device__ inline void dstage(const DSlot (&sl)[3], float* st, int t, int nkk, int lane) {
+  const int k0 = 16 * t;
+  if (k0 + 16 <= nkk) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = m0 + wm * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
-      if (i < p.M) {
-        const float t2 = sig * acc2[r];
-        const float re = acc1[r] - t2, im = acc3[r] - acc1[r] - t2;
-        float* d0 = out + (size_t)i * ldo + j;
-        float* d1 = d0 + p.N;
-        *d0 = acc_in ? *d0 + re : re;
-        *d1 = acc_in ? *d1 + im : im;
+    for (int j = 0; j < 3; ++j) dma16(sl[j].src + t * sl[j].step, st + sl[j].dst);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const float* q = sl[j].src + t * sl[j].step;
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+      if (sl[j].kc) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (k0 + sl[j].kofs + c < nkk) x[c] = q[c];
+      } else if (k0 + sl[j].kofs < nkk) {
+        x = *reinterpret_cast<const floatx4*>(q);
       }
+      *reinterpret_cast<floatx4*>(st + sl[j].dst + 4 * lane) = x;
     }
   }
+}
+// wait until this wave's loads of tile t have landed (those of tile t + 1,
+// if issued, may still be in flight) and publish the stage to the block
+__device__ __forceinline__ void dsync(bool next_in_flight) {
+  if (next_in_flight) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// MFMA operands of one staged tile for lane half lk: row `row`, k = 8 lk + s
+template <bool KCONTIG, int R>
+__device__ __forceinline__ void dfrag(const float* T, int row, int lk, float (&f)[8]) {
+  if (KCONTIG) {
+    const float* q = T + (row / 16) * 256 + (row % 16) * 4 + 128 * lk;
+    const floatx4 u = *reinterpret_cast<const floatx4*>(q);
+    const floatx4 w = *reinterpret_cast<const floatx4*>(q + 64);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f[c] = u[c];
+      f[4 + c] = w[c];
+    }
+  } else {
+    using D = DT<false, R>;
+    const float* q = T + lk * (8 / D::KPB) * D::BLK + row;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = q[(s / D::KPB) * D::BLK + (s % D::KPB) * R];
+  }
+}
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, 8))) void gemm_f32_dma_kernel(
+    GemmBatch batch) {
+  constexpr bool AK = !TA, BKC = TB;
+  using DA = DT<AK, BM>;
+  using DB = DT<BKC, BN>;
+  static_assert(DA::NB + DB::NB == 3 * (NT / 64), "three loads per wave and stage");
+  constexpr int STG = DA::FL + DB::FL;
+  __shared__ __attribute__((aligned(16))) float S[DNS * STG];
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
+  const int nkk = kend - kbeg, nk = (nkk + 15) / 16;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave / 2, wn = wave % 2, li = lane % 32, lk = lane / 32;
+  DSlot sl[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int g = 3 * wave + j;
+    sl[j] = g < DA::NB ? dslot<AK, BM>(g, static_cast<const float*>(p.A), p.lda, m0, p.M, kbeg, lane, 0)
+                       : dslot<BKC, BN>(g - DA::NB, static_cast<const float*>(p.B), p.ldb, n0, p.N, kbeg, lane, DA::FL);
+  }
+  floatx16 acc[WM][WN];
+#pragma unroll
+  for (int a = 0; a < WM; ++a)
+#pragma unroll
+    for (int b = 0; b < WN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  if (nk > 0) dstage(sl, S, 0, nkk, lane);
+  if (nk > 1) dstage(sl, S + STG, 1, nkk, lane);
+  const int ra0 = wm * 32 * WM + li, rb0 = wn * 32 * WN + li;
+  int cur = 0;
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    dsync(kt + 1 < nk);
+    if (kt + 2 < nk) dstage(sl, S + (cur == 0 ? 2 : cur - 1) * STG, kt + 2, nkk, lane);
+    const float* st = S + cur * STG;
+    float av[WM][8], bv[WN][8];
+#pragma unroll
+    for (int a = 0; a < WM; ++a) dfrag<AK, BM>(st, ra0 + 32 * a, lk, av[a]);
+#pragma unroll
+    for (int b = 0; b < WN; ++b) dfrag<BKC, BN>(st + DA::FL, rb0 + 32 * b, lk, bv[b]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][s], bv[b][s], acc[a][b], 0, 0, 0);
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  store_acc(p, split, m0, n0, wm, wn, li, lk, acc);
+}
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_cplx_dma_kernel(GemmBatch batch) {
+  constexpr bool AK = !TA, BKC = TB;
+  using DA = DT<AK, CBM>;
+  using DB = DT<BKC, CBN>;
+  static_assert(2 * DA::NB + 2 * DB::NB == 3 * (CNT / 64), "three loads per wave and stage");
+  constexpr int STG = 2 * DA::FL + 2 * DB::FL;
+  __shared__ __attribute__((aligned(16))) float S[DNS * STG];
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * CBM, n0 = tn * CBN;
+  const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
+  const int nkk = kend - kbeg, nk = (nkk + 15) / 16;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave / 2, wn = wave % 2, li = lane % 32, lk = lane / 32;
+  const float* A0 = static_cast<const float*>(p.A);
+  const float* B0 = static_cast<const float*>(p.B);
+  DSlot sl[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int g = 3 * wave + j;
+    if (g < 2 * DA::NB) {
+      const int part = g / DA::NB;
+      sl[j] = dslot<AK, CBM>(g - part * DA::NB, A0 + (part ? p.dA : 0), p.lda, m0, p.M, kbeg, lane, part * DA::FL);
+    } else {
+      const int h = g - 2 * DA::NB, part = h / DB::NB;
+      sl[j] = dslot<BKC, CBN>(h - part * DB::NB, B0 + (part ? p.dB : 0), p.ldb, n0, p.N, kbeg, lane,
+                              2 * DA::FL + part * DB::FL);
+    }
+  }
+  floatx16 acc1, acc2, acc3;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc1[r] = acc2[r] = acc3[r] = 0.f;
+  const float sA = p.sA, sB = p.sB;
+  if (nk > 0) dstage(sl, S, 0, nkk, lane);
+  if (nk > 1) dstage(sl, S + STG, 1, nkk, lane);
+  const int ar = wm * 32 + li, br = wn * 32 + li;
+  int cur = 0;
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    dsync(kt + 1 < nk);
+    if (kt + 2 < nk) dstage(sl, S + (cur == 0 ? 2 : cur - 1) * STG, kt + 2, nkk, lane);
+    const float* st = S + cur * STG;
+    float fa[8], fb[8], fc[8], fd[8];
+    dfrag<AK, CBM>(st, ar, lk, fa);
+    dfrag<AK, CBM>(st + DA::FL, ar, lk, fb);
+    dfrag<BKC, CBN>(st + 2 * DA::FL, br, lk, fc);
+    dfrag<BKC, CBN>(st + 2 * DA::FL + DB::FL, br, lk, fd);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float fs = fa[s] + sA * fb[s], fw = fc[s] + sB * fd[s];
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s], fc[s], acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[s], fd[s], acc2, 0, 0, 0);
+      acc3 = __builtin_amdgcn_mfma_f32_32x32x2f32(fs, fw, acc3, 0, 0, 0);
+    }
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  cplx_store(p, split, m0, n0, wm, wn, li, lk, sA * sB, acc1, acc2, acc3);
 }
 
 // ---------------------------------------------------------------- bfloat16 operands
@@ -647,6 +933,21 @@ __global__ void gemm_reduce_kernel(const float* __restrict__ P, int splits, int 
   }
 }
 
+// direct-to-LDS kernels: every operand 16-byte aligned, leading dimensions
+// (and complex part offsets) multiples of four elements, and the dimension a
+// k-major operand's chunks run along a multiple of four
+bool dma_ok(const GemmBatch& b, bool TA, bool TB) {
+  for (int q = 0; q < b.nprob; ++q) {
+    const GemmProb& p = b.p[q];
+    if (p.M <= 0 || p.N <= 0) continue;
+    if ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) % 16) return false;
+    if (p.lda % 4 || p.ldb % 4) return false;
+    if (p.cplx && (p.dA % 4 || p.dB % 4)) return false;
+    if ((TA && p.M % 4) || (!TB && p.N % 4)) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
@@ -670,6 +971,22 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
   dim3 grid(total), block(NT);
+  if (!bf16 && dma_ok(b, TA, TB)) {
+    if (cx) {
+      if (!TA && !TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, false>), grid, dim3(CNT), 0, s, b);
+      else if (!TA && TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, true>), grid, dim3(CNT), 0, s, b);
+      else hipLaunchKernelGGL((gemm_cplx_dma_kernel<true, false>), grid, dim3(CNT), 0, s, b);
+    } else if (!TA && !TB) {
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, false>), grid, block, 0, s, b);
+    } else if (!TA && TB) {
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, true>), grid, block, 0, s, b);
+    } else if (TA && !TB) {
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<true, false>), grid, block, 0, s, b);
+    } else {
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<true, true>), grid, block, 0, s, b);
+    }
+    return hipGetLastError();
+  }
   if (cx) {
     if (!TA && !TB) hipLaunchKernelGGL((gemm_cplx_kernel<false, false>), grid, dim3(CNT), 0, s, b);
     else if (!TA && TB) hipLaunchKernelGGL((gemm_cplx_kernel<false, true>), grid, dim3(CNT), 0, s, b);
