@@ -341,7 +341,7 @@ def main():
     achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_BF16_MFMA_TFLOPS if dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     kname = ("gemm_bf16_kernel (bf16 MFMA per-order linears)" if dtype == "bf16" else
-             "gemm_f32_kernel (order 0) and gemm_cplx_kernel (orders >= 1, three real products per complex "
+             "gemm_f32_dma_kernel (order 0) and gemm_cplx_dma_kernel (orders >= 1, three real products per complex "
              "one; fp32 MFMA)") + ", all launches of the timed steps"
     out = {
         "metric": METRIC,

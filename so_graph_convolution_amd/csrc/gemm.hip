@@ -503,7 +503,9 @@ __global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 // through registers, zero-filled, into the same positions. Rows (columns)
 // past the operand's edge load the last valid row (column chunk) instead:
 // they only reach outputs that are not stored.
-constexpr int DNS = 3;   // stages
+constexpr int DNS = 3;       // stages
+constexpr int kF32WNW = 2;   // float32 blocks: 256 x 64 kF32WNW
+constexpr int kCxWNW = 2;    // complex blocks: 128 x 32 kCxWNW complex
 template <bool KCONTIG, int R>
 struct DT {
   static constexpr int NB = R / 16;                     // 1 KB blocks per tile
@@ -544,14 +546,15 @@ __device__ __forceinline__ void dma16(const float* src, float* dst) {
                                    (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 // stage k tile t (of a split holding nkk k values) into st
-__device__ inline void dstage(const DSlot (&sl)[3], float* st, int t, int nkk, int lane) {
+template <int SL>
+__device__ inline void dstage(const DSlot (&sl)[SL], float* st, int t, int nkk, int lane) {
   const int k0 = 16 * t;
   if (k0 + 16 <= nkk) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) dma16(sl[j].src + t * sl[j].step, st + sl[j].dst);
+    for (int j = 0; j < SL; ++j) dma16(sl[j].src + t * sl[j].step, st + sl[j].dst);
   } else {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < SL; ++j) {
       const float* q = sl[j].src + t * sl[j].step;
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
       if (sl[j].kc) {
@@ -565,11 +568,14 @@ __device__ inline void dstage(const DSlot (&sl)[3], float* st, int t, int nkk, i
     }
   }
 }
-// wait until this wave's loads of tile t have landed (those of tile t + 1,
-// if issued, may still be in flight) and publish the stage to the block
+// wait until this wave's loads of tile t have landed (the SL loads of tile
+// t + 1, if issued, may still be in flight) and publish the stage to the block
+template <int SL>
 __device__ __forceinline__ void dsync(bool next_in_flight) {
-  if (next_in_flight) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  static_assert(SL == 2 || SL == 3, "loads per wave and stage");
+  if (!next_in_flight) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  else if (SL == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -593,13 +599,16 @@ __device__ __forceinline__ void dfrag(const float* T, int row, int lk, float (&f
   }
 }
 
-template <bool TA, bool TB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, 8))) void gemm_f32_dma_kernel(
-    GemmBatch batch) {
+// WNW waves along N (64 columns each), WAVES_M along M
+template <bool TA, bool TB, int WNW>
+__global__ __launch_bounds__(64 * WAVES_M * WNW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, 8))) void
+gemm_f32_dma_kernel(GemmBatch batch) {
   constexpr bool AK = !TA, BKC = TB;
+  constexpr int BNW = 64 * WNW, NWV = WAVES_M * WNW;
   using DA = DT<AK, BM>;
-  using DB = DT<BKC, BN>;
-  static_assert(DA::NB + DB::NB == 3 * (NT / 64), "three loads per wave and stage");
+  using DB = DT<BKC, BNW>;
+  constexpr int SL = (DA::NB + DB::NB) / NWV;
+  static_assert(SL * NWV == DA::NB + DB::NB, "equal loads per wave and stage");
   constexpr int STG = DA::FL + DB::FL;
   __shared__ __attribute__((aligned(16))) float S[DNS * STG];
   int pi, local;
@@ -609,17 +618,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   const int split = local / per_split;
   local -= split * per_split;
   const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BNW;
   const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
   const int nkk = kend - kbeg, nk = (nkk + 15) / 16;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int wm = wave / 2, wn = wave % 2, li = lane % 32, lk = lane / 32;
-  DSlot sl[3];
+  const int wm = wave / WNW, wn = wave % WNW, li = lane % 32, lk = lane / 32;
+  DSlot sl[SL];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int g = 3 * wave + j;
+  for (int j = 0; j < SL; ++j) {
+    const int g = SL * wave + j;
     sl[j] = g < DA::NB ? dslot<AK, BM>(g, static_cast<const float*>(p.A), p.lda, m0, p.M, kbeg, lane, 0)
-                       : dslot<BKC, BN>(g - DA::NB, static_cast<const float*>(p.B), p.ldb, n0, p.N, kbeg, lane, DA::FL);
+                       : dslot<BKC, BNW>(g - DA::NB, static_cast<const float*>(p.B), p.ldb, n0, p.N, kbeg, lane, DA::FL);
   }
   floatx16 acc[WM][WN];
 #pragma unroll
@@ -634,14 +643,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   int cur = 0;
 #pragma unroll 1
   for (int kt = 0; kt < nk; ++kt) {
-    dsync(kt + 1 < nk);
+    dsync<SL>(kt + 1 < nk);
     if (kt + 2 < nk) dstage(sl, S + (cur == 0 ? 2 : cur - 1) * STG, kt + 2, nkk, lane);
     const float* st = S + cur * STG;
     float av[WM][8], bv[WN][8];
 #pragma unroll
     for (int a = 0; a < WM; ++a) dfrag<AK, BM>(st, ra0 + 32 * a, lk, av[a]);
 #pragma unroll
-    for (int b = 0; b < WN; ++b) dfrag<BKC, BN>(st + DA::FL, rb0 + 32 * b, lk, bv[b]);
+    for (int b = 0; b < WN; ++b) dfrag<BKC, BNW>(st + DA::FL, rb0 + 32 * b, lk, bv[b]);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
@@ -654,12 +663,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SI
   store_acc(p, split, m0, n0, wm, wn, li, lk, acc);
 }
 
-template <bool TA, bool TB>
-__global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_cplx_dma_kernel(GemmBatch batch) {
+// WNW waves along N (32 complex columns each), 4 along M
+template <bool TA, bool TB, int WNW>
+__global__ __launch_bounds__(256 * WNW) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_cplx_dma_kernel(
+    GemmBatch batch) {
   constexpr bool AK = !TA, BKC = TB;
+  constexpr int BNW = 32 * WNW, NWV = 4 * WNW;
   using DA = DT<AK, CBM>;
-  using DB = DT<BKC, CBN>;
-  static_assert(2 * DA::NB + 2 * DB::NB == 3 * (CNT / 64), "three loads per wave and stage");
+  using DB = DT<BKC, BNW>;
+  constexpr int SL = (2 * DA::NB + 2 * DB::NB) / NWV;
+  static_assert(SL * NWV == 2 * DA::NB + 2 * DB::NB, "equal loads per wave and stage");
   constexpr int STG = 2 * DA::FL + 2 * DB::FL;
   __shared__ __attribute__((aligned(16))) float S[DNS * STG];
   int pi, local;
@@ -669,23 +682,23 @@ __global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int split = local / per_split;
   local -= split * per_split;
   const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
-  const int m0 = tm * CBM, n0 = tn * CBN;
+  const int m0 = tm * CBM, n0 = tn * BNW;
   const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
   const int nkk = kend - kbeg, nk = (nkk + 15) / 16;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int wm = wave / 2, wn = wave % 2, li = lane % 32, lk = lane / 32;
+  const int wm = wave / WNW, wn = wave % WNW, li = lane % 32, lk = lane / 32;
   const float* A0 = static_cast<const float*>(p.A);
   const float* B0 = static_cast<const float*>(p.B);
-  DSlot sl[3];
+  DSlot sl[SL];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int g = 3 * wave + j;
+  for (int j = 0; j < SL; ++j) {
+    const int g = SL * wave + j;
     if (g < 2 * DA::NB) {
       const int part = g / DA::NB;
       sl[j] = dslot<AK, CBM>(g - part * DA::NB, A0 + (part ? p.dA : 0), p.lda, m0, p.M, kbeg, lane, part * DA::FL);
     } else {
       const int h = g - 2 * DA::NB, part = h / DB::NB;
-      sl[j] = dslot<BKC, CBN>(h - part * DB::NB, B0 + (part ? p.dB : 0), p.ldb, n0, p.N, kbeg, lane,
+      sl[j] = dslot<BKC, BNW>(h - part * DB::NB, B0 + (part ? p.dB : 0), p.ldb, n0, p.N, kbeg, lane,
                               2 * DA::FL + part * DB::FL);
     }
   }
@@ -699,14 +712,14 @@ __global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   int cur = 0;
 #pragma unroll 1
   for (int kt = 0; kt < nk; ++kt) {
-    dsync(kt + 1 < nk);
+    dsync<SL>(kt + 1 < nk);
     if (kt + 2 < nk) dstage(sl, S + (cur == 0 ? 2 : cur - 1) * STG, kt + 2, nkk, lane);
     const float* st = S + cur * STG;
     float fa[8], fb[8], fc[8], fd[8];
     dfrag<AK, CBM>(st, ar, lk, fa);
     dfrag<AK, CBM>(st + DA::FL, ar, lk, fb);
-    dfrag<BKC, CBN>(st + 2 * DA::FL, br, lk, fc);
-    dfrag<BKC, CBN>(st + 2 * DA::FL + DB::FL, br, lk, fd);
+    dfrag<BKC, BNW>(st + 2 * DA::FL, br, lk, fc);
+    dfrag<BKC, BNW>(st + 2 * DA::FL + DB::FL, br, lk, fd);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const float fs = fa[s] + sA * fb[s], fw = fc[s] + sB * fd[s];
@@ -957,7 +970,9 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   if (cx && (bf16 || (TA && TB))) return hipErrorInvalidValue;
   for (int q = 0; q < b.nprob; ++q)
     if ((b.p[q].cplx != 0) != cx) return hipErrorInvalidValue;
-  const int bm = cx ? CBM : (bf16 ? BMH : BM), bn = cx ? CBN : (bf16 ? BNH : BN);
+  const bool dma = !bf16 && dma_ok(b, TA, TB);
+  const int bm = cx ? CBM : (bf16 ? BMH : BM);
+  const int bn = cx ? (dma ? 32 * kCxWNW : CBN) : (bf16 ? BNH : (dma ? 64 * kF32WNW : BN));
   int total = 0;
   for (int q = 0; q < b.nprob; ++q) {
     GemmProb& p = b.p[q];
@@ -971,19 +986,21 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
   dim3 grid(total), block(NT);
-  if (!bf16 && dma_ok(b, TA, TB)) {
+  if (dma) {
+    constexpr int W = kF32WNW, CW = kCxWNW;
+    const dim3 fb(64 * WAVES_M * W), cb(256 * CW);
     if (cx) {
-      if (!TA && !TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, false>), grid, dim3(CNT), 0, s, b);
-      else if (!TA && TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, true>), grid, dim3(CNT), 0, s, b);
-      else hipLaunchKernelGGL((gemm_cplx_dma_kernel<true, false>), grid, dim3(CNT), 0, s, b);
+      if (!TA && !TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, false, CW>), grid, cb, 0, s, b);
+      else if (!TA && TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, true, CW>), grid, cb, 0, s, b);
+      else hipLaunchKernelGGL((gemm_cplx_dma_kernel<true, false, CW>), grid, cb, 0, s, b);
     } else if (!TA && !TB) {
-      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, false>), grid, block, 0, s, b);
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, false, W>), grid, fb, 0, s, b);
     } else if (!TA && TB) {
-      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, true>), grid, block, 0, s, b);
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, true, W>), grid, fb, 0, s, b);
     } else if (TA && !TB) {
-      hipLaunchKernelGGL((gemm_f32_dma_kernel<true, false>), grid, block, 0, s, b);
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<true, false, W>), grid, fb, 0, s, b);
     } else {
-      hipLaunchKernelGGL((gemm_f32_dma_kernel<true, true>), grid, block, 0, s, b);
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<true, true, W>), grid, fb, 0, s, b);
     }
     return hipGetLastError();
   }
