@@ -27,11 +27,16 @@ int upload_generators_bwd(const float* host) { return upload_generators_here(hos
 namespace {
 
 // edges per LDS tile so that the tile state stays below 48 KB
-template <int L, int M, int EXTRA>
+template <int L, int M, int EXTRA, int BYTES = 48 * 1024>
 constexpr int tile_edges() {
   constexpr int per = 9 + k_count(L, M) + 2 * wig_stride_c(L, M) + EXTRA + 16;
-  return (32 * per * 4 <= 48 * 1024) ? 32 : (16 * per * 4 <= 48 * 1024) ? 16 : (8 * per * 4 <= 48 * 1024) ? 8 : 4;
+  return (32 * per * 4 <= BYTES) ? 32 : (16 * per * 4 <= BYTES) ? 16 : (8 * per * 4 <= BYTES) ? 8 : 4;
 }
+// LDS budget of an edge kernel's tile. Its blocks hold one tile each, and
+// LDS bounds how many run per CU: smaller tiles, more blocks in flight to
+// hide the per-edge gathers. Measured on MI355X at lmax 4, C 128 (725k edges):
+// edge_bwd 9.6 -> 5.7 ms with 24 KB instead of 48 KB.
+constexpr int kEdgeTileBytes = 24 * 1024;
 
 __device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
@@ -46,7 +51,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
                                                        const float* __restrict__ env, OT* __restrict__ tbar,
                                                        float* __restrict__ tau, float* __restrict__ genv) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
+  constexpr int TE = tile_edges<L, M, 3 * k_count(L, M), kEdgeTileBytes>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
@@ -136,7 +141,7 @@ template <int L, int M>
 struct EdgeBwd {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V,
                  const float* env, void* tbar, float* tau, float* genv, int bf16, hipStream_t s) {
-    constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
+    constexpr int TE = tile_edges<L, M, 3 * k_count(L, M), kEdgeTileBytes>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
