@@ -66,6 +66,25 @@ void compute_generators(float* out) {
   }
 }
 
+// the kernels apply the generators through two candidate orders per row and
+// per column (gen_cand); a table entry outside them would be dropped
+bool generators_sparse(const float* table) {
+  for (int k = 0; k < 3; ++k)
+    for (int l = 1; l <= kMaxL; ++l) {
+      const int n = 2 * l + 1;
+      const float* G = table + k * kGenSize + gen_off(l);
+      for (int i = -l; i <= l; ++i)
+        for (int c = -l; c <= l; ++c) {
+          if (G[(i + l) * n + c + l] == 0.f) continue;
+          int a0, a1, b0, b1;
+          gen_cand(k, i, &a0, &a1);   // row i
+          gen_cand(k, c, &b0, &b1);   // column c
+          if ((c != a0 && c != a1) || (i != b0 && i != b1)) return false;
+        }
+    }
+  return true;
+}
+
 std::mutex g_init_mu;
 bool g_init_done[64];
 
@@ -79,6 +98,8 @@ int ensure_init() {
   static bool have = false;
   if (!have) {
     compute_generators(table);
+    if (!generators_sparse(table))
+      return fail(SO2_EUNSUPPORTED, "so(3) generator table outside the two-candidate pattern the kernels use");
     have = true;
   }
   SO2_HIP(upload_generators_fwd(table));

@@ -51,17 +51,18 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
                                                        const float* __restrict__ env, OT* __restrict__ tbar,
                                                        float* __restrict__ tau, float* __restrict__ genv) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, 3 * k_count(L, M), kEdgeTileBytes>();
+  constexpr int TE = tile_edges<L, M, 0, kEdgeTileBytes>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
-  __shared__ float sRL[TE * 3 * K];
   __shared__ float sRed[TE * 4 * 4];
   __shared__ float sHead[TE * kMaxHeads];
   __shared__ int sDst[TE];
+  __shared__ float sG[3 * gen_off(L + 1)];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
   const int ne = (int)min((long)TE, g.e1 - e0);
+  gen_stage<L>(sG);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int i = g.dst[e];
@@ -70,7 +71,6 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   }
   __syncthreads();
   wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
-  rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
   __syncthreads();
   const int H = d.H, head = c_head(d, threadIdx.x);
 
@@ -104,13 +104,16 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
 #pragma unroll
         for (int m = -q; m <= q; ++m) st(tr + mm_col(l, m, 0, L, C), ev * o[ridx(l, m, M)]);
       }
+      // torque: <v, (R G_k) gy> taken as <G_k^T u, gy> with u = R^T v
+      float u[D];
+#pragma unroll
+      for (int r = 0; r < D; ++r) u[r] = 0.f;
+      rot_bwd_acc<L, M>(sR + t * K, vv, u);
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
-        float w[Q];
-        rot_fwd<L, M>(sRL + t * 3 * K + k * K, gv, w);
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < Q; ++j) s += vv[j] * w[j];
+        for (int l = 1; l <= L; ++l) s += gen_form<L>(sG, k, l, u + l * l, gv + l * l);
         tk[k] = ev * s;
       }
 #pragma unroll
@@ -141,7 +144,7 @@ template <int L, int M>
 struct EdgeBwd {
   static int run(const Dims& d, const GraphDev& g, const float* pos, const float* gy, const float* V,
                  const float* env, void* tbar, float* tau, float* genv, int bf16, hipStream_t s) {
-    constexpr int TE = tile_edges<L, M, 3 * k_count(L, M), kEdgeTileBytes>();
+    constexpr int TE = tile_edges<L, M, 0, kEdgeTileBytes>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     if (nb <= 0) return hipSuccess;
     const int threads = ((d.C + 63) / 64) * 64;
@@ -156,13 +159,14 @@ struct EdgeBwd {
 };
 
 // ------------------------------------------------------------------ node_bwd
+// The torque terms sum_rows xb <(R G_k)_row, x_n> of a degree are taken as
+// <G_k^T y, x_n> with y = R^T xb, the edge's contribution to acc.
 template <int L, int M>
-__device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, RotPtr sRLt,
+__device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, RotPtr sG,
                                                    const float (&xn)[(L + 1) * (L + 1)],
                                                    const float* __restrict__ S, const float* __restrict__ Tbar,
                                                    float* __restrict__ Sbar, long e, int cin,
                                                    float (&acc)[(L + 1) * (L + 1)], float (&tk)[3]) {
-  constexpr int K = k_count(L, M);
   const int Ci = 2 * d.C, wT = d.wT(), wS = (L + 1) * Ci;
   const float* tb = Tbar + (size_t)e * wT + cin;
   const float* sr = S + (size_t)e * wS + cin;
@@ -178,7 +182,9 @@ __device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, Ro
 #pragma unroll
     for (int m = -q; m <= q; ++m) tv[m + q] = tb[mm_col(l, m, 0, L, Ci)];
     const float sc = sr[l * Ci];
-    float sacc = 0.f;
+    float sacc = 0.f, y[2 * L + 1];
+#pragma unroll
+    for (int i = 0; i < 2 * L + 1; ++i) y[i] = 0.f;
 #pragma unroll
     for (int m = -q; m <= q; ++m) {
       const int off = rot_off(l, M) + (m + q) * n;
@@ -187,14 +193,14 @@ __device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, Ro
       float r[2 * L + 1];
       load_row<L>(sRt, off, n, r);
       sacc += v * row_dot<L>(r, xn + l * l, n);
-      row_axpy<L>(r, xb, acc + l * l, n);
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        float g[2 * L + 1];
-        load_row<L>(sRLt + k * K, off, n, g);
-        tk[k] += xb * row_dot<L>(g, xn + l * l, n);
-      }
+      row_axpy<L>(r, xb, y, n);
     }
+#pragma unroll
+    for (int i = 0; i < 2 * L + 1; ++i)
+      if (i < n) acc[l * l + i] += y[i];
+    if (l > 0)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) tk[k] += gen_form<L>(sG, k, l, y, xn + l * l);
     sb[l * Ci] = sacc;
   }
 }
@@ -206,16 +212,17 @@ __global__ __launch_bounds__(512) void node_bwd_kernel(Dims d, GraphDev g, const
                                                        float* __restrict__ Sbar, float* __restrict__ tau_dst,
                                                        float* __restrict__ tau_src, int accumulate) {
   constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, 3 * k_count(L, M)>();
+  constexpr int TE = tile_edges<L, M, 0>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
-  __shared__ float sRL[TE * 3 * K];
   __shared__ float sRed[TE * 8 * 3];
   __shared__ int sE[TE];
   __shared__ float sComb[kCombFallback];
+  __shared__ float sG[3 * gen_off(L + 1)];
 
   const int node = blockIdx.x;
+  gen_stage<L>(sG);
   const int C = d.C;
   const int CW = blockDim.x / 2;
   const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
@@ -246,13 +253,12 @@ __global__ __launch_bounds__(512) void node_bwd_kernel(Dims d, GraphDev g, const
       }
       __syncthreads();
       wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
-      rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
       __syncthreads();
       for (int t = grp; t < ne; t += 2) {
         float tk[3] = {0.f, 0.f, 0.f};
         if (act) {
           const int cin = pass == 0 ? C + c : c;
-          node_bwd_edge_half<L, M>(d, sR + t * K, sRL + t * 3 * K, xn, S, Tbar, Sbar, sE[t], cin, acc, tk);
+          node_bwd_edge_half<L, M>(d, sR + t * K, sG, xn, S, Tbar, Sbar, sE[t], cin, acc, tk);
         }
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(512) void node_bwd_kernel(Dims d, GraphDev g, const
   }
   if (gx) {
     int cap;
-    float* cb = comb_buffer(sRL, TE * 3 * K, sComb, CW, &cap);
+    float* cb = comb_buffer(sR, TE * K, sComb, CW, &cap);
     combine_groups<D>(acc, cb, cap, c, grp, CW, act, gx + (size_t)node * D * C, C, accumulate);
   }
 }

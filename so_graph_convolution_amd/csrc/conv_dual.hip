@@ -60,16 +60,17 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
                                                         const float* __restrict__ Sdot, OT* __restrict__ Tdot,
                                                         float* __restrict__ omega) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3, kEdgeTileBytes>();
+  constexpr int TE = tile_edges<L, M, 3, kEdgeTileBytes>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
-  __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
   __shared__ int sNode[2][TE];
+  __shared__ float sG[3 * gen_off(L + 1)];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
   const int ne = (int)min((long)TE, g.e1 - e0);
+  gen_stage<L>(sG);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int j = g.src[e], i = g.dst[e];
@@ -96,7 +97,6 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
   }
   __syncthreads();
   wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
-  rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
   __syncthreads();
 
   const int C = d.C, Ci = 2 * C, wT = d.wT(), wS = (L + 1) * Ci;
@@ -120,18 +120,20 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
         svv[l] = sr[l * Ci];
         sdvv[l] = sd[l * Ci];
       }
+      const float w[3] = {sW[t * 3], sW[t * 3 + 1], sW[t * 3 + 2]};
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const float sv = svv[l], sdv = sdvv[l];
         const int q = qhalf(l, M), n = 2 * l + 1;
+        float ga[2 * L + 1];   // G_w a: the rows of Rdot = R G_w applied as R (G_w a)
+        gw_apply<L, false>(sG, w, l, a + l * l, ga);
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
           const int off = rot_off(l, M) + (m + q) * n;
-          float r[2 * L + 1], rd[2 * L + 1];
+          float r[2 * L + 1];
           load_row<L>(sR + t * K, off, n, r);
-          load_row<L>(sRd + t * K, off, n, rd);
           const float xt = row_dot<L>(r, a + l * l, n), y2 = row_dot<L>(r, ad + l * l, n);
-          const float y1 = row_dot<L>(rd, a + l * l, n);
+          const float y1 = row_dot<L>(r, ga, n);
           st(tr + mm_col(l, m, c, L, Ci), sdv * xt + sv * (y1 + y2));
         }
       }
@@ -144,7 +146,7 @@ struct EdgeDual {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
                  const float* ppos, const float* pedge, const float* S, const float* Sdot, void* Tdot, float* omega,
                  int bf16, hipStream_t s) {
-    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3, kEdgeTileBytes>();
+    constexpr int TE = tile_edges<L, M, 3, kEdgeTileBytes>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     if (nb <= 0) return hipSuccess;
     const int threads = min(256, ((2 * d.C + 63) / 64) * 64);
@@ -166,15 +168,16 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
                                                         const float* __restrict__ penv, float* __restrict__ ydot,
                                                         int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3>();
+  constexpr int TE = tile_edges<L, M, 3>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
-  __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
   __shared__ float sComb[kCombFallback];
+  __shared__ float sG[3 * gen_off(L + 1)];
 
   const int node = blockIdx.x;
+  gen_stage<L>(sG);
   int beg, end;
   in_range(g, node, &beg, &end);
   if (accumulate && beg == end) return;
@@ -193,7 +196,6 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
     }
     __syncthreads();
     wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
-    rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
     __syncthreads();
     if (c < C) {
       for (int t = grp; t < ne; t += 2) {
@@ -202,6 +204,7 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
         // message env V (weights of c's head): tangent env (Rdot^T V + R^T Vdot) + penv R^T V
         const size_t wi = (size_t)(t0 + t) * d.H + c / d.hs();
         const float ev = env ? env[wi] : 1.f, pv = penv ? penv[wi] : 0.f;
+        const float w[3] = {sW[t * 3], sW[t * 3 + 1], sW[t * 3 + 2]};
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
           const int q = qhalf(l, M), n = 2 * l + 1;
@@ -211,16 +214,23 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
             vv[m + q] = vr[mm_col(l, m, 0, L, C)];
             vvd[m + q] = vd[mm_col(l, m, 0, L, C)];
           }
+          // Rdot^T (ev v) = G_w^T (R^T ev v): z gathers R^T ev v over the rows
+          float z[2 * L + 1], zw[2 * L + 1];
+#pragma unroll
+          for (int i = 0; i < 2 * L + 1; ++i) z[i] = 0.f;
 #pragma unroll
           for (int m = -q; m <= q; ++m) {
             const int off = rot_off(l, M) + (m + q) * n;
             const float v = vv[m + q], vdv = vvd[m + q];
-            float r[2 * L + 1], rd[2 * L + 1];
+            float r[2 * L + 1];
             load_row<L>(sR + t * K, off, n, r);
-            load_row<L>(sRd + t * K, off, n, rd);
-            row_axpy<L>(rd, ev * v, acc + l * l, n);
+            row_axpy<L>(r, ev * v, z, n);
             row_axpy<L>(r, ev * vdv + pv * v, acc + l * l, n);
           }
+          gw_apply<L, true>(sG, w, l, z, zw);
+#pragma unroll
+          for (int i = 0; i < 2 * L + 1; ++i)
+            if (i < n) acc[l * l + i] += zw[i];
         }
       }
     }
@@ -262,19 +272,19 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
                                                             const float* __restrict__ penv, float* __restrict__ p2,
                                                             float* __restrict__ genv2) {
   constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + 28 + (P2 ? 6 * k_count(L, M) : 0), kEdgeTileBytes>();
+  constexpr int TE = tile_edges<L, M, 3 + 28, kEdgeTileBytes>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
-  __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
-  __shared__ float sRL[P2 ? TE * 3 * K : 1], sRdL[P2 ? TE * 3 * K : 1];
   __shared__ float sRed[TE * 4 * 7];
   __shared__ float sHead[TE * kMaxHeads];
   __shared__ int sDst[TE];
+  __shared__ float sG[3 * gen_off(L + 1)];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
   const int ne = (int)min((long)TE, g.e1 - e0);
+  gen_stage<L>(sG);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int i = g.dst[e];
@@ -284,12 +294,6 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   }
   __syncthreads();
   wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
-  rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
-  if (P2) {
-    __syncthreads();
-    rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
-    rot_generator_products(L, M, ne, sRd, K, sRdL, 3 * K);
-  }
   __syncthreads();
   const int C = d.C, wZ = d.wZ();
   const int c = threadIdx.x, lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -308,40 +312,50 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
       OT* r2 = G2 + ((size_t)(g.e1 - g.e0) + e) * wZ + c;
       const float* vr0 = V + (size_t)e * wZ + c;
       const float* vdr0 = Vdot + (size_t)e * wZ + c;
+      const float w[3] = {sW[t * 3], sW[t * 3 + 1], sW[t * 3 + 2]};
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
         const int q = qhalf(l, M), n = 2 * l + 1;
+        float gw[2 * L + 1];   // G_w gy: the rows of Rdot = R G_w applied as R (G_w gy)
+        gw_apply<L, false>(sG, w, l, gv + l * l, gw);
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
           const int off = rot_off(l, M) + (m + q) * n;
-          float r[2 * L + 1], rd[2 * L + 1];
+          float r[2 * L + 1];
           load_row<L>(sR + t * K, off, n, r);
-          load_row<L>(sRd + t * K, off, n, rd);
-          const float s1 = row_dot<L>(r, gv + l * l, n), s2 = row_dot<L>(rd, gv + l * l, n);
+          const float s1 = row_dot<L>(r, gv + l * l, n), s2 = row_dot<L>(r, gw, n);
           st(r1 + mm_col(l, m, 0, L, C), ev * s1);
           st(r2 + mm_col(l, m, 0, L, C), __builtin_fmaf(ev, s2, pv * s1));   // fused alike in every instantiation
           if (genv2) tk[6] += vr0[mm_col(l, m, 0, L, C)] * s2 + vdr0[mm_col(l, m, 0, L, C)] * s1;
         }
       }
-      if (P2) {   // a pass of its own: no stores between the generator-row loads
+      if (P2) {
+        // sum over rows of vd (R G_k gy) and v (Rdot G_k gy) = v (R G_w G_k gy):
+        // <G_k^T u1, gy> and <G_k^T G_w^T u0, gy> with u0 = R^T v, u1 = R^T vd
         const float* vr = V + (size_t)e * wZ + c;
         const float* vdr = Vdot + (size_t)e * wZ + c;
 #pragma unroll
-        for (int l = 0; l <= L; ++l) {
+        for (int l = 1; l <= L; ++l) {
           const int q = qhalf(l, M), n = 2 * l + 1;
+          float u0[2 * L + 1], u1[2 * L + 1], u0w[2 * L + 1];
+#pragma unroll
+          for (int i = 0; i < 2 * L + 1; ++i) u0[i] = u1[i] = 0.f;
 #pragma unroll
           for (int m = -q; m <= q; ++m) {
             const int off = rot_off(l, M) + (m + q) * n;
             const float v = vr[mm_col(l, m, 0, L, C)], vd = vdr[mm_col(l, m, 0, L, C)];
+            float r[2 * L + 1];
+            load_row<L>(sR + t * K, off, n, r);
+            row_axpy<L>(r, v, u0, n);
+            row_axpy<L>(r, vd, u1, n);
+          }
+          gw_apply<L, true>(sG, w, l, u0, u0w);
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-              float gk[2 * L + 1], gdk[2 * L + 1];
-              load_row<L>(sRL + t * 3 * K + k * K, off, n, gk);
-              load_row<L>(sRdL + t * 3 * K + k * K, off, n, gdk);
-              const float a = row_dot<L>(gk, gv + l * l, n), b = row_dot<L>(gdk, gv + l * l, n);
-              tk[k] += ev * (vd * a + v * b) + pv * v * a;
-              tk[3 + k] += ev * v * a;
-            }
+          for (int k = 0; k < 3; ++k) {
+            const float a0 = gen_form<L>(sG, k, l, u0, gv + l * l);
+            const float a1 = gen_form<L>(sG, k, l, u1, gv + l * l) + gen_form<L>(sG, k, l, u0w, gv + l * l);
+            tk[k] += ev * a1 + pv * a0;
+            tk[3 + k] += ev * a0;
           }
         }
       }
@@ -379,7 +393,7 @@ struct EdgeBwdDual {
   static void go(const Dims& d, const GraphDev& g, const float* pos, const float* omega, const float* gy, void* G2,
                  const float* V, const float* Vdot, const float* env, const float* penv, float* p2, float* genv2,
                  hipStream_t s) {
-    constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + 28 + (P2 ? 6 * k_count(L, M) : 0), kEdgeTileBytes>();
+    constexpr int TE = tile_edges<L, M, 3 + 28, kEdgeTileBytes>();
     const long nb = (g.e1 - g.e0 + TE - 1) / TE;
     const int threads = ((d.C + 63) / 64) * 64;
     hipLaunchKernelGGL((edge_bwd_dual_kernel<L, M, OT, P2>), dim3(nb), dim3(threads), 0, s, d, g, pos, omega, gy,
@@ -418,18 +432,19 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
                                                             float* __restrict__ p2_dst, float* __restrict__ p2_src,
                                                             int accumulate) {
   constexpr int D = (L + 1) * (L + 1), Q = q_count(L, M), K = k_count(L, M), ST = wig_stride_c(L, M);
-  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 6 * k_count(L, M) + 48 : 0)>();
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 48 : 0)>();
   __shared__ float sD1[TE * 9];
   __shared__ float sR[TE * K];
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRd[TE * K];
   __shared__ float sW[TE * 3];
-  __shared__ float sRL[P2 ? TE * 3 * K : 1], sRdL[P2 ? TE * 3 * K : 1];
   __shared__ float sRed[P2 ? TE * 8 * 6 : 1];
   __shared__ int sE[TE];
   __shared__ float sComb[kCombFallback];
+  __shared__ float sG[P2 ? 3 * gen_off(L + 1) : 1];
 
   const int node = blockIdx.x;
+  if (P2) gen_stage<L>(sG);
   const int C = d.C, Ci = 2 * C, wT = d.wT(), wS = (L + 1) * Ci;
   const int CW = blockDim.x / 2;
   const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
@@ -463,11 +478,6 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
       __syncthreads();
       wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
       rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
-      if (P2) {
-        __syncthreads();
-        rot_generator_products(L, M, ne, sR, K, sRL, 3 * K);
-        rot_generator_products(L, M, ne, sRd, K, sRdL, 3 * K);
-      }
       __syncthreads();
       const int cin = pass == 0 ? C + c : c;
       for (int t = grp; t < ne; t += 2) {
@@ -493,6 +503,11 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
             }
             const float sv = sr[l * Ci], sdv = sd[l * Ci];
             float sb = 0.f, sdb = 0.f;
+            // position terms: the row sums y = R^T u1, z = R^T u2, zw = Rdot^T u2
+            float y[P2 ? 2 * L + 1 : 1], z[P2 ? 2 * L + 1 : 1], zw[P2 ? 2 * L + 1 : 1];
+            if (P2)
+#pragma unroll
+              for (int i = 0; i < (P2 ? 2 * L + 1 : 1); ++i) y[i] = z[i] = zw[i] = 0.f;
 #pragma unroll
             for (int m = -q; m <= q; ++m) {
               const int off = rot_off(l, M) + (m + q) * n;
@@ -510,16 +525,23 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
               const float u1 = __builtin_fmaf(sv, a0, sdv * a1), u2 = sv * a1;
               row_axpy<L>(r, u1, acc + l * l, n);
               row_axpy<L>(rd, u2, acc + l * l, n);
-              if (P2) {
+              if (P2)
 #pragma unroll
-                for (int k = 0; k < 3; ++k) {
-                  float gk[2 * L + 1], gdk[2 * L + 1];
-                  load_row<L>(sRL + t * 3 * K + k * K, off, n, gk);
-                  load_row<L>(sRdL + t * 3 * K + k * K, off, n, gdk);
-                  const float ga = row_dot<L>(gk, xn + l * l, n);
-                  tk[k] += u1 * ga + u2 * (row_dot<L>(gk, xdn + l * l, n) + row_dot<L>(gdk, xn + l * l, n));
-                  tk[3 + k] += u2 * ga;
-                }
+                for (int i = 0; i < (P2 ? 2 * L + 1 : 1); ++i)
+                  if (i < n) {
+                    y[i] = __builtin_fmaf(r[i], u1, y[i]);
+                    z[i] = __builtin_fmaf(r[i], u2, z[i]);
+                    zw[i] = __builtin_fmaf(rd[i], u2, zw[i]);
+                  }
+            }
+            if (P2 && l > 0) {
+              // sum over rows of u1 (R G_k x) + u2 ((R G_k) xd + (Rdot G_k) x), u2 (R G_k x)
+#pragma unroll
+              for (int k = 0; k < 3; ++k) {
+                const float ga = gen_form<L>(sG, k, l, z, xn + l * l);
+                tk[k] += gen_form<L>(sG, k, l, y, xn + l * l) + gen_form<L>(sG, k, l, z, xdn + l * l) +
+                         gen_form<L>(sG, k, l, zw, xn + l * l);
+                tk[3 + k] += ga;
               }
             }
             Sbar[(size_t)e * wS + l * Ci + cin] = sb;

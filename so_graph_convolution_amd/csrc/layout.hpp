@@ -53,6 +53,17 @@ __host__ __device__ constexpr inline int mm_col(int l, int m, int c, int L, int 
   return a == 0 ? l * W + c : mm_block(a, L, W) + (m < 0 ? (L - a + 1) * W : 0) + (l - a) * W + c;
 }
 
+// The so(3) generators in the real harmonic basis have at most two nonzeros
+// per row: G_x couples order m to orders -(m+1) and -(m-1), G_y to m-1 and
+// m+1, G_z to -m. gen_cand gives the candidate orders of row m (ascending; a
+// candidate outside -l..l, or c1 == c0, is not used).
+__host__ __device__ constexpr inline void gen_cand(int k, int m, int* c0, int* c1) {
+  const int a = k == 0 ? -(m + 1) : (k == 1 ? m - 1 : -m);
+  const int b = k == 0 ? -(m - 1) : (k == 1 ? m + 1 : -m);
+  *c0 = a < b ? a : b;
+  *c1 = a < b ? b : a;
+}
+
 // so(3) generator table: degree l block at gen_off(l), (2l+1)^2 entries
 __host__ __device__ constexpr inline int gen_off(int l) { return l == 0 ? 0 : gen_off(l - 1) + (2 * l - 1) * (2 * l - 1); }
 constexpr int kGenSize = gen_off(kMaxL + 1);   // 455 per generator

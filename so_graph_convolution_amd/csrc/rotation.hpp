@@ -110,6 +110,70 @@ __device__ __forceinline__ float rot_ld(RotPtr p) {
 }
 
 // o[ridx(l,m)] = sum_n R[l][m][n] a[l*l + l + n]   (rotate degree-major -> retained rows)
+// The generator blocks of degrees <= L, staged in LDS once per block (three
+// tables of gen_off(L + 1) floats) and read like the rotation rows: a table
+// value in constant memory is loop-invariant, and a kernel that applies the
+// generators inside its edge loop would otherwise keep every value it uses in
+// registers.
+template <int L>
+__device__ __forceinline__ void gen_stage(float* sG) {
+  constexpr int n = gen_off(L + 1);
+  for (int i = threadIdx.x; i < 3 * n; i += blockDim.x) sG[i] = c_gen[(i / n) * kGenSize + i % n];
+}
+
+// <a, G_k^(l) b> for degree-l blocks a, b (k, l compile-time after
+// unrolling), taken as <G_k^T a, b>: column c of G_k has its nonzeros at the
+// rows gen_cand gives for order c (the generators are antisymmetric), so each
+// entry of G_k^T a is two table products.
+// (Explicit fused forms throughout: every kernel instantiation rounds alike.)
+template <int L>
+__device__ __forceinline__ float gen_form(RotPtr G3, int k, int l, const float* a, const float* b) {
+  RotPtr G = G3 + k * gen_off(L + 1) + gen_off(l);
+  const int n = 2 * l + 1;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2 * L + 1; ++c) {
+    if (c < n) {
+      int i0, i1;
+      gen_cand(k, c - l, &i0, &i1);
+      float g = 0.f;
+      if (i0 >= -l && i0 <= l) g = __builtin_fmaf(rot_ld(G + (i0 + l) * n + c), a[i0 + l], g);
+      if (i1 != i0 && i1 >= -l && i1 <= l) g = __builtin_fmaf(rot_ld(G + (i1 + l) * n + c), a[i1 + l], g);
+      s = __builtin_fmaf(g, b[c], s);
+    }
+  }
+  return s;
+}
+
+// g = G_w^(l) a (TR: G_w^(l)T a) for G_w = sum_k w_k G_k with per-edge
+// weights w: the directional derivative of the rotation rows is R G_w, so
+// (R G_w) a = R (G_w a) and (R G_w)^T t = G_w^T (R^T t) need no per-edge
+// table of R G_w.
+// Each table entry is scaled by its w_k before it meets a: no partial sum
+// depends on a alone, so nothing is hoisted out of a loop over edges that
+// share a.
+template <int L, bool TR>
+__device__ __forceinline__ void gw_apply(RotPtr G3, const float (&w)[3], int l, const float* a,
+                                         float (&g)[2 * L + 1]) {
+  const int n = 2 * l + 1;
+#pragma unroll
+  for (int i = 0; i < 2 * L + 1; ++i) {
+    if (i < n) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        RotPtr G = G3 + k * gen_off(L + 1) + gen_off(l);
+        int j0, j1;
+        gen_cand(k, i - l, &j0, &j1);
+        if (j0 >= -l && j0 <= l) s = __builtin_fmaf(w[k] * rot_ld(G + (TR ? (j0 + l) * n + i : i * n + j0 + l)), a[j0 + l], s);
+        if (j1 != j0 && j1 >= -l && j1 <= l)
+          s = __builtin_fmaf(w[k] * rot_ld(G + (TR ? (j1 + l) * n + i : i * n + j1 + l)), a[j1 + l], s);
+      }
+      g[i] = s;
+    }
+  }
+}
+
 template <int L, int M>
 __device__ __forceinline__ void rot_fwd(RotPtr R, const float (&a)[(L + 1) * (L + 1)],
                                         float (&o)[q_count(L, M)]) {
