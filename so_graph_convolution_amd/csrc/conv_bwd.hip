@@ -298,33 +298,47 @@ struct NodeBwd {
 };
 
 // ------------------------------------------------------------------ gate_bwd
+// one thread per (edge, l, four channels; launch shape gate_dims)
 template <typename OT>
 __global__ void gate_bwd_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Zb,
                                 OT* __restrict__ Ub) {
   const int L = d.L, M = d.M, C = d.C;
-  const long n = E * (L + 1) * C;
+  const int c = 4 * threadIdx.x, l = threadIdx.y;
   const int wU = d.wU(), wZ = d.wZ();
-  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
-    const long e = idx / ((L + 1) * C);
-    const int rem = (int)(idx - e * (L + 1) * C);
-    const int l = rem / C, c = rem - l * C;
+  for (long e = (long)blockIdx.x * blockDim.z + threadIdx.z; e < E; e += (long)gridDim.x * blockDim.z) {
     const float* ur = U + e * wU;
     const float* zb = Zb + e * wZ;
     OT* ub = Ub + e * wU;
+    float u[4], z[4], o[4];
     if (l == 0) {
-      const float u = ur[c], s = sigm(u);
-      st(ub + c, zb[c] * s * (1.f + u * (1.f - s)));
-    } else {
-      const float s = sigm(ur[d.gate_col(l, c)]);
-      const int q = qhalf(l, M);
-      float gsum = 0.f;
-      for (int m = -q; m <= q; ++m) {
-        const float z = zb[mm_col(l, m, c, L, C)];
-        const int uc = d.u_col(l, m, c);
-        gsum += z * ur[uc];
-        st(ub + uc, s * z);
+      ld4(ur + c, u);
+      ld4(zb + c, z);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = sigm(u[i]);
+        o[i] = z[i] * s * (1.f + u[i] * (1.f - s));
       }
-      st(ub + d.gate_col(l, c), s * (1.f - s) * gsum);
+      st4(ub + c, o);
+    } else {
+      float s[4], gsum[4] = {0.f, 0.f, 0.f, 0.f};
+      ld4(ur + d.gate_col(l, c), s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = sigm(s[i]);
+      const int q = qhalf(l, M);
+      for (int m = -q; m <= q; ++m) {
+        ld4(zb + mm_col(l, m, c, L, C), z);
+        const int uc = d.u_col(l, m, c);
+        ld4(ur + uc, u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gsum[i] += z[i] * u[i];
+          o[i] = s[i] * z[i];
+        }
+        st4(ub + uc, o);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = s[i] * (1.f - s[i]) * gsum[i];
+      st4(ub + d.gate_col(l, c), o);
     }
   }
 }
@@ -387,14 +401,13 @@ int launch_edge_bwd(const Dims& d, const GraphDev& g, const float* pos, const fl
 }
 
 int launch_gate_bwd(const Dims& d, long E, const float* U, const float* Zbar, void* Ubar, int bf16, hipStream_t s) {
-  const long n = E * (d.L + 1) * d.C;
-  if (n == 0) return hipSuccess;
+  if (E == 0) return hipSuccess;
+  dim3 grid, block;
+  gate_dims(d, E, &grid, &block);
   if (bf16)
-    hipLaunchKernelGGL(gate_bwd_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Zbar,
-                       static_cast<bf16s*>(Ubar));
+    hipLaunchKernelGGL(gate_bwd_kernel<bf16s>, grid, block, 0, s, d, E, U, Zbar, static_cast<bf16s*>(Ubar));
   else
-    hipLaunchKernelGGL(gate_bwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Zbar,
-                       static_cast<float*>(Ubar));
+    hipLaunchKernelGGL(gate_bwd_kernel<float>, grid, block, 0, s, d, E, U, Zbar, static_cast<float*>(Ubar));
   return hipGetLastError();
 }
 

@@ -629,29 +629,45 @@ __global__ void pos2_kernel(GraphDev g, const float* __restrict__ pos, const flo
 }
 
 // ------------------------------------------------------------------ gates
+// one thread per (edge, l, four channels; launch shape gate_dims)
 template <typename OT>
 __global__ void gate_dual_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Ud,
                                  OT* __restrict__ Zd) {
   const int L = d.L, M = d.M, C = d.C;
-  const long n = E * (L + 1) * C;
+  const int c = 4 * threadIdx.x, l = threadIdx.y;
   const int wU = d.wU(), wZ = d.wZ();
-  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
-    const long e = idx / ((L + 1) * C);
-    const int rem = (int)(idx - e * (L + 1) * C);
-    const int l = rem / C, c = rem - l * C;
+  for (long e = (long)blockIdx.x * blockDim.z + threadIdx.z; e < E; e += (long)gridDim.x * blockDim.z) {
     const float* ur = U + e * wU;
     const float* udr = Ud + e * wU;
     OT* zr = Zd + e * wZ;
+    float u[4], ud[4], o[4];
     if (l == 0) {
-      const float u = ur[c], s = sigm(u);
-      st(zr + c, s * (1.f + u * (1.f - s)) * udr[c]);
+      ld4(ur + c, u);
+      ld4(udr + c, ud);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = sigm(u[i]);
+        o[i] = s * (1.f + u[i] * (1.f - s)) * ud[i];
+      }
+      st4(zr + c, o);
     } else {
       const int gc = d.gate_col(l, c);
-      const float s = sigm(ur[gc]), sp = s * (1.f - s), gd = udr[gc];
+      float s[4], sp[4], gd[4];
+      ld4(ur + gc, s);
+      ld4(udr + gc, gd);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = sigm(s[i]);
+        sp[i] = s[i] * (1.f - s[i]);
+      }
       const int q = qhalf(l, M);
       for (int m = -q; m <= q; ++m) {
         const int uc = d.u_col(l, m, c);
-        st(zr + mm_col(l, m, c, L, C), s * udr[uc] + sp * gd * ur[uc]);
+        ld4(udr + uc, ud);
+        ld4(ur + uc, u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = s[i] * ud[i] + sp[i] * gd[i] * u[i];
+        st4(zr + mm_col(l, m, c, L, C), o);
       }
     }
   }
@@ -662,39 +678,63 @@ template <typename OT>
 __global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Ud,
                                  const float* __restrict__ ZZ, OT* __restrict__ UU) {
   const int L = d.L, M = d.M, C = d.C;
-  const long n = E * (L + 1) * C;
+  const int c = 4 * threadIdx.x, l = threadIdx.y;
   const int wU = d.wU(), wZ = d.wZ();
-  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
-    const long e = idx / ((L + 1) * C);
-    const int rem = (int)(idx - e * (L + 1) * C);
-    const int l = rem / C, c = rem - l * C;
+  for (long e = (long)blockIdx.x * blockDim.z + threadIdx.z; e < E; e += (long)gridDim.x * blockDim.z) {
     const float* ur = U + e * wU;
     const float* udr = Ud + e * wU;
     const float* zdb = ZZ + e * wZ;
     const float* zb = ZZ + (E + e) * wZ;
     OT* udb = UU + e * wU;
     OT* ub = UU + (E + e) * wU;
+    float u[4], ud[4], a[4], b[4], o1[4], o2[4];
     if (l == 0) {
-      const float u = ur[c], s = sigm(u);
-      const float s1 = s * (1.f + u * (1.f - s));
-      const float s2 = s * (1.f - s) * (2.f + u * (1.f - 2.f * s));
-      st(udb + c, s1 * zdb[c]);
-      st(ub + c, s2 * udr[c] * zdb[c] + s1 * zb[c]);
+      ld4(ur + c, u);
+      ld4(udr + c, ud);
+      ld4(zdb + c, a);
+      ld4(zb + c, b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = sigm(u[i]);
+        const float s1 = s * (1.f + u[i] * (1.f - s));
+        const float s2 = s * (1.f - s) * (2.f + u[i] * (1.f - 2.f * s));
+        o1[i] = s1 * a[i];
+        o2[i] = s2 * ud[i] * a[i] + s1 * b[i];
+      }
+      st4(udb + c, o1);
+      st4(ub + c, o2);
     } else {
       const int gc = d.gate_col(l, c);
-      const float s = sigm(ur[gc]), sp = s * (1.f - s), spp = sp * (1.f - 2.f * s), gd = udr[gc];
+      float s[4], sp[4], spp[4], gd[4], gdb[4] = {0.f, 0.f, 0.f, 0.f}, gb[4] = {0.f, 0.f, 0.f, 0.f};
+      ld4(ur + gc, s);
+      ld4(udr + gc, gd);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = sigm(s[i]);
+        sp[i] = s[i] * (1.f - s[i]);
+        spp[i] = sp[i] * (1.f - 2.f * s[i]);
+      }
       const int q = qhalf(l, M);
-      float gdb = 0.f, gb = 0.f;
       for (int m = -q; m <= q; ++m) {
         const int uc = d.u_col(l, m, c), zc = mm_col(l, m, c, L, C);
-        const float a = zdb[zc], b = zb[zc], u = ur[uc], ud = udr[uc];
-        st(udb + uc, s * a);
-        st(ub + uc, sp * gd * a + s * b);
-        gdb += a * u;
-        gb += spp * gd * u * a + sp * ud * a + sp * u * b;
+        ld4(zdb + zc, a);
+        ld4(zb + zc, b);
+        ld4(ur + uc, u);
+        ld4(udr + uc, ud);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o1[i] = s[i] * a[i];
+          o2[i] = sp[i] * gd[i] * a[i] + s[i] * b[i];
+          gdb[i] += a[i] * u[i];
+          gb[i] += spp[i] * gd[i] * u[i] * a[i] + sp[i] * ud[i] * a[i] + sp[i] * u[i] * b[i];
+        }
+        st4(udb + uc, o1);
+        st4(ub + uc, o2);
       }
-      st(udb + gc, sp * gdb);
-      st(ub + gc, gb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o1[i] = sp[i] * gdb[i];
+      st4(udb + gc, o1);
+      st4(ub + gc, gb);
     }
   }
 }
@@ -715,14 +755,13 @@ int launch_edge_dual(const Dims& d, const GraphDev& g, const float* x, const flo
 }
 
 int launch_gate_dual(const Dims& d, long E, const float* U, const float* Udot, void* Zdot, int bf16, hipStream_t s) {
-  const long n = E * (d.L + 1) * d.C;
-  if (n == 0) return hipSuccess;
+  if (E == 0) return hipSuccess;
+  dim3 grid, block;
+  gate_dims(d, E, &grid, &block);
   if (bf16)
-    hipLaunchKernelGGL(gate_dual_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot,
-                       static_cast<bf16s*>(Zdot));
+    hipLaunchKernelGGL(gate_dual_kernel<bf16s>, grid, block, 0, s, d, E, U, Udot, static_cast<bf16s*>(Zdot));
   else
-    hipLaunchKernelGGL(gate_dual_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot,
-                       static_cast<float*>(Zdot));
+    hipLaunchKernelGGL(gate_dual_kernel<float>, grid, block, 0, s, d, E, U, Udot, static_cast<float*>(Zdot));
   return hipGetLastError();
 }
 
@@ -748,14 +787,13 @@ int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const fl
 
 int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, void* UU, int bf16,
                      hipStream_t s) {
-  const long n = E * (d.L + 1) * d.C;
-  if (n == 0) return hipSuccess;
+  if (E == 0) return hipSuccess;
+  dim3 grid, block;
+  gate_dims(d, E, &grid, &block);
   if (bf16)
-    hipLaunchKernelGGL(gate_dbwd_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, ZZ,
-                       static_cast<bf16s*>(UU));
+    hipLaunchKernelGGL(gate_dbwd_kernel<bf16s>, grid, block, 0, s, d, E, U, Udot, ZZ, static_cast<bf16s*>(UU));
   else
-    hipLaunchKernelGGL(gate_dbwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, Udot, ZZ,
-                       static_cast<float*>(UU));
+    hipLaunchKernelGGL(gate_dbwd_kernel<float>, grid, block, 0, s, d, E, U, Udot, ZZ, static_cast<float*>(UU));
   return hipGetLastError();
 }
 

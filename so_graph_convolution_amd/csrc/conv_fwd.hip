@@ -157,25 +157,34 @@ struct NodeFwd {
 // ------------------------------------------------------------------ gate_fwd
 __device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
-// one thread per (edge, l, c): reads the gate once, scales every retained order of l
+// one thread per (edge, l, four channels; launch shape gate_dims): reads the
+// gate once, scales every retained order of l
 template <typename OT>
 __global__ void gate_fwd_kernel(Dims d, long E, const float* __restrict__ U, OT* __restrict__ Z) {
   const int L = d.L, M = d.M, C = d.C;
-  const long n = E * (L + 1) * C;
+  const int c = 4 * threadIdx.x, l = threadIdx.y;
   const int wU = d.wU(), wZ = d.wZ();
-  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
-    const long e = idx / ((L + 1) * C);
-    const int rem = (int)(idx - e * (L + 1) * C);
-    const int l = rem / C, c = rem - l * C;
+  for (long e = (long)blockIdx.x * blockDim.z + threadIdx.z; e < E; e += (long)gridDim.x * blockDim.z) {
     const float* ur = U + e * wU;
     OT* zr = Z + e * wZ;
+    float u[4], z[4];
     if (l == 0) {
-      const float u = ur[c];
-      st(zr + c, u * sigm(u));
+      ld4(ur + c, u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = u[i] * sigm(u[i]);
+      st4(zr + c, z);
     } else {
-      const float gs = sigm(ur[d.gate_col(l, c)]);
+      float gs[4];
+      ld4(ur + d.gate_col(l, c), gs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gs[i] = sigm(gs[i]);
       const int q = qhalf(l, M);
-      for (int m = -q; m <= q; ++m) st(zr + mm_col(l, m, c, L, C), gs * ur[d.u_col(l, m, c)]);
+      for (int m = -q; m <= q; ++m) {
+        ld4(ur + d.u_col(l, m, c), u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = gs[i] * u[i];
+        st4(zr + mm_col(l, m, c, L, C), z);
+      }
     }
   }
 }
@@ -246,12 +255,13 @@ int launch_node_fwd(const Dims& d, const GraphDev& g, const float* pos, const fl
 }
 
 int launch_gate_fwd(const Dims& d, long E, const float* U, void* Z, int bf16, hipStream_t s) {
-  const long n = E * (d.L + 1) * d.C;
-  if (n == 0) return hipSuccess;
+  if (E == 0) return hipSuccess;
+  dim3 grid, block;
+  gate_dims(d, E, &grid, &block);
   if (bf16)
-    hipLaunchKernelGGL(gate_fwd_kernel<bf16s>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, static_cast<bf16s*>(Z));
+    hipLaunchKernelGGL(gate_fwd_kernel<bf16s>, grid, block, 0, s, d, E, U, static_cast<bf16s*>(Z));
   else
-    hipLaunchKernelGGL(gate_fwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, d, E, U, static_cast<float*>(Z));
+    hipLaunchKernelGGL(gate_fwd_kernel<float>, grid, block, 0, s, d, E, U, static_cast<float*>(Z));
   return hipGetLastError();
 }
 

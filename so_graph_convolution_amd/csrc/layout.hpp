@@ -91,4 +91,23 @@ struct Dims {
   }
 };
 
+// Launch shape of the elementwise gate kernels: one thread per (edge, degree,
+// four channels), block (C/4, L+1, edges per block) with whole waves per
+// block; blocks stride over the edges. Needs C % 4 == 0 (C is a multiple of 16).
+inline void gate_dims(const Dims& d, long E, dim3* grid, dim3* block) {
+  const int tpe = (d.C / 4) * (d.L + 1);
+  int g = tpe, b = 64;
+  while (b) {
+    const int t = g % b;
+    g = b;
+    b = t;
+  }
+  int epb = 64 / g;
+  while (epb > 1 && epb * tpe > 1024) epb /= 2;
+  *block = dim3(d.C / 4, d.L + 1, epb);
+  long nb = (E + epb - 1) / epb;
+  if (nb > 65536) nb = 65536;
+  *grid = dim3((unsigned)(nb > 0 ? nb : 1));
+}
+
 }  // namespace so2

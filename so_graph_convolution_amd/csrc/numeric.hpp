@@ -23,6 +23,24 @@ __host__ __device__ inline unsigned short f32_to_bf16(float f) {
   return (unsigned short)(u >> 16);
 }
 
+// four consecutive elements (16-byte aligned float, 8-byte aligned bf16)
+__device__ __forceinline__ void ld4(const float* p, float (&v)[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+}
+__device__ __forceinline__ void st4(float* p, const float (&v)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st4(bf16s* p, const float (&v)[4]) {
+  uint2 u;
+  u.x = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
+  u.y = (unsigned)f32_to_bf16(v[2]) | ((unsigned)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
 __device__ __forceinline__ void st(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st(bf16s* p, float v) { p->u = f32_to_bf16(v); }
 __device__ __forceinline__ float ld(const float* p) { return *p; }
