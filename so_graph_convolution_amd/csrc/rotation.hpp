@@ -57,28 +57,8 @@ __device__ inline EdgeGeo edge_geometry(const float* __restrict__ pos, const flo
   return g;
 }
 
-// RL[e][k][K] = R_e G_k (retained rows of D_e G_k), k = 0..2; cooperative.
-__device__ inline void rot_generator_products(int L, int M, int ne, const float* R, int ldr, float* RL, int ldrl) {
-  const int K = k_count(L, M);
-  for (int idx = threadIdx.x; idx < ne * 3 * K; idx += blockDim.x) {
-    const int e = idx / (3 * K);
-    int rem = idx - e * 3 * K;
-    const int k = rem / K;
-    rem -= k * K;
-    int l = 0;
-    while (rem >= rot_off(l + 1, M)) ++l;
-    const int n = 2 * l + 1;
-    const int loc = rem - rot_off(l, M);
-    const int mi = loc / n, col = loc - mi * n;
-    const float* Rrow = R + e * ldr + rot_off(l, M) + mi * n;
-    const float* G = c_gen + k * kGenSize + gen_off(l);
-    float s = 0.f;
-    for (int p = 0; p < n; ++p) s += Rrow[p] * G[p * n + col];
-    RL[e * ldrl + k * K + rem] = s;
-  }
-}
-
 // Rd[e][K] = R_e (sum_k w_k G_k) with per-edge weights w[e][3]; cooperative.
+// Column col of G_k has its nonzeros at the rows gen_cand gives for col.
 __device__ inline void rot_directional(int L, int M, int ne, const float* R, int ldr, const float* w, int ldw,
                                        float* Rd, int ldd) {
   const int K = k_count(L, M);
@@ -91,12 +71,16 @@ __device__ inline void rot_directional(int L, int M, int ne, const float* R, int
     const int loc = rem - rot_off(l, M);
     const int mi = loc / n, col = loc - mi * n;
     const float* Rrow = R + e * ldr + rot_off(l, M) + mi * n;
-    const float w0 = w[e * ldw], w1 = w[e * ldw + 1], w2 = w[e * ldw + 2];
-    const float* G0 = c_gen + gen_off(l);
-    const float* G1 = c_gen + kGenSize + gen_off(l);
-    const float* G2 = c_gen + 2 * kGenSize + gen_off(l);
     float s = 0.f;
-    for (int p = 0; p < n; ++p) s += Rrow[p] * (w0 * G0[p * n + col] + w1 * G1[p * n + col] + w2 * G2[p * n + col]);
+    for (int k = 0; k < 3; ++k) {
+      const float* G = c_gen + k * kGenSize + gen_off(l);
+      int p0, p1;
+      gen_cand(k, col - l, &p0, &p1);
+      float t = 0.f;
+      if (p0 >= -l && p0 <= l) t = __builtin_fmaf(Rrow[p0 + l], G[(p0 + l) * n + col], t);
+      if (p1 != p0 && p1 >= -l && p1 <= l) t = __builtin_fmaf(Rrow[p1 + l], G[(p1 + l) * n + col], t);
+      s = __builtin_fmaf(w[e * ldw + k], t, s);
+    }
     Rd[e * ldd + rem] = s;
   }
 }
