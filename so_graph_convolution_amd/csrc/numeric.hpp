@@ -15,12 +15,13 @@ __host__ __device__ inline float bf16_to_f32(unsigned short h) {
   return __builtin_bit_cast(float, (unsigned)h << 16);
 }
 
-// round to nearest even; NaN stays NaN
+// round to nearest even; NaN stays NaN (a select, not a branch: no divergent
+// control flow around every store)
 __host__ __device__ inline unsigned short f32_to_bf16(float f) {
-  unsigned u = __builtin_bit_cast(unsigned, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+  const unsigned u = __builtin_bit_cast(unsigned, f);
+  const unsigned rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const unsigned quiet = (u >> 16) | 0x40u;
+  return (unsigned short)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
 }
 
 // four consecutive elements (16-byte aligned float, 8-byte aligned bf16)
