@@ -258,6 +258,35 @@ int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const 
                  const float* A, const float* gU, const float* px, const float* pW, const float* pA, float* ggU,
                  float* gx2, float* gW2, float* gA2, void* ws, size_t ws_bytes, void* stream);
 
+/* Spherical-grid SwiGLU activation on edges (SwiGLU-S2; TrimSO(2) page,
+ * Table 5 and Section 5.1: EquiformerV3's Edge -> Edge activation; Appendix
+ * B.4: the degree-l basis evaluated at n_g grid points, the nonlinearity on
+ * grid values). The pages name the activation without a formula; read here,
+ * per edge e and channel c of q coefficient rows with a value half
+ * (channels 0..C-1) and a gate half (C..2C-1):
+ *   v = G u_v,  a = G u_g,  s = SiLU(a) * v,  z = P s
+ * with G [n_grid][rows] (the basis of the retained rows at the grid points)
+ * and P [rows][n_grid] (the projection back) supplied by the caller; both are
+ * constants (no gradients for them).
+ * Arrays (device, float32, row-major): U and pU, gU, gU2 [n_edges][rows][2C];
+ * Z and gZ, ggZ [n_edges][rows][C]. rows in [1, 32], channels in [1, 256],
+ * n_grid >= 1 with n_grid * rows <= 8192 (G and P are staged in LDS), else
+ * SO2_EUNSUPPORTED; NULL inputs or outputs are SO2_EINVAL (in dbwd one of
+ * ggZ, gU2 may be NULL: not requested). No workspace; n_edges == 0 is a no-op.
+ *   fwd : Z
+ *   bwd : gU = dZ/dU^T gZ
+ *   dbwd: with L = <pU, gU>: ggZ = dL/dgZ (the forward's directional
+ *         derivative along pU), gU2 = dL/dU */
+typedef struct {
+  int32_t rows, channels, n_grid, dtype /* SO2_F32 */, flags /* 0 */;
+} so2s2_cfg;
+int so2s2_fwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P, float* Z,
+              void* stream);
+int so2s2_bwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P,
+              const float* gZ, float* gU, void* stream);
+int so2s2_dbwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P,
+               const float* gZ, const float* pU, float* ggZ, float* gU2, void* stream);
+
 /* Measurement hook for the per-order GEMMs (the dense products of Section
  * 3.1 and Eq.(1)). While enabled, every matrix-core GEMM launch is bracketed
  * by HIP events on the launching stream and its algorithmic flop count (2 M N K

@@ -11,3 +11,4 @@ from .ops import (DBWD_KEYS, GRAD_KEYS, Graph, SO2Config, so2conv_bwd, so2conv_d
 from .grid_ops import GridConfig, so2grid_bwd, so2grid_dbwd, so2grid_fwd, so2grid_workspace_bytes  # noqa: F401
 from .mole_ops import (Mixture, expert_shapes, so2mole_bwd, so2mole_dbwd, so2mole_fwd,  # noqa: F401
                        so2mole_workspace_bytes)
+from .s2_ops import S2Config, so2s2_bwd, so2s2_dbwd, so2s2_fwd  # noqa: F401

@@ -31,6 +31,10 @@ class GridCfg(ctypes.Structure):
                 ("dtype", c_i32), ("flags", c_i32)]
 
 
+class S2Cfg(ctypes.Structure):
+    _fields_ = [("rows", c_i32), ("channels", c_i32), ("n_grid", c_i32), ("dtype", c_i32), ("flags", c_i32)]
+
+
 class MoleCfg(ctypes.Structure):
     _fields_ = [("n_systems", c_i32), ("n_experts", c_i32), ("sys_edge_ptr", c_vp)]
 
@@ -78,6 +82,12 @@ EXPORTS = {
     "so2grid_bwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 9 + [c_sz, c_vp]),
     # (cfg, N, x, G, W, A, gU, px, pW, pA, ggU, gx2, gW2, gA2, ws, ws_bytes, stream)
     "so2grid_dbwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 13 + [c_sz, c_vp]),
+    # (cfg, E, U, G, P, Z, stream)
+    "so2s2_fwd": (ctypes.c_int, [ctypes.POINTER(S2Cfg), c_i64] + [c_vp] * 5),
+    # (cfg, E, U, G, P, gZ, gU, stream)
+    "so2s2_bwd": (ctypes.c_int, [ctypes.POINTER(S2Cfg), c_i64] + [c_vp] * 6),
+    # (cfg, E, U, G, P, gZ, pU, ggZ, gU2, stream)
+    "so2s2_dbwd": (ctypes.c_int, [ctypes.POINTER(S2Cfg), c_i64] + [c_vp] * 8),
 }
 
 _lib = None

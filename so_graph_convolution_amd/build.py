@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libso2conv.so")
-SOURCES = ["api.cpp", "gemm.hip", "graph.hip", "conv_fwd.hip", "conv_bwd.hip", "conv_dual.hip", "grid.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "graph.hip", "conv_fwd.hip", "conv_bwd.hip", "conv_dual.hip", "grid.hip",
+           "s2act.hip"]
 ARCH = os.environ.get("SO2_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-result", "-Wno-unused-variable"]

@@ -1897,3 +1897,59 @@ int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- spherical-grid SwiGLU activation
+namespace so2 {
+namespace {
+int check_s2(const so2s2_cfg* cfg, int64_t E) {
+  if (!cfg) return fail(SO2_EINVAL, "cfg is NULL");
+  if (cfg->rows < 1 || cfg->rows > 32) return fail(SO2_EUNSUPPORTED, "rows must be in [1, 32]");
+  if (cfg->channels < 1 || cfg->channels > 256) return fail(SO2_EUNSUPPORTED, "channels must be in [1, 256]");
+  if (cfg->n_grid < 1 || (long)cfg->n_grid * cfg->rows > 8192)
+    return fail(SO2_EUNSUPPORTED, "n_grid must be >= 1 with n_grid * rows <= 8192");
+  if (cfg->dtype != SO2_F32) return fail(SO2_EUNSUPPORTED, "the grid activation is float32 only");
+  if (cfg->flags) return fail(SO2_EINVAL, "unknown cfg flags");
+  if (E < 0) return fail(SO2_EINVAL, "negative edge count");
+  return SO2_OK;
+}
+}  // namespace
+}  // namespace so2
+
+extern "C" {
+
+int so2s2_fwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P, float* Z,
+              void* stream) {
+  g_err.clear();
+  int r;
+  if ((r = check_s2(cfg, n_edges))) return r;
+  if (n_edges == 0) return SO2_OK;
+  if (!U || !G || !P || !Z) return fail(SO2_EINVAL, "NULL input or output");
+  SO2_HIP(launch_s2_fwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, Z, (hipStream_t)stream));
+  return SO2_OK;
+}
+
+int so2s2_bwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P,
+              const float* gZ, float* gU, void* stream) {
+  g_err.clear();
+  int r;
+  if ((r = check_s2(cfg, n_edges))) return r;
+  if (n_edges == 0) return SO2_OK;
+  if (!U || !G || !P || !gZ || !gU) return fail(SO2_EINVAL, "NULL input or output");
+  SO2_HIP(launch_s2_bwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, gZ, gU, (hipStream_t)stream));
+  return SO2_OK;
+}
+
+int so2s2_dbwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P,
+               const float* gZ, const float* pU, float* ggZ, float* gU2, void* stream) {
+  g_err.clear();
+  int r;
+  if ((r = check_s2(cfg, n_edges))) return r;
+  if (n_edges == 0) return SO2_OK;
+  if (!U || !G || !P || !gZ || !pU) return fail(SO2_EINVAL, "NULL input");
+  if (!ggZ && !gU2) return fail(SO2_EINVAL, "no output requested");
+  SO2_HIP(launch_s2_dbwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, gZ, pU, ggZ, gU2,
+                         (hipStream_t)stream));
+  return SO2_OK;
+}
+
+}  // extern "C"

@@ -110,6 +110,13 @@ long realified_size(const Dims& d, int second);
 // U: [N][ng][C]) and Z = G^T U
 int launch_grid_apply(int L, int N, int ng, int C, const float* G, const float* Y, float* U, hipStream_t s);
 int launch_grid_apply_t(int L, int N, int ng, int C, const float* G, const float* U, float* Z, hipStream_t s);
+// spherical-grid SwiGLU activation on edges (s2act.hip)
+int launch_s2_fwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, float* Z,
+                  hipStream_t s);
+int launch_s2_bwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* gZ,
+                  float* gU, hipStream_t s);
+int launch_s2_dbwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* gZ,
+                   const float* pU, float* ggZ, float* gU2, hipStream_t s);
 
 // ---- graph preparation
 size_t graph_ws_bytes(int N, long E);

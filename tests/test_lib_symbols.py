@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "so2conv.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(so2(?:conv|grid|mole)_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(so2(?:conv|grid|mole|s2)_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_entry_points():
@@ -92,3 +92,22 @@ def test_mixture_host_checks():
     m = MoleCfg(3, 10, np.array([0, 100, 200, 1000], dtype=np.int64).ctypes.data)
     r = K.lib().so2mole_bwd(ctypes.byref(c), ctypes.byref(g), ctypes.byref(m), *([None] * 20), 0, None)
     assert r == -2 and b"n_experts" in K.lib().so2conv_last_error()
+
+
+def test_grid_activation_host_checks():
+    """so2s2_*: every size check runs on the host before any GPU call."""
+    from so_graph_convolution_amd import _binding
+    from so_graph_convolution_amd._binding import S2Cfg
+    lib = _binding.lib()
+    E_UNSUP, E_INVAL = -2, -1
+    cases = [((0, 16, 10, 0, 0), E_UNSUP), ((33, 16, 10, 0, 0), E_UNSUP), ((8, 0, 10, 0, 0), E_UNSUP),
+             ((8, 257, 10, 0, 0), E_UNSUP), ((8, 16, 0, 0, 0), E_UNSUP), ((32, 16, 257, 0, 0), E_UNSUP),
+             ((8, 16, 10, 1, 0), E_UNSUP), ((8, 16, 10, 0, 4), E_INVAL)]
+    for fields, code in cases:
+        c = S2Cfg(*fields)
+        assert lib.so2s2_fwd(ctypes.byref(c), 5, None, None, None, None, None) == code, fields
+    c = S2Cfg(8, 16, 10, 0, 0)
+    assert lib.so2s2_fwd(ctypes.byref(c), 0, None, None, None, None, None) == 0          # no edges: no-op
+    assert lib.so2s2_fwd(ctypes.byref(c), -1, None, None, None, None, None) == E_INVAL
+    assert lib.so2s2_bwd(ctypes.byref(c), 4, None, None, None, None, None, None) == E_INVAL
+    assert lib.so2s2_dbwd(ctypes.byref(c), 4, None, None, None, None, None, None, None, None) == E_INVAL
