@@ -187,6 +187,86 @@ def bench_grid(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_s2act(args):
+    """Spherical-grid SwiGLU activation on edges (EquiformerV3's Edge -> Edge
+    activation; Table 5, Section 5.1 and Appendix B.4) at the high-degree
+    system's size: 1,045,678 edges, 29 retained rows (lmax 6, mmax 2), C 128
+    (U carries 2C), a 100-point grid; fwd + bwd + dbwd (both outputs)."""
+    import numpy as np
+    import torch
+    import so_graph_convolution_amd as K
+
+    def progress(msg):
+        print(f"[bench s2act] {msg}", file=sys.stderr, flush=True)
+    E, q, C, ng = 1045678, 29, 128, 100
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    g = dict(U=torch.randn(E, q, 2 * C, device="cuda", generator=gen),
+             gZ=torch.randn(E, q, C, device="cuda", generator=gen),
+             pU=torch.randn(E, q, 2 * C, device="cuda", generator=gen),
+             G=torch.randn(ng, q, device="cuda", generator=gen) / math.sqrt(q),
+             P=torch.randn(q, ng, device="cuda", generator=gen) / math.sqrt(ng))
+    cfg = K.S2Config(q, C, ng)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    progress(f"E={E} rows={q} C={C} n_grid={ng}")
+
+    def step(times=None):
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        K.so2s2_fwd(cfg, g["U"], g["G"], g["P"])
+        e[1].record()
+        K.so2s2_bwd(cfg, g["U"], g["G"], g["P"], g["gZ"])
+        e[2].record()
+        K.so2s2_dbwd(cfg, g["U"], g["G"], g["P"], g["gZ"], g["pU"])
+        e[3].record()
+        if times is not None:
+            times.append(e)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in st]).mean(0)
+    # contraction flops per (edge, channel, grid point) as the kernels compute
+    # them (grid values recomputed, never stored): fwd 6q, bwd 10q, dbwd 16q
+    units = float(E) * C * ng
+    flops = {"fwd": 6 * q * units, "bwd": 10 * q * units, "dbwd": 16 * q * units}
+    # the matrix cores see rows and grid points padded to whole 16x16x4 tiles:
+    # 8 products of 2 x 16*ceil(q/16) x 16*ceil(ng/16) per dbwd column
+    issued = 8 * 2 * (16 * -(-q // 16)) * (16 * -(-ng // 16)) * float(E) * C
+    ach = flops["dbwd"] / (ms[2] * 1e-3) / 1e12
+    out = {"metric": "edges/sec fwd+bwd+dbwd SwiGLU-S2 edge activation (lmax=6, mmax=2, C=128, 100-point grid)",
+           "value": E * args.steps / wall, "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "SwiGLU-S2 on the edges of the EquiformerV3-like high-degree system",
+                      "n_edges": E, "rows": q, "channels": C, "n_grid": ng},
+           "stage_ms": {"fwd": float(ms[0]), "bwd": float(ms[1]), "dbwd": float(ms[2])},
+           "roofline": {"bound": "mfma", "kernel": "s2_dbwd_kernel", "achieved": ach,
+                        "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_FP32_MFMA_TFLOPS,
+                        "traffic": None, "flops_per_launch": flops["dbwd"], "flops_issued_per_launch": issued}}
+    progress(f"{out['ms_per_step']:.2f} ms/step  stages {ms.round(2).tolist()}  dbwd {ach:.1f} TFLOP/s")
+    if args.cpu_edges > 0:
+        import oracle.s2act_oracle as SO
+        torch.set_num_threads(min(16, len(os.sched_getaffinity(0))))
+        n, chunk = min(args.cpu_edges, 8192), 2048
+        h = {k: v.double().cpu() for k, v in (("G", g["G"]), ("P", g["P"]))}
+        t1 = time.perf_counter()
+        for i in range(0, n, chunk):
+            U, gZ, pU = (g[k][i:i + chunk].double().cpu() for k in ("U", "gZ", "pU"))
+            SO.forward(U, h["G"], h["P"])
+            SO.backward(U, h["G"], h["P"], gZ)
+            SO.double_backward(U, h["G"], h["P"], gZ, pU)
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": n / dt, "unit": "edges/s", "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": f"first {n} of {E} edges, fwd+bwd+dbwd in float64 (PyTorch CPU, autograd), "
+                                         f"{chunk}-edge chunks, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,9 +277,10 @@ def main():
                     help="array dtype (default: the workload's own: f32 for M, bf16 for H and X)")
     ap.add_argument("--pos2", action="store_true",
                     help="the double backward also returns position derivatives (gpos2)")
-    ap.add_argument("--op", choices=("conv", "grid", "mole"), default="conv",
+    ap.add_argument("--op", choices=("conv", "grid", "mole", "s2act"), default="conv",
                     help="conv: the SO(2) convolution step (default); grid: the node-to-node spherical projection; "
-                         "mole: the convolution with a system-dependent mixture of linear experts")
+                         "mole: the convolution with a system-dependent mixture of linear experts; "
+                         "s2act: the spherical-grid SwiGLU activation on edges")
     ap.add_argument("--systems", type=int, default=16, help="systems of the batch (--op mole)")
     ap.add_argument("--experts", type=int, default=64, help="linear experts (--op mole; 64 for UMA)")
     ap.add_argument("--envelope", action="store_true",
@@ -223,6 +304,9 @@ def main():
         return
     if args.op == "grid" and args.gpus == 1:
         bench_grid(args)
+        return
+    if args.op == "s2act" and args.gpus == 1:
+        bench_s2act(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the convolution runs on a "

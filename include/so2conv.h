@@ -269,10 +269,11 @@ int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const 
  * and P [rows][n_grid] (the projection back) supplied by the caller; both are
  * constants (no gradients for them).
  * Arrays (device, float32, row-major): U and pU, gU, gU2 [n_edges][rows][2C];
- * Z and gZ, ggZ [n_edges][rows][C]. rows in [1, 32], channels in [1, 256],
- * n_grid >= 1 with n_grid * rows <= 8192 (G and P are staged in LDS), else
- * SO2_EUNSUPPORTED; NULL inputs or outputs are SO2_EINVAL (in dbwd one of
- * ggZ, gU2 may be NULL: not requested). No workspace; n_edges == 0 is a no-op.
+ * Z and gZ, ggZ [n_edges][rows][C]. rows in [1, 32], channels in
+ * [1, 65536], n_grid in [1, 256] (G and P are staged in LDS as matrix-core
+ * operands), else SO2_EUNSUPPORTED; NULL inputs or outputs are SO2_EINVAL (in
+ * dbwd one of ggZ, gU2 may be NULL: not requested). No workspace;
+ * n_edges == 0 is a no-op. Runs asynchronously on `stream`.
  *   fwd : Z
  *   bwd : gU = dZ/dU^T gZ
  *   dbwd: with L = <pU, gU>: ggZ = dL/dgZ (the forward's directional

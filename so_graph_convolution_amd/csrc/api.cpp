@@ -1904,9 +1904,8 @@ namespace {
 int check_s2(const so2s2_cfg* cfg, int64_t E) {
   if (!cfg) return fail(SO2_EINVAL, "cfg is NULL");
   if (cfg->rows < 1 || cfg->rows > 32) return fail(SO2_EUNSUPPORTED, "rows must be in [1, 32]");
-  if (cfg->channels < 1 || cfg->channels > 256) return fail(SO2_EUNSUPPORTED, "channels must be in [1, 256]");
-  if (cfg->n_grid < 1 || (long)cfg->n_grid * cfg->rows > 8192)
-    return fail(SO2_EUNSUPPORTED, "n_grid must be >= 1 with n_grid * rows <= 8192");
+  if (cfg->channels < 1 || cfg->channels > 65536) return fail(SO2_EUNSUPPORTED, "channels must be in [1, 65536]");
+  if (cfg->n_grid < 1 || cfg->n_grid > 256) return fail(SO2_EUNSUPPORTED, "n_grid must be in [1, 256]");
   if (cfg->dtype != SO2_F32) return fail(SO2_EUNSUPPORTED, "the grid activation is float32 only");
   if (cfg->flags) return fail(SO2_EINVAL, "unknown cfg flags");
   if (E < 0) return fail(SO2_EINVAL, "negative edge count");

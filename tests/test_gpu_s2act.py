@@ -1,9 +1,10 @@
 """GPU parity of the spherical-grid SwiGLU activation on edges (so2s2_*;
 TrimSO(2) page, Table 5 and Appendix B.4; the reading is stated in
 oracle/s2act_oracle.py) against the float64 oracle: forward, backward and
-double backward at small and ragged shapes (channel counts that do not divide
-the block, the largest row and channel counts), an empty edge set, and the
-full high-degree size on sampled edges."""
+double backward at small and ragged shapes (column counts that leave a partial
+16-column block, both row-tile variants and their boundary at 16 rows, the
+largest row count and grid), an empty edge set, and the full high-degree size
+on sampled edges."""
 import numpy as np
 import pytest
 import torch
@@ -17,9 +18,13 @@ DT = torch.float64
 CASES = [  # (name, E, rows, C, n_grid)
     ("tiny", 5, 3, 16, 7),
     ("lmax4_rows", 37, 19, 128, 100),
-    ("lmax6_rows", 50, 27, 64, 60),
+    ("lmax6_rows", 50, 29, 64, 60),
     ("ragged_channels", 13, 8, 24, 33),
     ("max_rows_channels", 7, 32, 256, 40),
+    ("rows16_boundary", 11, 16, 20, 17),
+    ("rows17_wide_channels", 3, 17, 300, 48),
+    ("one_row_max_grid", 9, 1, 40, 256),
+    ("max_grid_two_row_tiles", 5, 20, 32, 256),
 ]
 
 
@@ -68,11 +73,11 @@ def test_grid_activation_single_outputs_and_no_edges():
 
 
 def test_grid_activation_full_size_sampled():
-    """High-degree size (1,045,678 edges, 27 rows of lmax 6 / mmax 2, C = 128,
+    """High-degree size (1,045,678 edges, 29 rows of lmax 6 / mmax 2, C = 128,
     100 grid points) as the benchmark runs it; 48 sampled edges against the
     oracle."""
     import so_graph_convolution_amd as K
-    E, q, C, ng = 1045678, 27, 128, 100
+    E, q, C, ng = 1045678, 29, 128, 100
     gen = torch.Generator(device="cuda").manual_seed(0)
     U = torch.randn(E, q, 2 * C, device="cuda", generator=gen)
     gZ = torch.randn(E, q, C, device="cuda", generator=gen)

@@ -101,7 +101,7 @@ def test_grid_activation_host_checks():
     lib = _binding.lib()
     E_UNSUP, E_INVAL = -2, -1
     cases = [((0, 16, 10, 0, 0), E_UNSUP), ((33, 16, 10, 0, 0), E_UNSUP), ((8, 0, 10, 0, 0), E_UNSUP),
-             ((8, 257, 10, 0, 0), E_UNSUP), ((8, 16, 0, 0, 0), E_UNSUP), ((32, 16, 257, 0, 0), E_UNSUP),
+             ((8, 65537, 10, 0, 0), E_UNSUP), ((8, 16, 0, 0, 0), E_UNSUP), ((32, 16, 257, 0, 0), E_UNSUP),
              ((8, 16, 10, 1, 0), E_UNSUP), ((8, 16, 10, 0, 4), E_INVAL)]
     for fields, code in cases:
         c = S2Cfg(*fields)
