@@ -365,10 +365,16 @@ def main():
             ws_b = max(K.so2mole_workspace_bytes(kc, mix, N, E, s, 262144) for s in (0, 1, 2))
         else:
             ws_b = max(K.so2conv_chunked_workspace_bytes(kc, N, E, s, 262144) for s in (0, 1, 2))
+    # the backward keeps its cotangents for the double backward of the same step
+    # (one data-gradient product per linear less there) when memory allows
+    sb_b = 0 if mole else K.so2conv_saved_bwd_bytes(kc, E)
+    keep_bwd = not mole and saved_b + ws_b + sb_b <= 230 * 2**30
     progress(f"saved state {saved_b / 2**30:.1f} GiB, workspace {ws_b / 2**30:.1f} GiB"
-             + (" (edge chunks)" if chunked else ""))
+             + (" (edge chunks)" if chunked else "")
+             + (f", backward cotangents kept {sb_b / 2**30:.1f} GiB" if keep_bwd else ""))
     saved = torch.empty(saved_b, dtype=torch.uint8, device=dev)
     ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    saved_bwd = torch.empty(sb_b, dtype=torch.uint8, device=dev) if keep_bwd else None
     args_c = (kc, g, x, pos, rbf, w_rad, w1, w2)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -387,9 +393,10 @@ def main():
         else:
             K.so2conv_fwd(*args_c, saved=saved, ws=ws, env=env)
             e1.record()
-            K.so2conv_bwd(*args_c, saved, gy, ws=ws, env=env)
+            K.so2conv_bwd(*args_c, saved, gy, ws=ws, env=env, saved_bwd=saved_bwd)
             e2.record()
-            K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env, need=db_need)
+            K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env, need=db_need,
+                           saved_bwd=saved_bwd)
         e3.record()
         if times is not None:
             times.append((e0, e1, e2, e3))
@@ -447,7 +454,7 @@ def main():
                    + (f", {args.heads}-head attention weights times the cutoff envelope" if args.heads > 1
                       else (", cutoff envelope" if args.envelope else ""))
                    + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else ""),
-                   "edge_chunks": chunked},
+                   "edge_chunks": chunked, "backward_cotangents_kept": keep_bwd},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": None if mole else measured_gemm_traffic(args.config, dtype),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),

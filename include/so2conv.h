@@ -140,6 +140,16 @@ size_t so2conv_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t 
 size_t so2conv_chunked_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage,
                                        int64_t chunk_edges);
 size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges);
+/* so2conv_saved_bwd_bytes: the backward's per-edge cotangents of the two
+ * linears' outputs and of the first linear's input (Zbar, Ubar, Tbar; 40 KB
+ * per edge at lmax 4, C 128 in float32, 34 KB with bfloat16 operands) that
+ * so2conv_bwd writes into `saved_bwd` and so2conv_dbwd reads. In force training (Appendix A.3,
+ * Eq.(3)) the double backward follows the backward with the same gy; its
+ * reverse pass carries gy back through the tangent copy of the forward, and
+ * those cotangents depend only on gy and the forward state, so they equal
+ * the backward's. With them the double backward runs each linear's
+ * data-gradient product on E rows instead of 2E. */
+size_t so2conv_saved_bwd_bytes(const so2conv_cfg* cfg, int64_t n_edges);
 
 /* Forward: y [N,d,C]. `saved` (may be NULL) receives the state needed by
  * so2conv_bwd / so2conv_dbwd for the same inputs. */
@@ -150,11 +160,13 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
 /* Backward (vector-Jacobian product with cotangent gy, Section 3.3): gx, gpos,
  * grbf, genv, gw_rad, gw1[m], gw2[m] and gedge = dL/dv_e (for virials). `saved`
  * comes from so2conv_fwd on the same inputs, or is NULL (the forward state is
- * recomputed chunk by chunk). gw1/gw2 may be NULL, or hold NULL entries. */
+ * recomputed chunk by chunk). gw1/gw2 may be NULL, or hold NULL entries.
+ * saved_bwd (may be NULL; so2conv_saved_bwd_bytes) receives the cotangents
+ * a later so2conv_dbwd with the same inputs and gy can reuse. */
 int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
                 const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
                 const void* gy, void* gx, float* gpos, float* grbf, float* genv, void* gw_rad, void* const* gw1,
-                void* const* gw2, float* gedge, void* ws, size_t ws_bytes, void* stream);
+                void* const* gw2, float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream);
 
 /* Double backward: derivatives of
  *   L = <px, gx> + <ppos, gpos> + <pedge, gedge> + <prbf, grbf> + <penv, genv> + <pw, gw>
@@ -169,7 +181,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
                  const void* gy, const void* px, const float* ppos, const float* pedge, const float* prbf,
                  const float* penv, const void* pw_rad, const void* const* pw1, const void* const* pw2, void* ggy,
                  void* gx2, float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1_2,
-                 void* const* gw2_2, void* ws, size_t ws_bytes, void* stream);
+                 void* const* gw2_2, const void* saved_bwd, void* ws, size_t ws_bytes, void* stream);
 
 /* Test hook: the first linear's m-major input T (rotation on gather,
  * Appendix B.1) [E, q*2C], block |m| = 0..M: block 0 columns (l, c_in), block

@@ -6,6 +6,7 @@ include/so2conv.h); this package is its thin PyTorch binding.
 from ._binding import EXPORTS, LIB_PATH, So2Error, lib  # noqa: F401
 from .ops import (DBWD_KEYS, GRAD_KEYS, Graph, SO2Config, so2conv_bwd, so2conv_dbwd,  # noqa: F401
                   so2conv_debug_rotate_gather, so2conv_fwd, so2conv_graph_prepare, so2conv_saved_bytes,
+                  so2conv_saved_bwd_bytes,
                   so2conv_workspace_bytes, weight_shapes, so2conv_profile_enable, so2conv_profile_read,
                   so2conv_profile_reset, so2conv_chunked_workspace_bytes, so2conv_debug_status)
 from .grid_ops import GridConfig, so2grid_bwd, so2grid_dbwd, so2grid_fwd, so2grid_workspace_bytes  # noqa: F401

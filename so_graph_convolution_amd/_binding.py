@@ -49,15 +49,16 @@ EXPORTS = {
     "so2conv_graph_prepare": (ctypes.c_int, [c_i32, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "so2conv_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i32, c_i64, ctypes.c_int]),
     "so2conv_saved_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i64]),
+    "so2conv_saved_bwd_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i64]),
     "so2conv_chunked_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i32, c_i64, ctypes.c_int, c_i64]),
     # (cfg, g, x, pos, rbf, env, w_rad, w1, w2, y, saved, ws, ws_bytes, stream)
     "so2conv_fwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 10 + [c_sz, c_vp]),
     # (cfg, g, x, pos, rbf, env, w_rad, w1, w2, saved, gy, gx, gpos, grbf, genv, gw_rad, gw1, gw2, gedge,
     #  ws, ws_bytes, stream)
-    "so2conv_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 18 + [c_sz, c_vp]),
+    "so2conv_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 19 + [c_sz, c_vp]),
     # (cfg, g, x, pos, rbf, env, w_rad, w1, w2, saved, gy, px, ppos, pedge, prbf, penv, pw_rad, pw1, pw2,
     #  ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1_2, gw2_2, ws, ws_bytes, stream)
-    "so2conv_dbwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 26 + [c_sz, c_vp]),
+    "so2conv_dbwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 27 + [c_sz, c_vp]),
     "so2conv_debug_rotate_gather": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), c_vp, c_vp, c_vp,
                                                    c_vp, c_vp, c_vp, c_sz, c_vp]),
     "so2conv_last_error": (ctypes.c_char_p, []),

@@ -263,6 +263,37 @@ SavedLayout saved_layout(const Ctx& c, long E) {
   return s;
 }
 
+// State the backward can keep for the double backward with the same inputs
+// and gy: the cotangents Zbar [E, wZ] (float32), Ubar [E, wU] (operand type)
+// and Tbar [E, wT] (float32). They equal the cotangents of the tangent chain
+// (Zdot_bar, Udot_bar, Tdot_bar) that the double backward's reverse pass
+// would otherwise form with one more data-gradient product per linear.
+struct BwdSavedLayout {
+  size_t Z, U, T, total;
+};
+BwdSavedLayout bwd_saved_layout(const Ctx& c, long E) {
+  const Dims& d = c.d;
+  BwdSavedLayout s;
+  size_t o = 0;
+  const size_t e = (size_t)E;
+  s.Z = o; o += al(sizeof(float) * e * d.wZ());
+  s.U = o; o += al((size_t)c.es * e * d.wU());
+  s.T = o; o += al(sizeof(float) * e * d.wT());
+  s.total = o;
+  return s;
+}
+struct BwdRows {
+  float* Z;
+  void* U;
+  float* T;
+};
+BwdRows bwd_rows(const Ctx& c, const void* sb, long E, long e0) {
+  const BwdSavedLayout L = bwd_saved_layout(c, E);
+  char* b = static_cast<char*>(const_cast<void*>(sb));
+  return {reinterpret_cast<float*>(b + L.Z) + (size_t)e0 * c.d.wZ(), b + L.U + (size_t)c.es * e0 * c.d.wU(),
+          reinterpret_cast<float*>(b + L.T) + (size_t)e0 * c.d.wT()};
+}
+
 // K chunk of split-K weight-gradient products over edges (a multiple of the GEMM K tile)
 void split_plan(long K, int* splits, int* chunk) {
   long c = 4096;
@@ -1226,7 +1257,7 @@ int conv_fwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
 int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, const float* pos, const float* rbf,
              const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
              const void* gy, void* gx, float* gpos, float* grbf, float* genv, void* gw_rad, void* const* gw1,
-             void* const* gw2, float* gcoef, float* gedge, void* ws, size_t ws_bytes, void* stream) {
+             void* const* gw2, float* gcoef, float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
   int r;
   const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
@@ -1271,23 +1302,25 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
     } else {
       pr = saved_rows(c, saved, gd.E, e0);
     }
+    // the cotangents go to the caller's saved state when it keeps them
+    const BwdRows cb = saved_bwd ? bwd_rows(c, saved_bwd, gd.E, e0) : BwdRows{w.Zbar, w.Ubar, w.Tbar};
     // E -> N transpose: tbar = R gy[dst], tau1 = rotation torque of <V, R gy>
     SO2_HIP(launch_edge_bwd(d, gc, pos, gy32, pr.V, env, w.tbar, w.tau1, genv, c.bf, s));
-    if ((r = run_lin(c, 1, true, w.tbar, w.Zbar, W2, e0, n, 1, 0, s))) return r;
+    if ((r = run_lin(c, 1, true, w.tbar, cb.Z, W2, e0, n, 1, 0, s))) return r;
     if (want_w2) {
       const void* in[1] = {pr.Z};
       const void* out[1] = {w.tbar};
       if ((r = run_lin_grad(c, 1, in, out, 1, n, W2, e0, w.gW2r, mx != nullptr, w.P, s))) return r;
     }
-    SO2_HIP(launch_gate_bwd(d, n, pr.U, w.Zbar, w.Ubar, c.bf, s));
-    if ((r = run_lin(c, 0, true, w.Ubar, w.Tbar, W1, e0, n, 1, 0, s))) return r;
+    SO2_HIP(launch_gate_bwd(d, n, pr.U, cb.Z, cb.U, c.bf, s));
+    if ((r = run_lin(c, 0, true, cb.U, cb.T, W1, e0, n, 1, 0, s))) return r;
     if (want_w1) {
       const void* in[1] = {pr.T};
-      const void* out[1] = {w.Ubar};
+      const void* out[1] = {cb.U};
       if ((r = run_lin_grad(c, 0, in, out, 1, n, W1, e0, w.gW1r, mx != nullptr, w.P, s))) return r;
     }
     // N -> E transpose: gx (both halves), Sbar, position torques
-    SO2_HIP(launch_node_bwd(d, gc, x32, pos, pr.S, w.Tbar, gx_acc, w.Sbar, w.tau2, w.tau3, acc, s));
+    SO2_HIP(launch_node_bwd(d, gc, x32, pos, pr.S, cb.T, gx_acc, w.Sbar, w.tau2, w.tau3, acc, s));
     if (grbf) {
       std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, grbf + (size_t)e0 * n_rbf, n_rbf, n, n_rbf, wS)};
       if ((r = run_batch(ps, false, true, 0, s))) return r;
@@ -1324,7 +1357,8 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
               const void* gy, const void* px, const float* ppos, const float* pedge, const float* prbf,
               const float* penv, const void* pw_rad, const void* const* pw1, const void* const* pw2,
               const float* pcoef, void* ggy, void* gx2, float* gpos2, float* grbf2, float* genv2, void* gw_rad2,
-              void* const* gw1_2, void* const* gw2_2, float* gcoef2, void* ws, size_t ws_bytes, void* stream) {
+              void* const* gw1_2, void* const* gw2_2, float* gcoef2, const void* saved_bwd, void* ws,
+              size_t ws_bytes, void* stream) {
   int r;
   const Dims& d = c.d;
   if ((r = check_weights(d, w_rad, w1, w2))) return r;
@@ -1428,10 +1462,27 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     // ---- reverse of the tangent output with cotangent gy
     SO2_HIP(launch_edge_bwd_dual(d, gc, pos, w.omega, gy32, w.G2, c.bf, pr.V, w.Vdot, env, penv,
                                  gpos2 ? w.p2e : nullptr, genv2, s));
+    // The reverse pass's cotangents of the tangent chain (Zdot_bar, Udot_bar,
+    // Tdot_bar) depend only on gy and the primal: they are the backward's
+    // (Zbar, Ubar, Tbar). With the backward's saved state only the second
+    // halves (cotangents of the primal chain) are formed here.
+    const BwdRows sb = saved_bwd ? bwd_rows(c, saved_bwd, gd.E, e0) : BwdRows{nullptr, nullptr, nullptr};
+    float* Zb = w.ZZ + (size_t)n * d.wZ();
+    const float* Zdb = saved_bwd ? sb.Z : w.ZZ;
+    void* Ub = offs(w.UU, (size_t)n * d.wU(), c.es);
+    const void* Udb = saved_bwd ? sb.U : w.UU;
+    float* Tb = w.TT + (size_t)n * d.wT();
+    const float* Tdb = saved_bwd ? sb.T : w.TT;
     // [Zdot_bar; Zbar] = G2 W2^T (2n stacked rows)
-    if ((r = run_lin(c, 1, true, w.G2, w.ZZ, W2, e0, n, 2, 0, s))) return r;
+    if (saved_bwd) {
+      if ((r = run_lin(c, 1, true, offs(static_cast<const void*>(w.G2), (size_t)n * d.wZ(), c.es), Zb, W2, e0, n, 1,
+                       0, s)))
+        return r;
+    } else if ((r = run_lin(c, 1, true, w.G2, w.ZZ, W2, e0, n, 2, 0, s))) {
+      return r;
+    }
     // Zbar += tbar pW2^T
-    if (has_pw2 && (r = run_lin(c, 1, true, w.G2, w.ZZ + (size_t)n * d.wZ(), pW2, e0, n, 1, 1, s))) return r;
+    if (has_pw2 && (r = run_lin(c, 1, true, w.G2, Zb, pW2, e0, n, 1, 1, s))) return r;
     if (want_w2) {
       const void* in[2] = {w.Zdot, pr.Z};
       const void* out[2] = {w.G2, offs(static_cast<const void*>(w.G2), (size_t)n * d.wZ(), c.es)};
@@ -1439,19 +1490,24 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
       // first-order gradient Z^T tbar (tbar: the first n rows of G2)
       if (first && (r = run_lin_grad(c, 1, &in[1], out, 1, n, W2, e0, w.gW2f, true, w.P, s))) return r;
     }
-    SO2_HIP(launch_gate_dbwd(d, n, pr.U, w.Udot, w.ZZ, w.UU, c.bf, s));   // [Udot_bar; Ubar]
+    // [Udot_bar; Ubar]
+    SO2_HIP(launch_gate_dbwd(d, n, pr.U, w.Udot, Zdb, Zb, saved_bwd ? nullptr : w.UU, Ub, c.bf, s));
     // [Tdot_bar; Tbar] = UU W1^T
-    if ((r = run_lin(c, 0, true, w.UU, w.TT, W1, e0, n, 2, 0, s))) return r;
+    if (saved_bwd) {
+      if ((r = run_lin(c, 0, true, Ub, Tb, W1, e0, n, 1, 0, s))) return r;
+    } else if ((r = run_lin(c, 0, true, w.UU, w.TT, W1, e0, n, 2, 0, s))) {
+      return r;
+    }
     // Tbar += Udot_bar pW1^T
-    if (has_pw1 && (r = run_lin(c, 0, true, w.UU, w.TT + (size_t)n * d.wT(), pW1, e0, n, 1, 1, s))) return r;
+    if (has_pw1 && (r = run_lin(c, 0, true, Udb, Tb, pW1, e0, n, 1, 1, s))) return r;
     if (want_w1) {
       const void* in[2] = {w.Tdot, pr.T};
-      const void* out[2] = {w.UU, offs(static_cast<const void*>(w.UU), (size_t)n * d.wU(), c.es)};
+      const void* out[2] = {Udb, Ub};
       if ((r = run_lin_grad(c, 0, in, out, 2, n, W1, e0, w.gW1r, mx != nullptr, w.P, s))) return r;
       // first-order gradient T^T Ubar (Ubar: the first n rows of UU)
       if (first && (r = run_lin_grad(c, 0, &in[1], out, 1, n, W1, e0, w.gW1f, true, w.P, s))) return r;
     }
-    SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, w.TT, gx2_acc, w.Sbar, w.Sdb,
+    SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, Tdb, Tb, gx2_acc, w.Sbar, w.Sdb,
                                  gpos2 ? w.p2d : nullptr, gpos2 ? w.p2s : nullptr, acc, s));
     if (gpos2) SO2_HIP(launch_pos2(gc, pos, ppos, pedge, w.omega, w.p2e, w.p2d, w.p2s, w.vbar2_all, s));
     if (grbf2) {
@@ -1567,6 +1623,12 @@ size_t so2conv_saved_bytes(const so2conv_cfg* cfg, int64_t n_edges) {
   return saved_layout(c, n_edges).total;
 }
 
+size_t so2conv_saved_bwd_bytes(const so2conv_cfg* cfg, int64_t n_edges) {
+  Ctx c;
+  if (check_cfg(cfg, &c) || n_edges < 0) return 0;
+  return bwd_saved_layout(c, n_edges).total;
+}
+
 size_t so2conv_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, int64_t n_edges, int stage) {
   Ctx c;
   if (check_cfg(cfg, &c) || stage < 0 || stage > 2 || n_nodes < 0 || n_edges < 0) return 0;
@@ -1625,14 +1687,14 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
 int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
                 const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
                 const void* gy, void* gx, float* gpos, float* grbf, float* genv, void* gw_rad, void* const* gw1,
-                void* const* gw2, float* gedge, void* ws, size_t ws_bytes, void* stream) {
+                void* const* gw2, float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   Ctx c;
   GraphDev gd;
   int r;
   if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
   return conv_bwd(c, gd, nullptr, x, pos, rbf, env, w_rad, w1, w2, saved, gy, gx, gpos, grbf, genv, gw_rad, gw1, gw2,
-                  nullptr, gedge, ws, ws_bytes, stream);
+                  nullptr, gedge, saved_bwd, ws, ws_bytes, stream);
 }
 
 int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
@@ -1640,15 +1702,15 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
                  const void* gy, const void* px, const float* ppos, const float* pedge, const float* prbf,
                  const float* penv, const void* pw_rad, const void* const* pw1, const void* const* pw2, void* ggy,
                  void* gx2, float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1_2,
-                 void* const* gw2_2, void* ws, size_t ws_bytes, void* stream) {
+                 void* const* gw2_2, const void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   Ctx c;
   GraphDev gd;
   int r;
   if ((r = check_cfg(cfg, &c)) || (r = check_graph(g, &gd))) return r;
   return conv_dbwd(c, gd, nullptr, x, pos, rbf, env, w_rad, w1, w2, saved, gy, px, ppos, pedge, prbf, penv, pw_rad,
-                   pw1, pw2, nullptr, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1_2, gw2_2, nullptr, ws, ws_bytes,
-                   stream);
+                   pw1, pw2, nullptr, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1_2, gw2_2, nullptr, saved_bwd, ws,
+                   ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- mixture of linear experts entry points
@@ -1743,7 +1805,7 @@ int so2mole_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cf
     return zero_mole_grads(c, gw1e, gw2e, gcoef, s);
   }
   return conv_bwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, saved, gy, gx, gpos, grbf, genv, gw_rad, gw1e, gw2e,
-                  gcoef, gedge, ws, ws_bytes, stream);
+                  gcoef, gedge, nullptr, ws, ws_bytes, stream);
 }
 
 int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
@@ -1767,8 +1829,8 @@ int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_c
     return zero_mole_grads(c, gw1e_2, gw2e_2, gcoef2, s);
   }
   return conv_dbwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, saved, gy, px, ppos, pedge, prbf, penv, pw_rad,
-                   pw1e, pw2e, pcoef, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2, ws, ws_bytes,
-                   stream);
+                   pw1e, pw2e, pcoef, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2, nullptr, ws,
+                   ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- spherical projection entry points

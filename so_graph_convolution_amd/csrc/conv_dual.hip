@@ -427,7 +427,8 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
                                                             const float* __restrict__ omega,
                                                             const float* __restrict__ S,
                                                             const float* __restrict__ Sdot,
-                                                            const float* __restrict__ TT, float* __restrict__ gx2,
+                                                            const float* __restrict__ Tdb,
+                                                            const float* __restrict__ Tb, float* __restrict__ gx2,
                                                             float* __restrict__ Sbar, float* __restrict__ Sdb,
                                                             float* __restrict__ p2_dst, float* __restrict__ p2_src,
                                                             int accumulate) {
@@ -458,8 +459,6 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
     xdn[r] = (act && px) ? px[o] : 0.f;
     acc[r] = 0.f;
   }
-  const float* Tdb = TT;
-  const float* Tb = TT + (size_t)(g.e1 - g.e0) * wT;
   for (int pass = 0; pass < 2; ++pass) {
     int beg, end;
     if (pass == 0) in_range(g, node, &beg, &end);
@@ -579,16 +578,17 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
 template <int L, int M>
 struct NodeBwdDual {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
-                 const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2, float* Sbar,
+                 const float* omega, const float* S, const float* Sdot, const float* Tdb, const float* Tb,
+                 float* gx2, float* Sbar,
                  float* Sdb, float* p2_dst, float* p2_src, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = 2 * ((d.C + 63) / 64) * 64;
     if (p2_dst)
       hipLaunchKernelGGL((node_bwd_dual_kernel<L, M, true>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega,
-                         S, Sdot, TT, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
+                         S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
     else
       hipLaunchKernelGGL((node_bwd_dual_kernel<L, M, false>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega,
-                         S, Sdot, TT, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
+                         S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
     return hipGetLastError();
   }
 };
@@ -673,20 +673,22 @@ __global__ void gate_dual_kernel(Dims d, long E, const float* __restrict__ U, co
   }
 }
 
-// ZZ = [zdot_bar (E rows); zbar (E rows)] -> UU = [udot_bar; ubar]
-template <typename OT>
+// (zdot_bar, zbar) -> (udot_bar, ubar), E rows each; with WD false udot_bar
+// is not written (the caller already holds it: it is the backward's ubar)
+template <typename OT, bool WD>
 __global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, const float* __restrict__ Ud,
-                                 const float* __restrict__ ZZ, OT* __restrict__ UU) {
+                                 const float* __restrict__ Zdb, const float* __restrict__ Zb,
+                                 OT* __restrict__ Udb, OT* __restrict__ Ub) {
   const int L = d.L, M = d.M, C = d.C;
   const int c = 4 * threadIdx.x, l = threadIdx.y;
   const int wU = d.wU(), wZ = d.wZ();
   for (long e = (long)blockIdx.x * blockDim.z + threadIdx.z; e < E; e += (long)gridDim.x * blockDim.z) {
     const float* ur = U + e * wU;
     const float* udr = Ud + e * wU;
-    const float* zdb = ZZ + e * wZ;
-    const float* zb = ZZ + (E + e) * wZ;
-    OT* udb = UU + e * wU;
-    OT* ub = UU + (E + e) * wU;
+    const float* zdb = Zdb + e * wZ;
+    const float* zb = Zb + e * wZ;
+    OT* udb = WD ? Udb + e * wU : nullptr;
+    OT* ub = Ub + e * wU;
     float u[4], ud[4], a[4], b[4], o1[4], o2[4];
     if (l == 0) {
       ld4(ur + c, u);
@@ -701,7 +703,7 @@ __global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, co
         o1[i] = s1 * a[i];
         o2[i] = s2 * ud[i] * a[i] + s1 * b[i];
       }
-      st4(udb + c, o1);
+      if (WD) st4(udb + c, o1);
       st4(ub + c, o2);
     } else {
       const int gc = d.gate_col(l, c);
@@ -728,12 +730,12 @@ __global__ void gate_dbwd_kernel(Dims d, long E, const float* __restrict__ U, co
           gdb[i] += a[i] * u[i];
           gb[i] += spp[i] * gd[i] * u[i] * a[i] + sp[i] * ud[i] * a[i] + sp[i] * u[i] * b[i];
         }
-        st4(udb + uc, o1);
+        if (WD) st4(udb + uc, o1);
         st4(ub + uc, o2);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) o1[i] = sp[i] * gdb[i];
-      st4(udb + gc, o1);
+      if (WD) st4(udb + gc, o1);
       st4(ub + gc, gb);
     }
   }
@@ -785,23 +787,33 @@ int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const fl
   return hipGetLastError();
 }
 
-int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, void* UU, int bf16,
-                     hipStream_t s) {
+int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* Zdb, const float* Zb,
+                     void* Udb, void* Ub, int bf16, hipStream_t s) {
   if (E == 0) return hipSuccess;
   dim3 grid, block;
   gate_dims(d, E, &grid, &block);
-  if (bf16)
-    hipLaunchKernelGGL(gate_dbwd_kernel<bf16s>, grid, block, 0, s, d, E, U, Udot, ZZ, static_cast<bf16s*>(UU));
-  else
-    hipLaunchKernelGGL(gate_dbwd_kernel<float>, grid, block, 0, s, d, E, U, Udot, ZZ, static_cast<float*>(UU));
+  if (bf16) {
+    bf16s *o1 = static_cast<bf16s*>(Udb), *o2 = static_cast<bf16s*>(Ub);
+    if (Udb)
+      hipLaunchKernelGGL((gate_dbwd_kernel<bf16s, true>), grid, block, 0, s, d, E, U, Udot, Zdb, Zb, o1, o2);
+    else
+      hipLaunchKernelGGL((gate_dbwd_kernel<bf16s, false>), grid, block, 0, s, d, E, U, Udot, Zdb, Zb, o1, o2);
+  } else {
+    float *o1 = static_cast<float*>(Udb), *o2 = static_cast<float*>(Ub);
+    if (Udb)
+      hipLaunchKernelGGL((gate_dbwd_kernel<float, true>), grid, block, 0, s, d, E, U, Udot, Zdb, Zb, o1, o2);
+    else
+      hipLaunchKernelGGL((gate_dbwd_kernel<float, false>), grid, block, 0, s, d, E, U, Udot, Zdb, Zb, o1, o2);
+  }
   return hipGetLastError();
 }
 
 int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
-                         const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
-                         float* Sbar, float* Sdot_bar, float* p2_dst, float* p2_src, int accumulate, hipStream_t s) {
-  return dispatch_lm<NodeBwdDual>(d.L, d.M, d, g, x, px, pos, omega, S, Sdot, TT, gx2, Sbar, Sdot_bar, p2_dst, p2_src,
-                                  accumulate, s);
+                         const float* omega, const float* S, const float* Sdot, const float* Tdb, const float* Tb,
+                         float* gx2, float* Sbar, float* Sdot_bar, float* p2_dst, float* p2_src, int accumulate,
+                         hipStream_t s) {
+  return dispatch_lm<NodeBwdDual>(d.L, d.M, d, g, x, px, pos, omega, S, Sdot, Tdb, Tb, gx2, Sbar, Sdot_bar, p2_dst,
+                                  p2_src, accumulate, s);
 }
 
 }  // namespace so2

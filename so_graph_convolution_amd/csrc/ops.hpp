@@ -76,14 +76,16 @@ int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, con
 // from the three [E][6] torque/rate parts (chunk-relative rows)
 int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const float* pedge, const float* omega,
                 const float* pe, const float* pd, const float* ps, float* vbar2, hipStream_t s);
-// from ZZ = [Zdot_bar; Zbar] produce UU (operand) = [Udot_bar; Ubar]
-int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* ZZ, void* UU, int bf16,
-                     hipStream_t s);
-// gx2 and (Sbar, Sdot_bar) from TT = [Tdot_bar; Tbar]; with p2_dst/p2_src (not null) also the
-// per-edge torque and rate cotangent [E][6] of the rotation on gather, per half
+// from (Zdot_bar, Zbar) produce the operands (Udot_bar, Ubar), E rows each;
+// Udb NULL: Udot_bar is not written
+int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* Zdb, const float* Zb,
+                     void* Udb, void* Ub, int bf16, hipStream_t s);
+// gx2 and (Sbar, Sdot_bar) from Tdot_bar (Tdb) and Tbar (Tb), chunk rows each; with p2_dst/p2_src
+// (not null) also the per-edge torque and rate cotangent [E][6] of the rotation on gather, per half
 int launch_node_bwd_dual(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
-                         const float* omega, const float* S, const float* Sdot, const float* TT, float* gx2,
-                         float* Sbar, float* Sdot_bar, float* p2_dst, float* p2_src, int accumulate, hipStream_t s);
+                         const float* omega, const float* S, const float* Sdot, const float* Tdb, const float* Tb,
+                         float* gx2, float* Sbar, float* Sdot_bar, float* p2_dst, float* p2_src, int accumulate,
+                         hipStream_t s);
 
 // ---- weights
 // Wr (realified per order): block 0 = W[0]; block m = [[W_m0, W_m1], [-W_m1, W_m0]].

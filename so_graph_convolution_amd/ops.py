@@ -14,7 +14,8 @@ import torch
 from ._binding import SO2_DEBUG_CHECKS, Cfg, GraphC, check, lib
 
 __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_bwd", "so2conv_dbwd",
-           "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes", "weight_shapes",
+           "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes",
+           "so2conv_saved_bwd_bytes", "weight_shapes",
            "so2conv_profile_enable", "so2conv_profile_reset", "so2conv_profile_read",
            "so2conv_chunked_workspace_bytes", "so2conv_debug_status"]
 
@@ -149,6 +150,11 @@ def so2conv_saved_bytes(cfg: SO2Config, n_edges) -> int:
     return int(lib().so2conv_saved_bytes(ctypes.byref(c), n_edges))
 
 
+def so2conv_saved_bwd_bytes(cfg: SO2Config, n_edges) -> int:
+    c = cfg.c()
+    return int(lib().so2conv_saved_bwd_bytes(ctypes.byref(c), n_edges))
+
+
 def so2conv_chunked_workspace_bytes(cfg: SO2Config, n_nodes, n_edges, stage, chunk_edges) -> int:
     c = cfg.c()
     return int(lib().so2conv_chunked_workspace_bytes(ctypes.byref(c), n_nodes, n_edges, stage, chunk_edges))
@@ -205,9 +211,11 @@ GRAD_KEYS = ("x", "pos", "rbf", "w_rad", "w1", "w2", "edge", "env")
 
 
 def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, need=GRAD_KEYS, ws=None,
-                chunk_edges=None, env=None):
+                chunk_edges=None, env=None, saved_bwd=None):
     """Returns dict gx, gpos, grbf, gw_rad, gw1, gw2, gedge and, with an envelope,
-    genv (requested ones). saved=None recomputes the forward state chunk by chunk."""
+    genv (requested ones). saved=None recomputes the forward state chunk by chunk.
+    saved_bwd=True (or a buffer of so2conv_saved_bwd_bytes) keeps the cotangents
+    a double backward with the same inputs and gy can reuse (out["saved_bwd"])."""
     _common(cfg, g, x, pos, rbf, w_rad, env)
     dt = cfg.torch_dtype
     _dev(gy, "gy", dtype=dt, shape=x.shape)
@@ -226,12 +234,19 @@ def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy,
     out["genv"] = torch.empty_like(env) if ("env" in need and env is not None) else None
     q1, k3 = _ptr_array(out["gw1"], "gw1", s1, dt)
     q2, k4 = _ptr_array(out["gw2"], "gw2", s2, dt)
+    if saved_bwd is True:
+        saved_bwd = _ws(so2conv_saved_bwd_bytes(cfg, g.n_edges), dev)
+    elif saved_bwd is not None:
+        _dev(saved_bwd, "saved_bwd", dtype=torch.uint8)
+        if saved_bwd.numel() < so2conv_saved_bwd_bytes(cfg, g.n_edges):
+            raise ValueError("saved_bwd is smaller than so2conv_saved_bwd_bytes")
+    out["saved_bwd"] = saved_bwd
     ws = _ws_for(cfg, g, 1, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_bwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1, p2,
                             _p(saved), _p(gy), _p(out["gx"]), _p(out["gpos"]), _p(out["grbf"]), _p(out["genv"]),
-                            _p(out["gw_rad"]), q1, q2, _p(out["gedge"]), _p(ws), ws.numel(), _stream()),
-          "so2conv_bwd")
+                            _p(out["gw_rad"]), q1, q2, _p(out["gedge"]), _p(saved_bwd), _p(ws), ws.numel(),
+                            _stream()), "so2conv_bwd")
     return out
 
 
@@ -240,9 +255,10 @@ DBWD_KEYS = ("gy", "x", "rbf", "w_rad", "w1", "w2")   # the force-training patte
 
 def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy, px=None, ppos=None, pedge=None,
                  prbf=None, pw_rad=None, pw1=None, pw2=None, need=DBWD_KEYS, ws=None, chunk_edges=None, env=None,
-                 penv=None):
+                 penv=None, saved_bwd=None):
     """Returns dict ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1_2, gw2_2 (requested ones;
-    gpos2 only when "pos" is in need, genv2 when "env" is and an envelope is given)."""
+    gpos2 only when "pos" is in need, genv2 when "env" is and an envelope is given).
+    saved_bwd: out["saved_bwd"] of so2conv_bwd on the same inputs and gy, or None."""
     _common(cfg, g, x, pos, rbf, w_rad, env)
     _dev(penv, "penv", shape=cfg.env_shape(g.n_edges))
     dt = cfg.torch_dtype
@@ -269,12 +285,16 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     out["gw2_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     q1, k3 = _ptr_array(out["gw1_2"], "gw1_2", s1, dt)
     q2, k4 = _ptr_array(out["gw2_2"], "gw2_2", s2, dt)
+    if saved_bwd is not None:
+        _dev(saved_bwd, "saved_bwd", dtype=torch.uint8)
+        if saved_bwd.numel() < so2conv_saved_bwd_bytes(cfg, g.n_edges):
+            raise ValueError("saved_bwd is smaller than so2conv_saved_bwd_bytes")
     ws = _ws_for(cfg, g, 2, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1,
                              p2, _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf), _p(penv), _p(pw_rad), pp1,
                              pp2, _p(out["ggy"]), _p(out["gx2"]), _p(out["gpos2"]), _p(out["grbf2"]),
-                             _p(out["genv2"]), _p(out["gw_rad2"]), q1, q2,
+                             _p(out["genv2"]), _p(out["gw_rad2"]), q1, q2, _p(saved_bwd),
                              _p(ws), ws.numel(), _stream()), "so2conv_dbwd")
     return out
 

@@ -40,13 +40,16 @@ def medium():
     kc = dd["kcfg"]
     saved = torch.empty(K.so2conv_saved_bytes(kc, E), dtype=torch.uint8, device="cuda")
     ws = torch.empty(max(K.so2conv_workspace_bytes(kc, N, E, s) for s in (0, 1, 2)), dtype=torch.uint8, device="cuda")
+    # as bench.py runs it: the backward keeps its cotangents for the double backward
+    kept = torch.empty(K.so2conv_saved_bwd_bytes(kc, E), dtype=torch.uint8, device="cuda")
     y, _ = K.so2conv_fwd(*args, saved=saved, ws=ws)
-    bw = K.so2conv_bwd(*args, saved, dd["gy"], ws=ws)
-    db = K.so2conv_dbwd(*args, saved, dd["gy"], px=dd["px"], ppos=dd["ppos"], prbf=dd["prbf"], ws=ws)
+    bw = K.so2conv_bwd(*args, saved, dd["gy"], ws=ws, saved_bwd=kept)
+    db = K.so2conv_dbwd(*args, saved, dd["gy"], px=dd["px"], ppos=dd["ppos"], prbf=dd["prbf"], ws=ws,
+                        saved_bwd=kept)
     torch.cuda.synchronize()
     out = dict(y=y.cpu(), **{k: (v.cpu() if isinstance(v, torch.Tensor) else [w.cpu() for w in v])
-                             for k, v in {**bw, **db}.items() if v is not None})
-    del saved, ws
+                             for k, v in {**bw, **db}.items() if v is not None and k != "saved_bwd"})
+    del saved, ws, kept, bw, db
     torch.cuda.empty_cache()
     rng = np.random.default_rng(123)
     nodes = np.sort(rng.choice(N, 4, replace=False))

@@ -111,3 +111,14 @@ def test_grid_activation_host_checks():
     assert lib.so2s2_fwd(ctypes.byref(c), -1, None, None, None, None, None) == E_INVAL
     assert lib.so2s2_bwd(ctypes.byref(c), 4, None, None, None, None, None, None) == E_INVAL
     assert lib.so2s2_dbwd(ctypes.byref(c), 4, None, None, None, None, None, None, None, None) == E_INVAL
+
+
+def test_saved_backward_state_bytes():
+    """The backward's kept cotangents: Zbar and Tbar float32, Ubar in the
+    operand type."""
+    import so_graph_convolution_amd as K
+    f32, bf16 = K.SO2Config(4, 2, 128, 64), K.SO2Config(4, 2, 128, 64, "bf16")
+    # per edge at lmax 4, C 128: Zbar 2432 + Tbar 4864 floats, Ubar 2944 elements
+    assert K.so2conv_saved_bwd_bytes(f32, 1024) == 1024 * 40960
+    assert K.so2conv_saved_bwd_bytes(bf16, 1024) == 1024 * 35072
+    assert K.so2conv_saved_bwd_bytes(K.SO2Config(4, 5, 128, 64), 10) == 0   # mmax > lmax
