@@ -50,10 +50,11 @@ def gemm_flops_per_edge(L, M, C):
     return 2.0 * (mac1 + mac2)
 
 
-def measured_gemm_traffic(config, dtype):
+def measured_gemm_traffic(config, dtype, keep_bwd):
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters (copy-calibrated) of the medium float32 step, or None for another
-    workload or if the GEMM source (gemm.hip, gemm.hpp) changed since."""
+    workload, another launch mix (backward cotangents kept or not) or if the
+    GEMM source (gemm.hip, gemm.hpp) changed since."""
     import hashlib
     if config != "M" or dtype != "f32":
         return None
@@ -64,6 +65,8 @@ def measured_gemm_traffic(config, dtype):
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    if bool(rec.get("backward_cotangents_kept")) != bool(keep_bwd):
         return None
     return rec["gemm_bytes_per_step"] / rec["gemm_launches_per_step"]
 
@@ -456,7 +459,7 @@ def main():
                    + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else ""),
                    "edge_chunks": chunked, "backward_cotangents_kept": keep_bwd},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None if mole else measured_gemm_traffic(args.config, dtype),
+                     "frac": achieved / peak, "traffic": None if mole else measured_gemm_traffic(args.config, dtype, keep_bwd),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
                      "kernel": kname,
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
