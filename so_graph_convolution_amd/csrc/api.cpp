@@ -653,12 +653,17 @@ int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int acc
            hipStream_t s) {
   std::vector<GemmProb> ps;
   int total_splits = 0;
+  // a thin side of at most 64 (the radial map's n_rbf rows) becomes the
+  // product's columns: the partials then hold G^T and the reduction
+  // writes G back transposed
+  const bool swap = M <= 64 && N > M && !bf;
   for (int q = 0; q < nseg; ++q) {
     if (segs[q].K <= 0) continue;
     int sp, ch;
     split_plan(segs[q].K, &sp, &ch);
-    GemmProb p = prob(segs[q].A, segs[q].lda, segs[q].B, segs[q].ldb, P + (size_t)total_splits * M * N, N, M, N,
-                      (int)segs[q].K);
+    float* Pq = P + (size_t)total_splits * M * N;
+    GemmProb p = swap ? prob(segs[q].B, segs[q].ldb, segs[q].A, segs[q].lda, Pq, M, N, M, (int)segs[q].K)
+                      : prob(segs[q].A, segs[q].lda, segs[q].B, segs[q].ldb, Pq, N, M, N, (int)segs[q].K);
     p.k_splits = sp;
     p.k_chunk = ch;
     p.partial = 1;
@@ -668,7 +673,8 @@ int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int acc
   if (total_splits == 0) return SO2_OK;
   int r = run_batch(ps, true, false, bf, s);
   if (r) return r;
-  SO2_HIP(gemm_reduce(P, total_splits, M, N, G, ldg, accumulate, s));
+  SO2_HIP(swap ? gemm_reduce(P, total_splits, N, M, G, ldg, accumulate, s, 1)
+               : gemm_reduce(P, total_splits, M, N, G, ldg, accumulate, s));
   return SO2_OK;
 }
 

@@ -572,10 +572,11 @@ __device__ inline void dstage(const DSlot (&sl)[SL], float* st, int t, int nkk, 
 // t + 1, if issued, may still be in flight) and publish the stage to the block
 template <int SL>
 __device__ __forceinline__ void dsync(bool next_in_flight) {
-  static_assert(SL == 2 || SL == 3, "loads per wave and stage");
+  static_assert(SL == 2 || SL == 3 || SL == 5, "loads per wave and stage");
   if (!next_in_flight) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   else if (SL == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
+  else if (SL == 3) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -940,13 +941,13 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 }
 
 __global__ void gemm_reduce_kernel(const float* __restrict__ P, int splits, int M, int N, float* __restrict__ C,
-                                   int ldc, int accumulate) {
+                                   int ldc, int accumulate, int trans) {
   const size_t n = (size_t)M * N;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
     float s = 0.f;
     for (int q = 0; q < splits; ++q) s += P[(size_t)q * n + idx];
     const size_t i = idx / N, j = idx - i * N;
-    float* dst = C + i * ldc + j;
+    float* dst = trans ? C + j * ldc + i : C + i * ldc + j;
     *dst = accumulate ? *dst + s : s;
   }
 }
@@ -976,8 +977,12 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   for (int q = 0; q < b.nprob; ++q)
     if ((b.p[q].cplx != 0) != cx) return hipErrorInvalidValue;
   const bool dma = !bf16 && dma_ok(b, TA, TB);
+  // weight-gradient products at most 64 columns wide (the radial map's, with
+  // the n_rbf side as columns): blocks of 256 x 64, four waves
+  bool narrow = dma && !cx && TA && !TB;
+  for (int q = 0; q < b.nprob && narrow; ++q) narrow = b.p[q].N <= 64;
   const int bm = cx ? CBM : (bf16 ? BMH : BM);
-  const int bn = cx ? (dma ? 32 * kCxWNW : CBN) : (bf16 ? BNH : (dma ? 64 * kF32WNW : BN));
+  const int bn = cx ? (dma ? 32 * kCxWNW : CBN) : (bf16 ? BNH : (narrow ? 64 : (dma ? 64 * kF32WNW : BN)));
   int total = 0;
   for (int q = 0; q < b.nprob; ++q) {
     GemmProb& p = b.p[q];
@@ -1002,6 +1007,8 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
       hipLaunchKernelGGL((gemm_f32_dma_kernel<false, false, W>), grid, fb, 0, s, b);
     } else if (!TA && TB) {
       hipLaunchKernelGGL((gemm_f32_dma_kernel<false, true, W>), grid, fb, 0, s, b);
+    } else if (TA && !TB && narrow) {
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<true, false, 1>), grid, dim3(64 * WAVES_M), 0, s, b);
     } else if (TA && !TB) {
       hipLaunchKernelGGL((gemm_f32_dma_kernel<true, false, W>), grid, fb, 0, s, b);
     } else {
@@ -1027,12 +1034,13 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
-int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s) {
+int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s,
+                int trans) {
   const size_t n = (size_t)M * N;
   if (n == 0) return hipSuccess;
   int blocks = (int)((n + 255) / 256);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(gemm_reduce_kernel, dim3(blocks), dim3(256), 0, s, P, splits, M, N, C, ldc, accumulate);
+  hipLaunchKernelGGL(gemm_reduce_kernel, dim3(blocks), dim3(256), 0, s, P, splits, M, N, C, ldc, accumulate, trans);
   return hipGetLastError();
 }
 

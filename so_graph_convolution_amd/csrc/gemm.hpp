@@ -60,7 +60,9 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s);
 // K tile of the kernels: split chunks of TA problems are multiples of it
 constexpr int kGemmKTile = 64;
 
-// C[i*ldc + j] (+)= sum_{s < splits} P[s][i][j]  (fixed order)
-int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s);
+// C[i*ldc + j] (+)= sum_{s < splits} P[s][i][j]  (fixed order); with trans,
+// C[j*ldc + i] instead (the partials hold the transposed product)
+int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s,
+                int trans = 0);
 
 }  // namespace so2
