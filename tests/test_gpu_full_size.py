@@ -1,4 +1,6 @@
-"""Parity at the benchmark's full sizes, in the launch configuration bench.py times.
+"""Parity at the benchmark's full sizes, in the launch configuration bench.py times
+(the medium system with forward, backward and double backward; the eSEN-like
+small system with forward and backward).
 
 Node outputs are sums over a node's incident edges and per-edge outputs
 depend on their own edge only, so the oracle evaluates them exactly on the
@@ -136,5 +138,77 @@ def test_full_size_weight_gradients_additive(medium):
             errs[key] = H.relerr(full, [(x + y).cpu() for x, y in zip(a, b)])
         else:
             errs[key] = H.relerr(full, (a + b).cpu())
+    H.note("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= H.TOL_F32 for v in errs.values()), errs
+
+
+@pytest.fixture(scope="module")
+def small():
+    """eSEN-like small system: 2,000 atoms at 0.1 atoms/A^3, 6 A cutoff (~181k
+    edges), lmax 2, mmax 2, C 128, float32; forward and backward with respect
+    to features, weights and positions, with the saved forward state."""
+    import so_graph_convolution_amd as K
+    cfg = so2_synth.CONFIGS["S"]
+    d = so2_synth.make_inputs(cfg)
+    E, N = len(d["src"]), cfg.n_atoms
+    H.note(f"[full size] small workload N={N} E={E}")
+    dd = H.to_dev(d)
+    args = (dd["kcfg"], dd["g"], dd["x"], dd["pos"], dd["rbf"], dd["w_rad"], dd["w1"], dd["w2"])
+    y, saved = K.so2conv_fwd(*args, saved=True)
+    bw = K.so2conv_bwd(*args, saved, dd["gy"])
+    torch.cuda.synchronize()
+    out = dict(y=y.cpu(), **{k: (v.cpu() if isinstance(v, torch.Tensor) else [w.cpu() for w in v])
+                             for k, v in bw.items() if v is not None and k != "saved_bwd"})
+    del saved, bw
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(321)
+    nodes = np.sort(rng.choice(N, 6, replace=False))
+    edges = np.sort(rng.choice(E, 64, replace=False))
+    return d, dd, out, nodes, edges
+
+
+def test_small_full_size_forward_backward_sampled(small):
+    d, dd, out, nodes, edges = small
+    inp = H.oracle_inputs(d)
+    gy = torch.tensor(d["gy"], dtype=DT)
+    ry = O.forward(inp, edges=_incoming(d, nodes))[nodes]
+    rn = O.backward(inp, gy, edges=_incident(d, nodes))
+    re = O.backward(inp, gy, edges=edges, with_edge_grad=True)
+    errs = {"y": H.relerr(out["y"][nodes], ry),
+            "gx": H.relerr(out["gx"][nodes], rn["gx"][nodes]),
+            "gpos": H.relerr(out["gpos"][nodes], rn["gpos"][nodes]),
+            "grbf": H.relerr(out["grbf"][edges], re["grbf"][edges]),
+            "gedge": H.relerr(out["gedge"][edges], re["gedge"][edges])}
+    H.note("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= H.TOL_F32 for v in errs.values()), errs
+
+
+def test_small_full_size_weight_gradients(small):
+    """<gW2, W2> = <gy, y> (y is linear in W2), and every weight gradient over
+    all edges equals the sum over two halves of the receivers."""
+    import so_graph_convolution_amd as K
+    d, dd, out, _, _ = small
+    lhs = sum(float((g.double() * torch.tensor(w, dtype=DT)).sum()) for g, w in zip(out["gw2"], d["w2"]))
+    rhs = float((out["y"].double() * torch.tensor(d["gy"], dtype=DT)).sum())
+    H.note(f"  <gW2,W2>={lhs:.6e} <gy,y>={rhs:.6e}")
+    assert abs(lhs - rhs) <= 1e-4 * abs(rhs)
+    N = d["cfg"].n_atoms
+    cut = int(np.searchsorted(d["dst"], N // 2))
+    parts = []
+    for sl in (slice(0, cut), slice(cut, len(d["src"]))):
+        g = K.so2conv_graph_prepare(N, torch.tensor(d["src"][sl], device="cuda"),
+                                    torch.tensor(d["dst"][sl], device="cuda"),
+                                    torch.tensor(d["shift"][sl], device="cuda"))
+        args = (dd["kcfg"], g, dd["x"], dd["pos"], torch.tensor(d["rbf"][sl], device="cuda"), dd["w_rad"],
+                dd["w1"], dd["w2"])
+        _, saved = K.so2conv_fwd(*args, saved=True)
+        parts.append(K.so2conv_bwd(*args, saved, dd["gy"], need=("w1", "w2", "w_rad")))
+        torch.cuda.synchronize()
+    errs = {}
+    for key in ("gw1", "gw2", "gw_rad"):
+        a, b = parts[0][key], parts[1][key]
+        full = out[key]
+        errs[key] = H.relerr(full, [(x + y).cpu() for x, y in zip(a, b)]) if isinstance(full, list) \
+            else H.relerr(full, (a + b).cpu())
     H.note("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= H.TOL_F32 for v in errs.values()), errs
