@@ -1034,10 +1034,41 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
+// four adjacent columns per thread with 16-byte loads and stores (same order of
+// the split sums per element as gemm_reduce_kernel)
+__global__ void gemm_reduce4_kernel(const float* __restrict__ P, int splits, int M, int N, float* __restrict__ C,
+                                    int ldc, int accumulate) {
+  const size_t n4 = (size_t)M * N / 4;
+  const size_t n = (size_t)M * N;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n4; idx += (size_t)gridDim.x * blockDim.x) {
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < splits; ++q) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(P + (size_t)q * n + 4 * idx);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] += v[c];
+    }
+    const size_t i = 4 * idx / N, j = 4 * idx - i * N;
+    floatx4* dst = reinterpret_cast<floatx4*>(C + i * ldc + j);
+    if (accumulate) {
+      const floatx4 o = *dst;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] += o[c];
+    }
+    *dst = s;
+  }
+}
+
 int gemm_reduce(const float* P, int splits, int M, int N, float* C, int ldc, int accumulate, hipStream_t s,
                 int trans) {
   const size_t n = (size_t)M * N;
   if (n == 0) return hipSuccess;
+  if (!trans && N % 4 == 0 && ldc % 4 == 0 &&
+      (reinterpret_cast<uintptr_t>(P) | reinterpret_cast<uintptr_t>(C)) % 16 == 0) {
+    int blocks = (int)((n / 4 + 255) / 256);
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(gemm_reduce4_kernel, dim3(blocks), dim3(256), 0, s, P, splits, M, N, C, ldc, accumulate);
+    return hipGetLastError();
+  }
   int blocks = (int)((n + 255) / 256);
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(gemm_reduce_kernel, dim3(blocks), dim3(256), 0, s, P, splits, M, N, C, ldc, accumulate, trans);
