@@ -71,8 +71,9 @@ def measured_gemm_traffic(config, dtype, keep_bwd):
     return rec["gemm_bytes_per_step"] / rec["gemm_launches_per_step"]
 
 
-def cpu_baseline(d, n_edges_sample, seed=0):
-    """Time the float64 oracle (fwd, bwd, dbwd) on a leading block of edges."""
+def cpu_baseline(d, n_edges_sample, seed=0, dbwd=True):
+    """Time the float64 oracle (fwd, bwd and, with dbwd, the double backward) on a
+    leading block of edges."""
     import numpy as np
     import torch
     from oracle import so2conv_oracle as O
@@ -87,11 +88,12 @@ def cpu_baseline(d, n_edges_sample, seed=0):
     t0 = time.perf_counter()
     O.forward(inp, chunk=2048, edges=edges)
     O.backward(inp, gy, chunk=2048, edges=edges)
-    O.double_backward(inp, gy, px=t(d["px"]), ppos=t(d["ppos"]), prbf=t(d["prbf"]), chunk=2048, edges=edges)
+    if dbwd:
+        O.double_backward(inp, gy, px=t(d["px"]), ppos=t(d["ppos"]), prbf=t(d["prbf"]), chunk=2048, edges=edges)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "edges/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"first {n} of {E} edges of the same workload, fwd+bwd+dbwd in float64 "
-                      f"(PyTorch CPU, autograd), {dt:.1f} s"}
+            "sample": f"first {n} of {E} edges of the same workload, {'fwd+bwd+dbwd' if dbwd else 'fwd+bwd'} in "
+                      f"float64 (PyTorch CPU, autograd), {dt:.1f} s"}
 
 
 def cpu_baseline_mole(d, m, n_edges_sample):
@@ -355,6 +357,8 @@ def main():
         w1e, w2e = [t(w, ft) for w in mix_in["w1e"]], [t(w, ft) for w in mix_in["w2e"]]
         coef = t(mix_in["coef"])
         progress(f"mixture: {args.systems} systems, {args.experts} experts")
+    # the eSEN-like small and the large systems are specified as forward + backward
+    two_stage = args.config in ("S", "X")
     db_need = ("gy", "x", "rbf", "w_rad", "w1", "w2") + (("pos",) if args.pos2 else ()) + \
         (("env",) if args.envelope else ())
     saved_b = K.so2conv_saved_bytes(kc, E)
@@ -368,14 +372,19 @@ def main():
             ws_b = max(K.so2mole_workspace_bytes(kc, mix, N, E, s, 262144) for s in (0, 1, 2))
         else:
             ws_b = max(K.so2conv_chunked_workspace_bytes(kc, N, E, s, 262144) for s in (0, 1, 2))
+    # without room for the per-edge forward state (the large system), every
+    # chunk recomputes it inside the workspace
+    keep_state = saved_b + ws_b <= 200 * 2**30
+    if not keep_state:
+        saved_b = 0
     # the backward keeps its cotangents for the double backward of the same step
     # (one data-gradient product per linear less there) when memory allows
-    sb_b = 0 if mole else K.so2conv_saved_bwd_bytes(kc, E)
-    keep_bwd = not mole and saved_b + ws_b + sb_b <= 230 * 2**30
+    sb_b = 0 if (mole or two_stage) else K.so2conv_saved_bwd_bytes(kc, E)
+    keep_bwd = not (mole or two_stage) and saved_b + ws_b + sb_b <= 230 * 2**30
     progress(f"saved state {saved_b / 2**30:.1f} GiB, workspace {ws_b / 2**30:.1f} GiB"
              + (" (edge chunks)" if chunked else "")
              + (f", backward cotangents kept {sb_b / 2**30:.1f} GiB" if keep_bwd else ""))
-    saved = torch.empty(saved_b, dtype=torch.uint8, device=dev)
+    saved = torch.empty(saved_b, dtype=torch.uint8, device=dev) if keep_state else None
     ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
     saved_bwd = torch.empty(sb_b, dtype=torch.uint8, device=dev) if keep_bwd else None
     args_c = (kc, g, x, pos, rbf, w_rad, w1, w2)
@@ -398,8 +407,9 @@ def main():
             e1.record()
             K.so2conv_bwd(*args_c, saved, gy, ws=ws, env=env, saved_bwd=saved_bwd)
             e2.record()
-            K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env, need=db_need,
-                           saved_bwd=saved_bwd)
+            if not two_stage:
+                K.so2conv_dbwd(*args_c, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env, need=db_need,
+                               saved_bwd=saved_bwd)
         e3.record()
         if times is not None:
             times.append((e0, e1, e2, e3))
@@ -437,8 +447,17 @@ def main():
     kname = ("gemm_bf16_kernel (bf16 MFMA per-order linears)" if dtype == "bf16" else
              "gemm_f32_dma_kernel (order 0) and gemm_cplx_dma_kernel (orders >= 1, three real products per complex "
              "one; fp32 MFMA)") + ", all launches of the timed steps"
+    # Appendix B.5's intermediates of the separate-operation schedule (retained-order
+    # layout, one stored copy each) and the per-edge forward state the fused path
+    # keeps when it does not recompute: the memory a materialising implementation
+    # would hold beyond the fused one
+    qlm = sum(2 * min(l, cfg.mmax) + 1 for l in range(cfg.lmax + 1))
+    dd_, C0, C1 = (cfg.lmax + 1) ** 2, 2 * cfg.channels, cfg.channels
+    elem = 2 if dtype == "bf16" else 4
+    mat_gib = elem * E * (dd_ * (C0 + C1) + qlm * (C0 + 2 * C1 + C1 + 2 * C1)) / 2**30
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not two_stage else
+        f"edges/sec fwd+bwd SO(2) conv (lmax={cfg.lmax},C={cfg.channels})",
         "value": value,
         "unit": "edges/s",
         "n_gpus": 1,
@@ -452,27 +471,31 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{WORKLOADS.get(cfg.name, cfg.name)} ({cfg.name})", "n_atoms": N,
                    "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
-                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, "stages": "fwd+bwd+dbwd (force-training pattern)"
+                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc,
+                   "stages": ("fwd+bwd" if two_stage else "fwd+bwd+dbwd (force-training pattern)")
                    + (", dbwd with gpos2" if args.pos2 else "")
                    + (f", {args.heads}-head attention weights times the cutoff envelope" if args.heads > 1
                       else (", cutoff envelope" if args.envelope else ""))
                    + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else ""),
-                   "edge_chunks": chunked, "backward_cotangents_kept": keep_bwd},
+                   "edge_chunks": chunked, "forward_state_kept": keep_state, "backward_cotangents_kept": keep_bwd},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": None if mole else measured_gemm_traffic(args.config, dtype, keep_bwd),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
                      "kernel": kname,
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
                      "algorithmic_flops_per_step": gemm_fl / args.steps, "per_kind": per_kind},
-        "stage_ms": {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean()), "dbwd": float(st[:, 2].mean())},
+        "stage_ms": {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean())} if two_stage else
+        {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean()), "dbwd": float(st[:, 2].mean())},
         "step_gemm_share": gemm_ms / args.steps / ms_step,
         "peak_device_memory_GiB": torch.cuda.max_memory_allocated() / 2**30,
-        "step_tflops_8F": 8 * F * E / (ms_step * 1e-3) / 1e12,
+        "materialising_estimate_GiB": {"forward_state": K.so2conv_saved_bytes(kc, E) / 2**30,
+                                       "separate_operation_intermediates": mat_gib},
+        ("step_tflops_3F" if two_stage else "step_tflops_8F"): (3 if two_stage else 8) * F * E / (ms_step * 1e-3) / 1e12,
     }
     progress(f"timed {args.steps} steps: {ms_step:.1f} ms/step")
     if args.cpu_edges > 0:
         out["cpu_baseline"] = cpu_baseline_mole(d, mix_in, args.cpu_edges) if mole else \
-            cpu_baseline(d, args.cpu_edges)
+            cpu_baseline(d, args.cpu_edges, dbwd=not two_stage)
     print(json.dumps(out), flush=True)
 
 
