@@ -977,9 +977,9 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   for (int q = 0; q < b.nprob; ++q)
     if ((b.p[q].cplx != 0) != cx) return hipErrorInvalidValue;
   const bool dma = !bf16 && dma_ok(b, TA, TB);
-  // weight-gradient products at most 64 columns wide (the radial map's, with
+  // real products at most 64 columns wide (the radial map's gradients, with
   // the n_rbf side as columns): blocks of 256 x 64, four waves
-  bool narrow = dma && !cx && TA && !TB;
+  bool narrow = dma && !cx && !(TA && TB);
   for (int q = 0; q < b.nprob && narrow; ++q) narrow = b.p[q].N <= 64;
   const int bm = cx ? CBM : (bf16 ? BMH : BM);
   const int bn = cx ? (dma ? 32 * kCxWNW : CBN) : (bf16 ? BNH : (narrow ? 64 : (dma ? 64 * kF32WNW : BN)));
@@ -1003,8 +1003,12 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
       if (!TA && !TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, false, CW>), grid, cb, 0, s, b);
       else if (!TA && TB) hipLaunchKernelGGL((gemm_cplx_dma_kernel<false, true, CW>), grid, cb, 0, s, b);
       else hipLaunchKernelGGL((gemm_cplx_dma_kernel<true, false, CW>), grid, cb, 0, s, b);
+    } else if (!TA && !TB && narrow) {
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, false, 1>), grid, dim3(64 * WAVES_M), 0, s, b);
     } else if (!TA && !TB) {
       hipLaunchKernelGGL((gemm_f32_dma_kernel<false, false, W>), grid, fb, 0, s, b);
+    } else if (!TA && TB && narrow) {
+      hipLaunchKernelGGL((gemm_f32_dma_kernel<false, true, 1>), grid, dim3(64 * WAVES_M), 0, s, b);
     } else if (!TA && TB) {
       hipLaunchKernelGGL((gemm_f32_dma_kernel<false, true, W>), grid, fb, 0, s, b);
     } else if (TA && !TB && narrow) {
