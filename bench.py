@@ -379,8 +379,8 @@ def main():
         saved_b = 0
     # the backward keeps its cotangents for the double backward of the same step
     # (one data-gradient product per linear less there) when memory allows
-    sb_b = 0 if (mole or two_stage) else K.so2conv_saved_bwd_bytes(kc, E)
-    keep_bwd = not (mole or two_stage) and saved_b + ws_b + sb_b <= 230 * 2**30
+    sb_b = 0 if two_stage else K.so2conv_saved_bwd_bytes(kc, E)
+    keep_bwd = not two_stage and keep_state and saved_b + ws_b + sb_b <= 230 * 2**30
     progress(f"saved state {saved_b / 2**30:.1f} GiB, workspace {ws_b / 2**30:.1f} GiB"
              + (" (edge chunks)" if chunked else "")
              + (f", backward cotangents kept {sb_b / 2**30:.1f} GiB" if keep_bwd else ""))
@@ -398,10 +398,10 @@ def main():
         if mole:
             K.so2mole_fwd(*args_m, saved=saved, ws=ws, env=env)
             e1.record()
-            K.so2mole_bwd(*args_m, saved, gy, ws=ws, env=env)
+            K.so2mole_bwd(*args_m, saved, gy, ws=ws, env=env, saved_bwd=saved_bwd)
             e2.record()
             K.so2mole_dbwd(*args_m, saved, gy, px=px, ppos=ppos, prbf=prbf, ws=ws, env=env,
-                           need=db_need + ("coef",))
+                           need=db_need + ("coef",), saved_bwd=saved_bwd)
         else:
             K.so2conv_fwd(*args_c, saved=saved, ws=ws, env=env)
             e1.record()

@@ -219,7 +219,10 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
  * Workspace: so2mole_workspace_bytes(stage, chunk_edges): chunk_edges = 0
  * sizes one chunk over all edges that uses `saved` (as so2conv_workspace_bytes);
  * chunk_edges > 0 sizes chunks of that many edges that recompute the forward
- * state when `saved` is NULL (as so2conv_chunked_workspace_bytes). */
+ * state when `saved` is NULL (as so2conv_chunked_workspace_bytes).
+ * saved_bwd (may be NULL; so2conv_saved_bwd_bytes) as in so2conv_bwd/dbwd: the
+ * backward's cotangents, per system formed with that system's merged weights
+ * in both calls. */
 typedef struct {
   int32_t n_systems;
   int32_t n_experts;
@@ -235,14 +238,14 @@ int so2mole_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cf
                 const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
                 const void* const* w2e, const float* coef, const void* saved, const void* gy, void* gx, float* gpos,
                 float* grbf, float* genv, void* gw_rad, void* const* gw1e, void* const* gw2e, float* gcoef,
-                float* gedge, void* ws, size_t ws_bytes, void* stream);
+                float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream);
 int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
                  const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
                  const void* const* w2e, const float* coef, const void* saved, const void* gy, const void* px,
                  const float* ppos, const float* pedge, const float* prbf, const float* penv, const void* pw_rad,
                  const void* const* pw1e, const void* const* pw2e, const float* pcoef, void* ggy, void* gx2,
                  float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1e_2, void* const* gw2e_2,
-                 float* gcoef2, void* ws, size_t ws_bytes, void* stream);
+                 float* gcoef2, const void* saved_bwd, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- Node-to-node spherical projection with fused channel maps (Appendix B.4,
  * spherical activations). Per node i with coefficient rows X_i^(l) = x[i][l^2..(l+1)^2)

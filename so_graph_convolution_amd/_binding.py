@@ -72,10 +72,10 @@ EXPORTS = {
                                        c_i64]),
     "so2mole_fwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), ctypes.POINTER(MoleCfg)] + [c_vp] * 11
                     + [c_sz, c_vp]),
-    "so2mole_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), ctypes.POINTER(MoleCfg)] + [c_vp] * 20
+    "so2mole_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), ctypes.POINTER(MoleCfg)] + [c_vp] * 21
                     + [c_sz, c_vp]),
     "so2mole_dbwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC), ctypes.POINTER(MoleCfg)]
-                     + [c_vp] * 29 + [c_sz, c_vp]),
+                     + [c_vp] * 30 + [c_sz, c_vp]),
     "so2grid_workspace_bytes": (c_sz, [ctypes.POINTER(GridCfg), c_i32, ctypes.c_int]),
     # (cfg, N, x, G, W, A, U, ws, ws_bytes, stream)
     "so2grid_fwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 6 + [c_sz, c_vp]),

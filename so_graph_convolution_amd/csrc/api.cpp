@@ -1797,7 +1797,7 @@ int so2mole_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cf
                 const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
                 const void* const* w2e, const float* coef, const void* saved, const void* gy, void* gx, float* gpos,
                 float* grbf, float* genv, void* gw_rad, void* const* gw1e, void* const* gw2e, float* gcoef,
-                float* gedge, void* ws, size_t ws_bytes, void* stream) {
+                float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   Ctx c;
   GraphDev gd;
@@ -1811,7 +1811,7 @@ int so2mole_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cf
     return zero_mole_grads(c, gw1e, gw2e, gcoef, s);
   }
   return conv_bwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, saved, gy, gx, gpos, grbf, genv, gw_rad, gw1e, gw2e,
-                  gcoef, gedge, nullptr, ws, ws_bytes, stream);
+                  gcoef, gedge, saved_bwd, ws, ws_bytes, stream);
 }
 
 int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cfg* mole, const void* x,
@@ -1820,7 +1820,7 @@ int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_c
                  const float* ppos, const float* pedge, const float* prbf, const float* penv, const void* pw_rad,
                  const void* const* pw1e, const void* const* pw2e, const float* pcoef, void* ggy, void* gx2,
                  float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1e_2, void* const* gw2e_2,
-                 float* gcoef2, void* ws, size_t ws_bytes, void* stream) {
+                 float* gcoef2, const void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   Ctx c;
   GraphDev gd;
@@ -1835,7 +1835,7 @@ int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_c
     return zero_mole_grads(c, gw1e_2, gw2e_2, gcoef2, s);
   }
   return conv_dbwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, saved, gy, px, ppos, pedge, prbf, penv, pw_rad,
-                   pw1e, pw2e, pcoef, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2, nullptr, ws,
+                   pw1e, pw2e, pcoef, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2, saved_bwd, ws,
                    ws_bytes, stream);
 }
 

@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 from ._binding import MoleCfg, check, lib
-from .ops import GRAD_KEYS, DBWD_KEYS, Graph, SO2Config, _common, _dev, _p, _ptr_array, _stream, _ws, weight_shapes
+from .ops import (GRAD_KEYS, DBWD_KEYS, Graph, SO2Config, _common, _dev, _p, _ptr_array, _saved_bwd, _stream, _ws,
+                  weight_shapes)
 
 __all__ = ["Mixture", "so2mole_workspace_bytes", "so2mole_fwd", "so2mole_bwd", "so2mole_dbwd", "expert_shapes"]
 
@@ -77,8 +78,9 @@ def so2mole_fwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e,
 
 
 def so2mole_bwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e, w2e, coef, saved, gy,
-                need=GRAD_KEYS + ("coef",), ws=None, chunk_edges=None, env=None):
-    """Returns dict gx, gpos, grbf, gw_rad, gw1e, gw2e, gcoef, gedge, genv (requested ones)."""
+                need=GRAD_KEYS + ("coef",), ws=None, chunk_edges=None, env=None, saved_bwd=None):
+    """Returns dict gx, gpos, grbf, gw_rad, gw1e, gw2e, gcoef, gedge, genv (requested ones);
+    saved_bwd as in so2conv_bwd (out["saved_bwd"])."""
     _common(cfg, g, x, pos, rbf, w_rad, env)
     dt = cfg.torch_dtype
     _dev(gy, "gy", dtype=dt, shape=x.shape)
@@ -97,19 +99,21 @@ def so2mole_bwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e,
     out["gedge"] = torch.empty(g.n_edges, 3, device=dev) if "edge" in need else None
     out["genv"] = torch.empty_like(env) if ("env" in need and env is not None) else None
     q1, q2, keep2 = _experts(cfg, mix, out["gw1e"], out["gw2e"], "gw1e", "gw2e")
+    out["saved_bwd"] = saved_bwd = _saved_bwd(cfg, g, saved_bwd, dev, allocate=True)
     ws = _ws_for(cfg, mix, g, 1, saved, ws, chunk_edges, dev)
     c, gc, m = cfg.c(), g.c(), mix.c()
     check(lib().so2mole_bwd(ctypes.byref(c), ctypes.byref(gc), ctypes.byref(m), _p(x), _p(pos), _p(rbf), _p(env),
                             _p(w_rad), p1, p2, _p(coef), _p(saved), _p(gy), _p(out["gx"]), _p(out["gpos"]),
                             _p(out["grbf"]), _p(out["genv"]), _p(out["gw_rad"]), q1, q2, _p(out["gcoef"]),
-                            _p(out["gedge"]), _p(ws), ws.numel(), _stream()), "so2mole_bwd")
+                            _p(out["gedge"]), _p(saved_bwd), _p(ws), ws.numel(), _stream()), "so2mole_bwd")
     return out
 
 
 def so2mole_dbwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e, w2e, coef, saved, gy, px=None,
                  ppos=None, pedge=None, prbf=None, pw_rad=None, pw1e=None, pw2e=None, pcoef=None,
-                 need=DBWD_KEYS + ("coef",), ws=None, chunk_edges=None, env=None, penv=None):
-    """Returns dict ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2 (requested ones)."""
+                 need=DBWD_KEYS + ("coef",), ws=None, chunk_edges=None, env=None, penv=None, saved_bwd=None):
+    """Returns dict ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2 (requested ones);
+    saved_bwd: out["saved_bwd"] of so2mole_bwd on the same inputs and gy, or None."""
     _common(cfg, g, x, pos, rbf, w_rad, env)
     dt = cfg.torch_dtype
     for t, n, shp, tdt in ((gy, "gy", x.shape, dt), (px, "px", x.shape, dt), (ppos, "ppos", pos.shape, torch.float32),
@@ -133,11 +137,12 @@ def so2mole_dbwd(cfg: SO2Config, g: Graph, mix: Mixture, x, pos, rbf, w_rad, w1e
     out["gw2e_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     out["gcoef2"] = torch.empty_like(coef) if "coef" in need else None
     q1, q2, keep3 = _experts(cfg, mix, out["gw1e_2"], out["gw2e_2"], "gw1e_2", "gw2e_2")
+    saved_bwd = _saved_bwd(cfg, g, saved_bwd, dev, allocate=False)
     ws = _ws_for(cfg, mix, g, 2, saved, ws, chunk_edges, dev)
     c, gc, m = cfg.c(), g.c(), mix.c()
     check(lib().so2mole_dbwd(ctypes.byref(c), ctypes.byref(gc), ctypes.byref(m), _p(x), _p(pos), _p(rbf), _p(env),
                              _p(w_rad), p1, p2, _p(coef), _p(saved), _p(gy), _p(px), _p(ppos), _p(pedge), _p(prbf),
                              _p(penv), _p(pw_rad), pp1, pp2, _p(pcoef), _p(out["ggy"]), _p(out["gx2"]),
                              _p(out["gpos2"]), _p(out["grbf2"]), _p(out["genv2"]), _p(out["gw_rad2"]), q1, q2,
-                             _p(out["gcoef2"]), _p(ws), ws.numel(), _stream()), "so2mole_dbwd")
+                             _p(out["gcoef2"]), _p(saved_bwd), _p(ws), ws.numel(), _stream()), "so2mole_dbwd")
     return out

@@ -155,6 +155,19 @@ def so2conv_saved_bwd_bytes(cfg: SO2Config, n_edges) -> int:
     return int(lib().so2conv_saved_bwd_bytes(ctypes.byref(c), n_edges))
 
 
+def _saved_bwd(cfg, g, saved_bwd, device, allocate):
+    """The backward's kept-cotangent buffer: allocated for saved_bwd=True when
+    `allocate` (the backward), else checked (dtype uint8, large enough)."""
+    if saved_bwd is True and allocate:
+        return _ws(so2conv_saved_bwd_bytes(cfg, g.n_edges), device)
+    if saved_bwd is None:
+        return None
+    _dev(saved_bwd, "saved_bwd", dtype=torch.uint8)
+    if saved_bwd.numel() < so2conv_saved_bwd_bytes(cfg, g.n_edges):
+        raise ValueError("saved_bwd is smaller than so2conv_saved_bwd_bytes")
+    return saved_bwd
+
+
 def so2conv_chunked_workspace_bytes(cfg: SO2Config, n_nodes, n_edges, stage, chunk_edges) -> int:
     c = cfg.c()
     return int(lib().so2conv_chunked_workspace_bytes(ctypes.byref(c), n_nodes, n_edges, stage, chunk_edges))
@@ -234,13 +247,7 @@ def so2conv_bwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy,
     out["genv"] = torch.empty_like(env) if ("env" in need and env is not None) else None
     q1, k3 = _ptr_array(out["gw1"], "gw1", s1, dt)
     q2, k4 = _ptr_array(out["gw2"], "gw2", s2, dt)
-    if saved_bwd is True:
-        saved_bwd = _ws(so2conv_saved_bwd_bytes(cfg, g.n_edges), dev)
-    elif saved_bwd is not None:
-        _dev(saved_bwd, "saved_bwd", dtype=torch.uint8)
-        if saved_bwd.numel() < so2conv_saved_bwd_bytes(cfg, g.n_edges):
-            raise ValueError("saved_bwd is smaller than so2conv_saved_bwd_bytes")
-    out["saved_bwd"] = saved_bwd
+    out["saved_bwd"] = saved_bwd = _saved_bwd(cfg, g, saved_bwd, dev, allocate=True)
     ws = _ws_for(cfg, g, 1, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_bwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1, p2,
@@ -285,10 +292,7 @@ def so2conv_dbwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved, gy
     out["gw2_2"] = [torch.empty(s, dtype=dt, device=dev) for s in s2] if "w2" in need else None
     q1, k3 = _ptr_array(out["gw1_2"], "gw1_2", s1, dt)
     q2, k4 = _ptr_array(out["gw2_2"], "gw2_2", s2, dt)
-    if saved_bwd is not None:
-        _dev(saved_bwd, "saved_bwd", dtype=torch.uint8)
-        if saved_bwd.numel() < so2conv_saved_bwd_bytes(cfg, g.n_edges):
-            raise ValueError("saved_bwd is smaller than so2conv_saved_bwd_bytes")
+    saved_bwd = _saved_bwd(cfg, g, saved_bwd, dev, allocate=False)
     ws = _ws_for(cfg, g, 2, saved, ws, chunk_edges, dev)
     c, gc = cfg.c(), g.c()
     check(lib().so2conv_dbwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1,

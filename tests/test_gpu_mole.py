@@ -1,7 +1,8 @@
 """Mixture of linear experts (so2mole_*: system s uses sum_k coef[s,k] W^(k) in
 both SO(2) linears) through the C ABI against the mixture oracle: forward,
 backward (incl. expert and coefficient gradients) and double backward with
-directions on x, positions, rbf, coefficients and experts; float32 and bf16,
+directions on x, positions, rbf, coefficients and experts, also reusing the
+backward's kept cotangents (saved_bwd); float32 and bf16,
 one chunk and 1024-edge chunks whose borders cut systems, an empty system in
 every case. A single system with a one-hot coefficient is bitwise the plain
 operator with that expert."""
@@ -55,10 +56,15 @@ def test_mixture_matches_oracle(name, over, dtype, chunk, S, K, use_env):
     keep = chunk is None
     y, saved = Kx.so2mole_fwd(*args, saved=True if keep else None, chunk_edges=chunk, env=env)
     bw = Kx.so2mole_bwd(*args, saved, dd["gy"], chunk_edges=chunk, env=env)
-    db = Kx.so2mole_dbwd(*args, saved, dd["gy"], px=dd["px"], ppos=dd["ppos"], prbf=dd["prbf"], pcoef=mx["pcoef"],
-                         pw1e=mx["pw1e"], pw2e=mx["pw2e"], chunk_edges=chunk, env=env,
-                         need=("gy", "x", "pos", "rbf", "w_rad", "w1", "w2", "coef"))
+    dirs = dict(px=dd["px"], ppos=dd["ppos"], prbf=dd["prbf"], pcoef=mx["pcoef"], pw1e=mx["pw1e"], pw2e=mx["pw2e"],
+                chunk_edges=chunk, env=env, need=("gy", "x", "pos", "rbf", "w_rad", "w1", "w2", "coef"))
+    db = Kx.so2mole_dbwd(*args, saved, dd["gy"], **dirs)
+    # the double backward again, reusing the backward's kept cotangents
+    bw_k = Kx.so2mole_bwd(*args, saved, dd["gy"], chunk_edges=chunk, env=env, saved_bwd=True)
+    db_k = Kx.so2mole_dbwd(*args, saved, dd["gy"], saved_bwd=bw_k["saved_bwd"], **dirs)
     torch.cuda.synchronize()
+    for k in ("gx", "gpos", "grbf", "gw_rad", "gcoef", "gedge"):
+        assert torch.equal(bw_k[k], bw[k]), k
     base = H.oracle_inputs(d)
     w1e, w2e = [_t(w) for w in m["w1e"]], [_t(w) for w in m["w2e"]]
     coef, sp, gy = _t(m["coef"]), m["sys_edge_ptr"].tolist(), _t(d["gy"])
@@ -74,6 +80,7 @@ def test_mixture_matches_oracle(name, over, dtype, chunk, S, K, use_env):
     for k, v in (("ggy", "ggy"), ("gx2", "gx"), ("gpos2", "gpos"), ("grbf2", "grbf"), ("gw_rad2", "gw_rad"),
                  ("gw1e_2", "gw1e"), ("gw2e_2", "gw2e"), ("gcoef2", "gcoef")):
         errs[k] = H.relerr(db[k], rd[v])
+        errs[k + " kept"] = H.relerr(db_k[k], rd[v])
     H.note("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     tol = H.TOL_BF16 if dtype == "bf16" else H.TOL_F32
     assert all(v <= tol for v in errs.values()), errs

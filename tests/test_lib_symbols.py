@@ -90,7 +90,7 @@ def test_mixture_host_checks():
     r = K.lib().so2mole_fwd(ctypes.byref(c), ctypes.byref(g), ctypes.byref(m), *([None] * 11), 0, None)
     assert r == -1 and b"non-decreasing" in K.lib().so2conv_last_error()
     m = MoleCfg(3, 10, np.array([0, 100, 200, 1000], dtype=np.int64).ctypes.data)
-    r = K.lib().so2mole_bwd(ctypes.byref(c), ctypes.byref(g), ctypes.byref(m), *([None] * 20), 0, None)
+    r = K.lib().so2mole_bwd(ctypes.byref(c), ctypes.byref(g), ctypes.byref(m), *([None] * 21), 0, None)
     assert r == -2 and b"n_experts" in K.lib().so2conv_last_error()
 
 
