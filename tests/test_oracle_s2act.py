@@ -1,11 +1,13 @@
 """Pins for the SwiGLU-S2 oracle (TrimSO(2) page, Table 5 and Appendix B.4; the
 reading is stated in the oracle's header): a brute-force loop over the
 definition, the identity grid (where it is plain SwiGLU on the coefficients),
-linearity in the value half, a zero gate, and central finite differences for
-the backward and the double backward."""
+linearity in the value half, a zero gate, a constant gate on an exact
+quadrature grid of real harmonics (where the round trip is exact), and central
+finite differences for the backward and the double backward."""
 import itertools
 import math
 
+import numpy as np
 import torch
 
 from oracle import s2act_oracle as SO
@@ -83,3 +85,37 @@ def test_double_backward_matches_finite_differences():
     L = lambda X: _dot(SO.backward(X, G, P, gZ), pU)  # noqa: E731
     fd = (L(U + eps * qd) - L(U - eps * qd)) / (2 * eps)
     assert abs(_dot(dd["gU2"], qd) - fd) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_constant_gate_on_an_exact_sphere_grid():
+    """G = the retained real harmonics (lmax 4, mmax 2: 19 rows) at the nodes of
+    a product grid exact to degree 8 (Gauss-Legendre in cos(theta) x uniform
+    phi), P = G^T times the quadrature weights. A gate half that is nonzero
+    only on the (0, 0) row makes SiLU(G u_g) constant over the sphere, so the
+    grid round trip returns SiLU(g / sqrt(4 pi)) times the value half exactly
+    (orthonormality of the harmonics under an exact quadrature)."""
+    from oracle import so2conv_oracle as O
+    L, M = 4, 2
+    zs, wz = np.polynomial.legendre.leggauss(L + 1)
+    nphi = 2 * L + 1
+    phi = 2 * math.pi * np.arange(nphi) / nphi
+    Zg, Pg = np.meshgrid(zs, phi, indexing="ij")
+    st = np.sqrt(1 - Zg * Zg)
+    u = torch.tensor(np.stack([st * np.cos(Pg), st * np.sin(Pg), Zg], -1).reshape(-1, 3), dtype=DT)
+    w = torch.tensor((np.repeat(wz[:, None], nphi, axis=1) * (2 * math.pi / nphi)).reshape(-1), dtype=DT)
+    cols = []
+    for l in range(L + 1):
+        Y = O.real_sh(l, u)                       # [n_g, 2l+1], m = -l..l
+        q = min(l, M)
+        cols.append(Y[:, l - q:l + q + 1])
+    G = torch.cat(cols, dim=1)                    # [n_g, 19]
+    P = (G * w[:, None]).T.contiguous()           # [19, n_g]
+    gen = torch.Generator().manual_seed(5)
+    E, C = 3, 4
+    U = torch.zeros(E, G.shape[1], 2 * C, dtype=DT)
+    U[:, :, :C] = torch.randn(E, G.shape[1], C, generator=gen, dtype=DT)
+    g0 = torch.randn(E, 1, C, generator=gen, dtype=DT) * 3
+    U[:, 0:1, C:] = g0
+    a = g0 / math.sqrt(4 * math.pi)
+    ref = a / (1 + torch.exp(-a)) * U[:, :, :C]
+    assert torch.allclose(SO.forward(U, G, P), ref, rtol=0, atol=1e-12)
