@@ -43,6 +43,7 @@ def _cached(key, fn):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_high_degree_full_size_chunked(dtype):
+    """Recompute chunks of 256k edges (no per-edge state across calls)."""
     import so_graph_convolution_amd as K
     cfg = so2_synth.CONFIGS["H"]
     d = _inputs("H", True)
@@ -57,6 +58,38 @@ def test_high_degree_full_size_chunked(dtype):
     db = K.so2conv_dbwd(*args, None, dd["gy"], px=dd["px"], ppos=dd["ppos"], prbf=dd["prbf"], chunk_edges=ce)
     torch.cuda.synchronize()
     H.note(f"  peak device memory {torch.cuda.max_memory_allocated() / 2**30:.1f} GiB")
+    _check_high_degree(d, dtype, y, bw, db)
+
+
+@pytest.mark.timeout(900)
+def test_high_degree_full_size_bench_configuration():
+    """bf16 as bench.py --config H runs it: the saved forward state, one
+    workspace sized for 256k-edge chunks, and the backward's cotangents kept
+    for the double backward."""
+    import so_graph_convolution_amd as K
+    cfg = so2_synth.CONFIGS["H"]
+    d = _inputs("H", True)
+    E, N = len(d["src"]), cfg.n_atoms
+    H.note(f"[high degree bench configuration] N={N} E={E} L={cfg.lmax} C={cfg.channels}")
+    dd = H.to_dev(d, "bf16")
+    kc = dd["kcfg"]
+    args = (kc, dd["g"], dd["x"], dd["pos"], dd["rbf"], dd["w_rad"], dd["w1"], dd["w2"])
+    saved = torch.empty(K.so2conv_saved_bytes(kc, E), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(K.so2conv_chunked_workspace_bytes(kc, N, E, s, 262144) for s in (0, 1, 2)),
+                     dtype=torch.uint8, device="cuda")
+    kept = torch.empty(K.so2conv_saved_bwd_bytes(kc, E), dtype=torch.uint8, device="cuda")
+    y, _ = K.so2conv_fwd(*args, saved=saved, ws=ws)
+    bw = K.so2conv_bwd(*args, saved, dd["gy"], ws=ws, saved_bwd=kept)
+    db = K.so2conv_dbwd(*args, saved, dd["gy"], px=dd["px"], ppos=dd["ppos"], prbf=dd["prbf"], ws=ws, saved_bwd=kept)
+    torch.cuda.synchronize()
+    del saved, ws, kept
+    torch.cuda.empty_cache()
+    _check_high_degree(d, "bf16", y, bw, db)
+
+
+def _check_high_degree(d, dtype, y, bw, db):
+    cfg = so2_synth.CONFIGS["H"]
+    E, N = len(d["src"]), cfg.n_atoms
     rng = np.random.default_rng(7)
     nodes = np.sort(rng.choice(N, 3, replace=False))
     edges = np.sort(rng.choice(E, 32, replace=False))
