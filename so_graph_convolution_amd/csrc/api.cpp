@@ -322,7 +322,14 @@ LinBuf take_lin(Arena& ar, const Ctx& c, int second) {
   const size_t n = (size_t)realified_size(c.d, second);
   LinBuf b;
   b.W = ar.bytes(n * c.es);
-  b.WT = c.bf ? ar.bytes(n * c.es) : nullptr;
+  if (c.bf) {
+    b.WT = ar.bytes(n * c.es);
+  } else {   // float32: the transposed order-0 block (the data-gradient products read it k-major)
+    int r, cc;
+    long off;
+    realified_shape(c.d, second, 0, &r, &cc, &off);
+    b.WT = ar.bytes((size_t)r * cc * sizeof(float));
+  }
   return b;
 }
 
@@ -783,6 +790,9 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
   const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
   const int lda = transposed ? wout : win, ldc = transposed ? win : wout;
   std::vector<GemmProb> ps, pc;   // real products; complex products (float32, orders >= 1)
+  // float32 data-gradient products of order 0 read the transposed weight copy
+  bool use_wt = !c.bf && transposed;
+  for (const Lin& l : w.W) use_wt = use_wt && l.WT != nullptr;
   for (int q = 0; q < stacks; ++q)
     for (size_t sy = 0; sy < w.W.size(); ++sy) {
       const long lo = std::max(w.e[sy], e0), hi = std::min(w.e[sy + 1], e0 + n);
@@ -812,12 +822,15 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
             ps.push_back(prob(offs(Ar, ib, c.es), win, offs(W.WT, off, c.es), r, Cr + ob, wout, rows, cc, r, acc));
           else
             ps.push_back(prob(offs(Ar, ib, c.es), win, offs(W.W, off, c.es), cc, Cr + ob, wout, rows, cc, r, acc));
+        } else if (use_wt) {
+          // float32 order 0: A (W^T) with the transposed copy, its rows k-major
+          ps.push_back(prob(offs(Ar, ob, c.es), wout, offs(W.WT, off, c.es), r, Cr + ib, win, rows, r, cc, acc));
         } else {
           ps.push_back(prob(offs(Ar, ob, c.es), wout, offs(W.W, off, c.es), cc, Cr + ib, win, rows, r, cc, acc));
         }
       }
     }
-  int rr = run_batch(ps, false, transposed || c.bf, c.bf, s);
+  int rr = run_batch(ps, false, (transposed && !use_wt) || c.bf, c.bf, s);
   if (rr) return rr;
   return run_batch(pc, false, transposed, 0, s);
 }

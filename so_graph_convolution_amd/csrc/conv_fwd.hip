@@ -319,6 +319,8 @@ int launch_realify(const Dims& d, int second, const void* const* w, void* wr, vo
       if (plain) {
         e = hipMemcpyAsync(static_cast<float*>(wr) + off, w[0], sizeof(float) * (size_t)r * c,
                            hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && wrt)
+          e = realify_block<float, float, true>(w[0], k, h, 1, static_cast<float*>(wrt) + off, s);
       } else {
         e = realify_block<float, float, false>(w[a], k, h, 0, static_cast<float*>(wr) + off, s);
       }
