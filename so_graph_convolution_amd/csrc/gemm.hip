@@ -490,9 +490,11 @@ __global__ __launch_bounds__(CNT) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 //
 // The lane -> element map of a block is free, which gives the tile layouts:
 //   k-contiguous tile (R rows x 16 k): block b holds rows 16b .. 16b+15; lane
-//     l carries k chunk q = l/16 (four k) of row 16b + l%16, so chunk q of a
-//     row sits at 16q + row%16 (16-byte units). A fragment read (16 rows, one
-//     chunk) covers 256 contiguous bytes.
+//     l = 4r + s carries row 16b + r, k chunk q = (s - r/4) mod 4 (four k), so
+//     chunk q of row r sits at 16-byte unit 4r + (q + r/4) mod 4. A
+//     quarter-wave (16 lanes) then loads four whole 64-byte row segments, and
+//     a fragment read (16 rows, one chunk) still falls on 16 distinct groups
+//     of four banks (the rotation by r/4 separates rows r, r+4, r+8, r+12).
 //   k-major tile (16 k x R columns): block b holds k rows b KPB .. b KPB +
 //     KPB-1 (KPB = 256/R) at R floats apart, and blocks sit BLK = 256 + 1024/R
 //     floats apart, so k and k + 8 (the two lane halves of a read) are 32
@@ -524,7 +526,8 @@ template <bool KCONTIG, int R>
 __device__ inline DSlot dslot(int b, const float* P, int ld, int r0, int rlim, int kbeg, int lane, int base) {
   DSlot d;
   if (KCONTIG) {
-    const int row = min(r0 + 16 * b + lane % 16, rlim - 1), q = lane / 16;
+    const int rr = lane / 4, q = (lane % 4 - rr / 4) & 3;
+    const int row = min(r0 + 16 * b + rr, rlim - 1);
     d.src = P + (size_t)row * ld + kbeg + 4 * q;
     d.step = 16;
     d.kofs = 4 * q;
@@ -584,9 +587,10 @@ __device__ __forceinline__ void dsync(bool next_in_flight) {
 template <bool KCONTIG, int R>
 __device__ __forceinline__ void dfrag(const float* T, int row, int lk, float (&f)[8]) {
   if (KCONTIG) {
-    const float* q = T + (row / 16) * 256 + (row % 16) * 4 + 128 * lk;
-    const floatx4 u = *reinterpret_cast<const floatx4*>(q);
-    const floatx4 w = *reinterpret_cast<const floatx4*>(q + 64);
+    const int r = row % 16;
+    const float* q = T + (row / 16) * 256 + 16 * r;
+    const floatx4 u = *reinterpret_cast<const floatx4*>(q + 4 * ((2 * lk + r / 4) & 3));
+    const floatx4 w = *reinterpret_cast<const floatx4*>(q + 4 * ((2 * lk + 1 + r / 4) & 3));
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       f[c] = u[c];
