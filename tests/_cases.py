@@ -1,10 +1,14 @@
 """Shared helpers of the GPU parity tests: seeded workloads, device copies,
 oracle evaluation and the comparison metric.
 
-Metric: per output tensor, max |gpu - oracle| / max |oracle| (max-norm
-relative error). The bar is 1e-4 for float32 and 2e-2 for bfloat16 features
-and weights (the oracle then receives the same bf16-representable values in
-float64, so the error measures only the GPU's own rounding).
+Metrics: per output tensor, max |gpu - oracle| / max |oracle| (max-norm
+relative error, `relerr`), and the element-wise relative error with a floor,
+max |gpu - oracle| / (|oracle| + floor * max |oracle|) (`elemerr`), which
+also sees small elements of a tensor whose maximum is large. The bar is 1e-4
+for float32 and 2e-2 for bfloat16 features and weights (the oracle then
+receives the same bf16-representable values in float64, so the error measures
+only the GPU's own rounding); the floors are 1e-2 (float32) and 1e-1
+(bfloat16) of the tensor's maximum.
 """
 from __future__ import annotations
 
@@ -18,6 +22,8 @@ from oracle import so2conv_oracle as O
 
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
+FLOOR_F32 = 1e-2
+FLOOR_BF16 = 1e-1
 BF16_KEYS = ("x", "gy", "px", "w_rad", "w1", "w2")   # arrays of the call's dtype
 
 
@@ -67,6 +73,25 @@ def relerr(gpu, ref):
     if den == 0.0:
         return float((g - r).abs().max())
     return float((g - r).abs().max()) / den
+
+
+def elemerr(gpu, ref, floor=FLOOR_F32):
+    """max |g - r| / (|r| + floor * max |r|) over the elements of one tensor (or the max over a list)."""
+    if isinstance(gpu, (list, tuple)):
+        return max(elemerr(a, b, floor) for a, b in zip(gpu, ref))
+    g = gpu.detach().double().cpu() if isinstance(gpu, torch.Tensor) else torch.as_tensor(gpu, dtype=torch.float64)
+    r = ref.detach().double().cpu() if isinstance(ref, torch.Tensor) else torch.as_tensor(ref, dtype=torch.float64)
+    if r.numel() == 0:
+        return 0.0
+    den = r.abs() + floor * float(r.abs().max())
+    if float(den.max()) == 0.0:
+        return float((g - r).abs().max())
+    return float(((g - r).abs() / den.clamp_min(1e-300)).max())
+
+
+def errs_both(gpu, ref, dtype="f32"):
+    """(max-norm error, floored element-wise error) of one output."""
+    return relerr(gpu, ref), elemerr(gpu, ref, FLOOR_BF16 if dtype == "bf16" else FLOOR_F32)
 
 
 def oracle_inputs(d):

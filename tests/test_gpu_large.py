@@ -122,11 +122,16 @@ def _check_high_degree(d, dtype, y, bw, db):
     errs["grbf"] = H.relerr(bw["grbf"].cpu()[edges], re_b["grbf"])
     errs["gedge"] = H.relerr(bw["gedge"].cpu()[edges], re_b["gedge"])
     errs["grbf2"] = H.relerr(db["grbf2"].cpu()[edges], re_d["grbf"])
-    if dtype == "f32":
-        # y is linear in W2, so <gW2, W2> = <y, gy> (every output row and weight at once)
-        lhs = sum(float((g.double().cpu() * t(w)).sum()) for g, w in zip(bw["gw2"], d["w2"]))
-        rhs = float((y.double().cpu() * t(d["gy"])).sum())
-        errs["<gW2,W2>"] = abs(lhs - rhs) / abs(rhs)
+    # weight gradients over all ~1.05M edges: y is linear in W2, so <gW2, W2> = <y, gy>;
+    # T = s * (D a) is linear in x, rbf and W_rad and T W1 is bilinear, so
+    # <gW1, W1> = <gW_rad, W_rad> = <grbf, rbf> = <gx, x>
+    dot = lambda a, b: float((a.double().cpu() * t(np.asarray(b))).sum())  # noqa: E731
+    rhs = dot(y, d["gy"])
+    errs["<gW2,W2>"] = abs(sum(dot(g, w) for g, w in zip(bw["gw2"], d["w2"])) - rhs) / abs(rhs)
+    ref = dot(bw["gx"], d["x"])
+    errs["<gW1,W1>"] = abs(sum(dot(g, w) for g, w in zip(bw["gw1"], d["w1"])) - ref) / abs(ref)
+    errs["<gWrad,Wrad>"] = abs(dot(bw["gw_rad"], d["w_rad"]) - ref) / abs(ref)
+    errs["<grbf,rbf>"] = abs(dot(bw["grbf"], d["rbf"]) - ref) / abs(ref)
     H.note("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     tol = H.TOL_BF16 if dtype == "bf16" else H.TOL_F32
     assert all(v <= tol for v in errs.values()), errs
@@ -149,7 +154,7 @@ def test_large_system_full_size_chunked():
     torch.cuda.reset_peak_memory_stats()
     ce = 262144
     y, _ = K.so2conv_fwd(*args, saved=None, chunk_edges=ce)
-    bw = K.so2conv_bwd(*args, None, dd["gy"], need=("x", "pos", "rbf", "w2", "edge"), chunk_edges=ce)
+    bw = K.so2conv_bwd(*args, None, dd["gy"], need=("x", "pos", "rbf", "w_rad", "w1", "w2", "edge"), chunk_edges=ce)
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated()
     kc = dd["kcfg"]
@@ -177,5 +182,15 @@ def test_large_system_full_size_chunked():
     re_b = bwd(sub)
     errs["grbf"] = H.relerr(bw["grbf"].cpu()[edges], re_b["grbf"])
     errs["gedge"] = H.relerr(bw["gedge"].cpu()[edges], re_b["gedge"])
+    # weight gradients over all ~10M edges: T = s * (D a) is linear in x, rbf and W_rad and
+    # T W1 is bilinear, so <gW1, W1> = <gW_rad, W_rad> = <grbf, rbf> = <gx, x>; y is linear
+    # in W2, so <gW2, W2> = <gy, y> (gx and grbf are checked element-wise above)
+    dot = lambda a, b: float((a.double().cpu() * torch.as_tensor(np.asarray(b), dtype=DT)).sum())  # noqa: E731
+    ref = dot(bw["gx"], d["x"])
+    for key, val in (("<gW1,W1>", sum(dot(g, w) for g, w in zip(bw["gw1"], d["w1"]))),
+                     ("<gWrad,Wrad>", dot(bw["gw_rad"], d["w_rad"])), ("<grbf,rbf>", dot(bw["grbf"], d["rbf"]))):
+        errs[key] = abs(val - ref) / abs(ref)
+    yy = dot(y, d["gy"])
+    errs["<gW2,W2>"] = abs(sum(dot(g, w) for g, w in zip(bw["gw2"], d["w2"])) - yy) / abs(yy)
     H.note("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     assert all(v <= H.TOL_BF16 for v in errs.values()), errs

@@ -253,3 +253,22 @@ def test_double_backward_hessian_symmetry(small):
     h2 = O.double_backward(inp, gy, px=p2)["gx"]
     a, b = float((p2 * h1).sum()), float((p1 * h2).sum())
     assert abs(a - b) <= 1e-10 * max(1.0, abs(a))
+
+
+def test_backward_scaling_identities(small):
+    """The first linear's input T = s * (D a) is linear in x, in rbf and in W_rad
+    (s = rbf W_rad), and T W1 is bilinear, so scaling any one of x, rbf, W_rad,
+    W1 by (1 + t) changes every first-linear output the same way: the four
+    directional derivatives agree, <gx, x> = <grbf, rbf> = <gW_rad, W_rad> =
+    <gW1, W1>. y is linear in W2: <gW2, W2> = <gy, y>. (These hold at any size
+    and tie the weight gradients to per-node and per-edge outputs.)"""
+    _, inp, gy = small
+    g = O.backward(inp, gy)
+    y = O.forward(inp)
+    vals = [float(_dot(g["gx"], inp.x)), float(_dot(g["grbf"], inp.rbf)), float(_dot(g["gw_rad"], inp.w_rad)),
+            float(_dot(g["gw1"], inp.w1))]
+    ref = vals[0]
+    assert abs(ref) > 1e-6
+    assert all(abs(v - ref) <= 1e-11 * abs(ref) for v in vals), vals
+    a, b = float(_dot(g["gw2"], inp.w2)), float((gy * y).sum())
+    assert abs(a - b) <= 1e-11 * abs(b)
