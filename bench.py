@@ -31,7 +31,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-METRIC = "edges/sec fwd+bwd+dbwd SO(2) conv (lmax=4,C=128); HBM GB/s % of peak"
+def metric_name(lmax, channels, two_stage):
+    stages = "fwd+bwd" if two_stage else "fwd+bwd+dbwd"
+    return f"edges/sec {stages} SO(2) conv (lmax={lmax},C={channels}); HBM GB/s % of peak"
+
+
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0     # dense
 PEAK_HBM_GBS = 8000.0
@@ -48,6 +52,46 @@ def gemm_flops_per_edge(L, M, C):
     mac1 = 2 * C * C * ((L + 1) * (2 * L + 1) + 4 * s)
     mac2 = C * C * ((L + 1) ** 2 + 4 * s)
     return 2.0 * (mac1 + mac2)
+
+
+def host_cores():
+    """Cores this process may run on: its CPU affinity, limited by a cgroup CPU
+    quota when one is set (a container's share of the host)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            n = max(1, min(n, int(float(quota) / float(period))))
+    except (OSError, ValueError):
+        pass
+    return n
+
+
+def _sources_sha256():
+    import hashlib
+    csrc = os.path.join(ROOT, "so_graph_convolution_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_step_traffic(config, dtype, keep_bwd, ms_step):
+    """HBM bytes of one whole step from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record (copy-calibrated, every kernel of the step), if the record covers this
+    workload and launch mix and every kernel source is unchanged since; else None."""
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"hbm_bytes_step_{config}_{dtype}.json")))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != _sources_sha256() or bool(rec.get("backward_cotangents_kept")) != bool(keep_bwd):
+        return None
+    b = float(rec["step_bytes"])
+    return {"counted_bytes_per_step": b, "GBps": b / (ms_step * 1e-3) / 1e9,
+            "frac_of_peak": b / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, "peak_GBps": PEAK_HBM_GBS,
+            "per_stage_bytes": rec.get("per_stage_bytes"), "source": rec.get("summary")}
 
 
 def measured_gemm_traffic(config, dtype, keep_bwd):
@@ -77,14 +121,14 @@ def cpu_baseline(d, n_edges_sample, seed=0, dbwd=True):
     import numpy as np
     import torch
     from oracle import so2conv_oracle as O
-    cores = min(16, len(os.sched_getaffinity(0)))
-    torch.set_num_threads(cores)
+    torch.set_num_threads(host_cores())
     inp = O.to_oracle_inputs(d)
     E = len(d["src"])
     n = min(n_edges_sample, E)
     edges = np.arange(n)
     t = lambda a: torch.tensor(a, dtype=torch.float64)  # noqa: E731
     gy = t(d["gy"])
+    O.backward(inp, gy, chunk=2048, edges=np.arange(min(256, E)))       # warmup (thread pool, allocator)
     t0 = time.perf_counter()
     O.forward(inp, chunk=2048, edges=edges)
     O.backward(inp, gy, chunk=2048, edges=edges)
@@ -93,7 +137,8 @@ def cpu_baseline(d, n_edges_sample, seed=0, dbwd=True):
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "edges/s", "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": f"first {n} of {E} edges of the same workload, {'fwd+bwd+dbwd' if dbwd else 'fwd+bwd'} in "
-                      f"float64 (PyTorch CPU, autograd), {dt:.1f} s"}
+                      f"float64 (PyTorch CPU, autograd) after a 256-edge warmup, {dt:.1f} s; "
+                      f"{len(os.sched_getaffinity(0))} cores in the process's affinity"}
 
 
 def cpu_baseline_mole(d, m, n_edges_sample):
@@ -103,8 +148,7 @@ def cpu_baseline_mole(d, m, n_edges_sample):
     import torch
     from oracle import mole_oracle as MO
     from oracle import so2conv_oracle as O
-    cores = min(16, len(os.sched_getaffinity(0)))
-    torch.set_num_threads(cores)
+    torch.set_num_threads(host_cores())
     base = O.to_oracle_inputs(d)
     E = len(d["src"])
     n = min(n_edges_sample, E)
@@ -179,7 +223,7 @@ def bench_grid(args):
     progress(f"{out['ms_per_step']:.2f} ms/step")
     if args.cpu_edges > 0:
         import oracle.grid_oracle as GO
-        torch.set_num_threads(min(16, len(os.sched_getaffinity(0))))
+        torch.set_num_threads(host_cores())
         n = 200
         r = {k: torch.tensor(v[:n] if k in ("x", "gU", "px") else v, dtype=torch.float64) for k, v in host.items()}
         t1 = time.perf_counter()
@@ -256,7 +300,7 @@ def bench_s2act(args):
     progress(f"{out['ms_per_step']:.2f} ms/step  stages {ms.round(2).tolist()}  dbwd {ach:.1f} TFLOP/s")
     if args.cpu_edges > 0:
         import oracle.s2act_oracle as SO
-        torch.set_num_threads(min(16, len(os.sched_getaffinity(0))))
+        torch.set_num_threads(host_cores())
         n, chunk = min(args.cpu_edges, 8192), 2048
         h = {k: v.double().cpu() for k, v in (("G", g["G"]), ("P", g["P"]))}
         t1 = time.perf_counter()
@@ -292,7 +336,10 @@ def main():
                     help="per-edge cutoff envelope on the messages (with genv, and genv2 in the double backward)")
     ap.add_argument("--heads", type=int, default=1,
                     help="per-head attention weights on the messages (EquiformerV3: 8 heads), times the envelope")
-    ap.add_argument("--cpu-edges", type=int, default=8192, help="edge sample of the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-edges", type=int, default=16384, help="edge sample of the CPU oracle baseline (0: skip)")
+    ap.add_argument("--bounded-gib", type=float, default=32.0,
+                    help="after the main line, time the same step with the workspace capped at this many GiB "
+                         "(edge chunks), reported as bounded_memory (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -456,8 +503,7 @@ def main():
     elem = 2 if dtype == "bf16" else 4
     mat_gib = elem * E * (dd_ * (C0 + C1) + qlm * (C0 + 2 * C1 + C1 + 2 * C1)) / 2**30
     out = {
-        "metric": METRIC if not two_stage else
-        f"edges/sec fwd+bwd SO(2) conv (lmax={cfg.lmax},C={cfg.channels})",
+        "metric": metric_name(cfg.lmax, cfg.channels, two_stage),
         "value": value,
         "unit": "edges/s",
         "n_gpus": 1,
@@ -490,9 +536,39 @@ def main():
         "peak_device_memory_GiB": torch.cuda.max_memory_allocated() / 2**30,
         "materialising_estimate_GiB": {"forward_state": K.so2conv_saved_bytes(kc, E) / 2**30,
                                        "separate_operation_intermediates": mat_gib},
-        ("step_tflops_3F" if two_stage else "step_tflops_8F"): (3 if two_stage else 8) * F * E / (ms_step * 1e-3) / 1e12,
+        ("step_tflops_3F_equivalent" if two_stage else "step_tflops_8F_equivalent"):
+            (3 if two_stage else 8) * F * E / (ms_step * 1e-3) / 1e12,
+        "hbm": measured_step_traffic(args.config, dtype, keep_bwd, ms_step) if not (mole or args.envelope) else None,
     }
     progress(f"timed {args.steps} steps: {ms_step:.1f} ms/step")
+    if args.bounded_gib > 0 and not mole and keep_state and not chunked:
+        # the same step with the workspace capped (edge chunks), kept state and cotangents as above
+        del ws
+        torch.cuda.empty_cache()
+        cap = args.bounded_gib * 2**30
+        ce = 1 << max(12, int(math.log2(max(E, 4096))) + 1)
+        while ce > 4096 and max(K.so2conv_chunked_workspace_bytes(kc, N, E, s_, ce) for s_ in (0, 1, 2)) > cap:
+            ce //= 2
+        ws = torch.empty(max(K.so2conv_chunked_workspace_bytes(kc, N, E, s_, ce) for s_ in (0, 1, 2)),
+                         dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        step()
+        torch.cuda.synchronize()
+        nb = max(1, min(args.steps, 3))
+        t0 = time.perf_counter()
+        for _ in range(nb):
+            step()
+        torch.cuda.synchronize()
+        wall_b = time.perf_counter() - t0
+        out["bounded_memory"] = {
+            "value": E * nb / wall_b, "unit": "edges/s", "ms_per_step": wall_b * 1e3 / nb, "steps": nb,
+            "workspace_cap_GiB": args.bounded_gib, "workspace_GiB": ws.numel() / 2**30, "edge_chunk": ce,
+            "peak_device_memory_GiB": torch.cuda.max_memory_allocated() / 2**30,
+            "note": "same step, workspace for edge chunks within the cap; forward state and backward "
+                    "cotangents kept as in the main line"}
+        progress(f"bounded memory: {wall_b * 1e3 / nb:.1f} ms/step, chunk {ce} edges, peak "
+                 f"{out['bounded_memory']['peak_device_memory_GiB']:.1f} GiB")
     if args.cpu_edges > 0:
         out["cpu_baseline"] = cpu_baseline_mole(d, mix_in, args.cpu_edges) if mole else \
             cpu_baseline(d, args.cpu_edges, dbwd=not two_stage)
