@@ -157,6 +157,22 @@ int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
                 const float* env, const void* w_rad, const void* const* w1, const void* const* w2, void* y,
                 void* saved, void* ws, size_t ws_bytes, void* stream);
 
+/* so2conv_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * inputs and output y as so2conv_fwd with saved = NULL (no per-edge state is
+ * kept; the forward runs in edge chunks that recompute it). The workspace is
+ * a fixed 256 MiB device array inside the library, one per GPU, held until
+ * the process ends; the call allocates nothing and synchronises nothing.
+ * Returns SO2_EWORKSPACE (with a message naming the bytes needed) when a
+ * 1024-edge chunk of this configuration does not fit in 256 MiB (for example
+ * bfloat16 calls with many nodes, whose float32 node copies live in the
+ * workspace); other errors as so2conv_fwd. Every call on one GPU uses that
+ * GPU's one array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. */
+int so2conv_fwd_noalloc(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos,
+                        const float* rbf, const float* env, const void* w_rad, const void* const* w1,
+                        const void* const* w2, void* y, void* stream);
+
 /* Backward (vector-Jacobian product with cotangent gy, Section 3.3): gx, gpos,
  * grbf, genv, gw_rad, gw1[m], gw2[m] and gedge = dL/dv_e (for virials). `saved`
  * comes from so2conv_fwd on the same inputs, or is NULL (the forward state is

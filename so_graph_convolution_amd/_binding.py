@@ -53,6 +53,8 @@ EXPORTS = {
     "so2conv_chunked_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), c_i32, c_i64, ctypes.c_int, c_i64]),
     # (cfg, g, x, pos, rbf, env, w_rad, w1, w2, y, saved, ws, ws_bytes, stream)
     "so2conv_fwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 10 + [c_sz, c_vp]),
+    # (cfg, g, x, pos, rbf, env, w_rad, w1, w2, y, stream)
+    "so2conv_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 9),
     # (cfg, g, x, pos, rbf, env, w_rad, w1, w2, saved, gy, gx, gpos, grbf, genv, gw_rad, gw1, gw2, gedge,
     #  ws, ws_bytes, stream)
     "so2conv_bwd": (ctypes.c_int, [ctypes.POINTER(Cfg), ctypes.POINTER(GraphC)] + [c_vp] * 19 + [c_sz, c_vp]),

@@ -2033,3 +2033,8 @@ int so2s2_dbwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const floa
 }
 
 }  // extern "C"
+
+namespace so2 {
+// error message of the library's other translation units (read by so2conv_last_error)
+int set_error(int code, const std::string& msg) { return fail(code, msg); }
+}  // namespace so2

@@ -13,7 +13,8 @@ import torch
 
 from ._binding import SO2_DEBUG_CHECKS, Cfg, GraphC, check, lib
 
-__all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_bwd", "so2conv_dbwd",
+__all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_fwd_noalloc", "so2conv_bwd",
+           "so2conv_dbwd",
            "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes",
            "so2conv_saved_bwd_bytes", "weight_shapes",
            "so2conv_profile_enable", "so2conv_profile_reset", "so2conv_profile_read",
@@ -218,6 +219,21 @@ def so2conv_fwd(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, saved=None
     check(lib().so2conv_fwd(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad), p1, p2,
                             _p(y), _p(saved), _p(ws), ws.numel(), _stream()), "so2conv_fwd")
     return y, saved
+
+
+def so2conv_fwd_noalloc(cfg: SO2Config, g: Graph, x, pos, rbf, w_rad, w1, w2, env=None, y=None):
+    """Forward through the library's fixed device scratch (no workspace argument,
+    no state kept). y: optional preallocated output."""
+    _common(cfg, g, x, pos, rbf, w_rad, env)
+    s1, s2 = weight_shapes(cfg)
+    dt = cfg.torch_dtype
+    p1, k1 = _ptr_array(w1, "w1", s1, dt)
+    p2, k2 = _ptr_array(w2, "w2", s2, dt)
+    y = torch.empty_like(x) if y is None else _dev(y, "y", dtype=dt, shape=x.shape)
+    c, gc = cfg.c(), g.c()
+    check(lib().so2conv_fwd_noalloc(ctypes.byref(c), ctypes.byref(gc), _p(x), _p(pos), _p(rbf), _p(env), _p(w_rad),
+                                    p1, p2, _p(y), _stream()), "so2conv_fwd_noalloc")
+    return y
 
 
 GRAD_KEYS = ("x", "pos", "rbf", "w_rad", "w1", "w2", "edge", "env")
