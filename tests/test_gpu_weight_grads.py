@@ -104,6 +104,7 @@ def _compare(name):
     got = _run(cfg_name, stage, e_end)
     dtype = so2_synth.CONFIGS[cfg_name].dtype
     tol = H.TOL_BF16 if dtype == "bf16" else H.TOL_F32
+    tol_elem = H.TOL_ELEM_BF16 if dtype == "bf16" else H.TOL_ELEM_F32
     floor = H.FLOOR_BF16 if dtype == "bf16" else H.FLOOR_F32
     worst = {}
     for k_tensor, (key, g) in enumerate(FX.tensor_list(got)):
@@ -118,7 +119,8 @@ def _compare(name):
                       "maxabs": abs(float(np.abs(a).max()) - mx) / mx}
     for key, e in worst.items():
         H.note(f"  {key}: " + " ".join(f"{k}={v:.2e}" for k, v in e.items()))
-    bad = {key: e for key, e in worst.items() if not all(v <= tol for v in e.values())}
+    bad = {key: e for key, e in worst.items()
+           if not all(v <= (tol_elem if k == "elem" else tol) for k, v in e.items())}
     assert not bad, bad
 
 
