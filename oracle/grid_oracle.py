@@ -1,5 +1,6 @@
 """Oracle (test infrastructure only) of the node-to-node spherical projection
-with its channel maps: TrimSO(2) page, Appendix B.4 (Spherical activations).
+with its channel maps, and of the back-projection from the grid: TrimSO(2)
+page, Appendix B.4 (Spherical activations).
 
 For one atom with features X^(l) (n_l x C_in, degree-major rows of the node
 array), the grid values before the nonlinearity are
@@ -64,3 +65,41 @@ def double_backward(x, G, W, A, gU, px=None, pW=None, pA=None):
     out = torch.autograd.grad(Lval, [gUl, xl, Wl, Al], allow_unused=True)
     z = [torch.zeros_like(t) if o is None else o for o, t in zip(out, (gUl, xl, Wl, Al))]
     return dict(ggU=z[0], gx=z[1], gW=z[2], gA=z[3])
+
+
+# ----------------------------------------------------------------------------- back-projection
+# TrimSO(2) page, Appendix B.4 (Forward computation, the second identity):
+# after the nonlinearity on the grid, the values Y (n_g x C_h per atom) return
+# to coefficients through H_l (n_l x n_g, the degree-l rows of a caller-
+# supplied (L+1)^2 x n_g matrix) and an output channel map A_out (C_h x C_out):
+#     Z^(l) = H_l (Y A_out)                                  (definition)
+# The page's reordering (H_l Y) A_out is what the HIP path computes; the
+# oracle keeps the definition's order.
+
+def back_forward(Y: torch.Tensor, H: torch.Tensor, A: torch.Tensor) -> torch.Tensor:
+    """Y [N, n_g, C_h], H [(L+1)^2, n_g], A [C_h, C_out] -> Z [N, (L+1)^2, C_out]."""
+    YA = Y @ A                                                   # [N, n_g, C_out]
+    return torch.einsum("jg,ngc->njc", H, YA)
+
+
+def back_backward(Y, H, A, gZ):
+    """dict gY, gA of <gZ, Z> (H is a fixed basis, not differentiated)."""
+    Yl, Al = _leaves(Y, A)
+    Z = back_forward(Yl, H, Al)
+    gY, gA = torch.autograd.grad(Z, [Yl, Al], gZ)
+    return dict(gY=gY, gA=gA)
+
+
+def back_double_backward(Y, H, A, gZ, pY=None, pA=None):
+    """Derivatives of L = <pY, gY> + <pA, gA> (None = zero) with respect to gZ, Y and A."""
+    Yl, Al = _leaves(Y, A)
+    gZl = gZ.detach().clone().requires_grad_(True)
+    Z = back_forward(Yl, H, Al)
+    g = torch.autograd.grad(Z, [Yl, Al], gZl, create_graph=True)
+    Lval = torch.zeros((), dtype=DT)
+    for gi, p in zip(g, (pY, pA)):
+        if p is not None:
+            Lval = Lval + (gi * p).sum()
+    out = torch.autograd.grad(Lval, [gZl, Yl, Al], allow_unused=True)
+    z = [torch.zeros_like(t) if o is None else o for o, t in zip(out, (gZl, Yl, Al))]
+    return dict(ggZ=z[0], gY=z[1], gA=z[2])

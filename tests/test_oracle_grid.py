@@ -139,3 +139,117 @@ def test_rotating_features_rotates_the_grid():
     lhs = GO.forward(xr, _basis(L, u), W, A)
     rhs = GO.forward(x, _basis(L, u @ Q), W, A)
     assert torch.allclose(lhs, rhs, atol=1e-11, rtol=0)
+
+
+# ----------------------------------------------------------------------------- back-projection
+def _back_case(L=2, C_h=4, C_out=3, n_g=6, N=3, seed=10):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=g, dtype=DT)  # noqa: E731
+    return r(N, n_g, C_h), r((L + 1) ** 2, n_g), r(C_h, C_out)
+
+
+def test_back_brute_force_definition():
+    Y, H, A = _back_case()
+    N, n_g, C_h = Y.shape
+    d, C_out = H.shape[0], A.shape[1]
+    Z = GO.back_forward(Y, H, A)
+    for i, j, c in itertools.product(range(N), range(d), range(C_out)):
+        s = sum(float(H[j, gp]) * float(Y[i, gp, h]) * float(A[h, c]) for gp in range(n_g) for h in range(C_h))
+        assert abs(float(Z[i, j, c]) - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def _scipy_basis(L, u):
+    """[n, (L+1)^2] real orthonormal harmonics from scipy (no Condon-Shortley
+    phase, orders -l..l, Y_1 = sqrt(3/4pi) (y, z, x))."""
+    import math
+
+    import numpy as np
+    import scipy.special
+    u = u.numpy()
+    polar = np.arccos(np.clip(u[:, 2], -1, 1))
+    azim = np.arctan2(u[:, 1], u[:, 0])
+    cols = []
+    for l in range(L + 1):
+        out = np.zeros((len(u), 2 * l + 1))
+        for m in range(l + 1):
+            c = scipy.special.sph_harm_y(l, m, polar, azim)
+            if m == 0:
+                out[:, l] = c.real
+            else:
+                out[:, l + m] = math.sqrt(2) * (-1) ** m * c.real
+                out[:, l - m] = math.sqrt(2) * (-1) ** m * c.imag
+        cols.append(out)
+    return torch.tensor(np.concatenate(cols, 1), dtype=DT)
+
+
+def test_back_projection_inverts_an_exact_quadrature_grid():
+    """G = harmonics at a Gauss-Legendre x uniform grid exact to degree 2L and
+    H = G^T diag(w): H_l G_l' = delta_ll' I, so back-projecting the grid values
+    of band-limited coefficients with an identity channel map returns them
+    (and a channel map A maps them by A)."""
+    import numpy as np
+    L = 3
+    zs, wz = np.polynomial.legendre.leggauss(L + 1)
+    nphi = 2 * L + 1
+    phi = 2 * np.pi * np.arange(nphi) / nphi
+    Zg, Pg = np.meshgrid(zs, phi, indexing="ij")
+    st = np.sqrt(1 - Zg * Zg)
+    u = torch.tensor(np.stack([st * np.cos(Pg), st * np.sin(Pg), Zg], -1).reshape(-1, 3), dtype=DT)
+    w = torch.tensor((np.repeat(wz[:, None], nphi, 1) * 2 * np.pi / nphi).reshape(-1), dtype=DT)
+    G = _scipy_basis(L, u)                                   # [n_g, d]
+    H = G.T * w                                              # [d, n_g]
+    g = torch.Generator().manual_seed(11)
+    X = torch.randn(2, (L + 1) ** 2, 5, generator=g, dtype=DT)
+    Y = torch.einsum("gj,njc->ngc", G, X)                    # grid values
+    assert torch.allclose(GO.back_forward(Y, H, torch.eye(5, dtype=DT)), X, atol=1e-12)
+    A = torch.randn(5, 3, generator=g, dtype=DT)
+    assert torch.allclose(GO.back_forward(Y, H, A), X @ A, atol=1e-12)
+
+
+def test_back_reordering_and_linearity():
+    """(H_l Y) A_out equals the definition H_l (Y A_out); Z is linear in Y and in A."""
+    Y, H, A = _back_case(L=3, C_h=5, C_out=4, n_g=9, N=2, seed=12)
+    Y2, _, A2 = _back_case(L=3, C_h=5, C_out=4, n_g=9, N=2, seed=13)
+    Z = GO.back_forward(Y, H, A)
+    assert torch.allclose(torch.einsum("jg,ngh->njh", H, Y) @ A, Z, atol=1e-12)
+    f = GO.back_forward
+    assert torch.allclose(f(Y + 3 * Y2, H, A), Z + 3 * f(Y2, H, A), atol=1e-12)
+    assert torch.allclose(f(Y, H, A - A2), Z - f(Y, H, A2), atol=1e-12)
+
+
+@pytest.mark.parametrize("which", ["Y", "A"])
+def test_back_backward_matches_fd(which):
+    Y, H, A = _back_case(L=2, C_h=4, C_out=3, n_g=7, N=3, seed=14)
+    gZ = torch.randn(Y.shape[0], H.shape[0], A.shape[1], generator=torch.Generator().manual_seed(15), dtype=DT)
+    g = GO.back_backward(Y, H, A, gZ)
+    q = torch.randn_like({"Y": Y, "A": A}[which])
+    eps = 1e-6
+
+    def f(e):
+        a = dict(Y=Y, A=A)
+        a[which] = a[which] + e * q
+        return _dot(GO.back_forward(a["Y"], H, a["A"]), gZ)
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    assert abs(_dot(g["g" + which], q) - fd) <= 1e-7 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("which", ["gZ", "Y", "A"])
+def test_back_double_backward_matches_fd(which):
+    Y, H, A = _back_case(L=2, C_h=4, C_out=3, n_g=7, N=3, seed=16)
+    gen = torch.Generator().manual_seed(17)
+    r = lambda t: torch.randn(t.shape, generator=gen, dtype=DT)  # noqa: E731
+    gZ = torch.randn(Y.shape[0], H.shape[0], A.shape[1], generator=gen, dtype=DT)
+    pY, pA = r(Y), r(A)
+    dd = GO.back_double_backward(Y, H, A, gZ, pY=pY, pA=pA)
+    base = dict(Y=Y, A=A, gZ=gZ)
+    q = r(base[which])
+    eps = 1e-6
+
+    def L(e):
+        a = dict(base)
+        a[which] = a[which] + e * q
+        g = GO.back_backward(a["Y"], H, a["A"], a["gZ"])
+        return _dot(g["gY"], pY) + _dot(g["gA"], pA)
+    fd = (L(eps) - L(-eps)) / (2 * eps)
+    key = {"gZ": "ggZ", "Y": "gY", "A": "gA"}[which]
+    assert abs(_dot(dd[key], q) - fd) <= 1e-7 * max(1.0, abs(fd))
