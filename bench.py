@@ -39,6 +39,7 @@ def metric_name(lmax, channels, two_stage):
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0     # dense
 PEAK_HBM_GBS = 8000.0
+SPLIT_PRODUCTS = 6                 # bf16 MFMA products per float32 product of the split GEMMs
 WORKLOADS = {"T": "tiny periodic radius graph", "S": "eSEN-like small periodic radius graph",
              "M": "UMA/eSEN-like medium periodic radius graph", "H": "EquiformerV3-like high-degree periodic radius graph",
              "X": "large clustered periodic radius graph", "P1": "EquiformerV3 captured-batch-sized radius graph",
@@ -94,23 +95,24 @@ def measured_step_traffic(config, dtype, keep_bwd, ms_step):
             "per_stage_bytes": rec.get("per_stage_bytes"), "source": rec.get("summary")}
 
 
-def measured_gemm_traffic(config, dtype, keep_bwd):
+def measured_gemm_traffic(config, dtype, keep_bwd, split):
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters (copy-calibrated) of the medium float32 step, or None for another
-    workload, another launch mix (backward cotangents kept or not) or if the
-    GEMM source (gemm.hip, gemm.hpp) changed since."""
+    workload, another launch mix (backward cotangents kept or not, split or
+    float32 products) or if a GEMM source changed since."""
     import hashlib
     if config != "M" or dtype != "f32":
         return None
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "gemm_hbm_traffic_medium.json")))
         csrc = os.path.join(ROOT, "so_graph_convolution_amd", "csrc")
-        src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("gemm.hip", "gemm.hpp"))
+        src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                       for f in ("gemm.hip", "gemm.hpp", "gemm_x3.hip", "gemm_dma.hpp", "gemm_tile.hpp"))
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
         return None
-    if bool(rec.get("backward_cotangents_kept")) != bool(keep_bwd):
+    if bool(rec.get("backward_cotangents_kept")) != bool(keep_bwd) or bool(rec.get("split_products")) != bool(split):
         return None
     return rec["gemm_bytes_per_step"] / rec["gemm_launches_per_step"]
 
@@ -324,6 +326,9 @@ def main():
     ap.add_argument("--config", default="M")
     ap.add_argument("--dtype", choices=("f32", "bf16"), default=None,
                     help="array dtype (default: the workload's own: f32 for M, bf16 for H and X)")
+    ap.add_argument("--f32-native", action="store_true",
+                    help="float32 per-order products on the float32 matrix cores (SO2_F32_NATIVE) instead of the "
+                         "default bfloat16-piece products")
     ap.add_argument("--pos2", action="store_true",
                     help="the double backward also returns position derivatives (gpos2)")
     ap.add_argument("--op", choices=("conv", "grid", "mole", "s2act"), default="conv",
@@ -386,7 +391,8 @@ def main():
         return torch.tensor(np.ascontiguousarray(a), dtype=dt, device=dev)
 
     ft = torch.bfloat16 if dtype == "bf16" else torch.float32
-    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype, heads=args.heads)
+    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype, heads=args.heads,
+                     f32_native=args.f32_native)
     g = K.so2conv_graph_prepare(N, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
     x, pos, rbf, w_rad = t(d["x"], ft), t(d["pos"]), t(d["rbf"]), t(d["w_rad"], ft)
     w1, w2 = [t(w, ft) for w in d["w1"]], [t(w, ft) for w in d["w2"]]
@@ -476,24 +482,39 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     K.so2conv_profile_enable(False)
-    n_l, gemm_ms, gemm_fl, gemm_by = K.so2conv_profile_read(-1)
-    per_kind = {}
-    kinds = ((3, "ABt"), (4, "AtB")) if dtype == "bf16" else \
-        ((0, "AB"), (1, "ABt"), (2, "AtB"), (5, "AB complex"), (6, "ABt complex"), (7, "AtB complex"))
-    for kind, name in kinds:
+    kinds = {0: "AB", 1: "ABt", 2: "AtB", 3: "ABt bf16", 4: "AtB bf16", 5: "AB complex", 6: "ABt complex",
+             7: "AtB complex", 8: "AB pieces", 9: "ABt pieces", 10: "AtB pieces"}
+    per_kind, raw = {}, {}
+    for kind, name in kinds.items():
         n, ms, fl, by = K.so2conv_profile_read(kind)
-        per_kind[name] = {"launches": n, "avg_ms": ms / max(n, 1), "tflops": fl / max(ms, 1e-9) / 1e9,
-                          "algorithmic_bytes_per_launch": by / max(n, 1)}
+        raw[kind] = (n, ms, fl, by)
+        if n:
+            per_kind[name] = {"launches": n, "avg_ms": ms / n, "algorithmic_tflops": fl / max(ms, 1e-9) / 1e9,
+                              "algorithmic_bytes_per_launch": by / n}
     K.so2conv_profile_reset()
+    # the dominant kernel: the per-order products (float32 through bfloat16 pieces,
+    # SPLIT_PRODUCTS bf16 MFMA products per float32 product; float32 on the float32
+    # matrix cores with SO2_F32_NATIVE; bfloat16), not the small radial products
+    split = sum(raw[k][0] for k in (8, 9, 10)) > 0
+    dom = (8, 9, 10) if split else ((3, 4) if dtype == "bf16" else (0, 1, 2, 5, 6, 7))
+    n_l, gemm_ms, gemm_fl, gemm_by = (sum(raw[k][i] for k in dom) for i in range(4))
     st = np.array([[a.elapsed_time(b), b.elapsed_time(c), c.elapsed_time(e)] for a, b, c, e in stage])
     ms_step = wall * 1e3 / args.steps
     value = E * args.steps / wall
     F = gemm_flops_per_edge(cfg.lmax, cfg.mmax, cfg.channels)
-    achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12
-    peak = PEAK_BF16_MFMA_TFLOPS if dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    kname = ("gemm_bf16_kernel (bf16 MFMA per-order linears)" if dtype == "bf16" else
-             "gemm_f32_dma_kernel (order 0) and gemm_cplx_dma_kernel (orders >= 1, three real products per complex "
-             "one; fp32 MFMA)") + ", all launches of the timed steps"
+    alg_tflops = gemm_fl / (gemm_ms * 1e-3) / 1e12
+    executed = gemm_fl * (SPLIT_PRODUCTS if split else 1)
+    achieved = executed / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_MFMA_TFLOPS if (dtype == "bf16" or split) else PEAK_FP32_MFMA_TFLOPS
+    if split:
+        kname = ("gemm_x3_kernel: float32 per-order products (orders >= 1 realified) with every operand the exact "
+                 f"sum of three bfloat16 pieces, {SPLIT_PRODUCTS} bf16 MFMA products per float32 product")
+    elif dtype == "bf16":
+        kname = "gemm_bf16_kernel (bf16 MFMA per-order linears)"
+    else:
+        kname = ("gemm_f32_dma_kernel (order 0) and gemm_cplx_dma_kernel (orders >= 1, three real products per "
+                 "complex one; fp32 MFMA)")
+    kname += ", all launches of the timed steps"
     # Appendix B.5's intermediates of the separate-operation schedule (retained-order
     # layout, one stored copy each) and the per-edge forward state the fused path
     # keeps when it does not recompute: the memory a materialising implementation
@@ -522,14 +543,20 @@ def main():
                    + (", dbwd with gpos2" if args.pos2 else "")
                    + (f", {args.heads}-head attention weights times the cutoff envelope" if args.heads > 1
                       else (", cutoff envelope" if args.envelope else ""))
-                   + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else ""),
+                   + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else "")
+                   + (", float32 products on the float32 matrix cores" if args.f32_native and dtype == "f32" else ""),
                    "edge_chunks": chunked, "forward_state_kept": keep_state, "backward_cotangents_kept": keep_bwd},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None if mole else measured_gemm_traffic(args.config, dtype, keep_bwd),
+                     "frac": achieved / peak,
+                     "traffic": None if mole else measured_gemm_traffic(args.config, dtype, keep_bwd, split),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
                      "kernel": kname,
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
-                     "algorithmic_flops_per_step": gemm_fl / args.steps, "per_kind": per_kind},
+                     "executed_flops_per_step": executed / args.steps,
+                     "algorithmic_flops_per_step": gemm_fl / args.steps,
+                     "algorithmic_tflops": alg_tflops,
+                     "algorithmic_frac_of_fp32_peak": alg_tflops / PEAK_FP32_MFMA_TFLOPS if dtype == "f32" else None,
+                     "per_kind": per_kind},
         "stage_ms": {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean())} if two_stage else
         {"fwd": float(st[:, 0].mean()), "bwd": float(st[:, 1].mean()), "dbwd": float(st[:, 2].mean())},
         "step_gemm_share": gemm_ms / args.steps / ms_step,

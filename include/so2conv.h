@@ -89,7 +89,16 @@ enum {
    * shifts, rbf and message weights. The call then synchronises its stream and returns
    * SO2_EDEVICE (message: the failed checks) instead of computing; the word of
    * the last checked call stays readable through so2conv_debug_status. */
-  SO2_DEBUG_CHECKS = 2
+  SO2_DEBUG_CHECKS = 2,
+  /* float32 calls: run the per-order products on the float32 matrix cores
+   * (v_mfma_f32_32x32x2_f32, orders >= 1 as three-product complex GEMMs)
+   * instead of the default, which writes every float32 operand as the exact
+   * sum of three bfloat16 pieces and multiplies the pieces on the bfloat16
+   * matrix cores with float32 accumulation (six piece products per float32
+   * product; the three dropped ones sum to below 2^-23 of it). Both give
+   * float32-accurate products; the default is faster on gfx950, whose
+   * bfloat16 matrix rate is sixteen times its float32 one. */
+  SO2_F32_NATIVE = 4
 };
 
 /* heads: 0 or 1 = one weight per edge; H > 1 divides channels, C / H is 16,

@@ -118,6 +118,7 @@ struct Ctx {
   int bf;    // 1: bfloat16 boundary arrays and GEMM operands
   int es;    // bytes per GEMM-operand element
   int debug; // SO2_DEBUG_CHECKS
+  int split = 0; // float32 products through bfloat16 pieces (float32 calls without SO2_F32_NATIVE)
   int ns = 1; // weight sets: one per system (the plain operator has one)
   int nk = 0; // experts of a mixture (0: plain operator)
   size_t node_floats() const { return (size_t)d.d() * d.C; }   // one node row
@@ -134,7 +135,7 @@ int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
   if (cfg->n_rbf < 4 || cfg->n_rbf % 4 || cfg->n_rbf > 1024)
     return fail(SO2_EUNSUPPORTED, "n_rbf must be a multiple of 4 in [4, 1024]");
   if (cfg->dtype != SO2_F32 && cfg->dtype != SO2_BF16) return fail(SO2_EUNSUPPORTED, "dtype must be SO2_F32 or SO2_BF16");
-  if (cfg->flags & ~SO2_DEBUG_CHECKS) return fail(SO2_EINVAL, "unknown cfg flags");
+  if (cfg->flags & ~(SO2_DEBUG_CHECKS | SO2_F32_NATIVE)) return fail(SO2_EINVAL, "unknown cfg flags");
   const int H = cfg->heads == 0 ? 1 : cfg->heads;
   if (H < 1 || H > kMaxHeads || C % H) return fail(SO2_EUNSUPPORTED, "heads must divide channels, at most 16");
   if (H > 1 && (C / H) % 64 && C / H != 16 && C / H != 32)
@@ -147,6 +148,7 @@ int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
   c->n_rbf = cfg->n_rbf;
   c->bf = cfg->dtype == SO2_BF16;
   c->es = c->bf ? 2 : 4;
+  c->split = !c->bf && !(cfg->flags & SO2_F32_NATIVE);
   return SO2_OK;
 }
 
@@ -605,7 +607,8 @@ void* offs(void* p, size_t elems, int es) { return static_cast<char*>(p) + elems
 // launching stream and its algorithmic flop count (2 M N K summed over the
 // launch's problems) is recorded; so2conv_profile_read reports the totals.
 struct ProfRec {
-  int kind;          // 0 NN, 1 NT, 2 TN (float32); 3 NT, 4 TN (bfloat16); 5 NN, 6 NT, 7 TN (complex float32)
+  int kind;          // 0 NN, 1 NT, 2 TN (float32); 3 NT, 4 TN (bfloat16); 5 NN, 6 NT, 7 TN (complex float32);
+                     // 8 NN, 9 NT, 10 TN (float32 through bfloat16 pieces, kSplitProducts MFMA products each)
   double flops;
   double bytes;      // algorithmic: A, B read once, C (or the split partials) written once
   hipEvent_t a, b;
@@ -614,8 +617,15 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 
-int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int bf, hipStream_t s) {
+// Operand kinds of run_batch: float32 on the float32 matrix cores, bfloat16,
+// or float32 through bfloat16 pieces (gemm_x3_run; problems it does not take
+// run on the float32 matrix cores).
+enum { kOpF32 = 0, kOpBF16 = 1, kOpSplit = 2 };
+constexpr int kSplitProducts = 6;
+
+int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s) {
   if (ps.empty()) return SO2_OK;
+  const bool bf = op == kOpBF16;
   const double es = bf ? 2.0 : 4.0;
   size_t i = 0;
   while (i < ps.size()) {
@@ -630,18 +640,30 @@ int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int bf, hipStream_t s
                4.0 * f * (double)q.M * q.N * (q.partial ? q.k_splits : 1) * (q.accumulate ? 2 : 1);
       b.p[b.nprob++] = ps[i++];
     }
+    bool split = false;
+    auto launch = [&]() -> int {
+      if (op == kOpSplit) {
+        const int e = gemm_x3_run(b, TA, TB, kSplitProducts, s);
+        if (e != hipErrorNotSupported) {
+          split = true;
+          return e;
+        }
+      }
+      return gemm_run(b, TA, TB, bf, s);
+    };
     if (g_prof_on) {
-      const int kind = ps[0].cplx ? (TA ? 7 : (TB ? 6 : 5)) : (bf ? (TA ? 4 : 3) : (TA ? 2 : (TB ? 1 : 0)));
-      ProfRec r{kind, flops, bytes, nullptr, nullptr};
+      ProfRec r{0, flops, bytes, nullptr, nullptr};
       SO2_HIP(hipEventCreate(&r.a));
       SO2_HIP(hipEventCreate(&r.b));
       SO2_HIP(hipEventRecord(r.a, s));
-      SO2_HIP(gemm_run(b, TA, TB, bf != 0, s));
+      SO2_HIP(launch());
       SO2_HIP(hipEventRecord(r.b, s));
+      r.kind = split ? (TA ? 10 : (TB ? 9 : 8))
+                     : (ps[0].cplx ? (TA ? 7 : (TB ? 6 : 5)) : (bf ? (TA ? 4 : 3) : (TA ? 2 : (TB ? 1 : 0))));
       std::lock_guard<std::mutex> lk(g_prof_mu);
       g_prof.push_back(r);
     } else {
-      SO2_HIP(gemm_run(b, TA, TB, bf != 0, s));
+      SO2_HIP(launch());
     }
   }
   return SO2_OK;
@@ -789,7 +811,8 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
   const Dims& d = c.d;
   const int win = second ? d.wZ() : d.wT(), wout = second ? d.wZ() : d.wU();
   const int lda = transposed ? wout : win, ldc = transposed ? win : wout;
-  std::vector<GemmProb> ps, pc;   // real products; complex products (float32, orders >= 1)
+  std::vector<GemmProb> ps, pc;   // order-0 products; products of orders >= 1 (float32)
+  const int op = c.bf ? kOpBF16 : (c.split ? kOpSplit : kOpF32);
   // float32 data-gradient products of order 0 read the transposed weight copy
   bool use_wt = !c.bf && transposed;
   for (const Lin& l : w.W) use_wt = use_wt && l.WT != nullptr;
@@ -808,6 +831,14 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
         realified_shape(d, second, a, &r, &cc, &off);
         const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
         const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
+        if (a > 0 && c.split) {
+          // realified: [T+ T-] W_a forward, [U+ U-] W_a^T transposed (W_a [r][cc] row-major)
+          if (!transposed)
+            pc.push_back(prob(offs(Ar, ib, c.es), win, offs(W.W, off, c.es), cc, Cr + ob, wout, rows, cc, r, acc));
+          else
+            pc.push_back(prob(offs(Ar, ob, c.es), wout, offs(W.W, off, c.es), cc, Cr + ib, win, rows, r, cc, acc));
+          continue;
+        }
         if (a > 0 && !c.bf) {
           // (T+ + i T-)(W0 + i W1) forward; (U+ + i U-)(W0 - i W1)^T transposed
           const int k = r / 2, h = cc / 2;
@@ -830,9 +861,9 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
         }
       }
     }
-  int rr = run_batch(ps, false, (transposed && !use_wt) || c.bf, c.bf, s);
+  int rr = run_batch(ps, false, (transposed && !use_wt) || c.bf, op, s);
   if (rr) return rr;
-  return run_batch(pc, false, transposed, 0, s);
+  return run_batch(pc, false, transposed, op, s);
 }
 
 // weight gradient of linear `second` per system (realified, float32) over the
@@ -855,7 +886,7 @@ int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* co
     realified_shape(d, second, a, &r, &cc, &off);
     const long ib = mm_block(a, d.L, second ? d.C : d.Ci());
     const long ob = second ? mm_block(a, d.L, d.C) : d.u_block(a);
-    const bool cx = a > 0 && !c.bf;
+    const bool cx = a > 0 && !c.bf && !c.split;   // float32 complex products into the user layout
     std::vector<GemmProb> ps;
     std::vector<Red> red;
     size_t poff = 0;
@@ -882,7 +913,7 @@ int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* co
       red.push_back(rd);
     }
     if (ps.empty()) continue;
-    int rr = run_batch(ps, true, false, c.bf, s);
+    int rr = run_batch(ps, true, false, c.bf ? kOpBF16 : (c.split ? kOpSplit : kOpF32), s);
     if (rr) return rr;
     for (const Red& rd : red)
       SO2_HIP(gemm_reduce(P + rd.poff, rd.splits, cx ? r / 2 : r, cc, G[rd.sy] + off, cc, rd.acc, s));
@@ -962,7 +993,7 @@ int fold_systems(const Ctx& c, int second, const std::vector<float*>& G, float* 
   for (int sy = 0; sy < c.ns; ++sy) {
     void* bp[kMaxL + 1];
     sys_blocks(c, second, merged, sy, bp);
-    SO2_HIP(launch_fold_grad(c.d, second, G[sy], bp, 0, s, !c.bf));
+    SO2_HIP(launch_fold_grad(c.d, second, G[sy], bp, 0, s, !c.bf && !c.split));
   }
   return SO2_OK;
 }
@@ -1351,8 +1382,8 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
     if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, w.tau1, w.tau2, w.tau3, vbar, s));
   }
   if (!mx) {
-    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2, c.bf, s, !c.bf));
-    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1, c.bf, s, !c.bf));
+    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2, c.bf, s, !c.bf && !c.split));
+    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1, c.bf, s, !c.bf && !c.split));
   } else {
     for (int second = 0; second < 2; ++second) {
       if (!(second ? want_w2 : want_w1)) continue;
@@ -1544,8 +1575,8 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     }
   }
   if (!mx) {
-    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2_2, c.bf, s, !c.bf));
-    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1_2, c.bf, s, !c.bf));
+    if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2_2, c.bf, s, !c.bf && !c.split));
+    if (want_w1) SO2_HIP(launch_fold_grad(d, 0, w.gW1r[0], gw1_2, c.bf, s, !c.bf && !c.split));
   } else {
     for (int second = 0; second < 2; ++second) {
       if (!(second ? want_w2 : want_w1)) continue;

@@ -1,0 +1,253 @@
+// float32 GEMMs on the bfloat16 matrix cores: every float32 operand is the
+// exact sum of three bfloat16 pieces, and the products of the pieces run on
+// v_mfma_f32_32x32x16_bf16 with float32 accumulation.
+//
+// Split (truncation, no rounding): for a float32 x with a 24-bit significand,
+//   h = x with the low 16 bits cleared,  r = x - h  (exact),
+//   m = r with the low 16 bits cleared,  l = r - m  (exact, at most 8 bits),
+// so x = h + m + l exactly and each piece is a bfloat16 value (its upper 16
+// bits). A product x y is the sum of the nine piece products, each exact in
+// float32 (8-bit by 8-bit significands). NP = 9 takes all nine; NP = 6 drops
+// m l, l m and l l, whose sum is below 2^-23 |x y| (2^-8 per piece step).
+//
+// The float32 matrix cores run at 1/16 of the bfloat16 rate on gfx950 (157.3
+// vs 2500 TFLOP/s dense), so six or nine bfloat16 products per float32
+// product still leave 1.8-2.6x the float32 peak, and one k tile of operands
+// feeds 16 NP MFMAs per wave: the kernel is bound by the matrix cores, not by
+// operand traffic.
+//
+// Block tile 256 x 256 of eight waves (128 x 64 each: 4 x 2 tiles of 32 x 32,
+// 128 accumulator registers, two waves per SIMD), K tile 16. The operand
+// tiles arrive as float32 straight into LDS (global_load_lds_dwordx4, the
+// float32 kernels' tile layouts) in a ring of four stages; each wave splits
+// the fragments it multiplies (its four A and two B fragments of the tile).
+// The two waves of a SIMD overlap one's split arithmetic with the other's
+// matrix products.
+#include "gemm.hpp"
+#include "gemm_dma.hpp"
+#include "gemm_tile.hpp"
+
+namespace so2 {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int ZM = 256, ZN = 256;   // block tile
+constexpr int ZST = 4;              // stages
+constexpr int ZNT = 512;            // threads (eight waves: 2 along M, 4 along N)
+
+// the three pieces of the eight float32 values of one operand fragment
+struct Pieces {
+  bf16x8 h, m, l;
+};
+__device__ __forceinline__ unsigned hi16(float x) { return __float_as_uint(x) & 0xffff0000u; }
+__device__ __forceinline__ Pieces split8(const float (&f)[8]) {
+  unsigned ph[4], pm[4], pl[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float x0 = f[2 * q], x1 = f[2 * q + 1];
+    const float r0 = x0 - __uint_as_float(hi16(x0)), r1 = x1 - __uint_as_float(hi16(x1));
+    const float s0 = r0 - __uint_as_float(hi16(r0)), s1 = r1 - __uint_as_float(hi16(r1));
+    // upper halves of (x0, x1) -> one dword, element 2q in the low half
+    ph[q] = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+    pm[q] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+    pl[q] = __builtin_amdgcn_perm(__float_as_uint(s1), __float_as_uint(s0), 0x07060302u);
+  }
+  Pieces p;
+  p.h = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+  p.m = __builtin_bit_cast(bf16x8, u32x4{pm[0], pm[1], pm[2], pm[3]});
+  p.l = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+  return p;
+}
+
+__device__ __forceinline__ floatx16 mfma(const bf16x8& a, const bf16x8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// the NP piece products of one row of 32 x 32 tiles (a with each b), smallest
+// pieces first; consecutive MFMAs go to different accumulators
+template <int NP>
+__device__ __forceinline__ void row_products(const Pieces& a, const Pieces (&b)[2], floatx16 (&acc)[2]) {
+  if constexpr (NP == 9) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] = mfma(a.l, b[j].l, acc[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] = mfma(a.m, b[j].l, acc[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] = mfma(a.l, b[j].m, acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma(a.h, b[j].l, acc[j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma(a.m, b[j].m, acc[j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma(a.l, b[j].h, acc[j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma(a.h, b[j].m, acc[j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma(a.m, b[j].h, acc[j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma(a.h, b[j].h, acc[j]);
+}
+
+// wait until this wave's loads of the tile to be read have landed (`ahead`
+// later tiles may still be in flight, four loads each) and publish it to the
+// block; the wait on lgkmcnt also retires this wave's fragment reads
+__device__ __forceinline__ void zsync(int ahead) {
+  if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// C = op(A) op(B) with float32 operands (op as in GemmProb), NP piece products
+template <bool TA, bool TB, int NP>
+__global__ __launch_bounds__(ZNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_x3_kernel(
+    GemmBatch batch) {
+  constexpr bool AK = !TA, BKC = TB;
+  using DA = DT<AK, ZM>;
+  using DB = DT<BKC, ZN>;
+  constexpr int SL = (DA::NB + DB::NB) / (ZNT / 64);
+  static_assert(SL == 4, "four loads per wave and stage");
+  constexpr int STG = DA::FL + DB::FL;
+  __shared__ __attribute__((aligned(16))) float S[ZST * STG];
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * ZM, n0 = tn * ZN;
+  const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
+  const int nkk = kend - kbeg, nk = (nkk + 15) / 16;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave >> 2, wn = wave & 3, li = lane % 32, lk = lane / 32;
+  DSlot sl[SL];
+#pragma unroll
+  for (int j = 0; j < SL; ++j) {
+    const int g = SL * wave + j;
+    sl[j] = g < DA::NB ? dslot<AK, ZM>(g, static_cast<const float*>(p.A), p.lda, m0, p.M, kbeg, lane, 0)
+                       : dslot<BKC, ZN>(g - DA::NB, static_cast<const float*>(p.B), p.ldb, n0, p.N, kbeg, lane,
+                                        DA::FL);
+  }
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+#pragma unroll
+  for (int t = 0; t < ZST - 1; ++t)
+    if (t < nk) dstage(sl, S + t * STG, t, nkk, lane);
+  const int ra = wm * 128 + li, rb = wn * 64 + li;
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    zsync(min(ZST - 2, nk - 1 - kt));
+    if (kt + ZST - 1 < nk) dstage(sl, S + ((kt + ZST - 1) % ZST) * STG, kt + ZST - 1, nkk, lane);
+    const float* st = S + (kt % ZST) * STG;
+    Pieces pb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float f[8];
+      dfrag<BKC, ZN>(st + DA::FL, rb + 32 * b, lk, f);
+      pb[b] = split8(f);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float f[8];
+      dfrag<AK, ZM>(st, ra + 32 * a, lk, f);
+      const Pieces pa = split8(f);
+      row_products<NP>(pa, pb, acc[a]);
+    }
+  }
+
+  // epilogue: lane (li, lk) of MFMA tile (a, b) holds column 32 b + li, rows
+  // 32 a + 8 g + 4 lk + i (g, i < 4) of the wave's 128 x 64 tile
+  const int i0 = m0 + wm * 128 + 4 * lk, j0 = n0 + wn * 64 + li;
+  if (p.partial || !p.accumulate) {
+    float* out = p.partial ? p.C + (size_t)split * p.M * p.N : p.C;
+    const int ldo = p.partial ? p.N : p.ldc;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int j = j0 + 32 * b;
+        if (j >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + 32 * a + 8 * (r / 4) + (r % 4);
+          if (i < p.M) out[(size_t)i * ldo + j] = acc[a][b][r];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int j = j0 + 32 * b;
+        if (j >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + 32 * a + 8 * (r / 4) + (r % 4);
+          if (i < p.M) p.C[(size_t)i * p.ldc + j] += acc[a][b][r];
+        }
+      }
+  }
+}
+
+// operands of the direct-to-LDS layouts: real problems, 16-byte aligned,
+// leading dimensions multiples of four, and a k-major operand a multiple of
+// four wide along its rows (its loads are four-column chunks)
+bool zdma_ok(const GemmBatch& b, bool TA, bool TB) {
+  for (int q = 0; q < b.nprob; ++q) {
+    const GemmProb& p = b.p[q];
+    if (p.M <= 0 || p.N <= 0) continue;
+    if (p.cplx) return false;
+    if ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) % 16) return false;
+    if (p.lda % 4 || p.ldb % 4) return false;
+    if ((TA && p.M % 4) || (!TB && p.N % 4)) return false;
+    if (p.k_splits > 1 && p.k_chunk % 16) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+// float32 products through bfloat16 pieces; hipErrorNotSupported (nothing
+// launched) for operands the direct-to-LDS layouts do not take, complex
+// problems, or A^T.B^T
+int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s) {
+  if ((TA && TB) || (nprod != 6 && nprod != 9) || !zdma_ok(b, TA, TB)) return hipErrorNotSupported;
+  int total = 0;
+  for (int q = 0; q < b.nprob; ++q) {
+    GemmProb& p = b.p[q];
+    p.tiles_m = (p.M + ZM - 1) / ZM;
+    p.tiles_n = (p.N + ZN - 1) / ZN;
+    if (p.k_splits < 1) p.k_splits = 1;
+    if (p.k_splits == 1 && p.k_chunk <= 0) p.k_chunk = p.K;
+    p.tile_begin = total;
+    if (p.M > 0 && p.N > 0) total += p.tiles_m * p.tiles_n * p.k_splits;
+  }
+  b.total_tiles = total;
+  if (total == 0) return hipSuccess;
+  const dim3 grid(total), block(ZNT);
+  if (nprod == 6) {
+    if (!TA && !TB) hipLaunchKernelGGL((gemm_x3_kernel<false, false, 6>), grid, block, 0, s, b);
+    else if (!TA) hipLaunchKernelGGL((gemm_x3_kernel<false, true, 6>), grid, block, 0, s, b);
+    else hipLaunchKernelGGL((gemm_x3_kernel<true, false, 6>), grid, block, 0, s, b);
+  } else {
+    if (!TA && !TB) hipLaunchKernelGGL((gemm_x3_kernel<false, false, 9>), grid, block, 0, s, b);
+    else if (!TA) hipLaunchKernelGGL((gemm_x3_kernel<false, true, 9>), grid, block, 0, s, b);
+    else hipLaunchKernelGGL((gemm_x3_kernel<true, false, 9>), grid, block, 0, s, b);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace so2

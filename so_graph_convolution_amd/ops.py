@@ -11,7 +11,7 @@ import dataclasses
 
 import torch
 
-from ._binding import SO2_DEBUG_CHECKS, Cfg, GraphC, check, lib
+from ._binding import SO2_DEBUG_CHECKS, SO2_F32_NATIVE, Cfg, GraphC, check, lib
 
 __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_fwd_noalloc", "so2conv_bwd",
            "so2conv_dbwd",
@@ -32,7 +32,9 @@ class SO2Config:
     accumulation. debug_checks: validate the inputs on the device before
     computing (the call synchronises and raises on bad inputs). heads: the
     per-edge message weights `env` are [E] (heads = 1: a cutoff envelope) or
-    [E, heads] (attention weights per head of channels/heads channels)."""
+    [E, heads] (attention weights per head of channels/heads channels).
+    f32_native: float32 per-order products on the float32 matrix cores
+    instead of the default exact bfloat16-piece products."""
     lmax: int
     mmax: int
     channels: int
@@ -40,14 +42,15 @@ class SO2Config:
     dtype: str = "f32"
     debug_checks: bool = False
     heads: int = 1
+    f32_native: bool = False
 
     def __post_init__(self):
         if self.dtype not in _DTYPES:
             raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
 
     def c(self) -> Cfg:
-        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0],
-                   SO2_DEBUG_CHECKS if self.debug_checks else 0, self.heads)
+        flags = (SO2_DEBUG_CHECKS if self.debug_checks else 0) | (SO2_F32_NATIVE if self.f32_native else 0)
+        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0], flags, self.heads)
 
     def env_shape(self, n_edges):
         return (n_edges,) if self.heads == 1 else (n_edges, self.heads)
