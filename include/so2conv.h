@@ -298,6 +298,34 @@ int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const 
                  const float* A, const float* gU, const float* px, const float* pW, const float* pA, float* ggU,
                  float* gx2, float* gW2, float* gA2, void* ws, size_t ws_bytes, void* stream);
 
+/* Back-projection from the grid (TrimSO(2) page, Appendix B.4, Forward
+ * computation, the second identity H_l (Y A_out) = (H_l Y) A_out): the grid
+ * values after the nonlinearity return to coefficients,
+ *   Z^(l) = H_l (Y A),  computed as (H_l Y) A,
+ * so the [n_grid x c_out] product Y A is never formed per node. H
+ * [(lmax+1)^2][n_grid] stacks the H_l (degree-l rows), a constant (no
+ * gradient). Uses cfg->lmax, c_h (grid channels), c_out and n_grid; c_in is
+ * not used (it must still be a valid channel count).
+ * Arrays (device, float32, row-major): Y, gY, pY, gY2 [n_nodes][n_grid][c_h];
+ * H [(lmax+1)^2][n_grid]; A, gA, pA, gA2 [c_h][c_out];
+ * Z, gZ, ggZ [n_nodes][(lmax+1)^2][c_out].
+ *   fwd : Z
+ *   bwd : gY = H^T (gZ A^T), gA = sum over nodes (H Y)^T gZ (either may be NULL)
+ *   dbwd: L = <pY, gY> + <pA, gA> (NULL direction = zero):
+ *         ggZ = dL/dgZ = (H pY) A + (H Y) pA, gY2 = dL/dY = H^T (gZ pA^T),
+ *         gA2 = dL/dA = sum over nodes (H pY)^T gZ (outputs may be NULL)
+ * Workspace from so2grid_back_workspace_bytes (stage 0 fwd, 1 bwd, 2 dbwd).
+ * Weight-map gradients sum over nodes in a fixed order (bitwise
+ * reproducible); errors as for so2grid_fwd. */
+size_t so2grid_back_workspace_bytes(const so2grid_cfg* cfg, int32_t n_nodes, int stage);
+int so2grid_back_fwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* Y, const float* H, const float* A,
+                     float* Z, void* ws, size_t ws_bytes, void* stream);
+int so2grid_back_bwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* Y, const float* H, const float* A,
+                     const float* gZ, float* gY, float* gA, void* ws, size_t ws_bytes, void* stream);
+int so2grid_back_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* Y, const float* H, const float* A,
+                      const float* gZ, const float* pY, const float* pA, float* ggZ, float* gY2, float* gA2,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Spherical-grid SwiGLU activation on edges (SwiGLU-S2; TrimSO(2) page,
  * Table 5 and Section 5.1: EquiformerV3's Edge -> Edge activation; Appendix
  * B.4: the degree-l basis evaluated at n_g grid points, the nonlinearity on

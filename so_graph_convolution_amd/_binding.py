@@ -86,6 +86,13 @@ EXPORTS = {
     "so2grid_bwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 9 + [c_sz, c_vp]),
     # (cfg, N, x, G, W, A, gU, px, pW, pA, ggU, gx2, gW2, gA2, ws, ws_bytes, stream)
     "so2grid_dbwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 13 + [c_sz, c_vp]),
+    "so2grid_back_workspace_bytes": (c_sz, [ctypes.POINTER(GridCfg), c_i32, ctypes.c_int]),
+    # (cfg, N, Y, H, A, Z, ws, ws_bytes, stream)
+    "so2grid_back_fwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 5 + [c_sz, c_vp]),
+    # (cfg, N, Y, H, A, gZ, gY, gA, ws, ws_bytes, stream)
+    "so2grid_back_bwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 7 + [c_sz, c_vp]),
+    # (cfg, N, Y, H, A, gZ, pY, pA, ggZ, gY2, gA2, ws, ws_bytes, stream)
+    "so2grid_back_dbwd": (ctypes.c_int, [ctypes.POINTER(GridCfg), c_i32] + [c_vp] * 10 + [c_sz, c_vp]),
     # (cfg, E, U, G, P, Z, stream)
     "so2s2_fwd": (ctypes.c_int, [ctypes.POINTER(S2Cfg), c_i64] + [c_vp] * 5),
     # (cfg, E, U, G, P, gZ, gU, stream)

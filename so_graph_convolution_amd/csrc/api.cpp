@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/so2conv.h"
+#include "api_common.hpp"
 #include "gemm.hpp"
 #include "ops.hpp"
 #include "wigner.hpp"
@@ -20,23 +21,23 @@ int upload_generators_dual(const float* host);
 
 using namespace so2;
 
-namespace {
+namespace so2 {
 
+namespace {
 thread_local std::string g_err;
+}  // namespace
 
 int fail(int code, const std::string& msg) {
   g_err = msg;
   return code;
 }
+void clear_error() { g_err.clear(); }
+const char* last_error() { return g_err.c_str(); }
+int set_error(int code, const std::string& msg) { return fail(code, msg); }
 
-#define SO2_HIP(expr)                                                                       \
-  do {                                                                                      \
-    int _e = (int)(expr);                                                                   \
-    if (_e != 0) return fail(SO2_EHIP, std::string("HIP error in ") + #expr + ": " +       \
-                                           hipGetErrorString((hipError_t)_e));              \
-  } while (0)
+}  // namespace so2
 
-inline size_t al(size_t v) { return (v + 255) & ~size_t(255); }
+namespace {
 
 // ---------------------------------------------------------------- generators
 // G_k^(l) = d/dt D^(l)(exp(t [e_k]_x)) at t = 0, evaluated exactly by a
@@ -234,19 +235,6 @@ int debug_validate(const Ctx& c, const GraphDev& g, const float* pos, const floa
 }
 
 // ---------------------------------------------------------------- layouts
-// Bump allocator over the caller's workspace. With a null base it only
-// measures: every stage lays out its buffers through one function, used both
-// to size the workspace and to carve it.
-struct Arena {
-  char* base;
-  size_t used;
-  void* bytes(size_t n) {
-    void* p = base ? base + used : nullptr;
-    used += al(n);
-    return p;
-  }
-  float* take(size_t floats) { return static_cast<float*>(bytes(sizeof(float) * floats)); }
-};
 
 struct SavedLayout {
   size_t S, T, U, Z, V, total;
@@ -296,8 +284,10 @@ BwdRows bwd_rows(const Ctx& c, const void* sb, long E, long e0) {
           reinterpret_cast<float*>(b + L.T) + (size_t)e0 * c.d.wT()};
 }
 
+}  // namespace
+
 // K chunk of split-K weight-gradient products over edges (a multiple of the GEMM K tile)
-void split_plan(long K, int* splits, int* chunk) {
+void so2::split_plan(long K, int* splits, int* chunk) {
   long c = 4096;
   long s = (K + c - 1) / c;
   if (s > 256) {
@@ -308,6 +298,8 @@ void split_plan(long K, int* splits, int* chunk) {
   *splits = (int)s;
   *chunk = (int)c;
 }
+
+namespace {
 
 // realified weights of one linear as GEMM B operands: W [rows][cols] and, for
 // bfloat16, its transpose (the forward product A.W runs as A.(W^T)^T)
@@ -590,7 +582,9 @@ long pick_chunk(const Ctx& c, int N, long E, int stage, bool recompute, size_t w
 }
 
 // ---------------------------------------------------------------- gemm helpers
-GemmProb prob(const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N, int K, int acc = 0) {
+}  // namespace
+
+GemmProb so2::prob(const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N, int K, int acc) {
   GemmProb p{};
   p.A = A; p.B = B; p.C = C;
   p.M = M; p.N = N; p.K = K;
@@ -598,6 +592,8 @@ GemmProb prob(const void* A, int lda, const void* B, int ldb, float* C, int ldc,
   p.k_splits = 1; p.k_chunk = K; p.accumulate = acc;
   return p;
 }
+
+namespace {
 
 const void* offs(const void* p, size_t elems, int es) { return static_cast<const char*>(p) + elems * es; }
 void* offs(void* p, size_t elems, int es) { return static_cast<char*>(p) + elems * es; }
@@ -617,13 +613,11 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 
-// Operand kinds of run_batch: float32 on the float32 matrix cores, bfloat16,
-// or float32 through bfloat16 pieces (gemm_x3_run; problems it does not take
-// run on the float32 matrix cores).
-enum { kOpF32 = 0, kOpBF16 = 1, kOpSplit = 2 };
-constexpr int kSplitProducts = 6;
+constexpr int kSplitProducts = 6;   // bf16 piece products per float32 product of the split GEMMs
 
-int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s) {
+}  // namespace
+
+int so2::run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s) {
   if (ps.empty()) return SO2_OK;
   const bool bf = op == kOpBF16;
   const double es = bf ? 2.0 : 4.0;
@@ -669,17 +663,8 @@ int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s
   return SO2_OK;
 }
 
-// Weight gradient G[M][N] (+)= sum over segments of A_s^T B_s, A_s [K_s][lda], B_s [K_s][ldb];
-// deterministic split-K through the partial buffer P.
-struct TnSeg {
-  const void* A;
-  int lda;
-  const void* B;
-  int ldb;
-  long K;
-};
-int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int accumulate, float* P, int bf,
-           hipStream_t s) {
+int so2::run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int accumulate, float* P, int bf,
+                hipStream_t s) {
   std::vector<GemmProb> ps;
   int total_splits = 0;
   // a thin side of at most 64 (the radial map's n_rbf rows) becomes the
@@ -707,13 +692,16 @@ int run_tn(const TnSeg* segs, int nseg, int M, int N, float* G, int ldg, int acc
   return SO2_OK;
 }
 
+namespace {
 __global__ void fill_kernel(float* p, size_t n, float v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 __global__ void fill16_kernel(unsigned short* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
-int fill(float* p, size_t n, hipStream_t s) {
+}  // namespace
+
+int so2::fill(float* p, size_t n, hipStream_t s) {
   if (n == 0) return SO2_OK;
   size_t b = (n + 255) / 256;
   if (b > 16384) b = 16384;
@@ -721,6 +709,8 @@ int fill(float* p, size_t n, hipStream_t s) {
   SO2_HIP(hipGetLastError());
   return SO2_OK;
 }
+
+namespace {
 // zero n elements of the boundary type
 int zero(const Ctx& c, void* p, size_t n, hipStream_t s) {
   if (!c.bf) return fill(static_cast<float*>(p), n, s);
@@ -1110,144 +1100,6 @@ int zero_grads(const Ctx& c, int N, void* gx, float* gpos, void* gw_rad, void* c
   return SO2_OK;
 }
 
-// ---------------------------------------------------------------- spherical projection
-struct GridCtx {
-  int L, Cin, Ch, Cout, ng, N;
-  int d() const { return (L + 1) * (L + 1); }
-};
-
-int check_grid(const so2grid_cfg* cfg, int32_t N, GridCtx* g) {
-  if (!cfg) return fail(SO2_EINVAL, "cfg is NULL");
-  if (cfg->lmax < 0 || cfg->lmax > kMaxL) return fail(SO2_EUNSUPPORTED, "lmax must be in [0, 6]");
-  for (int c : {cfg->c_in, cfg->c_h, cfg->c_out})
-    if (c < 4 || c > 1024 || c % 4) return fail(SO2_EUNSUPPORTED, "channel counts must be multiples of 4 in [4, 1024]");
-  if (cfg->n_grid < 1 || cfg->n_grid > 65536) return fail(SO2_EUNSUPPORTED, "n_grid must be in [1, 65536]");
-  if (cfg->dtype != SO2_F32) return fail(SO2_EUNSUPPORTED, "the spherical projection is float32 only");
-  if (cfg->flags) return fail(SO2_EINVAL, "unknown cfg flags");
-  if (N < 0) return fail(SO2_EINVAL, "negative node count");
-  *g = GridCtx{cfg->lmax, cfg->c_in, cfg->c_h, cfg->c_out, cfg->n_grid, N};
-  return SO2_OK;
-}
-
-// per-(l, m) row problems over all nodes: C[:, j] (+)= op(A[:, j]) with the
-// channel map of degree l; rows are node rows j = l^2 + m of [N][d][.]
-int grid_rows(const GridCtx& g, const float* A, int wa, const float* Bm, int ldb, bool tb, float* C, int wc,
-              int K, int Nn, int acc, hipStream_t s) {
-  std::vector<GemmProb> ps;
-  for (int l = 0; l <= g.L; ++l)
-    for (int m = 0; m < 2 * l + 1; ++m) {
-      const int j = l * l + m;
-      ps.push_back(prob(A + (size_t)j * wa, g.d() * wa, Bm + (size_t)l * (tb ? Nn : K) * ldb, ldb,
-                        C + (size_t)j * wc, g.d() * wc, g.N, Nn, K, acc));
-    }
-  return run_batch(ps, false, tb, 0, s);
-}
-
-// split of the node dimension of the weight-gradient products: about 16
-// splits (so that all (l, m) products together fill the GPU), 256..4096 rows
-void grid_split(long N, int* splits, int* chunk) {
-  long c = ((N + 15) / 16 + kGemmKTile - 1) / kGemmKTile * kGemmKTile;
-  c = c < 256 ? 256 : (c > 4096 ? 4096 : c);
-  long s = (N + c - 1) / c;
-  *splits = (int)(s < 1 ? 1 : s);
-  *chunk = (int)c;
-}
-
-// Gm_l (+)= sum_m X[:, l^2+m]^T Z[:, l^2+m]  (Gm: [L+1][wx][wz]): every (l, m)
-// product in one grouped launch, split over nodes into partials, then one
-// fixed-order reduction per degree
-int grid_wgrad(const GridCtx& g, const float* X, int wx, const float* Z, int wz, float* Gm, int acc, float* P,
-               hipStream_t s) {
-  if (g.N == 0) return SO2_OK;
-  int sp, ch;
-  grid_split(g.N, &sp, &ch);
-  std::vector<GemmProb> ps;
-  size_t off = 0;
-  for (int j = 0; j < g.d(); ++j) {
-    GemmProb p = prob(X + (size_t)j * wx, g.d() * wx, Z + (size_t)j * wz, g.d() * wz, P + off, wz, wx, wz, g.N);
-    p.k_splits = sp;
-    p.k_chunk = ch;
-    p.partial = 1;
-    ps.push_back(p);
-    off += (size_t)sp * wx * wz;
-  }
-  int r = run_batch(ps, true, false, 0, s);
-  if (r) return r;
-  off = 0;
-  for (int l = 0; l <= g.L; ++l) {
-    const int n = (2 * l + 1) * sp;
-    SO2_HIP(gemm_reduce(P + off, n, wx, wz, Gm + (size_t)l * wx * wz, wz, acc, s));
-    off += (size_t)n * wx * wz;
-  }
-  return SO2_OK;
-}
-
-// partials: every (l, m) product's splits at once, or the channel-map products
-// (L+1 segments of one split each)
-size_t grid_partials(const GridCtx& g) {
-  int sp, ch;
-  grid_split(g.N, &sp, &ch);
-  const int mx = std::max(std::max(g.Cin, g.Ch), g.Cout);
-  return (size_t)std::max(g.d() * sp, g.L + 1) * mx * mx;
-}
-
-struct GridWs {
-  float *B, *pB, *Y, *Z, *gB, *gB2, *P;
-};
-void layout_grid(Arena& ar, const GridCtx& g, int stage, GridWs* w) {
-  const size_t bsz = (size_t)(g.L + 1) * g.Cin * g.Cout, nf = (size_t)g.N * g.d() * g.Cout;
-  *w = GridWs{};
-  w->B = ar.take(bsz);
-  if (stage == 0) {
-    w->Y = ar.take(nf);
-    return;
-  }
-  w->Z = ar.take(nf);
-  w->gB = ar.take(bsz);
-  if (stage == 2) {
-    w->pB = ar.take(bsz);
-    w->Y = ar.take(nf);
-    w->gB2 = ar.take(bsz);
-  }
-  w->P = ar.take(grid_partials(g));
-}
-
-size_t grid_ws_need(const GridCtx& g, int stage) {
-  Arena ar{nullptr, 0};
-  GridWs w;
-  layout_grid(ar, g, stage, &w);
-  return ar.used + 4096;
-}
-
-// B_l = W_l A (or += )
-int grid_channel_map(const GridCtx& g, const float* W, const float* A, float* B, int acc, hipStream_t s) {
-  std::vector<GemmProb> ps;
-  for (int l = 0; l <= g.L; ++l)
-    ps.push_back(prob(W + (size_t)l * g.Cin * g.Ch, g.Ch, A, g.Cout, B + (size_t)l * g.Cin * g.Cout, g.Cout, g.Cin,
-                      g.Cout, g.Ch, acc));
-  return run_batch(ps, false, false, 0, s);
-}
-
-// gW_l (+)= Gm_l A^T   and   gA (+)= sum_l W_l^T Gm_l
-int grid_map_grads(const GridCtx& g, const float* Gm, const float* W, const float* A, float* gW, float* gA, int acc,
-                   float* P, hipStream_t s) {
-  int r;
-  if (gW) {
-    std::vector<GemmProb> ps;
-    for (int l = 0; l <= g.L; ++l)
-      ps.push_back(prob(Gm + (size_t)l * g.Cin * g.Cout, g.Cout, A, g.Cout, gW + (size_t)l * g.Cin * g.Ch, g.Ch, g.Cin,
-                        g.Ch, g.Cout, acc));
-    if ((r = run_batch(ps, false, true, 0, s))) return r;
-  }
-  if (gA) {
-    std::vector<TnSeg> segs;
-    for (int l = 0; l <= g.L; ++l)
-      segs.push_back(TnSeg{W + (size_t)l * g.Cin * g.Ch, g.Ch, Gm + (size_t)l * g.Cin * g.Cout, g.Cout, g.Cin});
-    if ((r = run_tn(segs.data(), (int)segs.size(), g.Ch, g.Cout, gA, g.Cout, acc, P, 0, s))) return r;
-  }
-  return SO2_OK;
-}
-
 // forward of the plain operator (mx == NULL) or of the mixture of experts
 // (w1, w2: expert stacks)
 int conv_fwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, const float* pos, const float* rbf,
@@ -1600,7 +1452,7 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
 // =====================================================================================
 extern "C" {
 
-const char* so2conv_last_error(void) { return g_err.c_str(); }
+const char* so2conv_last_error(void) { return last_error(); }
 
 int so2conv_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -1642,7 +1494,7 @@ int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* 
 int so2conv_supported(int32_t lmax, int32_t mmax) { return lm_supported(lmax, mmax) ? 1 : 0; }
 
 int so2conv_debug_status(void* stream) {
-  g_err.clear();
+  clear_error();
   SO2_HIP(hipStreamSynchronize((hipStream_t)stream));
   unsigned w = 0, zero = 0;
   SO2_HIP(hipMemcpyFromSymbol(&w, HIP_SYMBOL(g_debug_word), sizeof(w)));
@@ -1656,7 +1508,7 @@ size_t so2conv_graph_workspace_bytes(int32_t n_nodes, int64_t n_edges) { return 
 int so2conv_graph_prepare(int32_t n_nodes, int64_t n_edges, const int32_t* src, const int32_t* dst, int32_t* dst_ptr,
                           int32_t* src_perm, int32_t* src_ptr, int32_t* err_word, void* ws, size_t ws_bytes,
                           void* stream) {
-  g_err.clear();
+  clear_error();
   if (n_nodes < 0 || n_edges < 0) return fail(SO2_EINVAL, "negative graph size");
   if (n_edges > 0x3fffffffLL) return fail(SO2_EUNSUPPORTED, "too many edges");
   if (n_edges > 0 && (!src || !dst || !src_perm)) return fail(SO2_EINVAL, "NULL edge arrays");
@@ -1696,7 +1548,7 @@ size_t so2conv_chunked_workspace_bytes(const so2conv_cfg* cfg, int32_t n_nodes, 
 int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos,
                                 const float* rbf, const void* w_rad, void* T_out, void* ws, size_t ws_bytes,
                                 void* stream) {
-  g_err.clear();
+  clear_error();
   Ctx c;
   GraphDev gd;
   int r;
@@ -1726,7 +1578,7 @@ int so2conv_debug_rotate_gather(const so2conv_cfg* cfg, const so2conv_graph* g, 
 int so2conv_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, const float* pos, const float* rbf,
                 const float* env, const void* w_rad, const void* const* w1, const void* const* w2, void* y,
                 void* saved, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+  clear_error();
   Ctx c;
   GraphDev gd;
   int r;
@@ -1738,7 +1590,7 @@ int so2conv_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, c
                 const float* env, const void* w_rad, const void* const* w1, const void* const* w2, const void* saved,
                 const void* gy, void* gx, float* gpos, float* grbf, float* genv, void* gw_rad, void* const* gw1,
                 void* const* gw2, float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+  clear_error();
   Ctx c;
   GraphDev gd;
   int r;
@@ -1753,7 +1605,7 @@ int so2conv_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const void* x, 
                  const float* penv, const void* pw_rad, const void* const* pw1, const void* const* pw2, void* ggy,
                  void* gx2, float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1_2,
                  void* const* gw2_2, const void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+  clear_error();
   Ctx c;
   GraphDev gd;
   int r;
@@ -1828,7 +1680,7 @@ int so2mole_fwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cf
                 const float* pos, const float* rbf, const float* env, const void* w_rad, const void* const* w1e,
                 const void* const* w2e, const float* coef, void* y, void* saved, void* ws, size_t ws_bytes,
                 void* stream) {
-  g_err.clear();
+  clear_error();
   Ctx c;
   GraphDev gd;
   MixIn mx;
@@ -1842,7 +1694,7 @@ int so2mole_bwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_cf
                 const void* const* w2e, const float* coef, const void* saved, const void* gy, void* gx, float* gpos,
                 float* grbf, float* genv, void* gw_rad, void* const* gw1e, void* const* gw2e, float* gcoef,
                 float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+  clear_error();
   Ctx c;
   GraphDev gd;
   MixIn mx;
@@ -1865,7 +1717,7 @@ int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_c
                  const void* const* pw1e, const void* const* pw2e, const float* pcoef, void* ggy, void* gx2,
                  float* gpos2, float* grbf2, float* genv2, void* gw_rad2, void* const* gw1e_2, void* const* gw2e_2,
                  float* gcoef2, const void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+  clear_error();
   Ctx c;
   GraphDev gd;
   MixIn mx;
@@ -1881,131 +1733,6 @@ int so2mole_dbwd(const so2conv_cfg* cfg, const so2conv_graph* g, const so2mole_c
   return conv_dbwd(c, gd, &mx, x, pos, rbf, env, w_rad, w1e, w2e, saved, gy, px, ppos, pedge, prbf, penv, pw_rad,
                    pw1e, pw2e, pcoef, ggy, gx2, gpos2, grbf2, genv2, gw_rad2, gw1e_2, gw2e_2, gcoef2, saved_bwd, ws,
                    ws_bytes, stream);
-}
-
-// ---------------------------------------------------------------- spherical projection entry points
-size_t so2grid_workspace_bytes(const so2grid_cfg* cfg, int32_t n_nodes, int stage) {
-  GridCtx g;
-  if (check_grid(cfg, n_nodes, &g) || stage < 0 || stage > 2) return 0;
-  return grid_ws_need(g, stage);
-}
-
-int so2grid_fwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
-                const float* A, float* U, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
-  GridCtx g;
-  int r;
-  if ((r = check_grid(cfg, n_nodes, &g))) return r;
-  if (!G || !W || !A || (g.N > 0 && (!x || !U))) return fail(SO2_EINVAL, "NULL input or output");
-  if (g.N == 0) return SO2_OK;
-  if (!ws || ws_bytes < grid_ws_need(g, 0)) return fail(SO2_EWORKSPACE, "workspace too small");
-  hipStream_t s = (hipStream_t)stream;
-  Arena ar{static_cast<char*>(ws), 0};
-  GridWs w;
-  layout_grid(ar, g, 0, &w);
-  if ((r = grid_channel_map(g, W, A, w.B, 0, s))) return r;                          // B_l = W_l A
-  if ((r = grid_rows(g, x, g.Cin, w.B, g.Cout, false, w.Y, g.Cout, g.Cin, g.Cout, 0, s))) return r;   // Y = X B
-  SO2_HIP(launch_grid_apply(g.L, g.N, g.ng, g.Cout, G, w.Y, U, s));                 // U = G Y
-  return SO2_OK;
-}
-
-int so2grid_bwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
-                const float* A, const float* gU, float* gx, float* gW, float* gA, void* ws, size_t ws_bytes,
-                void* stream) {
-  g_err.clear();
-  GridCtx g;
-  int r;
-  if ((r = check_grid(cfg, n_nodes, &g))) return r;
-  if (!G || !W || !A || (g.N > 0 && (!x || !gU))) return fail(SO2_EINVAL, "NULL input");
-  hipStream_t s = (hipStream_t)stream;
-  if (g.N == 0) {   // no nodes: zero weight gradients
-    if (gW && (r = fill(gW, (size_t)(g.L + 1) * g.Cin * g.Ch, s))) return r;
-    if (gA && (r = fill(gA, (size_t)g.Ch * g.Cout, s))) return r;
-    return SO2_OK;
-  }
-  if (!ws || ws_bytes < grid_ws_need(g, 1)) return fail(SO2_EWORKSPACE, "workspace too small");
-  Arena ar{static_cast<char*>(ws), 0};
-  GridWs w;
-  layout_grid(ar, g, 1, &w);
-  if ((r = grid_channel_map(g, W, A, w.B, 0, s))) return r;
-  SO2_HIP(launch_grid_apply_t(g.L, g.N, g.ng, g.Cout, G, gU, w.Z, s));              // Z = G^T gU
-  if (gx && (r = grid_rows(g, w.Z, g.Cout, w.B, g.Cout, true, gx, g.Cin, g.Cout, g.Cin, 0, s))) return r;  // Z B^T
-  if (gW || gA) {
-    if ((r = grid_wgrad(g, x, g.Cin, w.Z, g.Cout, w.gB, 0, w.P, s))) return r;      // Bbar_l = X^T Z
-    if ((r = grid_map_grads(g, w.gB, W, A, gW, gA, 0, w.P, s))) return r;
-  }
-  return SO2_OK;
-}
-
-int so2grid_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* x, const float* G, const float* W,
-                 const float* A, const float* gU, const float* px, const float* pW, const float* pA, float* ggU,
-                 float* gx2, float* gW2, float* gA2, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
-  GridCtx g;
-  int r;
-  if ((r = check_grid(cfg, n_nodes, &g))) return r;
-  if (!G || !W || !A || (g.N > 0 && (!x || !gU))) return fail(SO2_EINVAL, "NULL input");
-  hipStream_t s = (hipStream_t)stream;
-  if (g.N == 0) {
-    if (gW2 && (r = fill(gW2, (size_t)(g.L + 1) * g.Cin * g.Ch, s))) return r;
-    if (gA2 && (r = fill(gA2, (size_t)g.Ch * g.Cout, s))) return r;
-    return SO2_OK;
-  }
-  if (!ws || ws_bytes < grid_ws_need(g, 2)) return fail(SO2_EWORKSPACE, "workspace too small");
-  Arena ar{static_cast<char*>(ws), 0};
-  GridWs w;
-  layout_grid(ar, g, 2, &w);
-  const size_t nf = (size_t)g.N * g.d();
-  const bool has_pB = pW || pA;
-  if ((r = grid_channel_map(g, W, A, w.B, 0, s))) return r;
-  if (pW && (r = grid_channel_map(g, pW, A, w.pB, 0, s))) return r;                 // pB = pW A + W pA
-  if (pA && (r = grid_channel_map(g, W, pA, w.pB, pW ? 1 : 0, s))) return r;
-  SO2_HIP(launch_grid_apply_t(g.L, g.N, g.ng, g.Cout, G, gU, w.Z, s));              // Z = G^T gU
-  // dL/dgU = G (px B + x pB)
-  if (ggU) {
-    if (!px && !has_pB) {
-      if ((r = fill(ggU, (size_t)g.N * g.ng * g.Cout, s))) return r;
-    } else {
-      if (px && (r = grid_rows(g, px, g.Cin, w.B, g.Cout, false, w.Y, g.Cout, g.Cin, g.Cout, 0, s))) return r;
-      if (has_pB && (r = grid_rows(g, x, g.Cin, w.pB, g.Cout, false, w.Y, g.Cout, g.Cin, g.Cout, px ? 1 : 0, s)))
-        return r;
-      SO2_HIP(launch_grid_apply(g.L, g.N, g.ng, g.Cout, G, w.Y, ggU, s));
-    }
-  }
-  // dL/dx = Z pB^T
-  if (gx2) {
-    if (has_pB) {
-      if ((r = grid_rows(g, w.Z, g.Cout, w.pB, g.Cout, true, gx2, g.Cin, g.Cout, g.Cin, 0, s))) return r;
-    } else if ((r = fill(gx2, nf * g.Cin, s))) {
-      return r;
-    }
-  }
-  // dL/dW = (px^T Z) A^T + Bbar pA^T ; dL/dA = sum W^T (px^T Z) + sum pW^T Bbar
-  if (gW2 || gA2) {
-    if (gW2 && (r = fill(gW2, (size_t)(g.L + 1) * g.Cin * g.Ch, s))) return r;
-    if (gA2 && (r = fill(gA2, (size_t)g.Ch * g.Cout, s))) return r;
-    if (px) {
-      if ((r = grid_wgrad(g, px, g.Cin, w.Z, g.Cout, w.gB2, 0, w.P, s))) return r;
-      if ((r = grid_map_grads(g, w.gB2, W, A, gW2, gA2, 1, w.P, s))) return r;
-    }
-    if (has_pB) {
-      if ((r = grid_wgrad(g, x, g.Cin, w.Z, g.Cout, w.gB, 0, w.P, s))) return r;   // Bbar
-      if (pA && gW2) {   // gW2_l += Bbar_l pA^T
-        std::vector<GemmProb> ps;
-        for (int l = 0; l <= g.L; ++l)
-          ps.push_back(prob(w.gB + (size_t)l * g.Cin * g.Cout, g.Cout, pA, g.Cout, gW2 + (size_t)l * g.Cin * g.Ch,
-                            g.Ch, g.Cin, g.Ch, g.Cout, 1));
-        if ((r = run_batch(ps, false, true, 0, s))) return r;
-      }
-      if (pW && gA2) {   // gA2 += sum_l pW_l^T Bbar_l
-        std::vector<TnSeg> segs;
-        for (int l = 0; l <= g.L; ++l)
-          segs.push_back(TnSeg{pW + (size_t)l * g.Cin * g.Ch, g.Ch, w.gB + (size_t)l * g.Cin * g.Cout, g.Cout, g.Cin});
-        if ((r = run_tn(segs.data(), (int)segs.size(), g.Ch, g.Cout, gA2, g.Cout, 1, w.P, 0, s))) return r;
-      }
-    }
-  }
-  return SO2_OK;
 }
 
 }  // extern "C"
@@ -2030,7 +1757,7 @@ extern "C" {
 
 int so2s2_fwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P, float* Z,
               void* stream) {
-  g_err.clear();
+  clear_error();
   int r;
   if ((r = check_s2(cfg, n_edges))) return r;
   if (n_edges == 0) return SO2_OK;
@@ -2041,7 +1768,7 @@ int so2s2_fwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float
 
 int so2s2_bwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P,
               const float* gZ, float* gU, void* stream) {
-  g_err.clear();
+  clear_error();
   int r;
   if ((r = check_s2(cfg, n_edges))) return r;
   if (n_edges == 0) return SO2_OK;
@@ -2052,7 +1779,7 @@ int so2s2_bwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float
 
 int so2s2_dbwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float* G, const float* P,
                const float* gZ, const float* pU, float* ggZ, float* gU2, void* stream) {
-  g_err.clear();
+  clear_error();
   int r;
   if ((r = check_s2(cfg, n_edges))) return r;
   if (n_edges == 0) return SO2_OK;
@@ -2065,7 +1792,3 @@ int so2s2_dbwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const floa
 
 }  // extern "C"
 
-namespace so2 {
-// error message of the library's other translation units (read by so2conv_last_error)
-int set_error(int code, const std::string& msg) { return fail(code, msg); }
-}  // namespace so2

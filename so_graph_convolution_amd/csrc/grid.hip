@@ -2,9 +2,11 @@
 // activations): per node, U = G Y with G the n_g x (L+1)^2 basis-at-grid
 // matrix and Y = [X^(l) B_l]_l the node's coefficient rows after the fused
 // channel map; and the transposed application Z = G^T Ubar of the backward.
-// Both stream one node array in and one out (HBM-bound); G is staged in LDS
-// 32 grid rows at a time and read as a broadcast, one thread per channel,
-// several nodes per block.
+// The back-projection from the grid applies H ((L+1)^2 x n_g) the same way,
+// given as the transposed basis (BT: element (g, j) at j * n_g + g).
+// Both stream one node array in and one out (HBM-bound); the basis is staged
+// in LDS 32 grid rows at a time and read as a broadcast, one thread per
+// channel, several nodes per block.
 #include "ops.hpp"
 
 namespace so2 {
@@ -13,7 +15,14 @@ namespace {
 
 constexpr int kGridRows = 32;
 
-template <int D>
+// 32 grid rows of the basis from row g0 (gn rows) into sG [gn][D]
+template <int D, bool BT>
+__device__ inline void stage_basis(float* sG, const float* __restrict__ G, int ng, int g0, int gn) {
+  for (int idx = threadIdx.x; idx < gn * D; idx += blockDim.x)
+    sG[idx] = BT ? G[(size_t)(idx % D) * ng + g0 + idx / D] : G[(size_t)g0 * D + idx];
+}
+
+template <int D, bool BT>
 __global__ __launch_bounds__(1024) void grid_apply_kernel(int N, int ng, int C, const float* __restrict__ G,
                                                           const float* __restrict__ Y, float* __restrict__ U) {
   __shared__ float sG[kGridRows * D];
@@ -27,7 +36,7 @@ __global__ __launch_bounds__(1024) void grid_apply_kernel(int N, int ng, int C, 
   for (int g0 = 0; g0 < ng; g0 += kGridRows) {
     const int gn = min(kGridRows, ng - g0);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < gn * D; idx += blockDim.x) sG[idx] = G[(size_t)g0 * D + idx];
+    stage_basis<D, BT>(sG, G, ng, g0, gn);
     __syncthreads();
     if (act) {
       float* u = U + ((size_t)node * ng + g0) * C + c;
@@ -41,7 +50,7 @@ __global__ __launch_bounds__(1024) void grid_apply_kernel(int N, int ng, int C, 
   }
 }
 
-template <int D>
+template <int D, bool BT>
 __global__ __launch_bounds__(1024) void grid_apply_t_kernel(int N, int ng, int C, const float* __restrict__ G,
                                                             const float* __restrict__ U, float* __restrict__ Z) {
   __shared__ float sG[kGridRows * D];
@@ -55,7 +64,7 @@ __global__ __launch_bounds__(1024) void grid_apply_t_kernel(int N, int ng, int C
   for (int g0 = 0; g0 < ng; g0 += kGridRows) {
     const int gn = min(kGridRows, ng - g0);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < gn * D; idx += blockDim.x) sG[idx] = G[(size_t)g0 * D + idx];
+    stage_basis<D, BT>(sG, G, ng, g0, gn);
     __syncthreads();
     if (act) {
       const float* u = U + ((size_t)node * ng + g0) * C + c;
@@ -72,40 +81,43 @@ __global__ __launch_bounds__(1024) void grid_apply_t_kernel(int N, int ng, int C
   }
 }
 
-template <int D, bool T>
+template <int D, bool T, bool BT>
 int grid_launch_d(int N, int ng, int C, const float* G, const float* in, float* out, hipStream_t s) {
   if (N == 0) return hipSuccess;
   const int CP = ((C + 63) / 64) * 64, npb = CP >= 256 ? 1 : 256 / CP;
   const long blocks = ((long)N + npb - 1) / npb;
   if (T)
-    hipLaunchKernelGGL((grid_apply_t_kernel<D>), dim3((unsigned)blocks), dim3(CP * npb), 0, s, N, ng, C, G, in, out);
+    hipLaunchKernelGGL((grid_apply_t_kernel<D, BT>), dim3((unsigned)blocks), dim3(CP * npb), 0, s, N, ng, C, G, in,
+                       out);
   else
-    hipLaunchKernelGGL((grid_apply_kernel<D>), dim3((unsigned)blocks), dim3(CP * npb), 0, s, N, ng, C, G, in, out);
+    hipLaunchKernelGGL((grid_apply_kernel<D, BT>), dim3((unsigned)blocks), dim3(CP * npb), 0, s, N, ng, C, G, in, out);
   return hipGetLastError();
 }
 
-template <bool T>
+template <bool T, bool BT>
 int grid_launch(int L, int N, int ng, int C, const float* G, const float* in, float* out, hipStream_t s) {
   switch (L) {
-    case 0: return grid_launch_d<1, T>(N, ng, C, G, in, out, s);
-    case 1: return grid_launch_d<4, T>(N, ng, C, G, in, out, s);
-    case 2: return grid_launch_d<9, T>(N, ng, C, G, in, out, s);
-    case 3: return grid_launch_d<16, T>(N, ng, C, G, in, out, s);
-    case 4: return grid_launch_d<25, T>(N, ng, C, G, in, out, s);
-    case 5: return grid_launch_d<36, T>(N, ng, C, G, in, out, s);
-    case 6: return grid_launch_d<49, T>(N, ng, C, G, in, out, s);
+    case 0: return grid_launch_d<1, T, BT>(N, ng, C, G, in, out, s);
+    case 1: return grid_launch_d<4, T, BT>(N, ng, C, G, in, out, s);
+    case 2: return grid_launch_d<9, T, BT>(N, ng, C, G, in, out, s);
+    case 3: return grid_launch_d<16, T, BT>(N, ng, C, G, in, out, s);
+    case 4: return grid_launch_d<25, T, BT>(N, ng, C, G, in, out, s);
+    case 5: return grid_launch_d<36, T, BT>(N, ng, C, G, in, out, s);
+    case 6: return grid_launch_d<49, T, BT>(N, ng, C, G, in, out, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int launch_grid_apply(int L, int N, int ng, int C, const float* G, const float* Y, float* U, hipStream_t s) {
-  return grid_launch<false>(L, N, ng, C, G, Y, U, s);
+int launch_grid_apply(int L, int N, int ng, int C, const float* G, const float* Y, float* U, hipStream_t s,
+                      int basis_t) {
+  return basis_t ? grid_launch<false, true>(L, N, ng, C, G, Y, U, s) : grid_launch<false, false>(L, N, ng, C, G, Y, U, s);
 }
 
-int launch_grid_apply_t(int L, int N, int ng, int C, const float* G, const float* U, float* Z, hipStream_t s) {
-  return grid_launch<true>(L, N, ng, C, G, U, Z, s);
+int launch_grid_apply_t(int L, int N, int ng, int C, const float* G, const float* U, float* Z, hipStream_t s,
+                        int basis_t) {
+  return basis_t ? grid_launch<true, true>(L, N, ng, C, G, U, Z, s) : grid_launch<true, false>(L, N, ng, C, G, U, Z, s);
 }
 
 }  // namespace so2

@@ -110,8 +110,12 @@ long realified_size(const Dims& d, int second);
 
 // ---- node-to-node spherical projection: per node U = G Y (G: [ng][(L+1)^2]; Y, Z: [N][(L+1)^2][C];
 // U: [N][ng][C]) and Z = G^T U
-int launch_grid_apply(int L, int N, int ng, int C, const float* G, const float* Y, float* U, hipStream_t s);
-int launch_grid_apply_t(int L, int N, int ng, int C, const float* G, const float* U, float* Z, hipStream_t s);
+// U = G Y per node (G [ng][d]; basis_t: G given as [d][ng])
+int launch_grid_apply(int L, int N, int ng, int C, const float* G, const float* Y, float* U, hipStream_t s,
+                      int basis_t = 0);
+// Z = G^T U per node (G [ng][d]; basis_t: G given as [d][ng], so Z = H U for H = G^T)
+int launch_grid_apply_t(int L, int N, int ng, int C, const float* G, const float* U, float* Z, hipStream_t s,
+                        int basis_t = 0);
 // spherical-grid SwiGLU activation on edges (s2act.hip)
 int launch_s2_fwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, float* Z,
                   hipStream_t s);

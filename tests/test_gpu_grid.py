@@ -85,3 +85,43 @@ def test_grid_no_nodes():
     torch.cuda.synchronize()
     assert U.shape == (0, 10, 8)
     assert not bool(bw["gW"].any()) and not bool(bw["gA"].any())
+
+
+BACK_CASES = [  # (name, lmax, c_h, c_out, n_grid, n_nodes)
+    ("back_l2_small_ragged", 2, 32, 16, 18, 37),
+    ("back_l4_eqv3_widths", 4, 512, 128, 100, 301),
+    ("back_l6_ragged", 6, 64, 48, 200, 75),
+    ("back_l0_tiny", 0, 8, 4, 1, 5),
+]
+
+
+@pytest.mark.parametrize("name,L,ch,co,ng,N", BACK_CASES, ids=[c[0] for c in BACK_CASES])
+def test_grid_back_projection_matches_oracle(name, L, ch, co, ng, N):
+    """Z^(l) = H_l (Y A) (Appendix B.4, the second identity), its backward and
+    double backward through the C ABI against the oracle's definition order."""
+    import so_graph_convolution_amd as K
+    cfg = K.GridConfig(L, 4, ch, co, ng)
+    rng = np.random.default_rng(100 + L + ng)
+    d = (L + 1) ** 2
+    a = {k: v.astype(np.float32) for k, v in dict(
+        Y=rng.normal(size=(N, ng, ch)), H=rng.normal(size=(d, ng)) / np.sqrt(ng),
+        A=rng.normal(size=(ch, co)) / np.sqrt(ch), gZ=rng.normal(size=(N, d, co)), pY=rng.normal(size=(N, ng, ch)),
+        pA=rng.normal(size=(ch, co)) / np.sqrt(ch)).items()}
+    g, r = _dev(a), _ref(a)
+    H.note(f"[grid back] {name} L={L} c={ch}/{co} n_grid={ng} N={N}")
+    Z = K.so2grid_back_fwd(cfg, g["Y"], g["H"], g["A"])
+    bw = K.so2grid_back_bwd(cfg, g["Y"], g["H"], g["A"], g["gZ"])
+    db = K.so2grid_back_dbwd(cfg, g["Y"], g["H"], g["A"], g["gZ"], pY=g["pY"], pA=g["pA"])
+    d1 = K.so2grid_back_dbwd(cfg, g["Y"], g["H"], g["A"], g["gZ"], pY=g["pY"])     # one direction only
+    torch.cuda.synchronize()
+    rZ = GO.back_forward(r["Y"], r["H"], r["A"])
+    rb = GO.back_backward(r["Y"], r["H"], r["A"], r["gZ"])
+    rd = GO.back_double_backward(r["Y"], r["H"], r["A"], r["gZ"], pY=r["pY"], pA=r["pA"])
+    r1 = GO.back_double_backward(r["Y"], r["H"], r["A"], r["gZ"], pY=r["pY"])
+    errs = {"Z": H.relerr(Z, rZ), "gY": H.relerr(bw["gY"], rb["gY"]), "gA": H.relerr(bw["gA"], rb["gA"]),
+            "ggZ": H.relerr(db["ggZ"], rd["ggZ"]), "gY2": H.relerr(db["gY2"], rd["gY"]),
+            "gA2": H.relerr(db["gA2"], rd["gA"]), "ggZ(pY)": H.relerr(d1["ggZ"], r1["ggZ"]),
+            "gA2(pY)": H.relerr(d1["gA2"], r1["gA"])}
+    assert float(d1["gY2"].abs().max()) == 0.0          # no pA: dL/dY is zero
+    H.note("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    assert all(v <= H.TOL_F32 for v in errs.values()), errs
