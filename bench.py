@@ -21,6 +21,7 @@ weights) for the same step; the default is the medium system in float32.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -240,7 +241,7 @@ def bench_grid(args):
 
 def bench_s2act(args):
     """Spherical-grid SwiGLU activation on edges (EquiformerV3's Edge -> Edge
-    activation; Table 5, Section 5.1 and Appendix B.4) at the high-degree
+    activation; Table 2, Appendix C.1 and Appendix B.4) at the high-degree
     system's size: 1,045,678 edges, 29 retained rows (lmax 6, mmax 2), C 128
     (U carries 2C), a 100-point grid; fwd + bwd + dbwd (both outputs)."""
     import numpy as np
@@ -341,6 +342,10 @@ def main():
                     help="per-edge cutoff envelope on the messages (with genv, and genv2 in the double backward)")
     ap.add_argument("--heads", type=int, default=1,
                     help="per-head attention weights on the messages (EquiformerV3: 8 heads), times the envelope")
+    ap.add_argument("--act", choices=("gate", "swiglu_s2"), default="gate",
+                    help="Edge -> Edge activation: the gate (eSEN/UMA) or the spherical-grid SwiGLU (EquiformerV3)")
+    ap.add_argument("--n-grid", type=int, default=0,
+                    help="grid points of --act swiglu_s2 (default 2(L+1) latitudes x (2M+3) longitudes)")
     ap.add_argument("--cpu-edges", type=int, default=16384, help="edge sample of the CPU oracle baseline (0: skip)")
     ap.add_argument("--bounded-gib", type=float, default=32.0,
                     help="after the main line, time the same step with the workspace capped at this many GiB "
@@ -382,6 +387,10 @@ def main():
     dtype = args.dtype or cfg.dtype
     if dtype == "bf16" and cfg.dtype != "bf16":
         cfg = so2_synth.make_config(args.config, dtype="bf16")   # bf16-representable inputs
+    s2 = args.act == "swiglu_s2"
+    if s2:
+        ng = args.n_grid or 2 * (cfg.lmax + 1) * (2 * cfg.mmax + 3)
+        cfg = dataclasses.replace(cfg, act="swiglu_s2", n_grid=ng)
     d = so2_synth.make_inputs(cfg)
     progress(f"inputs ready: N={cfg.n_atoms} E={len(d['src'])}")
     E, N = len(d["src"]), cfg.n_atoms
@@ -392,7 +401,8 @@ def main():
 
     ft = torch.bfloat16 if dtype == "bf16" else torch.float32
     kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype, heads=args.heads,
-                     f32_native=args.f32_native)
+                     f32_native=args.f32_native, act=args.act,
+                     grid=(t(d["grid_G"]), t(d["grid_P"])) if s2 else None)
     g = K.so2conv_graph_prepare(N, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]))
     x, pos, rbf, w_rad = t(d["x"], ft), t(d["pos"]), t(d["rbf"]), t(d["w_rad"], ft)
     w1, w2 = [t(w, ft) for w in d["w1"]], [t(w, ft) for w in d["w2"]]
@@ -544,11 +554,12 @@ def main():
                    + (f", {args.heads}-head attention weights times the cutoff envelope" if args.heads > 1
                       else (", cutoff envelope" if args.envelope else ""))
                    + (f", mixture of {args.experts} linear experts over {args.systems} systems" if mole else "")
-                   + (", float32 products on the float32 matrix cores" if args.f32_native and dtype == "f32" else ""),
+                   + (", float32 products on the float32 matrix cores" if args.f32_native and dtype == "f32" else "")
+                   + (f", spherical-grid SwiGLU activation on {cfg.n_grid} grid points" if s2 else ""),
                    "edge_chunks": chunked, "forward_state_kept": keep_state, "backward_cotangents_kept": keep_bwd},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak,
-                     "traffic": None if mole else measured_gemm_traffic(args.config, dtype, keep_bwd, split),
+                     "traffic": None if (mole or s2) else measured_gemm_traffic(args.config, dtype, keep_bwd, split),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
                      "kernel": kname,
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
@@ -565,7 +576,8 @@ def main():
                                        "separate_operation_intermediates": mat_gib},
         ("step_tflops_3F_equivalent" if two_stage else "step_tflops_8F_equivalent"):
             (3 if two_stage else 8) * F * E / (ms_step * 1e-3) / 1e12,
-        "hbm": measured_step_traffic(args.config, dtype, keep_bwd, ms_step) if not (mole or args.envelope) else None,
+        "hbm": measured_step_traffic(args.config, dtype, keep_bwd, ms_step) if not (mole or args.envelope or s2)
+        else None,
     }
     progress(f"timed {args.steps} steps: {ms_step:.1f} ms/step")
     if args.bounded_gib > 0 and not mole and keep_state and not chunked:

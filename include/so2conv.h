@@ -34,7 +34,8 @@
  *          is order +m, "-" is order -m.
  *   w2[0]: [(L+1)*C, (L+1)*C];  w2[m]: [(L-m+1)*C, 2*(L-m+1)*C].
  *   Gate: l = 0 -> SiLU(u); l >= 1 -> sigmoid(gate_{l,c}) * u for every
- *   retained order |m| <= min(l, M).
+ *   retained order |m| <= min(l, M). (cfg->act selects the spherical-grid
+ *   SwiGLU instead, which changes the first linear's columns; see act.)
  *   Graph: dst non-decreasing (edges grouped by receiver).
  *
  * dtype (cfg->dtype): SO2_F32 -- every array float32, float32 arithmetic.
@@ -101,10 +102,40 @@ enum {
   SO2_F32_NATIVE = 4
 };
 
+/* cfg->act: the Edge -> Edge activation between the two SO(2) linears
+ * (TrimSO(2) page, Appendix C.1 "Implementation": eSEN and UMA recombine with
+ * a gated activation, EquiformerV3 uses its spherical-grid activation; Table
+ * 2 names it SwiGLU-S2).
+ *   SO2_ACT_GATE: the gate described at the top of this file.
+ *   SO2_ACT_SWIGLU_S2: the first linear has 2C output channels per retained
+ *     row (channels 0..C-1 the value half u_v, C..2C-1 the gate half u_g):
+ *       w1[0]: [(L+1)*2C, (L+1)*2C], columns (l, c'), c' in [0, 2C);
+ *       w1[m]: [(L-m+1)*2C, 2*(L-m+1)*2C] = [W_m0 | W_m1], columns of each
+ *              half (l = m..L, c'), Eq.(1) as above.
+ *     Per edge and channel c, over the q retained rows of the edge frame:
+ *       v = G u_v,  a = G u_g,  s = SiLU(a) * v,  z = P s
+ *     with G = grid_basis [n_grid][q] (the retained basis at n_grid points of
+ *     the edge-frame sphere) and P = grid_proj [q][n_grid] (the projection
+ *     back), device float32 arrays the calls only read; a row index r counts
+ *     the retained rows in degree-major order (l = 0..L, then m =
+ *     -min(l,M)..min(l,M)). q <= 32 and n_grid in [1, 256] (else
+ *     SO2_EUNSUPPORTED); the compute calls return SO2_EINVAL for NULL tables.
+ *     G and P are constants: no gradients are formed for them. The grid
+ *     products run on the float32 matrix cores with float32 operands (also
+ *     for SO2_BF16 calls, whose first-linear outputs are float32); z is
+ *     stored in the operand type of the second linear.
+ *   The size queries read only act and n_grid. The mixture entry points
+ *   (so2mole_*) take SO2_ACT_GATE only. */
+enum { SO2_ACT_GATE = 0, SO2_ACT_SWIGLU_S2 = 1 };
+
 /* heads: 0 or 1 = one weight per edge; H > 1 divides channels, C / H is 16,
  * 32 or a multiple of 64, H <= 16 (else SO2_EUNSUPPORTED). */
 typedef struct {
   int32_t lmax, mmax, channels, n_rbf, dtype, flags, heads;
+  int32_t act;               /* SO2_ACT_GATE or SO2_ACT_SWIGLU_S2 */
+  int32_t n_grid;            /* SO2_ACT_SWIGLU_S2: grid points */
+  const float* grid_basis;   /* SO2_ACT_SWIGLU_S2: G [n_grid][q], device */
+  const float* grid_proj;    /* SO2_ACT_SWIGLU_S2: P [q][n_grid], device */
 } so2conv_cfg;
 
 typedef struct {
@@ -327,7 +358,7 @@ int so2grid_back_dbwd(const so2grid_cfg* cfg, int32_t n_nodes, const float* Y, c
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Spherical-grid SwiGLU activation on edges (SwiGLU-S2; TrimSO(2) page,
- * Table 5 and Section 5.1: EquiformerV3's Edge -> Edge activation; Appendix
+ * Table 2 and Appendix C.1 "Implementation": EquiformerV3's Edge -> Edge activation; Appendix
  * B.4: the degree-l basis evaluated at n_g grid points, the nonlinearity on
  * grid values). The pages name the activation without a formula; read here,
  * per edge e and channel c of q coefficient rows with a value half

@@ -1,6 +1,6 @@
 """Oracle (test infrastructure only) of the spherical-grid SwiGLU activation on
-edges (SwiGLU-S2): TrimSO(2) page, Table 5 (EquiformerV3's activation is
-SwiGLU-S2), Section 5.1 (EquiformerV3 uses its spherical-grid activation for
+edges (SwiGLU-S2): TrimSO(2) page, Table 2 (EquiformerV3's activation is
+SwiGLU-S2), Appendix C.1 "Implementation" (EquiformerV3 uses its spherical-grid activation for
 Edge -> Edge) and Appendix B.4 (G_l evaluates the degree-l basis at n_g grid
 points; the nonlinearity acts on grid values).
 

@@ -18,6 +18,10 @@ Interatomic Potentials, Section 2 Eq.(1)-(2), Appendix A.1-A.2, B.1-B.3):
         m > 0 : [Q00 Q01; Q10 Q11] = [T_+; T_-][W_m0 W_m1],
                 u_+ = Q00 - Q11, u_- = Q10 + Q01
     gate (B.2): l = 0 -> SiLU(u); l >= 1 -> sigmoid(gamma_l) * u for all retained m
+      or, with grid tables (G, P) (EquiformerV3's spherical-grid SwiGLU, Appendix
+      C.1 "Implementation" and Table 2): the first linear has 2C output channels
+      per retained row (value half, then gate half) and the activation is
+      s2act_oracle.forward over each edge's retained rows in degree-major order
     second SO(2) linear (same structure, no gate columns) -> t_e
     y_i  += sum_e (J D_e)^T t_e                                     (B.3 inverse rotation)
 
@@ -48,8 +52,11 @@ import math
 import numpy as np
 import torch
 
+from . import s2act_oracle
+
 __all__ = ["real_sh", "wigner_d", "edge_frame", "forward", "backward", "double_backward",
-           "retained_orders", "q_count", "k_count", "OracleInputs", "to_oracle_inputs"]
+           "retained_orders", "q_count", "k_count", "OracleInputs", "to_oracle_inputs", "grid_rows",
+           "activation_input"]
 
 DT = torch.float64
 
@@ -168,14 +175,19 @@ class OracleInputs:
     page, Appendix C.1 Implementation: eSEN and UMA sum messages with their
     cutoff envelopes, one weight per edge; EquiformerV3 applies attention
     weights before aggregation, one weight per edge and head, head h covering
-    channels [h C/H, (h+1) C/H))."""
+    channels [h C/H, (h+1) C/H)). `grid` (None or (G, P)) selects the
+    spherical-grid SwiGLU activation instead of the gate (Appendix C.1
+    "Implementation": EquiformerV3's Edge -> Edge activation)."""
 
-    def __init__(self, lmax, mmax, channels, pos, x, src, dst, shift, rbf, w_rad, w1, w2, env=None):
+    def __init__(self, lmax, mmax, channels, pos, x, src, dst, shift, rbf, w_rad, w1, w2, env=None, grid=None):
         self.L, self.M, self.C = lmax, mmax, channels
         self.pos, self.x, self.rbf, self.w_rad = pos, x, rbf, w_rad
         self.w1, self.w2 = list(w1), list(w2)
         self.src, self.dst, self.shift = src, dst, shift
         self.env = env
+        # spherical-grid SwiGLU activation (None: the gate): constant tables
+        # (G [n_g, q], P [q, n_g]) over the retained rows in degree-major order
+        self.grid = grid
 
     def leaves(self):
         return [self.x, self.pos, self.rbf, self.w_rad] + self.w1 + self.w2 + \
@@ -188,11 +200,14 @@ def to_oracle_inputs(d: dict, requires_grad=False) -> OracleInputs:
     def t(a):
         return torch.tensor(np.asarray(a, dtype=np.float64), dtype=DT, requires_grad=requires_grad)
 
+    grid = None
+    if d.get("grid_G") is not None:
+        grid = tuple(torch.tensor(np.asarray(d[k], np.float64), dtype=DT) for k in ("grid_G", "grid_P"))
     return OracleInputs(cfg.lmax, cfg.mmax, cfg.channels, t(d["pos"]), t(d["x"]),
                         torch.tensor(d["src"], dtype=torch.int64), torch.tensor(d["dst"], dtype=torch.int64),
                         torch.tensor(np.asarray(d["shift"], np.float64), dtype=DT), t(d["rbf"]),
                         t(d["w_rad"]), [t(w) for w in d["w1"]], [t(w) for w in d["w2"]],
-                        t(d["env"]) if d.get("env") is not None else None)
+                        t(d["env"]) if d.get("env") is not None else None, grid)
 
 
 # ----------------------------------------------------------------------------- forward
@@ -231,6 +246,48 @@ def rotated_inputs(inp: OracleInputs, e_idx=None):
     return _rotated_inputs(inp, e_idx, D)
 
 
+def grid_rows(L: int, M: int):
+    """The retained rows (l, m) in degree-major order: the row order of the
+    spherical-grid activation's tables."""
+    return [(l, m) for l in range(L + 1) for m in retained_orders(l, M)]
+
+
+def _first_linear(inp: OracleInputs, T):
+    """Eq.(1) per order on the rotated inputs T (list over l of [E, 2l+1, 2C]):
+    u[(l, m)] of width C (gate; gamma[l] the gate columns of degree l >= 1) or
+    2C (spherical-grid SwiGLU: value channels, then gate channels; gamma None)."""
+    L, M, C = inp.L, inp.M, inp.C
+    hw = C if inp.grid is None else 2 * C
+    u = {}
+    T0 = torch.cat([T[l][:, l, :] for l in range(L + 1)], -1)
+    o0 = T0 @ inp.w1[0]
+    for l in range(L + 1):
+        u[(l, 0)] = o0[:, l * hw:(l + 1) * hw]
+    gamma = None
+    if inp.grid is None:
+        gamma = {l: o0[:, (L + 1) * C + (l - 1) * C:(L + 1) * C + l * C] for l in range(1, L + 1)}
+    for m in range(1, M + 1):
+        Tp = torch.cat([T[l][:, l + m, :] for l in range(m, L + 1)], -1)
+        Tm = torch.cat([T[l][:, l - m, :] for l in range(m, L + 1)], -1)
+        up, um = _so2_linear(Tp, Tm, inp.w1[m])
+        for k, l in enumerate(range(m, L + 1)):
+            u[(l, m)] = up[:, k * hw:(k + 1) * hw]
+            u[(l, -m)] = um[:, k * hw:(k + 1) * hw]
+    return u, gamma
+
+
+def activation_input(inp: OracleInputs, e_idx=None):
+    """The first linear's output of the edges e_idx as [E', q, width] rows in
+    degree-major order (grid_rows): what the Edge -> Edge activation reads."""
+    if e_idx is None:
+        e_idx = torch.arange(inp.src.shape[0])
+    v = inp.pos[inp.src[e_idx]] - inp.pos[inp.dst[e_idx]] + inp.shift[e_idx]
+    R = edge_frame(v / torch.linalg.norm(v, dim=-1, keepdim=True))
+    D = [wigner_d(l, R) for l in range(inp.L + 1)]
+    u, _ = _first_linear(inp, _rotated_inputs(inp, e_idx, D))
+    return torch.stack([u[r] for r in grid_rows(inp.L, inp.M)], 1)
+
+
 def edge_messages(inp: OracleInputs, e_idx: torch.Tensor, roll: torch.Tensor | None = None):
     """Global-frame messages of the edges e_idx: list over l of [E', 2l+1, C].
 
@@ -246,24 +303,17 @@ def edge_messages(inp: OracleInputs, e_idx: torch.Tensor, roll: torch.Tensor | N
         R = _rot_z(roll) @ R
     D = [wigner_d(l, R) for l in range(L + 1)]
     T = _rotated_inputs(inp, e_idx, D)
-    # first SO(2) linear
-    u = {}
-    T0 = torch.cat([T[l][:, l, :] for l in range(L + 1)], -1)
-    o0 = T0 @ inp.w1[0]
-    for l in range(L + 1):
-        u[(l, 0)] = o0[:, l * C:(l + 1) * C]
-    gamma = {l: o0[:, (L + 1) * C + (l - 1) * C:(L + 1) * C + l * C] for l in range(1, L + 1)}
-    for m in range(1, M + 1):
-        Tp = torch.cat([T[l][:, l + m, :] for l in range(m, L + 1)], -1)
-        Tm = torch.cat([T[l][:, l - m, :] for l in range(m, L + 1)], -1)
-        up, um = _so2_linear(Tp, Tm, inp.w1[m])
-        for k, l in enumerate(range(m, L + 1)):
-            u[(l, m)] = up[:, k * C:(k + 1) * C]
-            u[(l, -m)] = um[:, k * C:(k + 1) * C]
-    # gated activation
-    z = {}
-    for (l, m), val in u.items():
-        z[(l, m)] = torch.nn.functional.silu(val) if l == 0 else torch.sigmoid(gamma[l]) * val
+    u, gamma = _first_linear(inp, T)
+    if inp.grid is None:
+        # gated activation
+        z = {}
+        for (l, m), val in u.items():
+            z[(l, m)] = torch.nn.functional.silu(val) if l == 0 else torch.sigmoid(gamma[l]) * val
+    else:
+        # spherical-grid SwiGLU over each edge's retained rows
+        rows = grid_rows(L, M)
+        Z = s2act_oracle.forward(torch.stack([u[r] for r in rows], 1), *inp.grid)
+        z = {r: Z[:, k, :] for k, r in enumerate(rows)}
     # second SO(2) linear
     t = {}
     Z0 = torch.cat([z[(l, 0)] for l in range(L + 1)], -1)
@@ -337,7 +387,8 @@ def backward(inp: OracleInputs, gy: torch.Tensor, chunk=4096, edges=None, with_e
     has_env = inp.env is not None
     inp2 = OracleInputs(inp.L, inp.M, inp.C, leaves[1], leaves[0], inp.src, inp.dst,
                         inp.shift.detach().clone().requires_grad_(with_edge_grad), leaves[2], leaves[3],
-                        leaves[4:4 + nw], leaves[4 + nw:4 + 2 * nw], leaves[4 + 2 * nw] if has_env else None)
+                        leaves[4:4 + nw], leaves[4 + nw:4 + 2 * nw], leaves[4 + 2 * nw] if has_env else None,
+                        inp.grid)
     N = inp.x.shape[0]
     acc = [torch.zeros_like(t) for t in leaves]
     gedge = torch.zeros_like(inp.shift) if with_edge_grad else None
@@ -371,7 +422,7 @@ def double_backward(inp: OracleInputs, gy: torch.Tensor, px=None, ppos=None, prb
     shift = inp.shift.detach().clone().requires_grad_(pedge is not None)
     inp2 = OracleInputs(inp.L, inp.M, inp.C, leaves[1], leaves[0], inp.src, inp.dst, shift,
                         leaves[2], leaves[3], leaves[4:4 + nw], leaves[4 + nw:4 + 2 * nw],
-                        leaves[4 + 2 * nw] if has_env else None)
+                        leaves[4 + 2 * nw] if has_env else None, inp.grid)
     dirs = [px, ppos, prbf, pw_rad] + list(pw1 or [None] * nw) + list(pw2 or [None] * nw) + \
         ([penv] if has_env else [])
     N = inp.x.shape[0]

@@ -28,7 +28,7 @@ import math
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "make_config", "radius_graph_pbc", "gaussian_rbf",
-           "random_targets_graph", "make_inputs", "weight_shapes"]
+           "random_targets_graph", "make_inputs", "weight_shapes", "swiglu_s2_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,6 +49,8 @@ class Config:
     cluster_radius: float = 0.0
     min_dist: float = 0.0  # rejection-sample positions until min pair distance >= this
     k_targets: int = 0     # >0: sweep graph, each node picks k distinct targets
+    act: str = "gate"      # Edge -> Edge activation: "gate" or "swiglu_s2"
+    n_grid: int = 0        # swiglu_s2: grid points of the activation's tables
 
 
 CONFIGS = {
@@ -74,20 +76,25 @@ def make_config(name: str, **overrides) -> Config:
     return dataclasses.replace(CONFIGS[name], **overrides) if overrides else CONFIGS[name]
 
 
-def weight_shapes(lmax: int, mmax: int, channels: int):
-    """Shapes of W1[m], W2[m] for m = 0..mmax (input width 2C, hidden and output width C).
+def weight_shapes(lmax: int, mmax: int, channels: int, act: str = "gate"):
+    """Shapes of W1[m], W2[m] for m = 0..mmax (input width 2C, output width C).
 
-    W1[0]: [(L+1)*2C, (L+1)*C + L*C]  rows (l, c_in); columns (l, c) then gate columns (l=1..L, c)
-    W1[m]: [(L-m+1)*2C, 2*(L-m+1)*C]  = [W_{m,0} | W_{m,1}]
+    act "gate" (hidden width C plus gate columns):
+      W1[0]: [(L+1)*2C, (L+1)*C + L*C]  rows (l, c_in); columns (l, c) then gate columns (l=1..L, c)
+      W1[m]: [(L-m+1)*2C, 2*(L-m+1)*C]  = [W_{m,0} | W_{m,1}]
+    act "swiglu_s2" (hidden width 2C per row: value channels, then gate channels):
+      W1[0]: [(L+1)*2C, (L+1)*2C]
+      W1[m]: [(L-m+1)*2C, 2*(L-m+1)*2C]
     W2[0]: [(L+1)*C, (L+1)*C]
     W2[m]: [(L-m+1)*C, 2*(L-m+1)*C]
     """
     L, M, C = lmax, mmax, channels
-    w1 = [((L + 1) * 2 * C, (L + 1) * C + L * C)]
+    hw = 2 * C if act == "swiglu_s2" else C
+    w1 = [((L + 1) * 2 * C, (L + 1) * hw + (0 if act == "swiglu_s2" else L * C))]
     w2 = [((L + 1) * C, (L + 1) * C)]
     for m in range(1, M + 1):
         nl = L - m + 1
-        w1.append((nl * 2 * C, 2 * nl * C))
+        w1.append((nl * 2 * C, 2 * nl * hw))
         w2.append((nl * C, 2 * nl * C))
     return w1, w2
 
@@ -267,6 +274,8 @@ def make_inputs(cfg: Config, with_directions=True):
     out = dict(cfg=cfg, pos=pos, src=src, dst=dst, shift=shift, rbf=rbf, x=x,
                w_rad=w_rad.astype(np.float32),
                w1=[w.astype(np.float32) for w in w1], w2=[w.astype(np.float32) for w in w2])
+    if cfg.act == "swiglu_s2":
+        out.update(swiglu_s2_inputs(cfg))
     # with_directions: True (all), False (none) or a tuple naming a prefix of
     # ("gy", "px", "ppos", "prbf"); draws stop after the last one requested, so a
     # prefix draws exactly the same values as the full set.
@@ -286,6 +295,33 @@ def make_inputs(cfg: Config, with_directions=True):
         out["w1"] = [round_bf16(w) for w in out["w1"]]
         out["w2"] = [round_bf16(w) for w in out["w2"]]
     return out
+
+
+def swiglu_s2_inputs(cfg: Config) -> dict:
+    """First-linear weights of the spherical-grid SwiGLU activation (value and
+    gate halves per retained row, drawn like the plain weights) and synthetic
+    grid tables grid_G [n_grid, q] ~ N(0, 1/q), grid_P [q, n_grid] ~ N(0, 1/n_grid)
+    of the size of a grid with n_grid points (the values of the tables do not
+    change the work; a model evaluates the retained harmonics at its grid).
+    Drawn from a stream of their own, so every other input equals the gated
+    workload's."""
+    rng = np.random.default_rng(30_000 + cfg.seed)
+    L, M, C = cfg.lmax, cfg.mmax, cfg.channels
+    q = (L + 1) * (2 * M + 1) - M * (M + 1)
+    ng = cfg.n_grid
+    if ng < 1:
+        raise ValueError("swiglu_s2 needs n_grid >= 1")
+    w1s, _ = weight_shapes(L, M, C, "swiglu_s2")
+
+    def draw(shape):
+        if cfg.weight_init == "glorot":
+            a = math.sqrt(6.0 / (shape[0] + shape[1]))
+            return rng.uniform(-a, a, size=shape)
+        return rng.normal(0.0, 1.0 / math.sqrt(C), size=shape)
+    w1 = [draw(s).astype(np.float32) for s in w1s]
+    G = (rng.normal(size=(ng, q)) / math.sqrt(q)).astype(np.float32)
+    P = (rng.normal(size=(q, ng)) / math.sqrt(ng)).astype(np.float32)
+    return dict(w1=w1, grid_G=G, grid_P=P)
 
 
 def mixture_inputs(d: dict, n_systems: int, n_experts: int, seed: int = 0, empty_system: bool = False,

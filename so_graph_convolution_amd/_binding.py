@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(HERE, "libso2conv.so")
 SO2_OK, SO2_EINVAL, SO2_EUNSUPPORTED, SO2_EWORKSPACE, SO2_EHIP, SO2_EDEVICE = 0, -1, -2, -3, -4, -5
 SO2_DEBUG_CHECKS = 2
 SO2_F32_NATIVE = 4
+SO2_ACT_GATE = 0
+SO2_ACT_SWIGLU_S2 = 1
 
 c_vp = ctypes.c_void_p
 c_sz = ctypes.c_size_t
@@ -24,7 +26,8 @@ c_i64 = ctypes.c_int64
 
 class Cfg(ctypes.Structure):
     _fields_ = [("lmax", c_i32), ("mmax", c_i32), ("channels", c_i32), ("n_rbf", c_i32), ("dtype", c_i32),
-                ("flags", c_i32), ("heads", c_i32)]
+                ("flags", c_i32), ("heads", c_i32), ("act", c_i32), ("n_grid", c_i32), ("grid_basis", c_vp),
+                ("grid_proj", c_vp)]
 
 
 class GridCfg(ctypes.Structure):

@@ -122,6 +122,9 @@ struct Ctx {
   int split = 0; // float32 products through bfloat16 pieces (float32 calls without SO2_F32_NATIVE)
   int ns = 1; // weight sets: one per system (the plain operator has one)
   int nk = 0; // experts of a mixture (0: plain operator)
+  int ng = 0; // spherical-grid activation: grid points, and the caller's tables (degree-major rows)
+  const float* gG = nullptr;
+  const float* gP = nullptr;
   size_t node_floats() const { return (size_t)d.d() * d.C; }   // one node row
   int wS() const { return (d.L + 1) * d.Ci(); }
 };
@@ -150,6 +153,15 @@ int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
   c->bf = cfg->dtype == SO2_BF16;
   c->es = c->bf ? 2 : 4;
   c->split = !c->bf && !(cfg->flags & SO2_F32_NATIVE);
+  if (cfg->act != SO2_ACT_GATE && cfg->act != SO2_ACT_SWIGLU_S2) return fail(SO2_EINVAL, "unknown activation");
+  c->d.s2 = cfg->act == SO2_ACT_SWIGLU_S2;
+  if (c->d.s2) {
+    if (c->d.q() > 32) return fail(SO2_EUNSUPPORTED, "the grid activation takes at most 32 retained rows");
+    if (cfg->n_grid < 1 || cfg->n_grid > 256) return fail(SO2_EUNSUPPORTED, "n_grid must be in [1, 256]");
+    c->ng = cfg->n_grid;
+    c->gG = cfg->grid_basis;
+    c->gP = cfg->grid_proj;
+  }
   return SO2_OK;
 }
 
@@ -443,13 +455,17 @@ Primal saved_rows(const Ctx& c, const void* saved, long E, long e0) {
           reinterpret_cast<const float*>(st + sl.V) + (size_t)e0 * d.wZ()};
 }
 
+// m-major grid tables of the spherical-grid activation (NULL with the gate)
+float* take_s2(Arena& ar, const Ctx& c) { return c.d.s2 ? ar.take(2 * (size_t)c.ng * c.d.q()) : nullptr; }
+
 struct FwdWs {
   std::vector<LinBuf> W1, W2;
   MixWs mix;
-  float *w_rad32, *x32, *y32;
+  float *w_rad32, *x32, *y32, *s2t;
   PrimalBuf pr;
 };
 void layout_fwd(Arena& ar, const Ctx& c, int N, long ec, bool recompute, FwdWs* w) {
+  w->s2t = take_s2(ar, c);
   w->W1 = take_lins(ar, c, 0);
   w->W2 = take_lins(ar, c, 1);
   take_mix(ar, c, 0, &w->mix);
@@ -464,7 +480,7 @@ struct BwdWs {
   std::vector<float*> gW1r, gW2r;
   MixWs mix;
   float* vbar_all;
-  float *w_rad32, *x32, *gy32, *gx32, *gw_rad32;
+  float *w_rad32, *x32, *gy32, *gx32, *gw_rad32, *s2t;
   PrimalBuf pr;
   void *tbar, *Ubar;
   float *Zbar, *Tbar, *Sbar, *tau1, *tau2, *tau3, *P;
@@ -472,6 +488,7 @@ struct BwdWs {
 void layout_bwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute, BwdWs* w) {
   const Dims& d = c.d;
   const size_t e = (size_t)ec;
+  w->s2t = take_s2(ar, c);
   w->W1 = take_lins(ar, c, 0);
   w->W2 = take_lins(ar, c, 1);
   w->gW1r = take_grads(ar, c, 0);
@@ -500,7 +517,7 @@ struct DbwdWs {
   std::vector<float*> gW1r, gW2r, gW1f, gW2f;   // gW*f: first-order weight gradients (mixture directions)
   MixWs mix;
   float *vbar2_all, *p2e, *p2d, *p2s;
-  float *w_rad32, *pw_rad32, *x32, *px32, *gy32, *ggy32, *gx2_32, *gw_rad2_32;
+  float *w_rad32, *pw_rad32, *x32, *px32, *gy32, *ggy32, *gx2_32, *gw_rad2_32, *s2t;
   PrimalBuf pr;
   void *Tdot, *Zdot, *G2, *UU;
   float *Sdot, *omega, *Udot, *Vdot, *ZZ, *TT, *Sbar, *Sdb, *P;
@@ -508,6 +525,7 @@ struct DbwdWs {
 void layout_dbwd(Arena& ar, const Ctx& c, int N, long E, long ec, bool recompute, DbwdWs* w) {
   const Dims& d = c.d;
   const size_t e = (size_t)ec;
+  w->s2t = take_s2(ar, c);
   w->W1 = take_lins(ar, c, 0);
   w->W2 = take_lins(ar, c, 1);
   w->pW1 = take_lins(ar, c, 0);
@@ -1070,15 +1088,68 @@ int zero_sets(const std::vector<float*>& G, size_t n, hipStream_t s) {
   return SO2_OK;
 }
 
+// ---------------------------------------------------------------- Edge -> Edge activation
+int check_act(const Ctx& c) {
+  if (c.d.s2 && (!c.gG || !c.gP)) return fail(SO2_EINVAL, "grid_basis or grid_proj is NULL");
+  return SO2_OK;
+}
+// The gate, or the spherical-grid SwiGLU with the call's m-major grid tables
+// G [ng][q], P [q][ng] (copied from the caller's degree-major tables into the
+// workspace once per call). Inputs U, Udot, Zbar... float32; outputs of the
+// operand type.
+struct ActTab {
+  const float* G = nullptr;
+  const float* P = nullptr;
+};
+int act_tables(const Ctx& c, float* s2t, ActTab* t, hipStream_t s) {
+  if (!c.d.s2) return SO2_OK;
+  float* Gm = s2t;
+  float* Pm = s2t + (size_t)c.ng * c.d.q();
+  SO2_HIP(launch_s2_mmajor(c.d.L, c.d.M, c.ng, c.gG, c.gP, Gm, Pm, s));
+  t->G = Gm;
+  t->P = Pm;
+  return SO2_OK;
+}
+// Z = A(U)
+int act_fwd(const Ctx& c, const ActTab& t, long n, const float* U, void* Z, hipStream_t s) {
+  if (c.d.s2) SO2_HIP(launch_s2_fwd(n, c.d.q(), c.d.C, c.ng, U, t.G, t.P, Z, c.bf, s));
+  else SO2_HIP(launch_gate_fwd(c.d, n, U, Z, c.bf, s));
+  return SO2_OK;
+}
+// Ubar = J(U)^T Zbar
+int act_bwd(const Ctx& c, const ActTab& t, long n, const float* U, const float* Zbar, void* Ubar, hipStream_t s) {
+  if (c.d.s2) SO2_HIP(launch_s2_bwd(n, c.d.q(), c.d.C, c.ng, U, t.G, t.P, Zbar, Ubar, c.bf, s));
+  else SO2_HIP(launch_gate_bwd(c.d, n, U, Zbar, Ubar, c.bf, s));
+  return SO2_OK;
+}
+// Zdot = J(U) Udot
+int act_dual(const Ctx& c, const ActTab& t, long n, const float* U, const float* Udot, void* Zdot, hipStream_t s) {
+  if (c.d.s2)
+    SO2_HIP(launch_s2_dbwd(n, c.d.q(), c.d.C, c.ng, U, t.G, t.P, nullptr, Udot, Zdot, nullptr, c.bf, s));
+  else
+    SO2_HIP(launch_gate_dual(c.d, n, U, Udot, Zdot, c.bf, s));
+  return SO2_OK;
+}
+// reverse of the tangent chain: Ub = J^T Zb + d/dU <Zdb, J Udot>; Udb = J^T Zdb (may be NULL)
+int act_dbwd(const Ctx& c, const ActTab& t, long n, const float* U, const float* Udot, const float* Zdb,
+             const float* Zb, void* Udb, void* Ub, hipStream_t s) {
+  if (c.d.s2)
+    SO2_HIP(launch_s2_rev(n, c.d.q(), c.d.C, c.ng, U, t.G, t.P, Udot, Zdb, Zb, Udb, Ub, c.bf, s));
+  else
+    SO2_HIP(launch_gate_dbwd(c.d, n, U, Udot, Zdb, Zb, Udb, Ub, c.bf, s));
+  return SO2_OK;
+}
+
 // forward state of the chunk [g.e0, g.e1) into (S, T, U, Z, V)
-int forward_chunk(const Ctx& c, const GraphDev& g, const float* x, const float* pos, const float* rbf,
-                  const float* w_rad, const WSet& W1, const WSet& W2, const PrimalBuf& p, hipStream_t s) {
+int forward_chunk(const Ctx& c, const ActTab& at, const GraphDev& g, const float* x, const float* pos,
+                  const float* rbf, const float* w_rad, const WSet& W1, const WSet& W2, const PrimalBuf& p,
+                  hipStream_t s) {
   const int ec = (int)(g.e1 - g.e0);
   int r;
   if ((r = radial(c, ec, rbf + (size_t)g.e0 * c.n_rbf, w_rad, p.S, s))) return r;
   SO2_HIP(launch_edge_fwd(c.d, g, x, pos, p.S, p.T, c.bf, s));
   if ((r = run_lin(c, 0, false, p.T, p.U, W1, g.e0, ec, 1, 0, s))) return r;
-  SO2_HIP(launch_gate_fwd(c.d, ec, p.U, p.Z, c.bf, s));
+  if ((r = act_fwd(c, at, ec, p.U, p.Z, s))) return r;
   return run_lin(c, 1, false, p.Z, p.V, W2, g.e0, ec, 1, 0, s);
 }
 
@@ -1107,7 +1178,7 @@ int conv_fwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
              void* ws, size_t ws_bytes, void* stream) {
   int r;
   const Dims& d = c.d;
-  if ((r = check_weights(d, w_rad, w1, w2))) return r;
+  if ((r = check_weights(d, w_rad, w1, w2)) || (r = check_act(c))) return r;
   if (!x || !pos || (!rbf && gd.E > 0) || !y) return fail(SO2_EINVAL, "NULL input or output");
   if ((r = ensure_init())) return r;
   if ((r = debug_validate(c, gd, pos, rbf, env, (hipStream_t)stream))) return r;
@@ -1126,6 +1197,8 @@ int conv_fwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
   if ((r = f32_in(c, w_rad, w.w_rad32, (size_t)c.n_rbf * c.wS(), &wr32, s))) return r;
   float* y32 = f32_acc(c, y, w.y32);
   if ((r = prepare_weights(c, mx, w1, w2, w.W1, w.W2, w.mix, s))) return r;
+  ActTab at;
+  if ((r = act_tables(c, w.s2t, &at, s))) return r;
   const std::vector<long> se = sys_edges(mx, gd.E);
   const WSet W1 = wset(c, 0, se, w.W1, w1, w.mix.merged[0]), W2 = wset(c, 1, se, w.W2, w2, w.mix.merged[1]);
   if (gd.E == 0) {
@@ -1148,7 +1221,7 @@ int conv_fwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
       p.Z = st + sl.Z + (size_t)e0 * d.wZ() * c.es;
       p.V = reinterpret_cast<float*>(st + sl.V) + (size_t)e0 * d.wZ();
     }
-    if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, p, s))) return r;
+    if ((r = forward_chunk(c, at, gc, x32, pos, rbf, wr32, W1, W2, p, s))) return r;
     SO2_HIP(launch_node_fwd(d, gc, pos, p.V, env, y32, k > 0, s));
   }
   return f32_out(c, y32, y, nf, s);
@@ -1162,7 +1235,7 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
              void* const* gw2, float* gcoef, float* gedge, void* saved_bwd, void* ws, size_t ws_bytes, void* stream) {
   int r;
   const Dims& d = c.d;
-  if ((r = check_weights(d, w_rad, w1, w2))) return r;
+  if ((r = check_weights(d, w_rad, w1, w2)) || (r = check_act(c))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
   if (genv && !env) return fail(SO2_EINVAL, "genv requested without an envelope");
   if ((r = ensure_init())) return r;
@@ -1187,6 +1260,8 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
   float* vbar = gedge ? gedge : w.vbar_all;
   const bool want_w1 = !all_null(gw1, d.M + 1) || gcoef, want_w2 = !all_null(gw2, d.M + 1) || gcoef;
   if ((r = prepare_weights(c, mx, w1, w2, w.W1, w.W2, w.mix, s))) return r;
+  ActTab at;
+  if ((r = act_tables(c, w.s2t, &at, s))) return r;
   const std::vector<long> se = sys_edges(mx, gd.E);
   const WSet W1 = wset(c, 0, se, w.W1, w1, w.mix.merged[0]), W2 = wset(c, 1, se, w.W2, w2, w.mix.merged[1]);
   if (mx && want_w1 && (r = zero_sets(w.gW1r, realified_size(d, 0), s))) return r;
@@ -1199,7 +1274,7 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
     const int acc = k > 0;
     Primal pr;
     if (recompute) {
-      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
+      if ((r = forward_chunk(c, at, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
       pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
     } else {
       pr = saved_rows(c, saved, gd.E, e0);
@@ -1214,7 +1289,7 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
       const void* out[1] = {w.tbar};
       if ((r = run_lin_grad(c, 1, in, out, 1, n, W2, e0, w.gW2r, mx != nullptr, w.P, s))) return r;
     }
-    SO2_HIP(launch_gate_bwd(d, n, pr.U, cb.Z, cb.U, c.bf, s));
+    if ((r = act_bwd(c, at, n, pr.U, cb.Z, cb.U, s))) return r;
     if ((r = run_lin(c, 0, true, cb.U, cb.T, W1, e0, n, 1, 0, s))) return r;
     if (want_w1) {
       const void* in[1] = {pr.T};
@@ -1231,7 +1306,7 @@ int conv_bwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, c
       TnSeg seg{rbf + (size_t)e0 * n_rbf, n_rbf, w.Sbar, wS, n};
       if ((r = run_tn(&seg, 1, n_rbf, wS, gwr_acc, wS, acc, w.P, 0, s))) return r;
     }
-    if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, w.tau1, w.tau2, w.tau3, vbar, s));
+    if (gpos || gedge) SO2_HIP(launch_vbar(gc, pos, w.tau1, w.tau2, w.tau3, vbar, d.s2, s));
   }
   if (!mx) {
     if (want_w2) SO2_HIP(launch_fold_grad(d, 1, w.gW2r[0], gw2, c.bf, s, !c.bf && !c.split));
@@ -1263,7 +1338,7 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
               size_t ws_bytes, void* stream) {
   int r;
   const Dims& d = c.d;
-  if ((r = check_weights(d, w_rad, w1, w2))) return r;
+  if ((r = check_weights(d, w_rad, w1, w2)) || (r = check_act(c))) return r;
   if (!x || !pos || !gy || (!rbf && gd.E > 0)) return fail(SO2_EINVAL, "NULL input");
   if ((penv || genv2) && !env) return fail(SO2_EINVAL, "penv or genv2 given without an envelope");
   if ((r = ensure_init())) return r;
@@ -1324,6 +1399,8 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     if (first && want_w1 && (r = zero_sets(w.gW1f, realified_size(d, 0), s))) return r;
     if (first && want_w2 && (r = zero_sets(w.gW2f, realified_size(d, 1), s))) return r;
   }
+  ActTab at;
+  if ((r = act_tables(c, w.s2t, &at, s))) return r;
   const std::vector<long> se = sys_edges(mx, gd.E);
   const WSet W1 = wset(c, 0, se, w.W1, w1, w.mix.merged[0]), W2 = wset(c, 1, se, w.W2, w2, w.mix.merged[1]);
   const WSet pW1 = wset(c, 0, se, w.pW1, pw1, w.mix.pmerged[0]), pW2 = wset(c, 1, se, w.pW2, pw2, w.mix.pmerged[1]);
@@ -1337,7 +1414,7 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     const float* prbf_c = prbf ? prbf + (size_t)e0 * n_rbf : nullptr;
     Primal pr;
     if (recompute) {
-      if ((r = forward_chunk(c, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
+      if ((r = forward_chunk(c, at, gc, x32, pos, rbf, wr32, W1, W2, w.pr, s))) return r;
       pr = {w.pr.S, w.pr.T, w.pr.U, w.pr.Z, w.pr.V};
     } else {
       pr = saved_rows(c, saved, gd.E, e0);
@@ -1355,7 +1432,7 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     SO2_HIP(launch_edge_dual(d, gc, x32, px32, pos, ppos, pedge, pr.S, w.Sdot, w.Tdot, w.omega, c.bf, s));
     if ((r = run_lin(c, 0, false, w.Tdot, w.Udot, W1, e0, n, 1, 0, s))) return r;
     if (has_pw1 && (r = run_lin(c, 0, false, pr.T, w.Udot, pW1, e0, n, 1, 1, s))) return r;
-    SO2_HIP(launch_gate_dual(d, n, pr.U, w.Udot, w.Zdot, c.bf, s));
+    if ((r = act_dual(c, at, n, pr.U, w.Udot, w.Zdot, s))) return r;
     if ((r = run_lin(c, 1, false, w.Zdot, w.Vdot, W2, e0, n, 1, 0, s))) return r;
     if (has_pw2 && (r = run_lin(c, 1, false, pr.Z, w.Vdot, pW2, e0, n, 1, 1, s))) return r;
     // dL/dgy = the forward's directional derivative (Eq.(5))
@@ -1393,7 +1470,7 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
       if (first && (r = run_lin_grad(c, 1, &in[1], out, 1, n, W2, e0, w.gW2f, true, w.P, s))) return r;
     }
     // [Udot_bar; Ubar]
-    SO2_HIP(launch_gate_dbwd(d, n, pr.U, w.Udot, Zdb, Zb, saved_bwd ? nullptr : w.UU, Ub, c.bf, s));
+    if ((r = act_dbwd(c, at, n, pr.U, w.Udot, Zdb, Zb, saved_bwd ? nullptr : w.UU, Ub, s))) return r;
     // [Tdot_bar; Tbar] = UU W1^T
     if (saved_bwd) {
       if ((r = run_lin(c, 0, true, Ub, Tb, W1, e0, n, 1, 0, s))) return r;
@@ -1411,7 +1488,7 @@ int conv_dbwd(const Ctx& c, const GraphDev& gd, const MixIn* mx, const void* x, 
     }
     SO2_HIP(launch_node_bwd_dual(d, gc, x32, px32, pos, w.omega, pr.S, w.Sdot, Tdb, Tb, gx2_acc, w.Sbar, w.Sdb,
                                  gpos2 ? w.p2d : nullptr, gpos2 ? w.p2s : nullptr, acc, s));
-    if (gpos2) SO2_HIP(launch_pos2(gc, pos, ppos, pedge, w.omega, w.p2e, w.p2d, w.p2s, w.vbar2_all, s));
+    if (gpos2) SO2_HIP(launch_pos2(gc, pos, ppos, pedge, w.omega, w.p2e, w.p2d, w.p2s, w.vbar2_all, d.s2, s));
     if (grbf2) {
       float* out = grbf2 + (size_t)e0 * n_rbf;
       std::vector<GemmProb> ps{prob(w.Sbar, wS, wr32, wS, out, n_rbf, n, n_rbf, wS)};
@@ -1623,6 +1700,7 @@ namespace {
 int check_mole(const Ctx& c0, const so2mole_cfg* m, long E, Ctx* c, MixIn* mx) {
   *c = c0;
   if (!m) return fail(SO2_EINVAL, "mixture cfg is NULL");
+  if (c0.d.s2) return fail(SO2_EUNSUPPORTED, "the mixture of linear experts takes the gated activation only");
   if (m->n_systems < 1 || m->n_systems > 65536) return fail(SO2_EUNSUPPORTED, "n_systems must be in [1, 65536]");
   if (m->n_experts < 4 || m->n_experts > 1024 || m->n_experts % 4)
     return fail(SO2_EUNSUPPORTED, "n_experts must be a multiple of 4 in [4, 1024]");
@@ -1762,7 +1840,7 @@ int so2s2_fwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float
   if ((r = check_s2(cfg, n_edges))) return r;
   if (n_edges == 0) return SO2_OK;
   if (!U || !G || !P || !Z) return fail(SO2_EINVAL, "NULL input or output");
-  SO2_HIP(launch_s2_fwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, Z, (hipStream_t)stream));
+  SO2_HIP(launch_s2_fwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, Z, 0, (hipStream_t)stream));
   return SO2_OK;
 }
 
@@ -1773,7 +1851,7 @@ int so2s2_bwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const float
   if ((r = check_s2(cfg, n_edges))) return r;
   if (n_edges == 0) return SO2_OK;
   if (!U || !G || !P || !gZ || !gU) return fail(SO2_EINVAL, "NULL input or output");
-  SO2_HIP(launch_s2_bwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, gZ, gU, (hipStream_t)stream));
+  SO2_HIP(launch_s2_bwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, gZ, gU, 0, (hipStream_t)stream));
   return SO2_OK;
 }
 
@@ -1785,7 +1863,7 @@ int so2s2_dbwd(const so2s2_cfg* cfg, int64_t n_edges, const float* U, const floa
   if (n_edges == 0) return SO2_OK;
   if (!U || !G || !P || !gZ || !pU) return fail(SO2_EINVAL, "NULL input");
   if (!ggZ && !gU2) return fail(SO2_EINVAL, "no output requested");
-  SO2_HIP(launch_s2_dbwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, gZ, pU, ggZ, gU2,
+  SO2_HIP(launch_s2_dbwd(n_edges, cfg->rows, cfg->channels, cfg->n_grid, U, G, P, gZ, pU, ggZ, gU2, 0,
                          (hipStream_t)stream));
   return SO2_OK;
 }

@@ -344,8 +344,13 @@ __global__ void gate_bwd_kernel(Dims d, long E, const float* __restrict__ U, con
 }
 
 // ------------------------------------------------------------------ position gradient
+// With `roll` the frame's turn about the edge axis counts (a grid activation
+// is not invariant to it): the torque's axial part adds
+// -(tau . v) s (vy, -vx, 0) / (rho^2 (rho + s vz)), s the sign of vz (the
+// branch of edge_frame), from the roll rate -s (vy dvx - vx dvy) / (rho (rho + s vz)).
 __global__ void vbar_kernel(GraphDev g, const float* __restrict__ pos, const float* __restrict__ t1,
-                            const float* __restrict__ t2, const float* __restrict__ t3, float* __restrict__ vbar) {
+                            const float* __restrict__ t2, const float* __restrict__ t3, float* __restrict__ vbar,
+                            int roll) {
   for (long e = g.e0 + (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.e1; e += (long)gridDim.x * blockDim.x) {
     const long le = e - g.e0;
     const int j = g.src[e], i = g.dst[e];
@@ -360,9 +365,17 @@ __global__ void vbar_kernel(GraphDev g, const float* __restrict__ pos, const flo
     const float tx = t1[3 * le] + t2[3 * le] + t3[3 * le];
     const float ty = t1[3 * le + 1] + t2[3 * le + 1] + t3[3 * le + 1];
     const float tz = t1[3 * le + 2] + t2[3 * le + 2] + t3[3 * le + 2];
-    vbar[3 * e] = (ry * tz - rz * ty) * inv;
-    vbar[3 * e + 1] = (rz * tx - rx * tz) * inv;
-    vbar[3 * e + 2] = (rx * ty - ry * tx) * inv;
+    float o0 = (ry * tz - rz * ty) * inv, o1 = (rz * tx - rx * tz) * inv;
+    const float o2 = (rx * ty - ry * tx) * inv;
+    if (roll) {
+      const float sg = vz >= 0.f ? 1.f : -1.f;
+      const float f = -sg * (tx * vx + ty * vy + tz * vz) * inv * inv / (rho + sg * vz);
+      o0 += f * vy;
+      o1 -= f * vx;
+    }
+    vbar[3 * e] = o0;
+    vbar[3 * e + 1] = o1;
+    vbar[3 * e + 2] = o2;
   }
 }
 
@@ -418,10 +431,10 @@ int launch_node_bwd(const Dims& d, const GraphDev& g, const float* x, const floa
 }
 
 int launch_vbar(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
-                float* vbar, hipStream_t s) {
+                float* vbar, int roll, hipStream_t s) {
   const long n = g.e1 - g.e0;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(vbar_kernel, dim3(grid_for(n)), dim3(256), 0, s, g, pos, tau1, tau2, tau3, vbar);
+  hipLaunchKernelGGL(vbar_kernel, dim3(grid_for(n)), dim3(256), 0, s, g, pos, tau1, tau2, tau3, vbar, roll);
   return hipGetLastError();
 }
 

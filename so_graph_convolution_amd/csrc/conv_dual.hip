@@ -40,8 +40,12 @@ constexpr int kEdgeTileBytes = 16 * 1024;
 
 __device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
-// direction of the edge frame's rotation for an edge-vector direction dv
-__device__ inline void frame_rate(const EdgeGeo& gg, float dx, float dy, float dz, float* w) {
+// direction of the edge frame's rotation for an edge-vector direction dv.
+// With `roll` it includes the frame's turn about the edge axis: the frame of
+// edge_frame rolls at rate beta = -s (ry dx - rx dy) / (rho (1 + s rz)),
+// s = sign of rz (the branch the frame takes), which the gated operator
+// does not see (it is invariant to the roll) but a grid activation does.
+__device__ inline void frame_rate(const EdgeGeo& gg, float dx, float dy, float dz, float* w, bool roll) {
   const float inv = 1.f / gg.rho;
   const float pr = gg.rx * dx + gg.ry * dy + gg.rz * dz;
   const float ax = (dx - gg.rx * pr) * inv, ay = (dy - gg.ry * pr) * inv, az = (dz - gg.rz * pr) * inv;
@@ -49,6 +53,13 @@ __device__ inline void frame_rate(const EdgeGeo& gg, float dx, float dy, float d
   w[0] = ay * gg.rz - az * gg.ry;
   w[1] = az * gg.rx - ax * gg.rz;
   w[2] = ax * gg.ry - ay * gg.rx;
+  if (roll) {
+    const float sg = gg.rz >= 0.f ? 1.f : -1.f;
+    const float beta = -sg * (gg.ry * dx - gg.rx * dy) * inv / (1.f + sg * gg.rz);
+    w[0] += beta * gg.rx;
+    w[1] += beta * gg.ry;
+    w[2] += beta * gg.rz;
+  }
 }
 
 // ------------------------------------------------------------------ edge_dual
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
       dz += pedge[3 * e + 2];
     }
     float w[3];
-    frame_rate(gg, dx, dy, dz, w);
+    frame_rate(gg, dx, dy, dz, w, d.s2 != 0);
     for (int k = 0; k < 3; ++k) {
       sW[t * 3 + k] = w[k];
       omega[(e - g.e0) * 3 + k] = w[k];
@@ -600,10 +611,16 @@ struct NodeBwdDual {
 // R-dependence adds <Rdotbar, Rdot G_k> + (w x wbar)_k through the so(3)
 // commutators) and the rate cotangent wbar:
 //   vbar2 = r x tau / |v| + (wbar x dv)/|v|^2 - 2 (wbar . w) v/|v|^2
+// With `roll` (the frame's turn about the edge axis counts, see frame_rate)
+// the rate is w + beta r with beta = -s N / (|v| D), N = vy dvx - vx dvy,
+// D = |v| + s vz, and two terms join: the torque's axial part through the
+// roll, -(tau . r) s (vy, -vx, 0) / (|v| D), and the gradient of
+// (wbar . r) beta, -s / (|v|^2 D) [(wbar . v)(-dvy, dvx, 0) + N wbar
+// - N (wbar . v)(2 v / |v|^2 + (v / |v| + s z) / D)].
 __global__ void pos2_kernel(GraphDev g, const float* __restrict__ pos, const float* __restrict__ ppos,
                             const float* __restrict__ pedge, const float* __restrict__ omega,
                             const float* __restrict__ pe, const float* __restrict__ pd, const float* __restrict__ ps,
-                            float* __restrict__ vbar2) {
+                            float* __restrict__ vbar2, int roll) {
   for (long e = g.e0 + (long)blockIdx.x * blockDim.x + threadIdx.x; e < g.e1; e += (long)gridDim.x * blockDim.x) {
     const long le = e - g.e0;
     const int j = g.src[e], i = g.dst[e];
@@ -621,10 +638,30 @@ __global__ void pos2_kernel(GraphDev g, const float* __restrict__ pos, const flo
     tau[2] += w[0] * wb[1] - w[1] * wb[0];
     const float rho2 = v[0] * v[0] + v[1] * v[1] + v[2] * v[2], inv2 = 1.f / rho2, inv = sqrtf(inv2);
     const float r[3] = {v[0] * inv, v[1] * inv, v[2] * inv};
-    const float wbw = 2.f * (wb[0] * w[0] + wb[1] * w[1] + wb[2] * w[2]);
-    vbar2[3 * e] = (r[1] * tau[2] - r[2] * tau[1]) * inv + (wb[1] * dv[2] - wb[2] * dv[1] - wbw * v[0]) * inv2;
-    vbar2[3 * e + 1] = (r[2] * tau[0] - r[0] * tau[2]) * inv + (wb[2] * dv[0] - wb[0] * dv[2] - wbw * v[1]) * inv2;
-    vbar2[3 * e + 2] = (r[0] * tau[1] - r[1] * tau[0]) * inv + (wb[0] * dv[1] - wb[1] * dv[0] - wbw * v[2]) * inv2;
+    // the rate's part across the edge, (dv x v) / |v|^2: w without its axial part
+    const float wr = w[0] * r[0] + w[1] * r[1] + w[2] * r[2];
+    const float wbr = wb[0] * r[0] + wb[1] * r[1] + wb[2] * r[2];
+    const float wbw = 2.f * (wb[0] * w[0] + wb[1] * w[1] + wb[2] * w[2] - (roll ? wr * wbr : 0.f));
+    float o[3];
+    o[0] = (r[1] * tau[2] - r[2] * tau[1]) * inv + (wb[1] * dv[2] - wb[2] * dv[1] - wbw * v[0]) * inv2;
+    o[1] = (r[2] * tau[0] - r[0] * tau[2]) * inv + (wb[2] * dv[0] - wb[0] * dv[2] - wbw * v[1]) * inv2;
+    o[2] = (r[0] * tau[1] - r[1] * tau[0]) * inv + (wb[0] * dv[1] - wb[1] * dv[0] - wbw * v[2]) * inv2;
+    if (roll) {
+      const float rho = rho2 * inv, sg = v[2] >= 0.f ? 1.f : -1.f, D = rho + sg * v[2];
+      const float tv = tau[0] * v[0] + tau[1] * v[1] + tau[2] * v[2];
+      const float N = v[1] * dv[0] - v[0] * dv[1];
+      const float wv = wb[0] * v[0] + wb[1] * v[1] + wb[2] * v[2];
+      const float a = -sg * inv2 / D, c = N * wv;
+      const float h[3] = {2.f * v[0] * inv2 + v[0] * inv / D, 2.f * v[1] * inv2 + v[1] * inv / D,
+                          2.f * v[2] * inv2 + (v[2] * inv + sg) / D};
+      const float tr = -sg * tv * inv2 / D;   // -(tau . r) s / (|v| D)
+      o[0] += tr * v[1] + a * (-wv * dv[1] + N * wb[0] - c * h[0]);
+      o[1] += -tr * v[0] + a * (wv * dv[0] + N * wb[1] - c * h[1]);
+      o[2] += a * (N * wb[2] - c * h[2]);
+    }
+    vbar2[3 * e] = o[0];
+    vbar2[3 * e + 1] = o[1];
+    vbar2[3 * e + 2] = o[2];
   }
 }
 
@@ -780,10 +817,11 @@ int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, con
 }
 
 int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const float* pedge, const float* omega,
-                const float* pe, const float* pd, const float* ps, float* vbar2, hipStream_t s) {
+                const float* pe, const float* pd, const float* ps, float* vbar2, int roll, hipStream_t s) {
   const long n = g.e1 - g.e0;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pos2_kernel, dim3(grid_for(n)), dim3(256), 0, s, g, pos, ppos, pedge, omega, pe, pd, ps, vbar2);
+  hipLaunchKernelGGL(pos2_kernel, dim3(grid_for(n)), dim3(256), 0, s, g, pos, ppos, pedge, omega, pe, pd, ps, vbar2,
+                     roll);
   return hipGetLastError();
 }
 

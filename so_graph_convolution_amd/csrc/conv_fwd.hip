@@ -270,12 +270,13 @@ void realified_shape(const Dims& d, int second, int a, int* rows, int* cols, lon
   long o = 0;
   for (int b = 0; b <= d.M; ++b) {
     int r, c;
+    const int hout = second ? d.C : d.hw();
     if (b == 0) {
       r = (d.L + 1) * win;
-      c = second ? (d.L + 1) * d.C : (2 * d.L + 1) * d.C;
+      c = second || d.s2 ? (d.L + 1) * hout : (2 * d.L + 1) * d.C;
     } else {
       r = 2 * (d.L - b + 1) * win;
-      c = 2 * (d.L - b + 1) * d.C;
+      c = 2 * (d.L - b + 1) * hout;
     }
     if (b == a) {
       *rows = r;

@@ -8,8 +8,10 @@
 // edge, blocks for |m| = 0..M. With channel width W:
 //   block 0 : columns (l = 0..L, c)                               width (L+1) W
 //   block m : columns [ +m : (l = m..L, c) | -m : (l = m..L, c) ] width 2 (L-m+1) W
-// Total width q_{L,M} W. The first linear's output adds L*C gate columns
-// (l = 1..L, c) to block 0.
+// Total width q_{L,M} W. With the gated activation the first linear's output
+// adds L*C gate columns (l = 1..L, c) to block 0; with the spherical-grid
+// SwiGLU activation it has width 2C per row (value channels, then gate
+// channels) and no extra columns.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -72,7 +74,8 @@ constexpr int kMaxHeads = 16;   // heads of the per-edge message weights (C / he
 
 struct Dims {
   int L, M, C;
-  int H = 1;   // heads of the per-edge message weights: channel c belongs to head c / (C / H)
+  int H = 1;    // heads of the per-edge message weights: channel c belongs to head c / (C / H)
+  int s2 = 0;   // Edge -> Edge activation: 0 gate, 1 spherical-grid SwiGLU
   __host__ __device__ int Ci() const { return 2 * C; }
   __host__ __device__ int hs() const { return C / H; }                // channels per head
   __host__ __device__ int d() const { return (L + 1) * (L + 1); }
@@ -80,10 +83,15 @@ struct Dims {
   __host__ __device__ int K() const { return k_count(L, M); }
   __host__ __device__ int wT() const { return q() * 2 * C; }        // rotated input row
   __host__ __device__ int wZ() const { return q() * C; }            // hidden / message row
-  __host__ __device__ int wU() const { return q() * C + L * C; }    // first-linear output row
-  // column of block a in the first-linear output (block 0 carries the gate columns)
-  __host__ __device__ int u_block(int a) const { return a == 0 ? 0 : mm_block(a, L, C) + L * C; }
-  __host__ __device__ int u_width(int a) const { return a == 0 ? (2 * L + 1) * C : mm_width(a, L, C); }
+  __host__ __device__ int hw() const { return s2 ? 2 * C : C; }     // first-linear output width per row
+  __host__ __device__ int wU() const { return s2 ? q() * 2 * C : q() * C + L * C; }   // first-linear output row
+  // column of block a in the first-linear output (with the gate, block 0 carries the gate columns)
+  __host__ __device__ int u_block(int a) const {
+    return s2 ? mm_block(a, L, 2 * C) : (a == 0 ? 0 : mm_block(a, L, C) + L * C);
+  }
+  __host__ __device__ int u_width(int a) const {
+    return s2 ? mm_width(a, L, 2 * C) : (a == 0 ? (2 * L + 1) * C : mm_width(a, L, C));
+  }
   __host__ __device__ int gate_col(int l, int c) const { return (L + 1) * C + (l - 1) * C + c; }
   // U column of (l, m, c)
   __host__ __device__ int u_col(int l, int m, int c) const {

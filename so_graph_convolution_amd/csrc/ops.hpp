@@ -49,8 +49,9 @@ int launch_node_bwd(const Dims& d, const GraphDev& g, const float* x, const floa
                     const float* Tbar, float* gx, float* Sbar, float* tau_dst, float* tau_src, int accumulate,
                     hipStream_t s);
 // vbar[e] = rhat x (tau1 + tau2 + tau3) / rho for the chunk's edges (vbar indexed globally)
+// roll != 0: the frame's turn about the edge axis counts (activations that are not roll-invariant)
 int launch_vbar(const GraphDev& g, const float* pos, const float* tau1, const float* tau2, const float* tau3,
-                float* vbar, hipStream_t s);
+                float* vbar, int roll, hipStream_t s);
 // gpos[n] = sum_out vbar - sum_in vbar over every edge
 int launch_node_pos(const GraphDev& g, const float* vbar, float* gpos, hipStream_t s);
 
@@ -75,7 +76,7 @@ int launch_edge_bwd_dual(const Dims& d, const GraphDev& g, const float* pos, con
 // vbar2[e] (global edge index) = position derivative of the double backward per edge vector,
 // from the three [E][6] torque/rate parts (chunk-relative rows)
 int launch_pos2(const GraphDev& g, const float* pos, const float* ppos, const float* pedge, const float* omega,
-                const float* pe, const float* pd, const float* ps, float* vbar2, hipStream_t s);
+                const float* pe, const float* pd, const float* ps, float* vbar2, int roll, hipStream_t s);
 // from (Zdot_bar, Zbar) produce the operands (Udot_bar, Ubar), E rows each;
 // Udb NULL: Udot_bar is not written
 int launch_gate_dbwd(const Dims& d, long E, const float* U, const float* Udot, const float* Zdb, const float* Zb,
@@ -116,13 +117,20 @@ int launch_grid_apply(int L, int N, int ng, int C, const float* G, const float* 
 // Z = G^T U per node (G [ng][d]; basis_t: G given as [d][ng], so Z = H U for H = G^T)
 int launch_grid_apply_t(int L, int N, int ng, int C, const float* G, const float* U, float* Z, hipStream_t s,
                         int basis_t = 0);
-// spherical-grid SwiGLU activation on edges (s2act.hip)
-int launch_s2_fwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, float* Z,
+// spherical-grid SwiGLU activation on edges (s2act.hip); U-shaped arrays
+// [E][q][2C], Z-shaped [E][q][C]; float32 inputs, outputs of the operand type
+// (bfloat16 when bf16 != 0)
+int launch_s2_fwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, void* Z, int bf16,
                   hipStream_t s);
 int launch_s2_bwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* gZ,
-                  float* gU, hipStream_t s);
+                  void* gU, int bf16, hipStream_t s);
 int launch_s2_dbwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* gZ,
-                   const float* pU, float* ggZ, float* gU2, hipStream_t s);
+                   const float* pU, void* ggZ, void* gU2, int bf16, hipStream_t s);
+// o2 = J^T Zb + d/dU <Za, J Ud>, o1 = J^T Za (o1 may be NULL)
+int launch_s2_rev(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* Ud,
+                  const float* Za, const float* Zb, void* o1, void* o2, int bf16, hipStream_t s);
+// caller's degree-major grid tables -> m-major row order
+int launch_s2_mmajor(int L, int M, int ng, const float* G, const float* P, float* Gm, float* Pm, hipStream_t s);
 
 // ---- graph preparation
 size_t graph_ws_bytes(int N, long E);

@@ -1,5 +1,5 @@
 // Spherical-grid SwiGLU activation on edges (SwiGLU-S2): TrimSO(2) page,
-// Table 5 (EquiformerV3's activation), Section 5.1 (its Edge -> Edge
+// Table 2 (EquiformerV3's activation), Appendix C.1 "Implementation" (its Edge -> Edge
 // spherical-grid activation) and Appendix B.4 (G_l evaluates the degree-l
 // basis at n_g grid points; the nonlinearity acts on grid values).
 //
@@ -99,8 +99,8 @@ __device__ __forceinline__ void s2_load(const float* __restrict__ p, size_t stri
 }
 
 // accumulator rows of this lane: r = 16m + 4 (lane / 16) + i
-template <int QR>
-__device__ __forceinline__ void s2_store(float* __restrict__ p, size_t stride, int q, bool ok, const s2f4 (&x)[QR]) {
+template <int QR, typename OT>
+__device__ __forceinline__ void s2_store(OT* __restrict__ p, size_t stride, int q, bool ok, const s2f4 (&x)[QR]) {
   if (!ok) return;
   const int h = (threadIdx.x & 63) >> 4;
 #pragma unroll
@@ -108,7 +108,7 @@ __device__ __forceinline__ void s2_store(float* __restrict__ p, size_t stride, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * m + 4 * h + i;
-      if (r < q) p[(size_t)r * stride] = x[m][i];
+      if (r < q) st(p + (size_t)r * stride, x[m][i]);
     }
 }
 
@@ -137,10 +137,10 @@ __device__ __forceinline__ void s2_grid(const s2f4* __restrict__ tab, int t, int
   }
 }
 
-template <int QR>
+template <int QR, typename OT>
 __global__ __launch_bounds__(kS2Threads) void s2_fwd_kernel(long ncol, int q, int C, int ng, int NT,
                                                            const float* __restrict__ U, const float* __restrict__ G,
-                                                           const float* __restrict__ P, float* __restrict__ Z) {
+                                                           const float* __restrict__ P, OT* __restrict__ Z) {
   extern __shared__ s2f4 s2_lds[];
   s2f4* sGa = s2_lds;
   s2f4* sPb = s2_lds + NT * QR * 64;
@@ -169,11 +169,11 @@ __global__ __launch_bounds__(kS2Threads) void s2_fwd_kernel(long ncol, int q, in
 }
 
 // gU = [G^T (sb SiLU(a)) ; G^T (sb v SiLU'(a))], sb = P^T gZ
-template <int QR>
+template <int QR, typename OT>
 __global__ __launch_bounds__(kS2Threads) void s2_bwd_kernel(long ncol, int q, int C, int ng, int NT,
                                                            const float* __restrict__ U, const float* __restrict__ G,
                                                            const float* __restrict__ P, const float* __restrict__ gZ,
-                                                           float* __restrict__ gU) {
+                                                           OT* __restrict__ gU) {
   extern __shared__ s2f4 s2_lds[];
   s2f4* sGa = s2_lds;
   s2f4* sPa = s2_lds + NT * QR * 64;
@@ -213,12 +213,12 @@ __global__ __launch_bounds__(kS2Threads) void s2_bwd_kernel(long ncol, int q, in
 
 // L = <pU, gU>: ggZ = P (SiLU'(a) ad v + SiLU(a) vd), gU2 = G^T [sb ad SiLU'(a) ;
 // sb (vd SiLU'(a) + ad v SiLU''(a))] with vd = G pU_v, ad = G pU_g, sb = P^T gZ
-template <int QR>
+template <int QR, typename OT>
 __global__ __launch_bounds__(kS2Threads) void s2_dbwd_kernel(long ncol, int q, int C, int ng, int NT,
                                                             const float* __restrict__ U, const float* __restrict__ G,
                                                             const float* __restrict__ P, const float* __restrict__ gZ,
-                                                            const float* __restrict__ pU, float* __restrict__ ggZ,
-                                                            float* __restrict__ gU2) {
+                                                            const float* __restrict__ pU, OT* __restrict__ ggZ,
+                                                            OT* __restrict__ gU2) {
   extern __shared__ s2f4 s2_lds[];
   s2f4* sGa = s2_lds;
   s2f4* sPa = s2_lds + NT * QR * 64;
@@ -280,6 +280,99 @@ __global__ __launch_bounds__(kS2Threads) void s2_dbwd_kernel(long ncol, int q, i
   }
 }
 
+// Reverse pass of the convolution's double backward through the activation,
+// with a = the cotangent of the tangent output Zdot and b = the cotangent of
+// the primal output Z:
+//   o2 = J(U)^T b + d/dU <a, J(U) Ud>     (Ud: the tangent of U)
+//   o1 = J(U)^T a                         (optional)
+// Per grid point, with v, g the value and gate grid values of U, vd, gd those
+// of Ud, sa = P^T a and sb = P^T b:
+//   o2 value half: G^T (sb SiLU(g) + sa gd SiLU'(g))
+//   o2 gate half : G^T (sb v SiLU'(g) + sa (vd SiLU'(g) + gd v SiLU''(g)))
+//   o1           : G^T [sa SiLU(g) ; sa v SiLU'(g)]
+template <int QR, typename OT>
+__global__ __launch_bounds__(kS2Threads) void s2_rev_kernel(long ncol, int q, int C, int ng, int NT,
+                                                           const float* __restrict__ U, const float* __restrict__ G,
+                                                           const float* __restrict__ P, const float* __restrict__ Ud,
+                                                           const float* __restrict__ Za, const float* __restrict__ Zb,
+                                                           OT* __restrict__ o1, OT* __restrict__ o2) {
+  extern __shared__ s2f4 s2_lds[];
+  s2f4* sGa = s2_lds;
+  s2f4* sPa = s2_lds + NT * QR * 64;
+  s2f4* sGb = s2_lds + 2 * NT * QR * 64;
+  s2_build_rows<QR>(sGa, G, q, 1, q, ng, NT);
+  s2_build_rows<QR>(sPa, P, 1, ng, q, ng, NT);
+  s2_build_grid<QR>(sGb, G, q, 1, q, ng, NT);
+  __syncthreads();
+  const bool w1 = o1 != nullptr;
+  const long ncb = (ncol + 15) / 16;
+  for (long cb = (long)blockIdx.x * kS2Waves + threadIdx.x / 64; cb < ncb; cb += (long)gridDim.x * kS2Waves) {
+    const S2Col col = s2_col(cb, ncol, C, q);
+    float uv[4 * QR], ug[4 * QR], dv[4 * QR], dg[4 * QR], za[4 * QR], zb[4 * QR];
+    s2_load<QR>(U + col.o2, 2 * C, q, col.ok, uv);
+    s2_load<QR>(U + col.o2 + C, 2 * C, q, col.ok, ug);
+    s2_load<QR>(Ud + col.o2, 2 * C, q, col.ok, dv);
+    s2_load<QR>(Ud + col.o2 + C, 2 * C, q, col.ok, dg);
+    s2_load<QR>(Za + col.o1, C, q, col.ok, za);
+    s2_load<QR>(Zb + col.o1, C, q, col.ok, zb);
+    s2f4 av[QR], ag[QR], bv[QR], bg[QR];
+#pragma unroll
+    for (int m = 0; m < QR; ++m) av[m] = ag[m] = bv[m] = bg[m] = s2f4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) {
+      const s2f4 v = s2_rows<QR>(sGa, t, uv, s2f4{0.f, 0.f, 0.f, 0.f});
+      const s2f4 g = s2_rows<QR>(sGa, t, ug, s2f4{0.f, 0.f, 0.f, 0.f});
+      const s2f4 vd = s2_rows<QR>(sGa, t, dv, s2f4{0.f, 0.f, 0.f, 0.f});
+      const s2f4 gd = s2_rows<QR>(sGa, t, dg, s2f4{0.f, 0.f, 0.f, 0.f});
+      const s2f4 sa = s2_rows<QR>(sPa, t, za, s2f4{0.f, 0.f, 0.f, 0.f});
+      const s2f4 sb = s2_rows<QR>(sPa, t, zb, s2f4{0.f, 0.f, 0.f, 0.f});
+      s2f4 wv, wg, xv, xg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sg = s2_sigm(g[i]);
+        const float si = g[i] * sg;                                               // SiLU(g)
+        const float ds = sg * (1.f + g[i] * (1.f - sg));                          // SiLU'(g)
+        const float dds = sg * (1.f - sg) * (2.f + g[i] * (1.f - 2.f * sg));      // SiLU''(g)
+        wv[i] = sb[i] * si + sa[i] * gd[i] * ds;
+        wg[i] = sb[i] * v[i] * ds + sa[i] * (vd[i] * ds + gd[i] * v[i] * dds);
+        xv[i] = sa[i] * si;
+        xg[i] = sa[i] * v[i] * ds;
+      }
+      s2_grid<QR>(sGb, t, NT, wv, bv);
+      s2_grid<QR>(sGb, t, NT, wg, bg);
+      if (w1) {
+        s2_grid<QR>(sGb, t, NT, xv, av);
+        s2_grid<QR>(sGb, t, NT, xg, ag);
+      }
+    }
+    s2_store<QR>(o2 + col.o2, 2 * C, q, col.ok, bv);
+    s2_store<QR>(o2 + col.o2 + C, 2 * C, q, col.ok, bg);
+    if (w1) {
+      s2_store<QR>(o1 + col.o2, 2 * C, q, col.ok, av);
+      s2_store<QR>(o1 + col.o2 + C, 2 * C, q, col.ok, ag);
+    }
+  }
+}
+
+// Grid tables of the convolution's activation, from the caller's degree-major
+// retained rows (l = 0..L, m = -min(l,M)..min(l,M)) to the m-major row order
+// of the edge arrays: Gm[g][mm(l,m)] = G[g][dm(l,m)], Pm[mm(l,m)][g] = P[dm(l,m)][g].
+__global__ void s2_mmajor_kernel(int L, int M, int ng, const float* __restrict__ G, const float* __restrict__ P,
+                                 float* __restrict__ Gm, float* __restrict__ Pm) {
+  const int q = q_count(L, M);
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < ng * q; idx += gridDim.x * blockDim.x) {
+    const int g = idx / q, rd = idx - g * q;
+    int l = 0, base = 0;
+    while (rd >= base + 2 * qhalf(l, M) + 1) {
+      base += 2 * qhalf(l, M) + 1;
+      ++l;
+    }
+    const int m = rd - base - qhalf(l, M);
+    const int rm = mm_col(l, m, 0, L, 1);
+    Gm[(size_t)g * q + rm] = G[(size_t)g * q + rd];
+    Pm[(size_t)rm * ng + g] = P[(size_t)rd * ng + g];
+  }
+}
+
 struct S2Launch {
   dim3 grid;
   size_t lds;
@@ -304,40 +397,62 @@ hipError_t s2_allow_lds(K* kernel, size_t lds) {
 
 }  // namespace
 
-#define SO2_S2_LAUNCH(KERNEL, TABLES, ...)                                                              \
+#define SO2_S2_LAUNCH_T(KERNEL, OT, TABLES, ...)                                                       \
   do {                                                                                                  \
     const long ncol_ = E * (long)C;                                                                     \
     const S2Launch L_ = s2_launch(ncol_, q, ng, TABLES);                                                \
     hipError_t st_;                                                                                     \
     if (q <= 16) {                                                                                      \
-      if ((st_ = s2_allow_lds(KERNEL<1>, L_.lds)) != hipSuccess) return st_;                            \
-      hipLaunchKernelGGL((KERNEL<1>), L_.grid, dim3(kS2Threads), L_.lds, s, ncol_, q, C, ng, L_.NT,     \
+      if ((st_ = s2_allow_lds(KERNEL<1, OT>, L_.lds)) != hipSuccess) return st_;                        \
+      hipLaunchKernelGGL((KERNEL<1, OT>), L_.grid, dim3(kS2Threads), L_.lds, s, ncol_, q, C, ng, L_.NT, \
                          __VA_ARGS__);                                                                  \
     } else {                                                                                            \
-      if ((st_ = s2_allow_lds(KERNEL<2>, L_.lds)) != hipSuccess) return st_;                            \
-      hipLaunchKernelGGL((KERNEL<2>), L_.grid, dim3(kS2Threads), L_.lds, s, ncol_, q, C, ng, L_.NT,     \
+      if ((st_ = s2_allow_lds(KERNEL<2, OT>, L_.lds)) != hipSuccess) return st_;                        \
+      hipLaunchKernelGGL((KERNEL<2, OT>), L_.grid, dim3(kS2Threads), L_.lds, s, ncol_, q, C, ng, L_.NT, \
                          __VA_ARGS__);                                                                  \
     }                                                                                                   \
   } while (0)
 
-int launch_s2_fwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, float* Z,
+// outputs of the operand type: float32, or bfloat16 (bf16 != 0)
+int launch_s2_fwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, void* Z, int bf16,
                   hipStream_t s) {
   if (E == 0) return hipSuccess;
-  SO2_S2_LAUNCH(s2_fwd_kernel, 2, U, G, P, Z);
+  if (bf16) SO2_S2_LAUNCH_T(s2_fwd_kernel, bf16s, 2, U, G, P, static_cast<bf16s*>(Z));
+  else SO2_S2_LAUNCH_T(s2_fwd_kernel, float, 2, U, G, P, static_cast<float*>(Z));
   return hipGetLastError();
 }
 
 int launch_s2_bwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* gZ,
-                  float* gU, hipStream_t s) {
+                  void* gU, int bf16, hipStream_t s) {
   if (E == 0) return hipSuccess;
-  SO2_S2_LAUNCH(s2_bwd_kernel, 3, U, G, P, gZ, gU);
+  if (bf16) SO2_S2_LAUNCH_T(s2_bwd_kernel, bf16s, 3, U, G, P, gZ, static_cast<bf16s*>(gU));
+  else SO2_S2_LAUNCH_T(s2_bwd_kernel, float, 3, U, G, P, gZ, static_cast<float*>(gU));
   return hipGetLastError();
 }
 
 int launch_s2_dbwd(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* gZ,
-                   const float* pU, float* ggZ, float* gU2, hipStream_t s) {
+                   const float* pU, void* ggZ, void* gU2, int bf16, hipStream_t s) {
   if (E == 0) return hipSuccess;
-  SO2_S2_LAUNCH(s2_dbwd_kernel, 4, U, G, P, gZ, pU, ggZ, gU2);
+  if (bf16)
+    SO2_S2_LAUNCH_T(s2_dbwd_kernel, bf16s, 4, U, G, P, gZ, pU, static_cast<bf16s*>(ggZ), static_cast<bf16s*>(gU2));
+  else
+    SO2_S2_LAUNCH_T(s2_dbwd_kernel, float, 4, U, G, P, gZ, pU, static_cast<float*>(ggZ), static_cast<float*>(gU2));
+  return hipGetLastError();
+}
+
+int launch_s2_rev(long E, int q, int C, int ng, const float* U, const float* G, const float* P, const float* Ud,
+                  const float* Za, const float* Zb, void* o1, void* o2, int bf16, hipStream_t s) {
+  if (E == 0) return hipSuccess;
+  if (bf16)
+    SO2_S2_LAUNCH_T(s2_rev_kernel, bf16s, 3, U, G, P, Ud, Za, Zb, static_cast<bf16s*>(o1), static_cast<bf16s*>(o2));
+  else
+    SO2_S2_LAUNCH_T(s2_rev_kernel, float, 3, U, G, P, Ud, Za, Zb, static_cast<float*>(o1), static_cast<float*>(o2));
+  return hipGetLastError();
+}
+
+int launch_s2_mmajor(int L, int M, int ng, const float* G, const float* P, float* Gm, float* Pm, hipStream_t s) {
+  const int n = ng * q_count(L, M);
+  hipLaunchKernelGGL(s2_mmajor_kernel, dim3((n + 255) / 256), dim3(256), 0, s, L, M, ng, G, P, Gm, Pm);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ import dataclasses
 
 import torch
 
-from ._binding import SO2_DEBUG_CHECKS, SO2_F32_NATIVE, Cfg, GraphC, check, lib
+from ._binding import SO2_ACT_GATE, SO2_ACT_SWIGLU_S2, SO2_DEBUG_CHECKS, SO2_F32_NATIVE, Cfg, GraphC, check, lib
 
 __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_fwd_noalloc", "so2conv_bwd",
            "so2conv_dbwd",
@@ -22,6 +22,7 @@ __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2con
 
 
 _DTYPES = {"f32": (0, torch.float32), "bf16": (1, torch.bfloat16)}
+_ACTS = {"gate": SO2_ACT_GATE, "swiglu_s2": SO2_ACT_SWIGLU_S2}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -34,7 +35,12 @@ class SO2Config:
     per-edge message weights `env` are [E] (heads = 1: a cutoff envelope) or
     [E, heads] (attention weights per head of channels/heads channels).
     f32_native: float32 per-order products on the float32 matrix cores
-    instead of the default exact bfloat16-piece products."""
+    instead of the default exact bfloat16-piece products.
+    act: the Edge -> Edge activation, "gate" or "swiglu_s2" (the spherical-grid
+    SwiGLU; the first linear then has 2C output channels per retained row,
+    value half first). grid: for "swiglu_s2", the tables (G, P): CUDA float32
+    tensors G [n_grid, q] (the retained basis at the grid points, rows of U in
+    degree-major order) and P [q, n_grid] (the projection back)."""
     lmax: int
     mmax: int
     channels: int
@@ -43,14 +49,38 @@ class SO2Config:
     debug_checks: bool = False
     heads: int = 1
     f32_native: bool = False
+    act: str = "gate"
+    grid: tuple | None = dataclasses.field(default=None, compare=False, repr=False)
 
     def __post_init__(self):
         if self.dtype not in _DTYPES:
             raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
+        if self.act not in _ACTS:
+            raise ValueError(f"act must be one of {sorted(_ACTS)}")
+        if self.act == "swiglu_s2":
+            if self.grid is None:
+                raise ValueError('act="swiglu_s2" needs grid=(G, P)')
+            G, P = self.grid
+            _dev(G, "grid G")
+            if G.dim() != 2 or G.shape[1] != self.q:
+                raise ValueError(f"grid G must be [n_grid, {self.q}]")
+            _dev(P, "grid P", shape=(self.q, G.shape[0]))
+
+    @property
+    def q(self) -> int:
+        L, M = self.lmax, self.mmax
+        return (L + 1) * (2 * M + 1) - M * (M + 1)
+
+    @property
+    def n_grid(self) -> int:
+        return 0 if self.grid is None else int(self.grid[0].shape[0])
 
     def c(self) -> Cfg:
         flags = (SO2_DEBUG_CHECKS if self.debug_checks else 0) | (SO2_F32_NATIVE if self.f32_native else 0)
-        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0], flags, self.heads)
+        G, P = self.grid if self.grid is not None else (None, None)
+        return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0], flags, self.heads,
+                   _ACTS[self.act], self.n_grid, None if G is None else G.data_ptr(),
+                   None if P is None else P.data_ptr())
 
     def env_shape(self, n_edges):
         return (n_edges,) if self.heads == 1 else (n_edges, self.heads)
@@ -66,7 +96,12 @@ class SO2Config:
 
 def weight_shapes(cfg: SO2Config):
     L, M, C = cfg.lmax, cfg.mmax, cfg.channels
-    w1 = [((L + 1) * 2 * C, (L + 1) * C + L * C)] + [((L - m + 1) * 2 * C, 2 * (L - m + 1) * C) for m in range(1, M + 1)]
+    if cfg.act == "swiglu_s2":   # value and gate halves per retained row
+        w1 = [((L + 1) * 2 * C, (L + 1) * 2 * C)] + \
+            [((L - m + 1) * 2 * C, 2 * (L - m + 1) * 2 * C) for m in range(1, M + 1)]
+    else:
+        w1 = [((L + 1) * 2 * C, (L + 1) * C + L * C)] + \
+            [((L - m + 1) * 2 * C, 2 * (L - m + 1) * C) for m in range(1, M + 1)]
     w2 = [((L + 1) * C, (L + 1) * C)] + [((L - m + 1) * C, 2 * (L - m + 1) * C) for m in range(1, M + 1)]
     return w1, w2
 

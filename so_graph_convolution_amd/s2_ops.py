@@ -1,5 +1,5 @@
 """PyTorch-facing calls of the spherical-grid SwiGLU activation on edges (C ABI
-so2s2_*; TrimSO(2) page, Table 5 and Appendix B.4): per edge and channel
+so2s2_*; TrimSO(2) page, Table 2, Appendix C.1 and Appendix B.4): per edge and channel
 z = P (SiLU(G u_g) * (G u_v)), its backward and double backward. Every step
 runs in libso2conv.so; this module checks shapes and passes pointers and the
 stream."""

@@ -58,7 +58,11 @@ def to_dev(d, dtype="f32", validate_graph=True):
         return torch.tensor(np.ascontiguousarray(a), dtype=dt, device=dev)
 
     ft = torch.bfloat16 if dtype == "bf16" else torch.float32
-    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype)
+    grid = None
+    if d.get("grid_G") is not None:   # spherical-grid SwiGLU activation
+        grid = (t(d["grid_G"]), t(d["grid_P"]))
+    kc = K.SO2Config(cfg.lmax, cfg.mmax, cfg.channels, cfg.n_rbf, dtype,
+                     act="swiglu_s2" if grid is not None else "gate", grid=grid)
     g = K.so2conv_graph_prepare(cfg.n_atoms, t(d["src"], torch.int32), t(d["dst"], torch.int32), t(d["shift"]),
                                 validate=validate_graph)
     out = dict(kcfg=kc, g=g, x=t(d["x"], ft), pos=t(d["pos"]), rbf=t(d["rbf"]), w_rad=t(d["w_rad"], ft),

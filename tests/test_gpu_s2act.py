@@ -1,5 +1,5 @@
 """GPU parity of the spherical-grid SwiGLU activation on edges (so2s2_*;
-TrimSO(2) page, Table 5 and Appendix B.4; the reading is stated in
+TrimSO(2) page, Table 2, Appendix C.1 and Appendix B.4; the reading is stated in
 oracle/s2act_oracle.py) against the float64 oracle: forward, backward and
 double backward at small and ragged shapes (column counts that leave a partial
 16-column block, both row-tile variants and their boundary at 16 rows, the

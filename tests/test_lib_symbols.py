@@ -123,3 +123,27 @@ def test_saved_backward_state_bytes():
     assert K.so2conv_saved_bwd_bytes(f32, 1024) == 1024 * 40960
     assert K.so2conv_saved_bwd_bytes(bf16, 1024) == 1024 * 35072
     assert K.so2conv_saved_bwd_bytes(K.SO2Config(4, 5, 128, 64), 10) == 0   # mmax > lmax
+
+
+def test_swiglu_s2_config_host_checks():
+    """The spherical-grid SwiGLU activation widens the first linear's output to
+    2C per retained row; at most 32 retained rows and 1..256 grid points."""
+    import ctypes
+
+    import so_graph_convolution_amd as K
+    from so_graph_convolution_amd._binding import SO2_ACT_SWIGLU_S2, Cfg
+
+    def saved(*fields):
+        return K.lib().so2conv_saved_bytes(ctypes.byref(Cfg(*fields)), 1024)
+    # per edge at lmax 4, C 128 (q = 19): S 5,120 + T 19,456 + U 19,456 + Z 9,728 + V 9,728 bytes
+    assert saved(4, 2, 128, 64, 0, 0, 1, SO2_ACT_SWIGLU_S2, 70) == 1024 * 63488
+    assert saved(4, 2, 128, 64, 0, 0, 1, 0, 0) == 1024 * 55808          # the gate ignores n_grid
+    assert saved(6, 2, 128, 64, 1, 0, 8, SO2_ACT_SWIGLU_S2, 98) > 0      # q = 29, bfloat16, 8 heads
+    assert saved(6, 3, 128, 64, 0, 0, 1, SO2_ACT_SWIGLU_S2, 98) == 0     # q = 37 > 32
+    assert saved(4, 2, 128, 64, 0, 0, 1, SO2_ACT_SWIGLU_S2, 0) == 0      # no grid points
+    assert saved(4, 2, 128, 64, 0, 0, 1, SO2_ACT_SWIGLU_S2, 257) == 0
+    assert saved(4, 2, 128, 64, 0, 0, 1, 2, 70) == 0                     # unknown activation
+    with pytest.raises(ValueError):
+        K.SO2Config(4, 2, 128, 64, act="swiglu_s2")                      # tables missing
+    with pytest.raises(ValueError):
+        K.SO2Config(4, 2, 128, 64, act="relu")

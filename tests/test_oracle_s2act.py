@@ -1,4 +1,4 @@
-"""Pins for the SwiGLU-S2 oracle (TrimSO(2) page, Table 5 and Appendix B.4; the
+"""Pins for the SwiGLU-S2 oracle (TrimSO(2) page, Table 2, Appendix C.1 and Appendix B.4; the
 reading is stated in the oracle's header): a brute-force loop over the
 definition, the identity grid (where it is plain SwiGLU on the coefficients),
 linearity in the value half, a zero gate, a constant gate on an exact
