@@ -73,7 +73,8 @@ def _run(cfg_name, stage, e_end):
         K.so2conv_fwd(*args, saved=None, chunk_edges=ce)
         out = K.so2conv_bwd(*args, None, dd["gy"], need=("w1", "w2", "w_rad"), chunk_edges=ce)
         torch.cuda.synchronize()
-        return {k: out[k] for k in ("gw1", "gw2", "gw_rad")}
+        return {k: (out[k].cpu() if isinstance(out[k], torch.Tensor) else [w.cpu() for w in out[k]])
+                for k in ("gw1", "gw2", "gw_rad")}
     chunk = 262144 if cfg_name == "H" else None
     if chunk:
         wsb = max(K.so2conv_chunked_workspace_bytes(kc, N, E, s, chunk) for s in (0, 1, 2))
