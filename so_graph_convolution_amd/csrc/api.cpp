@@ -661,6 +661,10 @@ int so2::run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStrea
           return e;
         }
       }
+      if (bf && !TA && TB) {   // bfloat16 A.B^T: the direct-to-LDS kernel where its layout takes the operands
+        const int e = gemm_b16_run(b, s);
+        if (e != hipErrorNotSupported) return e;
+      }
       return gemm_run(b, TA, TB, bf, s);
     };
     if (g_prof_on) {

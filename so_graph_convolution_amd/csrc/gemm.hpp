@@ -59,10 +59,14 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s);
 
 // float32 products through bfloat16 pieces (each operand the exact sum of
 // three bfloat16 values; nprod = 6 or 9 piece products per float32 product) on
-// 256 x 256 blocks of four 128 x 128 waves; real problems only, no A^T.B^T.
+// 256 x 256 blocks of eight 128 x 64 waves; real problems only, no A^T.B^T.
 // hipErrorNotSupported (nothing launched) unless every operand is 16-byte
 // aligned with leading dimensions (and a k-major operand's width) multiples of four.
 int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s);
+// bfloat16 A.B^T on the same block structure; hipErrorNotSupported (nothing
+// launched) unless operands are 16-byte aligned, leading dimensions multiples
+// of eight and K even (split chunks multiples of 32).
+int gemm_b16_run(GemmBatch& b, hipStream_t s);
 
 // K tile of the kernels: split chunks of TA problems are multiples of it
 constexpr int kGemmKTile = 64;

@@ -202,6 +202,119 @@ __global__ __launch_bounds__(ZNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// A.B^T with bfloat16 operands, both k-contiguous (the forward products with
+// the transposed weight copy, the data-gradient products), on the same block
+// structure: 256 x 256 blocks of eight 128 x 64 waves at two per SIMD, a
+// four-stage ring of direct-to-LDS tiles. A tile holds 32 k per row as 16
+// dwords (two bfloat16 each), in the float32 kernels' k-contiguous layout; a
+// lane half's eight dwords of a fragment read are its k values of two MFMA
+// steps (4 dwords = 8 k each). A and B fragments take the same dwords, so
+// every k of the tile meets its partner exactly once, whichever lanes carry
+// it.
+__global__ __launch_bounds__(ZNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_b16_kernel(GemmBatch batch) {
+  using DA = DT<true, ZM>;
+  using DB = DT<true, ZN>;
+  constexpr int SL = (DA::NB + DB::NB) / (ZNT / 64);
+  static_assert(SL == 4, "four loads per wave and stage");
+  constexpr int STG = DA::FL + DB::FL;
+  __shared__ __attribute__((aligned(16))) float S[ZST * STG];
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * ZM, n0 = tn * ZN;
+  // k in dwords (pairs of bfloat16); K and the split chunks are even
+  const int kbeg = split * p.k_chunk / 2, kend = min(p.K, split * p.k_chunk + p.k_chunk) / 2;
+  const int nkk = kend - kbeg, nk = (nkk + 15) / 16;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave >> 2, wn = wave & 3, li = lane % 32, lk = lane / 32;
+  DSlot sl[SL];
+#pragma unroll
+  for (int j = 0; j < SL; ++j) {
+    const int g = SL * wave + j;
+    sl[j] = g < DA::NB ? dslot<true, ZM>(g, static_cast<const float*>(p.A), p.lda / 2, m0, p.M, kbeg, lane, 0)
+                       : dslot<true, ZN>(g - DA::NB, static_cast<const float*>(p.B), p.ldb / 2, n0, p.N, kbeg, lane,
+                                         DA::FL);
+  }
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+#pragma unroll
+  for (int t = 0; t < ZST - 1; ++t)
+    if (t < nk) dstage(sl, S + t * STG, t, nkk, lane);
+  const int ra = wm * 128 + li, rb = wn * 64 + li;
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    zsync(min(ZST - 2, nk - 1 - kt));
+    if (kt + ZST - 1 < nk) dstage(sl, S + ((kt + ZST - 1) % ZST) * STG, kt + ZST - 1, nkk, lane);
+    const float* st = S + (kt % ZST) * STG;
+    bf16x8 fb[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float f[8];
+      dfrag<true, ZN>(st + DA::FL, rb + 32 * b, lk, f);
+      fb[b][0] = __builtin_bit_cast(bf16x8, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                                  __float_as_uint(f[2]), __float_as_uint(f[3])});
+      fb[b][1] = __builtin_bit_cast(bf16x8, u32x4{__float_as_uint(f[4]), __float_as_uint(f[5]),
+                                                  __float_as_uint(f[6]), __float_as_uint(f[7])});
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float f[8];
+      dfrag<true, ZM>(st, ra + 32 * a, lk, f);
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                                         __float_as_uint(f[2]), __float_as_uint(f[3])});
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{__float_as_uint(f[4]), __float_as_uint(f[5]),
+                                                         __float_as_uint(f[6]), __float_as_uint(f[7])});
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = mfma(a0, fb[b][0], acc[a][b]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = mfma(a1, fb[b][1], acc[a][b]);
+    }
+  }
+  const int i0 = m0 + wm * 128 + 4 * lk, j0 = n0 + wn * 64 + li;
+  float* out = p.partial ? p.C + (size_t)split * p.M * p.N : p.C;
+  const int ldo = p.partial ? p.N : p.ldc;
+  const bool add = p.accumulate && !p.partial;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int j = j0 + 32 * b;
+      if (j >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 32 * a + 8 * (r / 4) + (r % 4);
+        if (i < p.M) {
+          float* o = out + (size_t)i * ldo + j;
+          *o = add ? *o + acc[a][b][r] : acc[a][b][r];
+        }
+      }
+    }
+}
+
+// bfloat16 operands of the direct-to-LDS A.B^T kernel: 16-byte aligned rows
+// (leading dimensions multiples of eight elements), even K and split chunks
+bool b16_ok(const GemmBatch& b) {
+  for (int q = 0; q < b.nprob; ++q) {
+    const GemmProb& p = b.p[q];
+    if (p.M <= 0 || p.N <= 0) continue;
+    if (p.cplx) return false;
+    if ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) % 16) return false;
+    if (p.lda % 8 || p.ldb % 8 || p.K % 2) return false;
+    if (p.k_splits > 1 && p.k_chunk % 32) return false;
+  }
+  return true;
+}
+
 // operands of the direct-to-LDS layouts: real problems, 16-byte aligned,
 // leading dimensions multiples of four, and a k-major operand a multiple of
 // four wide along its rows (its loads are four-column chunks)
@@ -218,13 +331,8 @@ bool zdma_ok(const GemmBatch& b, bool TA, bool TB) {
   return true;
 }
 
-}  // namespace
-
-// float32 products through bfloat16 pieces; hipErrorNotSupported (nothing
-// launched) for operands the direct-to-LDS layouts do not take, complex
-// problems, or A^T.B^T
-int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s) {
-  if ((TA && TB) || (nprod != 6 && nprod != 9) || !zdma_ok(b, TA, TB)) return hipErrorNotSupported;
+// tile counts of every problem of a batch; the batch's block count
+int z_tiles(GemmBatch& b) {
   int total = 0;
   for (int q = 0; q < b.nprob; ++q) {
     GemmProb& p = b.p[q];
@@ -236,6 +344,27 @@ int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s) {
     if (p.M > 0 && p.N > 0) total += p.tiles_m * p.tiles_n * p.k_splits;
   }
   b.total_tiles = total;
+  return total;
+}
+
+}  // namespace
+
+// bfloat16 A.B^T on the direct-to-LDS block structure; hipErrorNotSupported
+// (nothing launched) for operands its layout does not take
+int gemm_b16_run(GemmBatch& b, hipStream_t s) {
+  if (!b16_ok(b)) return hipErrorNotSupported;
+  const int total = z_tiles(b);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_b16_kernel, dim3(total), dim3(ZNT), 0, s, b);
+  return hipGetLastError();
+}
+
+// float32 products through bfloat16 pieces; hipErrorNotSupported (nothing
+// launched) for operands the direct-to-LDS layouts do not take, complex
+// problems, or A^T.B^T
+int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s) {
+  if ((TA && TB) || (nprod != 6 && nprod != 9) || !zdma_ok(b, TA, TB)) return hipErrorNotSupported;
+  const int total = z_tiles(b);
   if (total == 0) return hipSuccess;
   const dim3 grid(total), block(ZNT);
   if (nprod == 6) {
