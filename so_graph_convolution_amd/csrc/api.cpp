@@ -635,7 +635,7 @@ constexpr int kSplitProducts = 6;   // bf16 piece products per float32 product o
 
 }  // namespace
 
-int so2::run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s) {
+int so2::run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s, const GateCols* gate) {
   if (ps.empty()) return SO2_OK;
   const bool bf = op == kOpBF16;
   const double es = bf ? 2.0 : 4.0;
@@ -643,6 +643,12 @@ int so2::run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStrea
   while (i < ps.size()) {
     GemmBatch b{};
     b.nprob = 0;
+    if (gate) {
+      b.gC = gate->C;
+      b.gL = gate->L;
+      b.ldz = gate->ldz;
+      b.ldgam = gate->ldgam;
+    }
     double flops = 0, bytes = 0;
     while (i < ps.size() && b.nprob < kGemmMaxProbs) {
       const GemmProb& q = ps[i];
@@ -665,21 +671,29 @@ int so2::run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStrea
         const int e = gemm_b16_run(b, s);
         if (e != hipErrorNotSupported) return e;
       }
-      return gemm_run(b, TA, TB, bf, s);
+      return gemm_run(b, TA, TB, bf, s);   // hipErrorNotSupported for gated problems
     };
     if (g_prof_on) {
       ProfRec r{0, flops, bytes, nullptr, nullptr};
       SO2_HIP(hipEventCreate(&r.a));
       SO2_HIP(hipEventCreate(&r.b));
       SO2_HIP(hipEventRecord(r.a, s));
-      SO2_HIP(launch());
+      const int e = launch();
+      if (gate && e == hipErrorNotSupported) {   // nothing ran: the caller takes the ungated products
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+        return kNoFusedGate;
+      }
+      SO2_HIP(e);
       SO2_HIP(hipEventRecord(r.b, s));
       r.kind = split ? (TA ? 10 : (TB ? 9 : 8))
                      : (ps[0].cplx ? (TA ? 7 : (TB ? 6 : 5)) : (bf ? (TA ? 4 : 3) : (TA ? 2 : (TB ? 1 : 0))));
       std::lock_guard<std::mutex> lk(g_prof_mu);
       g_prof.push_back(r);
     } else {
-      SO2_HIP(launch());
+      const int e = launch();
+      if (gate && e == hipErrorNotSupported) return kNoFusedGate;
+      SO2_HIP(e);
     }
   }
   return SO2_OK;
@@ -876,6 +890,52 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
   int rr = run_batch(ps, false, (transposed && !use_wt) || c.bf, op, s);
   if (rr) return rr;
   return run_batch(pc, false, transposed, op, s);
+}
+
+// The first linear's forward over the chunk of n edges at e0 with the gate in
+// the products' epilogue: the gate columns of order 0 first, then every other
+// product of the first linear writes its output U and the gated Z together
+// (degree 0: SiLU(u); degree l >= 1: sigmoid(gamma_l) u, gamma_l read from
+// the row's gate columns). Runs on the float32 path through bfloat16 pieces
+// and on bfloat16 calls; kNoFusedGate where those kernels do not take the
+// operands (the caller then runs the products and the gate kernel).
+int run_lin_gated(const Ctx& c, const void* A, float* U, void* Z, const WSet& w, long e0, int n, hipStream_t s) {
+  const Dims& d = c.d;
+  if (d.s2 || !(c.split || c.bf)) return kNoFusedGate;
+  const int win = d.wT(), wout = d.wU(), wz = d.wZ(), L = d.L, C = d.C;
+  const int op = c.bf ? kOpBF16 : kOpSplit;
+  std::vector<GemmProb> pg, pu;   // gate columns; gated products
+  for (size_t sy = 0; sy < w.W.size(); ++sy) {
+    const long lo = std::max(w.e[sy], e0), hi = std::min(w.e[sy + 1], e0 + n);
+    if (hi <= lo) continue;
+    const long r0 = lo - e0;
+    const int rows = (int)(hi - lo);
+    const Lin& W = w.W[sy];
+    const void* Ar = offs(A, (size_t)r0 * win, c.es);
+    float* Ur = U + (size_t)r0 * wout;
+    void* Zr = offs(Z, (size_t)r0 * wz, c.es);
+    for (int a = 0; a <= d.M; ++a) {
+      int r, cc;
+      long off;
+      realified_shape(d, 0, a, &r, &cc, &off);
+      const long ib = mm_block(a, L, d.Ci()), ob = d.u_block(a);
+      const int nu = a == 0 ? (L + 1) * C : cc;   // the block's gated columns
+      // weights as B: W [r][cc] (float32, A.B) or its transpose [cc][r] (bfloat16, A.B^T)
+      auto wcols = [&](long col) { return c.bf ? offs(W.WT, off + col * r, c.es) : offs(W.W, off + col, c.es); };
+      const int ldb = c.bf ? r : cc;
+      if (a == 0 && L > 0)
+        pg.push_back(prob(offs(Ar, ib, c.es), win, wcols((long)(L + 1) * C), ldb, Ur + (L + 1) * C, wout, rows, L * C, r));
+      GemmProb q = prob(offs(Ar, ib, c.es), win, wcols(0), ldb, Ur + ob, wout, rows, nu, r);
+      q.gate = a + 1;
+      q.Z = offs(Zr, mm_block(a, L, C), c.es);
+      q.gam = Ur + (L + 1) * C;
+      pu.push_back(q);
+    }
+  }
+  int rr;
+  if ((rr = run_batch(pg, false, c.bf, op, s))) return rr;
+  const GateCols gcols{C, L, wz, wout};
+  return run_batch(pu, false, c.bf, op, s, &gcols);
 }
 
 // weight gradient of linear `second` per system (realified, float32) over the
@@ -1152,8 +1212,12 @@ int forward_chunk(const Ctx& c, const ActTab& at, const GraphDev& g, const float
   int r;
   if ((r = radial(c, ec, rbf + (size_t)g.e0 * c.n_rbf, w_rad, p.S, s))) return r;
   SO2_HIP(launch_edge_fwd(c.d, g, x, pos, p.S, p.T, c.bf, s));
-  if ((r = run_lin(c, 0, false, p.T, p.U, W1, g.e0, ec, 1, 0, s))) return r;
-  if ((r = act_fwd(c, at, ec, p.U, p.Z, s))) return r;
+  r = run_lin_gated(c, p.T, p.U, p.Z, W1, g.e0, ec, s);   // the gate in the first linear's epilogue
+  if (r == kNoFusedGate) {
+    if ((r = run_lin(c, 0, false, p.T, p.U, W1, g.e0, ec, 1, 0, s))) return r;
+    r = act_fwd(c, at, ec, p.U, p.Z, s);
+  }
+  if (r) return r;
   return run_lin(c, 1, false, p.Z, p.V, W2, g.e0, ec, 1, 0, s);
 }
 

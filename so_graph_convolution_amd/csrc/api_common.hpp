@@ -49,9 +49,18 @@ GemmProb prob(const void* A, int lda, const void* B, int ldb, float* C, int ldc,
 // run on the float32 matrix cores).
 enum { kOpF32 = 0, kOpBF16 = 1, kOpSplit = 2 };
 
+// Batch-wide fields of the gated epilogue (GemmBatch::gC, gL, ldz, ldgam)
+struct GateCols {
+  int C, L, ldz, ldgam;
+};
+// run_batch's return when gated problems reach a launch whose kernels have no
+// gated epilogue (nothing of that launch ran; the caller falls back)
+constexpr int kNoFusedGate = 1;
+
 // launch the problems (all with the same TA, TB and operand kind), several per
-// launch; records their timing when GEMM profiling is on
-int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s);
+// launch; records their timing when GEMM profiling is on. With `gate`, the
+// problems carry the gated epilogue.
+int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s, const GateCols* gate = nullptr);
 
 // splits and K chunk of a split-K product over K rows (a multiple of the GEMM K
 // tile); run_tn's partial buffer holds sum over segments of splits * M * N floats

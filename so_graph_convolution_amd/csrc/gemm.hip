@@ -810,6 +810,8 @@ bool dma_ok(const GemmBatch& b, bool TA, bool TB) {
 
 int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s) {
   constexpr int BK = BK_TILE;
+  for (int q = 0; q < b.nprob; ++q)
+    if (b.p[q].gate) return hipErrorNotSupported;   // the gated epilogue lives in the split and bf16 A.B^T kernels
   const bool cx = b.nprob > 0 && b.p[0].cplx;
   if (bf16 && TA == TB) return hipErrorInvalidValue;
   if (cx && (bf16 || (TA && TB))) return hipErrorInvalidValue;

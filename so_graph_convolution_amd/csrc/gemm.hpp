@@ -44,13 +44,25 @@ struct GemmProb {
   int cplx;          // complex problem (all problems of a launch agree)
   int dA, dB;        // complex: element offsets of b from a and of d from c
   float sA, sB;      // complex: signs of b and d (+1 or -1)
+  // gated epilogue (0: none; a + 1: the first linear's output block of order
+  // a): besides C it writes Z = the gated activation of C, reading the gate
+  // pre-activations of each row from gam (see GemmBatch)
+  int gate;
+  void* Z;           // Z block of this problem (row pitch GemmBatch::ldz)
+  const float* gam;  // gate columns (l = 1..L, c) of this problem's first row (row pitch GemmBatch::ldgam)
 };
 
 struct GemmBatch {
   GemmProb p[kGemmMaxProbs];
   int nprob;
   int total_tiles;
+  // gated epilogue, shared by the batch: channels C, degree L, row pitches of
+  // Z and of the gate columns. Column j of block a holds degree
+  // l = a + (j mod (L - a + 1) C) / C and channel j mod C; l = 0 takes
+  // SiLU(u), l >= 1 takes sigmoid(gam[(l - 1) C + c]) u.
+  int gC, gL, ldz, ldgam;
 };
+static_assert(sizeof(GemmBatch) <= 4096, "a GemmBatch is passed as one kernel argument (4 KB at most)");
 
 // Fill tiling fields and launch. Every problem of one batch shares TA/TB and
 // the operand type. Returns a hipError_t (hipErrorInvalidValue for a bfloat16
@@ -67,6 +79,8 @@ int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s);
 // launched) unless operands are 16-byte aligned, leading dimensions multiples
 // of eight and K even (split chunks multiples of 32).
 int gemm_b16_run(GemmBatch& b, hipStream_t s);
+// Gated problems (GemmProb::gate) run only on gemm_x3_run (Z float32) and
+// gemm_b16_run (Z bfloat16); gemm_run does not take them.
 
 // K tile of the kernels: split chunks of TA problems are multiples of it
 constexpr int kGemmKTile = 64;

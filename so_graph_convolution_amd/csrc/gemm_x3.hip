@@ -26,6 +26,7 @@
 #include "gemm.hpp"
 #include "gemm_dma.hpp"
 #include "gemm_tile.hpp"
+#include "numeric.hpp"
 
 namespace so2 {
 
@@ -91,6 +92,38 @@ __device__ __forceinline__ void row_products(const Pieces& a, const Pieces (&b)[
   for (int j = 0; j < 2; ++j) acc[j] = mfma(a.m, b[j].h, acc[j]);
 #pragma unroll
   for (int j = 0; j < 2; ++j) acc[j] = mfma(a.h, b[j].h, acc[j]);
+}
+
+__device__ __forceinline__ float zsig(float v) { return 1.f / (1.f + __expf(-v)); }
+
+// Gated epilogue of the first linear (GemmProb::gate): C = u as usual and
+// Z = SiLU(u) (degree 0) or sigmoid(gamma) u, gamma the row's gate column of
+// the element's degree and channel. Lane (li, lk) of MFMA tile (a, b) holds
+// column 32 b + li and rows 32 a + 8 g + 4 lk + i of the wave's 128 x 64 tile.
+template <typename ZT>
+__device__ __forceinline__ void gated_store(const GemmBatch& batch, const GemmProb& p, const floatx16 (&acc)[4][2],
+                                            int i0, int j0) {
+  const int C = batch.gC, ga = p.gate - 1, hwid = (batch.gL - ga + 1) * C;
+  ZT* Zo = static_cast<ZT*>(p.Z);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int j = j0 + 32 * b;
+    if (j >= p.N) continue;
+    const int l = ga + (j % hwid) / C, c = j % C;
+    const float* g = p.gam + (l > 0 ? (l - 1) * C + c : 0);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 32 * a + 8 * (r / 4) + (r % 4);
+        if (i < p.M) {
+          const float u = acc[a][b][r];
+          p.C[(size_t)i * p.ldc + j] = u;
+          const float z = l == 0 ? u * zsig(u) : zsig(g[(size_t)i * batch.ldgam]) * u;
+          st(Zo + (size_t)i * batch.ldz + j, z);
+        }
+      }
+  }
 }
 
 // wait until this wave's loads of the tile to be read have landed (`ahead`
@@ -171,6 +204,10 @@ __global__ __launch_bounds__(ZNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // epilogue: lane (li, lk) of MFMA tile (a, b) holds column 32 b + li, rows
   // 32 a + 8 g + 4 lk + i (g, i < 4) of the wave's 128 x 64 tile
   const int i0 = m0 + wm * 128 + 4 * lk, j0 = n0 + wn * 64 + li;
+  if (p.gate) {
+    gated_store<float>(batch, p, acc, i0, j0);
+    return;
+  }
   if (p.partial || !p.accumulate) {
     float* out = p.partial ? p.C + (size_t)split * p.M * p.N : p.C;
     const int ldo = p.partial ? p.N : p.ldc;
@@ -281,6 +318,10 @@ __global__ __launch_bounds__(ZNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   const int i0 = m0 + wm * 128 + 4 * lk, j0 = n0 + wn * 64 + li;
+  if (p.gate) {
+    gated_store<bf16s>(batch, p, acc, i0, j0);
+    return;
+  }
   float* out = p.partial ? p.C + (size_t)split * p.M * p.N : p.C;
   const int ldo = p.partial ? p.N : p.ldc;
   const bool add = p.accumulate && !p.partial;
@@ -311,6 +352,7 @@ bool b16_ok(const GemmBatch& b) {
     if ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) % 16) return false;
     if (p.lda % 8 || p.ldb % 8 || p.K % 2) return false;
     if (p.k_splits > 1 && p.k_chunk % 32) return false;
+    if (p.gate && (p.k_splits > 1 || p.partial || p.accumulate)) return false;
   }
   return true;
 }
@@ -327,6 +369,7 @@ bool zdma_ok(const GemmBatch& b, bool TA, bool TB) {
     if (p.lda % 4 || p.ldb % 4) return false;
     if ((TA && p.M % 4) || (!TB && p.N % 4)) return false;
     if (p.k_splits > 1 && p.k_chunk % 16) return false;
+    if (p.gate && (p.k_splits > 1 || p.partial || p.accumulate)) return false;
   }
   return true;
 }
