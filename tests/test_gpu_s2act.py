@@ -74,8 +74,8 @@ def test_grid_activation_single_outputs_and_no_edges():
 
 def test_grid_activation_full_size_sampled():
     """High-degree size (1,045,678 edges, 29 rows of lmax 6 / mmax 2, C = 128,
-    100 grid points) as the benchmark runs it; 48 sampled edges against the
-    oracle."""
+    100 grid points) as the benchmark runs it: forward, backward and both
+    double-backward outputs on 48 sampled edges against the oracle."""
     import so_graph_convolution_amd as K
     E, q, C, ng = 1045678, 29, 128, 100
     gen = torch.Generator(device="cuda").manual_seed(0)
@@ -85,12 +85,22 @@ def test_grid_activation_full_size_sampled():
     P = torch.randn(q, ng, device="cuda", generator=gen) / ng ** 0.5
     cfg = K.S2Config(q, C, ng)
     H.note(f"[s2act full] E={E} rows={q} C={C} n_grid={ng}")
+    idx = torch.tensor(np.random.default_rng(1).choice(E, 48, replace=False)).cuda()
+    Us, gZs = U[idx].double().cpu(), gZ[idx].double().cpu()
+    Gd, Pd = G.double().cpu(), P.double().cpu()
     Z = K.so2s2_fwd(cfg, U, G, P)
+    torch.cuda.synchronize()
+    errs = {"Z": H.relerr(Z[idx], SO.forward(Us, Gd, Pd))}
+    del Z
     gU = K.so2s2_bwd(cfg, U, G, P, gZ)
     torch.cuda.synchronize()
-    idx = torch.tensor(np.random.default_rng(1).choice(E, 48, replace=False))
-    Us, gZs = U[idx.cuda()].double().cpu(), gZ[idx.cuda()].double().cpu()
-    Gd, Pd = G.double().cpu(), P.double().cpu()
-    errs = {"Z": H.relerr(Z[idx.cuda()], SO.forward(Us, Gd, Pd)), "gU": H.relerr(gU[idx.cuda()], SO.backward(Us, Gd, Pd, gZs))}
+    errs["gU"] = H.relerr(gU[idx], SO.backward(Us, Gd, Pd, gZs))
+    del gU
+    pU = torch.randn(E, q, 2 * C, device="cuda", generator=gen)
+    dd = K.so2s2_dbwd(cfg, U, G, P, gZ, pU)
+    torch.cuda.synchronize()
+    rd = SO.double_backward(Us, Gd, Pd, gZs, pU[idx].double().cpu())
+    errs["ggZ"] = H.relerr(dd["ggZ"][idx], rd["ggZ"])
+    errs["gU2"] = H.relerr(dd["gU2"][idx], rd["gU2"])
     H.note("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     assert all(v <= H.TOL_F32 for v in errs.values()), errs
