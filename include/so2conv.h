@@ -121,9 +121,11 @@ enum {
  *     -min(l,M)..min(l,M)). q <= 32 and n_grid in [1, 256] (else
  *     SO2_EUNSUPPORTED); the compute calls return SO2_EINVAL for NULL tables.
  *     G and P are constants: no gradients are formed for them. The grid
- *     products run on the float32 matrix cores with float32 operands (also
- *     for SO2_BF16 calls, whose first-linear outputs are float32); z is
- *     stored in the operand type of the second linear.
+ *     products take float32 operands on the float32 matrix cores in SO2_F32
+ *     calls, and bfloat16 operands (the float32 rows, the tables and the
+ *     grid values rounded to nearest even) with float32 accumulation in
+ *     SO2_BF16 calls; the nonlinearity is float32 in both, and z is stored
+ *     in the operand type of the second linear.
  *   The size queries read only act and n_grid. The mixture entry points
  *   (so2mole_*) take SO2_ACT_GATE only. */
 enum { SO2_ACT_GATE = 0, SO2_ACT_SWIGLU_S2 = 1 };
