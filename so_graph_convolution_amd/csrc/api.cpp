@@ -671,6 +671,10 @@ int so2::run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStrea
         const int e = gemm_b16_run(b, s);
         if (e != hipErrorNotSupported) return e;
       }
+      if (bf && TA && !TB) {   // bfloat16 A^T.B (weight gradients): register-staged transposed tiles
+        const int e = gemm_b16t_run(b, s);
+        if (e != hipErrorNotSupported) return e;
+      }
       return gemm_run(b, TA, TB, bf, s);   // hipErrorNotSupported for gated problems
     };
     if (g_prof_on) {

@@ -79,6 +79,11 @@ int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s);
 // launched) unless operands are 16-byte aligned, leading dimensions multiples
 // of eight and K even (split chunks multiples of 32).
 int gemm_b16_run(GemmBatch& b, hipStream_t s);
+// bfloat16 A^T.B (both operands k-major) on 256 x 256 blocks of eight 128 x 64
+// waves with register-staged, transposed tiles; hipErrorNotSupported (nothing
+// launched) unless rows are 16-byte aligned, M, N and leading dimensions
+// multiples of eight and split chunks multiples of 64.
+int gemm_b16t_run(GemmBatch& b, hipStream_t s);
 // Gated problems (GemmProb::gate) run only on gemm_x3_run (Z float32) and
 // gemm_b16_run (Z bfloat16); gemm_run does not take them.
 

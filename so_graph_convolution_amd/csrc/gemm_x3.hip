@@ -342,6 +342,125 @@ __global__ __launch_bounds__(ZNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// A^T.B with bfloat16 operands, both k-major (the weight gradients: A [K][M],
+// B [K][N], K = edges), on 256 x 256 blocks of eight 128 x 64 waves. A k tile
+// of 64 arrives through registers: each thread loads an 8 (k) x 8 (columns)
+// block of one operand as eight 16-byte rows, transposes it with byte
+// permutes (one per output dword) and writes eight 16-byte k-runs, one per
+// column, into a k-contiguous LDS tile (128 bytes per column, 16-byte units
+// swizzled by (row ^ row / 8) mod 8 so that a fragment read and the 16
+// lanes of a quarter-wave fall on distinct bank groups). Two stages: the
+// next tile's loads are in flight while the current one is multiplied.
+constexpr int TK = 64;   // k per tile
+__device__ __forceinline__ int t_unit(int row, int u) { return row * 8 + (u ^ ((row ^ (row >> 3)) & 7)); }
+
+__global__ __launch_bounds__(ZNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_b16t_kernel(GemmBatch batch) {
+  __shared__ __attribute__((aligned(16))) u32x4 T[2][512 * 8];   // [stage][row (A 0..255, B 256..511)][unit]
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * ZM, n0 = tn * ZN;
+  const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
+  const int nk = (kend - kbeg + TK - 1) / TK;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave >> 2, wn = wave & 3, li = lane % 32, lk = lane / 32;
+  // staging role: operand, k block (8 k) and column block (8 columns)
+  const int op = threadIdx.x >> 8, idx = threadIdx.x & 255, kb = idx >> 5, cb = idx & 31;
+  const unsigned short* src = static_cast<const unsigned short*>(op ? p.B : p.A);
+  const int ld = op ? p.ldb : p.lda, lim = op ? p.N : p.M;
+  const int col = (op ? n0 : m0) + 8 * cb;
+  const bool colok = col < lim;   // widths are multiples of eight: a column block is all in or all out
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  u32x4 rg[8];
+  auto load = [&](int t) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int k = kbeg + t * TK + kb * 8 + kk;
+      rg[kk] = (colok && k < kend) ? *reinterpret_cast<const u32x4*>(src + (size_t)k * ld + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int stg) {
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+      const unsigned sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 o;
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) o[kp] = __builtin_amdgcn_perm(rg[2 * kp + 1][mm >> 1], rg[2 * kp][mm >> 1], sel);
+      T[stg][t_unit(256 * op + 8 * cb + mm, kb)] = o;
+    }
+  };
+  if (nk > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  const int ra = wm * 128 + li, rb = 256 + wn * 64 + li;
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load(kt + 1);
+    const u32x4* st = T[kt & 1];
+#pragma unroll
+    for (int sq = 0; sq < TK / 16; ++sq) {
+      const int u = 2 * sq + lk;
+      bf16x8 fb[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) fb[b] = __builtin_bit_cast(bf16x8, st[t_unit(rb + 32 * b, u)]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const bf16x8 fa = __builtin_bit_cast(bf16x8, st[t_unit(ra + 32 * a, u)]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma(fa, fb[b], acc[a][b]);
+      }
+    }
+    if (kt + 1 < nk) store((kt + 1) & 1);
+    __syncthreads();
+  }
+  const int i0 = m0 + wm * 128 + 4 * lk, j0 = n0 + wn * 64 + li;
+  float* out = p.partial ? p.C + (size_t)split * p.M * p.N : p.C;
+  const int ldo = p.partial ? p.N : p.ldc;
+  const bool add = p.accumulate && !p.partial;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int j = j0 + 32 * b;
+      if (j >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 32 * a + 8 * (r / 4) + (r % 4);
+        if (i < p.M) {
+          float* o = out + (size_t)i * ldo + j;
+          *o = add ? *o + acc[a][b][r] : acc[a][b][r];
+        }
+      }
+    }
+}
+
+// bfloat16 k-major operands of the A^T.B kernel: 16-byte aligned rows and
+// column blocks (leading dimensions, M and N multiples of eight), split
+// chunks multiples of the k tile
+bool b16t_ok(const GemmBatch& b) {
+  for (int q = 0; q < b.nprob; ++q) {
+    const GemmProb& p = b.p[q];
+    if (p.M <= 0 || p.N <= 0) continue;
+    if (p.cplx || p.gate) return false;
+    if ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) % 16) return false;
+    if (p.lda % 8 || p.ldb % 8 || p.M % 8 || p.N % 8) return false;
+    if (p.k_splits > 1 && p.k_chunk % TK) return false;
+  }
+  return true;
+}
+
 // bfloat16 operands of the direct-to-LDS A.B^T kernel: 16-byte aligned rows
 // (leading dimensions multiples of eight elements), even K and split chunks
 bool b16_ok(const GemmBatch& b) {
@@ -391,6 +510,16 @@ int z_tiles(GemmBatch& b) {
 }
 
 }  // namespace
+
+// bfloat16 A^T.B with register-staged transposed tiles; hipErrorNotSupported
+// (nothing launched) for operands its layout does not take
+int gemm_b16t_run(GemmBatch& b, hipStream_t s) {
+  if (!b16t_ok(b)) return hipErrorNotSupported;
+  const int total = z_tiles(b);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_b16t_kernel, dim3(total), dim3(ZNT), 0, s, b);
+  return hipGetLastError();
+}
 
 // bfloat16 A.B^T on the direct-to-LDS block structure; hipErrorNotSupported
 // (nothing launched) for operands its layout does not take

@@ -16,7 +16,10 @@ Cases, each in the launch configuration bench.py times for its workload:
     with >= 100,000 incoming edges;
   * high-degree system (lmax 6, bf16), backward and double backward on a
     >= 100,000-edge receiver block;
-  * large clustered system (C 256, bf16), backward on a >= 65,536-edge block.
+  * large clustered system (C 256, bf16), backward on a >= 65,536-edge block;
+  * the mixture of 64 linear experts on the medium system split into 16
+    systems, backward on the first two systems' edges: expert, radial and
+    coefficient gradients.
 """
 import functools
 import os
@@ -98,11 +101,42 @@ def _run(cfg_name, stage, e_end):
     return res
 
 
+def _run_mole(cfg_name, e_end, n_sys):
+    """Expert, radial and coefficient gradients of the mixture as bench.py --op
+    mole runs it (saved forward state, one workspace), on the first n_sys
+    systems' edges."""
+    import so_graph_convolution_amd as K
+    d = _block(_inputs(cfg_name), e_end)
+    _, mb = FX.mole_block(_inputs(cfg_name), n_sys)
+    dd = H.to_dev(d)
+    kc, N, E = dd["kcfg"], so2_synth.CONFIGS[cfg_name].n_atoms, e_end
+    H.note(f"[weight grads] {cfg_name} mixture bwd over {E} edges, {n_sys} systems, {FX.MOLE_EXPERTS} experts")
+    w1e = [torch.tensor(w, device="cuda") for w in mb["w1e"]]
+    w2e = [torch.tensor(w, device="cuda") for w in mb["w2e"]]
+    coef = torch.tensor(mb["coef"], device="cuda")
+    mix = K.Mixture(FX.MOLE_EXPERTS, mb["sys_edge_ptr"])
+    args = (kc, dd["g"], mix, dd["x"], dd["pos"], dd["rbf"], dd["w_rad"], w1e, w2e, coef)
+    saved = torch.empty(K.so2conv_saved_bytes(kc, E), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(K.so2mole_workspace_bytes(kc, mix, N, E, s, 0) for s in (0, 1)), dtype=torch.uint8,
+                     device="cuda")
+    K.so2mole_fwd(*args, saved=saved, ws=ws)
+    bw = K.so2mole_bwd(*args, saved, dd["gy"], ws=ws)
+    torch.cuda.synchronize()
+    res = {"gw1e": [w.cpu() for w in bw["gw1e"]], "gw2e": [w.cpu() for w in bw["gw2e"]],
+           "gw_rad": bw["gw_rad"].cpu(), "gcoef": bw["gcoef"].cpu()}
+    del saved, ws, bw
+    torch.cuda.empty_cache()
+    return res
+
+
 def _compare(name):
     fx = _fixture(name)
     cfg_name, stage = str(fx["config"]), str(fx["stage"])
     e_end = int(fx["edge_end"])
-    got = _run(cfg_name, stage, e_end)
+    if stage == "mole_bwd":
+        got = _run_mole(cfg_name, e_end, FX.FIXTURES[name][2])
+    else:
+        got = _run(cfg_name, stage, e_end)
     dtype = so2_synth.CONFIGS[cfg_name].dtype
     tol = H.TOL_BF16 if dtype == "bf16" else H.TOL_F32
     tol_elem = H.TOL_ELEM_BF16 if dtype == "bf16" else H.TOL_ELEM_F32
@@ -153,3 +187,8 @@ def test_high_degree_double_backward_receiver_block():
 @pytest.mark.timeout(600)
 def test_large_backward_receiver_block():
     _compare("X_bwd_block")
+
+
+@pytest.mark.timeout(300)
+def test_mixture_backward_two_systems():
+    _compare("M_mole_bwd_block")
