@@ -99,7 +99,18 @@ enum {
    * product; the three dropped ones sum to below 2^-23 of it). Both give
    * float32-accurate products; the default is faster on gfx950, whose
    * bfloat16 matrix rate is sixteen times its float32 one. */
-  SO2_F32_NATIVE = 4
+  SO2_F32_NATIVE = 4,
+  /* Gate the first linear's forward products in their epilogue (TrimSO(2)
+   * page, Section 3.2 "Recombination with activation"): the gate columns
+   * run first, then every other first-linear product writes U and the
+   * gated Z together, instead of a separate gate pass over U. Float32 calls
+   * through bfloat16 pieces and bfloat16 calls with the gated activation;
+   * otherwise ignored. Results are bitwise those without the flag. Off by
+   * default: measured on MI355X it is slower (medium workload 438 against
+   * 435 ms per step, high-degree 537 against 528), the per-element gate
+   * reads and sigmoids in the epilogue costing more than the pass over U
+   * they replace. */
+  SO2_FUSED_GATE = 8
 };
 
 /* cfg->act: the Edge -> Edge activation between the two SO(2) linears

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libso2conv.so")
 SO2_OK, SO2_EINVAL, SO2_EUNSUPPORTED, SO2_EWORKSPACE, SO2_EHIP, SO2_EDEVICE = 0, -1, -2, -3, -4, -5
 SO2_DEBUG_CHECKS = 2
 SO2_F32_NATIVE = 4
+SO2_FUSED_GATE = 8
 SO2_ACT_GATE = 0
 SO2_ACT_SWIGLU_S2 = 1
 

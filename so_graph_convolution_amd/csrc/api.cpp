@@ -120,6 +120,7 @@ struct Ctx {
   int es;    // bytes per GEMM-operand element
   int debug; // SO2_DEBUG_CHECKS
   int split = 0; // float32 products through bfloat16 pieces (float32 calls without SO2_F32_NATIVE)
+  int fused_gate = 0; // SO2_FUSED_GATE
   int ns = 1; // weight sets: one per system (the plain operator has one)
   int nk = 0; // experts of a mixture (0: plain operator)
   int ng = 0; // spherical-grid activation: grid points, and the caller's tables (degree-major rows)
@@ -139,7 +140,7 @@ int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
   if (cfg->n_rbf < 4 || cfg->n_rbf % 4 || cfg->n_rbf > 1024)
     return fail(SO2_EUNSUPPORTED, "n_rbf must be a multiple of 4 in [4, 1024]");
   if (cfg->dtype != SO2_F32 && cfg->dtype != SO2_BF16) return fail(SO2_EUNSUPPORTED, "dtype must be SO2_F32 or SO2_BF16");
-  if (cfg->flags & ~(SO2_DEBUG_CHECKS | SO2_F32_NATIVE)) return fail(SO2_EINVAL, "unknown cfg flags");
+  if (cfg->flags & ~(SO2_DEBUG_CHECKS | SO2_F32_NATIVE | SO2_FUSED_GATE)) return fail(SO2_EINVAL, "unknown cfg flags");
   const int H = cfg->heads == 0 ? 1 : cfg->heads;
   if (H < 1 || H > kMaxHeads || C % H) return fail(SO2_EUNSUPPORTED, "heads must divide channels, at most 16");
   if (H > 1 && (C / H) % 64 && C / H != 16 && C / H != 32)
@@ -153,6 +154,7 @@ int check_cfg(const so2conv_cfg* cfg, Ctx* c) {
   c->bf = cfg->dtype == SO2_BF16;
   c->es = c->bf ? 2 : 4;
   c->split = !c->bf && !(cfg->flags & SO2_F32_NATIVE);
+  c->fused_gate = (cfg->flags & SO2_FUSED_GATE) != 0;
   if (cfg->act != SO2_ACT_GATE && cfg->act != SO2_ACT_SWIGLU_S2) return fail(SO2_EINVAL, "unknown activation");
   c->d.s2 = cfg->act == SO2_ACT_SWIGLU_S2;
   if (c->d.s2) {
@@ -897,15 +899,16 @@ int run_lin(const Ctx& c, int second, bool transposed, const void* A, float* C, 
 }
 
 // The first linear's forward over the chunk of n edges at e0 with the gate in
-// the products' epilogue: the gate columns of order 0 first, then every other
-// product of the first linear writes its output U and the gated Z together
-// (degree 0: SiLU(u); degree l >= 1: sigmoid(gamma_l) u, gamma_l read from
-// the row's gate columns). Runs on the float32 path through bfloat16 pieces
-// and on bfloat16 calls; kNoFusedGate where those kernels do not take the
-// operands (the caller then runs the products and the gate kernel).
+// the products' epilogue (SO2_FUSED_GATE): the gate columns of order 0 first,
+// then every other product of the first linear writes its output U and the
+// gated Z together (degree 0: SiLU(u); degree l >= 1: sigmoid(gamma_l) u,
+// gamma_l read from the row's gate columns). Runs on the float32 path through
+// bfloat16 pieces and on bfloat16 calls; kNoFusedGate without the flag or
+// where those kernels do not take the operands (the caller then runs the
+// products and the gate kernel).
 int run_lin_gated(const Ctx& c, const void* A, float* U, void* Z, const WSet& w, long e0, int n, hipStream_t s) {
   const Dims& d = c.d;
-  if (d.s2 || !(c.split || c.bf)) return kNoFusedGate;
+  if (!c.fused_gate || d.s2 || !(c.split || c.bf)) return kNoFusedGate;
   const int win = d.wT(), wout = d.wU(), wz = d.wZ(), L = d.L, C = d.C;
   const int op = c.bf ? kOpBF16 : kOpSplit;
   std::vector<GemmProb> pg, pu;   // gate columns; gated products

@@ -11,7 +11,8 @@ import dataclasses
 
 import torch
 
-from ._binding import SO2_ACT_GATE, SO2_ACT_SWIGLU_S2, SO2_DEBUG_CHECKS, SO2_F32_NATIVE, Cfg, GraphC, check, lib
+from ._binding import (SO2_ACT_GATE, SO2_ACT_SWIGLU_S2, SO2_DEBUG_CHECKS, SO2_F32_NATIVE, SO2_FUSED_GATE, Cfg,
+                       GraphC, check, lib)
 
 __all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_fwd_noalloc", "so2conv_bwd",
            "so2conv_dbwd",
@@ -40,7 +41,9 @@ class SO2Config:
     SwiGLU; the first linear then has 2C output channels per retained row,
     value half first). grid: for "swiglu_s2", the tables (G, P): CUDA float32
     tensors G [n_grid, q] (the retained basis at the grid points, rows of U in
-    degree-major order) and P [q, n_grid] (the projection back)."""
+    degree-major order) and P [q, n_grid] (the projection back).
+    fused_gate: the forward gate in the first linear's epilogue (bitwise the
+    same results; measured slower on MI355X, so off by default)."""
     lmax: int
     mmax: int
     channels: int
@@ -51,6 +54,7 @@ class SO2Config:
     f32_native: bool = False
     act: str = "gate"
     grid: tuple | None = dataclasses.field(default=None, compare=False, repr=False)
+    fused_gate: bool = False
 
     def __post_init__(self):
         if self.dtype not in _DTYPES:
@@ -76,7 +80,8 @@ class SO2Config:
         return 0 if self.grid is None else int(self.grid[0].shape[0])
 
     def c(self) -> Cfg:
-        flags = (SO2_DEBUG_CHECKS if self.debug_checks else 0) | (SO2_F32_NATIVE if self.f32_native else 0)
+        flags = (SO2_DEBUG_CHECKS if self.debug_checks else 0) | (SO2_F32_NATIVE if self.f32_native else 0) | \
+            (SO2_FUSED_GATE if self.fused_gate else 0)
         G, P = self.grid if self.grid is not None else (None, None)
         return Cfg(self.lmax, self.mmax, self.channels, self.n_rbf, _DTYPES[self.dtype][0], flags, self.heads,
                    _ACTS[self.act], self.n_grid, None if G is None else G.data_ptr(),

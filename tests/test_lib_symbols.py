@@ -58,7 +58,8 @@ def test_host_side_dtype_and_flag_checks():
     assert K.so2conv_saved_bytes(bf16, 1024) == 1024 * 41216
     assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 128, 64, debug_checks=True), 8) > 0
     assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 128, 64, f32_native=True), 8) > 0
-    bad = Cfg(4, 2, 128, 64, 0, 8)       # unknown flag bit
+    assert K.so2conv_saved_bytes(K.SO2Config(4, 2, 128, 64, fused_gate=True), 8) > 0
+    bad = Cfg(4, 2, 128, 64, 0, 16)      # unknown flag bit
     assert K.lib().so2conv_saved_bytes(ctypes.byref(bad), 8) == 0
     odd = Cfg(4, 2, 128, 64, 7, 0)       # unknown dtype
     assert K.lib().so2conv_saved_bytes(ctypes.byref(odd), 8) == 0
