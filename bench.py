@@ -108,7 +108,7 @@ def measured_gemm_traffic(config, dtype, keep_bwd, split):
         rec = json.load(open(os.path.join(ROOT, "profiles", "gemm_hbm_traffic_medium.json")))
         csrc = os.path.join(ROOT, "so_graph_convolution_amd", "csrc")
         src = b"".join(open(os.path.join(csrc, f), "rb").read()
-                       for f in ("gemm.hip", "gemm.hpp", "gemm_x3.hip", "gemm_dma.hpp", "gemm_tile.hpp"))
+                       for f in ("gemm.hip", "gemm.hpp", "gemm_x3.hip", "gemm_s3.hip", "gemm_dma.hpp", "gemm_tile.hpp"))
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
@@ -517,8 +517,9 @@ def main():
     achieved = executed / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_BF16_MFMA_TFLOPS if (dtype == "bf16" or split) else PEAK_FP32_MFMA_TFLOPS
     if split:
-        kname = ("gemm_x3_kernel: float32 per-order products (orders >= 1 realified) with every operand the exact "
-                 f"sum of three bfloat16 pieces, {SPLIT_PRODUCTS} bf16 MFMA products per float32 product")
+        kname = ("gemm_s3_kernel (gemm_x3_kernel for gated launches): float32 per-order products (orders >= 1 "
+                 "realified) with every operand the exact sum of three bfloat16 pieces, "
+                 f"{SPLIT_PRODUCTS} bf16 MFMA products per float32 product")
     elif dtype == "bf16":
         kname = ("gemm_b16_kernel (A.B^T) and gemm_b16t_kernel (A^T.B weight gradients): bf16 MFMA per-order "
                  "linears")

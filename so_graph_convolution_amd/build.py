@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libso2conv.so")
 SOURCES = ["api.cpp", "gemm.hip", "graph.hip", "conv_fwd.hip", "conv_bwd.hip", "conv_dual.hip", "grid.hip",
-           "s2act.hip", "noalloc.hip", "gemm_x3.hip", "grid_api.cpp"]
+           "s2act.hip", "noalloc.hip", "gemm_x3.hip", "gemm_s3.hip", "grid_api.cpp"]
 ARCH = os.environ.get("SO2_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-result", "-Wno-unused-variable"]

@@ -75,6 +75,13 @@ int gemm_run(GemmBatch& b, bool TA, bool TB, bool bf16, hipStream_t s);
 // hipErrorNotSupported (nothing launched) unless every operand is 16-byte
 // aligned with leading dimensions (and a k-major operand's width) multiples of four.
 int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s);
+// The six-product float32 GEMM with every staged element split once per block
+// (256 x 256 blocks of four 128 x 128 waves); gemm_x3_run takes it first for
+// nprod = 6. hipErrorNotSupported (nothing launched) for complex or gated
+// problems, A^T.B^T, operands not 16-byte aligned or with leading dimensions
+// not multiples of four, K not a multiple of four where an operand is
+// k-contiguous, a k-major operand's width not a multiple of four.
+int gemm_s3_run(GemmBatch& b, bool TA, bool TB, hipStream_t s);
 // bfloat16 A.B^T on the same block structure; hipErrorNotSupported (nothing
 // launched) unless operands are 16-byte aligned, leading dimensions multiples
 // of eight and K even (split chunks multiples of 32).

@@ -535,6 +535,10 @@ int gemm_b16_run(GemmBatch& b, hipStream_t s) {
 // launched) for operands the direct-to-LDS layouts do not take, complex
 // problems, or A^T.B^T
 int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s) {
+  if (nprod == 6) {
+    const int e = gemm_s3_run(b, TA, TB, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   if ((TA && TB) || (nprod != 6 && nprod != 9) || !zdma_ok(b, TA, TB)) return hipErrorNotSupported;
   const int total = z_tiles(b);
   if (total == 0) return hipSuccess;
