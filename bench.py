@@ -346,6 +346,12 @@ def main():
                     help="Edge -> Edge activation: the gate (eSEN/UMA) or the spherical-grid SwiGLU (EquiformerV3)")
     ap.add_argument("--n-grid", type=int, default=0,
                     help="grid points of --act swiglu_s2 (default 2(L+1) latitudes x (2M+3) longitudes)")
+    ap.add_argument("--lmax", type=int, default=None, help="override the workload's lmax (sweeps)")
+    ap.add_argument("--mmax", type=int, default=None, help="override the workload's mmax (sweeps)")
+    ap.add_argument("--channels", type=int, default=None, help="override the workload's channels C (sweeps)")
+    ap.add_argument("--n-atoms", type=int, default=None, help="override the workload's atom count (sweeps)")
+    ap.add_argument("--k-targets", type=int, default=None,
+                    help="override the targets per node of a K-target sweep graph (P2)")
     ap.add_argument("--cpu-edges", type=int, default=16384, help="edge sample of the CPU oracle baseline (0: skip)")
     ap.add_argument("--bounded-gib", type=float, default=32.0,
                     help="after the main line, time the same step with the workspace capped at this many GiB "
@@ -384,9 +390,13 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = so2_synth.CONFIGS[args.config]
+    over = {k: v for k, v in (("lmax", args.lmax), ("mmax", args.mmax), ("channels", args.channels),
+                              ("n_atoms", args.n_atoms), ("k_targets", args.k_targets)) if v is not None}
+    if over:
+        cfg = dataclasses.replace(cfg, **over)
     dtype = args.dtype or cfg.dtype
     if dtype == "bf16" and cfg.dtype != "bf16":
-        cfg = so2_synth.make_config(args.config, dtype="bf16")   # bf16-representable inputs
+        cfg = dataclasses.replace(cfg, dtype="bf16")   # bf16-representable inputs
     s2 = args.act == "swiglu_s2"
     if s2:
         ng = args.n_grid or 2 * (cfg.lmax + 1) * (2 * cfg.mmax + 3)
@@ -550,7 +560,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{WORKLOADS.get(cfg.name, cfg.name)} ({cfg.name})", "n_atoms": N,
                    "n_edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "channels": cfg.channels,
-                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc,
+                   "n_rbf": cfg.n_rbf, "cutoff_A": cfg.rc, **({"k_targets": cfg.k_targets} if cfg.k_targets else {}),
                    "stages": ("fwd+bwd" if two_stage else "fwd+bwd+dbwd (force-training pattern)")
                    + (", dbwd with gpos2" if args.pos2 else "")
                    + (f", {args.heads}-head attention weights times the cutoff envelope" if args.heads > 1
@@ -561,7 +571,7 @@ def main():
                    "edge_chunks": chunked, "forward_state_kept": keep_state, "backward_cotangents_kept": keep_bwd},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak,
-                     "traffic": None if (mole or s2) else measured_gemm_traffic(args.config, dtype, keep_bwd, split),
+                     "traffic": None if (mole or s2 or over) else measured_gemm_traffic(args.config, dtype, keep_bwd, split),
                      "algorithmic_bytes_per_launch": gemm_by / max(n_l, 1),
                      "kernel": kname,
                      "launches": n_l, "avg_launch_ms": gemm_ms / max(n_l, 1),
@@ -578,7 +588,7 @@ def main():
                                        "separate_operation_intermediates": mat_gib},
         ("step_tflops_3F_equivalent" if two_stage else "step_tflops_8F_equivalent"):
             (3 if two_stage else 8) * F * E / (ms_step * 1e-3) / 1e12,
-        "hbm": measured_step_traffic(args.config, dtype, keep_bwd, ms_step) if not (mole or args.envelope or s2)
+        "hbm": measured_step_traffic(args.config, dtype, keep_bwd, ms_step) if not (mole or args.envelope or s2 or over)
         else None,
     }
     progress(f"timed {args.steps} steps: {ms_step:.1f} ms/step")

@@ -300,9 +300,17 @@ BwdRows bwd_rows(const Ctx& c, const void* sb, long E, long e0) {
 
 }  // namespace
 
-// K chunk of split-K weight-gradient products over edges (a multiple of the GEMM K tile)
-void so2::split_plan(long K, int* splits, int* chunk) {
+// K chunk of split-K weight-gradient products over edges (a multiple of the
+// GEMM K tile). With `small` (the rows of one system), rows that 4096-row
+// chunks would cut into fewer than 32 splits are cut into chunks of 512 to
+// 2048 rows, halving until there are 32 splits or the chunk is 512 rows: a
+// handful of long splits leaves most CUs idle (measured on MI355X at 17,880
+// edges, lmax 4, C 128). The splits of K <= K' rows then stay within
+// max(ceil(K' / 4096), min(64, ceil(K' / 512))), which take_partials sizes for.
+void so2::split_plan(long K, int* splits, int* chunk, bool small) {
   long c = 4096;
+  if (small)
+    while (c > 512 && (K + c - 1) / c < 32) c /= 2;
   long s = (K + c - 1) / c;
   if (s > 256) {
     c = ((K + 255) / 256 + kGemmKTile - 1) / kGemmKTile * kGemmKTile;
@@ -413,11 +421,15 @@ size_t max_grad_block(const Ctx& c) {
 
 // split-K partials of one order's weight-gradient launch: nseg segments of up
 // to ec rows, cut at system borders (each system's rows split on their own,
-// at most ceil(rows / 4096) + 1 splits each)
+// at most ceil(rows / 4096) + 1 splits each; the rows of one system, K <= ec,
+// at most max(ceil(ec / 4096), min(64, ceil(ec / 512))): chunks of fewer than
+// 4096 rows leave under 64 splits, and no chunk is below 512 rows)
 float* take_partials(Arena& ar, const Ctx& c, long ec, int nseg) {
   int sp, ch;
-  split_plan(ec, &sp, &ch);
-  const long bound = std::max<long>(sp, (ec + 4095) / 4096) + 1 + (c.ns > 1 ? c.ns : 0);
+  const bool small = c.ns <= 1;
+  split_plan(ec, &sp, &ch, small);
+  const long fine = small ? std::min<long>(64, (ec + 511) / 512) : 0;
+  const long bound = std::max<long>(std::max<long>(sp, (ec + 4095) / 4096), fine) + 1 + (c.ns > 1 ? c.ns : 0);
   return ar.take((size_t)nseg * bound * max_grad_block(c));
 }
 
@@ -975,7 +987,7 @@ int run_lin_grad(const Ctx& c, int second, const void* const* in, const void* co
       Red rd{sy, poff, 0, zeroed || lo != w.e[sy]};
       for (int q = 0; q < nseg; ++q) {
         int sp, ch;
-        split_plan(hi - lo, &sp, &ch);
+        split_plan(hi - lo, &sp, &ch, c.ns <= 1);
         const void* Aq = offs(in[q], (size_t)(lo - e0) * win + ib, c.es);
         const void* Bq = offs(out[q], (size_t)(lo - e0) * wout + ob, c.es);
         // float32, orders >= 1: (T+ - i T-)^T (Ubar+ + i Ubar-) straight into the user layout [k][2h]

@@ -64,7 +64,7 @@ int run_batch(std::vector<GemmProb>& ps, bool TA, bool TB, int op, hipStream_t s
 
 // splits and K chunk of a split-K product over K rows (a multiple of the GEMM K
 // tile); run_tn's partial buffer holds sum over segments of splits * M * N floats
-void split_plan(long K, int* splits, int* chunk);
+void split_plan(long K, int* splits, int* chunk, bool small = false);
 
 // Weight gradient G[M][N] (+)= sum over segments of A_s^T B_s, A_s [K_s][lda], B_s [K_s][ldb];
 // deterministic split-K through the partial buffer P.
