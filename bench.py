@@ -531,8 +531,8 @@ def main():
                  "realified) with every operand the exact sum of three bfloat16 pieces, "
                  f"{SPLIT_PRODUCTS} bf16 MFMA products per float32 product")
     elif dtype == "bf16":
-        kname = ("gemm_b16_kernel (A.B^T) and gemm_b16t_kernel (A^T.B weight gradients): bf16 MFMA per-order "
-                 "linears")
+        kname = ("gemm_b3_kernel (A.B^T; gemm_b16_kernel for gated launches) and gemm_b16t_kernel (A^T.B weight "
+                 "gradients): bf16 MFMA per-order linears")
     else:
         kname = ("gemm_f32_dma_kernel (order 0) and gemm_cplx_dma_kernel (orders >= 1, three real products per "
                  "complex one; fp32 MFMA)")

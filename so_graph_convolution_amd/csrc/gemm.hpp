@@ -82,6 +82,11 @@ int gemm_x3_run(GemmBatch& b, bool TA, bool TB, int nprod, hipStream_t s);
 // not multiples of four, K not a multiple of four where an operand is
 // k-contiguous, a k-major operand's width not a multiple of four.
 int gemm_s3_run(GemmBatch& b, bool TA, bool TB, hipStream_t s);
+// bfloat16 A.B^T on the same four-wave blocks (64 k per tile, register-staged
+// loads a tile ahead); gemm_b16_run takes it first. hipErrorNotSupported
+// (nothing launched) for complex or gated problems, operands not 16-byte
+// aligned or with leading dimensions or K not multiples of eight.
+int gemm_b3_run(GemmBatch& b, hipStream_t s);
 // bfloat16 A.B^T on the same block structure; hipErrorNotSupported (nothing
 // launched) unless operands are 16-byte aligned, leading dimensions multiples
 // of eight and K even (split chunks multiples of 32).

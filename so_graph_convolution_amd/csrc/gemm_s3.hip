@@ -257,6 +257,154 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
 }
 
+// bfloat16 A.B^T (both operands k-contiguous) on the same block structure:
+// 256 x 256 blocks of four 128 x 128 waves, 64 k per tile in two LDS stages
+// of 64 KB (per operand 256 rows of eight 16-byte units, unit u of row r at
+// u ^ ((r / 2) mod 8), so a fragment read of 16 rows covers the 64 banks
+// once). Each thread loads 16 units (eight lanes per 128-byte row segment) a
+// tile ahead and writes them to the other stage while the wave's 64 MFMAs of
+// the current tile run; within a tile the fragments of k step s + 1 are read
+// while the 16 MFMAs of step s run.
+constexpr int BK = 64;   // bfloat16 k per tile
+__device__ __forceinline__ int b_unit(int op, int row, int u) { return (op * 256 + row) * 8 + (u ^ ((row >> 1) & 7)); }
+
+struct BFrag {
+  bf16x8 a[4], b[4];
+};
+__device__ __forceinline__ void bread(const u32x4* S, int ra, int rb, int u, BFrag& F) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    F.a[i] = __builtin_bit_cast(bf16x8, S[b_unit(0, ra + 32 * i, u)]);
+    F.b[i] = __builtin_bit_cast(bf16x8, S[b_unit(1, rb + 32 * i, u)]);
+  }
+}
+__device__ __forceinline__ void bmma(const BFrag& F, floatx16 (&acc)[4][4]) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = mfma(F.a[a], F.b[b], acc[a][b]);
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_b3_kernel(GemmBatch batch) {
+  __shared__ u32x4 T[2][2 * 256 * 8];
+  int pi, local;
+  decode_tile(batch, xcd_remap(blockIdx.x, batch.total_tiles), &pi, &local);
+  const GemmProb& p = batch.p[pi];
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int split = local / per_split;
+  local -= split * per_split;
+  const int tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+  const int m0 = tm * TM, n0 = tn * TN;
+  const int kbeg = split * p.k_chunk, kend = min(p.K, kbeg + p.k_chunk);
+  const int nkk = kend - kbeg, nk = (nkk + BK - 1) / BK;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int wm = wave >> 1, wn = wave & 1, li = lane % 32, lk = lane / 32;
+  // staging: unit su (k 8 su .. 8 su + 7 of the tile) of rows sr + 32 j, j < 8,
+  // of each operand; rows past the edge load the last row, a unit past the
+  // split's k range loads its last unit and is stored as zeros
+  const int su = tid % 8, sr = tid / 8;
+  const unsigned short* Ap = static_cast<const unsigned short*>(p.A) + kbeg;
+  const unsigned short* Bp = static_cast<const unsigned short*>(p.B) + kbeg;
+  u32x4 xa[8], xb[8];
+  bool oka = false, okb = false;
+  auto load = [&](const unsigned short* P, int ld, int r0, int rlim, int t, u32x4 (&x)[8], bool& ok) {
+    const int k = BK * t + 8 * su;
+    ok = k < nkk;
+    const int kk = min(k, nkk - 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = min(r0 + sr + 32 * j, rlim - 1);
+      x[j] = *reinterpret_cast<const u32x4*>(P + (size_t)row * ld + kk);
+    }
+  };
+  auto store = [&](u32x4* S, int op, const u32x4 (&x)[8], bool ok, int j0) {
+#pragma unroll
+    for (int j = j0; j < j0 + 4; ++j) S[b_unit(op, sr + 32 * j, su)] = ok ? x[j] : u32x4{0u, 0u, 0u, 0u};
+  };
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  if (nk > 0) {
+    load(Ap, p.lda, m0, p.M, 0, xa, oka);
+    load(Bp, p.ldb, n0, p.N, 0, xb, okb);
+    store(T[0], 0, xa, oka, 0);
+    store(T[0], 0, xa, oka, 4);
+    store(T[0], 1, xb, okb, 0);
+    store(T[0], 1, xb, okb, 4);
+    load(Ap, p.lda, m0, p.M, min(1, nk - 1), xa, oka);
+    load(Bp, p.ldb, n0, p.N, min(1, nk - 1), xb, okb);
+  }
+  __syncthreads();
+  const int ra = wm * 128 + li, rb = wn * 128 + li;
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    const u32x4* st = T[kt & 1];
+    u32x4* nx = T[(kt + 1) & 1];   // the next tile (after the last tile a stale copy, never read)
+    BFrag F0, F1;
+    bread(st, ra, rb, lk, F0);
+    __builtin_amdgcn_sched_barrier(0);
+    // k step 0: step 1's fragments, A's first half of the next tile
+    bread(st, ra, rb, 2 + lk, F1);
+    store(nx, 0, xa, oka, 0);
+    bmma(F0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    // k step 1: step 2's fragments, A's second half, then A's loads of the tile after
+    bread(st, ra, rb, 4 + lk, F0);
+    store(nx, 0, xa, oka, 4);
+    load(Ap, p.lda, m0, p.M, min(kt + 2, nk - 1), xa, oka);
+    bmma(F1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    // k step 2: step 3's fragments, B's first half
+    bread(st, ra, rb, 6 + lk, F1);
+    store(nx, 1, xb, okb, 0);
+    bmma(F0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    // k step 3: B's second half, then B's loads
+    store(nx, 1, xb, okb, 4);
+    load(Bp, p.ldb, n0, p.N, min(kt + 2, nk - 1), xb, okb);
+    bmma(F1, acc);
+    __syncthreads();
+  }
+  const int i0 = m0 + wm * 128 + 4 * lk, j0 = n0 + wn * 128 + li;
+  float* out = p.partial ? p.C + (size_t)split * p.M * p.N : p.C;
+  const int ldo = p.partial ? p.N : p.ldc;
+  const bool add = p.accumulate && !p.partial;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + 32 * b;
+      if (j >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 32 * a + 8 * (r / 4) + (r % 4);
+        if (i < p.M) {
+          float* o = out + (size_t)i * ldo + j;
+          *o = add ? *o + acc[a][b][r] : acc[a][b][r];
+        }
+      }
+    }
+}
+
+// operands of the bfloat16 kernel: real, ungated problems, 16-byte aligned
+// rows (leading dimensions multiples of eight), K a multiple of eight, split
+// chunks multiples of the 64-k tile
+bool b3_ok(const GemmBatch& b) {
+  for (int q = 0; q < b.nprob; ++q) {
+    const GemmProb& p = b.p[q];
+    if (p.M <= 0 || p.N <= 0) continue;
+    if (p.cplx || p.gate) return false;
+    if ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) % 16) return false;
+    if (p.lda % 8 || p.ldb % 8 || p.K % 8) return false;
+    if (p.k_splits > 1 && p.k_chunk % BK) return false;
+  }
+  return true;
+}
+
 // operands the kernel takes: real, ungated problems; 16-byte aligned operands
 // with leading dimensions multiples of four; K a multiple of four where an
 // operand is k-contiguous, the row width (M or N) a multiple of four where it
@@ -291,6 +439,14 @@ int s3_tiles(GemmBatch& b) {
 }
 
 }  // namespace
+
+int gemm_b3_run(GemmBatch& b, hipStream_t s) {
+  if (!b3_ok(b)) return hipErrorNotSupported;
+  const int total = s3_tiles(b);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_b3_kernel, dim3(total), dim3(NT), 0, s, b);
+  return hipGetLastError();
+}
 
 int gemm_s3_run(GemmBatch& b, bool TA, bool TB, hipStream_t s) {
   if ((TA && TB) || !s3_ok(b, TA, TB)) return hipErrorNotSupported;

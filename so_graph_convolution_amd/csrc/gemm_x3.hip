@@ -525,6 +525,10 @@ int gemm_b16t_run(GemmBatch& b, hipStream_t s) {
 // (nothing launched) for operands its layout does not take
 int gemm_b16_run(GemmBatch& b, hipStream_t s) {
   if (!b16_ok(b)) return hipErrorNotSupported;
+  {
+    const int e = gemm_b3_run(b, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   const int total = z_tiles(b);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(gemm_b16_kernel, dim3(total), dim3(ZNT), 0, s, b);
