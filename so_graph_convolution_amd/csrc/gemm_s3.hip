@@ -344,22 +344,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   for (int kt = 0; kt < nk; ++kt) {
     const u32x4* st = T[kt & 1];
     u32x4* nx = T[(kt + 1) & 1];   // the next tile (after the last tile a stale copy, never read)
+    // k step s takes unit 4 (s / 2) + 2 lk + s mod 2 (k 16 lk + 8 (s mod 2) ..
+    // of the tile's 32-k half s / 2): the k values each MFMA meets are those
+    // of gemm_b16_kernel's 32-k tiles, so the two agree bit for bit
     BFrag F0, F1;
-    bread(st, ra, rb, lk, F0);
+    bread(st, ra, rb, 2 * lk, F0);
     __builtin_amdgcn_sched_barrier(0);
     // k step 0: step 1's fragments, A's first half of the next tile
-    bread(st, ra, rb, 2 + lk, F1);
+    bread(st, ra, rb, 2 * lk + 1, F1);
     store(nx, 0, xa, oka, 0);
     bmma(F0, acc);
     __builtin_amdgcn_sched_barrier(0);
     // k step 1: step 2's fragments, A's second half, then A's loads of the tile after
-    bread(st, ra, rb, 4 + lk, F0);
+    bread(st, ra, rb, 4 + 2 * lk, F0);
     store(nx, 0, xa, oka, 4);
     load(Ap, p.lda, m0, p.M, min(kt + 2, nk - 1), xa, oka);
     bmma(F1, acc);
     __builtin_amdgcn_sched_barrier(0);
     // k step 2: step 3's fragments, B's first half
-    bread(st, ra, rb, 6 + lk, F1);
+    bread(st, ra, rb, 5 + 2 * lk, F1);
     store(nx, 1, xb, okb, 0);
     bmma(F0, acc);
     __builtin_amdgcn_sched_barrier(0);
