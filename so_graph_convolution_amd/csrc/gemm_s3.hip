@@ -201,9 +201,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
     // The next tile's split goes to the other stage (read by every wave
     // before the last barrier; after the last tile a stale copy, never read)
-    // in eight units, each ahead of 12 of the 96 products (order: piece
-    // product, then A tile, then B tile), so the VALU work issues while the
-    // matrix core runs; scheduling barriers keep that order.
+    // in eight units, each ahead of 8 of the first 64 products (two A tiles
+    // of one piece product against the four B tiles), so the VALU work
+    // issues while the matrix core runs; scheduling barriers keep that order.
+    // The loads of the tile after it and the last 32 products follow.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
