@@ -284,6 +284,162 @@ __global__ __launch_bounds__(512) void node_bwd_kernel(Dims d, GraphDev g, const
   }
 }
 
+// ------------------------------------------------------------------ node_bwd, degree split
+// At lmax 6 a whole node row and its accumulator per thread hold 222
+// registers (two waves per SIMD); there the two thread groups of a node's
+// block own degrees [0, LS) and [LS, L] (deg_split, halves within 3% of each
+// other at mmax 2) instead of alternate edges. Measured on MI355X at lmax 6
+// (1.05M edges): 20.0 -> 17.4 ms per call; at lmax 4, where the halves are
+// 70 : 45, the edge-parity kernel above stays faster (7.95 vs 10.0 ms).
+// The torque terms sum_rows xb <(R G_k)_row, x_n> of a degree are taken as
+// <G_k^T y, x_n> with y = R^T xb, the edge's contribution to acc.
+// Degrees [LA, LB) of one edge side; xn and acc hold rows LA^2 .. LB^2 - 1.
+// Every load of the edge (T-bar rows, then the radial scales, into `v` of
+// capacity VN, the larger group's count) is issued before its first row is
+// used and before its radial cotangents are stored: one memory latency per
+// edge, not one per degree.
+template <int L, int M, int LA, int LB, int VN>
+__device__ __forceinline__ void node_bwd_load(const Dims& d, const float* __restrict__ S,
+                                              const float* __restrict__ Tbar, long e, int cin, float (&v)[VN]) {
+  constexpr int R0 = ridx(LA, -qhalf(LA, M), M), QR = q_range(LA, LB, M);
+  const int Ci = 2 * d.C;
+  const float* tb = Tbar + (size_t)e * d.wT() + cin;
+  const float* sr = S + (size_t)e * ((L + 1) * Ci) + cin;
+#pragma unroll
+  for (int l = LA; l < LB; ++l) {
+    const int q = qhalf(l, M);
+#pragma unroll
+    for (int m = -q; m <= q; ++m) v[ridx(l, m, M) - R0] = tb[mm_col(l, m, 0, L, Ci)];
+    v[QR + l - LA] = sr[l * Ci];
+  }
+}
+
+template <int L, int M, int LA, int LB, int DH, int VN>
+__device__ __forceinline__ void node_bwd_edge_degs(const Dims& d, RotPtr sRt, RotPtr sG, const float (&xn)[DH],
+                                                   const float (&v)[VN], float* __restrict__ Sbar, long e, int cin,
+                                                   float (&acc)[DH], float (&tk)[3]) {
+  constexpr int B = LA * LA, R0 = ridx(LA, -qhalf(LA, M), M), QR = q_range(LA, LB, M);
+  const int Ci = 2 * d.C;
+  float* sb = Sbar + (size_t)e * ((L + 1) * Ci) + cin;
+  // one pass over the rows of R and R G_k: radial cotangent, transposed
+  // product into acc and the torque
+#pragma unroll
+  for (int l = LA; l < LB; ++l) {
+    const int q = qhalf(l, M), n = 2 * l + 1;
+    const float scl = v[QR + l - LA];
+    float sacc = 0.f, y[2 * L + 1];
+#pragma unroll
+    for (int i = 0; i < 2 * L + 1; ++i) y[i] = 0.f;
+#pragma unroll
+    for (int m = -q; m <= q; ++m) {
+      const int off = rot_off(l, M) + (m + q) * n;
+      const float tv = v[ridx(l, m, M) - R0];
+      const float xb = scl * tv;
+      float r[2 * L + 1];
+      load_row<L>(sRt, off, n, r);
+      sacc += tv * row_dot<L>(r, xn + l * l - B, n);
+      row_axpy<L>(r, xb, y, n);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * L + 1; ++i)
+      if (i < n) acc[l * l - B + i] += y[i];
+    if (l > 0)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) tk[k] += gen_form<L>(sG, k, l, y, xn + l * l - B);
+    sb[l * Ci] = sacc;
+  }
+}
+
+template <int L, int M>
+__global__ __launch_bounds__(512) void node_bwd_split_kernel(Dims d, GraphDev g, const float* __restrict__ x,
+                                                       const float* __restrict__ pos, const float* __restrict__ S,
+                                                       const float* __restrict__ Tbar, float* __restrict__ gx,
+                                                       float* __restrict__ Sbar, float* __restrict__ tau_dst,
+                                                       float* __restrict__ tau_src, int accumulate) {
+  constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int LS = deg_split(L, M), DH = half_rows(L, M);
+  // values loaded per edge: retained T-bar rows and radial scales of a group's degrees
+  constexpr int VN0 = q_range(0, LS, M) + LS, VN1 = q_range(LS, L + 1, M) + L + 1 - LS;
+  constexpr int VN = VN0 > VN1 ? VN0 : VN1;
+  constexpr int TE = tile_edges<L, M, 0>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRed[TE * 8 * 3];
+  __shared__ int sE[TE];
+  __shared__ float sG[3 * gen_off(L + 1)];
+
+  const int node = blockIdx.x;
+  gen_stage<L>(sG);
+  const int C = d.C;
+  const int CW = blockDim.x / 2;
+  const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, degree half
+  const bool act = c < C;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nw = blockDim.x / 64;
+  const int r0 = grp == 0 ? 0 : LS * LS, nr = grp == 0 ? LS * LS : D - LS * LS;
+  float xn[DH], acc[DH];
+#pragma unroll
+  for (int r = 0; r < DH; ++r) {
+    xn[r] = (act && r < nr) ? x[((size_t)node * D + r0 + r) * C + c] : 0.f;
+    acc[r] = 0.f;
+  }
+
+  for (int pass = 0; pass < 2; ++pass) {
+    // pass 0: incoming edges (this node is the receiver, target half of the input)
+    // pass 1: outgoing edges via the source permutation (source half)
+    int beg, end;
+    if (pass == 0) in_range(g, node, &beg, &end);
+    else out_range(g, node, &beg, &end);
+    float* tau_out = pass == 0 ? tau_dst : tau_src;
+    for (int t0 = beg; t0 < end; t0 += TE) {
+      const int ne = min(TE, end - t0);
+      for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+        const long e = pass == 0 ? (long)(t0 + t) : (long)g.src_perm[t0 + t];
+        sE[t] = (int)(e - g.e0);   // chunk-relative row
+        const int j = pass == 0 ? g.src[e] : node;
+        const int i = pass == 0 ? node : g.dst[e];
+        edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
+      }
+      __syncthreads();
+      wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+      __syncthreads();
+      const int cin = pass == 0 ? C + c : c;
+      for (int t = 0; t < ne; ++t) {
+        float tk[3] = {0.f, 0.f, 0.f};
+        if (act) {
+          float v[VN];
+          if (grp == 0) {
+            node_bwd_load<L, M, 0, LS, VN>(d, S, Tbar, sE[t], cin, v);
+            node_bwd_edge_degs<L, M, 0, LS, DH, VN>(d, sR + t * K, sG, xn, v, Sbar, sE[t], cin, acc, tk);
+          } else {
+            node_bwd_load<L, M, LS, L + 1, VN>(d, S, Tbar, sE[t], cin, v);
+            node_bwd_edge_degs<L, M, LS, L + 1, DH, VN>(d, sR + t * K, sG, xn, v, Sbar, sE[t], cin, acc, tk);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const float s = wave_sum(tk[k]);
+          if (lane == 0) sRed[(t * 8 + wave) * 3 + k] = s;
+        }
+      }
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < ne * 3; idx += blockDim.x) {
+        const int t = idx / 3, k = idx - t * 3;
+        float s = 0.f;
+        for (int w = 0; w < nw; ++w) s += sRed[(t * 8 + w) * 3 + k];
+        tau_out[(size_t)sE[t] * 3 + k] = s;
+      }
+      __syncthreads();
+    }
+  }
+  if (gx && act) {
+    float* o = gx + ((size_t)node * D + r0) * C + c;
+#pragma unroll
+    for (int r = 0; r < DH; ++r)
+      if (r < nr) o[(size_t)r * C] = accumulate ? o[(size_t)r * C] + acc[r] : acc[r];
+  }
+}
+
 template <int L, int M>
 struct NodeBwd {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* pos, const float* S,
@@ -291,8 +447,12 @@ struct NodeBwd {
                  hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = 2 * ((d.C + 63) / 64) * 64;
-    hipLaunchKernelGGL((node_bwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, pos, S, Tbar, gx, Sbar,
-                       tau_dst, tau_src, accumulate);
+    if constexpr (L >= 6)
+      hipLaunchKernelGGL((node_bwd_split_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, pos, S, Tbar, gx,
+                         Sbar, tau_dst, tau_src, accumulate);
+    else
+      hipLaunchKernelGGL((node_bwd_kernel<L, M>), dim3(g.N), dim3(threads), 0, s, d, g, x, pos, S, Tbar, gx, Sbar,
+                         tau_dst, tau_src, accumulate);
     return hipGetLastError();
   }
 };

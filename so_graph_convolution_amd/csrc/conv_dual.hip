@@ -586,6 +586,202 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
   }
 }
 
+// ------------------------------------------------------------------ node_bwd_dual, degree split
+// The same outputs as node_bwd_dual_kernel without the position terms, for
+// lmax 6 (see node_bwd_split_kernel): 12.0 -> 10.6 ms per call at lmax 6,
+// mmax 2 on MI355X.
+// The two thread groups of a node's block own degrees [0, LS) and [LS, L]
+// (deg_split); each thread keeps x, xdot and the accumulator of its degrees.
+//
+// Every load of an edge's degrees (Tdotbar and Tbar rows, then S and Sdot)
+// is issued before its first rotation row is used and before its radial
+// cotangents are stored: one memory latency per edge, not one per degree.
+template <int L, int M, int LA, int LB, int VN>
+__device__ __forceinline__ void node_bwd_dual_load(const Dims& d, const float* __restrict__ S,
+                                                   const float* __restrict__ Sdot, const float* __restrict__ Tdb,
+                                                   const float* __restrict__ Tb, long e, int cin, float (&v)[VN]) {
+  constexpr int R0 = ridx(LA, -qhalf(LA, M), M), QR = q_range(LA, LB, M), NL = LB - LA;
+  const int Ci = 2 * d.C, wT = d.wT(), wS = (L + 1) * Ci;
+  const float* tdb = Tdb + (size_t)e * wT + cin;
+  const float* tb = Tb + (size_t)e * wT + cin;
+  const float* sr = S + (size_t)e * wS + cin;
+  const float* sd = Sdot + (size_t)e * wS + cin;
+#pragma unroll
+  for (int l = LA; l < LB; ++l) {
+    const int q = qhalf(l, M);
+#pragma unroll
+    for (int m = -q; m <= q; ++m) {
+      v[ridx(l, m, M) - R0] = tdb[mm_col(l, m, 0, L, Ci)];
+      v[QR + ridx(l, m, M) - R0] = tb[mm_col(l, m, 0, L, Ci)];
+    }
+    v[2 * QR + l - LA] = sr[l * Ci];
+    v[2 * QR + NL + l - LA] = sd[l * Ci];
+  }
+}
+
+template <int L, int M, bool P2, int LA, int LB, int DH, int VN>
+__device__ __forceinline__ void node_bwd_dual_degs(const Dims& d, RotPtr sRt, RotPtr sRdt, RotPtr sG,
+                                                   const float (&xn)[DH], const float (&xdn)[DH],
+                                                   const float (&v)[VN], float* __restrict__ Sbar,
+                                                   float* __restrict__ Sdb, long e, int cin, float (&acc)[DH],
+                                                   float (&tk)[6]) {
+  constexpr int B = LA * LA, R0 = ridx(LA, -qhalf(LA, M), M), QR = q_range(LA, LB, M), NL = LB - LA;
+  const int Ci = 2 * d.C, wS = (L + 1) * Ci;
+  float* sbo = Sbar + (size_t)e * wS + cin;
+  float* sdo = Sdb + (size_t)e * wS + cin;
+  // one pass over the rows of R and Rdot: forward products for the radial
+  // cotangents and the transposed products into acc
+#pragma unroll
+  for (int l = LA; l < LB; ++l) {
+    const int q = qhalf(l, M), n = 2 * l + 1;
+    const float sv = v[2 * QR + l - LA], sdv = v[2 * QR + NL + l - LA];
+    float sb = 0.f, sdb = 0.f;
+    // position terms: the row sums y = R^T u1, z = R^T u2, zw = Rdot^T u2
+    float y[P2 ? 2 * L + 1 : 1], z[P2 ? 2 * L + 1 : 1], zw[P2 ? 2 * L + 1 : 1];
+    if (P2)
+#pragma unroll
+      for (int i = 0; i < (P2 ? 2 * L + 1 : 1); ++i) y[i] = z[i] = zw[i] = 0.f;
+#pragma unroll
+    for (int m = -q; m <= q; ++m) {
+      const int off = rot_off(l, M) + (m + q) * n;
+      const float a1 = v[ridx(l, m, M) - R0];
+      const float a0 = v[QR + ridx(l, m, M) - R0];
+      float r[2 * L + 1], rd[2 * L + 1];
+      load_row<L>(sRt, off, n, r);
+      load_row<L>(sRdt, off, n, rd);
+      const float xt = row_dot<L>(r, xn + l * l - B, n), y2 = row_dot<L>(r, xdn + l * l - B, n);
+      const float y1 = row_dot<L>(rd, xn + l * l - B, n);
+      // explicit fused forms: every instantiation (with or without the
+      // position derivatives) rounds alike
+      sb = __builtin_fmaf(a0, xt, __builtin_fmaf(a1, y1 + y2, sb));
+      sdb = __builtin_fmaf(a1, xt, sdb);
+      const float u1 = __builtin_fmaf(sv, a0, sdv * a1), u2 = sv * a1;
+      row_axpy<L>(r, u1, acc + l * l - B, n);
+      row_axpy<L>(rd, u2, acc + l * l - B, n);
+      if (P2)
+#pragma unroll
+        for (int i = 0; i < (P2 ? 2 * L + 1 : 1); ++i)
+          if (i < n) {
+            y[i] = __builtin_fmaf(r[i], u1, y[i]);
+            z[i] = __builtin_fmaf(r[i], u2, z[i]);
+            zw[i] = __builtin_fmaf(rd[i], u2, zw[i]);
+          }
+    }
+    if (P2 && l > 0) {
+      // sum over rows of u1 (R G_k x) + u2 ((R G_k) xd + (Rdot G_k) x), u2 (R G_k x)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float ga = gen_form<L>(sG, k, l, z, xn + l * l - B);
+        tk[k] += gen_form<L>(sG, k, l, y, xn + l * l - B) + gen_form<L>(sG, k, l, z, xdn + l * l - B) +
+                 gen_form<L>(sG, k, l, zw, xn + l * l - B);
+        tk[3 + k] += ga;
+      }
+    }
+    sbo[l * Ci] = sb;
+    sdo[l * Ci] = sdb;
+  }
+}
+
+template <int L, int M, bool P2>
+__global__ __launch_bounds__(512) void node_bwd_dual_split_kernel(
+    Dims d, GraphDev g, const float* __restrict__ x, const float* __restrict__ px, const float* __restrict__ pos,
+    const float* __restrict__ omega, const float* __restrict__ S, const float* __restrict__ Sdot,
+    const float* __restrict__ Tdb, const float* __restrict__ Tb, float* __restrict__ gx2, float* __restrict__ Sbar,
+    float* __restrict__ Sdb, float* __restrict__ p2_dst, float* __restrict__ p2_src, int accumulate) {
+  constexpr int D = (L + 1) * (L + 1), K = k_count(L, M), ST = wig_stride_c(L, M);
+  constexpr int LS = deg_split(L, M), DH = half_rows(L, M);
+  // values loaded per edge: two rows per retained row, two scales per degree
+  constexpr int VN0 = 2 * (q_range(0, LS, M) + LS), VN1 = 2 * (q_range(LS, L + 1, M) + L + 1 - LS);
+  constexpr int VN = VN0 > VN1 ? VN0 : VN1;
+  constexpr int TE = tile_edges<L, M, k_count(L, M) + 3 + (P2 ? 48 : 0)>();
+  __shared__ float sD1[TE * 9];
+  __shared__ float sR[TE * K];
+  __shared__ float sA[TE * ST], sB[TE * ST];
+  __shared__ float sRd[TE * K];
+  __shared__ float sW[TE * 3];
+  __shared__ float sRed[P2 ? TE * 8 * 6 : 1];
+  __shared__ int sE[TE];
+  __shared__ float sG[P2 ? 3 * gen_off(L + 1) : 1];
+
+  const int node = blockIdx.x;
+  if (P2) gen_stage<L>(sG);
+  const int C = d.C;
+  const int CW = blockDim.x / 2;
+  const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, degree half
+  const bool act = c < C;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nw = blockDim.x / 64;
+  const int r0 = grp == 0 ? 0 : LS * LS, nr = grp == 0 ? LS * LS : D - LS * LS;
+  float xn[DH], xdn[DH], acc[DH];
+#pragma unroll
+  for (int r = 0; r < DH; ++r) {
+    const size_t o = ((size_t)node * D + r0 + r) * C + c;
+    xn[r] = (act && r < nr) ? x[o] : 0.f;
+    xdn[r] = (act && r < nr && px) ? px[o] : 0.f;
+    acc[r] = 0.f;
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    int beg, end;
+    if (pass == 0) in_range(g, node, &beg, &end);
+    else out_range(g, node, &beg, &end);
+    float* p2_out = pass == 0 ? p2_dst : p2_src;
+    for (int t0 = beg; t0 < end; t0 += TE) {
+      const int ne = min(TE, end - t0);
+      for (int t = threadIdx.x; t < ne; t += blockDim.x) {
+        const long e = pass == 0 ? (long)(t0 + t) : (long)g.src_perm[t0 + t];
+        sE[t] = (int)(e - g.e0);   // chunk-relative row
+        const int j = pass == 0 ? g.src[e] : node;
+        const int i = pass == 0 ? node : g.dst[e];
+        edge_geometry(pos, g.shift, j, i, e, sD1 + 9 * t);
+        for (int k = 0; k < 3; ++k) sW[t * 3 + k] = omega[(e - g.e0) * 3 + k];
+      }
+      __syncthreads();
+      wigner_rows_block(L, M, ne, sD1, sR, K, sA, sB, ST);
+      rot_directional(L, M, ne, sR, K, sW, 3, sRd, K);
+      __syncthreads();
+      const int cin = pass == 0 ? C + c : c;
+      for (int t = 0; t < ne; ++t) {
+        float tk[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (act) {
+          const long e = sE[t];
+          float v[VN];
+          if (grp == 0) {
+            node_bwd_dual_load<L, M, 0, LS, VN>(d, S, Sdot, Tdb, Tb, e, cin, v);
+            node_bwd_dual_degs<L, M, P2, 0, LS, DH, VN>(d, sR + t * K, sRd + t * K, sG, xn, xdn, v, Sbar, Sdb, e,
+                                                        cin, acc, tk);
+          } else {
+            node_bwd_dual_load<L, M, LS, L + 1, VN>(d, S, Sdot, Tdb, Tb, e, cin, v);
+            node_bwd_dual_degs<L, M, P2, LS, L + 1, DH, VN>(d, sR + t * K, sRd + t * K, sG, xn, xdn, v, Sbar, Sdb,
+                                                            e, cin, acc, tk);
+          }
+        }
+        if (P2) {
+#pragma unroll
+          for (int k = 0; k < 6; ++k) {
+            const float sum = wave_sum(tk[k]);
+            if (lane == 0) sRed[(t * 8 + wave) * 6 + k] = sum;
+          }
+        }
+      }
+      if (P2) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < ne * 6; idx += blockDim.x) {
+          const int t = idx / 6, k = idx - t * 6;
+          float sum = 0.f;
+          for (int w = 0; w < nw; ++w) sum += sRed[(t * 8 + w) * 6 + k];
+          p2_out[(size_t)sE[t] * 6 + k] = sum;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (gx2 && act) {
+    float* o = gx2 + ((size_t)node * D + r0) * C + c;
+#pragma unroll
+    for (int r = 0; r < DH; ++r)
+      if (r < nr) o[(size_t)r * C] = accumulate ? o[(size_t)r * C] + acc[r] : acc[r];
+  }
+}
+
 template <int L, int M>
 struct NodeBwdDual {
   static int run(const Dims& d, const GraphDev& g, const float* x, const float* px, const float* pos,
@@ -594,6 +790,15 @@ struct NodeBwdDual {
                  float* Sdb, float* p2_dst, float* p2_src, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = 2 * ((d.C + 63) / 64) * 64;
+    // the split kernel without the position terms (with them it spills: the
+    // edge-parity kernel keeps the P2 variant)
+    if constexpr (L >= 6) {
+      if (!p2_dst) {
+        hipLaunchKernelGGL((node_bwd_dual_split_kernel<L, M, false>), dim3(g.N), dim3(threads), 0, s, d, g, x, px,
+                           pos, omega, S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
+        return hipGetLastError();
+      }
+    }
     if (p2_dst)
       hipLaunchKernelGGL((node_bwd_dual_kernel<L, M, true>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega,
                          S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);

@@ -294,6 +294,41 @@ __device__ inline void combine_groups(const float (&acc)[D], float* buf, int cap
   }
 }
 
+// Degree split of the lmax-6 node-centric backward kernels: of the two
+// thread groups of a node's block, group 0 owns degrees [0, LS) and group 1
+// degrees [LS, L]; both walk every edge of a tile, each thread keeping the
+// node rows and accumulators of its own degrees only and writing those rows
+// itself (no combine through LDS). LS balances the rotation work of the two
+// groups: degree l has (2 min(l, M) + 1)(2l + 1) retained row entries.
+__host__ __device__ constexpr inline int deg_cost(int l, int M) { return (2 * qhalf(l, M) + 1) * (2 * l + 1); }
+__host__ __device__ constexpr inline int deg_split(int L, int M) {
+  int best = 1, bv = 1 << 30;
+  for (int s = 1; s <= L; ++s) {
+    int a = 0, b = 0;
+    for (int l = 0; l <= L; ++l) {
+      if (l < s) a += deg_cost(l, M);
+      else b += deg_cost(l, M);
+    }
+    const int v = a > b ? a : b;
+    if (v < bv) {
+      bv = v;
+      best = s;
+    }
+  }
+  return best;   // L = 0: 1, group 1 owns no degree
+}
+// node rows of the larger half
+__host__ __device__ constexpr inline int half_rows(int L, int M) {
+  const int s = deg_split(L, M), a = s * s, b = (L + 1) * (L + 1) - a;
+  return a > b ? a : b;
+}
+// retained rows (l, m) of degrees [LA, LB)
+__host__ __device__ constexpr inline int q_range(int LA, int LB, int M) {
+  int s = 0;
+  for (int l = LA; l < LB; ++l) s += 2 * qhalf(l, M) + 1;
+  return s;
+}
+
 // sum over a wavefront (64 lanes)
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
