@@ -587,9 +587,9 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
 }
 
 // ------------------------------------------------------------------ node_bwd_dual, degree split
-// The same outputs as node_bwd_dual_kernel without the position terms, for
-// lmax 6 (see node_bwd_split_kernel): 12.0 -> 10.6 ms per call at lmax 6,
-// mmax 2 on MI355X.
+// The same outputs as node_bwd_dual_kernel, for lmax 6 (see
+// node_bwd_split_kernel): 12.0 -> 10.6 ms per call at lmax 6, mmax 2 on
+// MI355X without the position terms.
 // The two thread groups of a node's block own degrees [0, LS) and [LS, L]
 // (deg_split); each thread keeps x, xdot and the accumulator of its degrees.
 //
@@ -790,21 +790,23 @@ struct NodeBwdDual {
                  float* Sdb, float* p2_dst, float* p2_src, int accumulate, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const int threads = 2 * ((d.C + 63) / 64) * 64;
-    // the split kernel without the position terms (with them it spills: the
-    // edge-parity kernel keeps the P2 variant)
+    // both variants on one schedule, so that asking for the position terms
+    // leaves gx2, Sbar and Sdb bitwise unchanged (the position-term variant
+    // of the split kernel spills 400 bytes per lane at lmax 6)
     if constexpr (L >= 6) {
-      if (!p2_dst) {
+      if (p2_dst)
+        hipLaunchKernelGGL((node_bwd_dual_split_kernel<L, M, true>), dim3(g.N), dim3(threads), 0, s, d, g, x, px,
+                           pos, omega, S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
+      else
         hipLaunchKernelGGL((node_bwd_dual_split_kernel<L, M, false>), dim3(g.N), dim3(threads), 0, s, d, g, x, px,
                            pos, omega, S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
-        return hipGetLastError();
-      }
-    }
-    if (p2_dst)
+    } else if (p2_dst) {
       hipLaunchKernelGGL((node_bwd_dual_kernel<L, M, true>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega,
                          S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
-    else
+    } else {
       hipLaunchKernelGGL((node_bwd_dual_kernel<L, M, false>), dim3(g.N), dim3(threads), 0, s, d, g, x, px, pos, omega,
                          S, Sdot, Tdb, Tb, gx2, Sbar, Sdb, p2_dst, p2_src, accumulate);
+    }
     return hipGetLastError();
   }
 };
