@@ -11,6 +11,7 @@
 #include "api_common.hpp"
 #include "gemm.hpp"
 #include "ops.hpp"
+#include "so3_gen.hpp"
 #include "wigner.hpp"
 
 namespace so2 {
@@ -40,32 +41,11 @@ int set_error(int code, const std::string& msg) { return fail(code, msg); }
 namespace {
 
 // ---------------------------------------------------------------- generators
-// G_k^(l) = d/dt D^(l)(exp(t [e_k]_x)) at t = 0, evaluated exactly by a
-// complex step through the Wigner recursion: D(I + i h K) = D(I) + i h G + O(h^2).
-void compute_generators(float* out) {
-  using cd = std::complex<double>;
-  const double h = 1e-30;
-  const int cross[3][9] = {{0, 0, 0, 0, 0, -1, 0, 1, 0}, {0, 0, 1, 0, 0, 0, -1, 0, 0}, {0, -1, 0, 1, 0, 0, 0, 0, 0}};
-  std::memset(out, 0, sizeof(float) * 3 * kGenSize);
-  for (int k = 0; k < 3; ++k) {
-    cd R[9], D1[9];
-    for (int a = 0; a < 9; ++a) R[a] = cd((a % 4 == 0) ? 1.0 : 0.0, h * cross[k][a]);
-    wigner_l1<cd>(R, D1);
-    float* G = out + k * kGenSize;
-    for (int a = 0; a < 9; ++a) G[1 + a] = (float)(D1[a].imag() / h);
-    std::vector<cd> prev(D1, D1 + 9), cur;
-    int off = 10;
-    for (int l = 2; l <= kMaxL; ++l) {
-      const int n = 2 * l + 1;
-      cur.assign(n * n, cd(0));
-      for (int m = -l; m <= l; ++m)
-        for (int c = -l; c <= l; ++c) cur[(m + l) * n + c + l] = wig_entry<cd>(l, m, c, D1, prev.data(), l - 1);
-      for (int a = 0; a < n * n; ++a) G[off + a] = (float)(cur[a].imag() / h);
-      off += n * n;
-      prev = cur;
-    }
-  }
-}
+// The so(3) generator table is evaluated at compile time (so3_gen.hpp, dual
+// numbers through the Wigner recursion), so the copy uploaded here for the
+// cooperative rotation-rate tables and the literals inside the kernels are
+// the same floats on every host.
+constexpr GenTable kGenHost = make_gen_table();
 
 // the kernels apply the generators through two candidate orders per row and
 // per column (gen_cand); a table entry outside them would be dropped
@@ -95,14 +75,9 @@ int ensure_init() {
   if (dev < 0 || dev >= 64) return fail(SO2_EUNSUPPORTED, "device index out of range");
   std::lock_guard<std::mutex> lk(g_init_mu);
   if (g_init_done[dev]) return SO2_OK;
-  static float table[3 * kGenSize];
-  static bool have = false;
-  if (!have) {
-    compute_generators(table);
-    if (!generators_sparse(table))
-      return fail(SO2_EUNSUPPORTED, "so(3) generator table outside the two-candidate pattern the kernels use");
-    have = true;
-  }
+  const float* table = kGenHost.v;
+  if (!generators_sparse(table))
+    return fail(SO2_EUNSUPPORTED, "so(3) generator table outside the two-candidate pattern the kernels use");
   SO2_HIP(upload_generators_fwd(table));
   SO2_HIP(upload_generators_bwd(table));
   SO2_HIP(upload_generators_dual(table));

@@ -58,11 +58,9 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
   __shared__ float sRed[TE * 4 * 4];
   __shared__ float sHead[TE * kMaxHeads];
   __shared__ int sDst[TE];
-  __shared__ float sG[3 * gen_off(L + 1)];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
   const int ne = (int)min((long)TE, g.e1 - e0);
-  gen_stage<L>(sG);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int i = g.dst[e];
@@ -113,7 +111,7 @@ __global__ __launch_bounds__(256) void edge_bwd_kernel(Dims d, GraphDev g, const
       for (int k = 0; k < 3; ++k) {
         float s = 0.f;
 #pragma unroll
-        for (int l = 1; l <= L; ++l) s += gen_form<L>(sG, k, l, u + l * l, gv + l * l);
+        for (int l = 1; l <= L; ++l) s += gen_form<L>(k, l, u + l * l, gv + l * l);
         tk[k] = ev * s;
       }
 #pragma unroll
@@ -162,7 +160,7 @@ struct EdgeBwd {
 // The torque terms sum_rows xb <(R G_k)_row, x_n> of a degree are taken as
 // <G_k^T y, x_n> with y = R^T xb, the edge's contribution to acc.
 template <int L, int M>
-__device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, RotPtr sG,
+__device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt,
                                                    const float (&xn)[(L + 1) * (L + 1)],
                                                    const float* __restrict__ S, const float* __restrict__ Tbar,
                                                    float* __restrict__ Sbar, long e, int cin,
@@ -200,7 +198,7 @@ __device__ __forceinline__ void node_bwd_edge_half(const Dims& d, RotPtr sRt, Ro
       if (i < n) acc[l * l + i] += y[i];
     if (l > 0)
 #pragma unroll
-      for (int k = 0; k < 3; ++k) tk[k] += gen_form<L>(sG, k, l, y, xn + l * l);
+      for (int k = 0; k < 3; ++k) tk[k] += gen_form<L>(k, l, y, xn + l * l);
     sb[l * Ci] = sacc;
   }
 }
@@ -219,10 +217,8 @@ __global__ __launch_bounds__(512) void node_bwd_kernel(Dims d, GraphDev g, const
   __shared__ float sRed[TE * 8 * 3];
   __shared__ int sE[TE];
   __shared__ float sComb[kCombFallback];
-  __shared__ float sG[3 * gen_off(L + 1)];
 
   const int node = blockIdx.x;
-  gen_stage<L>(sG);
   const int C = d.C;
   const int CW = blockDim.x / 2;
   const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
@@ -258,7 +254,7 @@ __global__ __launch_bounds__(512) void node_bwd_kernel(Dims d, GraphDev g, const
         float tk[3] = {0.f, 0.f, 0.f};
         if (act) {
           const int cin = pass == 0 ? C + c : c;
-          node_bwd_edge_half<L, M>(d, sR + t * K, sG, xn, S, Tbar, Sbar, sE[t], cin, acc, tk);
+          node_bwd_edge_half<L, M>(d, sR + t * K, xn, S, Tbar, Sbar, sE[t], cin, acc, tk);
         }
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -315,7 +311,7 @@ __device__ __forceinline__ void node_bwd_load(const Dims& d, const float* __rest
 }
 
 template <int L, int M, int LA, int LB, int DH, int VN>
-__device__ __forceinline__ void node_bwd_edge_degs(const Dims& d, RotPtr sRt, RotPtr sG, const float (&xn)[DH],
+__device__ __forceinline__ void node_bwd_edge_degs(const Dims& d, RotPtr sRt, const float (&xn)[DH],
                                                    const float (&v)[VN], float* __restrict__ Sbar, long e, int cin,
                                                    float (&acc)[DH], float (&tk)[3]) {
   constexpr int B = LA * LA, R0 = ridx(LA, -qhalf(LA, M), M), QR = q_range(LA, LB, M);
@@ -345,7 +341,7 @@ __device__ __forceinline__ void node_bwd_edge_degs(const Dims& d, RotPtr sRt, Ro
       if (i < n) acc[l * l - B + i] += y[i];
     if (l > 0)
 #pragma unroll
-      for (int k = 0; k < 3; ++k) tk[k] += gen_form<L>(sG, k, l, y, xn + l * l - B);
+      for (int k = 0; k < 3; ++k) tk[k] += gen_form<L>(k, l, y, xn + l * l - B);
     sb[l * Ci] = sacc;
   }
 }
@@ -367,10 +363,8 @@ __global__ __launch_bounds__(512) void node_bwd_split_kernel(Dims d, GraphDev g,
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sRed[TE * 8 * 3];
   __shared__ int sE[TE];
-  __shared__ float sG[3 * gen_off(L + 1)];
 
   const int node = blockIdx.x;
-  gen_stage<L>(sG);
   const int C = d.C;
   const int CW = blockDim.x / 2;
   const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, degree half
@@ -410,10 +404,10 @@ __global__ __launch_bounds__(512) void node_bwd_split_kernel(Dims d, GraphDev g,
           float v[VN];
           if (grp == 0) {
             node_bwd_load<L, M, 0, LS, VN>(d, S, Tbar, sE[t], cin, v);
-            node_bwd_edge_degs<L, M, 0, LS, DH, VN>(d, sR + t * K, sG, xn, v, Sbar, sE[t], cin, acc, tk);
+            node_bwd_edge_degs<L, M, 0, LS, DH, VN>(d, sR + t * K, xn, v, Sbar, sE[t], cin, acc, tk);
           } else {
             node_bwd_load<L, M, LS, L + 1, VN>(d, S, Tbar, sE[t], cin, v);
-            node_bwd_edge_degs<L, M, LS, L + 1, DH, VN>(d, sR + t * K, sG, xn, v, Sbar, sE[t], cin, acc, tk);
+            node_bwd_edge_degs<L, M, LS, L + 1, DH, VN>(d, sR + t * K, xn, v, Sbar, sE[t], cin, acc, tk);
           }
         }
 #pragma unroll

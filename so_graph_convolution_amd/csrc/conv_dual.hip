@@ -77,11 +77,9 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sW[TE * 3];
   __shared__ int sNode[2][TE];
-  __shared__ float sG[3 * gen_off(L + 1)];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
   const int ne = (int)min((long)TE, g.e1 - e0);
-  gen_stage<L>(sG);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int j = g.src[e], i = g.dst[e];
@@ -137,7 +135,7 @@ __global__ __launch_bounds__(256) void edge_dual_kernel(Dims d, GraphDev g, cons
         const float sv = svv[l], sdv = sdvv[l];
         const int q = qhalf(l, M), n = 2 * l + 1;
         float ga[2 * L + 1];   // G_w a: the rows of Rdot = R G_w applied as R (G_w a)
-        gw_apply<L, false>(sG, w, l, a + l * l, ga);
+        gw_apply<L, false>(w, l, a + l * l, ga);
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
           const int off = rot_off(l, M) + (m + q) * n;
@@ -185,10 +183,8 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
   __shared__ float sA[TE * ST], sB[TE * ST];
   __shared__ float sW[TE * 3];
   __shared__ float sComb[kCombFallback];
-  __shared__ float sG[3 * gen_off(L + 1)];
 
   const int node = blockIdx.x;
-  gen_stage<L>(sG);
   int beg, end;
   in_range(g, node, &beg, &end);
   if (accumulate && beg == end) return;
@@ -238,7 +234,7 @@ __global__ __launch_bounds__(512) void node_dual_kernel(Dims d, GraphDev g, cons
             row_axpy<L>(r, ev * v, z, n);
             row_axpy<L>(r, ev * vdv + pv * v, acc + l * l, n);
           }
-          gw_apply<L, true>(sG, w, l, z, zw);
+          gw_apply<L, true>(w, l, z, zw);
 #pragma unroll
           for (int i = 0; i < 2 * L + 1; ++i)
             if (i < n) acc[l * l + i] += zw[i];
@@ -291,11 +287,9 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
   __shared__ float sRed[TE * 4 * 7];
   __shared__ float sHead[TE * kMaxHeads];
   __shared__ int sDst[TE];
-  __shared__ float sG[3 * gen_off(L + 1)];
 
   const long e0 = g.e0 + (long)blockIdx.x * TE;
   const int ne = (int)min((long)TE, g.e1 - e0);
-  gen_stage<L>(sG);
   for (int t = threadIdx.x; t < ne; t += blockDim.x) {
     const long e = e0 + t;
     const int i = g.dst[e];
@@ -328,7 +322,7 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
       for (int l = 0; l <= L; ++l) {
         const int q = qhalf(l, M), n = 2 * l + 1;
         float gw[2 * L + 1];   // G_w gy: the rows of Rdot = R G_w applied as R (G_w gy)
-        gw_apply<L, false>(sG, w, l, gv + l * l, gw);
+        gw_apply<L, false>(w, l, gv + l * l, gw);
 #pragma unroll
         for (int m = -q; m <= q; ++m) {
           const int off = rot_off(l, M) + (m + q) * n;
@@ -360,11 +354,11 @@ __global__ __launch_bounds__(256) void edge_bwd_dual_kernel(Dims d, GraphDev g, 
             row_axpy<L>(r, v, u0, n);
             row_axpy<L>(r, vd, u1, n);
           }
-          gw_apply<L, true>(sG, w, l, u0, u0w);
+          gw_apply<L, true>(w, l, u0, u0w);
 #pragma unroll
           for (int k = 0; k < 3; ++k) {
-            const float a0 = gen_form<L>(sG, k, l, u0, gv + l * l);
-            const float a1 = gen_form<L>(sG, k, l, u1, gv + l * l) + gen_form<L>(sG, k, l, u0w, gv + l * l);
+            const float a0 = gen_form<L>(k, l, u0, gv + l * l);
+            const float a1 = gen_form<L>(k, l, u1, gv + l * l) + gen_form<L>(k, l, u0w, gv + l * l);
             tk[k] += ev * a1 + pv * a0;
             tk[3 + k] += ev * a0;
           }
@@ -453,10 +447,8 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
   __shared__ float sRed[P2 ? TE * 8 * 6 : 1];
   __shared__ int sE[TE];
   __shared__ float sComb[kCombFallback];
-  __shared__ float sG[P2 ? 3 * gen_off(L + 1) : 1];
 
   const int node = blockIdx.x;
-  if (P2) gen_stage<L>(sG);
   const int C = d.C, Ci = 2 * C, wT = d.wT(), wS = (L + 1) * Ci;
   const int CW = blockDim.x / 2;
   const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, edge parity
@@ -548,9 +540,9 @@ __global__ __launch_bounds__(512) void node_bwd_dual_kernel(Dims d, GraphDev g, 
               // sum over rows of u1 (R G_k x) + u2 ((R G_k) xd + (Rdot G_k) x), u2 (R G_k x)
 #pragma unroll
               for (int k = 0; k < 3; ++k) {
-                const float ga = gen_form<L>(sG, k, l, z, xn + l * l);
-                tk[k] += gen_form<L>(sG, k, l, y, xn + l * l) + gen_form<L>(sG, k, l, z, xdn + l * l) +
-                         gen_form<L>(sG, k, l, zw, xn + l * l);
+                const float ga = gen_form<L>(k, l, z, xn + l * l);
+                tk[k] += gen_form<L>(k, l, y, xn + l * l) + gen_form<L>(k, l, z, xdn + l * l) +
+                         gen_form<L>(k, l, zw, xn + l * l);
                 tk[3 + k] += ga;
               }
             }
@@ -620,7 +612,7 @@ __device__ __forceinline__ void node_bwd_dual_load(const Dims& d, const float* _
 }
 
 template <int L, int M, bool P2, int LA, int LB, int DH, int VN>
-__device__ __forceinline__ void node_bwd_dual_degs(const Dims& d, RotPtr sRt, RotPtr sRdt, RotPtr sG,
+__device__ __forceinline__ void node_bwd_dual_degs(const Dims& d, RotPtr sRt, RotPtr sRdt,
                                                    const float (&xn)[DH], const float (&xdn)[DH],
                                                    const float (&v)[VN], float* __restrict__ Sbar,
                                                    float* __restrict__ Sdb, long e, int cin, float (&acc)[DH],
@@ -671,9 +663,9 @@ __device__ __forceinline__ void node_bwd_dual_degs(const Dims& d, RotPtr sRt, Ro
       // sum over rows of u1 (R G_k x) + u2 ((R G_k) xd + (Rdot G_k) x), u2 (R G_k x)
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
-        const float ga = gen_form<L>(sG, k, l, z, xn + l * l - B);
-        tk[k] += gen_form<L>(sG, k, l, y, xn + l * l - B) + gen_form<L>(sG, k, l, z, xdn + l * l - B) +
-                 gen_form<L>(sG, k, l, zw, xn + l * l - B);
+        const float ga = gen_form<L>(k, l, z, xn + l * l - B);
+        tk[k] += gen_form<L>(k, l, y, xn + l * l - B) + gen_form<L>(k, l, z, xdn + l * l - B) +
+                 gen_form<L>(k, l, zw, xn + l * l - B);
         tk[3 + k] += ga;
       }
     }
@@ -701,10 +693,8 @@ __global__ __launch_bounds__(512) void node_bwd_dual_split_kernel(
   __shared__ float sW[TE * 3];
   __shared__ float sRed[P2 ? TE * 8 * 6 : 1];
   __shared__ int sE[TE];
-  __shared__ float sG[P2 ? 3 * gen_off(L + 1) : 1];
 
   const int node = blockIdx.x;
-  if (P2) gen_stage<L>(sG);
   const int C = d.C;
   const int CW = blockDim.x / 2;
   const int c = threadIdx.x % CW, grp = threadIdx.x / CW;   // channel, degree half
@@ -746,11 +736,11 @@ __global__ __launch_bounds__(512) void node_bwd_dual_split_kernel(
           float v[VN];
           if (grp == 0) {
             node_bwd_dual_load<L, M, 0, LS, VN>(d, S, Sdot, Tdb, Tb, e, cin, v);
-            node_bwd_dual_degs<L, M, P2, 0, LS, DH, VN>(d, sR + t * K, sRd + t * K, sG, xn, xdn, v, Sbar, Sdb, e,
+            node_bwd_dual_degs<L, M, P2, 0, LS, DH, VN>(d, sR + t * K, sRd + t * K, xn, xdn, v, Sbar, Sdb, e,
                                                         cin, acc, tk);
           } else {
             node_bwd_dual_load<L, M, LS, L + 1, VN>(d, S, Sdot, Tdb, Tb, e, cin, v);
-            node_bwd_dual_degs<L, M, P2, LS, L + 1, DH, VN>(d, sR + t * K, sRd + t * K, sG, xn, xdn, v, Sbar, Sdb,
+            node_bwd_dual_degs<L, M, P2, LS, L + 1, DH, VN>(d, sR + t * K, sRd + t * K, xn, xdn, v, Sbar, Sdb,
                                                             e, cin, acc, tk);
           }
         }

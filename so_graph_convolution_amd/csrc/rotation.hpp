@@ -4,6 +4,7 @@
 #pragma once
 #include "ops.hpp"
 #include "wigner.hpp"
+#include "so3_gen.hpp"
 
 namespace so2 {
 
@@ -93,17 +94,13 @@ __device__ __forceinline__ float rot_ld(RotPtr p) {
   return *(const volatile __attribute__((address_space(3))) float*)(p);
 }
 
+// The generator blocks as compile-time constants (so3_gen.hpp): every product
+// with a generator entry below has indices that are constants after
+// unrolling, so the entry is a literal operand of its instruction.
+constexpr GenTable kGenTab = make_gen_table();
+__device__ __forceinline__ float gen_at(int k, int l, int idx) { return kGenTab.v[k * kGenSize + gen_off(l) + idx]; }
+
 // o[ridx(l,m)] = sum_n R[l][m][n] a[l*l + l + n]   (rotate degree-major -> retained rows)
-// The generator blocks of degrees <= L, staged in LDS once per block (three
-// tables of gen_off(L + 1) floats) and read like the rotation rows: a table
-// value in constant memory is loop-invariant, and a kernel that applies the
-// generators inside its edge loop would otherwise keep every value it uses in
-// registers.
-template <int L>
-__device__ __forceinline__ void gen_stage(float* sG) {
-  constexpr int n = gen_off(L + 1);
-  for (int i = threadIdx.x; i < 3 * n; i += blockDim.x) sG[i] = c_gen[(i / n) * kGenSize + i % n];
-}
 
 // <a, G_k^(l) b> for degree-l blocks a, b (k, l compile-time after
 // unrolling), taken as <G_k^T a, b>: column c of G_k has its nonzeros at the
@@ -111,8 +108,7 @@ __device__ __forceinline__ void gen_stage(float* sG) {
 // entry of G_k^T a is two table products.
 // (Explicit fused forms throughout: every kernel instantiation rounds alike.)
 template <int L>
-__device__ __forceinline__ float gen_form(RotPtr G3, int k, int l, const float* a, const float* b) {
-  RotPtr G = G3 + k * gen_off(L + 1) + gen_off(l);
+__device__ __forceinline__ float gen_form(int k, int l, const float* a, const float* b) {
   const int n = 2 * l + 1;
   float s = 0.f;
 #pragma unroll
@@ -121,8 +117,8 @@ __device__ __forceinline__ float gen_form(RotPtr G3, int k, int l, const float* 
       int i0, i1;
       gen_cand(k, c - l, &i0, &i1);
       float g = 0.f;
-      if (i0 >= -l && i0 <= l) g = __builtin_fmaf(rot_ld(G + (i0 + l) * n + c), a[i0 + l], g);
-      if (i1 != i0 && i1 >= -l && i1 <= l) g = __builtin_fmaf(rot_ld(G + (i1 + l) * n + c), a[i1 + l], g);
+      if (i0 >= -l && i0 <= l) g = __builtin_fmaf(gen_at(k, l, (i0 + l) * n + c), a[i0 + l], g);
+      if (i1 != i0 && i1 >= -l && i1 <= l) g = __builtin_fmaf(gen_at(k, l, (i1 + l) * n + c), a[i1 + l], g);
       s = __builtin_fmaf(g, b[c], s);
     }
   }
@@ -137,8 +133,7 @@ __device__ __forceinline__ float gen_form(RotPtr G3, int k, int l, const float* 
 // depends on a alone, so nothing is hoisted out of a loop over edges that
 // share a.
 template <int L, bool TR>
-__device__ __forceinline__ void gw_apply(RotPtr G3, const float (&w)[3], int l, const float* a,
-                                         float (&g)[2 * L + 1]) {
+__device__ __forceinline__ void gw_apply(const float (&w)[3], int l, const float* a, float (&g)[2 * L + 1]) {
   const int n = 2 * l + 1;
 #pragma unroll
   for (int i = 0; i < 2 * L + 1; ++i) {
@@ -146,12 +141,11 @@ __device__ __forceinline__ void gw_apply(RotPtr G3, const float (&w)[3], int l, 
       float s = 0.f;
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
-        RotPtr G = G3 + k * gen_off(L + 1) + gen_off(l);
         int j0, j1;
         gen_cand(k, i - l, &j0, &j1);
-        if (j0 >= -l && j0 <= l) s = __builtin_fmaf(w[k] * rot_ld(G + (TR ? (j0 + l) * n + i : i * n + j0 + l)), a[j0 + l], s);
+        if (j0 >= -l && j0 <= l) s = __builtin_fmaf(w[k] * gen_at(k, l, TR ? (j0 + l) * n + i : i * n + j0 + l), a[j0 + l], s);
         if (j1 != j0 && j1 >= -l && j1 <= l)
-          s = __builtin_fmaf(w[k] * rot_ld(G + (TR ? (j1 + l) * n + i : i * n + j1 + l)), a[j1 + l], s);
+          s = __builtin_fmaf(w[k] * gen_at(k, l, TR ? (j1 + l) * n + i : i * n + j1 + l), a[j1 + l], s);
       }
       g[i] = s;
     }
