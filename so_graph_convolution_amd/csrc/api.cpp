@@ -1,7 +1,6 @@
 // C ABI of the fused SO(2) convolution: argument checks, workspace layout and
 // the kernel schedules of the forward, backward and double backward.
 #include <algorithm>
-#include <complex>
 #include <cstdio>
 #include <cstring>
 #include <mutex>

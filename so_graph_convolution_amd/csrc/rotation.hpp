@@ -100,8 +100,6 @@ __device__ __forceinline__ float rot_ld(RotPtr p) {
 constexpr GenTable kGenTab = make_gen_table();
 __device__ __forceinline__ float gen_at(int k, int l, int idx) { return kGenTab.v[k * kGenSize + gen_off(l) + idx]; }
 
-// o[ridx(l,m)] = sum_n R[l][m][n] a[l*l + l + n]   (rotate degree-major -> retained rows)
-
 // <a, G_k^(l) b> for degree-l blocks a, b (k, l compile-time after
 // unrolling), taken as <G_k^T a, b>: column c of G_k has its nonzeros at the
 // rows gen_cand gives for order c (the generators are antisymmetric), so each
@@ -152,6 +150,7 @@ __device__ __forceinline__ void gw_apply(const float (&w)[3], int l, const float
   }
 }
 
+// o[ridx(l,m)] = sum_n R[l][m][n] a[l*l + l + n]   (rotate degree-major -> retained rows)
 template <int L, int M>
 __device__ __forceinline__ void rot_fwd(RotPtr R, const float (&a)[(L + 1) * (L + 1)],
                                         float (&o)[q_count(L, M)]) {
