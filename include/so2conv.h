@@ -423,6 +423,17 @@ int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* 
  * cleared. */
 int so2conv_debug_status(void* stream);
 
+/* Copies the so(3) generator table the kernels use for the rotation torques
+ * and rotation rates (Section 2's frame rotation, differentiated: G_k^(l) =
+ * d/dt D^(l)(exp(t [e_k]_x)) at t = 0, k = x, y, z) to host memory `out`
+ * (so2conv_generator_table(NULL, 0) floats: generator k's table at offset
+ * k * (that count / 3), degree l = 0..6's (2l+1)^2 block row-major at offset
+ * sum_{l' < l} (2l'+1)^2 within it, rows and columns in order m = -l..l;
+ * the l = 0 block is the single zero). The table is evaluated when the
+ * library is compiled; no GPU is needed. Returns the number of floats, or
+ * SO2_EINVAL if out is non-NULL and n is smaller. */
+int so2conv_generator_table(float* out, int64_t n);
+
 /* message of the last failing call on this thread ("" if none) */
 const char* so2conv_last_error(void);
 /* 1 if (lmax, mmax) has compiled kernels */

@@ -74,6 +74,7 @@ EXPORTS = {
     "so2conv_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "so2conv_supported": (ctypes.c_int, [c_i32, c_i32]),
+    "so2conv_generator_table": (ctypes.c_int, [c_vp, c_i64]),
     "so2conv_debug_status": (ctypes.c_int, [c_vp]),
     "so2mole_workspace_bytes": (c_sz, [ctypes.POINTER(Cfg), ctypes.POINTER(MoleCfg), c_i32, c_i64, ctypes.c_int,
                                        c_i64]),

@@ -1631,6 +1631,14 @@ int so2conv_profile_read(int kind, int64_t* launches, double* total_ms, double* 
 
 int so2conv_supported(int32_t lmax, int32_t mmax) { return lm_supported(lmax, mmax) ? 1 : 0; }
 
+int so2conv_generator_table(float* out, int64_t n) {
+  const int64_t size = 3 * kGenSize;
+  if (!out) return (int)size;
+  if (n < size) return fail(SO2_EINVAL, "so2conv_generator_table: output holds fewer than 3 * kGenSize floats");
+  std::memcpy(out, kGenHost.v, sizeof(float) * size);
+  return (int)size;
+}
+
 int so2conv_debug_status(void* stream) {
   clear_error();
   SO2_HIP(hipStreamSynchronize((hipStream_t)stream));

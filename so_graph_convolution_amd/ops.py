@@ -12,9 +12,9 @@ import dataclasses
 import torch
 
 from ._binding import (SO2_ACT_GATE, SO2_ACT_SWIGLU_S2, SO2_DEBUG_CHECKS, SO2_F32_NATIVE, SO2_FUSED_GATE, Cfg,
-                       GraphC, check, lib)
+                       GraphC, So2Error, check, lib)
 
-__all__ = ["SO2Config", "Graph", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_fwd_noalloc", "so2conv_bwd",
+__all__ = ["SO2Config", "Graph", "so2conv_generator_table", "so2conv_graph_prepare", "so2conv_fwd", "so2conv_fwd_noalloc", "so2conv_bwd",
            "so2conv_dbwd",
            "so2conv_debug_rotate_gather", "so2conv_workspace_bytes", "so2conv_saved_bytes",
            "so2conv_saved_bwd_bytes", "weight_shapes",
@@ -197,6 +197,18 @@ def so2conv_saved_bytes(cfg: SO2Config, n_edges) -> int:
 def so2conv_saved_bwd_bytes(cfg: SO2Config, n_edges) -> int:
     c = cfg.c()
     return int(lib().so2conv_saved_bwd_bytes(ctypes.byref(c), n_edges))
+
+
+def so2conv_generator_table() -> torch.Tensor:
+    """The so(3) generator table compiled into the library (host memory, no
+    GPU): float32 [3, n] for k = x, y, z, degree l's (2l+1)^2 block
+    row-major at offset sum_{l' < l} (2l'+1)^2."""
+    n = int(lib().so2conv_generator_table(None, 0))
+    out = torch.empty(n, dtype=torch.float32)
+    got = lib().so2conv_generator_table(ctypes.c_void_p(out.data_ptr()), n)
+    if got != n:
+        raise So2Error(f"so2conv_generator_table failed ({got})")
+    return out.view(3, n // 3)
 
 
 def _saved_bwd(cfg, g, saved_bwd, device, allocate):
